@@ -1,0 +1,146 @@
+"""Seeded synthetic workloads for the GDN-2 recurrence.
+
+This module is shared by the oracle side and the HIP side and therefore holds
+none of the recurrence's arithmetic: it only draws inputs.  All draws come from
+``torch.Generator('cpu')`` so that a seed gives the same tensors on every host,
+in a fixed order: q, k, v, log_alpha, b, w, initial state, then extras.
+
+Distributions follow the workloads the pages describe (key/query paths end in an
+L2 normalisation and the two gates are sigmoid projections: page "Why NVIDIA
+Gated DeltaNet-2 separates erase and write gates", sections "Gated Delta Rule-2"
+and "implications for practitioners"; training shape of sequence 4K and a 0.5M
+token global batch with a 262,144-float recurrent state per layer: same page,
+section "1.3B parameters and 100B-token training spec"):
+
+* q, k ~ N(0,1), L2-normalised over the key dimension per (b, t, h)
+* v ~ N(0,1)
+* log_alpha ~ U[lo, hi] per key channel per token (fp32 always)
+* b, w = sigmoid(2 * N(0,1)) per channel
+* optional initial state ~ N(0, std^2) (fp32 always)
+
+Values are drawn in fp32 and then cast to the workload's dtype; the oracle is
+handed exactly the cast values.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    T: int
+    H: int
+    dk: int
+    dv: int
+    dtype: torch.dtype
+    seed: int
+    g_lo: float = -0.2
+    g_hi: float = -0.001
+    # heads [0, strong_heads) take log_alpha ~ U[strong_lo, strong_hi]
+    strong_heads: int = 0
+    strong_lo: float = -5.0
+    strong_hi: float = -1.0
+    weak_lo: Optional[float] = None
+    weak_hi: Optional[float] = None
+    s0_std: Optional[float] = None  # None = zero initial state
+    steps: int = 0  # decode workloads: number of steps
+    pool: int = 0  # decode workloads: distinct token sets, used cyclically
+
+    @property
+    def dtype_name(self) -> str:
+        return {torch.float32: "f32", torch.bfloat16: "bf16"}[self.dtype]
+
+
+# The five workloads.  Index i uses seed i.
+TINY_FP32 = Workload("tiny_fp32_B1_T256_H2_d64", B=1, T=256, H=2, dk=64, dv=64,
+                     dtype=torch.float32, seed=0)
+TRAIN_4K = Workload("train_bf16_B8_T4096_H16_d128", B=8, T=4096, H=16, dk=128, dv=128,
+                    dtype=torch.bfloat16, seed=1)
+DECODE = Workload("decode_bf16_N256_H16_d128_x1024", B=256, T=1, H=16, dk=128, dv=128,
+                  dtype=torch.bfloat16, seed=2, s0_std=0.02, steps=1024, pool=16)
+LONG_32K = Workload("long_bf16_B1_T32768_H16_d128", B=1, T=32768, H=16, dk=128, dv=128,
+                    dtype=torch.bfloat16, seed=3, strong_heads=8, strong_lo=-5.0,
+                    strong_hi=-1.0, weak_lo=-0.05, weak_hi=-0.0001)
+FWD_BWD_4K = Workload("fwdbwd_bf16_B4_T4096_H16_d128", B=4, T=4096, H=16, dk=128, dv=128,
+                      dtype=torch.bfloat16, seed=4, s0_std=0.02)
+
+ALL = (TINY_FP32, TRAIN_4K, DECODE, LONG_32K, FWD_BWD_4K)
+
+
+def _uniform(gen, shape, lo, hi):
+    return torch.rand(shape, generator=gen, dtype=torch.float32) * (hi - lo) + lo
+
+
+def _unit_normal_rows(gen, shape):
+    x = torch.randn(shape, generator=gen, dtype=torch.float32)
+    return x / x.norm(dim=-1, keepdim=True).clamp_min(1e-12)
+
+
+def _gate(gen, shape):
+    return torch.sigmoid(2.0 * torch.randn(shape, generator=gen, dtype=torch.float32))
+
+
+def make_inputs(wl: Workload, seed: Optional[int] = None, B: Optional[int] = None,
+                T: Optional[int] = None):
+    """Draw (q, k, v, log_alpha, b, w, s0) for a forward workload on the CPU.
+
+    ``B``/``T`` override the workload's sizes (same distributions), so that a
+    smaller case of the same recipe can be drawn.  Returns a dict of CPU
+    tensors; q,k,v,b,w in ``wl.dtype``, log_alpha and s0 in fp32 (s0 may be
+    None)."""
+    seed = wl.seed if seed is None else seed
+    B = wl.B if B is None else B
+    T = wl.T if T is None else T
+    H, dk, dv = wl.H, wl.dk, wl.dv
+    gen = torch.Generator("cpu").manual_seed(seed)
+    q = _unit_normal_rows(gen, (B, T, H, dk))
+    k = _unit_normal_rows(gen, (B, T, H, dk))
+    v = torch.randn((B, T, H, dv), generator=gen, dtype=torch.float32)
+    if wl.strong_heads:
+        g = torch.empty((B, T, H, dk), dtype=torch.float32)
+        hs = wl.strong_heads
+        g[:, :, :hs] = _uniform(gen, (B, T, hs, dk), wl.strong_lo, wl.strong_hi)
+        g[:, :, hs:] = _uniform(gen, (B, T, H - hs, dk), wl.weak_lo, wl.weak_hi)
+    else:
+        g = _uniform(gen, (B, T, H, dk), wl.g_lo, wl.g_hi)
+    b = _gate(gen, (B, T, H, dk))
+    w = _gate(gen, (B, T, H, dv))
+    s0 = None
+    if wl.s0_std is not None:
+        s0 = torch.randn((B, H, dk, dv), generator=gen, dtype=torch.float32) * wl.s0_std
+    dt = wl.dtype
+    return dict(q=q.to(dt), k=k.to(dt), v=v.to(dt), log_alpha=g, b=b.to(dt), w=w.to(dt), s0=s0)
+
+
+def make_upstream_grad(wl: Workload, seed: Optional[int] = None, B=None, T=None):
+    """do ~ N(0,1) of the output's shape, drawn after the forward inputs."""
+    seed = (wl.seed if seed is None else seed) + 1_000_003
+    B = wl.B if B is None else B
+    T = wl.T if T is None else T
+    gen = torch.Generator("cpu").manual_seed(seed)
+    return torch.randn((B, T, wl.H, wl.dv), generator=gen, dtype=torch.float32)
+
+
+def make_decode_pool(wl: Workload, seed: Optional[int] = None, N: Optional[int] = None):
+    """Decode workload: initial state [N,H,dk,dv] fp32 ~ N(0, s0_std^2) and a pool
+    of ``wl.pool`` token sets (q,k,v,log_alpha,b,w each [P,N,H,d]); step s uses
+    pool entry s mod P."""
+    seed = wl.seed if seed is None else seed
+    N = wl.B if N is None else N
+    H, dk, dv, P = wl.H, wl.dk, wl.dv, wl.pool
+    gen = torch.Generator("cpu").manual_seed(seed)
+    state = torch.randn((N, H, dk, dv), generator=gen, dtype=torch.float32) * wl.s0_std
+    q = _unit_normal_rows(gen, (P, N, H, dk))
+    k = _unit_normal_rows(gen, (P, N, H, dk))
+    v = torch.randn((P, N, H, dv), generator=gen, dtype=torch.float32)
+    g = _uniform(gen, (P, N, H, dk), wl.g_lo, wl.g_hi)
+    b = _gate(gen, (P, N, H, dk))
+    w = _gate(gen, (P, N, H, dv))
+    dt = wl.dtype
+    return dict(state=state, q=q.to(dt), k=k.to(dt), v=v.to(dt), log_alpha=g, b=b.to(dt),
+                w=w.to(dt))
