@@ -1,0 +1,172 @@
+"""Gated DeltaNet-2 recurrence on AMD MI355X (gfx950): Python binding.
+
+This module only marshals arguments to the C ABI of ``libgdn2.so``
+(``include/gdn2.h``): it checks tensor dtypes, shapes, devices and contiguity,
+allocates outputs with PyTorch (device memory and streams are all PyTorch is
+used for) and passes raw pointers plus the current HIP stream.  Every step of
+the computation runs in the library's HIP kernels; there is no fallback.
+
+    o, S_T = chunk_fwd(q, k, v, log_alpha, b, w, initial_state=None)
+    o      = decode_step(q, k, v, log_alpha, b, w, state)   # state updated in place
+
+Layouts: q, k, b, log_alpha [B,T,H,dk]; v, w, o [B,T,H,dv]; state [B,H,dk,dv]
+(decode: the same without T).  q, k, v, b, w are bf16 or fp32 (all the same);
+log_alpha and the state are fp32.  o is fp32 by default (the fp32 accumulation
+carried to the output); ``out_dtype=`` the input dtype rounds it on the store.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = ["chunk_fwd", "decode_step", "supported", "version", "library_path", "Gdn2Error",
+           "CHUNK"]
+
+CHUNK = 64
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libgdn2.so")
+_lock = threading.Lock()
+_lib = None
+
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+_STATUS = {0: "GDN2_OK", 1: "GDN2_ERR_NULL", 2: "GDN2_ERR_SHAPE", 3: "GDN2_ERR_UNSUPPORTED",
+           4: "GDN2_ERR_MISALIGNED", 5: "GDN2_ERR_ALIAS", 6: "GDN2_ERR_HIP"}
+
+
+class Gdn2Error(RuntimeError):
+    def __init__(self, call, status, message):
+        super().__init__("%s failed: %s (%s)" % (call, _STATUS.get(status, status), message))
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(
+                "libgdn2.so is not built (expected at %s); run "
+                "`python -m gated_delta_rule_gdn2_amd.build`" % _LIB_PATH)
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.gdn2_chunk_fwd.argtypes = [P] * 9 + [I64] * 5 + [I32, I32, P]
+        lib.gdn2_chunk_fwd.restype = I32
+        lib.gdn2_decode_step.argtypes = [P] * 8 + [I64] * 4 + [I32, I32, P]
+        lib.gdn2_decode_step.restype = I32
+        lib.gdn2_supported.argtypes = [I32, I64, I64, I32]
+        lib.gdn2_supported.restype = I32
+        lib.gdn2_status_string.argtypes = [I32]
+        lib.gdn2_status_string.restype = ctypes.c_char_p
+        lib.gdn2_version.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def version() -> str:
+    return _load().gdn2_version().decode()
+
+
+def supported(which: str, dk: int, dv: int, dtype: torch.dtype) -> bool:
+    w = {"chunk_fwd": 0, "decode_step": 1}[which]
+    return bool(_load().gdn2_supported(w, dk, dv, _DTYPES[dtype]))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(name, t, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stream_handle(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def chunk_fwd(q, k, v, log_alpha, b, w, initial_state=None, *, o=None, final_state=None,
+              output_final_state=True, out_dtype=torch.float32):
+    """Chunk-parallel forward.  Returns (o, S_T); S_T is None when
+    ``output_final_state`` is False.  ``final_state`` may be passed (and may be
+    ``initial_state`` itself, for an in-place update)."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B,T,H,dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("chunk_fwd runs on the GPU; got tensors on %s" % dev)
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise TypeError("q dtype must be float32 or bfloat16")
+    for name, t, shp, tdt in (("k", k, (B, T, H, dk), dt), ("v", v, (B, T, H, dv), dt),
+                              ("log_alpha", log_alpha, (B, T, H, dk), torch.float32),
+                              ("b", b, (B, T, H, dk), dt), ("w", w, (B, T, H, dv), dt),
+                              ("q", q, (B, T, H, dk), dt)):
+        _check(name, t, shp, tdt, dev)
+    if initial_state is not None:
+        _check("initial_state", initial_state, (B, H, dk, dv), torch.float32, dev)
+    if out_dtype not in (torch.float32, dt):
+        raise TypeError("out_dtype must be float32 or the input dtype")
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
+    else:
+        _check("o", o, (B, T, H, dv), out_dtype, dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _check("final_state", final_state, (B, H, dk, dv), torch.float32, dev)
+    st = _load().gdn2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+                                _ptr(initial_state), _ptr(o), _ptr(final_state), B, T, H, dk, dv,
+                                _DTYPES[dt], _DTYPES[out_dtype], _stream_handle(dev))
+    if st != 0:
+        raise Gdn2Error("gdn2_chunk_fwd", st, _load().gdn2_status_string(st).decode())
+    return o, final_state
+
+
+def decode_step(q, k, v, log_alpha, b, w, state, *, o=None, out_dtype=torch.float32):
+    """One recurrent step; ``state`` [N,H,dk,dv] fp32 is updated in place.  Returns o."""
+    if q.dim() != 3:
+        raise ValueError("q must be [N,H,dk]")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("decode_step runs on the GPU; got tensors on %s" % dev)
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise TypeError("q dtype must be float32 or bfloat16")
+    for name, t, shp, tdt in (("k", k, (N, H, dk), dt), ("v", v, (N, H, dv), dt),
+                              ("log_alpha", log_alpha, (N, H, dk), torch.float32),
+                              ("b", b, (N, H, dk), dt), ("w", w, (N, H, dv), dt),
+                              ("state", state, (N, H, dk, dv), torch.float32),
+                              ("q", q, (N, H, dk), dt)):
+        _check(name, t, shp, tdt, dev)
+    if out_dtype not in (torch.float32, dt):
+        raise TypeError("out_dtype must be float32 or the input dtype")
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
+    else:
+        _check("o", o, (N, H, dv), out_dtype, dev)
+    st = _load().gdn2_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+                                  _ptr(state), _ptr(o), N, H, dk, dv, _DTYPES[dt],
+                                  _DTYPES[out_dtype], _stream_handle(dev))
+    if st != 0:
+        raise Gdn2Error("gdn2_decode_step", st, _load().gdn2_status_string(st).decode())
+    return o

@@ -1,0 +1,163 @@
+// gdn2_api.hip -- the exported C ABI (include/gdn2.h): argument validation,
+// choice of the launch configuration, and dispatch to the kernels.
+//
+// Everything here runs on the host.  Validation is complete before any HIP
+// call, so an invalid call enqueues nothing and writes nothing.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+
+#include "../../include/gdn2.h"
+#include "gdn2_launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+Range range_of(const void* p, int64_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + static_cast<uintptr_t>(bytes)};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+bool chunk_supported(int64_t dk, int64_t dv, gdn2_dtype_t dt) {
+    if (dt == GDN2_DTYPE_BF16) return (dk == 128 && dv == 128) || (dk == 64 && dv == 64);
+    if (dt == GDN2_DTYPE_F32) return dk == 64 && dv == 64;
+    return false;
+}
+bool decode_supported(int64_t dk, int64_t dv, gdn2_dtype_t dt) {
+    if (dt != GDN2_DTYPE_BF16 && dt != GDN2_DTYPE_F32) return false;
+    return (dk == 128 && dv == 128) || (dk == 64 && dv == 64);
+}
+
+// Value columns per workgroup.  The columns of the state evolve independently,
+// so a (sequence, head) splits into dv / dvs workgroups; the smallest power of
+// two of slices that gives at least one workgroup per compute unit is taken
+// (more slices repeat the key-side work of every chunk in every slice).  A
+// slice holds at most 64 columns (LDS budget).
+int choose_dvs(int64_t BH, int64_t dv, int cus) {
+    const int64_t max_slices = dv / 16;
+    const int64_t min_slices = dv / 64;
+    int64_t s = min_slices < 1 ? 1 : min_slices;
+    while (s < max_slices && BH * s < cus) s *= 2;
+    return static_cast<int>(dv / s);
+}
+
+int device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    return cus;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn2_status_t gdn2_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                             const void* b, const void* w, const float* initial_state, void* o,
+                             float* final_state, int64_t B, int64_t T, int64_t H, int64_t dk,
+                             int64_t dv, gdn2_dtype_t dtype, gdn2_dtype_t o_dtype, void* stream) {
+    if (!q || !k || !v || !log_alpha || !b || !w || !o) return GDN2_ERR_NULL;
+    if (dtype != GDN2_DTYPE_F32 && dtype != GDN2_DTYPE_BF16) return GDN2_ERR_UNSUPPORTED;
+    if (o_dtype != GDN2_DTYPE_F32 && o_dtype != dtype) return GDN2_ERR_UNSUPPORTED;
+    if (B < 1 || T < 1 || H < 1 || dk < 1 || dv < 1) return GDN2_ERR_SHAPE;
+    if (!chunk_supported(dk, dv, dtype)) return GDN2_ERR_UNSUPPORTED;
+    // sizes: kernels index rows with 32-bit B, T, H and 64-bit element offsets
+    int64_t BT, BTH, nk, nv, ns;
+    if (B > INT_MAX || T > INT_MAX || H > INT_MAX) return GDN2_ERR_SHAPE;
+    if (!mul_ok(B, T, &BT) || !mul_ok(BT, H, &BTH) || !mul_ok(BTH, dk, &nk) || !mul_ok(BTH, dv, &nv))
+        return GDN2_ERR_SHAPE;
+    if (!mul_ok(B * H, dk * dv, &ns)) return GDN2_ERR_SHAPE;
+    if (B * H * (dv / 16) > UINT_MAX / 2) return GDN2_ERR_SHAPE;
+    const void* ptrs[] = {q, k, v, log_alpha, b, w, initial_state, o, final_state};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDN2_ERR_MISALIGNED;
+    const int64_t es = dtype == GDN2_DTYPE_BF16 ? 2 : 4;
+    const int64_t eo = o_dtype == GDN2_DTYPE_BF16 ? 2 : 4;
+    const Range in_ranges[] = {range_of(q, nk * es), range_of(k, nk * es), range_of(v, nv * es),
+                               range_of(log_alpha, nk * 4), range_of(b, nk * es),
+                               range_of(w, nv * es)};
+    const Range ro = range_of(o, nv * eo);
+    for (const Range& r : in_ranges)
+        if (overlap(ro, r)) return GDN2_ERR_ALIAS;
+    if (initial_state && overlap(ro, range_of(initial_state, ns * 4))) return GDN2_ERR_ALIAS;
+    if (final_state) {
+        const Range rf = range_of(final_state, ns * 4);
+        for (const Range& r : in_ranges)
+            if (overlap(rf, r)) return GDN2_ERR_ALIAS;
+        if (overlap(rf, ro)) return GDN2_ERR_ALIAS;
+        if (initial_state && initial_state != final_state && overlap(rf, range_of(initial_state, ns * 4)))
+            return GDN2_ERR_ALIAS;
+    }
+    const int cus = device_cus();
+    if (cus <= 0) return GDN2_ERR_HIP;
+    gdn2::ChunkArgs a{q, k, v, log_alpha, b, w, initial_state, o, final_state, B, T, H, dk, dv,
+                      dtype == GDN2_DTYPE_BF16, o_dtype == GDN2_DTYPE_F32, stream};
+    const int dvs = choose_dvs(B * H, dv, cus);
+    return gdn2::launch_chunk_fwd(a, dvs) == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
+gdn2_status_t gdn2_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
+                               const void* b, const void* w, float* state, void* o, int64_t N,
+                               int64_t H, int64_t dk, int64_t dv, gdn2_dtype_t dtype,
+                               gdn2_dtype_t o_dtype, void* stream) {
+    if (!q || !k || !v || !log_alpha || !b || !w || !state || !o) return GDN2_ERR_NULL;
+    if (dtype != GDN2_DTYPE_F32 && dtype != GDN2_DTYPE_BF16) return GDN2_ERR_UNSUPPORTED;
+    if (o_dtype != GDN2_DTYPE_F32 && o_dtype != dtype) return GDN2_ERR_UNSUPPORTED;
+    if (N < 1 || H < 1 || dk < 1 || dv < 1) return GDN2_ERR_SHAPE;
+    if (!decode_supported(dk, dv, dtype)) return GDN2_ERR_UNSUPPORTED;
+    int64_t NH, nk, nv, ns;
+    if (!mul_ok(N, H, &NH) || !mul_ok(NH, dk, &nk) || !mul_ok(NH, dv, &nv) || !mul_ok(NH, dk * dv, &ns))
+        return GDN2_ERR_SHAPE;
+    if (NH > UINT_MAX / 2) return GDN2_ERR_SHAPE;
+    const void* ptrs[] = {q, k, v, log_alpha, b, w, state, o};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return GDN2_ERR_MISALIGNED;
+    const int64_t es = dtype == GDN2_DTYPE_BF16 ? 2 : 4;
+    const Range in_ranges[] = {range_of(q, nk * es), range_of(k, nk * es), range_of(v, nv * es),
+                               range_of(log_alpha, nk * 4), range_of(b, nk * es),
+                               range_of(w, nv * es)};
+    const int64_t eo = o_dtype == GDN2_DTYPE_BF16 ? 2 : 4;
+    const Range ro = range_of(o, nv * eo), rs = range_of(state, ns * 4);
+    for (const Range& r : in_ranges)
+        if (overlap(ro, r) || overlap(rs, r)) return GDN2_ERR_ALIAS;
+    if (overlap(ro, rs)) return GDN2_ERR_ALIAS;
+    gdn2::DecodeArgs a{q, k, v, log_alpha, b, w, state, o, N, H, dk, dv, dtype == GDN2_DTYPE_BF16,
+                       o_dtype == GDN2_DTYPE_F32, stream};
+    return gdn2::launch_decode_step(a) == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
+int gdn2_supported(int which, int64_t dk, int64_t dv, gdn2_dtype_t dtype) {
+    if (which == 0) return chunk_supported(dk, dv, dtype) ? 1 : 0;
+    if (which == 1) return decode_supported(dk, dv, dtype) ? 1 : 0;
+    return 0;
+}
+
+const char* gdn2_status_string(gdn2_status_t s) {
+    switch (s) {
+        case GDN2_OK: return "ok";
+        case GDN2_ERR_NULL: return "a required pointer is NULL";
+        case GDN2_ERR_SHAPE: return "a size is out of range";
+        case GDN2_ERR_UNSUPPORTED: return "(dk, dv, dtype) is not supported";
+        case GDN2_ERR_MISALIGNED: return "a tensor pointer is not 16-byte aligned";
+        case GDN2_ERR_ALIAS: return "an output overlaps an input";
+        case GDN2_ERR_HIP: return "the HIP runtime rejected the call";
+    }
+    return "unknown status";
+}
+
+const char* gdn2_version(void) { return "gdn2-gfx950 0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,701 @@
+// gdn2_chunk_fwd.hip -- chunk-parallel forward of the GDN-2 recurrence on gfx950.
+//
+// Method (page "Why NVIDIA Gated DeltaNet-2 separates erase and write gates",
+// axbrief.com, section "Gated Delta Rule-2", recurrence equation, chunk size 64):
+//
+//   S_t = (I - k_t (b_t.k_t)^T) Diag(alpha_t) S_{t-1} + k_t (w_t.v_t)^T,  o_t = S_t^T q_t.
+//
+// Within a chunk of C = 64 tokens (local index i, j) write G_i = sum_{s<=i} g_s
+// (g = log alpha, chunk-local, per key channel) and Gamma_{i<-j} = e^{G_i - G_j}.
+// Unrolling the recurrence over the chunk gives, with S the state entering it,
+//
+//   A[i,j] = sum_c (b.k)_ic Gamma_{i<-j,c} k_jc  (j < i),   T = (I + A)^{-1}
+//   P[i,j] = sum_c  q_ic    Gamma_{i<-j,c} k_jc  (j <= i)
+//   U      = T (w.v) - W S,   W = T ((b.k).Gamma)                  (gated residuals)
+//   O      = (q.Gamma) S + P U
+//   S_next = Diag(Gamma_C) S + (k.Gamma')^T U,   Gamma_i = e^{G_i}, Gamma'_j = e^{G_63 - G_j}.
+//
+// This is the representation of a block of rank-1 updates as matrix products
+// (page "Why Qwen3.5 chose Gated DeltaNet", laonpeople.com, section on the WY
+// representation turning sequential updates into GEMMs); A is asymmetric
+// because the erase reads with b.k but writes along k.
+//
+// Decay factors are never formed by dividing by a cumulative product that can
+// underflow (page "Muir ...", molayo1419.me, item 3: decays pivoted at
+// boundaries stay in (0, 1]).  Two variants, chosen per chunk:
+//   * mild chunk (every channel's whole-chunk decay Gamma_C >= 2^-64): one pivot
+//     at the chunk start; the column factor 1/Gamma_j <= 2^64 is finite, so A
+//     and P are single MFMA products of (b.k.Gamma), (q.Gamma) with k/Gamma.
+//   * strong chunk: the chunk is split recursively at midpoints (64, 32, 16,
+//     8, 4, 2 tokens).  Every pair j < i straddles exactly one split point p,
+//     and Gamma_{i<-j} = Gamma_{i<-p} Gamma_{p<-j} with both factors <= 1, so
+//     each level is one masked MFMA pass whose operands never overflow; the
+//     diagonal of P is a last, unscaled pass.  Nothing is clamped.
+//
+// Precision of the bf16 path: inputs are bf16, every product accumulates in
+// fp32, the state stays fp32.  Operands that are not bf16 values themselves
+// (w.v, the residuals U and the matrix P) enter the MFMAs as a hi + lo pair
+// of bf16 numbers (about 16 mantissa bits); o can be written in fp32.
+//
+// Work decomposition: one workgroup (256 threads, 4 waves) per (sequence b,
+// head h, slice of DVS value columns); the columns of S are independent, so
+// slices never talk to each other.  Each workgroup walks the chunks in order,
+// keeps its fp32 state slice in MFMA accumulators for the whole sequence and
+// recomputes the key-side quantities (A, P, T, W) itself.
+#include "gdn2_device.h"
+#include "gdn2_launch.h"
+
+namespace gdn2 {
+
+template <typename T, int DK, int DVS>
+struct ChunkCfg {
+    static constexpr int C = 64;
+    static constexpr int NT = 256;                 // threads per workgroup
+    static constexpr int CPT = DK / 64;            // key channels per thread in the element phase
+    static constexpr int NCT = DVS / 16;           // 16-wide value column tiles per slice
+    static constexpr bool SPLIT = sizeof(T) == 2;  // hi/lo operand pairs for the bf16 path
+    static constexpr int NS = SPLIT ? 2 : 1;
+    static constexpr int ES = (int)sizeof(T);
+    static constexpr int PAD = 16 / ES;
+    static constexpr int LDK = DK + PAD;           // row stride of [64][DK] tiles (elements)
+    static constexpr int LC = C + PAD;             // row stride of [*][64] tiles (elements)
+    static constexpr int LA = C + 4;               // row stride of fp32 [64][64] tiles
+    // persistent regions (byte offsets)
+    static constexpr int QG = 0;                                    // [64][LDK] q.Gamma
+    static constexpr int BGT_BYTES = (DK * LC > C * LDK ? DK * LC : C * LDK) * ES;
+    static constexpr int BGT = QG + C * LDK * ES;                   // [DK][LC] (b.k.Gamma)^T, then W [64][LDK]
+    static constexpr int KGT = BGT + BGT_BYTES;                     // [DK][LC] (k.Gamma')^T
+    static constexpr int PM = KGT + DK * LC * ES;                   // NS x [64][LC] P (hi, lo)
+    static constexpr int A32 = PM + NS * C * LC * ES;               // [64][LA] fp32 A
+    static constexpr int WORK = A32 + C * LA * 4;                   // time-shared work area
+    // work area, element/A-P phase: fast -> BG, KI rows; strong -> 12 groups of 16 rows
+    static constexpr int W_AP = 192 * LDK * ES;
+    // work area, solve phase: T fp32, T operand, (w.v)^T hi/lo
+    static constexpr int T32 = WORK;
+    static constexpr int TOP = T32 + C * LA * 4;
+    static constexpr int WVT = TOP + C * LC * ES;
+    static constexpr int W_T = C * LA * 4 + C * LC * ES + NS * DVS * LC * ES;
+    static constexpr int WORK_BYTES = W_AP > W_T ? W_AP : W_T;
+    static constexpr int GC = WORK + WORK_BYTES;                    // [DK] fp32 Gamma_C
+    static constexpr int BLK = GC + DK * 4;                         // [4][DK] fp32 block decays
+    static constexpr int BYTES = BLK + 4 * DK * 4;
+    static_assert(BYTES <= 163840, "LDS budget exceeded");
+    static_assert(DK % 64 == 0 && DVS % 16 == 0 && DVS <= 64, "shape");
+};
+
+__device__ __forceinline__ void split_bf16(float x, bf16& hi, bf16& lo) {
+    hi = (bf16)x;
+    lo = (bf16)(x - (float)hi);
+}
+
+// hi / lo B-fragments from an accumulator pair (contraction rows [0,16) and [16,32))
+template <typename T> struct SplitFrag { Frag<T> hi, lo; };
+template <typename T> __device__ __forceinline__ SplitFrag<T> split_from_acc(const f32x4& a, const f32x4& b);
+template <> __device__ __forceinline__ SplitFrag<bf16> split_from_acc<bf16>(const f32x4& a, const f32x4& b) {
+    SplitFrag<bf16> f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        bf16 h, l;
+        split_bf16(a[e], h, l); f.hi.v[e] = h; f.lo.v[e] = l;
+        split_bf16(b[e], h, l); f.hi.v[e + 4] = h; f.lo.v[e + 4] = l;
+    }
+    return f;
+}
+template <> __device__ __forceinline__ SplitFrag<float> split_from_acc<float>(const f32x4& a, const f32x4& b) {
+    SplitFrag<float> f;
+    f.hi = frag_from_acc<float>(a, b);
+    return f;
+}
+
+template <typename T>
+__device__ __forceinline__ void store_split(T* hi, T* lo, float x);
+template <> __device__ __forceinline__ void store_split<bf16>(bf16* hi, bf16* lo, float x) {
+    bf16 h, l;
+    split_bf16(x, h, l);
+    *hi = h;
+    *lo = l;
+}
+template <> __device__ __forceinline__ void store_split<float>(float* hi, float*, float x) { *hi = x; }
+
+template <typename T, typename OutT, int DK, int DV, int DVS>
+__global__ __launch_bounds__(256) void chunk_fwd_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ log_alpha, const T* __restrict__ bgate, const T* __restrict__ wgate,
+    const float* initial_state, OutT* __restrict__ o, float* final_state, int B, int Tlen, int H,
+    int nslices, int xcd_map) {
+    using Cfg = ChunkCfg<T, DK, DVS>;
+    constexpr int C = Cfg::C, CPT = Cfg::CPT, NCT = Cfg::NCT;
+    constexpr int LDK = Cfg::LDK, LC = Cfg::LC, LA = Cfg::LA;
+    constexpr bool SPLIT = Cfg::SPLIT;
+    __shared__ __attribute__((aligned(16))) char smem[Cfg::BYTES];
+    T* sQG = reinterpret_cast<T*>(smem + Cfg::QG);
+    T* sBGT = reinterpret_cast<T*>(smem + Cfg::BGT);
+    T* sW = sBGT;  // W = T (b.k.Gamma) replaces (b.k.Gamma)^T once that is consumed
+    T* sKGT = reinterpret_cast<T*>(smem + Cfg::KGT);
+    T* sPh = reinterpret_cast<T*>(smem + Cfg::PM);
+    T* sPl = sPh + C * LC;  // only used with SPLIT
+    float* sA = reinterpret_cast<float*>(smem + Cfg::A32);
+    T* sWork = reinterpret_cast<T*>(smem + Cfg::WORK);
+    float* sT32 = reinterpret_cast<float*>(smem + Cfg::T32);
+    T* sTop = reinterpret_cast<T*>(smem + Cfg::TOP);
+    T* sWVh = reinterpret_cast<T*>(smem + Cfg::WVT);
+    T* sWVl = sWVh + DVS * LC;  // only used with SPLIT
+    float* sGC = reinterpret_cast<float*>(smem + Cfg::GC);
+    float* sBLK = reinterpret_cast<float*>(smem + Cfg::BLK);
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int l16 = lane & 15;
+    const int g4 = lane >> 4;
+
+    // workgroup -> (sequence, head, slice); slices of one (b, h) share an XCD
+    int bh, slice;
+    {
+        const int id = blockIdx.x;
+        if (xcd_map) {
+            const int kk = id >> 3;
+            bh = 8 * (kk / nslices) + (id & 7);
+            slice = kk % nslices;
+        } else {
+            bh = id / nslices;
+            slice = id % nslices;
+        }
+    }
+    const int bi = bh / H, h = bh % H;
+    const int col0 = slice * DVS;  // first value column of this slice
+
+    // upper blocks of A and P are never written below: clear once
+    for (int x = tid; x < C * LA; x += Cfg::NT) sA[x] = 0.f;
+    for (int x = tid; x < Cfg::NS * C * LC; x += Cfg::NT) sPh[x] = from_f32<T>(0.f);
+
+    // ---- state slice in accumulators: wave w owns column tiles w, w+4, ... ----
+    constexpr int TPW = NCT >= 4 ? NCT / 4 : 1;  // column tiles per owning wave
+    const bool owner = (NCT >= 4) || (wave < NCT);
+    f32x4 S[TPW][DK / 16];
+#pragma unroll
+    for (int a = 0; a < TPW; ++a)
+#pragma unroll
+        for (int st = 0; st < DK / 16; ++st) S[a][st] = zero4();
+    if (owner && initial_state) {
+#pragma unroll
+        for (int a = 0; a < TPW; ++a) {
+            const int ct = wave + 4 * a;
+            const float* src = initial_state + ((int64_t)bh * DK) * DV + col0 + ct * 16 + l16;
+#pragma unroll
+            for (int st = 0; st < DK / 16; ++st)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) S[a][st][r] = src[(int64_t)(st * 16 + g4 * 4 + r) * DV];
+        }
+    }
+    __syncthreads();
+
+    const int nchunks = (Tlen + C - 1) / C;
+    const int64_t tok_stride_k = (int64_t)H * DK;  // elements between consecutive tokens
+    const int64_t tok_stride_v = (int64_t)H * DV;
+    const int64_t seq_base_k = ((int64_t)bi * Tlen * H + h) * DK;
+    const int64_t seq_base_v = ((int64_t)bi * Tlen * H + h) * DV;
+    const int I = wave;             // 16-token block of this thread in the element phase
+    const int cbase = lane * CPT;   // first key channel of this thread in the element phase
+    constexpr int TPT = C * DVS / Cfg::NT;  // tokens per thread for w.v
+    const int cv = tid % DVS, tg = tid / DVS;
+
+    for (int n = 0; n < nchunks; ++n) {
+        const int t0 = n * C;
+        // =============== element phase, pass 1: per-channel decays ===============
+        float al[CPT][16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int t = t0 + I * 16 + i;
+            const int64_t off = seq_base_k + (int64_t)t * tok_stride_k + cbase;
+#pragma unroll
+            for (int cc = 0; cc < CPT; ++cc) al[cc][i] = exp_neg(t < Tlen ? log_alpha[off + cc] : 0.f);
+        }
+#pragma unroll
+        for (int cc = 0; cc < CPT; ++cc) {
+            float p = 1.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) p *= al[cc][i];
+            sBLK[I * DK + cbase + cc] = p;
+        }
+        // write gate times value for this thread's (column, tokens): kept in registers
+        float wv[TPT];
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) {
+            const int t = t0 + tg * TPT + i;
+            float x = 0.f;
+            if (t < Tlen) {
+                const int64_t off = seq_base_v + (int64_t)t * tok_stride_v + col0 + cv;
+                x = to_f32(wgate[off]) * to_f32(v[off]);
+            }
+            wv[i] = x;
+        }
+        __syncthreads();
+        float blk[CPT][4];
+        int strong = 0;
+#pragma unroll
+        for (int cc = 0; cc < CPT; ++cc) {
+#pragma unroll
+            for (int K = 0; K < 4; ++K) blk[cc][K] = sBLK[K * DK + cbase + cc];
+            const float gc = blk[cc][0] * blk[cc][1] * blk[cc][2] * blk[cc][3];
+            if (I == 0) sGC[cbase + cc] = gc;
+            strong |= !(gc >= 0x1p-64f);
+        }
+        strong = __syncthreads_or(strong);
+
+        // =============== element phase, pass 2: scaled operands ===============
+#pragma unroll
+        for (int cc = 0; cc < CPT; ++cc) {
+            const int c = cbase + cc;
+            float qv[16], kv[16], bk[16], pre[16], suf[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int t = t0 + I * 16 + i;
+                const int64_t off = seq_base_k + (int64_t)t * tok_stride_k + c;
+                const bool valid = t < Tlen;
+                qv[i] = valid ? to_f32(q[off]) : 0.f;
+                kv[i] = valid ? to_f32(k[off]) : 0.f;
+                bk[i] = valid ? to_f32(bgate[off]) * kv[i] : 0.f;
+            }
+            {
+                float p = 1.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) { p *= al[cc][i]; pre[i] = p; }
+                float s = 1.f;
+#pragma unroll
+                for (int i = 15; i >= 0; --i) { suf[i] = s; s *= al[cc][i]; }
+            }
+            float before = 1.f, after = 1.f;  // whole blocks before / after block I
+#pragma unroll
+            for (int K = 0; K < 4; ++K) {
+                if (K < I) before *= blk[cc][K];
+                if (K > I) after *= blk[cc][K];
+            }
+            T bgt[16], kgt[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int tl = I * 16 + i;
+                const float gam = before * pre[i];   // Gamma_i  (chunk start -> i)
+                const float gamr = suf[i] * after;   // Gamma'_i (i -> chunk end)
+                sQG[tl * LDK + c] = from_f32<T>(qv[i] * gam);
+                bgt[i] = from_f32<T>(bk[i] * gam);
+                kgt[i] = from_f32<T>(kv[i] * gamr);
+                if (!strong) {
+                    sWork[tl * LDK + c] = bgt[i];                                                   // BG
+                    sWork[(64 + tl) * LDK + c] = from_f32<T>(kv[i] * __builtin_amdgcn_rcpf(gam));  // KI
+                } else {
+                    // recursive split at the chunk level: groups of 16 rows in the work area
+                    //  level 64 (pivot 31): rows of blocks 2,3 (A: g0,g1; P: g2,g3), columns of blocks 0,1 (g4,g5)
+                    //  level 32 (pivots 15, 47): rows of blocks 1,3 (A: g6,g7; P: g8,g9), columns of blocks 0,2 (g10,g11)
+                    T* wk = sWork + i * LDK + c;
+                    if (I >= 2) {
+                        const float f = I == 3 ? blk[cc][2] * pre[i] : pre[i];
+                        wk[(I - 2) * 16 * LDK] = from_f32<T>(bk[i] * f);
+                        wk[(2 + I - 2) * 16 * LDK] = from_f32<T>(qv[i] * f);
+                    } else {
+                        const float f = I == 0 ? suf[i] * blk[cc][1] : suf[i];
+                        wk[(4 + I) * 16 * LDK] = from_f32<T>(kv[i] * f);
+                    }
+                    if (I & 1) {
+                        wk[(6 + I / 2) * 16 * LDK] = from_f32<T>(bk[i] * pre[i]);
+                        wk[(8 + I / 2) * 16 * LDK] = from_f32<T>(qv[i] * pre[i]);
+                    } else {
+                        wk[(10 + I / 2) * 16 * LDK] = from_f32<T>(kv[i] * suf[i]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                sBGT[c * LC + I * 16 + i] = bgt[i];
+                sKGT[c * LC + I * 16 + i] = kgt[i];
+            }
+        }
+        __syncthreads();
+
+        // =============== A and P ===============
+        // accumulators of up to two 16x16 block pairs per wave, stored after a barrier
+        if (!strong) {
+            // single pivot at the chunk start: A = BG KI^T, P = QG KI^T on the lower blocks
+#pragma unroll
+            for (int pi = 0; pi < 3; ++pi) {
+                const int p = wave + 4 * pi;
+                if (p < 10) {
+                    // pair list (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
+                    const int Ib = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
+                    const int Jb = p - (Ib * (Ib + 1)) / 2;
+                    f32x4 accA = zero4(), accP = zero4();
+#pragma unroll
+                    for (int kk = 0; kk < DK / 32; ++kk) {
+                        const int kc = kk * 32 + g4 * 8;
+                        Frag<T> fb = load_contig(sWork + (64 + Jb * 16 + l16) * LDK + kc);
+                        Frag<T> fa = load_contig(sWork + (Ib * 16 + l16) * LDK + kc);
+                        Frag<T> fq = load_contig(sQG + (Ib * 16 + l16) * LDK + kc);
+                        mma(accA, fa, fb);
+                        mma(accP, fq, fb);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = g4 * 4 + r, j = l16;
+                        const bool lowA = Ib > Jb || i > j;
+                        const bool lowP = Ib > Jb || i >= j;
+                        sA[(Ib * 16 + i) * LA + Jb * 16 + j] = lowA ? accA[r] : 0.f;
+                        const int pidx = (Ib * 16 + i) * LC + Jb * 16 + j;
+                        store_split<T>(sPh + pidx, sPl + pidx, lowP ? accP[r] : 0.f);
+                    }
+                }
+            }
+        } else {
+            // ---- strong decay: level 64 (pairs (2,0) (2,1) (3,0) (3,1)) and level 32 ((1,0) (3,2)) ----
+            // wave 0: (2,0) (1,0); wave 1: (2,1) (3,2); wave 2: (3,0); wave 3: (3,1)
+#pragma unroll
+            for (int pi = 0; pi < 2; ++pi) {
+                int Ib = -1, Jb = -1, ga = 0, gp = 0, gcol = 0;
+                if (pi == 0) {
+                    Ib = wave < 2 ? 2 : 3;
+                    Jb = wave & 1;
+                    ga = Ib - 2; gp = 2 + Ib - 2; gcol = 4 + Jb;
+                } else if (wave < 2) {
+                    Ib = wave == 0 ? 1 : 3;
+                    Jb = Ib - 1;
+                    ga = 6 + Ib / 2; gp = 8 + Ib / 2; gcol = 10 + Jb / 2;
+                }
+                if (Ib >= 0) {
+                    f32x4 accA = zero4(), accP = zero4();
+#pragma unroll
+                    for (int kk = 0; kk < DK / 32; ++kk) {
+                        const int kc = kk * 32 + g4 * 8;
+                        Frag<T> fb = load_contig(sWork + (gcol * 16 + l16) * LDK + kc);
+                        Frag<T> fa = load_contig(sWork + (ga * 16 + l16) * LDK + kc);
+                        Frag<T> fq = load_contig(sWork + (gp * 16 + l16) * LDK + kc);
+                        mma(accA, fa, fb);
+                        mma(accP, fq, fb);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = g4 * 4 + r;
+                        sA[(Ib * 16 + i) * LA + Jb * 16 + l16] = accA[r];
+                        const int pidx = (Ib * 16 + i) * LC + Jb * 16 + l16;
+                        store_split<T>(sPh + pidx, sPl + pidx, accP[r]);
+                    }
+                }
+            }
+            __syncthreads();
+            // ---- levels 16, 8, 4, 2 inside the diagonal block I = wave, then P's diagonal ----
+            float qv[CPT][16], kv[CPT][16], bk[CPT][16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int t = t0 + I * 16 + i;
+                const int64_t off = seq_base_k + (int64_t)t * tok_stride_k + cbase;
+                const bool valid = t < Tlen;
+#pragma unroll
+                for (int cc = 0; cc < CPT; ++cc) {
+                    qv[cc][i] = valid ? to_f32(q[off + cc]) : 0.f;
+                    kv[cc][i] = valid ? to_f32(k[off + cc]) : 0.f;
+                    bk[cc][i] = valid ? to_f32(bgate[off + cc]) * kv[cc][i] : 0.f;
+                }
+            }
+            T* lv = sWork + (wave * 48) * LDK;  // rows: [0,16) A rows, [16,32) P rows, [32,48) columns
+            f32x4 dA = zero4(), dP = zero4();
+#pragma unroll
+            for (int L = 0; L < 5; ++L) {
+                const int size = L < 4 ? (16 >> L) : 1;
+#pragma unroll
+                for (int cc = 0; cc < CPT; ++cc) {
+                    const int c = cbase + cc;
+                    float rf[16], cf[16];
+                    // row factor Gamma_{i<-p} for i in the upper half of its segment,
+                    // column factor Gamma_{p<-j} for j in the lower half (p = last of lower half)
+                    if (L < 4) {
+#pragma unroll
+                        for (int s0 = 0; s0 < 16; s0 += size) {
+                            const int p = s0 + size / 2 - 1;
+                            float f = 1.f;
+#pragma unroll
+                            for (int i = p + 1; i < s0 + size; ++i) { f *= al[cc][i]; rf[i] = f; }
+                            float gcl = 1.f;
+#pragma unroll
+                            for (int i = p; i >= s0; --i) { cf[i] = gcl; gcl *= al[cc][i]; }
+                        }
+                    }
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        float ra, rp, cl;
+                        if (L == 4) {
+                            ra = 0.f; rp = qv[cc][i]; cl = kv[cc][i];
+                        } else {
+                            const int p = (i / size) * size + size / 2 - 1;
+                            const bool row = i > p;
+                            ra = row ? bk[cc][i] * rf[i] : 0.f;
+                            rp = row ? qv[cc][i] * rf[i] : 0.f;
+                            cl = row ? 0.f : kv[cc][i] * cf[i];
+                        }
+                        lv[i * LDK + c] = from_f32<T>(ra);
+                        lv[(16 + i) * LDK + c] = from_f32<T>(rp);
+                        lv[(32 + i) * LDK + c] = from_f32<T>(cl);
+                    }
+                }
+                __syncthreads();
+                f32x4 tA = zero4(), tP = zero4();
+#pragma unroll
+                for (int kk = 0; kk < DK / 32; ++kk) {
+                    const int kc = kk * 32 + g4 * 8;
+                    Frag<T> fb = load_contig(lv + (32 + l16) * LDK + kc);
+                    Frag<T> fq = load_contig(lv + (16 + l16) * LDK + kc);
+                    mma(tP, fq, fb);
+                    if (L < 4) {
+                        Frag<T> fa = load_contig(lv + l16 * LDK + kc);
+                        mma(tA, fa, fb);
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = g4 * 4 + r, j = l16;
+                    const bool keep = L < 4 ? (i / size == j / size) : (i == j);
+                    if (keep) { dA[r] += tA[r]; dP[r] += tP[r]; }
+                }
+                __syncthreads();
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = g4 * 4 + r;
+                sA[(wave * 16 + i) * LA + wave * 16 + l16] = dA[r];
+                const int pidx = (wave * 16 + i) * LC + wave * 16 + l16;
+                store_split<T>(sPh + pidx, sPl + pidx, dP[r]);
+            }
+        }
+        __syncthreads();
+
+        // =============== T = (I + A)^{-1}, unit lower triangular ===============
+        // (w.v)^T into the work area now that the A/P operands are consumed
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) {
+            const int idx = cv * LC + tg * TPT + i;
+            store_split<T>(sWVh + idx, sWVl + idx, wv[i]);
+        }
+        // diagonal 16x16 blocks by forward substitution: wave I, lane j < 16 owns column j
+        if (lane < 16) {
+            const int j = lane;
+            const float* Ab = sA + (wave * 16) * LA + wave * 16;
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float acc = (i == j) ? 1.f : 0.f;
+#pragma unroll
+                for (int m = 0; m < i; ++m) acc -= Ab[i * LA + m] * x[m];
+                x[i] = (i < j) ? 0.f : acc;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                sT32[(wave * 16 + i) * LA + wave * 16 + j] = x[i];
+                sTop[(wave * 16 + i) * LC + wave * 16 + j] = from_f32<T>(x[i]);
+            }
+        }
+        // clear the operand copy above the diagonal blocks (rows of block I, columns past block I)
+        for (int x = lane; x < 16 * 64; x += 64) {
+            const int i = x >> 6, cidx = x & 63;
+            if (cidx >= (wave + 1) * 16) sTop[(wave * 16 + i) * LC + cidx] = from_f32<T>(0.f);
+        }
+        __syncthreads();
+        // off-diagonal blocks by sub-diagonal: T_IJ = -T_II * sum_{K=J}^{I-1} A_IK T_KJ
+#pragma unroll
+        for (int d = 1; d < 4; ++d) {
+            if (wave < 4 - d) {
+                const int Jb = wave, Ib = wave + d;
+                f32x4 z = zero4();
+                for (int Kb = Jb; Kb < Ib; ++Kb) {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const float a = sA[(Ib * 16 + l16) * LA + Kb * 16 + 4 * s + g4];
+                        const float b = sT32[(Kb * 16 + 4 * s + g4) * LA + Jb * 16 + l16];
+                        mma_f32x4(z, a, b);
+                    }
+                }
+                f32x4 tij = zero4();
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    // slot g of step s carries row 4g+s of z, held by this lane in z[s]
+                    const float a = sT32[(Ib * 16 + l16) * LA + Ib * 16 + 4 * g4 + s];
+                    mma_f32x4(tij, a, z[s]);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = Ib * 16 + g4 * 4 + r, colx = Jb * 16 + l16;
+                    sT32[row * LA + colx] = -tij[r];
+                    sTop[row * LC + colx] = from_f32<T>(-tij[r]);
+                }
+            }
+            __syncthreads();
+        }
+
+        // =============== W = T (b.k.Gamma), U0 = T (w.v) ===============
+        constexpr int WCT = DK / 16 / 4;  // W column tiles per wave
+        f32x4 Wacc[WCT][4];
+#pragma unroll
+        for (int a = 0; a < WCT; ++a) {
+            const int ct = wave + 4 * a;
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                Wacc[a][rt] = zero4();
+#pragma unroll
+                for (int kk = 0; kk <= rt / 2; ++kk) {
+                    const int kc = kk * 32 + g4 * 8;
+                    Frag<T> fa = load_contig(sTop + (rt * 16 + l16) * LC + kc);
+                    Frag<T> fb = load_contig(sBGT + (ct * 16 + l16) * LC + kc);
+                    mma(Wacc[a][rt], fa, fb);
+                }
+            }
+        }
+        f32x4 U[TPW][4];
+        if (owner) {
+#pragma unroll
+            for (int a = 0; a < TPW; ++a) {
+                const int ct = wave + 4 * a;
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    U[a][rt] = zero4();
+#pragma unroll
+                    for (int kk = 0; kk <= rt / 2; ++kk) {
+                        const int kc = kk * 32 + g4 * 8;
+                        Frag<T> fa = load_contig(sTop + (rt * 16 + l16) * LC + kc);
+                        Frag<T> fb = load_contig(sWVh + (ct * 16 + l16) * LC + kc);
+                        mma(U[a][rt], fa, fb);
+                        if constexpr (SPLIT) {
+                            Frag<T> fl = load_contig(sWVl + (ct * 16 + l16) * LC + kc);
+                            mma(U[a][rt], fa, fl);
+                        }
+                    }
+                }
+            }
+        }
+        __syncthreads();  // every read of (b.k.Gamma)^T is done
+#pragma unroll
+        for (int a = 0; a < WCT; ++a) {
+            const int ct = wave + 4 * a;
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sW[(rt * 16 + g4 * 4 + r) * LDK + ct * 16 + l16] = from_f32<T>(Wacc[a][rt][r]);
+        }
+        __syncthreads();
+
+        // =============== state pass ===============
+        if (owner) {
+            float gc[DK / 16][4];
+#pragma unroll
+            for (int st = 0; st < DK / 16; ++st) {
+                f32x4 x4 = *reinterpret_cast<const f32x4*>(sGC + st * 16 + g4 * 4);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) gc[st][r] = x4[r];
+            }
+#pragma unroll
+            for (int a = 0; a < TPW; ++a) {
+                const int ct = wave + 4 * a;
+                Frag<T> sf[DK / 32];
+#pragma unroll
+                for (int kk = 0; kk < DK / 32; ++kk) sf[kk] = frag_from_acc<T>(S[a][2 * kk], S[a][2 * kk + 1]);
+                f32x4 X[4], Y[4];
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) { X[rt] = zero4(); Y[rt] = zero4(); }
+#pragma unroll
+                for (int kk = 0; kk < DK / 32; ++kk) {
+                    const int kc = kk * 32 + g4 * 4;
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt) {
+                        Frag<T> fw = load_perm(sW + (rt * 16 + l16) * LDK + kc);
+                        Frag<T> fq = load_perm(sQG + (rt * 16 + l16) * LDK + kc);
+                        mma(X[rt], fw, sf[kk]);
+                        mma(Y[rt], fq, sf[kk]);
+                    }
+                }
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) U[a][rt] -= X[rt];
+                SplitFrag<T> uf[2];
+                uf[0] = split_from_acc<T>(U[a][0], U[a][1]);
+                uf[1] = split_from_acc<T>(U[a][2], U[a][3]);
+                // O = (q.Gamma) S + P U
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+                    for (int kk = 0; kk <= rt / 2; ++kk) {
+                        const int pofs = (rt * 16 + l16) * LC + kk * 32 + g4 * 4;
+                        Frag<T> fp = load_perm(sPh + pofs);
+                        mma(Y[rt], fp, uf[kk].hi);
+                        if constexpr (SPLIT) {
+                            mma(Y[rt], fp, uf[kk].lo);
+                            Frag<T> fpl = load_perm(sPl + pofs);
+                            mma(Y[rt], fpl, uf[kk].hi);
+                        }
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = t0 + rt * 16 + g4 * 4 + r;
+                        if (t < Tlen)
+                            o[seq_base_v + (int64_t)t * tok_stride_v + col0 + ct * 16 + l16] =
+                                from_f32<OutT>(Y[rt][r]);
+                    }
+                }
+                // S <- Diag(Gamma_C) S + (k.Gamma')^T U
+#pragma unroll
+                for (int st = 0; st < DK / 16; ++st) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) S[a][st][r] *= gc[st][r];
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        Frag<T> fk = load_perm(sKGT + (st * 16 + l16) * LC + kk * 32 + g4 * 4);
+                        mma(S[a][st], fk, uf[kk].hi);
+                        if constexpr (SPLIT) mma(S[a][st], fk, uf[kk].lo);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    if (owner && final_state) {
+#pragma unroll
+        for (int a = 0; a < TPW; ++a) {
+            const int ct = wave + 4 * a;
+            float* dst = final_state + ((int64_t)bh * DK) * DV + col0 + ct * 16 + l16;
+#pragma unroll
+            for (int st = 0; st < DK / 16; ++st)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dst[(int64_t)(st * 16 + g4 * 4 + r) * DV] = S[a][st][r];
+        }
+    }
+}
+
+template <typename T, typename OutT, int DK, int DV, int DVS>
+static hipError_t launch_chunk(const ChunkArgs& a) {
+    const int nslices = DV / DVS;
+    const int64_t groups = (int64_t)a.B * a.H * nslices;
+    const int xcd_map = ((int64_t)a.B * a.H) % 8 == 0 ? 1 : 0;
+    hipLaunchKernelGGL((chunk_fwd_kernel<T, OutT, DK, DV, DVS>), dim3((unsigned)groups), dim3(256), 0,
+                       (hipStream_t)a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.log_alpha,
+                       (const T*)a.b, (const T*)a.w, a.initial_state, (OutT*)a.o, a.final_state, (int)a.B,
+                       (int)a.T, (int)a.H, nslices, xcd_map);
+    return hipGetLastError();
+}
+
+template <typename T, typename OutT, int D>
+static hipError_t launch_dvs(const ChunkArgs& a, int dvs) {
+    switch (dvs) {
+        case 16: return launch_chunk<T, OutT, D, D, 16>(a);
+        case 32: return launch_chunk<T, OutT, D, D, 32>(a);
+        case 64: return launch_chunk<T, OutT, D, D, 64>(a);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_fwd(const ChunkArgs& a, int dvs) {
+    if (a.dk != a.dv) return hipErrorInvalidValue;
+    if (a.dtype_bf16) {
+        if (a.dk == 128) return a.out_f32 ? launch_dvs<bf16, float, 128>(a, dvs) : launch_dvs<bf16, bf16, 128>(a, dvs);
+        if (a.dk == 64) return a.out_f32 ? launch_dvs<bf16, float, 64>(a, dvs) : launch_dvs<bf16, bf16, 64>(a, dvs);
+    } else if (a.dk == 64 && a.out_f32) {
+        return launch_dvs<float, float, 64>(a, dvs);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdn2

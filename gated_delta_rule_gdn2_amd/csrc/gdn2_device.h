@@ -1,0 +1,110 @@
+// gdn2_device.h -- device-side building blocks for the gfx950 (CDNA4) kernels:
+// element types, MFMA fragments, LDS fragment loads and small helpers.
+//
+// MFMA tiles are 16x16 with fp32 accumulators.  A "fragment" holds the 32
+// contraction slots one K-step of a 16x16 output consumes, 8 per lane: lane l
+// covers output row/column (l % 16) and slot group g = l / 16, elements
+// e = 0..7.  For bf16 operands one v_mfma_f32_16x16x32_bf16 consumes the 8
+// elements at once; for fp32 operands eight v_mfma_f32_16x16x4_f32 consume one
+// element each.  Either way the product sums over all 32 (g, e) slots, so the
+// loader may map slots to contraction indices in any order, as long as both
+// operands use the same map.  Two maps are used:
+//   contiguous : slot (g, e) -> 8g + e                    (both operands from LDS)
+//   permuted   : slot (g, e) -> 4g + e (e < 4), 16 + 4g + e - 4 (e >= 4)
+// The permuted map is exactly where a 16x16 fp32 accumulator keeps its rows
+// (lane l holds rows 4g..4g+3 of column l % 16), so an accumulator pair that
+// covers 32 rows is directly a B operand, without a trip through LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn2 {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---- element conversion -------------------------------------------------
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+// ---- fragments ------------------------------------------------------------
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { float v[8]; };
+
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<bf16>& a, const Frag<bf16>& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], acc, 0, 0, 0);
+}
+
+// single fp32 MFMA step (16x16x4) for the small triangular solve
+__device__ __forceinline__ void mma_f32x4(f32x4& acc, float a, float b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+}
+
+// contiguous map: p points at element [row][kbase + 8g]; needs 16-byte alignment
+__device__ __forceinline__ Frag<bf16> load_contig(const bf16* p) {
+    Frag<bf16> f;
+    f.v = *reinterpret_cast<const bf16x8*>(p);
+    return f;
+}
+__device__ __forceinline__ Frag<float> load_contig(const float* p) {
+    Frag<float> f;
+    f32x4 lo = *reinterpret_cast<const f32x4*>(p);
+    f32x4 hi = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { f.v[e] = lo[e]; f.v[e + 4] = hi[e]; }
+    return f;
+}
+
+// permuted map: p points at element [row][kbase + 4g]; needs 8-byte alignment (bf16)
+__device__ __forceinline__ Frag<bf16> load_perm(const bf16* p) {
+    bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
+    bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
+    Frag<bf16> f;
+    f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return f;
+}
+__device__ __forceinline__ Frag<float> load_perm(const float* p) {
+    f32x4 lo = *reinterpret_cast<const f32x4*>(p);
+    f32x4 hi = *reinterpret_cast<const f32x4*>(p + 16);
+    Frag<float> f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { f.v[e] = lo[e]; f.v[e + 4] = hi[e]; }
+    return f;
+}
+
+// B operand from two accumulators covering contraction rows [0,16) and [16,32)
+template <typename T> __device__ __forceinline__ Frag<T> frag_from_acc(const f32x4& lo, const f32x4& hi);
+template <> __device__ __forceinline__ Frag<bf16> frag_from_acc<bf16>(const f32x4& lo, const f32x4& hi) {
+    Frag<bf16> f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { f.v[e] = (bf16)lo[e]; f.v[e + 4] = (bf16)hi[e]; }
+    return f;
+}
+template <> __device__ __forceinline__ Frag<float> frag_from_acc<float>(const f32x4& lo, const f32x4& hi) {
+    Frag<float> f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { f.v[e] = lo[e]; f.v[e + 4] = hi[e]; }
+    return f;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// exp(x) for x <= 0 through the hardware base-2 exponential
+__device__ __forceinline__ float exp_neg(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
+}  // namespace gdn2

@@ -1,0 +1,44 @@
+// gdn2_launch.h -- host-side launch entry points of the kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn2 {
+
+struct ChunkArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* log_alpha;
+    const void* b;
+    const void* w;
+    const float* initial_state;
+    void* o;
+    float* final_state;
+    int64_t B, T, H, dk, dv;
+    bool dtype_bf16;  // inputs q, k, v, b, w are bf16 (else fp32)
+    bool out_f32;     // o is fp32 (else the input dtype)
+    void* stream;
+};
+
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* log_alpha;
+    const void* b;
+    const void* w;
+    float* state;
+    void* o;
+    int64_t N, H, dk, dv;
+    bool dtype_bf16;
+    bool out_f32;
+    void* stream;
+};
+
+// dvs: value columns per workgroup slice (16, 32 or 64)
+hipError_t launch_chunk_fwd(const ChunkArgs& a, int dvs);
+hipError_t launch_decode_step(const DecodeArgs& a);
+
+}  // namespace gdn2

@@ -1,0 +1,126 @@
+/*
+ * gdn2.h -- C ABI of the MI355X (gfx950) Gated DeltaNet-2 recurrence library.
+ *
+ * The operation is the GDN-2 state update of the page "Why NVIDIA Gated
+ * DeltaNet-2 separates erase and write gates" (axbrief.com), section
+ * "Gated Delta Rule-2: channel-wise separation of erase and write", its
+ * recurrence equation:
+ *
+ *     S_t = (I - k_t (b_t . k_t)^T) Diag(alpha_t) S_{t-1} + k_t (w_t . v_t)^T
+ *     o_t = S_t^T q_t                       (read-out after the update)
+ *
+ * S is dk x dv (rows are key channels), alpha_t = exp(log_alpha_t) is a decay
+ * per key channel, b_t in [0,1]^dk is the erase gate (key side) and
+ * w_t in [0,1]^dv the write gate (value side).  There is no query scale.
+ *
+ * Two calls are exported: a chunk-parallel forward over whole sequences (the
+ * same page, section "Gated Delta Rule-2", gives the chunk size of 64 used by
+ * the fused training kernels) and a single-token recurrent decode step (the
+ * page's opening section: decoding keeps a constant-size state).
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers (HIP global memory) of the current
+ *     device, contiguous and row-major in the layouts stated below, and
+ *     16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
+ *     enqueued asynchronously; the caller keeps every buffer alive until the
+ *     stream has passed the call.
+ *   - The library never allocates, frees or synchronises, keeps no reference
+ *     after returning, and has no global mutable state: calls are reentrant.
+ *   - All validation happens before anything is enqueued.  On any error the
+ *     call returns a non-zero status and writes nothing.  A launch rejected by
+ *     the HIP runtime returns GDN2_ERR_HIP.  Faults inside a kernel surface at
+ *     the caller's next synchronisation, as for any HIP kernel.
+ *   - Inputs are not range-checked on the device: log_alpha must be finite and
+ *     <= 0; b and w are expected in [0,1] (values outside are used as given).
+ */
+#ifndef GDN2_H
+#define GDN2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Chunk length of the chunk-parallel forward (tokens per chunk). */
+#define GDN2_CHUNK 64
+
+/* Element type of q, k, v, b, w (`dtype`) and of o (`o_dtype`).  Arithmetic
+ * inside is fp32 either way; log_alpha and the state are always float32. */
+typedef enum gdn2_dtype {
+    GDN2_DTYPE_F32 = 0,
+    GDN2_DTYPE_BF16 = 1
+} gdn2_dtype_t;
+
+typedef enum gdn2_status {
+    GDN2_OK = 0,
+    GDN2_ERR_NULL = 1,        /* a required pointer is NULL */
+    GDN2_ERR_SHAPE = 2,       /* a size is < 1 or too large for 32-bit indexing of a row */
+    GDN2_ERR_UNSUPPORTED = 3, /* (dk, dv, dtype) is not built into this library */
+    GDN2_ERR_MISALIGNED = 4,  /* a tensor pointer is not 16-byte aligned */
+    GDN2_ERR_ALIAS = 5,       /* an output overlaps an input it must not overlap */
+    GDN2_ERR_HIP = 6          /* the HIP runtime rejected a query or a launch */
+} gdn2_status_t;
+
+/*
+ * gdn2_chunk_fwd -- forward over B sequences of T tokens and H heads.
+ *
+ *   q, k, b       [B, T, H, dk]  dtype        query, key, erase gate
+ *   v, w          [B, T, H, dv]  dtype        value, write gate
+ *   log_alpha     [B, T, H, dk]  float32      log of the per-channel decay
+ *   initial_state [B, H, dk, dv] float32      S_0, or NULL for zeros
+ *   o             [B, T, H, dv]  o_dtype      out: o_t = S_t^T q_t
+ *   final_state   [B, H, dk, dv] float32      out: S_T, or NULL to skip;
+ *                                             may be the same pointer as
+ *                                             initial_state (updated in place)
+ *
+ * T may be any value >= 1 (a last partial chunk is handled exactly).
+ * Built combinations: dtype BF16 with (dk, dv) = (64, 64) or (128, 128);
+ * dtype F32 with (64, 64).  o_dtype is F32, or equal to dtype: with bf16
+ * inputs an F32 output keeps the fp32 accumulation all the way out, a BF16
+ * output rounds it once on the store.  Others return GDN2_ERR_UNSUPPORTED.
+ * o must not overlap any input; final_state must not overlap any input other
+ * than an identical initial_state.
+ */
+gdn2_status_t gdn2_chunk_fwd(const void* q, const void* k, const void* v,
+                             const float* log_alpha, const void* b, const void* w,
+                             const float* initial_state, void* o, float* final_state,
+                             int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                             gdn2_dtype_t dtype, gdn2_dtype_t o_dtype, void* stream);
+
+/*
+ * gdn2_decode_step -- one recurrent step for N independent sequences.
+ *
+ *   q, k, b       [N, H, dk]     dtype
+ *   v, w          [N, H, dv]     dtype
+ *   log_alpha     [N, H, dk]     float32
+ *   state         [N, H, dk, dv] float32      read and updated in place
+ *   o             [N, H, dv]     o_dtype      out: o = S_new^T q
+ *
+ * Built combinations: dtype BF16 or F32 with (dk, dv) = (64, 64) or (128, 128);
+ * o_dtype is F32 or equal to dtype.
+ * o must not overlap any input or the state.
+ */
+gdn2_status_t gdn2_decode_step(const void* q, const void* k, const void* v,
+                               const float* log_alpha, const void* b, const void* w,
+                               float* state, void* o, int64_t N, int64_t H, int64_t dk,
+                               int64_t dv, gdn2_dtype_t dtype, gdn2_dtype_t o_dtype,
+                               void* stream);
+
+/* 1 if gdn2_chunk_fwd (which = 0) or gdn2_decode_step (which = 1) supports
+ * (dk, dv, dtype), else 0. */
+int gdn2_supported(int which, int64_t dk, int64_t dv, gdn2_dtype_t dtype);
+
+/* Static, NUL-terminated description of a status code. */
+const char* gdn2_status_string(gdn2_status_t status);
+
+/* Static version string of the library. */
+const char* gdn2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN2_H */

@@ -1,0 +1,148 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects invalid calls before touching the HIP runtime.
+
+The pointers used here are host addresses that are never dereferenced: every
+call below fails validation, which happens before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_gdn2_amd as gdn2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn2.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_ALIAS, ERR_HIP = range(7)
+BF16, F32 = 1, 0
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn2.library_path()):
+        pytest.skip("libgdn2.so not built")
+    return gdn2._load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn2_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_two_calls():
+    names = declared_functions()
+    assert "gdn2_chunk_fwd" in names and "gdn2_decode_step" in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    for s in range(7):
+        assert lib.gdn2_status_string(s)
+    assert gdn2.version().startswith("gdn2-gfx950")
+
+
+def test_supported_table(lib):
+    assert lib.gdn2_supported(0, 128, 128, BF16) == 1
+    assert lib.gdn2_supported(0, 64, 64, BF16) == 1
+    assert lib.gdn2_supported(0, 64, 64, F32) == 1
+    assert lib.gdn2_supported(0, 128, 128, F32) == 0
+    assert lib.gdn2_supported(0, 96, 96, BF16) == 0
+    assert lib.gdn2_supported(1, 128, 128, F32) == 1
+    assert lib.gdn2_supported(1, 32, 32, BF16) == 0
+    assert lib.gdn2_supported(2, 128, 128, BF16) == 0
+
+
+# --- validation paths (no HIP call is reached) ---------------------------------
+
+class Fake:
+    """Distinct, 16-byte aligned, never-dereferenced addresses."""
+
+    def __init__(self, nbytes=1 << 20):
+        self.buf = ctypes.create_string_buffer(nbytes * 12 + 64)
+        base = (ctypes.addressof(self.buf) + 15) & ~15
+        self.nbytes = nbytes
+        self.base = base
+
+    def p(self, i, offset=0):
+        return ctypes.c_void_p(self.base + i * self.nbytes + offset)
+
+
+def chunk(lib, f, B=1, T=64, H=1, dk=64, dv=64, dtype=BF16, odt=F32, **over):
+    args = dict(q=f.p(0), k=f.p(1), v=f.p(2), g=f.p(3), b=f.p(4), w=f.p(5), s0=None, o=f.p(7),
+                sT=None)
+    args.update(over)
+    return lib.gdn2_chunk_fwd(args["q"], args["k"], args["v"], args["g"], args["b"], args["w"],
+                              args["s0"], args["o"], args["sT"], B, T, H, dk, dv, dtype, odt, None)
+
+
+def decode(lib, f, N=1, H=1, dk=64, dv=64, dtype=BF16, odt=F32, **over):
+    args = dict(q=f.p(0), k=f.p(1), v=f.p(2), g=f.p(3), b=f.p(4), w=f.p(5), s=f.p(6), o=f.p(7))
+    args.update(over)
+    return lib.gdn2_decode_step(args["q"], args["k"], args["v"], args["g"], args["b"], args["w"],
+                                args["s"], args["o"], N, H, dk, dv, dtype, odt, None)
+
+
+def test_chunk_null_pointers(lib):
+    f = Fake()
+    for name in ("q", "k", "v", "g", "b", "w", "o"):
+        assert chunk(lib, f, **{name: None}) == ERR_NULL, name
+
+
+def test_chunk_bad_shapes(lib):
+    f = Fake()
+    assert chunk(lib, f, B=0) == ERR_SHAPE
+    assert chunk(lib, f, T=0) == ERR_SHAPE
+    assert chunk(lib, f, H=-1) == ERR_SHAPE
+    assert chunk(lib, f, B=1 << 40, T=1 << 40) == ERR_SHAPE
+
+
+def test_chunk_unsupported(lib):
+    f = Fake()
+    assert chunk(lib, f, dk=96, dv=96) == ERR_UNSUPPORTED
+    assert chunk(lib, f, dk=128, dv=128, dtype=F32) == ERR_UNSUPPORTED
+    assert chunk(lib, f, dtype=7) == ERR_UNSUPPORTED
+    assert chunk(lib, f, dtype=F32, dk=64, dv=64, odt=BF16) == ERR_UNSUPPORTED
+    assert chunk(lib, f, odt=9) == ERR_UNSUPPORTED
+
+
+def test_chunk_misaligned(lib):
+    f = Fake()
+    assert chunk(lib, f, q=f.p(0, 2)) == ERR_MISALIGNED
+    assert chunk(lib, f, sT=f.p(8, 4)) == ERR_MISALIGNED
+
+
+def test_chunk_aliasing(lib):
+    f = Fake()
+    # o on top of v
+    assert chunk(lib, f, o=f.p(2, 64)) == ERR_ALIAS
+    # final state overlapping k
+    assert chunk(lib, f, sT=f.p(1, 16)) == ERR_ALIAS
+    # final state partially overlapping the initial state
+    assert chunk(lib, f, s0=f.p(8), sT=f.p(8, 16)) == ERR_ALIAS
+
+
+def test_decode_validation(lib):
+    f = Fake()
+    for name in ("q", "k", "v", "g", "b", "w", "s", "o"):
+        assert decode(lib, f, **{name: None}) == ERR_NULL, name
+    assert decode(lib, f, N=0) == ERR_SHAPE
+    assert decode(lib, f, dk=32, dv=32) == ERR_UNSUPPORTED
+    assert decode(lib, f, dtype=F32, odt=BF16) == ERR_UNSUPPORTED
+    assert decode(lib, f, s=f.p(6, 8)) == ERR_MISALIGNED
+    assert decode(lib, f, o=f.p(6)) == ERR_ALIAS
+    assert decode(lib, f, s=f.p(0)) == ERR_ALIAS
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+
+    x = torch.zeros(1, 64, 1, 64, dtype=torch.bfloat16)
+    g = torch.zeros(1, 64, 1, 64)
+    with pytest.raises(ValueError):
+        gdn2.chunk_fwd(x, x, x, g, x, x)
