@@ -1,0 +1,173 @@
+"""Benchmark of the GDN-2 hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one chunk-parallel forward (gdn2_chunk_fwd) over the training-shape
+workload B=8, T=4096, H=16, dk=dv=128 (bf16 q,k,v,b,w, fp32 log alpha, zero
+initial state, fp32 o and final state), inputs resident in HBM before timing.
+The decode workload (N=256 sequences x H=16, 128x128 fp32 state, one token per
+step) is timed in the same run and reported under "decode".
+
+Prints one JSON line.  `value` is tokens/s (B*T tokens per step); `roofline`
+gives the chunk kernel's algorithmic HBM bytes per launch over its average
+launch time, measured with HIP events on the stream the kernel runs on;
+`cpu_baseline` is the fp64 oracle timed on a bounded sample of the same
+workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GDN-2 chunked fwd tokens/s (T=4K,H=16,d=128); decode state GB/s vs peak"
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+
+
+def chunk_bytes(B, T, H, dk, dv, in_bytes=2, out_bytes=4, with_s0=False):
+    """Algorithmic HBM bytes of one forward: every input read once, o and S_T written once."""
+    per_head_token = 3 * dk * in_bytes + 2 * dv * in_bytes + dk * 4 + dv * out_bytes
+    state = B * H * dk * dv * 4 * (2 if with_s0 else 1)
+    return B * T * H * per_head_token + state
+
+
+def decode_bytes(N, H, dk, dv, in_bytes=2, out_bytes=4):
+    """Algorithmic HBM bytes of one decode step: state read + written, token vectors, o."""
+    return N * H * (2 * dk * dv * 4 + 3 * dk * in_bytes + 2 * dv * in_bytes + dk * 4 + dv * out_bytes)
+
+
+def time_launches(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps  # ms per launch
+
+
+def cpu_baseline(wl, torch):
+    """The oracle as it stands, on a bounded sample: 2 sequences x all heads x 1024 tokens."""
+    import oracle
+    import workloads as W
+
+    Bs, Ts = 2, 1024
+    inp = W.make_inputs(wl, B=Bs, T=Ts)
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["b"], inp["w"], inp["s0"],
+               nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": Bs * Ts / dt, "unit": "tokens/s", "cores": min(threads, Bs * wl.H),
+            "kind": "oracle",
+            "sample": "fp64 oracle, B=%d T=%d H=%d d=%d (%d of %d sequences, first %d tokens), "
+                      "%.2f s wall" % (Bs, Ts, wl.H, wl.dk, Bs * wl.H, wl.B * wl.H, Ts, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--out-bf16", action="store_true", help="write o in bf16 instead of fp32")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the GDN-2 recurrence shards over independent "
+              "(sequence, head) pairs with no exchange, so more GPUs only replicate this "
+              "measurement; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_delta_rule_gdn2_amd as gdn2
+    import workloads as W
+
+    gdn2._load()
+    dev = torch.device("cuda:0")
+    out_dtype = torch.bfloat16 if args.out_bf16 else torch.float32
+
+    # ---------------- chunk forward, training-shape workload ----------------
+    wl = W.TRAIN_4K
+    inp = W.make_inputs(wl)
+    d = {n: (None if x is None else x.to(dev)) for n, x in inp.items()}
+    del inp
+    o = torch.empty((wl.B, wl.T, wl.H, wl.dv), dtype=out_dtype, device=dev)
+    sT = torch.empty((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=dev)
+
+    def step():
+        gdn2.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["s0"], o=o,
+                       final_state=sT, out_dtype=out_dtype)
+
+    ms = time_launches(step, args.steps, args.warmup, torch)
+    tokens = wl.B * wl.T
+    nbytes = chunk_bytes(wl.B, wl.T, wl.H, wl.dk, wl.dv, out_bytes=out_dtype.itemsize)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    del d, o, sT
+    torch.cuda.empty_cache()
+
+    # ---------------- decode workload ----------------
+    dwl = W.DECODE
+    pool = W.make_decode_pool(dwl)
+    state = pool["state"].to(dev)
+    dp = {n: pool[n].to(dev) for n in ("q", "k", "v", "log_alpha", "b", "w")}
+    del pool
+    o_dec = torch.empty((dwl.B, dwl.H, dwl.dv), dtype=out_dtype, device=dev)
+    it = [0]
+
+    def dstep():
+        p = it[0] % dwl.pool
+        it[0] += 1
+        gdn2.decode_step(dp["q"][p], dp["k"][p], dp["v"][p], dp["log_alpha"][p], dp["b"][p],
+                         dp["w"][p], state, o=o_dec, out_dtype=out_dtype)
+
+    dms = time_launches(dstep, args.decode_steps, 5, torch)
+    dbytes = decode_bytes(dwl.B, dwl.H, dwl.dk, dwl.dv, out_bytes=out_dtype.itemsize)
+    dgbps = dbytes / (dms * 1e-3) / 1e9
+    del state, dp, o_dec
+    torch.cuda.empty_cache()
+
+    result = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded, distributions of the training-shape workload)",
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": wl.H, "dk": wl.dk, "dv": wl.dv,
+                   "chunk": 64, "inputs": "bf16 q,k,v,b,w; fp32 log_alpha",
+                   "o_dtype": "bf16" if args.out_bf16 else "f32", "initial_state": "zeros"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "chunk_fwd_kernel", "algorithmic_bytes_per_launch": nbytes,
+                     "avg_launch_us": ms * 1e3},
+        "decode": {"workload": dwl.name, "us_per_step": dms * 1e3, "state_GBps": dgbps,
+                   "peak": HBM_PEAK_GBPS, "frac": dgbps / HBM_PEAK_GBPS,
+                   "algorithmic_bytes_per_step": dbytes, "steps": args.decode_steps},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, torch)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

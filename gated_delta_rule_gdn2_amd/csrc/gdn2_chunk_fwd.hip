@@ -70,13 +70,13 @@ struct ChunkCfg {
     static constexpr int WORK = A32 + C * LA * 4;                   // time-shared work area
     // work area, element/A-P phase: fast -> BG, KI rows; strong -> 12 groups of 16 rows
     static constexpr int W_AP = 192 * LDK * ES;
-    // work area, solve phase: T fp32, T operand, (w.v)^T hi/lo
+    // work area, solve phase: T fp32 and T as an MFMA operand
     static constexpr int T32 = WORK;
     static constexpr int TOP = T32 + C * LA * 4;
-    static constexpr int WVT = TOP + C * LC * ES;
-    static constexpr int W_T = C * LA * 4 + C * LC * ES + NS * DVS * LC * ES;
+    static constexpr int W_T = C * LA * 4 + C * LC * ES;
     static constexpr int WORK_BYTES = W_AP > W_T ? W_AP : W_T;
-    static constexpr int GC = WORK + WORK_BYTES;                    // [DK] fp32 Gamma_C
+    static constexpr int WVT = WORK + WORK_BYTES;                   // NS x [DVS][LC] (w.v)^T hi, lo
+    static constexpr int GC = WVT + NS * DVS * LC * ES;             // [DK] fp32 Gamma_C
     static constexpr int BLK = GC + DK * 4;                         // [4][DK] fp32 block decays
     static constexpr int BYTES = BLK + 4 * DK * 4;
     static_assert(BYTES <= 163840, "LDS budget exceeded");
@@ -117,6 +117,49 @@ template <> __device__ __forceinline__ void store_split<bf16>(bf16* hi, bf16* lo
 }
 template <> __device__ __forceinline__ void store_split<float>(float* hi, float*, float x) { *hi = x; }
 
+// N consecutive values converted to T and written with vector stores (p aligned to 16 bytes or to
+// N * sizeof(T), whichever is smaller)
+template <typename T, int N>
+__device__ __forceinline__ void store_vec(T* p, const float (&x)[N]) {
+    if constexpr (N == 1) {
+        *p = from_f32<T>(x[0]);
+    } else {
+        typedef T V __attribute__((ext_vector_type(N)));
+        constexpr int AL = N * (int)sizeof(T) < 16 ? N * (int)sizeof(T) : 16;
+        V y;
+#pragma unroll
+        for (int i = 0; i < N; ++i) y[i] = from_f32<T>(x[i]);
+        *reinterpret_cast<V*>(__builtin_assume_aligned(p, AL)) = y;
+    }
+}
+
+// the same as a hi / lo pair for bf16 (fp32: the value itself, lo unused)
+template <typename T, int N>
+__device__ __forceinline__ void store_vec_split(T* hi, T* lo, const float (&x)[N]) {
+    if constexpr (sizeof(T) == 2) {
+        float h[N], l[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            bf16 a, b;
+            split_bf16(x[i], a, b);
+            h[i] = (float)a;
+            l[i] = (float)b;
+        }
+        store_vec<T, N>(hi, h);  // exact: h and l are bf16 values
+        store_vec<T, N>(lo, l);
+    } else {
+        store_vec<T, N>(hi, x);
+    }
+}
+
+// Inputs of one chunk as one thread loads them.
+template <typename T, int CPT, int TPV>
+struct ChunkIn {
+    Vec<float, CPT> g[16];
+    Vec<T, CPT> q[16], k[16], b[16];
+    Vec<T, 2> w[TPV], v[TPV];
+};
+
 template <typename T, typename OutT, int DK, int DV, int DVS>
 __global__ __launch_bounds__(256) void chunk_fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -127,6 +170,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
     constexpr int C = Cfg::C, CPT = Cfg::CPT, NCT = Cfg::NCT;
     constexpr int LDK = Cfg::LDK, LC = Cfg::LC, LA = Cfg::LA;
     constexpr bool SPLIT = Cfg::SPLIT;
+    constexpr int TPV = C * DVS / (2 * Cfg::NT);  // tokens per thread for w.v (two columns each)
     __shared__ __attribute__((aligned(16))) char smem[Cfg::BYTES];
     T* sQG = reinterpret_cast<T*>(smem + Cfg::QG);
     T* sBGT = reinterpret_cast<T*>(smem + Cfg::BGT);
@@ -144,7 +188,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
     float* sBLK = reinterpret_cast<float*>(smem + Cfg::BLK);
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
     const int lane = tid & 63;
     const int l16 = lane & 15;
     const int g4 = lane >> 4;
@@ -188,7 +232,6 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
                 for (int r = 0; r < 4; ++r) S[a][st][r] = src[(int64_t)(st * 16 + g4 * 4 + r) * DV];
         }
     }
-    __syncthreads();
 
     const int nchunks = (Tlen + C - 1) / C;
     const int64_t tok_stride_k = (int64_t)H * DK;  // elements between consecutive tokens
@@ -197,38 +240,67 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
     const int64_t seq_base_v = ((int64_t)bi * Tlen * H + h) * DV;
     const int I = wave;             // 16-token block of this thread in the element phase
     const int cbase = lane * CPT;   // first key channel of this thread in the element phase
-    constexpr int TPT = C * DVS / Cfg::NT;  // tokens per thread for w.v
-    const int cv = tid % DVS, tg = tid / DVS;
+    const int cvp = (tid % (DVS / 2)) * 2, tgv = tid / (DVS / 2);  // w.v: column pair, token group
+
+    // Every global load of a chunk, issued without a branch: a token past the end
+    // of the sequence reads the last token and is zeroed where it is used.
+    auto load_chunk = [&](int n, ChunkIn<T, CPT, TPV>& in) {
+        const int t0 = n * C;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int t = min(t0 + I * 16 + i, Tlen - 1);
+            const int64_t off = seq_base_k + (int64_t)t * tok_stride_k + cbase;
+            in.g[i] = load_vec<float, CPT>(log_alpha + off);
+            in.q[i] = load_vec<T, CPT>(q + off);
+            in.k[i] = load_vec<T, CPT>(k + off);
+            in.b[i] = load_vec<T, CPT>(bgate + off);
+        }
+#pragma unroll
+        for (int i = 0; i < TPV; ++i) {
+            const int t = min(t0 + tgv * TPV + i, Tlen - 1);
+            const int64_t off = seq_base_v + (int64_t)t * tok_stride_v + col0 + cvp;
+            in.w[i] = load_vec<T, 2>(wgate + off);
+            in.v[i] = load_vec<T, 2>(v + off);
+        }
+    };
+
+    ChunkIn<T, CPT, TPV> in;
+    load_chunk(0, in);
+    __syncthreads();
 
     for (int n = 0; n < nchunks; ++n) {
         const int t0 = n * C;
         // =============== element phase, pass 1: per-channel decays ===============
-        float al[CPT][16];
+        float al[CPT][16], pre[CPT][16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int t = t0 + I * 16 + i;
-            const int64_t off = seq_base_k + (int64_t)t * tok_stride_k + cbase;
+            const bool valid = t0 + I * 16 + i < Tlen;
 #pragma unroll
-            for (int cc = 0; cc < CPT; ++cc) al[cc][i] = exp_neg(t < Tlen ? log_alpha[off + cc] : 0.f);
+            for (int cc = 0; cc < CPT; ++cc) al[cc][i] = valid ? exp_neg(in.g[i].v[cc]) : 1.f;
         }
+        {
+            float blkv[CPT];
 #pragma unroll
-        for (int cc = 0; cc < CPT; ++cc) {
-            float p = 1.f;
+            for (int cc = 0; cc < CPT; ++cc) {
+                float p = 1.f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) p *= al[cc][i];
-            sBLK[I * DK + cbase + cc] = p;
-        }
-        // write gate times value for this thread's (column, tokens): kept in registers
-        float wv[TPT];
-#pragma unroll
-        for (int i = 0; i < TPT; ++i) {
-            const int t = t0 + tg * TPT + i;
-            float x = 0.f;
-            if (t < Tlen) {
-                const int64_t off = seq_base_v + (int64_t)t * tok_stride_v + col0 + cv;
-                x = to_f32(wgate[off]) * to_f32(v[off]);
+                for (int i = 0; i < 16; ++i) { p *= al[cc][i]; pre[cc][i] = p; }
+                blkv[cc] = p;
             }
-            wv[i] = x;
+            store_vec<float, CPT>(sBLK + I * DK + cbase, blkv);
+        }
+        // write gate times value, transposed ([column][token]), hi / lo
+        {
+            float x0[TPV], x1[TPV];
+#pragma unroll
+            for (int i = 0; i < TPV; ++i) {
+                const bool valid = t0 + tgv * TPV + i < Tlen;
+                x0[i] = valid ? to_f32(in.w[i].v[0]) * to_f32(in.v[i].v[0]) : 0.f;
+                x1[i] = valid ? to_f32(in.w[i].v[1]) * to_f32(in.v[i].v[1]) : 0.f;
+            }
+            const int idx = cvp * LC + tgv * TPV;
+            store_vec_split<T, TPV>(sWVh + idx, sWVl + idx, x0);
+            store_vec_split<T, TPV>(sWVh + idx + LC, sWVl + idx + LC, x1);
         }
         __syncthreads();
         float blk[CPT][4];
@@ -244,76 +316,89 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
         strong = __syncthreads_or(strong);
 
         // =============== element phase, pass 2: scaled operands ===============
+        {
+            float before[CPT], after[CPT], sfx[CPT];  // whole blocks before / after block I; running suffix
 #pragma unroll
-        for (int cc = 0; cc < CPT; ++cc) {
-            const int c = cbase + cc;
-            float qv[16], kv[16], bk[16], pre[16], suf[16];
+            for (int cc = 0; cc < CPT; ++cc) {
+                before[cc] = 1.f;
+                after[cc] = 1.f;
+                sfx[cc] = 1.f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int t = t0 + I * 16 + i;
-                const int64_t off = seq_base_k + (int64_t)t * tok_stride_k + c;
-                const bool valid = t < Tlen;
-                qv[i] = valid ? to_f32(q[off]) : 0.f;
-                kv[i] = valid ? to_f32(k[off]) : 0.f;
-                bk[i] = valid ? to_f32(bgate[off]) * kv[i] : 0.f;
+                for (int K = 0; K < 4; ++K) {
+                    if (K < I) before[cc] *= blk[cc][K];
+                    if (K > I) after[cc] *= blk[cc][K];
+                }
             }
-            {
-                float p = 1.f;
+            float bgt[CPT][16], kgt[CPT][16];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) { p *= al[cc][i]; pre[i] = p; }
-                float s = 1.f;
-#pragma unroll
-                for (int i = 15; i >= 0; --i) { suf[i] = s; s *= al[cc][i]; }
-            }
-            float before = 1.f, after = 1.f;  // whole blocks before / after block I
-#pragma unroll
-            for (int K = 0; K < 4; ++K) {
-                if (K < I) before *= blk[cc][K];
-                if (K > I) after *= blk[cc][K];
-            }
-            T bgt[16], kgt[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
+            for (int i = 15; i >= 0; --i) {
                 const int tl = I * 16 + i;
-                const float gam = before * pre[i];   // Gamma_i  (chunk start -> i)
-                const float gamr = suf[i] * after;   // Gamma'_i (i -> chunk end)
-                sQG[tl * LDK + c] = from_f32<T>(qv[i] * gam);
-                bgt[i] = from_f32<T>(bk[i] * gam);
-                kgt[i] = from_f32<T>(kv[i] * gamr);
-                if (!strong) {
-                    sWork[tl * LDK + c] = bgt[i];                                                   // BG
-                    sWork[(64 + tl) * LDK + c] = from_f32<T>(kv[i] * __builtin_amdgcn_rcpf(gam));  // KI
-                } else {
-                    // recursive split at the chunk level: groups of 16 rows in the work area
-                    //  level 64 (pivot 31): rows of blocks 2,3 (A: g0,g1; P: g2,g3), columns of blocks 0,1 (g4,g5)
-                    //  level 32 (pivots 15, 47): rows of blocks 1,3 (A: g6,g7; P: g8,g9), columns of blocks 0,2 (g10,g11)
-                    T* wk = sWork + i * LDK + c;
+                const bool valid = t0 + tl < Tlen;
+                // x: QG, BG, KI for the mild variant; y: level-64 rows/columns, z: level-32 ones
+                float xq[CPT], xb[CPT], xki[CPT], ya[CPT], yp[CPT], za[CPT], zp[CPT];
+#pragma unroll
+                for (int cc = 0; cc < CPT; ++cc) {
+                    const float qv = valid ? to_f32(in.q[i].v[cc]) : 0.f;
+                    const float kv = valid ? to_f32(in.k[i].v[cc]) : 0.f;
+                    const float bk = valid ? to_f32(in.b[i].v[cc]) * kv : 0.f;
+                    const float gam = before[cc] * pre[cc][i];  // Gamma_i  (chunk start -> i)
+                    const float suf = sfx[cc];                 // decay from i to the end of block I
+                    sfx[cc] *= al[cc][i];
+                    xq[cc] = qv * gam;
+                    xb[cc] = bk * gam;
+                    xki[cc] = kv * __builtin_amdgcn_rcpf(gam);
+                    bgt[cc][i] = xb[cc];
+                    kgt[cc][i] = kv * suf * after[cc];         // k . Gamma'_i  (i -> chunk end)
+                    // strong chunks, recursive split at the chunk level:
+                    //  level 64, pivot = token 31: rows i >= 32 scale by Gamma_{i<-31}, columns j <= 31 by Gamma_{31<-j}
+                    //  level 32, pivots 15 and 47: rows of blocks 1, 3 by pre, columns of blocks 0, 2 by suf
                     if (I >= 2) {
-                        const float f = I == 3 ? blk[cc][2] * pre[i] : pre[i];
-                        wk[(I - 2) * 16 * LDK] = from_f32<T>(bk[i] * f);
-                        wk[(2 + I - 2) * 16 * LDK] = from_f32<T>(qv[i] * f);
+                        const float f = I == 3 ? blk[cc][2] * pre[cc][i] : pre[cc][i];
+                        ya[cc] = bk * f;
+                        yp[cc] = qv * f;
                     } else {
-                        const float f = I == 0 ? suf[i] * blk[cc][1] : suf[i];
-                        wk[(4 + I) * 16 * LDK] = from_f32<T>(kv[i] * f);
+                        ya[cc] = kv * suf * (I == 0 ? blk[cc][1] : 1.f);
+                        yp[cc] = 0.f;
                     }
                     if (I & 1) {
-                        wk[(6 + I / 2) * 16 * LDK] = from_f32<T>(bk[i] * pre[i]);
-                        wk[(8 + I / 2) * 16 * LDK] = from_f32<T>(qv[i] * pre[i]);
+                        za[cc] = bk * pre[cc][i];
+                        zp[cc] = qv * pre[cc][i];
                     } else {
-                        wk[(10 + I / 2) * 16 * LDK] = from_f32<T>(kv[i] * suf[i]);
+                        za[cc] = kv * suf;
+                        zp[cc] = 0.f;
+                    }
+                }
+                store_vec<T, CPT>(sQG + tl * LDK + cbase, xq);
+                if (!strong) {
+                    store_vec<T, CPT>(sWork + tl * LDK + cbase, xb);          // BG
+                    store_vec<T, CPT>(sWork + (64 + tl) * LDK + cbase, xki);  // KI
+                } else {
+                    // 16-row groups: g0,g1 A rows (blocks 2,3), g2,g3 P rows, g4,g5 columns (blocks 0,1);
+                    // g6,g7 A rows (blocks 1,3), g8,g9 P rows, g10,g11 columns (blocks 0,2)
+                    T* wk = sWork + i * LDK + cbase;
+                    if (I >= 2) {
+                        store_vec<T, CPT>(wk + (I - 2) * 16 * LDK, ya);
+                        store_vec<T, CPT>(wk + I * 16 * LDK, yp);
+                    } else {
+                        store_vec<T, CPT>(wk + (4 + I) * 16 * LDK, ya);
+                    }
+                    if (I & 1) {
+                        store_vec<T, CPT>(wk + (6 + I / 2) * 16 * LDK, za);
+                        store_vec<T, CPT>(wk + (8 + I / 2) * 16 * LDK, zp);
+                    } else {
+                        store_vec<T, CPT>(wk + (10 + I / 2) * 16 * LDK, za);
                     }
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                sBGT[c * LC + I * 16 + i] = bgt[i];
-                sKGT[c * LC + I * 16 + i] = kgt[i];
+            for (int cc = 0; cc < CPT; ++cc) {
+                store_vec<T, 16>(sBGT + (cbase + cc) * LC + I * 16, bgt[cc]);
+                store_vec<T, 16>(sKGT + (cbase + cc) * LC + I * 16, kgt[cc]);
             }
         }
         __syncthreads();
 
         // =============== A and P ===============
-        // accumulators of up to two 16x16 block pairs per wave, stored after a barrier
         if (!strong) {
             // single pivot at the chunk start: A = BG KI^T, P = QG KI^T on the lower blocks
 #pragma unroll
@@ -353,7 +438,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
                 if (pi == 0) {
                     Ib = wave < 2 ? 2 : 3;
                     Jb = wave & 1;
-                    ga = Ib - 2; gp = 2 + Ib - 2; gcol = 4 + Jb;
+                    ga = Ib - 2; gp = Ib; gcol = 4 + Jb;
                 } else if (wave < 2) {
                     Ib = wave == 0 ? 1 : 3;
                     Jb = Ib - 1;
@@ -379,30 +464,24 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
                     }
                 }
             }
-            __syncthreads();
             // ---- levels 16, 8, 4, 2 inside the diagonal block I = wave, then P's diagonal ----
-            float qv[CPT][16], kv[CPT][16], bk[CPT][16];
+            Vec<T, CPT> xq[16], xk[16], xb[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int t = t0 + I * 16 + i;
-                const int64_t off = seq_base_k + (int64_t)t * tok_stride_k + cbase;
-                const bool valid = t < Tlen;
-#pragma unroll
-                for (int cc = 0; cc < CPT; ++cc) {
-                    qv[cc][i] = valid ? to_f32(q[off + cc]) : 0.f;
-                    kv[cc][i] = valid ? to_f32(k[off + cc]) : 0.f;
-                    bk[cc][i] = valid ? to_f32(bgate[off + cc]) * kv[cc][i] : 0.f;
-                }
+                const int64_t off = seq_base_k + (int64_t)min(t0 + I * 16 + i, Tlen - 1) * tok_stride_k + cbase;
+                xq[i] = load_vec<T, CPT>(q + off);
+                xk[i] = load_vec<T, CPT>(k + off);
+                xb[i] = load_vec<T, CPT>(bgate + off);
             }
+            __syncthreads();  // the level tiles below reuse the work area
             T* lv = sWork + (wave * 48) * LDK;  // rows: [0,16) A rows, [16,32) P rows, [32,48) columns
             f32x4 dA = zero4(), dP = zero4();
 #pragma unroll
             for (int L = 0; L < 5; ++L) {
                 const int size = L < 4 ? (16 >> L) : 1;
+                float rf[CPT][16], cf[CPT][16];
 #pragma unroll
                 for (int cc = 0; cc < CPT; ++cc) {
-                    const int c = cbase + cc;
-                    float rf[16], cf[16];
                     // row factor Gamma_{i<-p} for i in the upper half of its segment,
                     // column factor Gamma_{p<-j} for j in the lower half (p = last of lower half)
                     if (L < 4) {
@@ -411,28 +490,35 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
                             const int p = s0 + size / 2 - 1;
                             float f = 1.f;
 #pragma unroll
-                            for (int i = p + 1; i < s0 + size; ++i) { f *= al[cc][i]; rf[i] = f; }
+                            for (int i = p + 1; i < s0 + size; ++i) { f *= al[cc][i]; rf[cc][i] = f; }
                             float gcl = 1.f;
 #pragma unroll
-                            for (int i = p; i >= s0; --i) { cf[i] = gcl; gcl *= al[cc][i]; }
+                            for (int i = p; i >= s0; --i) { cf[cc][i] = gcl; gcl *= al[cc][i]; }
                         }
                     }
+                }
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        float ra, rp, cl;
+                for (int i = 0; i < 16; ++i) {
+                    const bool valid = t0 + I * 16 + i < Tlen;
+                    float ra[CPT], rp[CPT], cl[CPT];
+#pragma unroll
+                    for (int cc = 0; cc < CPT; ++cc) {
+                        const float qv = valid ? to_f32(xq[i].v[cc]) : 0.f;
+                        const float kv = valid ? to_f32(xk[i].v[cc]) : 0.f;
+                        const float bk = valid ? to_f32(xb[i].v[cc]) * kv : 0.f;
                         if (L == 4) {
-                            ra = 0.f; rp = qv[cc][i]; cl = kv[cc][i];
+                            ra[cc] = 0.f; rp[cc] = qv; cl[cc] = kv;
                         } else {
                             const int p = (i / size) * size + size / 2 - 1;
                             const bool row = i > p;
-                            ra = row ? bk[cc][i] * rf[i] : 0.f;
-                            rp = row ? qv[cc][i] * rf[i] : 0.f;
-                            cl = row ? 0.f : kv[cc][i] * cf[i];
+                            ra[cc] = row ? bk * rf[cc][i] : 0.f;
+                            rp[cc] = row ? qv * rf[cc][i] : 0.f;
+                            cl[cc] = row ? 0.f : kv * cf[cc][i];
                         }
-                        lv[i * LDK + c] = from_f32<T>(ra);
-                        lv[(16 + i) * LDK + c] = from_f32<T>(rp);
-                        lv[(32 + i) * LDK + c] = from_f32<T>(cl);
                     }
+                    store_vec<T, CPT>(lv + i * LDK + cbase, ra);
+                    store_vec<T, CPT>(lv + (16 + i) * LDK + cbase, rp);
+                    store_vec<T, CPT>(lv + (32 + i) * LDK + cbase, cl);
                 }
                 __syncthreads();
                 f32x4 tA = zero4(), tP = zero4();
@@ -466,23 +552,19 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
         __syncthreads();
 
         // =============== T = (I + A)^{-1}, unit lower triangular ===============
-        // (w.v)^T into the work area now that the A/P operands are consumed
-#pragma unroll
-        for (int i = 0; i < TPT; ++i) {
-            const int idx = cv * LC + tg * TPT + i;
-            store_split<T>(sWVh + idx, sWVl + idx, wv[i]);
-        }
-        // diagonal 16x16 blocks by forward substitution: wave I, lane j < 16 owns column j
+        // diagonal 16x16 blocks by forward substitution, column j on lane j of wave I;
+        // the updates of step m to rows m+1..15 are independent of each other
         if (lane < 16) {
             const int j = lane;
             const float* Ab = sA + (wave * 16) * LA + wave * 16;
             float x[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float acc = (i == j) ? 1.f : 0.f;
+            for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
 #pragma unroll
-                for (int m = 0; m < i; ++m) acc -= Ab[i * LA + m] * x[m];
-                x[i] = (i < j) ? 0.f : acc;
+            for (int m = 0; m < 15; ++m) {
+                const float xm = x[m];
+#pragma unroll
+                for (int i = m + 1; i < 16; ++i) x[i] -= Ab[i * LA + m] * xm;
             }
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -526,6 +608,9 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
             }
             __syncthreads();
         }
+
+        // the next chunk's inputs are loaded while this one finishes
+        load_chunk(n + 1 < nchunks ? n + 1 : n, in);
 
         // =============== W = T (b.k.Gamma), U0 = T (w.v) ===============
         constexpr int WCT = DK / 16 / 4;  // W column tiles per wave

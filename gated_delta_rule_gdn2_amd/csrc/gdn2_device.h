@@ -104,6 +104,22 @@ template <> __device__ __forceinline__ Frag<float> frag_from_acc<float>(const f3
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// N consecutive elements through one aligned vector load (p aligned to N * sizeof(T))
+template <typename T, int N> struct Vec { T v[N]; };
+template <typename T, int N>
+__device__ __forceinline__ Vec<T, N> load_vec(const T* p) {
+    Vec<T, N> r;
+    if constexpr (N == 1) {
+        r.v[0] = *p;
+    } else {
+        typedef T V __attribute__((ext_vector_type(N)));
+        const V x = *reinterpret_cast<const V*>(__builtin_assume_aligned(p, N * sizeof(T)));
+#pragma unroll
+        for (int i = 0; i < N; ++i) r.v[i] = x[i];
+    }
+    return r;
+}
+
 // exp(x) for x <= 0 through the hardware base-2 exponential
 __device__ __forceinline__ float exp_neg(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
