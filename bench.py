@@ -59,11 +59,11 @@ def time_launches(fn, steps, warmup, torch):
 
 
 def cpu_baseline(wl, torch):
-    """The oracle as it stands, on a bounded sample: 2 sequences x all heads x 1024 tokens."""
+    """The oracle as it stands, on the same workload (all 128 sequences, all 4096 tokens)."""
     import oracle
     import workloads as W
 
-    Bs, Ts = 2, 1024
+    Bs, Ts = wl.B, wl.T
     inp = W.make_inputs(wl, B=Bs, T=Ts)
     threads = oracle.default_threads()
     t0 = time.perf_counter()
@@ -72,35 +72,13 @@ def cpu_baseline(wl, torch):
     dt = time.perf_counter() - t0
     return {"value": Bs * Ts / dt, "unit": "tokens/s", "cores": min(threads, Bs * wl.H),
             "kind": "oracle",
-            "sample": "fp64 oracle, B=%d T=%d H=%d d=%d (%d of %d sequences, first %d tokens), "
-                      "%.2f s wall" % (Bs, Ts, wl.H, wl.dk, Bs * wl.H, wl.B * wl.H, Ts, dt)}
+            "sample": "fp64 oracle on the whole workload: B=%d T=%d H=%d d=%d (%d of %d sequences, "
+                      "%d tokens each), %.2f s wall" % (Bs, Ts, wl.H, wl.dk, Bs * wl.H, wl.B * wl.H,
+                                                        Ts, dt)}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--decode-steps", type=int, default=64)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--out-bf16", action="store_true", help="write o in bf16 instead of fp32")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the GDN-2 recurrence shards over independent "
-              "(sequence, head) pairs with no exchange, so more GPUs only replicate this "
-              "measurement; run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-
-    import gated_delta_rule_gdn2_amd as gdn2
-    import workloads as W
-
-    gdn2._load()
-    dev = torch.device("cuda:0")
-    out_dtype = torch.bfloat16 if args.out_bf16 else torch.float32
-
-    # ---------------- chunk forward, training-shape workload ----------------
+def run_chunk(args, torch, gdn2, W, dev, out_dtype):
+    """Chunk forward on the training-shape workload; returns (ms per launch, workload, bytes)."""
     wl = W.TRAIN_4K
     inp = W.make_inputs(wl)
     d = {n: (None if x is None else x.to(dev)) for n, x in inp.items()}
@@ -113,13 +91,14 @@ def main():
                        final_state=sT, out_dtype=out_dtype)
 
     ms = time_launches(step, args.steps, args.warmup, torch)
-    tokens = wl.B * wl.T
     nbytes = chunk_bytes(wl.B, wl.T, wl.H, wl.dk, wl.dv, out_bytes=out_dtype.itemsize)
-    achieved = nbytes / (ms * 1e-3) / 1e9
     del d, o, sT
     torch.cuda.empty_cache()
+    return ms, wl, nbytes
 
-    # ---------------- decode workload ----------------
+
+def run_decode(args, torch, gdn2, W, dev, out_dtype):
+    """Decode workload: N=256 sequences x H=16, one token per step, state updated in place."""
     dwl = W.DECODE
     pool = W.make_decode_pool(dwl)
     state = pool["state"].to(dev)
@@ -139,6 +118,48 @@ def main():
     dgbps = dbytes / (dms * 1e-3) / 1e9
     del state, dp, o_dec
     torch.cuda.empty_cache()
+    return {"workload": dwl.name, "us_per_step": dms * 1e3, "state_GBps": dgbps,
+            "peak": HBM_PEAK_GBPS, "frac": dgbps / HBM_PEAK_GBPS,
+            "algorithmic_bytes_per_step": dbytes, "steps": args.decode_steps}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--out-bf16", action="store_true", help="write o in bf16 instead of fp32")
+    ap.add_argument("--only", choices=("chunk", "decode"), default=None,
+                    help="time one workload only (profiler runs); prints its figures")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the GDN-2 recurrence shards over independent "
+              "(sequence, head) pairs with no exchange, so more GPUs only replicate this "
+              "measurement; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_delta_rule_gdn2_amd as gdn2
+    import workloads as W
+
+    gdn2._load()
+    dev = torch.device("cuda:0")
+    out_dtype = torch.bfloat16 if args.out_bf16 else torch.float32
+
+    if args.only == "decode":
+        print(json.dumps({"decode": run_decode(args, torch, gdn2, W, dev, out_dtype)}))
+        return
+    ms, wl, nbytes = run_chunk(args, torch, gdn2, W, dev, out_dtype)
+    tokens = wl.B * wl.T
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    if args.only == "chunk":
+        print(json.dumps({"workload": wl.name, "avg_launch_us": ms * 1e3,
+                          "tokens_per_s": tokens / (ms * 1e-3), "achieved_GBps": achieved}))
+        return
+    dec = run_decode(args, torch, gdn2, W, dev, out_dtype)
 
     result = {
         "metric": METRIC,
@@ -160,9 +181,7 @@ def main():
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
                      "kernel": "chunk_fwd_kernel", "algorithmic_bytes_per_launch": nbytes,
                      "avg_launch_us": ms * 1e3},
-        "decode": {"workload": dwl.name, "us_per_step": dms * 1e3, "state_GBps": dgbps,
-                   "peak": HBM_PEAK_GBPS, "frac": dgbps / HBM_PEAK_GBPS,
-                   "algorithmic_bytes_per_step": dbytes, "steps": args.decode_steps},
+        "decode": dec,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, torch)

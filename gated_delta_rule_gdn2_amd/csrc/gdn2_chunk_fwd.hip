@@ -59,21 +59,20 @@ struct ChunkCfg {
     static constexpr int PAD = 16 / ES;
     static constexpr int LDK = DK + PAD;           // row stride of [64][DK] tiles (elements)
     static constexpr int LC = C + PAD;             // row stride of [*][64] tiles (elements)
-    static constexpr int LA = C + 4;               // row stride of fp32 [64][64] tiles
     // persistent regions (byte offsets)
     static constexpr int QG = 0;                                    // [64][LDK] q.Gamma
     static constexpr int BGT_BYTES = (DK * LC > C * LDK ? DK * LC : C * LDK) * ES;
     static constexpr int BGT = QG + C * LDK * ES;                   // [DK][LC] (b.k.Gamma)^T, then W [64][LDK]
     static constexpr int KGT = BGT + BGT_BYTES;                     // [DK][LC] (k.Gamma')^T
     static constexpr int PM = KGT + DK * LC * ES;                   // NS x [64][LC] P (hi, lo)
-    static constexpr int A32 = PM + NS * C * LC * ES;               // [64][LA] fp32 A
-    static constexpr int WORK = A32 + C * LA * 4;                   // time-shared work area
-    // work area, element/A-P phase: fast -> BG, KI rows; strong -> 12 groups of 16 rows
+    static constexpr int AOP = PM + NS * C * LC * ES;               // [64][LC] A
+    static constexpr int WORK = AOP + C * LC * ES;                  // time-shared work area
+    // work area, element/A-P phase: mild -> BG, KI rows; strong -> 12 groups of 16 rows
     static constexpr int W_AP = 192 * LDK * ES;
-    // work area, solve phase: T fp32 and T as an MFMA operand
-    static constexpr int T32 = WORK;
-    static constexpr int TOP = T32 + C * LA * 4;
-    static constexpr int W_T = C * LA * 4 + C * LC * ES;
+    // work area, solve phase: T and T^T as MFMA operands
+    static constexpr int TOP = WORK;
+    static constexpr int TOPT = TOP + C * LC * ES;
+    static constexpr int W_T = 2 * C * LC * ES;
     static constexpr int WORK_BYTES = W_AP > W_T ? W_AP : W_T;
     static constexpr int WVT = WORK + WORK_BYTES;                   // NS x [DVS][LC] (w.v)^T hi, lo
     static constexpr int GC = WVT + NS * DVS * LC * ES;             // [DK] fp32 Gamma_C
@@ -160,6 +159,24 @@ struct ChunkIn {
     Vec<T, 2> w[TPV], v[TPV];
 };
 
+// Store a transposed 16x16 A/P block pair: lane holds entry (i = l16, j = 4*g4 + r) of block
+// (Ib, Jb).  With diag = 1 the block is on the diagonal: A keeps j < i, P keeps j <= i.
+template <typename T>
+__device__ __forceinline__ void store_AP(T* sA, T* sPh, T* sPl, int Ib, int Jb, int l16, int g4,
+                                         const f32x4& accA, const f32x4& accP, int diag) {
+    constexpr int ES = (int)sizeof(T), LC = 64 + 16 / ES;
+    float a[4], p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int j = g4 * 4 + r;
+        a[r] = (!diag || j < l16) ? accA[r] : 0.f;
+        p[r] = (!diag || j <= l16) ? accP[r] : 0.f;
+    }
+    const int pidx = (Ib * 16 + l16) * LC + Jb * 16 + g4 * 4;
+    store_vec<T, 4>(sA + pidx, a);
+    store_vec_split<T, 4>(sPh + pidx, sPl + pidx, p);
+}
+
 template <typename T, typename OutT, int DK, int DV, int DVS>
 __global__ __launch_bounds__(256) void chunk_fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -168,7 +185,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
     int nslices, int xcd_map) {
     using Cfg = ChunkCfg<T, DK, DVS>;
     constexpr int C = Cfg::C, CPT = Cfg::CPT, NCT = Cfg::NCT;
-    constexpr int LDK = Cfg::LDK, LC = Cfg::LC, LA = Cfg::LA;
+    constexpr int LDK = Cfg::LDK, LC = Cfg::LC;
     constexpr bool SPLIT = Cfg::SPLIT;
     constexpr int TPV = C * DVS / (2 * Cfg::NT);  // tokens per thread for w.v (two columns each)
     __shared__ __attribute__((aligned(16))) char smem[Cfg::BYTES];
@@ -178,10 +195,10 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
     T* sKGT = reinterpret_cast<T*>(smem + Cfg::KGT);
     T* sPh = reinterpret_cast<T*>(smem + Cfg::PM);
     T* sPl = sPh + C * LC;  // only used with SPLIT
-    float* sA = reinterpret_cast<float*>(smem + Cfg::A32);
+    T* sA = reinterpret_cast<T*>(smem + Cfg::AOP);
     T* sWork = reinterpret_cast<T*>(smem + Cfg::WORK);
-    float* sT32 = reinterpret_cast<float*>(smem + Cfg::T32);
     T* sTop = reinterpret_cast<T*>(smem + Cfg::TOP);
+    T* sTopT = reinterpret_cast<T*>(smem + Cfg::TOPT);
     T* sWVh = reinterpret_cast<T*>(smem + Cfg::WVT);
     T* sWVl = sWVh + DVS * LC;  // only used with SPLIT
     float* sGC = reinterpret_cast<float*>(smem + Cfg::GC);
@@ -210,7 +227,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
     const int col0 = slice * DVS;  // first value column of this slice
 
     // upper blocks of A and P are never written below: clear once
-    for (int x = tid; x < C * LA; x += Cfg::NT) sA[x] = 0.f;
+    for (int x = tid; x < C * LC; x += Cfg::NT) sA[x] = from_f32<T>(0.f);
     for (int x = tid; x < Cfg::NS * C * LC; x += Cfg::NT) sPh[x] = from_f32<T>(0.f);
 
     // ---- state slice in accumulators: wave w owns column tiles w, w+4, ... ----
@@ -271,13 +288,33 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
     for (int n = 0; n < nchunks; ++n) {
         const int t0 = n * C;
         // =============== element phase, pass 1: per-channel decays ===============
+        if (t0 + C > Tlen) {
+            // tokens past the end of the sequence act as the identity: no decay, no read, no write
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (t0 + I * 16 + i >= Tlen) {
+#pragma unroll
+                    for (int cc = 0; cc < CPT; ++cc) {
+                        in.g[i].v[cc] = 0.f;
+                        in.q[i].v[cc] = from_f32<T>(0.f);
+                        in.k[i].v[cc] = from_f32<T>(0.f);
+                        in.b[i].v[cc] = from_f32<T>(0.f);
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < TPV; ++i) {
+                if (t0 + tgv * TPV + i >= Tlen) {
+                    in.w[i].v[0] = in.w[i].v[1] = from_f32<T>(0.f);
+                    in.v[i].v[0] = in.v[i].v[1] = from_f32<T>(0.f);
+                }
+            }
+        }
         float al[CPT][16], pre[CPT][16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const bool valid = t0 + I * 16 + i < Tlen;
+        for (int i = 0; i < 16; ++i)
 #pragma unroll
-            for (int cc = 0; cc < CPT; ++cc) al[cc][i] = valid ? exp_neg(in.g[i].v[cc]) : 1.f;
-        }
+            for (int cc = 0; cc < CPT; ++cc) al[cc][i] = exp_neg(in.g[i].v[cc]);
         {
             float blkv[CPT];
 #pragma unroll
@@ -294,16 +331,15 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
             float x0[TPV], x1[TPV];
 #pragma unroll
             for (int i = 0; i < TPV; ++i) {
-                const bool valid = t0 + tgv * TPV + i < Tlen;
-                x0[i] = valid ? to_f32(in.w[i].v[0]) * to_f32(in.v[i].v[0]) : 0.f;
-                x1[i] = valid ? to_f32(in.w[i].v[1]) * to_f32(in.v[i].v[1]) : 0.f;
+                x0[i] = to_f32(in.w[i].v[0]) * to_f32(in.v[i].v[0]);
+                x1[i] = to_f32(in.w[i].v[1]) * to_f32(in.v[i].v[1]);
             }
             const int idx = cvp * LC + tgv * TPV;
             store_vec_split<T, TPV>(sWVh + idx, sWVl + idx, x0);
             store_vec_split<T, TPV>(sWVh + idx + LC, sWVl + idx + LC, x1);
         }
         __syncthreads();
-        float blk[CPT][4];
+        float blk[CPT][4], invgc[CPT];
         int strong = 0;
 #pragma unroll
         for (int cc = 0; cc < CPT; ++cc) {
@@ -312,17 +348,17 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
             const float gc = blk[cc][0] * blk[cc][1] * blk[cc][2] * blk[cc][3];
             if (I == 0) sGC[cbase + cc] = gc;
             strong |= !(gc >= 0x1p-64f);
+            invgc[cc] = __builtin_amdgcn_rcpf(gc);
         }
         strong = __syncthreads_or(strong);
 
         // =============== element phase, pass 2: scaled operands ===============
         {
-            float before[CPT], after[CPT], sfx[CPT];  // whole blocks before / after block I; running suffix
+            float before[CPT], after[CPT];  // whole blocks before / after block I
 #pragma unroll
             for (int cc = 0; cc < CPT; ++cc) {
                 before[cc] = 1.f;
                 after[cc] = 1.f;
-                sfx[cc] = 1.f;
 #pragma unroll
                 for (int K = 0; K < 4; ++K) {
                     if (K < I) before[cc] *= blk[cc][K];
@@ -330,49 +366,67 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
                 }
             }
             float bgt[CPT][16], kgt[CPT][16];
+            if (!strong) {
+                // QG = q.Gamma, BG = (b.k).Gamma, KG = k.Gamma' and KI = k / Gamma = KG / Gamma_C
+                float tail[CPT];  // decay from token i+1 to the chunk end
 #pragma unroll
-            for (int i = 15; i >= 0; --i) {
-                const int tl = I * 16 + i;
-                const bool valid = t0 + tl < Tlen;
-                // x: QG, BG, KI for the mild variant; y: level-64 rows/columns, z: level-32 ones
-                float xq[CPT], xb[CPT], xki[CPT], ya[CPT], yp[CPT], za[CPT], zp[CPT];
+                for (int cc = 0; cc < CPT; ++cc) tail[cc] = after[cc];
 #pragma unroll
-                for (int cc = 0; cc < CPT; ++cc) {
-                    const float qv = valid ? to_f32(in.q[i].v[cc]) : 0.f;
-                    const float kv = valid ? to_f32(in.k[i].v[cc]) : 0.f;
-                    const float bk = valid ? to_f32(in.b[i].v[cc]) * kv : 0.f;
-                    const float gam = before[cc] * pre[cc][i];  // Gamma_i  (chunk start -> i)
-                    const float suf = sfx[cc];                 // decay from i to the end of block I
-                    sfx[cc] *= al[cc][i];
-                    xq[cc] = qv * gam;
-                    xb[cc] = bk * gam;
-                    xki[cc] = kv * __builtin_amdgcn_rcpf(gam);
-                    bgt[cc][i] = xb[cc];
-                    kgt[cc][i] = kv * suf * after[cc];         // k . Gamma'_i  (i -> chunk end)
-                    // strong chunks, recursive split at the chunk level:
-                    //  level 64, pivot = token 31: rows i >= 32 scale by Gamma_{i<-31}, columns j <= 31 by Gamma_{31<-j}
-                    //  level 32, pivots 15 and 47: rows of blocks 1, 3 by pre, columns of blocks 0, 2 by suf
-                    if (I >= 2) {
-                        const float f = I == 3 ? blk[cc][2] * pre[cc][i] : pre[cc][i];
-                        ya[cc] = bk * f;
-                        yp[cc] = qv * f;
-                    } else {
-                        ya[cc] = kv * suf * (I == 0 ? blk[cc][1] : 1.f);
-                        yp[cc] = 0.f;
+                for (int i = 15; i >= 0; --i) {
+                    const int tl = I * 16 + i;
+                    float xq[CPT], xb[CPT], xki[CPT];
+#pragma unroll
+                    for (int cc = 0; cc < CPT; ++cc) {
+                        const float kv = to_f32(in.k[i].v[cc]);
+                        const float gam = before[cc] * pre[cc][i];
+                        xq[cc] = to_f32(in.q[i].v[cc]) * gam;
+                        xb[cc] = to_f32(in.b[i].v[cc]) * kv * gam;
+                        kgt[cc][i] = kv * tail[cc];
+                        tail[cc] *= al[cc][i];
+                        xki[cc] = kgt[cc][i] * invgc[cc];
+                        bgt[cc][i] = xb[cc];
                     }
-                    if (I & 1) {
-                        za[cc] = bk * pre[cc][i];
-                        zp[cc] = qv * pre[cc][i];
-                    } else {
-                        za[cc] = kv * suf;
-                        zp[cc] = 0.f;
-                    }
-                }
-                store_vec<T, CPT>(sQG + tl * LDK + cbase, xq);
-                if (!strong) {
+                    store_vec<T, CPT>(sQG + tl * LDK + cbase, xq);
                     store_vec<T, CPT>(sWork + tl * LDK + cbase, xb);          // BG
                     store_vec<T, CPT>(sWork + (64 + tl) * LDK + cbase, xki);  // KI
-                } else {
+                }
+            } else {
+                float sfx[CPT];  // decay from token i+1 to the end of block I
+#pragma unroll
+                for (int cc = 0; cc < CPT; ++cc) sfx[cc] = 1.f;
+#pragma unroll
+                for (int i = 15; i >= 0; --i) {
+                    const int tl = I * 16 + i;
+                    // y: level-64 rows/columns (pivot token 31), z: level-32 ones (pivots 15, 47)
+                    float xq[CPT], ya[CPT], yp[CPT], za[CPT], zp[CPT];
+#pragma unroll
+                    for (int cc = 0; cc < CPT; ++cc) {
+                        const float qv = to_f32(in.q[i].v[cc]);
+                        const float kv = to_f32(in.k[i].v[cc]);
+                        const float bk = to_f32(in.b[i].v[cc]) * kv;
+                        const float gam = before[cc] * pre[cc][i];
+                        const float suf = sfx[cc];
+                        sfx[cc] *= al[cc][i];
+                        xq[cc] = qv * gam;
+                        bgt[cc][i] = bk * gam;
+                        kgt[cc][i] = kv * suf * after[cc];
+                        if (I >= 2) {
+                            const float f = I == 3 ? blk[cc][2] * pre[cc][i] : pre[cc][i];
+                            ya[cc] = bk * f;
+                            yp[cc] = qv * f;
+                        } else {
+                            ya[cc] = kv * suf * (I == 0 ? blk[cc][1] : 1.f);
+                            yp[cc] = 0.f;
+                        }
+                        if (I & 1) {
+                            za[cc] = bk * pre[cc][i];
+                            zp[cc] = qv * pre[cc][i];
+                        } else {
+                            za[cc] = kv * suf;
+                            zp[cc] = 0.f;
+                        }
+                    }
+                    store_vec<T, CPT>(sQG + tl * LDK + cbase, xq);
                     // 16-row groups: g0,g1 A rows (blocks 2,3), g2,g3 P rows, g4,g5 columns (blocks 0,1);
                     // g6,g7 A rows (blocks 1,3), g8,g9 P rows, g10,g11 columns (blocks 0,2)
                     T* wk = sWork + i * LDK + cbase;
@@ -408,25 +462,18 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
                     // pair list (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
                     const int Ib = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
                     const int Jb = p - (Ib * (Ib + 1)) / 2;
+                    // transposed tiles: lane holds A[Ib*16 + l16][Jb*16 + 4*g4 + r], same for P
                     f32x4 accA = zero4(), accP = zero4();
 #pragma unroll
                     for (int kk = 0; kk < DK / 32; ++kk) {
                         const int kc = kk * 32 + g4 * 8;
-                        Frag<T> fb = load_contig(sWork + (64 + Jb * 16 + l16) * LDK + kc);
+                        Frag<T> fk = load_contig(sWork + (64 + Jb * 16 + l16) * LDK + kc);
                         Frag<T> fa = load_contig(sWork + (Ib * 16 + l16) * LDK + kc);
                         Frag<T> fq = load_contig(sQG + (Ib * 16 + l16) * LDK + kc);
-                        mma(accA, fa, fb);
-                        mma(accP, fq, fb);
+                        mma(accA, fk, fa);
+                        mma(accP, fk, fq);
                     }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int i = g4 * 4 + r, j = l16;
-                        const bool lowA = Ib > Jb || i > j;
-                        const bool lowP = Ib > Jb || i >= j;
-                        sA[(Ib * 16 + i) * LA + Jb * 16 + j] = lowA ? accA[r] : 0.f;
-                        const int pidx = (Ib * 16 + i) * LC + Jb * 16 + j;
-                        store_split<T>(sPh + pidx, sPl + pidx, lowP ? accP[r] : 0.f);
-                    }
+                    store_AP<T>(sA, sPh, sPl, Ib, Jb, l16, g4, accA, accP, Ib > Jb ? 0 : 1);
                 }
             }
         } else {
@@ -449,19 +496,13 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
 #pragma unroll
                     for (int kk = 0; kk < DK / 32; ++kk) {
                         const int kc = kk * 32 + g4 * 8;
-                        Frag<T> fb = load_contig(sWork + (gcol * 16 + l16) * LDK + kc);
+                        Frag<T> fk = load_contig(sWork + (gcol * 16 + l16) * LDK + kc);
                         Frag<T> fa = load_contig(sWork + (ga * 16 + l16) * LDK + kc);
                         Frag<T> fq = load_contig(sWork + (gp * 16 + l16) * LDK + kc);
-                        mma(accA, fa, fb);
-                        mma(accP, fq, fb);
+                        mma(accA, fk, fa);
+                        mma(accP, fk, fq);
                     }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int i = g4 * 4 + r;
-                        sA[(Ib * 16 + i) * LA + Jb * 16 + l16] = accA[r];
-                        const int pidx = (Ib * 16 + i) * LC + Jb * 16 + l16;
-                        store_split<T>(sPh + pidx, sPl + pidx, accP[r]);
-                    }
+                    store_AP<T>(sA, sPh, sPl, Ib, Jb, l16, g4, accA, accP, 0);
                 }
             }
             // ---- levels 16, 8, 4, 2 inside the diagonal block I = wave, then P's diagonal ----
@@ -521,33 +562,28 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
                     store_vec<T, CPT>(lv + (32 + i) * LDK + cbase, cl);
                 }
                 __syncthreads();
+                // transposed: lane holds entry (i = l16, j = 4*g4 + r) of the block
                 f32x4 tA = zero4(), tP = zero4();
 #pragma unroll
                 for (int kk = 0; kk < DK / 32; ++kk) {
                     const int kc = kk * 32 + g4 * 8;
-                    Frag<T> fb = load_contig(lv + (32 + l16) * LDK + kc);
+                    Frag<T> fk = load_contig(lv + (32 + l16) * LDK + kc);
                     Frag<T> fq = load_contig(lv + (16 + l16) * LDK + kc);
-                    mma(tP, fq, fb);
+                    mma(tP, fk, fq);
                     if (L < 4) {
                         Frag<T> fa = load_contig(lv + l16 * LDK + kc);
-                        mma(tA, fa, fb);
+                        mma(tA, fk, fa);
                     }
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int i = g4 * 4 + r, j = l16;
+                    const int i = l16, j = g4 * 4 + r;
                     const bool keep = L < 4 ? (i / size == j / size) : (i == j);
                     if (keep) { dA[r] += tA[r]; dP[r] += tP[r]; }
                 }
                 __syncthreads();
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = g4 * 4 + r;
-                sA[(wave * 16 + i) * LA + wave * 16 + l16] = dA[r];
-                const int pidx = (wave * 16 + i) * LC + wave * 16 + l16;
-                store_split<T>(sPh + pidx, sPl + pidx, dP[r]);
-            }
+            store_AP<T>(sA, sPh, sPl, wave, wave, l16, g4, dA, dP, 0);
         }
         __syncthreads();
 
@@ -556,7 +592,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
         // the updates of step m to rows m+1..15 are independent of each other
         if (lane < 16) {
             const int j = lane;
-            const float* Ab = sA + (wave * 16) * LA + wave * 16;
+            const T* Ab = sA + (wave * 16) * LC + wave * 16;
             float x[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
@@ -564,15 +600,13 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
             for (int m = 0; m < 15; ++m) {
                 const float xm = x[m];
 #pragma unroll
-                for (int i = m + 1; i < 16; ++i) x[i] -= Ab[i * LA + m] * xm;
+                for (int i = m + 1; i < 16; ++i) x[i] -= to_f32(Ab[i * LC + m]) * xm;
             }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                sT32[(wave * 16 + i) * LA + wave * 16 + j] = x[i];
-                sTop[(wave * 16 + i) * LC + wave * 16 + j] = from_f32<T>(x[i]);
-            }
+            for (int i = 0; i < 16; ++i) sTop[(wave * 16 + i) * LC + wave * 16 + j] = from_f32<T>(x[i]);
+            store_vec<T, 16>(sTopT + (wave * 16 + j) * LC + wave * 16, x);
         }
-        // clear the operand copy above the diagonal blocks (rows of block I, columns past block I)
+        // clear T above the diagonal blocks (rows of block I, columns past block I)
         for (int x = lane; x < 16 * 64; x += 64) {
             const int i = x >> 6, cidx = x & 63;
             if (cidx >= (wave + 1) * 16) sTop[(wave * 16 + i) * LC + cidx] = from_f32<T>(0.f);
@@ -585,26 +619,19 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
                 const int Jb = wave, Ib = wave + d;
                 f32x4 z = zero4();
                 for (int Kb = Jb; Kb < Ib; ++Kb) {
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        const float a = sA[(Ib * 16 + l16) * LA + Kb * 16 + 4 * s + g4];
-                        const float b = sT32[(Kb * 16 + 4 * s + g4) * LA + Jb * 16 + l16];
-                        mma_f32x4(z, a, b);
-                    }
+                    const Frag16<T> fa = load16(sA + (Ib * 16 + l16) * LC + Kb * 16 + 4 * g4);
+                    const Frag16<T> ft = load16(sTopT + (Jb * 16 + l16) * LC + Kb * 16 + 4 * g4);
+                    mma16(z, fa, ft);
                 }
                 f32x4 tij = zero4();
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    // slot g of step s carries row 4g+s of z, held by this lane in z[s]
-                    const float a = sT32[(Ib * 16 + l16) * LA + Ib * 16 + 4 * g4 + s];
-                    mma_f32x4(tij, a, z[s]);
-                }
+                mma16(tij, load16(sTop + (Ib * 16 + l16) * LC + Ib * 16 + 4 * g4), frag16_from_acc<T>(z));
+                float nt[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int row = Ib * 16 + g4 * 4 + r, colx = Jb * 16 + l16;
-                    sT32[row * LA + colx] = -tij[r];
-                    sTop[row * LC + colx] = from_f32<T>(-tij[r]);
+                    nt[r] = -tij[r];
+                    sTop[(Ib * 16 + g4 * 4 + r) * LC + Jb * 16 + l16] = from_f32<T>(nt[r]);
                 }
+                store_vec<T, 4>(sTopT + (Jb * 16 + l16) * LC + Ib * 16 + g4 * 4, nt);
             }
             __syncthreads();
         }
@@ -614,19 +641,20 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
 
         // =============== W = T (b.k.Gamma), U0 = T (w.v) ===============
         constexpr int WCT = DK / 16 / 4;  // W column tiles per wave
+        // W^T tiles: lane holds W[it*16 + l16][ct*16 + 4*g4 + r]
         f32x4 Wacc[WCT][4];
 #pragma unroll
         for (int a = 0; a < WCT; ++a) {
             const int ct = wave + 4 * a;
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                Wacc[a][rt] = zero4();
+            for (int it = 0; it < 4; ++it) {
+                Wacc[a][it] = zero4();
 #pragma unroll
-                for (int kk = 0; kk <= rt / 2; ++kk) {
+                for (int kk = 0; kk <= it / 2; ++kk) {
                     const int kc = kk * 32 + g4 * 8;
-                    Frag<T> fa = load_contig(sTop + (rt * 16 + l16) * LC + kc);
                     Frag<T> fb = load_contig(sBGT + (ct * 16 + l16) * LC + kc);
-                    mma(Wacc[a][rt], fa, fb);
+                    Frag<T> ft = load_contig(sTop + (it * 16 + l16) * LC + kc);
+                    mma(Wacc[a][it], fb, ft);
                 }
             }
         }
@@ -657,10 +685,10 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
         for (int a = 0; a < WCT; ++a) {
             const int ct = wave + 4 * a;
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sW[(rt * 16 + g4 * 4 + r) * LDK + ct * 16 + l16] = from_f32<T>(Wacc[a][rt][r]);
+            for (int it = 0; it < 4; ++it) {
+                const float x[4] = {Wacc[a][it][0], Wacc[a][it][1], Wacc[a][it][2], Wacc[a][it][3]};
+                store_vec<T, 4>(sW + (it * 16 + l16) * LDK + ct * 16 + g4 * 4, x);
+            }
         }
         __syncthreads();
 

@@ -50,9 +50,50 @@ __device__ __forceinline__ void mma(f32x4& acc, const Frag<float>& a, const Frag
     for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], acc, 0, 0, 0);
 }
 
-// single fp32 MFMA step (16x16x4) for the small triangular solve
+// single fp32 MFMA step (16x16x4)
 __device__ __forceinline__ void mma_f32x4(f32x4& acc, float a, float b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+}
+
+// K = 16 steps: lane l covers row/column l % 16 and contraction slots 4g + e, e = 0..3.  An
+// accumulator (lane holds rows 4g..4g+3) is directly a K = 16 B operand in this map.
+template <typename T> struct Frag16;
+template <> struct Frag16<bf16> { bf16x4 v; };
+template <> struct Frag16<float> { float v[4]; };
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void mma16(f32x4& acc, const Frag16<bf16>& a, const Frag16<bf16>& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a.v),
+                                                    __builtin_bit_cast(s16x4, b.v), acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16(f32x4& acc, const Frag16<float>& a, const Frag16<float>& b) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], acc, 0, 0, 0);
+}
+// four contiguous elements (p aligned to 4 * sizeof(T))
+__device__ __forceinline__ Frag16<bf16> load16(const bf16* p) {
+    Frag16<bf16> f;
+    f.v = *reinterpret_cast<const bf16x4*>(p);
+    return f;
+}
+__device__ __forceinline__ Frag16<float> load16(const float* p) {
+    Frag16<float> f;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f.v[e] = x[e];
+    return f;
+}
+template <typename T> __device__ __forceinline__ Frag16<T> frag16_from_acc(const f32x4& a);
+template <> __device__ __forceinline__ Frag16<bf16> frag16_from_acc<bf16>(const f32x4& a) {
+    Frag16<bf16> f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f.v[e] = (bf16)a[e];
+    return f;
+}
+template <> __device__ __forceinline__ Frag16<float> frag16_from_acc<float>(const f32x4& a) {
+    Frag16<float> f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f.v[e] = a[e];
+    return f;
 }
 
 // contiguous map: p points at element [row][kbase + 8g]; needs 16-byte alignment

@@ -95,7 +95,11 @@ def _active():
 
 
 def default_threads() -> int:
-    return max(1, os.cpu_count() or 1)
+    """Host threads for the pool: OMP_NUM_THREADS when set, else the CPU count, at most 64."""
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        return int(env)
+    return max(1, min(os.cpu_count() or 1, 64))
 
 
 def _f64(x, name):
