@@ -51,7 +51,7 @@ template <typename T, int DK, int DVS>
 struct ChunkCfg {
     static constexpr int C = 64;
     static constexpr int NT = 256;                 // threads per workgroup
-    static constexpr int CPT = DK / 64;            // key channels per thread in the element phase
+    static constexpr int CPL = DK / 16;            // key channels per lane in the element phase
     static constexpr int NCT = DVS / 16;           // 16-wide value column tiles per slice
     static constexpr bool SPLIT = sizeof(T) == 2;  // hi/lo operand pairs for the bf16 path
     static constexpr int NS = SPLIT ? 2 : 1;
@@ -151,13 +151,39 @@ __device__ __forceinline__ void store_vec_split(T* hi, T* lo, const float (&x)[N
     }
 }
 
-// Inputs of one chunk as one thread loads them.
-template <typename T, int CPT, int TPV>
+// Inputs of one chunk as one thread loads them: CPL key channels of 4 tokens, and two
+// value columns of TPV tokens.
+template <typename T, int CPL, int TPV>
 struct ChunkIn {
-    Vec<float, CPT> g[16];
-    Vec<T, CPT> q[16], k[16], b[16];
+    Vec<float, CPL> g[4];
+    Vec<T, CPL> q[4], k[4], b[4];
     Vec<T, 2> w[TPV], v[TPV];
 };
+
+// Column position inside a transposed [channel][token] bf16 tile: 16-byte units (8 tokens) are
+// XOR-swizzled by (row / 16) % 8, so that the element phase's 8-byte stores to rows 8 apart hit
+// distinct LDS banks; the MFMA operand loads of 16 rows share one swizzle value.  fp32 tiles
+// are not swizzled.
+template <typename T>
+__device__ __forceinline__ int swz(int row, int col) {
+    if constexpr (sizeof(T) == 2) return (((col >> 3) ^ ((row >> 4) & 7)) << 3) | (col & 7);
+    else return col;
+}
+
+// permuted-map operand from a swizzled transposed tile (the two 4-element halves separately)
+template <typename T>
+__device__ __forceinline__ Frag<T> load_perm_swz(const T* tile, int row, int ldc, int col) {
+    const T* r = tile + row * ldc;
+    Frag<T> f;
+    if constexpr (sizeof(T) == 2) {
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(r + swz<T>(row, col));
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(r + swz<T>(row, col + 16));
+        f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+        f = load_perm(r + col);
+    }
+    return f;
+}
 
 // Store a transposed 16x16 A/P block pair: lane holds entry (i = l16, j = 4*g4 + r) of block
 // (Ib, Jb).  With diag = 1 the block is on the diagonal: A keeps j < i, P keeps j <= i.
@@ -177,6 +203,149 @@ __device__ __forceinline__ void store_AP(T* sA, T* sPh, T* sPl, int Ib, int Jb, 
     store_vec_split<T, 4>(sPh + pidx, sPl + pidx, p);
 }
 
+// A and P of a strong-decay chunk (some channel decays below 2^-64 over the chunk): the chunk is
+// split recursively at its midpoints and every pair (i, j) is formed at the level whose split
+// point p it straddles, as Gamma_{i<-p} Gamma_{p<-j} with both factors <= 1.  Levels 64 and 32
+// span blocks and read the row/column groups the element phase wrote to the work area; levels 16
+// to 2 lie inside one 16-token block and are formed here.  Kept out of line: it runs only for
+// strong chunks and would otherwise raise the register allocation of the whole loop.
+template <typename T, int DK>
+__device__ __noinline__ void strong_ap(T* sWork, T* sA, T* sPh, T* sPl, const T* __restrict__ q,
+                                   const T* __restrict__ k, const T* __restrict__ bgate,
+                                   const float* __restrict__ log_alpha, int64_t chunk_base,
+                                   int64_t tok_stride_k, int ntok) {
+    constexpr int CPL = DK / 16, PAD = 16 / (int)sizeof(T), LDK = DK + PAD;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int I = wave, ts = lane >> 4, c0 = (lane & 15) * CPL;
+    // ---- strong decay: level 64 (pairs (2,0) (2,1) (3,0) (3,1)) and level 32 ((1,0) (3,2)) ----
+    // wave 0: (2,0) (1,0); wave 1: (2,1) (3,2); wave 2: (3,0); wave 3: (3,1)
+#pragma unroll
+    for (int pi = 0; pi < 2; ++pi) {
+        int Ib = -1, Jb = -1, ga = 0, gp = 0, gcol = 0;
+        if (pi == 0) {
+            Ib = wave < 2 ? 2 : 3;
+            Jb = wave & 1;
+            ga = Ib - 2; gp = Ib; gcol = 4 + Jb;
+        } else if (wave < 2) {
+            Ib = wave == 0 ? 1 : 3;
+            Jb = Ib - 1;
+            ga = 6 + Ib / 2; gp = 8 + Ib / 2; gcol = 10 + Jb / 2;
+        }
+        if (Ib >= 0) {
+            f32x4 accA = zero4(), accP = zero4();
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) {
+                const int kc = kk * 32 + g4 * 8;
+                Frag<T> fk = load_contig(sWork + (gcol * 16 + l16) * LDK + kc);
+                Frag<T> fa = load_contig(sWork + (ga * 16 + l16) * LDK + kc);
+                Frag<T> fq = load_contig(sWork + (gp * 16 + l16) * LDK + kc);
+                mma(accA, fk, fa);
+                mma(accP, fk, fq);
+            }
+            store_AP<T>(sA, sPh, sPl, Ib, Jb, l16, g4, accA, accP, 0);
+        }
+    }
+    // ---- levels 16, 8, 4, 2 inside the diagonal block I = wave, then P's diagonal ----
+    // decays of this lane's tokens, and the 4-token product of the token slot ts ^ 1
+    float al[CPL][4], x16[CPL];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int i = I * 16 + ts * 4 + m;
+        const Vec<float, CPL> g = load_vec<float, CPL>(log_alpha + chunk_base + (int64_t)min(i, ntok - 1) * tok_stride_k + c0);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) al[c][m] = i < ntok ? exp_neg(g.v[c]) : 1.f;
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) x16[c] = __shfl_xor(al[c][0] * al[c][1] * al[c][2] * al[c][3], 16);
+    __syncthreads();  // the level tiles below reuse the work area
+    T* lv = sWork + (wave * 48) * LDK;  // rows: [0,16) A rows, [16,32) P rows, [32,48) columns
+    f32x4 dA = zero4(), dP = zero4();
+#pragma unroll
+    for (int L = 0; L < 5; ++L) {
+        const int size = L < 4 ? (16 >> L) : 1;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int i = ts * 4 + m;  // token within the block
+            // q, k, b of this token, reloaded per level (L2) to keep few registers live
+            const bool valid = I * 16 + i < ntok;
+            const int64_t off = chunk_base + (int64_t)min(I * 16 + i, ntok - 1) * tok_stride_k + c0;
+            const Vec<T, CPL> xq = load_vec<T, CPL>(q + off);
+            const Vec<T, CPL> xk = load_vec<T, CPL>(k + off);
+            const Vec<T, CPL> xb = load_vec<T, CPL>(bgate + off);
+            // split point p of the segment of i (last token of its lower half); a token in the
+            // upper half is a row with factor Gamma_{i<-p}, one in the lower half a column with
+            // factor Gamma_{p<-i}; both are products of at most one lane's decays and x16
+            bool row = false;
+            float f[CPL];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                // products over this lane's tokens up to and including m, and after m
+                const float lpm = m == 0 ? al[c][0] : m == 1 ? al[c][0] * al[c][1]
+                                : m == 2 ? al[c][0] * al[c][1] * al[c][2]
+                                         : al[c][0] * al[c][1] * al[c][2] * al[c][3];
+                const float lsm = m == 3 ? 1.f : m == 2 ? al[c][3] : m == 1 ? al[c][2] * al[c][3]
+                                                                    : al[c][1] * al[c][2] * al[c][3];
+                if (L == 0) {         // p = 7
+                    row = ts >= 2;
+                    f[c] = row ? (ts == 3 ? x16[c] : 1.f) * lpm : lsm * (ts == 0 ? x16[c] : 1.f);
+                } else if (L == 1) {  // p = 3, 11
+                    row = ts & 1;
+                    f[c] = row ? lpm : lsm;
+                } else if (L == 2) {  // p = 4 ts + 1
+                    row = m >= 2;
+                    f[c] = row ? (m == 2 ? al[c][2] : al[c][2] * al[c][3]) : (m == 1 ? 1.f : al[c][1]);
+                } else if (L == 3) {  // p = 4 ts + 2 (m / 2)
+                    row = m & 1;
+                    f[c] = row ? al[c][m] : 1.f;
+                } else {
+                    f[c] = 1.f;
+                }
+            }
+            float ra[CPL], rp[CPL], cl[CPL];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const float qv = valid ? to_f32(xq.v[c]) : 0.f;
+                const float kv = valid ? to_f32(xk.v[c]) : 0.f;
+                const float bk = valid ? to_f32(xb.v[c]) * kv : 0.f;
+                if (L == 4) {
+                    ra[c] = 0.f; rp[c] = qv; cl[c] = kv;
+                } else {
+                    ra[c] = row ? bk * f[c] : 0.f;
+                    rp[c] = row ? qv * f[c] : 0.f;
+                    cl[c] = row ? 0.f : kv * f[c];
+                }
+            }
+            store_vec<T, CPL>(lv + i * LDK + c0, ra);
+            store_vec<T, CPL>(lv + (16 + i) * LDK + c0, rp);
+            store_vec<T, CPL>(lv + (32 + i) * LDK + c0, cl);
+        }
+        __syncthreads();
+        // transposed: lane holds entry (i = l16, j = 4*g4 + r) of the block
+        f32x4 tA = zero4(), tP = zero4();
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) {
+            const int kc = kk * 32 + g4 * 8;
+            Frag<T> fk = load_contig(lv + (32 + l16) * LDK + kc);
+            Frag<T> fq = load_contig(lv + (16 + l16) * LDK + kc);
+            mma(tP, fk, fq);
+            if (L < 4) {
+                Frag<T> fa = load_contig(lv + l16 * LDK + kc);
+                mma(tA, fk, fa);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = l16, j = g4 * 4 + r;
+            const bool keep = L < 4 ? (i / size == j / size) : (i == j);
+            if (keep) { dA[r] += tA[r]; dP[r] += tP[r]; }
+        }
+        __syncthreads();
+    }
+    store_AP<T>(sA, sPh, sPl, wave, wave, l16, g4, dA, dP, 0);
+}
+
 template <typename T, typename OutT, int DK, int DV, int DVS>
 __global__ __launch_bounds__(256) void chunk_fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -184,7 +353,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
     const float* initial_state, OutT* __restrict__ o, float* final_state, int B, int Tlen, int H,
     int nslices, int xcd_map) {
     using Cfg = ChunkCfg<T, DK, DVS>;
-    constexpr int C = Cfg::C, CPT = Cfg::CPT, NCT = Cfg::NCT;
+    constexpr int C = Cfg::C, CPL = Cfg::CPL, NCT = Cfg::NCT;
     constexpr int LDK = Cfg::LDK, LC = Cfg::LC;
     constexpr bool SPLIT = Cfg::SPLIT;
     constexpr int TPV = C * DVS / (2 * Cfg::NT);  // tokens per thread for w.v (two columns each)
@@ -255,22 +424,35 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
     const int64_t tok_stride_v = (int64_t)H * DV;
     const int64_t seq_base_k = ((int64_t)bi * Tlen * H + h) * DK;
     const int64_t seq_base_v = ((int64_t)bi * Tlen * H + h) * DV;
-    const int I = wave;             // 16-token block of this thread in the element phase
-    const int cbase = lane * CPT;   // first key channel of this thread in the element phase
+    // element phase: wave I = 16-token block I; lane = (token slot ts, channel group cg) holds
+    // channels cg*CPL .. +CPL of tokens 4*ts .. 4*ts+3 of the block (one 16-byte load per token)
+    const int I = wave;
+    const int ts = lane >> 4;
+    const int c0 = (lane & 15) * CPL;
     const int cvp = (tid % (DVS / 2)) * 2, tgv = tid / (DVS / 2);  // w.v: column pair, token group
 
     // Every global load of a chunk, issued without a branch: a token past the end
-    // of the sequence reads the last token and is zeroed where it is used.
-    auto load_chunk = [&](int n, ChunkIn<T, CPT, TPV>& in) {
+    // of the sequence reads the last token and is zeroed before use.  The loads come
+    // in two batches (decays and queries; keys, gates and values) so that neither
+    // exceeds what one wave can keep in flight.
+    auto load_first = [&](int n, ChunkIn<T, CPL, TPV>& in) {
         const int t0 = n * C;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int t = min(t0 + I * 16 + i, Tlen - 1);
-            const int64_t off = seq_base_k + (int64_t)t * tok_stride_k + cbase;
-            in.g[i] = load_vec<float, CPT>(log_alpha + off);
-            in.q[i] = load_vec<T, CPT>(q + off);
-            in.k[i] = load_vec<T, CPT>(k + off);
-            in.b[i] = load_vec<T, CPT>(bgate + off);
+        for (int m = 0; m < 4; ++m) {
+            const int t = min(t0 + I * 16 + ts * 4 + m, Tlen - 1);
+            const int64_t off = seq_base_k + (int64_t)t * tok_stride_k + c0;
+            in.g[m] = load_vec<float, CPL>(log_alpha + off);
+            in.q[m] = load_vec<T, CPL>(q + off);
+        }
+    };
+    auto load_second = [&](int n, ChunkIn<T, CPL, TPV>& in) {
+        const int t0 = n * C;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int t = min(t0 + I * 16 + ts * 4 + m, Tlen - 1);
+            const int64_t off = seq_base_k + (int64_t)t * tok_stride_k + c0;
+            in.k[m] = load_vec<T, CPL>(k + off);
+            in.b[m] = load_vec<T, CPL>(bgate + off);
         }
 #pragma unroll
         for (int i = 0; i < TPV; ++i) {
@@ -281,8 +463,9 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
         }
     };
 
-    ChunkIn<T, CPT, TPV> in;
-    load_chunk(0, in);
+    ChunkIn<T, CPL, TPV> in;
+    load_first(0, in);
+    load_second(0, in);
     __syncthreads();
 
     for (int n = 0; n < nchunks; ++n) {
@@ -291,14 +474,14 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
         if (t0 + C > Tlen) {
             // tokens past the end of the sequence act as the identity: no decay, no read, no write
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                if (t0 + I * 16 + i >= Tlen) {
+            for (int m = 0; m < 4; ++m) {
+                if (t0 + I * 16 + ts * 4 + m >= Tlen) {
 #pragma unroll
-                    for (int cc = 0; cc < CPT; ++cc) {
-                        in.g[i].v[cc] = 0.f;
-                        in.q[i].v[cc] = from_f32<T>(0.f);
-                        in.k[i].v[cc] = from_f32<T>(0.f);
-                        in.b[i].v[cc] = from_f32<T>(0.f);
+                    for (int c = 0; c < CPL; ++c) {
+                        in.g[m].v[c] = 0.f;
+                        in.q[m].v[c] = from_f32<T>(0.f);
+                        in.k[m].v[c] = from_f32<T>(0.f);
+                        in.b[m].v[c] = from_f32<T>(0.f);
                     }
                 }
             }
@@ -310,21 +493,40 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
                 }
             }
         }
-        float al[CPT][16], pre[CPT][16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-#pragma unroll
-            for (int cc = 0; cc < CPT; ++cc) al[cc][i] = exp_neg(in.g[i].v[cc]);
+        // al: decays; lp / ls: products over this lane's tokens up to and including m / after m;
+        // x16: the 4-token product of the token slot ts ^ 1 (for the strong variant)
+        float al[CPL][4], pre[CPL][4], suf[CPL][4], x16[CPL];
         {
-            float blkv[CPT];
+            float blkv[CPL];
 #pragma unroll
-            for (int cc = 0; cc < CPT; ++cc) {
+            for (int c = 0; c < CPL; ++c) {
+                float lp[4], ls[4];
                 float p = 1.f;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) { p *= al[cc][i]; pre[cc][i] = p; }
-                blkv[cc] = p;
+                for (int m = 0; m < 4; ++m) {
+                    al[c][m] = exp_neg(in.g[m].v[c]);
+                    p *= al[c][m];
+                    lp[m] = p;
+                }
+                float sfx = 1.f;
+#pragma unroll
+                for (int m = 3; m >= 0; --m) { ls[m] = sfx; sfx *= al[c][m]; }
+                // products of the other token slots of the block (lanes ts ^ 1, ts ^ 2, ts ^ 3)
+                const float lt = p;
+                x16[c] = __shfl_xor(lt, 16);
+                const float x32 = __shfl_xor(lt, 32), x48 = __shfl_xor(lt, 48);
+                // slots before ts: ts & 1 -> slot ts ^ 1, ts & 2 -> slots ts ^ 2, ts ^ 3 (and after ts alike)
+                const float x3248 = x32 * x48;
+                const float ex = ((ts & 1) ? x16[c] : 1.f) * ((ts & 2) ? x3248 : 1.f);
+                const float es = ((ts & 1) ? 1.f : x16[c]) * ((ts & 2) ? 1.f : x3248);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    pre[c][m] = ex * lp[m];  // decay from the block start through token m
+                    suf[c][m] = ls[m] * es;  // decay after token m to the block end
+                }
+                blkv[c] = ex * lt * es;
             }
-            store_vec<float, CPT>(sBLK + I * DK + cbase, blkv);
+            if (ts == 0) store_vec<float, CPL>(sBLK + I * DK + c0, blkv);
         }
         // write gate times value, transposed ([column][token]), hi / lo
         {
@@ -339,121 +541,124 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
             store_vec_split<T, TPV>(sWVh + idx + LC, sWVl + idx + LC, x1);
         }
         __syncthreads();
-        float blk[CPT][4], invgc[CPT];
+        float blk[CPL][4], invgc[CPL];
         int strong = 0;
+        {
+            Vec<float, CPL> bl[4];
 #pragma unroll
-        for (int cc = 0; cc < CPT; ++cc) {
+            for (int K = 0; K < 4; ++K) bl[K] = load_vec<float, CPL>(sBLK + K * DK + c0);
+            float gcv[CPL];
 #pragma unroll
-            for (int K = 0; K < 4; ++K) blk[cc][K] = sBLK[K * DK + cbase + cc];
-            const float gc = blk[cc][0] * blk[cc][1] * blk[cc][2] * blk[cc][3];
-            if (I == 0) sGC[cbase + cc] = gc;
-            strong |= !(gc >= 0x1p-64f);
-            invgc[cc] = __builtin_amdgcn_rcpf(gc);
+            for (int c = 0; c < CPL; ++c) {
+#pragma unroll
+                for (int K = 0; K < 4; ++K) blk[c][K] = bl[K].v[c];
+                gcv[c] = blk[c][0] * blk[c][1] * blk[c][2] * blk[c][3];
+                strong |= !(gcv[c] >= 0x1p-64f);
+                invgc[c] = __builtin_amdgcn_rcpf(gcv[c]);
+            }
+            if (I == 0 && ts == 0) store_vec<float, CPL>(sGC + c0, gcv);
         }
         strong = __syncthreads_or(strong);
 
         // =============== element phase, pass 2: scaled operands ===============
         {
-            float before[CPT], after[CPT];  // whole blocks before / after block I
+            float before[CPL], after[CPL];  // whole blocks before / after block I
 #pragma unroll
-            for (int cc = 0; cc < CPT; ++cc) {
-                before[cc] = 1.f;
-                after[cc] = 1.f;
+            for (int c = 0; c < CPL; ++c) {
+                before[c] = 1.f;
+                after[c] = 1.f;
 #pragma unroll
                 for (int K = 0; K < 4; ++K) {
-                    if (K < I) before[cc] *= blk[cc][K];
-                    if (K > I) after[cc] *= blk[cc][K];
+                    if (K < I) before[c] *= blk[c][K];
+                    if (K > I) after[c] *= blk[c][K];
                 }
             }
-            float bgt[CPT][16], kgt[CPT][16];
+            float bgt[CPL][4], kgt[CPL][4];
             if (!strong) {
                 // QG = q.Gamma, BG = (b.k).Gamma, KG = k.Gamma' and KI = k / Gamma = KG / Gamma_C
-                float tail[CPT];  // decay from token i+1 to the chunk end
 #pragma unroll
-                for (int cc = 0; cc < CPT; ++cc) tail[cc] = after[cc];
+                for (int m = 0; m < 4; ++m) {
+                    const int tl = I * 16 + ts * 4 + m;
+                    float xq[CPL], xb[CPL], xki[CPL];
 #pragma unroll
-                for (int i = 15; i >= 0; --i) {
-                    const int tl = I * 16 + i;
-                    float xq[CPT], xb[CPT], xki[CPT];
-#pragma unroll
-                    for (int cc = 0; cc < CPT; ++cc) {
-                        const float kv = to_f32(in.k[i].v[cc]);
-                        const float gam = before[cc] * pre[cc][i];
-                        xq[cc] = to_f32(in.q[i].v[cc]) * gam;
-                        xb[cc] = to_f32(in.b[i].v[cc]) * kv * gam;
-                        kgt[cc][i] = kv * tail[cc];
-                        tail[cc] *= al[cc][i];
-                        xki[cc] = kgt[cc][i] * invgc[cc];
-                        bgt[cc][i] = xb[cc];
+                    for (int c = 0; c < CPL; ++c) {
+                        const float kv = to_f32(in.k[m].v[c]);
+                        const float gam = before[c] * pre[c][m];
+                        xq[c] = to_f32(in.q[m].v[c]) * gam;
+                        xb[c] = to_f32(in.b[m].v[c]) * kv * gam;
+                        kgt[c][m] = kv * suf[c][m] * after[c];
+                        xki[c] = kgt[c][m] * invgc[c];
+                        bgt[c][m] = xb[c];
                     }
-                    store_vec<T, CPT>(sQG + tl * LDK + cbase, xq);
-                    store_vec<T, CPT>(sWork + tl * LDK + cbase, xb);          // BG
-                    store_vec<T, CPT>(sWork + (64 + tl) * LDK + cbase, xki);  // KI
+                    store_vec<T, CPL>(sQG + tl * LDK + c0, xq);
+                    store_vec<T, CPL>(sWork + tl * LDK + c0, xb);          // BG
+                    store_vec<T, CPL>(sWork + (64 + tl) * LDK + c0, xki);  // KI
                 }
             } else {
-                float sfx[CPT];  // decay from token i+1 to the end of block I
 #pragma unroll
-                for (int cc = 0; cc < CPT; ++cc) sfx[cc] = 1.f;
-#pragma unroll
-                for (int i = 15; i >= 0; --i) {
-                    const int tl = I * 16 + i;
+                for (int m = 0; m < 4; ++m) {
+                    const int tl = I * 16 + ts * 4 + m;
                     // y: level-64 rows/columns (pivot token 31), z: level-32 ones (pivots 15, 47)
-                    float xq[CPT], ya[CPT], yp[CPT], za[CPT], zp[CPT];
+                    float xq[CPL], ya[CPL], yp[CPL], za[CPL], zp[CPL];
 #pragma unroll
-                    for (int cc = 0; cc < CPT; ++cc) {
-                        const float qv = to_f32(in.q[i].v[cc]);
-                        const float kv = to_f32(in.k[i].v[cc]);
-                        const float bk = to_f32(in.b[i].v[cc]) * kv;
-                        const float gam = before[cc] * pre[cc][i];
-                        const float suf = sfx[cc];
-                        sfx[cc] *= al[cc][i];
-                        xq[cc] = qv * gam;
-                        bgt[cc][i] = bk * gam;
-                        kgt[cc][i] = kv * suf * after[cc];
+                    for (int c = 0; c < CPL; ++c) {
+                        const float qv = to_f32(in.q[m].v[c]);
+                        const float kv = to_f32(in.k[m].v[c]);
+                        const float bk = to_f32(in.b[m].v[c]) * kv;
+                        const float gam = before[c] * pre[c][m];
+                        xq[c] = qv * gam;
+                        bgt[c][m] = bk * gam;
+                        kgt[c][m] = kv * suf[c][m] * after[c];
                         if (I >= 2) {
-                            const float f = I == 3 ? blk[cc][2] * pre[cc][i] : pre[cc][i];
-                            ya[cc] = bk * f;
-                            yp[cc] = qv * f;
+                            const float f = I == 3 ? blk[c][2] * pre[c][m] : pre[c][m];
+                            ya[c] = bk * f;
+                            yp[c] = qv * f;
                         } else {
-                            ya[cc] = kv * suf * (I == 0 ? blk[cc][1] : 1.f);
-                            yp[cc] = 0.f;
+                            ya[c] = kv * suf[c][m] * (I == 0 ? blk[c][1] : 1.f);
+                            yp[c] = 0.f;
                         }
                         if (I & 1) {
-                            za[cc] = bk * pre[cc][i];
-                            zp[cc] = qv * pre[cc][i];
+                            za[c] = bk * pre[c][m];
+                            zp[c] = qv * pre[c][m];
                         } else {
-                            za[cc] = kv * suf;
-                            zp[cc] = 0.f;
+                            za[c] = kv * suf[c][m];
+                            zp[c] = 0.f;
                         }
                     }
-                    store_vec<T, CPT>(sQG + tl * LDK + cbase, xq);
+                    store_vec<T, CPL>(sQG + tl * LDK + c0, xq);
                     // 16-row groups: g0,g1 A rows (blocks 2,3), g2,g3 P rows, g4,g5 columns (blocks 0,1);
                     // g6,g7 A rows (blocks 1,3), g8,g9 P rows, g10,g11 columns (blocks 0,2)
-                    T* wk = sWork + i * LDK + cbase;
+                    T* wk = sWork + (ts * 4 + m) * LDK + c0;
                     if (I >= 2) {
-                        store_vec<T, CPT>(wk + (I - 2) * 16 * LDK, ya);
-                        store_vec<T, CPT>(wk + I * 16 * LDK, yp);
+                        store_vec<T, CPL>(wk + (I - 2) * 16 * LDK, ya);
+                        store_vec<T, CPL>(wk + I * 16 * LDK, yp);
                     } else {
-                        store_vec<T, CPT>(wk + (4 + I) * 16 * LDK, ya);
+                        store_vec<T, CPL>(wk + (4 + I) * 16 * LDK, ya);
                     }
                     if (I & 1) {
-                        store_vec<T, CPT>(wk + (6 + I / 2) * 16 * LDK, za);
-                        store_vec<T, CPT>(wk + (8 + I / 2) * 16 * LDK, zp);
+                        store_vec<T, CPL>(wk + (6 + I / 2) * 16 * LDK, za);
+                        store_vec<T, CPL>(wk + (8 + I / 2) * 16 * LDK, zp);
                     } else {
-                        store_vec<T, CPT>(wk + (10 + I / 2) * 16 * LDK, za);
+                        store_vec<T, CPL>(wk + (10 + I / 2) * 16 * LDK, za);
                     }
                 }
             }
 #pragma unroll
-            for (int cc = 0; cc < CPT; ++cc) {
-                store_vec<T, 16>(sBGT + (cbase + cc) * LC + I * 16, bgt[cc]);
-                store_vec<T, 16>(sKGT + (cbase + cc) * LC + I * 16, kgt[cc]);
+            for (int c = 0; c < CPL; ++c) {
+                const int row = c0 + c;
+                store_vec<T, 4>(sBGT + row * LC + swz<T>(row, I * 16 + ts * 4), bgt[c]);
+                store_vec<T, 4>(sKGT + row * LC + swz<T>(row, I * 16 + ts * 4), kgt[c]);
             }
         }
         __syncthreads();
 
+        // decays and queries of the next chunk are loaded while this one finishes (a strong
+        // chunk issues them after its A and P, which need many registers)
+        const int nnext = n + 1 < nchunks ? n + 1 : n;
+
         // =============== A and P ===============
         if (!strong) {
+            load_first(nnext, in);
             // single pivot at the chunk start: A = BG KI^T, P = QG KI^T on the lower blocks
 #pragma unroll
             for (int pi = 0; pi < 3; ++pi) {
@@ -477,113 +682,9 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
                 }
             }
         } else {
-            // ---- strong decay: level 64 (pairs (2,0) (2,1) (3,0) (3,1)) and level 32 ((1,0) (3,2)) ----
-            // wave 0: (2,0) (1,0); wave 1: (2,1) (3,2); wave 2: (3,0); wave 3: (3,1)
-#pragma unroll
-            for (int pi = 0; pi < 2; ++pi) {
-                int Ib = -1, Jb = -1, ga = 0, gp = 0, gcol = 0;
-                if (pi == 0) {
-                    Ib = wave < 2 ? 2 : 3;
-                    Jb = wave & 1;
-                    ga = Ib - 2; gp = Ib; gcol = 4 + Jb;
-                } else if (wave < 2) {
-                    Ib = wave == 0 ? 1 : 3;
-                    Jb = Ib - 1;
-                    ga = 6 + Ib / 2; gp = 8 + Ib / 2; gcol = 10 + Jb / 2;
-                }
-                if (Ib >= 0) {
-                    f32x4 accA = zero4(), accP = zero4();
-#pragma unroll
-                    for (int kk = 0; kk < DK / 32; ++kk) {
-                        const int kc = kk * 32 + g4 * 8;
-                        Frag<T> fk = load_contig(sWork + (gcol * 16 + l16) * LDK + kc);
-                        Frag<T> fa = load_contig(sWork + (ga * 16 + l16) * LDK + kc);
-                        Frag<T> fq = load_contig(sWork + (gp * 16 + l16) * LDK + kc);
-                        mma(accA, fk, fa);
-                        mma(accP, fk, fq);
-                    }
-                    store_AP<T>(sA, sPh, sPl, Ib, Jb, l16, g4, accA, accP, 0);
-                }
-            }
-            // ---- levels 16, 8, 4, 2 inside the diagonal block I = wave, then P's diagonal ----
-            Vec<T, CPT> xq[16], xk[16], xb[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int64_t off = seq_base_k + (int64_t)min(t0 + I * 16 + i, Tlen - 1) * tok_stride_k + cbase;
-                xq[i] = load_vec<T, CPT>(q + off);
-                xk[i] = load_vec<T, CPT>(k + off);
-                xb[i] = load_vec<T, CPT>(bgate + off);
-            }
-            __syncthreads();  // the level tiles below reuse the work area
-            T* lv = sWork + (wave * 48) * LDK;  // rows: [0,16) A rows, [16,32) P rows, [32,48) columns
-            f32x4 dA = zero4(), dP = zero4();
-#pragma unroll
-            for (int L = 0; L < 5; ++L) {
-                const int size = L < 4 ? (16 >> L) : 1;
-                float rf[CPT][16], cf[CPT][16];
-#pragma unroll
-                for (int cc = 0; cc < CPT; ++cc) {
-                    // row factor Gamma_{i<-p} for i in the upper half of its segment,
-                    // column factor Gamma_{p<-j} for j in the lower half (p = last of lower half)
-                    if (L < 4) {
-#pragma unroll
-                        for (int s0 = 0; s0 < 16; s0 += size) {
-                            const int p = s0 + size / 2 - 1;
-                            float f = 1.f;
-#pragma unroll
-                            for (int i = p + 1; i < s0 + size; ++i) { f *= al[cc][i]; rf[cc][i] = f; }
-                            float gcl = 1.f;
-#pragma unroll
-                            for (int i = p; i >= s0; --i) { cf[cc][i] = gcl; gcl *= al[cc][i]; }
-                        }
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const bool valid = t0 + I * 16 + i < Tlen;
-                    float ra[CPT], rp[CPT], cl[CPT];
-#pragma unroll
-                    for (int cc = 0; cc < CPT; ++cc) {
-                        const float qv = valid ? to_f32(xq[i].v[cc]) : 0.f;
-                        const float kv = valid ? to_f32(xk[i].v[cc]) : 0.f;
-                        const float bk = valid ? to_f32(xb[i].v[cc]) * kv : 0.f;
-                        if (L == 4) {
-                            ra[cc] = 0.f; rp[cc] = qv; cl[cc] = kv;
-                        } else {
-                            const int p = (i / size) * size + size / 2 - 1;
-                            const bool row = i > p;
-                            ra[cc] = row ? bk * rf[cc][i] : 0.f;
-                            rp[cc] = row ? qv * rf[cc][i] : 0.f;
-                            cl[cc] = row ? 0.f : kv * cf[cc][i];
-                        }
-                    }
-                    store_vec<T, CPT>(lv + i * LDK + cbase, ra);
-                    store_vec<T, CPT>(lv + (16 + i) * LDK + cbase, rp);
-                    store_vec<T, CPT>(lv + (32 + i) * LDK + cbase, cl);
-                }
-                __syncthreads();
-                // transposed: lane holds entry (i = l16, j = 4*g4 + r) of the block
-                f32x4 tA = zero4(), tP = zero4();
-#pragma unroll
-                for (int kk = 0; kk < DK / 32; ++kk) {
-                    const int kc = kk * 32 + g4 * 8;
-                    Frag<T> fk = load_contig(lv + (32 + l16) * LDK + kc);
-                    Frag<T> fq = load_contig(lv + (16 + l16) * LDK + kc);
-                    mma(tP, fk, fq);
-                    if (L < 4) {
-                        Frag<T> fa = load_contig(lv + l16 * LDK + kc);
-                        mma(tA, fk, fa);
-                    }
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = l16, j = g4 * 4 + r;
-                    const bool keep = L < 4 ? (i / size == j / size) : (i == j);
-                    if (keep) { dA[r] += tA[r]; dP[r] += tP[r]; }
-                }
-                __syncthreads();
-            }
-            store_AP<T>(sA, sPh, sPl, wave, wave, l16, g4, dA, dP, 0);
+            strong_ap<T, DK>(sWork, sA, sPh, sPl, q, k, bgate, log_alpha, seq_base_k + (int64_t)t0 * tok_stride_k,
+                             tok_stride_k, Tlen - t0);
+            load_first(nnext, in);
         }
         __syncthreads();
 
@@ -636,8 +737,8 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
             __syncthreads();
         }
 
-        // the next chunk's inputs are loaded while this one finishes
-        load_chunk(n + 1 < nchunks ? n + 1 : n, in);
+        // the next chunk's keys, gates and values
+        load_second(nnext, in);
 
         // =============== W = T (b.k.Gamma), U0 = T (w.v) ===============
         constexpr int WCT = DK / 16 / 4;  // W column tiles per wave
@@ -652,7 +753,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
 #pragma unroll
                 for (int kk = 0; kk <= it / 2; ++kk) {
                     const int kc = kk * 32 + g4 * 8;
-                    Frag<T> fb = load_contig(sBGT + (ct * 16 + l16) * LC + kc);
+                    Frag<T> fb = load_contig(sBGT + (ct * 16 + l16) * LC + swz<T>(ct * 16 + l16, kc));
                     Frag<T> ft = load_contig(sTop + (it * 16 + l16) * LC + kc);
                     mma(Wacc[a][it], fb, ft);
                 }
@@ -755,7 +856,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
                     for (int r = 0; r < 4; ++r) S[a][st][r] *= gc[st][r];
 #pragma unroll
                     for (int kk = 0; kk < 2; ++kk) {
-                        Frag<T> fk = load_perm(sKGT + (st * 16 + l16) * LC + kk * 32 + g4 * 4);
+                        Frag<T> fk = load_perm_swz(sKGT, st * 16 + l16, LC, kk * 32 + g4 * 4);
                         mma(S[a][st], fk, uf[kk].hi);
                         if constexpr (SPLIT) mma(S[a][st], fk, uf[kk].lo);
                     }

@@ -145,7 +145,8 @@ template <> __device__ __forceinline__ Frag<float> frag_from_acc<float>(const f3
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// N consecutive elements through one aligned vector load (p aligned to N * sizeof(T))
+// N consecutive elements through vector loads (p aligned to 16 bytes or to N * sizeof(T),
+// whichever is smaller)
 template <typename T, int N> struct Vec { T v[N]; };
 template <typename T, int N>
 __device__ __forceinline__ Vec<T, N> load_vec(const T* p) {
@@ -154,7 +155,8 @@ __device__ __forceinline__ Vec<T, N> load_vec(const T* p) {
         r.v[0] = *p;
     } else {
         typedef T V __attribute__((ext_vector_type(N)));
-        const V x = *reinterpret_cast<const V*>(__builtin_assume_aligned(p, N * sizeof(T)));
+        constexpr int AL = N * (int)sizeof(T) < 16 ? N * (int)sizeof(T) : 16;
+        const V x = *reinterpret_cast<const V*>(__builtin_assume_aligned(p, AL));
 #pragma unroll
         for (int i = 0; i < N; ++i) r.v[i] = x[i];
     }
