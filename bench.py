@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 
 METRIC = "GDN-2 chunked fwd tokens/s (T=4K,H=16,d=128); decode state GB/s vs peak"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 
 def chunk_bytes(B, T, H, dk, dv, in_bytes=2, out_bytes=4, with_s0=False):
@@ -37,9 +38,45 @@ def chunk_bytes(B, T, H, dk, dv, in_bytes=2, out_bytes=4, with_s0=False):
     return B * T * H * per_head_token + state
 
 
+def chunk_flops(B, T, H, dk, dv, C=64):
+    """Algorithmic matrix flops of the chunk form per launch (2 per multiply-add): per chunk the
+    C x C products A and P (2 x C*C*dk), W = T(b.k.Gamma) and U = T(w.v) (C*C*(dk+dv)), the
+    triangular inverse (C^3/3), and the state products W S, (q.Gamma) S, k'^T U (3 x C*dk*dv) and
+    P U (C*C*dv)."""
+    nchunks = B * H * ((T + C - 1) // C)
+    per_chunk = 2 * (2 * C * C * dk + C * C * (dk + dv) + C ** 3 // 3 + 3 * C * dk * dv + C * C * dv)
+    return nchunks * per_chunk
+
+
 def decode_bytes(N, H, dk, dv, in_bytes=2, out_bytes=4):
     """Algorithmic HBM bytes of one decode step: state read + written, token vectors, o."""
     return N * H * (2 * dk * dv * 4 + 3 * dk * in_bytes + 2 * dv * in_bytes + dk * 4 + dv * out_bytes)
+
+
+def recorded_traffic(profile, sources):
+    """HBM bytes per launch from a committed counter summary, or None.
+
+    The summary's `traffic-record:` line holds FETCH_SIZE + WRITE_SIZE, scaled
+    by a plain copy of known size, and a hash of the kernel sources that were
+    profiled; the figure is reported only while the sources still hash to it."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", profile)
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for f in sources:
+        with open(os.path.join(ROOT, "gated_delta_rule_gdn2_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    with open(path) as fh:
+        m = re.search(r"^traffic-record: kernel=.* sources=([0-9a-f]+) bytes=(\d+)$", fh.read(), re.M)
+    if m is None or m.group(1) != h.hexdigest()[:len(m.group(1))]:
+        return None
+    return int(m.group(2))
+
+
+CHUNK_PROFILE = ("chunk_fwd_train_B8_T4096_H16_d128.md", ("gdn2_chunk_fwd.hip", "gdn2_device.h"))
+DECODE_PROFILE = ("decode_step_N256_H16_d128.md", ("gdn2_decode.hip", "gdn2_device.h"))
 
 
 def time_launches(fn, steps, warmup, torch):
@@ -120,6 +157,7 @@ def run_decode(args, torch, gdn2, W, dev, out_dtype):
     torch.cuda.empty_cache()
     return {"workload": dwl.name, "us_per_step": dms * 1e3, "state_GBps": dgbps,
             "peak": HBM_PEAK_GBPS, "frac": dgbps / HBM_PEAK_GBPS,
+            "traffic": recorded_traffic(*DECODE_PROFILE) if out_dtype == torch.float32 else None,
             "algorithmic_bytes_per_step": dbytes, "steps": args.decode_steps}
 
 
@@ -133,6 +171,9 @@ def main():
     ap.add_argument("--out-bf16", action="store_true", help="write o in bf16 instead of fp32")
     ap.add_argument("--only", choices=("chunk", "decode"), default=None,
                     help="time one workload only (profiler runs); prints its figures")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="run only a plain device-to-device copy of MIB MiB (--steps times): "
+                         "the reference point that scales the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the GDN-2 recurrence shards over independent "
@@ -149,6 +190,14 @@ def main():
     dev = torch.device("cuda:0")
     out_dtype = torch.bfloat16 if args.out_bf16 else torch.float32
 
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        ms = time_launches(lambda: dst.copy_(src), args.steps, args.warmup, torch)
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "avg_launch_us": ms * 1e3,
+                          "GBps": 2 * n / (ms * 1e-3) / 1e9}))
+        return
     if args.only == "decode":
         print(json.dumps({"decode": run_decode(args, torch, gdn2, W, dev, out_dtype)}))
         return
@@ -160,6 +209,7 @@ def main():
                           "tokens_per_s": tokens / (ms * 1e-3), "achieved_GBps": achieved}))
         return
     dec = run_decode(args, torch, gdn2, W, dev, out_dtype)
+    flops = chunk_flops(wl.B, wl.T, wl.H, wl.dk, wl.dv)
 
     result = {
         "metric": METRIC,
@@ -178,9 +228,13 @@ def main():
                    "chunk": 64, "inputs": "bf16 q,k,v,b,w; fp32 log_alpha",
                    "o_dtype": "bf16" if args.out_bf16 else "f32", "initial_state": "zeros"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": recorded_traffic(*CHUNK_PROFILE) if not args.out_bf16 else None,
                      "kernel": "chunk_fwd_kernel", "algorithmic_bytes_per_launch": nbytes,
-                     "avg_launch_us": ms * 1e3},
+                     "avg_launch_us": ms * 1e3,
+                     "mfma_context": {"algorithmic_flops_per_launch": flops,
+                                      "TFLOPs": flops / (ms * 1e-3) / 1e12,
+                                      "frac_of_bf16_peak": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}},
         "decode": dec,
     }
     if not args.no_cpu_baseline:

@@ -366,3 +366,25 @@ def test_vjp_zero_length_passes_state_gradient_through():
     zv = np.zeros((1, 0, 1, 2))
     gr = oracle.vjp(z, z, zv, z, z, zv, zv, np.zeros((1, 1, 3, 2)), dsT)
     np.testing.assert_array_equal(gr["ds0"], dsT)
+
+
+def test_oracle_matches_its_regression_fixture():
+    """Drift guard (not a pin): sampled outputs stored by tests/golden/make_oracle_regression.py."""
+    import importlib.util
+    import os
+
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    spec = importlib.util.spec_from_file_location("make_oracle_regression",
+                                                  os.path.join(here, "make_oracle_regression.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    _, o, s = mod.compute()
+    n = 0
+    for line in open(os.path.join(here, "oracle_regression_tiny.txt")):
+        if line.startswith("#"):
+            continue
+        kind, a, b_, c, d, val = line.split()
+        x = (o if kind == "o" else s)[int(a), int(b_), int(c), int(d)]
+        assert abs(x - float(val)) <= 1e-13 * max(1.0, abs(float(val))), line
+        n += 1
+    assert n == 60
