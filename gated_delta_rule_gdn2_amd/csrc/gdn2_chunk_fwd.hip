@@ -904,8 +904,7 @@ static hipError_t launch_dvs(const ChunkArgs& a, int dvs) {
 hipError_t launch_chunk_fwd(const ChunkArgs& a, int dvs) {
     if (a.dk != a.dv) return hipErrorInvalidValue;
     if (a.dtype_bf16) {
-        if (a.dk == 128) return a.out_f32 ? launch_dvs<bf16, float, 128>(a, dvs) : launch_dvs<bf16, bf16, 128>(a, dvs);
-        if (a.dk == 64) return a.out_f32 ? launch_dvs<bf16, float, 64>(a, dvs) : launch_dvs<bf16, bf16, 64>(a, dvs);
+        return launch_chunk_bf16(a, dvs);
     } else if (a.dk == 64 && a.out_f32) {
         return launch_dvs<float, float, 64>(a, dvs);
     }

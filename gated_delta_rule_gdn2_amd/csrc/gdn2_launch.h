@@ -39,6 +39,8 @@ struct DecodeArgs {
 
 // dvs: value columns per workgroup slice (16, 32 or 64)
 hipError_t launch_chunk_fwd(const ChunkArgs& a, int dvs);
+// bf16 inputs (dk = dv = 64 or 128)
+hipError_t launch_chunk_bf16(const ChunkArgs& a, int dvs);
 hipError_t launch_decode_step(const DecodeArgs& a);
 
 }  // namespace gdn2
