@@ -81,6 +81,8 @@ gdn2_status_t gdn2_chunk_fwd(const void* q, const void* k, const void* v, const 
         return GDN2_ERR_SHAPE;
     if (!mul_ok(B * H, dk * dv, &ns)) return GDN2_ERR_SHAPE;
     if (B * H * (dv / 16) > UINT_MAX / 2) return GDN2_ERR_SHAPE;
+    // per-lane offsets inside one chunk are formed with 24-bit multiplies of the token stride
+    if (H * dk >= (int64_t(1) << 24) || H * dv >= (int64_t(1) << 24)) return GDN2_ERR_SHAPE;
     const void* ptrs[] = {q, k, v, log_alpha, b, w, initial_state, o, final_state};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return GDN2_ERR_MISALIGNED;

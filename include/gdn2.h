@@ -82,7 +82,8 @@ typedef enum gdn2_status {
  * inputs an F32 output keeps the fp32 accumulation all the way out, a BF16
  * output rounds it once on the store.  Others return GDN2_ERR_UNSUPPORTED.
  * o must not overlap any input; final_state must not overlap any input other
- * than an identical initial_state.
+ * than an identical initial_state.  H * dk and H * dv (the elements between
+ * consecutive tokens of one tensor) must be below 2^24, else GDN2_ERR_SHAPE.
  */
 gdn2_status_t gdn2_chunk_fwd(const void* q, const void* k, const void* v,
                              const float* log_alpha, const void* b, const void* w,

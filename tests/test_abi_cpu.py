@@ -100,6 +100,8 @@ def test_chunk_bad_shapes(lib):
     assert chunk(lib, f, T=0) == ERR_SHAPE
     assert chunk(lib, f, H=-1) == ERR_SHAPE
     assert chunk(lib, f, B=1 << 40, T=1 << 40) == ERR_SHAPE
+    # token stride H * d must stay below 2^24 elements
+    assert chunk(lib, f, H=1 << 17, dk=128, dv=128) == ERR_SHAPE
 
 
 def test_chunk_unsupported(lib):
