@@ -75,7 +75,7 @@ def recorded_traffic(profile, sources):
     return int(m.group(2))
 
 
-CHUNK_PROFILE = ("chunk_fwd_train_B8_T4096_H16_d128.md", ("gdn2_chunk_fwd.hip", "gdn2_device.h"))
+CHUNK_PROFILE = ("chunk_fwd_train_B8_T4096_H16_d128.md", ("gdn2_chunk_bf16.hip", "gdn2_device.h"))
 DECODE_PROFILE = ("decode_step_N256_H16_d128.md", ("gdn2_decode.hip", "gdn2_device.h"))
 
 
@@ -230,7 +230,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": recorded_traffic(*CHUNK_PROFILE) if not args.out_bf16 else None,
-                     "kernel": "chunk_fwd_kernel", "algorithmic_bytes_per_launch": nbytes,
+                     "kernel": "chunk_bf16_kernel", "algorithmic_bytes_per_launch": nbytes,
                      "avg_launch_us": ms * 1e3,
                      "mfma_context": {"algorithmic_flops_per_launch": flops,
                                       "TFLOPs": flops / (ms * 1e-3) / 1e12,

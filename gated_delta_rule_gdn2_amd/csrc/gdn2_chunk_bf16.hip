@@ -27,13 +27,12 @@
 //   * A, P: waves 0-3 form the diagonal block of A in both orientations in fp32
 //     accumulators and invert I + A_II at once by doubling,
 //         (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8),   N strictly lower 16 x 16,
-//     on fp32 MFMAs; waves 4-6 form the off-diagonal blocks.
-//   * W and U0 by block forward substitution down the four 16-row blocks, one 16-column
-//     tile per wave at a time, with (I + A_II)^{-1} and -A_IJ as bf16 MFMA operands:
-//         X_I = (I + A_II)^{-1} (R_I - sum_{J<I} A_IJ X_J).
-//   * state: the fp32 state slice lives in MFMA accumulators of waves 4-7 (16-channel row
-//     tiles); waves 0..DVS/16-1 own one 16-column tile of U0, X = W S, U and O each.  The
-//     two groups exchange S (bf16) and U (hi / lo bf16) through LDS.
+//     with hi + lo bf16 MFMA products; waves 4-6 form the off-diagonal blocks.
+//   * the off-diagonal blocks of T = (I + A)^{-1} through halves of 32 tokens:
+//     T = [[T_A, 0], [T_C, T_B]], T_10 = -T_11 A_10 T_00, T_32 likewise, T_C = -T_B A_BA T_A.
+//   * W = T (b.k.Gamma) and U0 = T (w.v), then the state pass, as independent 16 x 16 tiles
+//     spread over all eight waves; the fp32 state slice lives in MFMA accumulators (four
+//     tiles per wave), and S (bf16) and U (hi / lo bf16) reach the other waves through LDS.
 // Operands that are not bf16 numbers themselves (w.v through U0, U, P) enter the MFMAs as
 // hi + lo bf16 pairs; every product accumulates in fp32.
 
@@ -195,31 +194,37 @@ __device__ __forceinline__ int opq(int x) {
     return x;
 }
 
-// acc + X Y for 16 x 16 fp32 matrices, on fp32 MFMAs.  xt: X^T in accumulator layout (lane
-// (m, g) holds X[m][4g + r]); y: Y in accumulator layout (lane (n, g) holds Y[4g + r][n]).
-__device__ __forceinline__ f32x4 mm16f(f32x4 acc, const f32x4& xt, const f32x4& y) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xt[e], y[e], acc, 0, 0, 0);
+// acc + X Y for 16 x 16 matrices, with both factors as hi + lo bf16 pairs (three bf16 MFMAs;
+// the lo * lo term, below 2^-16 of the product, is dropped).  xt: X^T in accumulator layout
+// (lane (m, g) holds X[m][4g + r]); y: Y in accumulator layout (lane (n, g) holds Y[4g + r][n]).
+__device__ __forceinline__ f32x4 mm16s(f32x4 acc, const Split16& xt, const Split16& y) {
+    mma16(acc, xt.hi, y.hi);
+    mma16(acc, xt.hi, y.lo);
+    mma16(acc, xt.lo, y.hi);
     return acc;
 }
 
 // (I + N)^{-1} for a strictly lower triangular 16 x 16 N.  N is nilpotent (N^16 = 0), so
 // the inverse is the finite sum of (-N)^n, n < 16, which factors as
 // (I - N)(I + N^2)(I + N^4)(I + N^8).  nt: lane (i, g) holds N[i][4g + r]; n: lane (j, g)
-// holds N[4g + r][j].  Returns T = (I + N)^{-1} as lane (i, g) holding T[i][4g + r].
+// holds N[4g + r][j].  Returns T = (I + N)^{-1} as lane (i, g) holding T[i][4g + r]; the
+// products carry about 16 significant bits, more than the bf16 T they feed.
 __device__ __forceinline__ f32x4 unit_lower_inverse(const f32x4& nt, const f32x4& n, int l16, int g4) {
-    const f32x4 n2 = mm16f(zero4(), nt, n);     // N^2
-    const f32x4 n2t = mm16f(zero4(), n, nt);    // (N^2)^T
-    const f32x4 n4 = mm16f(zero4(), n2t, n2);   // N^4
-    const f32x4 n4t = mm16f(zero4(), n2, n2t);  // (N^4)^T
-    const f32x4 n8 = mm16f(zero4(), n4t, n4);   // N^8
-    // t holds T_m^T in accumulator layout; T_2m^T = T_m^T + (N^m')^T T_m^T with m' = 2m
+    const Split16 s1t = split16(nt), s1 = split16(n);
+    const f32x4 n2 = mm16s(zero4(), s1t, s1);   // N^2
+    const f32x4 n2t = mm16s(zero4(), s1, s1t);  // (N^2)^T
+    const Split16 s2 = split16(n2), s2t = split16(n2t);
+    const f32x4 n4 = mm16s(zero4(), s2t, s2);   // N^4
+    const f32x4 n4t = mm16s(zero4(), s2, s2t);  // (N^4)^T
+    const Split16 s4 = split16(n4), s4t = split16(n4t);
+    const Split16 s8 = split16(mm16s(zero4(), s4t, s4));  // N^8
+    // t holds T_m^T in accumulator layout; T_2m^T = T_m^T + (N^2m)^T T_m^T
     f32x4 t;
 #pragma unroll
     for (int r = 0; r < 4; ++r) t[r] = (4 * g4 + r == l16 ? 1.f : 0.f) - nt[r];
-    t = mm16f(t, n2, t);
-    t = mm16f(t, n4, t);
-    t = mm16f(t, n8, t);
+    t = mm16s(t, s2, split16(t));
+    t = mm16s(t, s4, split16(t));
+    t = mm16s(t, s8, split16(t));
     return t;
 }
 
@@ -481,6 +486,8 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
     // addresses: a per-chunk base pointer (uniform) plus a per-lane offset within the chunk,
     // (token * H * D + channel) * element size, which the host keeps below 2^24 * 4 bytes
     const int rsk = H * DK, rsv = H * DV;  // elements between consecutive tokens
+    // The next chunk's inputs are loaded in two batches (decays and queries; keys, gates and
+    // values), issued well before they are needed.
     auto load_first = [&](int n, In<CPL, TPV, VC>& in) {
         const int t0 = n * C, last = Tlen - 1 - t0;
         const int64_t cb = seq_base_k + (int64_t)t0 * tok_stride_k;
@@ -522,6 +529,7 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
 
     for (int n = 0; n < nchunks; ++n) {
         const int t0 = n * C;
+        const int nnext = n + 1 < nchunks ? n + 1 : n;
         // lane-derived indices, recomputed every chunk: values derived from them are then
         // formed where they are used instead of being kept live (or spilled) across the loop
         const int tidv = opq(tid);
@@ -555,34 +563,30 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                 }
             }
         }
-        // pre: decay from the block start through token m; suf: after token m to the block end
-        float pre[CPL][4], suf[CPL][4];
+        // decay from the block start through token m = ex * lp[m]; after token m to the block
+        // end = ls[m] * es (lp, ls: this lane's 4 tokens; ex, es: the block's other token slots)
+        float lp[CPL][4], ls[CPL][4], ex[CPL], es[CPL];
         {
             float blkv[CPL];
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
-                float al[4], lp[4], ls[4];
+                float al[4];
                 float p = 1.f;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     al[m] = exp_neg(in.g[m].v[c]);
                     p *= al[m];
-                    lp[m] = p;
+                    lp[c][m] = p;
                 }
                 float sfx = 1.f;
 #pragma unroll
-                for (int m = 3; m >= 0; --m) { ls[m] = sfx; sfx *= al[m]; }
+                for (int m = 3; m >= 0; --m) { ls[c][m] = sfx; sfx *= al[m]; }
                 // products of the other token slots of the block (lanes ts ^ 1, ts ^ 2, ts ^ 3)
                 const float x16 = __shfl_xor(p, 16), x32 = __shfl_xor(p, 32), x48 = __shfl_xor(p, 48);
                 const float x3248 = x32 * x48;
-                const float ex = ((ts & 1) ? x16 : 1.f) * ((ts & 2) ? x3248 : 1.f);
-                const float es = ((ts & 1) ? 1.f : x16) * ((ts & 2) ? 1.f : x3248);
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    pre[c][m] = ex * lp[m];
-                    suf[c][m] = ls[m] * es;
-                }
-                blkv[c] = ex * p * es;
+                ex[c] = ((ts & 1) ? x16 : 1.f) * ((ts & 2) ? x3248 : 1.f);
+                es[c] = ((ts & 1) ? 1.f : x16) * ((ts & 2) ? 1.f : x3248);
+                blkv[c] = ex[c] * p * es[c];
             }
             // A chunk is mild when every channel's whole-chunk decay is at least 2^-64; a
             // sufficient test that needs no second exchange: every 16-token block >= 2^-16.
@@ -664,16 +668,22 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                 // QG = q.Gamma, BG = (b.k).Gamma, KG = k.Gamma' and KI = k / Gamma = KG / Gamma_C
                 const int eb = opq(((I * 16 + ts * 4) * LDK + c0) * 2);
                 const int ebx = opq(eb + G::RX);
+                float bex[CPL], esa[CPL];
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    bex[c] = before[c] * ex[c];
+                    esa[c] = es[c] * after[c];
+                }
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     float xq[CPL], xb[CPL], xki[CPL];
 #pragma unroll
                     for (int c = 0; c < CPL; ++c) {
                         const float kv = (float)in.k[m].v[c];
-                        const float gam = before[c] * pre[c][m];
+                        const float gam = bex[c] * lp[c][m];
                         xq[c] = (float)in.q[m].v[c] * gam;
                         xb[c] = (float)in.b[m].v[c] * kv * gam;
-                        kgt[c][m] = kv * suf[c][m] * after[c];
+                        kgt[c][m] = kv * (ls[c][m] * esa[c]);
                         xki[c] = kgt[c][m] * invgc[c];
                         bgt[c][m] = xb[c];
                     }
@@ -684,6 +694,14 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
             } else {
                 const int eb = opq(((I * 16 + ts * 4) * LDK + c0) * 2);
                 const int wkb = opq(G::RX + (ts * 4 * LDK + c0) * 2);
+                float pre[CPL][4], suf[CPL][4];
+#pragma unroll
+                for (int c = 0; c < CPL; ++c)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        pre[c][m] = ex[c] * lp[c][m];
+                        suf[c][m] = ls[c][m] * es[c];
+                    }
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     // y: level-64 rows/columns (pivot token 31), z: level-32 ones (pivots 15, 47)
@@ -741,7 +759,6 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
         }
         lds_barrier();
 
-        const int nnext = n + 1 < nchunks ? n + 1 : n;
 
         // =============== A, P and the diagonal blocks of T = (I + A)^{-1} ===============
         if (!strong) {
@@ -749,13 +766,15 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
             // single pivot at the chunk start: A = BG KI^T, P = QG KI^T on the lower blocks
             if (wave < 4) {
                 // diagonal block I = wave: A_II in both orientations, then its inverse
-                f32x4 nt = zero4(), nn = zero4();
-                const int rkx = opq(G::RX + ((wave * 16 + l16) * LDK + g4 * 8) * 2);
-                Frag<bf16> fk[DK / 32], fa[DK / 32];
+                f32x4 nt = zero4(), nn = zero4(), pd = zero4();
+                const int rk = opq(((wave * 16 + l16) * LDK + g4 * 8) * 2);
+                const int rkx = opq(rk + G::RX);
+                Frag<bf16> fk[DK / 32], fa[DK / 32], fq[DK / 32];
 #pragma unroll
                 for (int kk = 0; kk < DK / 32; ++kk) {
                     fk[kk] = load_contig(B16(rkx + C * LDK * 2 + kk * 64));
                     fa[kk] = load_contig(B16(rkx + kk * 64));
+                    fq[kk] = load_contig(B16(rk + kk * 64));
                 }
                 sched_fence();
 #pragma unroll
@@ -764,20 +783,26 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                     mma(nn, fa[kk], fk[kk]);  // lane holds A[4 g4 + r][l16]
                 }
 #pragma unroll
+                for (int kk = 0; kk < DK / 32; ++kk) mma(pd, fk[kk], fq[kk]);  // P[l16][4 g4 + r]
+                float pp[4];
+#pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int j = 4 * g4 + r;
                     nt[r] = j < l16 ? nt[r] : 0.f;
                     nn[r] = j > l16 ? nn[r] : 0.f;
+                    pp[r] = j <= l16 ? pd[r] : 0.f;
                 }
+                const int idx = (wave * 16 + l16) * LC + wave * 16 + g4 * 4;
+                store_bf16_split<4>(sPh + idx, sPl + idx, pp);
                 store_tdiag<G>(smem, wave, l16, g4, unit_lower_inverse(nt, nn, l16, g4));
             } else if (wave < 7) {
-                // off-diagonal pairs: wave 4: (1,0) (2,0); wave 5: (2,1) (3,0); wave 6: (3,1) (3,2)
+                // off-diagonal pairs, two per wave sharing a block row or column:
+                // wave 4: (1,0) (2,0); wave 5: (2,1) (3,1); wave 6: (3,0) (3,2)
                 const int rl = opq((l16 * LDK + g4 * 8) * 2);
 #pragma unroll
                 for (int pi = 0; pi < 2; ++pi) {
-                    const int p = 2 * (wave - 4) + pi;
-                    const int Ib = p < 1 ? 1 : p < 3 ? 2 : 3;
-                    const int Jb = p - (Ib * (Ib - 1)) / 2;
+                    const int Ib = wave == 4 ? 1 + pi : wave == 5 ? 2 + pi : 3;
+                    const int Jb = wave == 4 ? 0 : wave == 5 ? 1 : 2 * pi;
                     f32x4 accA = zero4(), accP = zero4();
                     Frag<bf16> fk[DK / 32], fa[DK / 32], fq[DK / 32];
 #pragma unroll
@@ -799,27 +824,6 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                     store_bf16<4>(sA + idx, a);
                     store_bf16_split<4>(sPh + idx, sPl + idx, pp);
                 }
-            } else {
-                // wave 7: the diagonal blocks of P
-                const int rl = opq((l16 * LDK + g4 * 8) * 2);
-#pragma unroll
-                for (int Ib = 0; Ib < 4; ++Ib) {
-                    f32x4 accP = zero4();
-                    Frag<bf16> fk[DK / 32], fq[DK / 32];
-#pragma unroll
-                    for (int kk = 0; kk < DK / 32; ++kk) {
-                        fk[kk] = load_contig(B16(rl + G::RX + (C + Ib * 16) * LDK * 2 + kk * 64));
-                        fq[kk] = load_contig(B16(rl + Ib * 16 * LDK * 2 + kk * 64));
-                    }
-                    sched_fence();
-#pragma unroll
-                    for (int kk = 0; kk < DK / 32; ++kk) mma(accP, fk[kk], fq[kk]);  // P[l16][4 g4 + r]
-                    float pp[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) pp[r] = 4 * g4 + r <= l16 ? accP[r] : 0.f;
-                    const int idx = (Ib * 16 + l16) * LC + Ib * 16 + g4 * 4;
-                    store_bf16_split<4>(sPh + idx, sPl + idx, pp);
-                }
             }
         } else {
             strong_ap<DK, DVS>(smem, q, k, bgate, log_alpha, seq_base_k + (int64_t)t0 * tok_stride_k, tok_stride_k,
@@ -835,11 +839,13 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
         if (wave < 2) {
             const int J = 2 * wave, Ib = J + 1;
             const int tb = opq((l16 * LC + g4 * 4) * 2);
-            f32x4 z = zero4();
-            mma16(z, load16(B16(G::AM + tb + (Ib * 16 * LC + J * 16) * 2)),
-                  load16(B16(G::TTR + tb + (J * 16 * LC + J * 16) * 2)));
-            const Frag16<bf16> zf = frag16_from_acc<bf16>(z);
+            const Frag16<bf16> fa = load16(B16(G::AM + tb + (Ib * 16 * LC + J * 16) * 2));
+            const Frag16<bf16> fj = load16(B16(G::TTR + tb + (J * 16 * LC + J * 16) * 2));
             const Frag16<bf16> ft = load16(B16(G::TR + tb + (Ib * 16 * LC + Ib * 16) * 2));
+            sched_fence();
+            f32x4 z = zero4();
+            mma16(z, fa, fj);
+            const Frag16<bf16> zf = frag16_from_acc<bf16>(z);
             if (wave == 0) {
                 // T_10 in the orientation of T^T (lane (n, g): T_10[4 g + r][n]), T_10 rows scattered
                 f32x4 t = zero4();
@@ -859,33 +865,46 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
             }
         }
         lds_barrier();
-        if (wave < 2) {
-            // column J of T_C: Z = (-A_BA) T_A[:, J], then T_2J = T_22 Z_2, T_3J = T_32 Z_2 + T_33 Z_3,
-            // formed transposed so that lane (i, g) holds a row: T_xJ[i][4 g + r]
-            const int J = wave;
+        if (wave < 4) {
+            // block (R, J) of T_C, one per wave: Z_xJ = (-A_x0) T_0J + (-A_x1) T_1J, then
+            // T_2J = T_22 Z_2J and T_3J = T_32 Z_2J + T_33 Z_3J, formed transposed so that
+            // lane (i, g) holds a row: T_RJ[i][4 g + r]
+            const int J = wave & 1, R = 2 + (wave >> 1);
             const int tb = opq((l16 * LC + g4 * 4) * 2);
+            Frag16<bf16> tf[2], a2[2], a3[2];
+#pragma unroll
+            for (int K = 0; K < 2; ++K) {
+                if (K < J) continue;
+                tf[K] = load16(B16(G::TTR + tb + (J * 16 * LC + K * 16) * 2));
+                a2[K] = load16(B16(G::AM + tb + (32 * LC + K * 16) * 2));
+                a3[K] = load16(B16(G::AM + tb + (48 * LC + K * 16) * 2));
+            }
+            const Frag16<bf16> t22 = load16(B16(G::TR + tb + (32 * LC + 32) * 2));
+            const Frag16<bf16> t32 = load16(B16(G::TR + tb + (48 * LC + 32) * 2));
+            const Frag16<bf16> t33 = load16(B16(G::TR + tb + (48 * LC + 48) * 2));
+            sched_fence();
             f32x4 z2 = zero4(), z3 = zero4();
 #pragma unroll
             for (int K = 0; K < 2; ++K) {
                 if (K < J) continue;
-                const Frag16<bf16> tf = load16(B16(G::TTR + tb + (J * 16 * LC + K * 16) * 2));
-                mma16(z2, load16(B16(G::AM + tb + (32 * LC + K * 16) * 2)), tf);
-                mma16(z3, load16(B16(G::AM + tb + (48 * LC + K * 16) * 2)), tf);
+                mma16(z2, a2[K], tf[K]);
+                if (R == 3) mma16(z3, a3[K], tf[K]);
             }
-            const Frag16<bf16> z2f = frag16_from_acc<bf16>(z2), z3f = frag16_from_acc<bf16>(z3);
-            f32x4 t2 = zero4(), t3 = zero4();
-            mma16(t2, z2f, load16(B16(G::TR + tb + (32 * LC + 32) * 2)));
-            mma16(t3, z2f, load16(B16(G::TR + tb + (48 * LC + 32) * 2)));
-            mma16(t3, z3f, load16(B16(G::TR + tb + (48 * LC + 48) * 2)));
-            float x2[4], x3[4];
-            acc_to_array(t2, x2);
-            acc_to_array(t3, x3);
-            store_bf16<4>(B16(G::TR + tb + (32 * LC + J * 16) * 2), x2);
-            store_bf16<4>(B16(G::TR + tb + (48 * LC + J * 16) * 2), x3);
+            const Frag16<bf16> z2f = frag16_from_acc<bf16>(z2);
+            f32x4 t = zero4();
+            if (R == 2) {
+                mma16(t, z2f, t22);
+            } else {
+                mma16(t, z2f, t32);
+                mma16(t, frag16_from_acc<bf16>(z3), t33);
+            }
+            float x[4];
+            acc_to_array(t, x);
+            store_bf16<4>(B16(G::TR + tb + (R * 16 * LC + J * 16) * 2), x);
         }
-
         // the next chunk's keys, gates and values
         load_second(nnext, in);
+
         lds_barrier();
 
         // =============== W = T (b.k.Gamma), U0 = T (w.v); bf16 copy of the state ===============
@@ -979,13 +998,16 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
         f32x4 Y[UPW];
         if (uo_owner) {
             const int rw = opq((l16 * LDK + g4 * 8) * 2);
-            Frag<bf16> sf[UPW][DK / 32], fw[UPW][DK / 32], fq[UPW][DK / 32];
+            // every tile of this wave has column tile wave % NCT
+            const int ctw = wave % NCT;
+            Frag<bf16> sf[DK / 32], fw[UPW][DK / 32], fq[UPW][DK / 32];
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) sf[kk] = load_contig(B16(G::SBT + rw + (ctw * 16 * LDK + kk * 32) * 2));
 #pragma unroll
             for (int i = 0; i < UPW; ++i) {
-                const int u = wave + 8 * i, ct = u % NCT, rt = u / NCT;
+                const int rt = (wave + 8 * i) / NCT;
 #pragma unroll
                 for (int kk = 0; kk < DK / 32; ++kk) {
-                    sf[i][kk] = load_contig(B16(G::SBT + rw + (ct * 16 * LDK + kk * 32) * 2));
                     fw[i][kk] = load_contig(B16(G::RX + rw + (rt * 16 * LDK + kk * 32) * 2));
                     fq[i][kk] = load_contig(B16(rw + (rt * 16 * LDK + kk * 32) * 2));
                 }
@@ -998,8 +1020,8 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                 Y[i] = zero4();
 #pragma unroll
                 for (int kk = 0; kk < DK / 32; ++kk) {
-                    mma(X, fw[i][kk], sf[i][kk]);
-                    mma(Y[i], sf[i][kk], fq[i][kk]);
+                    mma(X, fw[i][kk], sf[kk]);
+                    mma(Y[i], sf[kk], fq[i][kk]);
                 }
                 U[i] -= X;
                 float x[4];
@@ -1011,17 +1033,25 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
         lds_barrier();
         if (uo_owner) {
             const int rl = opq((l16 * LC + g4 * 8) * 2);
-            Frag<bf16> uh[UPW][2], ul[UPW][2], ph[UPW][2], pl[UPW][2];
+            // every tile of this wave has column tile wave % NCT; the last tile has the most rows
+            const int ctw = wave % NCT;
+            constexpr int KKU = 2;
+            const int kku = ((wave + 8 * (UPW - 1)) / NCT) / 2 + 1;  // U fragments the tiles use
+            Frag<bf16> uh[KKU], ul[KKU], ph[UPW][2], pl[UPW][2];
+#pragma unroll
+            for (int kk = 0; kk < KKU; ++kk) {
+                if (kk >= kku) continue;
+                const int uo = G::BGT + rl + (ctw * 16 * LC + kk * 32) * 2;
+                uh[kk] = load_contig(B16(uo));
+                ul[kk] = load_contig(B16(uo + DVS * LC * 2));
+            }
 #pragma unroll
             for (int i = 0; i < UPW; ++i) {
-                const int u = wave + 8 * i, ct = u % NCT, rt = u / NCT;
+                const int rt = (wave + 8 * i) / NCT;
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
                     if (kk > rt / 2) continue;
-                    const int uo = G::BGT + rl + (ct * 16 * LC + kk * 32) * 2;
                     const int po = G::PM + rl + (rt * 16 * LC + kk * 32) * 2;
-                    uh[i][kk] = load_contig(B16(uo));
-                    ul[i][kk] = load_contig(B16(uo + DVS * LC * 2));
                     ph[i][kk] = load_contig(B16(po));
                     pl[i][kk] = load_contig(B16(po + C * LC * 2));
                 }
@@ -1034,9 +1064,9 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
                     if (kk > rt / 2) continue;
-                    mma(Y[i], uh[i][kk], ph[i][kk]);
-                    mma(Y[i], ul[i][kk], ph[i][kk]);
-                    mma(Y[i], uh[i][kk], pl[i][kk]);
+                    mma(Y[i], uh[kk], ph[i][kk]);
+                    mma(Y[i], ul[kk], ph[i][kk]);
+                    mma(Y[i], uh[kk], pl[i][kk]);
                 }
                 if (t0 + rt * 16 + l16 < Tlen) {
                     const uint32_t e = __umul24(rt * 16 + l16, rsv) + ct * 16 + g4 * 4;
@@ -1053,15 +1083,18 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
         }
         if (state_owner) {
             const int rl = opq((l16 * LC + g4 * 8) * 2);
-            Frag<bf16> fk[SPW][2], fh[SPW][2], fl[SPW][2];
+            // every state tile of this wave has row tile wave % KT
+            const int stw = wave % KT;
+            const int y = (g4 ^ stw) & 7;  // swizzle of row 16 st + l16: unit (4 kk + g4) ^ st
+            const int kb = opq(G::KGT + (stw * 16 + l16) * LC * 2);
+            Frag<bf16> fk[2], fh[SPW][2], fl[SPW][2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) fk[kk] = load_contig(B16(kb + (((4 * kk) ^ y) << 4)));
 #pragma unroll
             for (int i = 0; i < SPW; ++i) {
-                const int st = (wave + 8 * i) % KT, ct = (wave + 8 * i) / KT;
-                const int y = (g4 ^ st) & 7;  // swizzle of row 16 st + l16: unit (4 kk + g4) ^ st
-                const int kb = opq(G::KGT + (st * 16 + l16) * LC * 2);
+                const int ct = (wave + 8 * i) / KT;
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    fk[i][kk] = load_contig(B16(kb + (((4 * kk) ^ y) << 4)));
                     const int uo = G::BGT + rl + (ct * 16 * LC + kk * 32) * 2;
                     fh[i][kk] = load_contig(B16(uo));
                     fl[i][kk] = load_contig(B16(uo + DVS * LC * 2));
@@ -1074,8 +1107,8 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                 S[i] *= *reinterpret_cast<const f32x4*>(sGC + st * 16 + g4 * 4);
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    mma(S[i], fk[i][kk], fh[i][kk]);
-                    mma(S[i], fk[i][kk], fl[i][kk]);
+                    mma(S[i], fk[kk], fh[i][kk]);
+                    mma(S[i], fk[kk], fl[i][kk]);
                 }
             }
         }
