@@ -134,6 +134,34 @@ def run_chunk(args, torch, gdn2, W, dev, out_dtype):
     return ms, wl, nbytes
 
 
+def run_prefill(args, torch, gdn2, W, dev, out_dtype):
+    """Serving prefill: 64 prompts of a seeded length mix packed along one token axis, with
+    continuation states, through the packed-sequence forward."""
+    wl = W.SERVE_PREFILL
+    lengths = W.make_lengths(wl.B, wl.seed)
+    inp = W.make_packed_inputs(wl, lengths)
+    d = {n: (None if x is None else x.to(dev)) for n, x in inp.items()}
+    del inp
+    total = sum(lengths)
+    o = torch.empty((total, wl.H, wl.dv), dtype=out_dtype, device=dev)
+    sT = torch.empty((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=dev)
+
+    def step():
+        gdn2.chunk_fwd_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["cu_seqlens"],
+                              d["s0"], o=o, final_state=sT, out_dtype=out_dtype)
+
+    ms = time_launches(step, args.steps, args.warmup, torch)
+    per_tok = 3 * wl.dk * 2 + 2 * wl.dv * 2 + wl.dk * 4 + wl.dv * out_dtype.itemsize
+    nbytes = total * wl.H * per_tok + 2 * wl.B * wl.H * wl.dk * wl.dv * 4 + (wl.B + 1) * 8
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    del d, o, sT
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "sequences": wl.B, "tokens": total,
+            "lengths": "log-normal around 512 (sigma 1), clipped to [1, 4096], seed %d" % wl.seed,
+            "us_per_launch": ms * 1e3, "tokens_per_s": total / (ms * 1e-3), "GBps": gbps,
+            "peak": HBM_PEAK_GBPS, "frac": gbps / HBM_PEAK_GBPS, "algorithmic_bytes_per_launch": nbytes}
+
+
 def run_decode(args, torch, gdn2, W, dev, out_dtype):
     """Decode workload: N=256 sequences x H=16, one token per step, state updated in place."""
     dwl = W.DECODE
@@ -169,7 +197,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out-bf16", action="store_true", help="write o in bf16 instead of fp32")
-    ap.add_argument("--only", choices=("chunk", "decode"), default=None,
+    ap.add_argument("--only", choices=("chunk", "decode", "prefill"), default=None,
                     help="time one workload only (profiler runs); prints its figures")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run only a plain device-to-device copy of MIB MiB (--steps times): "
@@ -201,6 +229,9 @@ def main():
     if args.only == "decode":
         print(json.dumps({"decode": run_decode(args, torch, gdn2, W, dev, out_dtype)}))
         return
+    if args.only == "prefill":
+        print(json.dumps({"prefill_varlen": run_prefill(args, torch, gdn2, W, dev, out_dtype)}))
+        return
     ms, wl, nbytes = run_chunk(args, torch, gdn2, W, dev, out_dtype)
     tokens = wl.B * wl.T
     achieved = nbytes / (ms * 1e-3) / 1e9
@@ -209,6 +240,7 @@ def main():
                           "tokens_per_s": tokens / (ms * 1e-3), "achieved_GBps": achieved}))
         return
     dec = run_decode(args, torch, gdn2, W, dev, out_dtype)
+    pre = run_prefill(args, torch, gdn2, W, dev, out_dtype)
     flops = chunk_flops(wl.B, wl.T, wl.H, wl.dk, wl.dv)
 
     result = {
@@ -236,6 +268,7 @@ def main():
                                       "TFLOPs": flops / (ms * 1e-3) / 1e12,
                                       "frac_of_bf16_peak": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}},
         "decode": dec,
+        "prefill_varlen": pre,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, torch)

@@ -7,10 +7,12 @@ used for) and passes raw pointers plus the current HIP stream.  Every step of
 the computation runs in the library's HIP kernels; there is no fallback.
 
     o, S_T = chunk_fwd(q, k, v, log_alpha, b, w, initial_state=None)
+    o, S_T = chunk_fwd_varlen(q, k, v, log_alpha, b, w, cu_seqlens)  # packed sequences
     o      = decode_step(q, k, v, log_alpha, b, w, state)   # state updated in place
 
 Layouts: q, k, b, log_alpha [B,T,H,dk]; v, w, o [B,T,H,dv]; state [B,H,dk,dv]
-(decode: the same without T).  q, k, v, b, w are bf16 or fp32 (all the same);
+(packed: [total_T,H,d] with int64 offsets cu_seqlens [N+1] and states [N,H,dk,dv];
+decode: [N,H,d] and the same states).  q, k, v, b, w are bf16 or fp32 (all the same);
 log_alpha and the state are fp32.  o is fp32 by default (the fp32 accumulation
 carried to the output); ``out_dtype=`` the input dtype rounds it on the store.
 """
@@ -22,7 +24,7 @@ import threading
 
 import torch
 
-__all__ = ["chunk_fwd", "decode_step", "supported", "version", "library_path", "Gdn2Error",
+__all__ = ["chunk_fwd", "chunk_fwd_varlen", "decode_step", "supported", "version", "library_path", "Gdn2Error",
            "CHUNK"]
 
 CHUNK = 64
@@ -59,6 +61,8 @@ def _load():
         P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         lib.gdn2_chunk_fwd.argtypes = [P] * 9 + [I64] * 5 + [I32, I32, P]
         lib.gdn2_chunk_fwd.restype = I32
+        lib.gdn2_chunk_fwd_varlen.argtypes = [P] * 10 + [I64] * 5 + [I32, I32, P]
+        lib.gdn2_chunk_fwd_varlen.restype = I32
         lib.gdn2_decode_step.argtypes = [P] * 8 + [I64] * 4 + [I32, I32, P]
         lib.gdn2_decode_step.restype = I32
         lib.gdn2_supported.argtypes = [I32, I64, I64, I32]
@@ -137,6 +141,52 @@ def chunk_fwd(q, k, v, log_alpha, b, w, initial_state=None, *, o=None, final_sta
                                 _DTYPES[dt], _DTYPES[out_dtype], _stream_handle(dev))
     if st != 0:
         raise Gdn2Error("gdn2_chunk_fwd", st, _load().gdn2_status_string(st).decode())
+    return o, final_state
+
+
+def chunk_fwd_varlen(q, k, v, log_alpha, b, w, cu_seqlens, initial_state=None, *, o=None,
+                     final_state=None, output_final_state=True, out_dtype=torch.float32):
+    """Forward over N sequences packed along the token axis: q, k, b, log_alpha
+    [total_T,H,dk], v, w [total_T,H,dv], cu_seqlens int64 [N+1] on the device
+    (sequence n is tokens cu_seqlens[n]:cu_seqlens[n+1]).  Returns (o, S_T) with
+    S_T [N,H,dk,dv], the layout decode_step continues from."""
+    if q.dim() != 3:
+        raise ValueError("q must be [total_T,H,dk]")
+    total_T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("chunk_fwd_varlen runs on the GPU; got tensors on %s" % dev)
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise TypeError("q dtype must be float32 or bfloat16")
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be [N+1] with N >= 1")
+    N = cu_seqlens.numel() - 1
+    for name, t, shp, tdt in (("k", k, (total_T, H, dk), dt), ("v", v, (total_T, H, dv), dt),
+                              ("log_alpha", log_alpha, (total_T, H, dk), torch.float32),
+                              ("b", b, (total_T, H, dk), dt), ("w", w, (total_T, H, dv), dt),
+                              ("q", q, (total_T, H, dk), dt),
+                              ("cu_seqlens", cu_seqlens, (N + 1,), torch.int64)):
+        _check(name, t, shp, tdt, dev)
+    if initial_state is not None:
+        _check("initial_state", initial_state, (N, H, dk, dv), torch.float32, dev)
+    if out_dtype not in (torch.float32, dt):
+        raise TypeError("out_dtype must be float32 or the input dtype")
+    if o is None:
+        o = torch.empty((total_T, H, dv), dtype=out_dtype, device=dev)
+    else:
+        _check("o", o, (total_T, H, dv), out_dtype, dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _check("final_state", final_state, (N, H, dk, dv), torch.float32, dev)
+    st = _load().gdn2_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+                                       _ptr(initial_state), _ptr(o), _ptr(final_state),
+                                       _ptr(cu_seqlens), N, total_T, H, dk, dv, _DTYPES[dt],
+                                       _DTYPES[out_dtype], _stream_handle(dev))
+    if st != 0:
+        raise Gdn2Error("gdn2_chunk_fwd_varlen", st, _load().gdn2_status_string(st).decode())
     return o, final_state
 
 

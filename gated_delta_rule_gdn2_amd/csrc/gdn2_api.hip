@@ -61,26 +61,26 @@ int device_cus() {
     return cus;
 }
 
-}  // namespace
-
-extern "C" {
-
-gdn2_status_t gdn2_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
-                             const void* b, const void* w, const float* initial_state, void* o,
-                             float* final_state, int64_t B, int64_t T, int64_t H, int64_t dk,
-                             int64_t dv, gdn2_dtype_t dtype, gdn2_dtype_t o_dtype, void* stream) {
+// Validation and launch shared by the fixed-length and the packed-sequence forward.  NS
+// sequences (states [NS, H, dk, dv]); the token tensors hold NT tokens in all; T_or_total is
+// the kernels' token parameter (T per sequence, or the packed total).
+gdn2_status_t chunk_fwd_common(const void* q, const void* k, const void* v, const float* log_alpha,
+                               const void* b, const void* w, const float* initial_state, void* o,
+                               float* final_state, const int64_t* cu_seqlens, int64_t NS,
+                               int64_t T_or_total, int64_t NT, int64_t H, int64_t dk, int64_t dv,
+                               gdn2_dtype_t dtype, gdn2_dtype_t o_dtype, void* stream) {
     if (!q || !k || !v || !log_alpha || !b || !w || !o) return GDN2_ERR_NULL;
     if (dtype != GDN2_DTYPE_F32 && dtype != GDN2_DTYPE_BF16) return GDN2_ERR_UNSUPPORTED;
     if (o_dtype != GDN2_DTYPE_F32 && o_dtype != dtype) return GDN2_ERR_UNSUPPORTED;
-    if (B < 1 || T < 1 || H < 1 || dk < 1 || dv < 1) return GDN2_ERR_SHAPE;
+    if (H < 1 || dk < 1 || dv < 1) return GDN2_ERR_SHAPE;
     if (!chunk_supported(dk, dv, dtype)) return GDN2_ERR_UNSUPPORTED;
-    // sizes: kernels index rows with 32-bit B, T, H and 64-bit element offsets
-    int64_t BT, BTH, nk, nv, ns;
-    if (B > INT_MAX || T > INT_MAX || H > INT_MAX) return GDN2_ERR_SHAPE;
-    if (!mul_ok(B, T, &BT) || !mul_ok(BT, H, &BTH) || !mul_ok(BTH, dk, &nk) || !mul_ok(BTH, dv, &nv))
-        return GDN2_ERR_SHAPE;
-    if (!mul_ok(B * H, dk * dv, &ns)) return GDN2_ERR_SHAPE;
-    if (B * H * (dv / 16) > UINT_MAX / 2) return GDN2_ERR_SHAPE;
+    // sizes: kernels index rows with 32-bit sequence, token and head counts and 64-bit
+    // element offsets
+    int64_t NTH, nk, nv, ns;
+    if (NS > INT_MAX || T_or_total > INT_MAX || H > INT_MAX) return GDN2_ERR_SHAPE;
+    if (!mul_ok(NT, H, &NTH) || !mul_ok(NTH, dk, &nk) || !mul_ok(NTH, dv, &nv)) return GDN2_ERR_SHAPE;
+    if (!mul_ok(NS * H, dk * dv, &ns)) return GDN2_ERR_SHAPE;
+    if (NS * H * (dv / 16) > UINT_MAX / 2) return GDN2_ERR_SHAPE;
     // per-lane offsets inside one chunk are formed with 24-bit multiplies of the token stride
     if (H * dk >= (int64_t(1) << 24) || H * dv >= (int64_t(1) << 24)) return GDN2_ERR_SHAPE;
     const void* ptrs[] = {q, k, v, log_alpha, b, w, initial_state, o, final_state};
@@ -95,20 +95,50 @@ gdn2_status_t gdn2_chunk_fwd(const void* q, const void* k, const void* v, const 
     for (const Range& r : in_ranges)
         if (overlap(ro, r)) return GDN2_ERR_ALIAS;
     if (initial_state && overlap(ro, range_of(initial_state, ns * 4))) return GDN2_ERR_ALIAS;
+    const Range rc = range_of(cu_seqlens, cu_seqlens ? (NS + 1) * 8 : 0);
+    if (overlap(ro, rc)) return GDN2_ERR_ALIAS;
     if (final_state) {
         const Range rf = range_of(final_state, ns * 4);
         for (const Range& r : in_ranges)
             if (overlap(rf, r)) return GDN2_ERR_ALIAS;
-        if (overlap(rf, ro)) return GDN2_ERR_ALIAS;
+        if (overlap(rf, ro) || overlap(rf, rc)) return GDN2_ERR_ALIAS;
         if (initial_state && initial_state != final_state && overlap(rf, range_of(initial_state, ns * 4)))
             return GDN2_ERR_ALIAS;
     }
+    if (NT == 0 && !final_state) return GDN2_OK;  // nothing to compute or write
     const int cus = device_cus();
     if (cus <= 0) return GDN2_ERR_HIP;
-    gdn2::ChunkArgs a{q, k, v, log_alpha, b, w, initial_state, o, final_state, B, T, H, dk, dv,
-                      dtype == GDN2_DTYPE_BF16, o_dtype == GDN2_DTYPE_F32, stream};
-    const int dvs = choose_dvs(B * H, dv, cus);
+    gdn2::ChunkArgs a{q, k, v, log_alpha, b, w, initial_state, o, final_state, NS, T_or_total, H, dk, dv,
+                      dtype == GDN2_DTYPE_BF16, o_dtype == GDN2_DTYPE_F32, stream, cu_seqlens};
+    const int dvs = choose_dvs(NS * H, dv, cus);
     return gdn2::launch_chunk_fwd(a, dvs) == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn2_status_t gdn2_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                             const void* b, const void* w, const float* initial_state, void* o,
+                             float* final_state, int64_t B, int64_t T, int64_t H, int64_t dk,
+                             int64_t dv, gdn2_dtype_t dtype, gdn2_dtype_t o_dtype, void* stream) {
+    if (B < 1 || T < 1) return GDN2_ERR_SHAPE;
+    int64_t BT;
+    if (!mul_ok(B, T, &BT)) return GDN2_ERR_SHAPE;
+    return chunk_fwd_common(q, k, v, log_alpha, b, w, initial_state, o, final_state, nullptr, B, T, BT, H,
+                            dk, dv, dtype, o_dtype, stream);
+}
+
+gdn2_status_t gdn2_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha,
+                                    const void* b, const void* w, const float* initial_state, void* o,
+                                    float* final_state, const int64_t* cu_seqlens, int64_t N,
+                                    int64_t total_T, int64_t H, int64_t dk, int64_t dv,
+                                    gdn2_dtype_t dtype, gdn2_dtype_t o_dtype, void* stream) {
+    if (!cu_seqlens) return GDN2_ERR_NULL;
+    if (N < 1 || total_T < 0) return GDN2_ERR_SHAPE;
+    if (reinterpret_cast<uintptr_t>(cu_seqlens) & 7u) return GDN2_ERR_MISALIGNED;
+    return chunk_fwd_common(q, k, v, log_alpha, b, w, initial_state, o, final_state, cu_seqlens, N, total_T,
+                            total_T, H, dk, dv, dtype, o_dtype, stream);
 }
 
 gdn2_status_t gdn2_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,

@@ -410,8 +410,8 @@ template <typename OutT, int DK, int DV, int DVS>
 __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ log_alpha, const bf16* __restrict__ bgate, const bf16* __restrict__ wgate,
-    const float* initial_state, OutT* __restrict__ o, float* final_state, int B, int Tlen, int H,
-    int nslices, int xcd_map) {
+    const float* initial_state, OutT* __restrict__ o, float* final_state, int B, int Tparam, int H,
+    int nslices, int xcd_map, const int64_t* __restrict__ cu_seqlens) {
     using G = Cfg<DK, DVS>;
     constexpr int CPL = G::CPL, KT = G::KT, NCT = G::NCT, SPW = G::SPW, UPW = G::UPW;
     constexpr int LDK = G::LDK, LC = G::LC, LCF = G::LCF, VC = G::VC, TPV = G::TPV;
@@ -447,6 +447,21 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
     }
     const int bi = bh / H, h = bh % H;
     const int col0 = slice * DVS;
+    // sequence bi covers tokens [tok0, tok0 + Tlen) of the token axis: fixed length Tparam,
+    // or packed sequences delimited by offsets (clamped into [0, Tparam], so any offsets
+    // keep every access in range)
+    int64_t tok0;
+    int Tlen;
+    if (cu_seqlens) {
+        const int64_t lo = min(max(cu_seqlens[bi], (int64_t)0), (int64_t)Tparam);
+        const int64_t hi = min(max(cu_seqlens[bi + 1], lo), (int64_t)Tparam);
+        tok0 = lo;
+        Tlen = (int)(hi - lo);
+    } else {
+        tok0 = (int64_t)bi * Tparam;
+        Tlen = Tparam;
+    }
+
 
     // element phase roles
     const int I = wave & 3, hf = wave >> 2;
@@ -477,8 +492,8 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
     const int nchunks = (Tlen + C - 1) / C;
     const int64_t tok_stride_k = (int64_t)H * DK;
     const int64_t tok_stride_v = (int64_t)H * DV;
-    const int64_t seq_base_k = ((int64_t)bi * Tlen * H + h) * DK;
-    const int64_t seq_base_v = ((int64_t)bi * Tlen * H + h) * DV;
+    const int64_t seq_base_k = (tok0 * H + h) * DK;
+    const int64_t seq_base_v = (tok0 * H + h) * DV;
 
     // Every global load of a chunk, issued without a branch: a token past the end of the
     // sequence reads the last token and is zeroed before use.  Two batches (decays and
@@ -523,8 +538,10 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
     };
 
     In<CPL, TPV, VC> in;
-    load_first(0, in);
-    load_second(0, in);
+    if (Tlen > 0) {
+        load_first(0, in);
+        load_second(0, in);
+    }
     __syncthreads();
 
     for (int n = 0; n < nchunks; ++n) {
@@ -1134,7 +1151,7 @@ hipError_t launch(const ChunkArgs& a) {
     hipLaunchKernelGGL((chunk_bf16_kernel<OutT, D, D, DVS>), dim3((unsigned)groups), dim3(NT), 0,
                        (hipStream_t)a.stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
                        a.log_alpha, (const bf16*)a.b, (const bf16*)a.w, a.initial_state, (OutT*)a.o,
-                       a.final_state, (int)a.B, (int)a.T, (int)a.H, nslices, xcd_map);
+                       a.final_state, (int)a.B, (int)a.T, (int)a.H, nslices, xcd_map, a.cu_seqlens);
     return hipGetLastError();
 }
 

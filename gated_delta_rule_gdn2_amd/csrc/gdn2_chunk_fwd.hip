@@ -350,8 +350,8 @@ template <typename T, typename OutT, int DK, int DV, int DVS>
 __global__ __launch_bounds__(256) void chunk_fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ log_alpha, const T* __restrict__ bgate, const T* __restrict__ wgate,
-    const float* initial_state, OutT* __restrict__ o, float* final_state, int B, int Tlen, int H,
-    int nslices, int xcd_map) {
+    const float* initial_state, OutT* __restrict__ o, float* final_state, int B, int Tparam, int H,
+    int nslices, int xcd_map, const int64_t* __restrict__ cu_seqlens) {
     using Cfg = ChunkCfg<T, DK, DVS>;
     constexpr int C = Cfg::C, CPL = Cfg::CPL, NCT = Cfg::NCT;
     constexpr int LDK = Cfg::LDK, LC = Cfg::LC;
@@ -394,6 +394,21 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
     }
     const int bi = bh / H, h = bh % H;
     const int col0 = slice * DVS;  // first value column of this slice
+    // sequence bi covers tokens [tok0, tok0 + Tlen) of the token axis: fixed length Tparam,
+    // or packed sequences delimited by offsets (clamped into [0, Tparam], so any offsets
+    // keep every access in range)
+    int64_t tok0;
+    int Tlen;
+    if (cu_seqlens) {
+        const int64_t lo = min(max(cu_seqlens[bi], (int64_t)0), (int64_t)Tparam);
+        const int64_t hi = min(max(cu_seqlens[bi + 1], lo), (int64_t)Tparam);
+        tok0 = lo;
+        Tlen = (int)(hi - lo);
+    } else {
+        tok0 = (int64_t)bi * Tparam;
+        Tlen = Tparam;
+    }
+
 
     // upper blocks of A and P are never written below: clear once
     for (int x = tid; x < C * LC; x += Cfg::NT) sA[x] = from_f32<T>(0.f);
@@ -422,8 +437,8 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
     const int nchunks = (Tlen + C - 1) / C;
     const int64_t tok_stride_k = (int64_t)H * DK;  // elements between consecutive tokens
     const int64_t tok_stride_v = (int64_t)H * DV;
-    const int64_t seq_base_k = ((int64_t)bi * Tlen * H + h) * DK;
-    const int64_t seq_base_v = ((int64_t)bi * Tlen * H + h) * DV;
+    const int64_t seq_base_k = (tok0 * H + h) * DK;
+    const int64_t seq_base_v = (tok0 * H + h) * DV;
     // element phase: wave I = 16-token block I; lane = (token slot ts, channel group cg) holds
     // channels cg*CPL .. +CPL of tokens 4*ts .. 4*ts+3 of the block (one 16-byte load per token)
     const int I = wave;
@@ -464,8 +479,10 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
     };
 
     ChunkIn<T, CPL, TPV> in;
-    load_first(0, in);
-    load_second(0, in);
+    if (Tlen > 0) {
+        load_first(0, in);
+        load_second(0, in);
+    }
     __syncthreads();
 
     for (int n = 0; n < nchunks; ++n) {
@@ -887,7 +904,7 @@ static hipError_t launch_chunk(const ChunkArgs& a) {
     hipLaunchKernelGGL((chunk_fwd_kernel<T, OutT, DK, DV, DVS>), dim3((unsigned)groups), dim3(256), 0,
                        (hipStream_t)a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.log_alpha,
                        (const T*)a.b, (const T*)a.w, a.initial_state, (OutT*)a.o, a.final_state, (int)a.B,
-                       (int)a.T, (int)a.H, nslices, xcd_map);
+                       (int)a.T, (int)a.H, nslices, xcd_map, a.cu_seqlens);
     return hipGetLastError();
 }
 

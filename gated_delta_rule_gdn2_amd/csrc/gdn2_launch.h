@@ -20,6 +20,9 @@ struct ChunkArgs {
     bool dtype_bf16;  // inputs q, k, v, b, w are bf16 (else fp32)
     bool out_f32;     // o is fp32 (else the input dtype)
     void* stream;
+    // packed sequences: B + 1 offsets into the token axis of length T (device memory), or
+    // nullptr for B sequences of T tokens each
+    const int64_t* cu_seqlens = nullptr;
 };
 
 struct DecodeArgs {

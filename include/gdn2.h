@@ -92,6 +92,38 @@ gdn2_status_t gdn2_chunk_fwd(const void* q, const void* k, const void* v,
                              gdn2_dtype_t dtype, gdn2_dtype_t o_dtype, void* stream);
 
 /*
+ * gdn2_chunk_fwd_varlen -- the same forward over N sequences of different
+ * lengths packed along one token axis (prefill of a serving batch).
+ *
+ *   q, k, b       [total_T, H, dk]  dtype
+ *   v, w          [total_T, H, dv]  dtype
+ *   log_alpha     [total_T, H, dk]  float32
+ *   cu_seqlens    [N + 1]           int64, DEVICE memory, 8-byte aligned:
+ *                                   sequence n holds tokens
+ *                                   [cu_seqlens[n], cu_seqlens[n + 1])
+ *   initial_state [N, H, dk, dv]    float32, or NULL for zeros
+ *   o             [total_T, H, dv]  o_dtype
+ *   final_state   [N, H, dk, dv]    float32 or NULL; may equal initial_state
+ *
+ * The offsets are expected to be non-decreasing with cu_seqlens[0] = 0 and
+ * cu_seqlens[N] = total_T (they are in device memory and are not read on the
+ * host).  Each sequence's range is clamped into [0, total_T] on the device, so
+ * any offsets keep every access inside the tensors; tokens outside every
+ * sequence are left unwritten in o.  A sequence of length 0 passes its initial
+ * state (or zeros) through to final_state.  The final states are laid out as
+ * gdn2_decode_step's state, so decoding continues from them directly.
+ * N >= 1, total_T >= 0; everything else as for gdn2_chunk_fwd (supported
+ * shapes and dtypes, alignment, aliasing; cu_seqlens must not overlap o or
+ * final_state).
+ */
+gdn2_status_t gdn2_chunk_fwd_varlen(const void* q, const void* k, const void* v,
+                                    const float* log_alpha, const void* b, const void* w,
+                                    const float* initial_state, void* o, float* final_state,
+                                    const int64_t* cu_seqlens, int64_t N, int64_t total_T,
+                                    int64_t H, int64_t dk, int64_t dv, gdn2_dtype_t dtype,
+                                    gdn2_dtype_t o_dtype, void* stream);
+
+/*
  * gdn2_decode_step -- one recurrent step for N independent sequences.
  *
  *   q, k, b       [N, H, dk]     dtype

@@ -148,3 +148,26 @@ def test_python_binding_rejects_cpu_tensors():
     g = torch.zeros(1, 64, 1, 64)
     with pytest.raises(ValueError):
         gdn2.chunk_fwd(x, x, x, g, x, x)
+
+
+def varlen(lib, f, N=2, total=64, H=1, dk=64, dv=64, dtype=BF16, odt=F32, **over):
+    args = dict(q=f.p(0), k=f.p(1), v=f.p(2), g=f.p(3), b=f.p(4), w=f.p(5), s0=None, o=f.p(7),
+                sT=None, cu=f.p(9))
+    args.update(over)
+    return lib.gdn2_chunk_fwd_varlen(args["q"], args["k"], args["v"], args["g"], args["b"], args["w"],
+                                     args["s0"], args["o"], args["sT"], args["cu"], N, total, H, dk,
+                                     dv, dtype, odt, None)
+
+
+def test_varlen_validation(lib):
+    f = Fake()
+    assert varlen(lib, f, cu=None) == ERR_NULL
+    for name in ("q", "k", "v", "g", "b", "w", "o"):
+        assert varlen(lib, f, **{name: None}) == ERR_NULL, name
+    assert varlen(lib, f, N=0) == ERR_SHAPE
+    assert varlen(lib, f, total=-1) == ERR_SHAPE
+    assert varlen(lib, f, cu=f.p(9, 4)) == ERR_MISALIGNED
+    assert varlen(lib, f, dk=96, dv=96) == ERR_UNSUPPORTED
+    # offsets inside o, final state overlapping the offsets
+    assert varlen(lib, f, cu=f.p(7, 8)) == ERR_ALIAS
+    assert varlen(lib, f, sT=f.p(9)) == ERR_ALIAS

@@ -1,0 +1,179 @@
+"""GPU parity of the packed-sequence forward (serving prefill) and its hand-off to decode.
+
+Every sequence of a packed batch is checked against the fp64 oracle run on that
+sequence alone, with the same bars as the fixed-length forward (max |x - x_ref| /
+RMS(x_ref): 1e-4 for fp32 inputs, 3e-2 for bf16 inputs).  Lengths mix empty, single
+token, one token short of, exactly and one past a chunk, and several chunks with a
+ragged tail."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_gdn2_amd as gdn2
+import oracle
+import workloads as W
+from tests.parity_util import TOL_BF16, TOL_F32, rel_max_err, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gdn2._load()
+
+
+def packed_case(dtype, d, H, lengths, seed, s0_std=0.05, g_lo=-0.2, g_hi=-0.001):
+    wl = dataclasses.replace(W.SERVE_PREFILL, name="varlen", dtype=dtype, dk=d, dv=d, H=H,
+                             s0_std=s0_std, g_lo=g_lo, g_hi=g_hi)
+    return W.make_packed_inputs(wl, lengths, seed=seed)
+
+
+def run_varlen(inp, **kw):
+    d = to_dev(inp)
+    o, s = gdn2.chunk_fwd_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"],
+                                 d["cu_seqlens"], d["s0"], **kw)
+    torch.cuda.synchronize()
+    return o, s
+
+
+def oracle_sequence(inp, n):
+    """The oracle on sequence n alone: returns o [L, H, dv] and S_T [H, dk, dv]."""
+    cu = inp["cu_seqlens"].tolist()
+    a, e = cu[n], cu[n + 1]
+    H, dk = inp["q"].shape[1], inp["q"].shape[2]
+    dv = inp["v"].shape[2]
+    s0 = None if inp["s0"] is None else inp["s0"][n:n + 1]
+    if e == a:
+        st = np.zeros((H, dk, dv)) if s0 is None else s0[0].double().numpy()
+        return np.zeros((0, H, dv)), st
+    x = {nm: inp[nm][a:e][None] for nm in ("q", "k", "v", "log_alpha", "b", "w")}
+    o, s = oracle.fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], s0)
+    return o[0], s[0]
+
+
+def check_all(inp, o, s, tol, label):
+    N = inp["cu_seqlens"].numel() - 1
+    refs = [oracle_sequence(inp, n) for n in range(N)]
+    o_ref = np.concatenate([r[0] for r in refs], axis=0)
+    s_ref = np.stack([r[1] for r in refs])
+    eo, es = rel_max_err(o, o_ref), rel_max_err(s, s_ref)
+    say("  %-44s o err %.3e   S_T err %.3e   (bar %.0e)" % (label, eo, es, tol))
+    assert eo <= tol and es <= tol, (label, eo, es)
+
+
+MIX = [0, 1, 63, 64, 65, 200, 7, 130]
+
+CASES = [
+    # dtype, d, H, seed
+    (torch.bfloat16, 128, 3, 201),
+    (torch.bfloat16, 64, 5, 202),
+    (torch.float32, 64, 2, 203),
+]
+
+
+@pytest.mark.parametrize("dtype,d,H,seed", CASES)
+def test_packed_mix_matches_oracle_per_sequence(dtype, d, H, seed):
+    say("case: varlen %s d%d H%d seed %d lengths %s" % (dtype, d, H, seed, MIX))
+    inp = packed_case(dtype, d, H, MIX, seed)
+    o, s = run_varlen(inp)
+    check_all(inp, o, s, TOL_F32 if dtype == torch.float32 else TOL_BF16, "packed mix")
+
+
+def test_packed_strong_decay():
+    say("case: varlen strong decay bf16 d128")
+    inp = packed_case(torch.bfloat16, 128, 2, [70, 1, 150, 64], 204, g_lo=-5.0, g_hi=-1.0)
+    o, s = run_varlen(inp)
+    check_all(inp, o, s, TOL_BF16, "packed strong decay")
+
+
+def test_equal_lengths_match_fixed_length_call_exactly():
+    say("case: varlen == fixed length, bf16 d128, 4 x 130 tokens")
+    L, N, H = 130, 4, 3
+    inp = packed_case(torch.bfloat16, 128, H, [L] * N, 205)
+    o, s = run_varlen(inp)
+    d = to_dev(inp)
+    shp = lambda x: x.reshape(N, L, H, x.shape[-1])
+    o2, s2 = gdn2.chunk_fwd(shp(d["q"]), shp(d["k"]), shp(d["v"]), shp(d["log_alpha"]), shp(d["b"]),
+                            shp(d["w"]), d["s0"])
+    torch.cuda.synchronize()
+    assert torch.equal(o.reshape(N, L, H, -1), o2)
+    assert torch.equal(s, s2)
+
+
+def test_empty_sequences_pass_their_state_through():
+    say("case: varlen with empty sequences")
+    inp = packed_case(torch.bfloat16, 128, 2, [0, 5, 0, 0], 206)
+    o, s = run_varlen(inp)
+    s0 = inp["s0"].cuda()
+    for n in (0, 2, 3):
+        assert torch.equal(s[n], s0[n]), n
+    check_all(inp, o, s, TOL_BF16, "empty sequences")
+
+
+def test_tokens_outside_every_sequence_are_untouched():
+    say("case: varlen offsets covering part of the token axis")
+    inp = packed_case(torch.bfloat16, 64, 2, [40, 30], 207)
+    d = to_dev(inp)
+    d["cu_seqlens"] = torch.tensor([5, 45, 60], dtype=torch.int64, device="cuda")  # tokens 0-4, 60-69 unused
+    o = torch.full((70, 2, 64), 7.0, device="cuda")
+    gdn2.chunk_fwd_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["cu_seqlens"],
+                          d["s0"], o=o)
+    torch.cuda.synchronize()
+    assert torch.all(o[:5] == 7.0) and torch.all(o[60:] == 7.0)
+    assert torch.isfinite(o[5:60]).all()
+
+
+def test_prefill_then_decode_continues_the_sequences():
+    """Prefill N prompts (packed, with initial states), then decode 8 tokens per sequence
+    from the prefill's final states; compare every decode output and the final state with
+    the oracle run over prompt + decoded tokens."""
+    say("case: varlen prefill -> decode hand-off, bf16 d128")
+    lengths, H, d, steps = [33, 64, 1, 97], 2, 128, 8
+    N = len(lengths)
+    inp = packed_case(torch.bfloat16, d, H, lengths, 208)
+    _, s = run_varlen(inp)
+    dec = packed_case(torch.bfloat16, d, H, [steps] * N, 209, s0_std=None)  # decode tokens
+    dd = to_dev(dec)
+    state = s.clone()
+    outs = []
+    for t in range(steps):
+        idx = torch.arange(N, device="cuda") * steps + t
+        x = {nm: dd[nm][idx].contiguous() for nm in ("q", "k", "v", "log_alpha", "b", "w")}
+        outs.append(gdn2.decode_step(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], state))
+    torch.cuda.synchronize()
+    cu = inp["cu_seqlens"].tolist()
+    worst = 0.0
+    for n in range(N):
+        cat = {nm: torch.cat([inp[nm][cu[n]:cu[n + 1]], dec[nm][n * steps:(n + 1) * steps]])[None]
+               for nm in ("q", "k", "v", "log_alpha", "b", "w")}
+        o_ref, s_ref = oracle.fwd(cat["q"], cat["k"], cat["v"], cat["log_alpha"], cat["b"], cat["w"],
+                                  inp["s0"][n:n + 1])
+        o_dec = torch.stack([outs[t][n] for t in range(steps)])
+        eo = rel_max_err(o_dec, o_ref[0, lengths[n]:])
+        es = rel_max_err(state[n], s_ref[0])
+        worst = max(worst, eo, es)
+        assert eo <= TOL_BF16 and es <= TOL_BF16, (n, eo, es)
+    say("  prefill -> decode, worst err %.3e (bar %.0e)" % (worst, TOL_BF16))
+
+
+def test_serving_prefill_workload_sampled():
+    """The serving prefill workload at full size (64 prompts, seeded length mix, H=16,
+    d=128, continuation states), in the launch the benchmark times; sampled sequences
+    against the oracle, every output finite."""
+    wl = W.SERVE_PREFILL
+    lengths = W.make_lengths(wl.B, wl.seed)
+    say("case: %s total %d tokens" % (wl.name, sum(lengths)))
+    inp = W.make_packed_inputs(wl, lengths)
+    o, s = run_varlen(inp)
+    assert torch.isfinite(o).all() and torch.isfinite(s).all()
+    cu = inp["cu_seqlens"].tolist()
+    for n in (0, 17, 63):
+        o_ref, s_ref = oracle_sequence({**inp, "q": inp["q"], "s0": inp["s0"]}, n)
+        eo = rel_max_err(o[cu[n]:cu[n + 1]], o_ref)
+        es = rel_max_err(s[n], s_ref)
+        say("  sequence %d (length %d): o err %.3e   S_T err %.3e" % (n, lengths[n], eo, es))
+        assert eo <= TOL_BF16 and es <= TOL_BF16

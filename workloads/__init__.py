@@ -69,6 +69,11 @@ LONG_32K = Workload("long_bf16_B1_T32768_H16_d128", B=1, T=32768, H=16, dk=128, 
 FWD_BWD_4K = Workload("fwdbwd_bf16_B4_T4096_H16_d128", B=4, T=4096, H=16, dk=128, dv=128,
                       dtype=torch.bfloat16, seed=4, s0_std=0.02)
 
+# Serving prefill: a batch of prompts of mixed lengths packed along one token axis, with
+# per-sequence initial states (a continuation), followed by decode steps from the final states.
+SERVE_PREFILL = Workload("serve_prefill_bf16_N64_H16_d128", B=64, T=0, H=16, dk=128, dv=128,
+                         dtype=torch.bfloat16, seed=5, s0_std=0.02)
+
 ALL = (TINY_FP32, TRAIN_4K, DECODE, LONG_32K, FWD_BWD_4K)
 
 
@@ -144,3 +149,33 @@ def make_decode_pool(wl: Workload, seed: Optional[int] = None, N: Optional[int] 
     dt = wl.dtype
     return dict(state=state, q=q.to(dt), k=k.to(dt), v=v.to(dt), log_alpha=g, b=b.to(dt),
                 w=w.to(dt))
+
+
+def make_lengths(n: int, seed: int, median: int = 512, lo: int = 1, hi: int = 4096):
+    """Seeded prompt lengths for a serving batch: log-normal around ``median``
+    (sigma 1), clipped to [lo, hi].  Returns a list of ints."""
+    gen = torch.Generator("cpu").manual_seed(seed + 7_000_001)
+    z = torch.randn((n,), generator=gen, dtype=torch.float64)
+    x = torch.exp(z + float(torch.log(torch.tensor(float(median)))))
+    return [int(min(max(round(float(t)), lo), hi)) for t in x]
+
+
+def make_packed_inputs(wl: Workload, lengths, seed: Optional[int] = None):
+    """Packed sequences: q, k, v, log_alpha, b, w as [total_T, H, d] (the recipe of
+    ``make_inputs`` over one axis of sum(lengths) tokens), cu_seqlens int64 [N+1], and
+    initial states [N, H, dk, dv] (~ N(0, s0_std^2), or None)."""
+    seed = wl.seed if seed is None else seed
+    total = int(sum(lengths))
+    d = make_inputs(wl, seed=seed, B=1, T=max(total, 1))
+    out = {n: d[n][0, :total] for n in ("q", "k", "v", "log_alpha", "b", "w")}
+    cu = [0]
+    for L in lengths:
+        cu.append(cu[-1] + int(L))
+    out["cu_seqlens"] = torch.tensor(cu, dtype=torch.int64)
+    s0 = None
+    if wl.s0_std is not None:
+        gen = torch.Generator("cpu").manual_seed(seed + 3_000_017)
+        s0 = torch.randn((len(lengths), wl.H, wl.dk, wl.dv), generator=gen,
+                         dtype=torch.float32) * wl.s0_std
+    out["s0"] = s0
+    return out
