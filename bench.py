@@ -77,6 +77,7 @@ def recorded_traffic(profile, sources):
 
 CHUNK_PROFILE = ("chunk_fwd_train_B8_T4096_H16_d128.md", ("gdn2_chunk_bf16.hip", "gdn2_device.h"))
 DECODE_PROFILE = ("decode_step_N256_H16_d128.md", ("gdn2_decode.hip", "gdn2_device.h"))
+PREFILL_PROFILE = ("prefill_varlen_N64_H16_d128.md", ("gdn2_chunk_bf16.hip", "gdn2_device.h"))
 
 
 def time_launches(fn, steps, warmup, torch):
@@ -159,7 +160,9 @@ def run_prefill(args, torch, gdn2, W, dev, out_dtype):
     return {"workload": wl.name, "sequences": wl.B, "tokens": total,
             "lengths": "log-normal around 512 (sigma 1), clipped to [1, 4096], seed %d" % wl.seed,
             "us_per_launch": ms * 1e3, "tokens_per_s": total / (ms * 1e-3), "GBps": gbps,
-            "peak": HBM_PEAK_GBPS, "frac": gbps / HBM_PEAK_GBPS, "algorithmic_bytes_per_launch": nbytes}
+            "peak": HBM_PEAK_GBPS, "frac": gbps / HBM_PEAK_GBPS,
+            "traffic": recorded_traffic(*PREFILL_PROFILE) if out_dtype == torch.float32 else None,
+            "algorithmic_bytes_per_launch": nbytes}
 
 
 def run_decode(args, torch, gdn2, W, dev, out_dtype):

@@ -177,3 +177,36 @@ def test_serving_prefill_workload_sampled():
         es = rel_max_err(s[n], s_ref)
         say("  sequence %d (length %d): o err %.3e   S_T err %.3e" % (n, lengths[n], eo, es))
         assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_multi_token_steps_in_place_continue_the_sequences():
+    """Decode several tokens per sequence per call: the fixed-length forward with T = 3 and
+    the state passed as both initial and final state, three calls in a row after a packed
+    prefill; every output and the final states against the oracle over prompt + steps."""
+    say("case: multi-token steps in place after prefill, bf16 d128")
+    lengths, H, d, per, calls = [20, 64, 90], 2, 128, 3, 3
+    N = len(lengths)
+    inp = packed_case(torch.bfloat16, d, H, lengths, 210)
+    _, state = run_varlen(inp)
+    steps = per * calls
+    dec = packed_case(torch.bfloat16, d, H, [steps] * N, 211, s0_std=None)
+    dd = {nm: dec[nm].reshape(N, steps, H, -1).cuda() for nm in ("q", "k", "v", "log_alpha", "b", "w")}
+    outs = []
+    for c in range(calls):
+        x = {nm: dd[nm][:, c * per:(c + 1) * per].contiguous() for nm in dd}
+        o, s = gdn2.chunk_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], state,
+                              final_state=state)
+        assert s.data_ptr() == state.data_ptr()
+        outs.append(o)
+    torch.cuda.synchronize()
+    o_all = torch.cat(outs, dim=1)  # [N, steps, H, dv]
+    cu = inp["cu_seqlens"].tolist()
+    for n in range(N):
+        cat = {nm: torch.cat([inp[nm][cu[n]:cu[n + 1]], dec[nm][n * steps:(n + 1) * steps]])[None]
+               for nm in ("q", "k", "v", "log_alpha", "b", "w")}
+        o_ref, s_ref = oracle.fwd(cat["q"], cat["k"], cat["v"], cat["log_alpha"], cat["b"], cat["w"],
+                                  inp["s0"][n:n + 1])
+        eo = rel_max_err(o_all[n], o_ref[0, lengths[n]:])
+        es = rel_max_err(state[n], s_ref[0])
+        say("  sequence %d: o err %.3e   S err %.3e" % (n, eo, es))
+        assert eo <= TOL_BF16 and es <= TOL_BF16, (n, eo, es)
