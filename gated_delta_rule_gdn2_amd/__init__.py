@@ -9,6 +9,7 @@ the computation runs in the library's HIP kernels; there is no fallback.
     o, S_T = chunk_fwd(q, k, v, log_alpha, b, w, initial_state=None)
     o, S_T = chunk_fwd_varlen(q, k, v, log_alpha, b, w, cu_seqlens)  # packed sequences
     o      = decode_step(q, k, v, log_alpha, b, w, state)   # state updated in place
+    grads  = chunk_bwd(q, k, v, log_alpha, b, w, d_o, initial_state=None, d_final_state=None)
 
 Layouts: q, k, b, log_alpha [B,T,H,dk]; v, w, o [B,T,H,dv]; state [B,H,dk,dv]
 (packed: [total_T,H,d] with int64 offsets cu_seqlens [N+1] and states [N,H,dk,dv];
@@ -24,8 +25,8 @@ import threading
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_varlen", "decode_step", "supported", "version", "library_path", "Gdn2Error",
-           "CHUNK"]
+__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_bwd", "chunk_bwd_workspace_bytes", "decode_step", "supported",
+           "version", "library_path", "Gdn2Error", "CHUNK"]
 
 CHUNK = 64
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,7 +36,7 @@ _lib = None
 
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 _STATUS = {0: "GDN2_OK", 1: "GDN2_ERR_NULL", 2: "GDN2_ERR_SHAPE", 3: "GDN2_ERR_UNSUPPORTED",
-           4: "GDN2_ERR_MISALIGNED", 5: "GDN2_ERR_ALIAS", 6: "GDN2_ERR_HIP"}
+           4: "GDN2_ERR_MISALIGNED", 5: "GDN2_ERR_ALIAS", 6: "GDN2_ERR_HIP", 7: "GDN2_ERR_WORKSPACE"}
 
 
 class Gdn2Error(RuntimeError):
@@ -65,6 +66,10 @@ def _load():
         lib.gdn2_chunk_fwd_varlen.restype = I32
         lib.gdn2_decode_step.argtypes = [P] * 8 + [I64] * 4 + [I32, I32, P]
         lib.gdn2_decode_step.restype = I32
+        lib.gdn2_chunk_bwd_workspace_bytes.argtypes = [I64] * 5
+        lib.gdn2_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.gdn2_chunk_bwd.argtypes = [P] * 17 + [ctypes.c_size_t] + [I64] * 5 + [I32, P]
+        lib.gdn2_chunk_bwd.restype = I32
         lib.gdn2_supported.argtypes = [I32, I64, I64, I32]
         lib.gdn2_supported.restype = I32
         lib.gdn2_status_string.argtypes = [I32]
@@ -79,7 +84,7 @@ def version() -> str:
 
 
 def supported(which: str, dk: int, dv: int, dtype: torch.dtype) -> bool:
-    w = {"chunk_fwd": 0, "decode_step": 1}[which]
+    w = {"chunk_fwd": 0, "decode_step": 1, "chunk_bwd": 2}[which]
     return bool(_load().gdn2_supported(w, dk, dv, _DTYPES[dtype]))
 
 
@@ -220,3 +225,59 @@ def decode_step(q, k, v, log_alpha, b, w, state, *, o=None, out_dtype=torch.floa
     if st != 0:
         raise Gdn2Error("gdn2_decode_step", st, _load().gdn2_status_string(st).decode())
     return o
+
+
+def chunk_bwd_workspace_bytes(B, T, H, dk, dv) -> int:
+    """Device workspace (bytes) that chunk_bwd needs for these sizes."""
+    return int(_load().gdn2_chunk_bwd_workspace_bytes(B, T, H, dk, dv))
+
+
+def chunk_bwd(q, k, v, log_alpha, b, w, d_o, initial_state=None, d_final_state=None, *, workspace=None,
+              grads=None, want_initial_state_grad=True):
+    """Gradients of sum(d_o * o) + sum(d_final_state * S_T) for the forward chunk_fwd(q, k, v,
+    log_alpha, b, w, initial_state).  d_o [B,T,H,dv] and d_final_state [B,H,dk,dv] are fp32.
+    Returns a dict of fp32 tensors dq, dk, dv, dlog_alpha, db, dw and d_initial_state (None
+    when not requested).  ``workspace`` (uint8, at least chunk_bwd_workspace_bytes) and
+    ``grads`` (a dict of preallocated outputs) may be passed to avoid allocations."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B,T,H,dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("chunk_bwd runs on the GPU; got tensors on %s" % dev)
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise TypeError("q dtype must be float32 or bfloat16")
+    for name, t, shp, tdt in (("k", k, (B, T, H, dk), dt), ("v", v, (B, T, H, dv), dt),
+                              ("log_alpha", log_alpha, (B, T, H, dk), torch.float32),
+                              ("b", b, (B, T, H, dk), dt), ("w", w, (B, T, H, dv), dt),
+                              ("q", q, (B, T, H, dk), dt), ("d_o", d_o, (B, T, H, dv), torch.float32)):
+        _check(name, t, shp, tdt, dev)
+    for name, t in (("initial_state", initial_state), ("d_final_state", d_final_state)):
+        if t is not None:
+            _check(name, t, (B, H, dk, dv), torch.float32, dev)
+    shapes = {"dq": (B, T, H, dk), "dk": (B, T, H, dk), "dv": (B, T, H, dv), "dlog_alpha": (B, T, H, dk),
+              "db": (B, T, H, dk), "dw": (B, T, H, dv), "d_initial_state": (B, H, dk, dv)}
+    out = dict(grads) if grads is not None else {}
+    for name, shp in shapes.items():
+        if name == "d_initial_state" and not want_initial_state_grad:
+            out[name] = None
+            continue
+        if out.get(name) is None:
+            out[name] = torch.empty(shp, dtype=torch.float32, device=dev)
+        else:
+            _check(name, out[name], shp, torch.float32, dev)
+    need = chunk_bwd_workspace_bytes(B, T, H, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on %s" % dev)
+    st = _load().gdn2_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+                                _ptr(initial_state), _ptr(d_o), _ptr(d_final_state), _ptr(out["dq"]),
+                                _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlog_alpha"]), _ptr(out["db"]),
+                                _ptr(out["dw"]), _ptr(out["d_initial_state"]), _ptr(workspace),
+                                workspace.numel(), B, T, H, dk, dv, _DTYPES[dt], _stream_handle(dev))
+    if st != 0:
+        raise Gdn2Error("gdn2_chunk_bwd", st, _load().gdn2_status_string(st).decode())
+    return out

@@ -61,6 +61,30 @@ int device_cus() {
     return cus;
 }
 
+// Workspace of the backward pass: byte offsets of its five fp32 parts, each rounded up to 256
+// bytes.  False if the sizes overflow.
+struct BwdLayout {
+    int64_t s_ckpt, ds_ckpt, u, dr, tp, total;
+};
+bool bwd_layout(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, BwdLayout* l) {
+    if (B < 0 || T < 0 || H < 0 || dk < 0 || dv < 0) return false;
+    const int64_t nc = (T + 63) / 64;
+    int64_t bh, bhn, st, btv, tpn;
+    if (!mul_ok(B, H, &bh) || !mul_ok(bh, nc, &bhn) || !mul_ok(bhn, dk * dv, &st) || !mul_ok(st, 4, &st))
+        return false;
+    if (!mul_ok(B * H, T, &btv) || !mul_ok(btv, dv * 4, &btv)) return false;
+    if (!mul_ok(bhn, 2 * 64 * 64 * 4, &tpn)) return false;
+    auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+    if (st > INT64_MAX / 8 || btv > INT64_MAX / 8 || tpn > INT64_MAX / 8) return false;
+    l->s_ckpt = 0;
+    l->ds_ckpt = up(st);
+    l->u = l->ds_ckpt + up(st);
+    l->dr = l->u + up(btv);
+    l->tp = l->dr + up(btv);
+    l->total = l->tp + up(tpn);
+    return true;
+}
+
 // Validation and launch shared by the fixed-length and the packed-sequence forward.  NS
 // sequences (states [NS, H, dk, dv]); the token tensors hold NT tokens in all; T_or_total is
 // the kernels' token parameter (T per sequence, or the packed total).
@@ -171,8 +195,65 @@ gdn2_status_t gdn2_decode_step(const void* q, const void* k, const void* v, cons
     return gdn2::launch_decode_step(a) == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
+size_t gdn2_chunk_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv) {
+    BwdLayout l;
+    return bwd_layout(B, T, H, dk, dv, &l) ? (size_t)l.total : 0;
+}
+
+gdn2_status_t gdn2_chunk_bwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                             const void* b, const void* w, const float* initial_state, const float* d_o,
+                             const float* d_final_state, float* dq, float* dk, float* dv, float* dlog_alpha,
+                             float* db, float* dw, float* d_initial_state, void* workspace,
+                             size_t workspace_bytes, int64_t B, int64_t T, int64_t H, int64_t dk_dim,
+                             int64_t dv_dim, gdn2_dtype_t dtype, void* stream) {
+    if (!q || !k || !v || !log_alpha || !b || !w || !d_o) return GDN2_ERR_NULL;
+    if (!dq || !dk || !dv || !dlog_alpha || !db || !dw) return GDN2_ERR_NULL;
+    if (dtype != GDN2_DTYPE_F32 && dtype != GDN2_DTYPE_BF16) return GDN2_ERR_UNSUPPORTED;
+    if (B < 1 || T < 1 || H < 1 || dk_dim < 1 || dv_dim < 1) return GDN2_ERR_SHAPE;
+    if (!chunk_supported(dk_dim, dv_dim, dtype)) return GDN2_ERR_UNSUPPORTED;
+    int64_t BT, NTH, nk, nv, ns;
+    if (B > INT_MAX || T > INT_MAX || H > INT_MAX) return GDN2_ERR_SHAPE;
+    if (!mul_ok(B, T, &BT) || !mul_ok(BT, H, &NTH) || !mul_ok(NTH, dk_dim, &nk) || !mul_ok(NTH, dv_dim, &nv))
+        return GDN2_ERR_SHAPE;
+    if (!mul_ok(B * H, dk_dim * dv_dim, &ns)) return GDN2_ERR_SHAPE;
+    if (H * dk_dim >= (int64_t(1) << 24) || H * dv_dim >= (int64_t(1) << 24)) return GDN2_ERR_SHAPE;
+    BwdLayout l;
+    if (!bwd_layout(B, T, H, dk_dim, dv_dim, &l)) return GDN2_ERR_SHAPE;
+    if (B * H * ((T + 63) / 64) > UINT_MAX / 2 || B * H * (dv_dim / 16) > UINT_MAX / 2) return GDN2_ERR_SHAPE;
+    const void* ptrs[] = {q, k, v, log_alpha, b, w, initial_state, d_o, d_final_state, dq, dk, dv,
+                          dlog_alpha, db, dw, d_initial_state};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDN2_ERR_MISALIGNED;
+    if (!workspace || workspace_bytes < (size_t)l.total) return GDN2_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return GDN2_ERR_MISALIGNED;
+    const int64_t es = dtype == GDN2_DTYPE_BF16 ? 2 : 4;
+    const Range ins[] = {range_of(q, nk * es), range_of(k, nk * es), range_of(v, nv * es),
+                         range_of(log_alpha, nk * 4), range_of(b, nk * es), range_of(w, nv * es),
+                         range_of(initial_state, initial_state ? ns * 4 : 0), range_of(d_o, nv * 4),
+                         range_of(d_final_state, d_final_state ? ns * 4 : 0)};
+    const Range outs[] = {range_of(dq, nk * 4), range_of(dk, nk * 4), range_of(dv, nv * 4),
+                          range_of(dlog_alpha, nk * 4), range_of(db, nk * 4), range_of(dw, nv * 4),
+                          range_of(d_initial_state, d_initial_state ? ns * 4 : 0), range_of(workspace, l.total)};
+    constexpr int NO = sizeof(outs) / sizeof(outs[0]);
+    for (int i = 0; i < NO; ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r)) return GDN2_ERR_ALIAS;
+        for (int j = i + 1; j < NO; ++j)
+            if (overlap(outs[i], outs[j])) return GDN2_ERR_ALIAS;
+    }
+    const int cus = device_cus();
+    if (cus <= 0) return GDN2_ERR_HIP;
+    char* ws = static_cast<char*>(workspace);
+    gdn2::BwdArgs a{q, k, v, log_alpha, b, w, initial_state, d_o, d_final_state, dq, dk, dv, dlog_alpha, db,
+                    dw, d_initial_state, reinterpret_cast<float*>(ws + l.s_ckpt),
+                    reinterpret_cast<float*>(ws + l.ds_ckpt), reinterpret_cast<float*>(ws + l.u),
+                    reinterpret_cast<float*>(ws + l.dr), reinterpret_cast<float*>(ws + l.tp), B, T, H, dk_dim,
+                    dv_dim, dtype == GDN2_DTYPE_BF16, stream, cus};
+    return gdn2::launch_chunk_bwd(a) == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
 int gdn2_supported(int which, int64_t dk, int64_t dv, gdn2_dtype_t dtype) {
-    if (which == 0) return chunk_supported(dk, dv, dtype) ? 1 : 0;
+    if (which == 0 || which == 2) return chunk_supported(dk, dv, dtype) ? 1 : 0;
     if (which == 1) return decode_supported(dk, dv, dtype) ? 1 : 0;
     return 0;
 }
@@ -186,6 +267,7 @@ const char* gdn2_status_string(gdn2_status_t s) {
         case GDN2_ERR_MISALIGNED: return "a tensor pointer is not 16-byte aligned";
         case GDN2_ERR_ALIAS: return "an output overlaps an input";
         case GDN2_ERR_HIP: return "the HIP runtime rejected the call";
+        case GDN2_ERR_WORKSPACE: return "the workspace is missing or too small";
     }
     return "unknown status";
 }

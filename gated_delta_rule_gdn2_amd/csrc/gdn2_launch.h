@@ -40,10 +40,43 @@ struct DecodeArgs {
     void* stream;
 };
 
+// Backward pass (vector-Jacobian product) of the chunk forward, fixed-length sequences.
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* log_alpha;
+    const void* b;
+    const void* w;
+    const float* initial_state;  // or nullptr (zeros)
+    const float* d_o;            // [B,T,H,dv] fp32
+    const float* d_final_state;  // [B,H,dk,dv] fp32 or nullptr (zeros)
+    // gradients, fp32, laid out like their inputs; g_s0 may be nullptr
+    float* g_q;
+    float* g_k;
+    float* g_v;
+    float* g_log_alpha;
+    float* g_b;
+    float* g_w;
+    float* g_s0;
+    // workspace (fp32): states entering every chunk and dS' of every chunk [B,H,NC,dk,dv],
+    // U and dR [B,T,H,dv], T and P of every chunk [B,H,NC,2,64,64]
+    float* s_ckpt;
+    float* ds_ckpt;
+    float* u;
+    float* dr;
+    float* tp;
+    int64_t B, T, H, dk, dv;
+    bool dtype_bf16;
+    void* stream;
+    int cus;  // compute units of the device
+};
+
 // dvs: value columns per workgroup slice (16, 32 or 64)
 hipError_t launch_chunk_fwd(const ChunkArgs& a, int dvs);
 // bf16 inputs (dk = dv = 64 or 128)
 hipError_t launch_chunk_bf16(const ChunkArgs& a, int dvs);
 hipError_t launch_decode_step(const DecodeArgs& a);
+hipError_t launch_chunk_bwd(const BwdArgs& a);
 
 }  // namespace gdn2

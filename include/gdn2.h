@@ -13,10 +13,13 @@
  * per key channel, b_t in [0,1]^dk is the erase gate (key side) and
  * w_t in [0,1]^dv the write gate (value side).  There is no query scale.
  *
- * Two calls are exported: a chunk-parallel forward over whole sequences (the
- * same page, section "Gated Delta Rule-2", gives the chunk size of 64 used by
- * the fused training kernels) and a single-token recurrent decode step (the
- * page's opening section: decoding keeps a constant-size state).
+ * The calls: a chunk-parallel forward over whole sequences (the same page,
+ * section "Gated Delta Rule-2", gives the chunk size of 64 used by the fused
+ * training kernels), the same forward over packed sequences of different
+ * lengths, its backward pass (vector-Jacobian product; the same section: the
+ * gates enter the gradient inner products, so the backward is derived with
+ * them), and a single-token recurrent decode step (the page's opening section:
+ * decoding keeps a constant-size state).
  *
  * Conventions for every call:
  *   - Tensor pointers are DEVICE pointers (HIP global memory) of the current
@@ -61,7 +64,8 @@ typedef enum gdn2_status {
     GDN2_ERR_UNSUPPORTED = 3, /* (dk, dv, dtype) is not built into this library */
     GDN2_ERR_MISALIGNED = 4,  /* a tensor pointer is not 16-byte aligned */
     GDN2_ERR_ALIAS = 5,       /* an output overlaps an input it must not overlap */
-    GDN2_ERR_HIP = 6          /* the HIP runtime rejected a query or a launch */
+    GDN2_ERR_HIP = 6,         /* the HIP runtime rejected a query or a launch */
+    GDN2_ERR_WORKSPACE = 7    /* the workspace is NULL or smaller than required */
 } gdn2_status_t;
 
 /*
@@ -142,8 +146,51 @@ gdn2_status_t gdn2_decode_step(const void* q, const void* k, const void* v,
                                int64_t dv, gdn2_dtype_t dtype, gdn2_dtype_t o_dtype,
                                void* stream);
 
-/* 1 if gdn2_chunk_fwd (which = 0) or gdn2_decode_step (which = 1) supports
- * (dk, dv, dtype), else 0. */
+/*
+ * gdn2_chunk_bwd_workspace_bytes -- bytes of device workspace gdn2_chunk_bwd
+ * needs for these sizes (NC = ceil(T / 64)): 4 * (2 B H NC dk dv +
+ * 2 B T H dv + 2 B H NC 64 64), each of the five parts rounded up to 256 bytes.
+ * Returns 0 if the sizes overflow.
+ */
+size_t gdn2_chunk_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv);
+
+/*
+ * gdn2_chunk_bwd -- backward pass of gdn2_chunk_fwd: the gradients of
+ * L = sum(d_o * o) + sum(d_final_state * S_T) with respect to every input.
+ *
+ *   q, k, v, log_alpha, b, w, initial_state   as for gdn2_chunk_fwd (dtype)
+ *   d_o            [B, T, H, dv]  float32     upstream gradient of o
+ *   d_final_state  [B, H, dk, dv] float32     upstream gradient of S_T, or NULL
+ *                                             for zeros
+ *   dq, dk, db     [B, T, H, dk]  float32     out
+ *   dv, dw         [B, T, H, dv]  float32     out
+ *   dlog_alpha     [B, T, H, dk]  float32     out
+ *   d_initial_state [B, H, dk, dv] float32    out: gradient of S_0, or NULL to
+ *                                             skip (zeros S_0 when
+ *                                             initial_state is NULL)
+ *   workspace      device memory of at least
+ *                  gdn2_chunk_bwd_workspace_bytes(B, T, H, dk, dv) bytes,
+ *                  16-byte aligned, owned by the caller; its contents on entry
+ *                  do not matter and on return are unspecified
+ *
+ * The call re-runs the forward to recover the state entering every chunk, so
+ * it needs neither o nor any saved state.  Built combinations and the limits
+ * on sizes are those of gdn2_chunk_fwd (B, T >= 1).  No output may overlap
+ * another output, an input or the workspace, and the workspace may not
+ * overlap an input (GDN2_ERR_ALIAS); a missing or short workspace returns
+ * GDN2_ERR_WORKSPACE.
+ */
+gdn2_status_t gdn2_chunk_bwd(const void* q, const void* k, const void* v,
+                             const float* log_alpha, const void* b, const void* w,
+                             const float* initial_state, const float* d_o,
+                             const float* d_final_state, float* dq, float* dk, float* dv,
+                             float* dlog_alpha, float* db, float* dw, float* d_initial_state,
+                             void* workspace, size_t workspace_bytes, int64_t B, int64_t T,
+                             int64_t H, int64_t dk_dim, int64_t dv_dim, gdn2_dtype_t dtype,
+                             void* stream);
+
+/* 1 if gdn2_chunk_fwd and gdn2_chunk_fwd_varlen (which = 0), gdn2_decode_step
+ * (which = 1) or gdn2_chunk_bwd (which = 2) support (dk, dv, dtype), else 0. */
 int gdn2_supported(int which, int64_t dk, int64_t dv, gdn2_dtype_t dtype);
 
 /* Static, NUL-terminated description of a status code. */

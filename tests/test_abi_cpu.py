@@ -14,7 +14,7 @@ import gated_delta_rule_gdn2_amd as gdn2
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdn2.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_ALIAS, ERR_HIP = range(7)
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_ALIAS, ERR_HIP, ERR_WORKSPACE = range(8)
 BF16, F32 = 1, 0
 
 
@@ -31,9 +31,11 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(gdn2_[a-z_]+)\s*\(", text)))
 
 
-def test_header_declares_the_two_calls():
+def test_header_declares_the_calls():
     names = declared_functions()
-    assert "gdn2_chunk_fwd" in names and "gdn2_decode_step" in names
+    for name in ("gdn2_chunk_fwd", "gdn2_chunk_fwd_varlen", "gdn2_chunk_bwd", "gdn2_chunk_bwd_workspace_bytes",
+                 "gdn2_decode_step"):
+        assert name in names, name
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -42,8 +44,9 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    for s in range(7):
+    for s in range(8):
         assert lib.gdn2_status_string(s)
+    assert lib.gdn2_status_string(ERR_WORKSPACE) != lib.gdn2_status_string(99)
     assert gdn2.version().startswith("gdn2-gfx950")
 
 
@@ -55,7 +58,10 @@ def test_supported_table(lib):
     assert lib.gdn2_supported(0, 96, 96, BF16) == 0
     assert lib.gdn2_supported(1, 128, 128, F32) == 1
     assert lib.gdn2_supported(1, 32, 32, BF16) == 0
-    assert lib.gdn2_supported(2, 128, 128, BF16) == 0
+    assert lib.gdn2_supported(2, 128, 128, BF16) == 1
+    assert lib.gdn2_supported(2, 64, 64, F32) == 1
+    assert lib.gdn2_supported(2, 128, 128, F32) == 0
+    assert lib.gdn2_supported(3, 128, 128, BF16) == 0
 
 
 # --- validation paths (no HIP call is reached) ---------------------------------
@@ -63,8 +69,8 @@ def test_supported_table(lib):
 class Fake:
     """Distinct, 16-byte aligned, never-dereferenced addresses."""
 
-    def __init__(self, nbytes=1 << 20):
-        self.buf = ctypes.create_string_buffer(nbytes * 12 + 64)
+    def __init__(self, nbytes=1 << 20, slots=12):
+        self.buf = ctypes.create_string_buffer(nbytes * slots + 64)
         base = (ctypes.addressof(self.buf) + 15) & ~15
         self.nbytes = nbytes
         self.base = base
@@ -171,3 +177,47 @@ def test_varlen_validation(lib):
     # offsets inside o, final state overlapping the offsets
     assert varlen(lib, f, cu=f.p(7, 8)) == ERR_ALIAS
     assert varlen(lib, f, sT=f.p(9)) == ERR_ALIAS
+
+
+def test_bwd_workspace_bytes(lib):
+    # 4 bytes x (2 B H NC dk dv + 2 B T H dv + 2 B H NC 64 64), parts rounded to 256 bytes
+    B, T, H, d = 2, 130, 3, 64
+    nc = 3
+    parts = [B * H * nc * d * d * 4] * 2 + [B * T * H * d * 4] * 2 + [B * H * nc * 2 * 64 * 64 * 4]
+    assert lib.gdn2_chunk_bwd_workspace_bytes(B, T, H, d, d) == sum((x + 255) // 256 * 256 for x in parts)
+    assert gdn2.chunk_bwd_workspace_bytes(B, T, H, d, d) == lib.gdn2_chunk_bwd_workspace_bytes(B, T, H, d, d)
+    assert lib.gdn2_chunk_bwd_workspace_bytes(1 << 40, 1 << 40, 1, 64, 64) == 0
+
+
+def bwd(lib, f, B=1, T=64, H=1, dk=64, dv=64, dtype=BF16, ws_bytes=None, **over):
+    names = ("q k v g b w s0 do dsT gq gk gv gg gb gw gs0 ws").split()
+    args = {n: f.p(i) for i, n in enumerate(names)}
+    args["s0"] = args["dsT"] = args["gs0"] = None
+    args.update(over)
+    if ws_bytes is None:
+        ws_bytes = lib.gdn2_chunk_bwd_workspace_bytes(B, T, H, dk, dv)
+    return lib.gdn2_chunk_bwd(*[args[n] for n in names], ws_bytes, B, T, H, dk, dv, dtype, None)
+
+
+def test_bwd_validation(lib):
+    f = Fake(slots=18)
+    for name in ("q", "k", "v", "g", "b", "w", "do", "gq", "gk", "gv", "gg", "gb", "gw"):
+        assert bwd(lib, f, **{name: None}) == ERR_NULL, name
+    assert bwd(lib, f, B=0) == ERR_SHAPE
+    assert bwd(lib, f, T=0) == ERR_SHAPE
+    assert bwd(lib, f, dk=96, dv=96) == ERR_UNSUPPORTED
+    assert bwd(lib, f, dk=128, dv=128, dtype=F32) == ERR_UNSUPPORTED
+    assert bwd(lib, f, dtype=5) == ERR_UNSUPPORTED
+    assert bwd(lib, f, H=1 << 17, dk=128, dv=128) == ERR_SHAPE
+    assert bwd(lib, f, gq=f.p(9, 4)) == ERR_MISALIGNED
+    assert bwd(lib, f, ws=None) == ERR_WORKSPACE
+    need = lib.gdn2_chunk_bwd_workspace_bytes(1, 64, 1, 64, 64)
+    assert bwd(lib, f, ws_bytes=need - 1) == ERR_WORKSPACE
+    assert bwd(lib, f, ws=f.p(16, 8)) == ERR_MISALIGNED
+    # an output on an input, two outputs on each other, the workspace on an input or output
+    assert bwd(lib, f, gq=f.p(0)) == ERR_ALIAS
+    assert bwd(lib, f, gk=f.p(9, 64)) == ERR_ALIAS
+    assert bwd(lib, f, gs0=f.p(14, 16)) == ERR_ALIAS
+    assert bwd(lib, f, ws=f.p(7)) == ERR_ALIAS
+    assert bwd(lib, f, ws=f.p(14, 256)) == ERR_ALIAS
+    assert bwd(lib, f, s0=f.p(6), gs0=f.p(6, 32)) == ERR_ALIAS

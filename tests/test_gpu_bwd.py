@@ -1,0 +1,154 @@
+"""GPU parity of the backward pass (gdn2_chunk_bwd) against the fp64 oracle's reverse sweep.
+
+Every gradient (q, k, v, log alpha, b, w and the initial state) is compared with the oracle
+VJP on the same inputs, upstream gradients d_o and d_final_state included, with the
+forward's bars: max |x - x_ref| / RMS(x_ref) <= 1e-4 for fp32 inputs, 3e-2 for bf16 inputs.
+The cases span several chunks with a ragged tail, a single token, chunks whose decay takes
+the element-by-element path (whole-chunk decay below e^-40), a mix of both kinds, and the
+full fwd+bwd workload on sampled sequences."""
+import dataclasses
+
+import pytest
+import torch
+
+import gated_delta_rule_gdn2_amd as gdn2
+import oracle
+import workloads as W
+from tests.parity_util import TOL_BF16, TOL_F32, rel_max_err, say, take_sequences, to_dev
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("dq", "dk", "dv", "dlog_alpha", "db", "dw")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gdn2._load()
+
+
+def make_case(dtype, d, B, T, H, seed, s0_std=0.05, g_lo=-0.2, g_hi=-0.001, with_dsT=True):
+    wl = dataclasses.replace(W.FWD_BWD_4K, name="bwd", dtype=dtype, dk=d, dv=d, B=B, T=T, H=H,
+                             s0_std=s0_std, g_lo=g_lo, g_hi=g_hi)
+    inp = W.make_inputs(wl, seed=seed)
+    inp["do"] = W.make_upstream_grad(wl, seed=seed)
+    inp["dsT"] = W.make_upstream_state_grad(wl, seed=seed) if with_dsT else None
+    return inp
+
+
+def run_bwd(inp, **kw):
+    d = to_dev(inp)
+    g = gdn2.chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["do"], d["s0"], d["dsT"], **kw)
+    torch.cuda.synchronize()
+    return g
+
+
+def oracle_vjp(inp):
+    return oracle.vjp(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["b"], inp["w"], inp["do"],
+                      inp["s0"], inp["dsT"])
+
+
+def check(g, ref, tol, label, with_s0=True):
+    errs = {n: rel_max_err(g[n], ref[n]) for n in GRADS}
+    if with_s0 and g.get("d_initial_state") is not None:
+        errs["d_initial_state"] = rel_max_err(g["d_initial_state"], ref["ds0"])
+    say("  %-34s %s  (bar %.0e)" % (label, "  ".join("%s %.2e" % (n, e) for n, e in errs.items()), tol))
+    bad = {n: e for n, e in errs.items() if not e <= tol}
+    assert not bad, (label, bad)
+
+
+CASES = [
+    # dtype, d, B, T, H, seed, s0_std, with_dsT
+    (torch.float32, 64, 1, 150, 2, 301, 0.05, True),
+    (torch.float32, 64, 2, 64, 1, 302, None, False),
+    (torch.bfloat16, 64, 2, 128, 3, 303, None, False),
+    (torch.bfloat16, 64, 1, 100, 2, 304, 0.05, True),
+    (torch.bfloat16, 128, 1, 200, 2, 305, 0.05, True),
+    (torch.bfloat16, 128, 2, 64, 1, 306, None, True),
+]
+
+
+@pytest.mark.parametrize("dtype,d,B,T,H,seed,s0_std,with_dsT", CASES)
+def test_bwd_matches_oracle(dtype, d, B, T, H, seed, s0_std, with_dsT):
+    say("case: bwd %s d%d B%d T%d H%d seed %d s0 %s dS_T %s" % (dtype, d, B, T, H, seed, s0_std, with_dsT))
+    inp = make_case(dtype, d, B, T, H, seed, s0_std=s0_std, with_dsT=with_dsT)
+    g = run_bwd(inp)
+    check(g, oracle_vjp(inp), TOL_F32 if dtype == torch.float32 else TOL_BF16, "bwd", with_s0=True)
+
+
+def test_bwd_single_token():
+    say("case: bwd T=1, fp32 d64")
+    inp = make_case(torch.float32, 64, 3, 1, 2, 307)
+    check(run_bwd(inp), oracle_vjp(inp), TOL_F32, "T=1")
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64)])
+def test_bwd_strong_decay_chunks(dtype, d):
+    """log alpha in [-5, -1]: every chunk's decay is far below e^-40, so the per-chunk gradient
+    kernel takes its element-by-element path."""
+    say("case: bwd strong decay %s d%d" % (dtype, d))
+    inp = make_case(dtype, d, 1, 130, 2, 308, g_lo=-5.0, g_hi=-1.0)
+    check(run_bwd(inp), oracle_vjp(inp), TOL_F32 if dtype == torch.float32 else TOL_BF16, "strong decay")
+
+
+def test_bwd_mixed_chunk_kinds():
+    """Chunks 1, 3 and 5 of each sequence take log alpha in [-3, -1] (whole-chunk decay far below
+    e^-40, element-by-element path), the others the default [-0.2, -0.001] (pivoted path)."""
+    say("case: bwd mixed chunk kinds bf16 d128")
+    inp = make_case(torch.bfloat16, 128, 1, 512, 2, 309)
+    gen = torch.Generator("cpu").manual_seed(309)
+    for n in (1, 3, 5):
+        inp["log_alpha"][:, n * 64:(n + 1) * 64] = -1.0 - 2.0 * torch.rand((1, 64, 2, 128), generator=gen)
+    G = inp["log_alpha"].double().reshape(1, 8, 64, 2, 128).sum(2)  # whole-chunk log decays
+    kinds = (G.min(-1).values >= -40.0)
+    assert kinds.any() and (~kinds).any(), "expected both chunk kinds"
+    check(run_bwd(inp), oracle_vjp(inp), TOL_BF16, "mixed chunks")
+
+
+def test_bwd_without_initial_state_grad():
+    inp = make_case(torch.bfloat16, 64, 1, 96, 2, 310)
+    g_all = run_bwd(inp)
+    g_no = run_bwd(inp, want_initial_state_grad=False)
+    assert g_no["d_initial_state"] is None
+    for n in GRADS:
+        assert torch.equal(g_all[n], g_no[n]), n
+
+
+def test_bwd_state_gradient_only():
+    """d_o = 0: only dS_T drives the gradients; the oracle agrees, and dq is exactly zero
+    (q reaches nothing but o)."""
+    inp = make_case(torch.bfloat16, 128, 1, 96, 2, 311)
+    inp["do"] = torch.zeros_like(inp["do"])
+    g = run_bwd(inp)
+    assert torch.count_nonzero(g["dq"]) == 0
+    check(g, oracle_vjp(inp), TOL_BF16, "dS_T only")
+
+
+def test_bwd_deterministic():
+    inp = make_case(torch.bfloat16, 128, 1, 200, 2, 312)
+    a, b = run_bwd(inp), run_bwd(inp)
+    for n in GRADS + ("d_initial_state",):
+        assert torch.equal(a[n], b[n]), n
+
+
+def test_fwdbwd_workload_sampled():
+    """The fwd+bwd workload at full size (B=4, T=4096, H=16, d=128, bf16, S_0 ~ N(0, 0.02^2),
+    d_o ~ N(0,1)) in the launch the benchmark times; two (b, h) sequences against the oracle,
+    every gradient finite."""
+    wl = W.FWD_BWD_4K
+    say("case: %s sampled" % wl.name)
+    inp = W.make_inputs(wl)
+    inp["do"] = W.make_upstream_grad(wl)
+    inp["dsT"] = None
+    g = run_bwd(inp)
+    for n in GRADS + ("d_initial_state",):
+        assert torch.isfinite(g[n]).all(), n
+    pairs = [(0, 0), (3, 15)]
+    sub = take_sequences(inp, pairs)
+    sub["do"] = torch.stack([inp["do"][b, :, h] for b, h in pairs])[:, :, None].contiguous()
+    sub["dsT"] = None
+    ref = oracle_vjp(sub)
+    got = {n: torch.stack([g[n][b, :, h] for b, h in pairs])[:, :, None] for n in GRADS}
+    got["d_initial_state"] = torch.stack([g["d_initial_state"][b, h] for b, h in pairs])[:, None]
+    check(got, ref, TOL_BF16, "fwdbwd sampled")

@@ -131,6 +131,14 @@ def make_upstream_grad(wl: Workload, seed: Optional[int] = None, B=None, T=None)
     return torch.randn((B, T, wl.H, wl.dv), generator=gen, dtype=torch.float32)
 
 
+def make_upstream_state_grad(wl: Workload, seed: Optional[int] = None, B=None):
+    """dS_T ~ N(0,1) of the final state's shape [B,H,dk,dv], from its own stream."""
+    seed = (wl.seed if seed is None else seed) + 2_000_029
+    B = wl.B if B is None else B
+    gen = torch.Generator("cpu").manual_seed(seed)
+    return torch.randn((B, wl.H, wl.dk, wl.dv), generator=gen, dtype=torch.float32)
+
+
 def make_decode_pool(wl: Workload, seed: Optional[int] = None, N: Optional[int] = None):
     """Decode workload: initial state [N,H,dk,dv] fp32 ~ N(0, s0_std^2) and a pool
     of ``wl.pool`` token sets (q,k,v,log_alpha,b,w each [P,N,H,d]); step s uses
