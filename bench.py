@@ -165,6 +165,46 @@ def run_prefill(args, torch, gdn2, W, dev, out_dtype):
             "algorithmic_bytes_per_launch": nbytes}
 
 
+def bwd_bytes(B, T, H, dk, dv, in_bytes=2, s0=True):
+    """Algorithmic HBM bytes of one backward call: the inputs (q, k, b, v, w in the input
+    dtype, log alpha fp32), the upstream gradient d_o (fp32) and S_0, and the gradients written
+    (dq, dk, db, dlog alpha, dv, dw fp32, dS_0).  The workspace round trips (states entering
+    every chunk, their gradients, U, dR, T and P) are the implementation's, not the method's."""
+    ht = B * T * H
+    per_tok = (3 * dk + 2 * dv) * in_bytes + dk * 4 + dv * 4 + (4 * dk + 2 * dv) * 4
+    return ht * per_tok + (2 if s0 else 1) * B * H * dk * dv * 4
+
+
+def run_bwd(args, torch, gdn2, W, dev):
+    """Backward pass on the fwd+bwd workload: gradients of every input from d_o ~ N(0,1),
+    with S_0 ~ N(0, 0.02^2) and no upstream state gradient."""
+    wl = W.FWD_BWD_4K
+    inp = W.make_inputs(wl)
+    d = {n: (None if x is None else x.to(dev)) for n, x in inp.items()}
+    d_o = W.make_upstream_grad(wl).to(dev)
+    del inp
+    ws = torch.empty(gdn2.chunk_bwd_workspace_bytes(wl.B, wl.T, wl.H, wl.dk, wl.dv), dtype=torch.uint8,
+                     device=dev)
+    grads = gdn2.chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d_o, d["s0"], workspace=ws)
+
+    def step():
+        gdn2.chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d_o, d["s0"], workspace=ws,
+                       grads=grads)
+
+    ms = time_launches(step, args.steps, args.warmup, torch)
+    nbytes = bwd_bytes(wl.B, wl.T, wl.H, wl.dk, wl.dv)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    tokens = wl.B * wl.T
+    out = {"workload": wl.name, "us_per_call": ms * 1e3, "tokens_per_s": tokens / (ms * 1e-3), "GBps": gbps,
+           "peak": HBM_PEAK_GBPS, "frac": gbps / HBM_PEAK_GBPS, "algorithmic_bytes_per_call": nbytes,
+           "workspace_bytes": ws.numel(),
+           "kernels": "bwd_fwd_kernel (forward re-run), bwd_state_kernel (reverse pass), "
+                      "bwd_chunk_kernel (per-chunk gradients)"}
+    del d, d_o, ws, grads
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_decode(args, torch, gdn2, W, dev, out_dtype):
     """Decode workload: N=256 sequences x H=16, one token per step, state updated in place."""
     dwl = W.DECODE
@@ -200,7 +240,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out-bf16", action="store_true", help="write o in bf16 instead of fp32")
-    ap.add_argument("--only", choices=("chunk", "decode", "prefill"), default=None,
+    ap.add_argument("--only", choices=("chunk", "decode", "prefill", "bwd"), default=None,
                     help="time one workload only (profiler runs); prints its figures")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run only a plain device-to-device copy of MIB MiB (--steps times): "
@@ -235,6 +275,9 @@ def main():
     if args.only == "prefill":
         print(json.dumps({"prefill_varlen": run_prefill(args, torch, gdn2, W, dev, out_dtype)}))
         return
+    if args.only == "bwd":
+        print(json.dumps({"backward": run_bwd(args, torch, gdn2, W, dev)}))
+        return
     ms, wl, nbytes = run_chunk(args, torch, gdn2, W, dev, out_dtype)
     tokens = wl.B * wl.T
     achieved = nbytes / (ms * 1e-3) / 1e9
@@ -244,6 +287,7 @@ def main():
         return
     dec = run_decode(args, torch, gdn2, W, dev, out_dtype)
     pre = run_prefill(args, torch, gdn2, W, dev, out_dtype)
+    bwd = run_bwd(args, torch, gdn2, W, dev)
     flops = chunk_flops(wl.B, wl.T, wl.H, wl.dk, wl.dv)
 
     result = {
@@ -272,6 +316,7 @@ def main():
                                       "frac_of_bf16_peak": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}},
         "decode": dec,
         "prefill_varlen": pre,
+        "backward": bwd,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, torch)
