@@ -184,3 +184,7 @@ def vjp(q, k, v, log_alpha, b, w, d_o, initial_state=None, d_final_state=None, n
 
 def version() -> str:
     return _active().gdn2_oracle_version().decode()
+
+
+# the mixer around the recurrence (numpy, fp64): see oracle/mixer.py
+from .mixer import mixer_out, mixer_prep  # noqa: E402,F401
