@@ -10,6 +10,8 @@ the computation runs in the library's HIP kernels; there is no fallback.
     o, S_T = chunk_fwd_varlen(q, k, v, log_alpha, b, w, cu_seqlens)  # packed sequences
     o      = decode_step(q, k, v, log_alpha, b, w, state)   # state updated in place
     grads  = chunk_bwd(q, k, v, log_alpha, b, w, d_o, initial_state=None, d_final_state=None)
+    ins    = mixer_prep(xq, xk, xv, xb, xw, xa, conv_q, conv_k, conv_v)  # q, k, v, b, w, log_alpha
+    y      = mixer_out(o, z, gamma)                            # RMS norm and SiLU output gate
 
 Layouts: q, k, b, log_alpha [B,T,H,dk]; v, w, o [B,T,H,dv]; state [B,H,dk,dv]
 (packed: [total_T,H,d] with int64 offsets cu_seqlens [N+1] and states [N,H,dk,dv];
@@ -25,8 +27,8 @@ import threading
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_bwd", "chunk_bwd_workspace_bytes", "decode_step", "supported",
-           "version", "library_path", "Gdn2Error", "CHUNK"]
+__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_bwd", "chunk_bwd_workspace_bytes", "decode_step", "mixer_prep",
+           "mixer_out", "supported", "version", "library_path", "Gdn2Error", "CHUNK"]
 
 CHUNK = 64
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -70,6 +72,10 @@ def _load():
         lib.gdn2_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.gdn2_chunk_bwd.argtypes = [P] * 17 + [ctypes.c_size_t] + [I64] * 5 + [I32, P]
         lib.gdn2_chunk_bwd.restype = I32
+        lib.gdn2_mixer_prep.argtypes = [P] * 15 + [I64] * 5 + [ctypes.c_float, I32, P]
+        lib.gdn2_mixer_prep.restype = I32
+        lib.gdn2_mixer_out.argtypes = [P] * 4 + [I64] * 4 + [ctypes.c_float, I32, I32, P]
+        lib.gdn2_mixer_out.restype = I32
         lib.gdn2_supported.argtypes = [I32, I64, I64, I32]
         lib.gdn2_supported.restype = I32
         lib.gdn2_status_string.argtypes = [I32]
@@ -84,7 +90,7 @@ def version() -> str:
 
 
 def supported(which: str, dk: int, dv: int, dtype: torch.dtype) -> bool:
-    w = {"chunk_fwd": 0, "decode_step": 1, "chunk_bwd": 2}[which]
+    w = {"chunk_fwd": 0, "decode_step": 1, "chunk_bwd": 2, "mixer": 3}[which]
     return bool(_load().gdn2_supported(w, dk, dv, _DTYPES[dtype]))
 
 
@@ -281,3 +287,72 @@ def chunk_bwd(q, k, v, log_alpha, b, w, d_o, initial_state=None, d_final_state=N
     if st != 0:
         raise Gdn2Error("gdn2_chunk_bwd", st, _load().gdn2_status_string(st).decode())
     return out
+
+
+def mixer_prep(xq, xk, xv, xb, xw, xa, conv_q, conv_k, conv_v, eps=1e-6, *, out=None):
+    """The recurrence's inputs from the layer's projection outputs, in one pass:
+    q, k = L2(SiLU(conv(xq, xk))), v = SiLU(conv(xv)), b, w = sigmoid(xb, xw),
+    log_alpha = log sigmoid(xa).  x* [B,T,H,d] in one dtype (bf16 or fp32); conv_* [H*d, 4]
+    fp32 causal depthwise taps.  Returns a dict q, k, v, b, w (input dtype) and log_alpha
+    (fp32); ``out`` may hold preallocated outputs."""
+    if xq.dim() != 4:
+        raise ValueError("xq must be [B,T,H,dk]")
+    B, T, H, dk = xq.shape
+    dv = xv.shape[-1]
+    dev = xq.device
+    if dev.type != "cuda":
+        raise ValueError("mixer_prep runs on the GPU; got tensors on %s" % dev)
+    dt = xq.dtype
+    if dt not in _DTYPES:
+        raise TypeError("xq dtype must be float32 or bfloat16")
+    for name, t, shp, tdt in (("xk", xk, (B, T, H, dk), dt), ("xv", xv, (B, T, H, dv), dt),
+                              ("xb", xb, (B, T, H, dk), dt), ("xw", xw, (B, T, H, dv), dt),
+                              ("xa", xa, (B, T, H, dk), dt), ("xq", xq, (B, T, H, dk), dt),
+                              ("conv_q", conv_q, (H * dk, 4), torch.float32),
+                              ("conv_k", conv_k, (H * dk, 4), torch.float32),
+                              ("conv_v", conv_v, (H * dv, 4), torch.float32)):
+        _check(name, t, shp, tdt, dev)
+    shapes = {"q": ((B, T, H, dk), dt), "k": ((B, T, H, dk), dt), "v": ((B, T, H, dv), dt),
+              "b": ((B, T, H, dk), dt), "w": ((B, T, H, dv), dt), "log_alpha": ((B, T, H, dk), torch.float32)}
+    res = dict(out) if out is not None else {}
+    for name, (shp, tdt) in shapes.items():
+        if res.get(name) is None:
+            res[name] = torch.empty(shp, dtype=tdt, device=dev)
+        else:
+            _check(name, res[name], shp, tdt, dev)
+    st = _load().gdn2_mixer_prep(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(xb), _ptr(xw), _ptr(xa), _ptr(conv_q),
+                                 _ptr(conv_k), _ptr(conv_v), _ptr(res["q"]), _ptr(res["k"]), _ptr(res["v"]),
+                                 _ptr(res["b"]), _ptr(res["w"]), _ptr(res["log_alpha"]), B, T, H, dk, dv,
+                                 float(eps), _DTYPES[dt], _stream_handle(dev))
+    if st != 0:
+        raise Gdn2Error("gdn2_mixer_prep", st, _load().gdn2_status_string(st).decode())
+    return res
+
+
+def mixer_out(o, z, gamma, eps=1e-6, *, y=None):
+    """Layer output y = o / sqrt(mean(o^2) + eps) * gamma * SiLU(z) (mean over dv), in one
+    pass.  o [B,T,H,dv] fp32 or z's dtype; z [B,T,H,dv] bf16 or fp32; gamma [dv] fp32.
+    Returns y in z's dtype."""
+    if o.dim() != 4:
+        raise ValueError("o must be [B,T,H,dv]")
+    B, T, H, dv = o.shape
+    dev = o.device
+    if dev.type != "cuda":
+        raise ValueError("mixer_out runs on the GPU; got tensors on %s" % dev)
+    dt = z.dtype
+    if dt not in _DTYPES:
+        raise TypeError("z dtype must be float32 or bfloat16")
+    if o.dtype not in (torch.float32, dt):
+        raise TypeError("o must be float32 or z's dtype")
+    _check("o", o, (B, T, H, dv), o.dtype, dev)
+    _check("z", z, (B, T, H, dv), dt, dev)
+    _check("gamma", gamma, (dv,), torch.float32, dev)
+    if y is None:
+        y = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    else:
+        _check("y", y, (B, T, H, dv), dt, dev)
+    st = _load().gdn2_mixer_out(_ptr(o), _ptr(z), _ptr(gamma), _ptr(y), B, T, H, dv, float(eps), _DTYPES[dt],
+                                _DTYPES[o.dtype], _stream_handle(dev))
+    if st != 0:
+        raise Gdn2Error("gdn2_mixer_out", st, _load().gdn2_status_string(st).decode())
+    return y

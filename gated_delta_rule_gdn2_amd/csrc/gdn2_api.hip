@@ -36,6 +36,10 @@ bool chunk_supported(int64_t dk, int64_t dv, gdn2_dtype_t dt) {
     if (dt == GDN2_DTYPE_F32) return dk == 64 && dv == 64;
     return false;
 }
+bool mixer_supported(int64_t dk, int64_t dv, gdn2_dtype_t dt) {
+    if (dt != GDN2_DTYPE_BF16 && dt != GDN2_DTYPE_F32) return false;
+    return (dk == 128 && dv == 128) || (dk == 64 && dv == 64);
+}
 bool decode_supported(int64_t dk, int64_t dv, gdn2_dtype_t dt) {
     if (dt != GDN2_DTYPE_BF16 && dt != GDN2_DTYPE_F32) return false;
     return (dk == 128 && dv == 128) || (dk == 64 && dv == 64);
@@ -252,7 +256,66 @@ gdn2_status_t gdn2_chunk_bwd(const void* q, const void* k, const void* v, const 
     return gdn2::launch_chunk_bwd(a) == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
+gdn2_status_t gdn2_mixer_prep(const void* xq, const void* xk, const void* xv, const void* xb, const void* xw,
+                              const void* xa, const float* conv_q, const float* conv_k, const float* conv_v,
+                              void* q, void* k, void* v, void* b, void* w, float* log_alpha, int64_t B,
+                              int64_t T, int64_t H, int64_t dk, int64_t dv, float eps, gdn2_dtype_t dtype,
+                              void* stream) {
+    if (!xq || !xk || !xv || !xb || !xw || !xa || !conv_q || !conv_k || !conv_v) return GDN2_ERR_NULL;
+    if (!q || !k || !v || !b || !w || !log_alpha) return GDN2_ERR_NULL;
+    if (dtype != GDN2_DTYPE_F32 && dtype != GDN2_DTYPE_BF16) return GDN2_ERR_UNSUPPORTED;
+    if (B < 1 || T < 1 || H < 1 || dk < 1 || dv < 1 || !(eps >= 0.f) || eps > 1e30f) return GDN2_ERR_SHAPE;
+    if (!mixer_supported(dk, dv, dtype)) return GDN2_ERR_UNSUPPORTED;
+    int64_t BT, nk, nv, blocks;
+    if (B > INT_MAX || T > INT_MAX || H > INT_MAX) return GDN2_ERR_SHAPE;
+    if (!mul_ok(B, T, &BT) || !mul_ok(BT, H * dk, &nk) || !mul_ok(BT, H * dv, &nv)) return GDN2_ERR_SHAPE;
+    if (!mul_ok(B * H, (T + 63) / 64, &blocks) || blocks > INT_MAX) return GDN2_ERR_SHAPE;
+    const void* ptrs[] = {xq, xk, xv, xb, xw, xa, conv_q, conv_k, conv_v, q, k, v, b, w, log_alpha};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return GDN2_ERR_MISALIGNED;
+    const int64_t es = dtype == GDN2_DTYPE_BF16 ? 2 : 4;
+    const Range ins[] = {range_of(xq, nk * es), range_of(xk, nk * es), range_of(xv, nv * es), range_of(xb, nk * es),
+                         range_of(xw, nv * es), range_of(xa, nk * es), range_of(conv_q, H * dk * 16),
+                         range_of(conv_k, H * dk * 16), range_of(conv_v, H * dv * 16)};
+    const Range outs[] = {range_of(q, nk * es), range_of(k, nk * es), range_of(v, nv * es), range_of(b, nk * es),
+                          range_of(w, nv * es), range_of(log_alpha, nk * 4)};
+    constexpr int NO = sizeof(outs) / sizeof(outs[0]);
+    for (int i = 0; i < NO; ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r)) return GDN2_ERR_ALIAS;
+        for (int j = i + 1; j < NO; ++j)
+            if (overlap(outs[i], outs[j])) return GDN2_ERR_ALIAS;
+    }
+    gdn2::MixerPrepArgs a{xq, xk, xv, xb, xw, xa, conv_q, conv_k, conv_v, q, k, v, b, w, log_alpha,
+                          B, T, H, dk, dv, dtype == GDN2_DTYPE_BF16, eps, stream};
+    return gdn2::launch_mixer_prep(a) == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
+gdn2_status_t gdn2_mixer_out(const void* o, const void* z, const float* gamma, void* y, int64_t B, int64_t T,
+                             int64_t H, int64_t dv, float eps, gdn2_dtype_t dtype, gdn2_dtype_t o_dtype,
+                             void* stream) {
+    if (!o || !z || !gamma || !y) return GDN2_ERR_NULL;
+    if (dtype != GDN2_DTYPE_F32 && dtype != GDN2_DTYPE_BF16) return GDN2_ERR_UNSUPPORTED;
+    if (o_dtype != GDN2_DTYPE_F32 && o_dtype != dtype) return GDN2_ERR_UNSUPPORTED;
+    if (B < 1 || T < 1 || H < 1 || dv < 1 || !(eps >= 0.f) || eps > 1e30f) return GDN2_ERR_SHAPE;
+    if (!mixer_supported(dv, dv, dtype)) return GDN2_ERR_UNSUPPORTED;
+    int64_t rows, nv;
+    if (!mul_ok(B, T, &rows) || !mul_ok(rows, H, &rows) || !mul_ok(rows, dv, &nv)) return GDN2_ERR_SHAPE;
+    if ((rows + 3) / 4 > INT_MAX) return GDN2_ERR_SHAPE;
+    const void* ptrs[] = {o, z, gamma, y};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return GDN2_ERR_MISALIGNED;
+    const int64_t es = dtype == GDN2_DTYPE_BF16 ? 2 : 4;
+    const int64_t eo = o_dtype == GDN2_DTYPE_BF16 ? 2 : 4;
+    const Range ry = range_of(y, nv * es);
+    if (overlap(ry, range_of(o, nv * eo)) || overlap(ry, range_of(z, nv * es)) || overlap(ry, range_of(gamma, dv * 4)))
+        return GDN2_ERR_ALIAS;
+    gdn2::MixerOutArgs a{o, z, gamma, y, B, T, H, dv, dtype == GDN2_DTYPE_BF16, o_dtype == GDN2_DTYPE_F32, eps, stream};
+    return gdn2::launch_mixer_out(a) == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
 int gdn2_supported(int which, int64_t dk, int64_t dv, gdn2_dtype_t dtype) {
+    if (which == 3) return mixer_supported(dk, dv, dtype) ? 1 : 0;
     if (which == 0 || which == 2) return chunk_supported(dk, dv, dtype) ? 1 : 0;
     if (which == 1) return decode_supported(dk, dv, dtype) ? 1 : 0;
     return 0;

@@ -72,11 +72,48 @@ struct BwdArgs {
     int cus;  // compute units of the device
 };
 
+// The mixer's fused elementwise passes before and after the recurrence.
+struct MixerPrepArgs {
+    const void* xq;
+    const void* xk;
+    const void* xv;
+    const void* xb;
+    const void* xw;
+    const void* xa;
+    const float* conv_q;  // [H*dk][4]
+    const float* conv_k;  // [H*dk][4]
+    const float* conv_v;  // [H*dv][4]
+    void* q;
+    void* k;
+    void* v;
+    void* b;
+    void* w;
+    float* log_alpha;
+    int64_t B, T, H, dk, dv;
+    bool dtype_bf16;
+    float eps;
+    void* stream;
+};
+
+struct MixerOutArgs {
+    const void* o;
+    const void* z;
+    const float* gamma;  // [dv]
+    void* y;
+    int64_t B, T, H, dv;
+    bool dtype_bf16;  // z and y (and o unless o_f32)
+    bool o_f32;
+    float eps;
+    void* stream;
+};
+
 // dvs: value columns per workgroup slice (16, 32 or 64)
 hipError_t launch_chunk_fwd(const ChunkArgs& a, int dvs);
 // bf16 inputs (dk = dv = 64 or 128)
 hipError_t launch_chunk_bf16(const ChunkArgs& a, int dvs);
 hipError_t launch_decode_step(const DecodeArgs& a);
 hipError_t launch_chunk_bwd(const BwdArgs& a);
+hipError_t launch_mixer_prep(const MixerPrepArgs& a);
+hipError_t launch_mixer_out(const MixerOutArgs& a);
 
 }  // namespace gdn2

@@ -18,8 +18,9 @@
  * training kernels), the same forward over packed sequences of different
  * lengths, its backward pass (vector-Jacobian product; the same section: the
  * gates enter the gradient inner products, so the backward is derived with
- * them), and a single-token recurrent decode step (the page's opening section:
- * decoding keeps a constant-size state).
+ * them), a single-token recurrent decode step (the page's opening section:
+ * decoding keeps a constant-size state), and the mixer's fused elementwise
+ * passes on either side of the recurrence.
  *
  * Conventions for every call:
  *   - Tensor pointers are DEVICE pointers (HIP global memory) of the current
@@ -189,8 +190,58 @@ gdn2_status_t gdn2_chunk_bwd(const void* q, const void* k, const void* v,
                              int64_t H, int64_t dk_dim, int64_t dv_dim, gdn2_dtype_t dtype,
                              void* stream);
 
+/*
+ * gdn2_mixer_prep -- the elementwise steps between the layer's projections and
+ * the recurrence, in one pass (page "Why NVIDIA Gated DeltaNet-2 separates
+ * erase and write gates", the section on the layer's architecture: query and
+ * key through a short causal convolution, SiLU and L2 normalisation, value
+ * through the convolution and SiLU; section "Gated Delta Rule-2": erase and
+ * write gates are sigmoids of projections):
+ *
+ *   q = xq' / sqrt(|xq'|^2 + eps),  xq' = SiLU(conv(xq))   (norm over dk)
+ *   k likewise from xk;  v = SiLU(conv(xv))
+ *   b = sigmoid(xb),  w = sigmoid(xw),  log_alpha = log sigmoid(xa)
+ *
+ *   xq, xk, xb, xa  [B, T, H, dk]  dtype   projection outputs (pre-activation)
+ *   xv, xw          [B, T, H, dv]  dtype
+ *   conv_q, conv_k  [H * dk, 4]    float32 depthwise causal taps: tap j of a
+ *   conv_v          [H * dv, 4]    float32 channel multiplies its input at token
+ *                                          t - 3 + j; tokens before 0 are zero
+ *   q, k, b         [B, T, H, dk]  dtype   out
+ *   v, w            [B, T, H, dv]  dtype   out
+ *   log_alpha       [B, T, H, dk]  float32 out (<= 0)
+ *
+ * The sigmoid form of the decay is this library's reading: the pages give the
+ * decay no activation.  Built: dtype BF16 or F32 with dk = dv = 64 or 128.  No
+ * output may overlap an input or another output.  eps >= 0.
+ */
+gdn2_status_t gdn2_mixer_prep(const void* xq, const void* xk, const void* xv, const void* xb,
+                              const void* xw, const void* xa, const float* conv_q,
+                              const float* conv_k, const float* conv_v, void* q, void* k,
+                              void* v, void* b, void* w, float* log_alpha, int64_t B, int64_t T,
+                              int64_t H, int64_t dk, int64_t dv, float eps, gdn2_dtype_t dtype,
+                              void* stream);
+
+/*
+ * gdn2_mixer_out -- the layer output from the recurrence output, in one pass
+ * (same page and section: RMS normalisation and a SiLU output gate):
+ *
+ *   y = o / sqrt(mean(o^2) + eps) * gamma * SiLU(z)      (mean over dv)
+ *
+ *   o      [B, T, H, dv]  o_dtype  recurrence output (F32, or equal to dtype)
+ *   z      [B, T, H, dv]  dtype    output-gate projection
+ *   gamma  [dv]           float32  norm weight, shared by the heads
+ *   y      [B, T, H, dv]  dtype    out; must not overlap o, z or gamma
+ *
+ * Built: dtype BF16 or F32 with dv = 64 or 128.  eps >= 0.
+ */
+gdn2_status_t gdn2_mixer_out(const void* o, const void* z, const float* gamma, void* y, int64_t B,
+                             int64_t T, int64_t H, int64_t dv, float eps, gdn2_dtype_t dtype,
+                             gdn2_dtype_t o_dtype, void* stream);
+
 /* 1 if gdn2_chunk_fwd and gdn2_chunk_fwd_varlen (which = 0), gdn2_decode_step
- * (which = 1) or gdn2_chunk_bwd (which = 2) support (dk, dv, dtype), else 0. */
+ * (which = 1), gdn2_chunk_bwd (which = 2) or gdn2_mixer_prep and gdn2_mixer_out
+ * (which = 3) support (dk, dv, dtype), else 0. */
 int gdn2_supported(int which, int64_t dk, int64_t dv, gdn2_dtype_t dtype);
 
 /* Static, NUL-terminated description of a status code. */

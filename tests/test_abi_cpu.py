@@ -34,7 +34,7 @@ def declared_functions():
 def test_header_declares_the_calls():
     names = declared_functions()
     for name in ("gdn2_chunk_fwd", "gdn2_chunk_fwd_varlen", "gdn2_chunk_bwd", "gdn2_chunk_bwd_workspace_bytes",
-                 "gdn2_decode_step"):
+                 "gdn2_decode_step", "gdn2_mixer_prep", "gdn2_mixer_out"):
         assert name in names, name
 
 
@@ -61,7 +61,10 @@ def test_supported_table(lib):
     assert lib.gdn2_supported(2, 128, 128, BF16) == 1
     assert lib.gdn2_supported(2, 64, 64, F32) == 1
     assert lib.gdn2_supported(2, 128, 128, F32) == 0
-    assert lib.gdn2_supported(3, 128, 128, BF16) == 0
+    assert lib.gdn2_supported(3, 128, 128, BF16) == 1
+    assert lib.gdn2_supported(3, 128, 128, F32) == 1
+    assert lib.gdn2_supported(3, 96, 96, BF16) == 0
+    assert lib.gdn2_supported(4, 128, 128, BF16) == 0
 
 
 # --- validation paths (no HIP call is reached) ---------------------------------
@@ -221,3 +224,40 @@ def test_bwd_validation(lib):
     assert bwd(lib, f, ws=f.p(7)) == ERR_ALIAS
     assert bwd(lib, f, ws=f.p(14, 256)) == ERR_ALIAS
     assert bwd(lib, f, s0=f.p(6), gs0=f.p(6, 32)) == ERR_ALIAS
+
+
+def prep(lib, f, B=1, T=64, H=1, dk=64, dv=64, eps=1e-6, dtype=BF16, **over):
+    names = "xq xk xv xb xw xa cq ck cv q k v b w g".split()
+    args = {n: f.p(i) for i, n in enumerate(names)}
+    args.update(over)
+    return lib.gdn2_mixer_prep(*[args[n] for n in names], B, T, H, dk, dv, eps, dtype, None)
+
+
+def mout(lib, f, B=1, T=64, H=1, dv=64, eps=1e-6, dtype=BF16, odt=F32, **over):
+    args = dict(o=f.p(0), z=f.p(1), gamma=f.p(2), y=f.p(3))
+    args.update(over)
+    return lib.gdn2_mixer_out(args["o"], args["z"], args["gamma"], args["y"], B, T, H, dv, eps, dtype, odt, None)
+
+
+def test_mixer_validation(lib):
+    f = Fake(slots=16)
+    for name in "xq xk xv xb xw xa cq ck cv q k v b w g".split():
+        assert prep(lib, f, **{name: None}) == ERR_NULL, name
+    assert prep(lib, f, T=0) == ERR_SHAPE
+    assert prep(lib, f, eps=-1.0) == ERR_SHAPE
+    assert prep(lib, f, eps=float("nan")) == ERR_SHAPE
+    assert prep(lib, f, dk=96, dv=96) == ERR_UNSUPPORTED
+    assert prep(lib, f, dk=64, dv=128) == ERR_UNSUPPORTED
+    assert prep(lib, f, dtype=3) == ERR_UNSUPPORTED
+    assert prep(lib, f, q=f.p(9, 2)) == ERR_MISALIGNED
+    assert prep(lib, f, q=f.p(0)) == ERR_ALIAS
+    assert prep(lib, f, v=f.p(9, 64)) == ERR_ALIAS
+    assert prep(lib, f, g=f.p(6)) == ERR_ALIAS
+    for name in ("o", "z", "gamma", "y"):
+        assert mout(lib, f, **{name: None}) == ERR_NULL, name
+    assert mout(lib, f, H=0) == ERR_SHAPE
+    assert mout(lib, f, dv=32) == ERR_UNSUPPORTED
+    assert mout(lib, f, dtype=F32, odt=BF16) == ERR_UNSUPPORTED
+    assert mout(lib, f, y=f.p(3, 4)) == ERR_MISALIGNED
+    assert mout(lib, f, y=f.p(0, 64)) == ERR_ALIAS
+    assert mout(lib, f, y=f.p(2)) == ERR_ALIAS

@@ -139,6 +139,33 @@ def make_upstream_state_grad(wl: Workload, seed: Optional[int] = None, B=None):
     return torch.randn((B, wl.H, wl.dk, wl.dv), generator=gen, dtype=torch.float32)
 
 
+def make_mixer_inputs(wl: Workload, seed: Optional[int] = None, B=None, T=None):
+    """The mixer's inputs for a workload's shape, from their own stream: projection outputs
+    xq, xk, xv ~ N(0,1); gate logits xb, xw ~ N(0, 2^2); decay logits xa ~ U[2, 7] (so that
+    log sigmoid(xa) lies in [-0.13, -0.001], the range of the workloads' log alpha); causal
+    taps ~ U[-0.5, 0.5] with the current-token tap U[0.5, 1.5]; output-gate logits
+    z ~ N(0,1); norm weight gamma ~ U[0.5, 1.5].  Projection outputs, gate logits and z in
+    the workload's dtype; taps and gamma fp32."""
+    seed = (wl.seed if seed is None else seed) + 3_000_041
+    B = wl.B if B is None else B
+    T = wl.T if T is None else T
+    H, dk, dv, dt = wl.H, wl.dk, wl.dv, wl.dtype
+    gen = torch.Generator("cpu").manual_seed(seed)
+    out = {}
+    for name, d in (("xq", dk), ("xk", dk), ("xv", dv)):
+        out[name] = torch.randn((B, T, H, d), generator=gen, dtype=torch.float32).to(dt)
+    for name, d in (("xb", dk), ("xw", dv)):
+        out[name] = (2.0 * torch.randn((B, T, H, d), generator=gen, dtype=torch.float32)).to(dt)
+    out["xa"] = _uniform(gen, (B, T, H, dk), 2.0, 7.0).to(dt)
+    for name, d in (("conv_q", dk), ("conv_k", dk), ("conv_v", dv)):
+        taps = _uniform(gen, (H * d, 4), -0.5, 0.5)
+        taps[:, 3] = _uniform(gen, (H * d,), 0.5, 1.5)
+        out[name] = taps.contiguous()
+    out["z"] = torch.randn((B, T, H, dv), generator=gen, dtype=torch.float32).to(dt)
+    out["gamma"] = _uniform(gen, (dv,), 0.5, 1.5)
+    return out
+
+
 def make_decode_pool(wl: Workload, seed: Optional[int] = None, N: Optional[int] = None):
     """Decode workload: initial state [N,H,dk,dv] fp32 ~ N(0, s0_std^2) and a pool
     of ``wl.pool`` token sets (q,k,v,log_alpha,b,w each [P,N,H,d]); step s uses
