@@ -205,6 +205,38 @@ def run_bwd(args, torch, gdn2, W, dev):
     return out
 
 
+def mixer_bytes(B, T, H, dk, dv, in_bytes=2, o_bytes=4):
+    """Algorithmic HBM bytes of the two fused mixer passes.  prep: the six projection outputs
+    read, q, k, v, b, w (input dtype) and log alpha (fp32) written, and the taps; out: o and z
+    read, y written, and gamma."""
+    ht = B * T * H
+    prep = ht * ((4 * dk + 2 * dv) * in_bytes + (3 * dk + 2 * dv) * in_bytes + dk * 4) + H * (2 * dk + dv) * 16
+    out = ht * (dv * o_bytes + 2 * dv * in_bytes) + dv * 4
+    return prep, out
+
+
+def run_mixer(args, torch, gdn2, W, dev):
+    """The mixer's fused passes on the training shape: prep (projection outputs to the
+    recurrence's inputs) and out (RMS norm and SiLU gate of an fp32 recurrence output)."""
+    wl = W.TRAIN_4K
+    x = {n: t.to(dev) for n, t in W.make_mixer_inputs(wl).items()}
+    names = ("xq", "xk", "xv", "xb", "xw", "xa", "conv_q", "conv_k", "conv_v")
+    res = gdn2.mixer_prep(*[x[n] for n in names])
+    o = torch.randn((wl.B, wl.T, wl.H, wl.dv), dtype=torch.float32, device=dev)
+    y = gdn2.mixer_out(o, x["z"], x["gamma"])
+    ms_p = time_launches(lambda: gdn2.mixer_prep(*[x[n] for n in names], out=res), args.steps, args.warmup, torch)
+    ms_o = time_launches(lambda: gdn2.mixer_out(o, x["z"], x["gamma"], y=y), args.steps, args.warmup, torch)
+    bp, bo = mixer_bytes(wl.B, wl.T, wl.H, wl.dk, wl.dv)
+    gp, go = bp / (ms_p * 1e-3) / 1e9, bo / (ms_o * 1e-3) / 1e9
+    del x, res, o, y
+    torch.cuda.empty_cache()
+    return {"workload": wl.name,
+            "prep": {"kernel": "prep_kernel", "us_per_launch": ms_p * 1e3, "GBps": gp, "peak": HBM_PEAK_GBPS,
+                     "frac": gp / HBM_PEAK_GBPS, "algorithmic_bytes_per_launch": bp},
+            "out": {"kernel": "out_kernel", "us_per_launch": ms_o * 1e3, "GBps": go, "peak": HBM_PEAK_GBPS,
+                    "frac": go / HBM_PEAK_GBPS, "algorithmic_bytes_per_launch": bo}}
+
+
 def run_decode(args, torch, gdn2, W, dev, out_dtype):
     """Decode workload: N=256 sequences x H=16, one token per step, state updated in place."""
     dwl = W.DECODE
@@ -240,7 +272,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out-bf16", action="store_true", help="write o in bf16 instead of fp32")
-    ap.add_argument("--only", choices=("chunk", "decode", "prefill", "bwd"), default=None,
+    ap.add_argument("--only", choices=("chunk", "decode", "prefill", "bwd", "mixer"), default=None,
                     help="time one workload only (profiler runs); prints its figures")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run only a plain device-to-device copy of MIB MiB (--steps times): "
@@ -278,6 +310,9 @@ def main():
     if args.only == "bwd":
         print(json.dumps({"backward": run_bwd(args, torch, gdn2, W, dev)}))
         return
+    if args.only == "mixer":
+        print(json.dumps({"mixer": run_mixer(args, torch, gdn2, W, dev)}))
+        return
     ms, wl, nbytes = run_chunk(args, torch, gdn2, W, dev, out_dtype)
     tokens = wl.B * wl.T
     achieved = nbytes / (ms * 1e-3) / 1e9
@@ -288,6 +323,7 @@ def main():
     dec = run_decode(args, torch, gdn2, W, dev, out_dtype)
     pre = run_prefill(args, torch, gdn2, W, dev, out_dtype)
     bwd = run_bwd(args, torch, gdn2, W, dev)
+    mixer = run_mixer(args, torch, gdn2, W, dev)
     flops = chunk_flops(wl.B, wl.T, wl.H, wl.dk, wl.dv)
 
     result = {
@@ -317,6 +353,7 @@ def main():
         "decode": dec,
         "prefill_varlen": pre,
         "backward": bwd,
+        "mixer": mixer,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, torch)

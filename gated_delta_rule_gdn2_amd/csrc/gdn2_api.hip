@@ -269,7 +269,8 @@ gdn2_status_t gdn2_mixer_prep(const void* xq, const void* xk, const void* xv, co
     int64_t BT, nk, nv, blocks;
     if (B > INT_MAX || T > INT_MAX || H > INT_MAX) return GDN2_ERR_SHAPE;
     if (!mul_ok(B, T, &BT) || !mul_ok(BT, H * dk, &nk) || !mul_ok(BT, H * dv, &nv)) return GDN2_ERR_SHAPE;
-    if (!mul_ok(B * H, (T + 63) / 64, &blocks) || blocks > INT_MAX) return GDN2_ERR_SHAPE;
+    // workgroups: B x ceil(T / 4) x ceil(H / heads per wave), bounded here by B H ceil(T / 4)
+    if (!mul_ok(B * H, (T + 3) / 4, &blocks) || blocks > INT_MAX) return GDN2_ERR_SHAPE;
     const void* ptrs[] = {xq, xk, xv, xb, xw, xa, conv_q, conv_k, conv_v, q, k, v, b, w, log_alpha};
     for (const void* p : ptrs)
         if (!aligned16(p)) return GDN2_ERR_MISALIGNED;

@@ -12,177 +12,210 @@
 // The convolution is depthwise and causal with 4 taps: tap j of a channel multiplies its input
 // at token t - 3 + j, and tokens before the start of the sequence are zero.
 //
-// prep: one workgroup per (sequence, head, block of 64 tokens) with DK + DV threads; thread c <
-// DK owns key channel c (q, k, b, log alpha), the others own value channels (v, w).  Each
-// thread walks the block's tokens with the last three convolution inputs in registers, so
-// every input element is read once (plus three tokens before the block).  SiLU(conv) of q and
-// k goes to LDS; one wave per (token, q or k) row forms its norm; the key threads then scale
-// and store.  out: one wave per (token, head) row.
+// prep: eight key and eight value channels per lane, a head per D / 8 lanes, a run of
+// consecutive tokens per wave with the convolution window in registers; the L2 norms of q and
+// k are reductions over a head's lanes (no LDS, no barrier).  out: rows of
+// dv fp32 values, four per lane (16-byte loads), two rows per wave at dv = 128.
 #include "gdn2_device.h"
 #include "gdn2_launch.h"
 
 namespace gdn2 {
 namespace mix {
 
-constexpr int TBK = 64;  // tokens per prep workgroup
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int NTW = 16;  // consecutive tokens per prep workgroup
 
+constexpr float kLn2 = 0.6931471805599453f;
+
+// The activations use the hardware base-2 exponential and logarithm and the hardware
+// reciprocal (about 1 ulp each); these passes are limited by vector ALU issue, not by HBM,
+// once IEEE division and a library log1p are in them.
 __device__ __forceinline__ float sigmoid_f(float x) {
     // 1 / (1 + e^-x) without overflow: e^-|x| <= 1
     const float e = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
-    const float r = 1.f / (1.f + e);
+    const float r = __builtin_amdgcn_rcpf(1.f + e);
     return x >= 0.f ? r : e * r;
 }
 __device__ __forceinline__ float log_sigmoid_f(float x) {
-    // min(x, 0) - log(1 + e^-|x|)
-    return fminf(x, 0.f) - log1pf(__builtin_amdgcn_exp2f(-fabsf(x) * kLog2e));
+    // min(x, 0) - log(1 + e), e = e^-|x| in (0, 1]; log(1 + e) by its series below 2^-7
+    // (three terms, error < e^4 / 4), else through the hardware logarithm
+    const float e = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
+    const float l = e < 0.0078125f ? e * (1.f - e * (0.5f - e * (1.f / 3.f)))
+                                   : __builtin_amdgcn_logf(1.f + e) * kLn2;
+    return fminf(x, 0.f) - l;
 }
 __device__ __forceinline__ float silu_f(float x) { return x * sigmoid_f(x); }
 
-__device__ __forceinline__ float wave_sum(float x) {
+// wave-wide sum over lanes [base, base + width) with width a power of two <= 64
+template <int WIDTH>
+__device__ __forceinline__ float group_sum(float x) {
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+    for (int m = WIDTH / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m);
     return x;
 }
 
+template <typename In, int N>
+__device__ __forceinline__ void store_n(In* p, const float (&x)[N]) {
+    if constexpr (N == 1) {
+        *p = from_f32<In>(x[0]);
+    } else {
+        typedef In V __attribute__((ext_vector_type(N)));
+        V v;
+#pragma unroll
+        for (int e = 0; e < N; ++e) v[e] = from_f32<In>(x[e]);
+        *reinterpret_cast<V*>(p) = v;
+    }
+}
+
+// Eight channels per lane (16-byte bf16 accesses): a head's D channels take D / 8 lanes, so a
+// wave holds 64 * 8 / D heads.  A workgroup has three waves for the same heads and the same
+// run of NTW consecutive tokens: wave 0 makes q (and b), wave 1 k (and log alpha), wave 2 v
+// (and w).  Each walks the run with its four taps per channel and the last three convolution
+// inputs in registers, so every input row is read once, plus three rows before the run; the
+// L2 norms are reductions over a head's lanes (no LDS, no barrier).
 template <typename In, int DK, int DV>
-__global__ __launch_bounds__(DK + DV) void prep_kernel(
+__global__ __launch_bounds__(192) void prep_kernel(
     const In* __restrict__ xq, const In* __restrict__ xk, const In* __restrict__ xv,
     const In* __restrict__ xb, const In* __restrict__ xw, const In* __restrict__ xa,
     const float* __restrict__ cq, const float* __restrict__ ck, const float* __restrict__ cv,
     In* __restrict__ q, In* __restrict__ k, In* __restrict__ v, In* __restrict__ b, In* __restrict__ w,
-    float* __restrict__ log_alpha, int T, int H, int nblk, float eps) {
-    constexpr int NTH = DK + DV;
-    __shared__ float sU[2][TBK][DK];  // SiLU(conv) of q and k
-    __shared__ float sInv[2][TBK];    // 1 / sqrt(sum of squares + eps)
-    const int tid = threadIdx.x;
-    const int blk = blockIdx.x % nblk, bh = blockIdx.x / nblk;
-    const int bi = bh / H, h = bh % H;
-    const int t0 = blk * TBK;
-    const int nt = min(TBK, T - t0);
-    const bool key = tid < DK;
-    const int c = key ? tid : tid - DK;
-    const int D = key ? DK : DV;
-    // element (t, h, c) of sequence bi: ((bi * T + t) * H + h) * D + c
-    const int64_t base = ((int64_t)bi * T * H + h) * D + c;
-    const int64_t stride = (int64_t)H * D;
-
-    if (key) {
-        const f32x4 wq = *reinterpret_cast<const f32x4*>(cq + (int64_t)(h * DK + c) * 4);
-        const f32x4 wk = *reinterpret_cast<const f32x4*>(ck + (int64_t)(h * DK + c) * 4);
-        float q1 = 0.f, q2 = 0.f, q3 = 0.f, k1 = 0.f, k2 = 0.f, k3 = 0.f;  // inputs at t-1, t-2, t-3
-        if (t0 >= 3) {
-            q3 = to_f32(xq[base + (t0 - 3) * stride]);
-            k3 = to_f32(xk[base + (t0 - 3) * stride]);
-        }
-        if (t0 >= 2) {
-            q2 = to_f32(xq[base + (t0 - 2) * stride]);
-            k2 = to_f32(xk[base + (t0 - 2) * stride]);
-        }
-        if (t0 >= 1) {
-            q1 = to_f32(xq[base + (t0 - 1) * stride]);
-            k1 = to_f32(xk[base + (t0 - 1) * stride]);
-        }
-        for (int i = 0; i < nt; ++i) {
-            const int64_t o = base + (t0 + i) * stride;
-            const float xq0 = to_f32(xq[o]), xk0 = to_f32(xk[o]);
-            const float yq = wq[0] * q3 + wq[1] * q2 + wq[2] * q1 + wq[3] * xq0;
-            const float yk = wk[0] * k3 + wk[1] * k2 + wk[2] * k1 + wk[3] * xk0;
-            sU[0][i][c] = silu_f(yq);
-            sU[1][i][c] = silu_f(yk);
-            q3 = q2; q2 = q1; q1 = xq0;
-            k3 = k2; k2 = k1; k1 = xk0;
-            b[o] = from_f32<In>(sigmoid_f(to_f32(xb[o])));
-            log_alpha[o] = log_sigmoid_f(to_f32(xa[o]));
-        }
-    } else {
-        const f32x4 wv = *reinterpret_cast<const f32x4*>(cv + (int64_t)(h * DV + c) * 4);
-        float v1 = 0.f, v2 = 0.f, v3 = 0.f;
-        if (t0 >= 3) v3 = to_f32(xv[base + (t0 - 3) * stride]);
-        if (t0 >= 2) v2 = to_f32(xv[base + (t0 - 2) * stride]);
-        if (t0 >= 1) v1 = to_f32(xv[base + (t0 - 1) * stride]);
-        for (int i = 0; i < nt; ++i) {
-            const int64_t o = base + (t0 + i) * stride;
-            const float xv0 = to_f32(xv[o]);
-            const float yv = wv[0] * v3 + wv[1] * v2 + wv[2] * v1 + wv[3] * xv0;
-            v3 = v2; v2 = v1; v1 = xv0;
-            v[o] = from_f32<In>(silu_f(yv));
-            w[o] = from_f32<In>(sigmoid_f(to_f32(xw[o])));
-        }
-    }
-    __syncthreads();
-    // norms: one wave per (q or k, token) row
-    constexpr int NW = NTH / 64;
-    const int wave = tid >> 6, lane = tid & 63;
-    for (int row = wave; row < 2 * nt; row += NW) {
-        const int which = row / nt, i = row % nt;
-        float s = 0.f;
+    float* __restrict__ log_alpha, int T, int H, int nrun, int nhg, float eps) {
+    static_assert(DK == DV, "one head per lane group");
+    constexpr int CH = 8, LPH = DK / CH;  // channels per lane, lanes per head
+    constexpr int HPW = 64 / LPH;         // heads per wave
+    const int role = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int g = blockIdx.x % nhg, rest = blockIdx.x / nhg;
+    const int t0 = (rest % nrun) * NTW, bi = rest / nrun;
+    const int h = g * HPW + lane / LPH;
+    const bool live = h < H;
+    const int c0 = (lane % LPH) * CH;
+    const int hs = live ? h : 0;
+    const int64_t st = (int64_t)H * DK;  // token stride (dk = dv)
+    const int64_t off0 = (((int64_t)bi * T + t0) * H + hs) * DK + c0;
+    const In* x = role == 0 ? xq : (role == 1 ? xk : xv);
+    const In* gx = role == 0 ? xb : (role == 1 ? xa : xw);
+    const float* cw = role == 0 ? cq : (role == 1 ? ck : cv);
+    In* dst = role == 0 ? q : (role == 1 ? k : v);
+    In* gdst = role == 0 ? b : w;
+    float tw[CH][4];
 #pragma unroll
-        for (int cc = lane; cc < DK; cc += 64) {
-            const float u = sU[which][i][cc];
-            s += u * u;
-        }
-        s = wave_sum(s);
-        if (lane == 0) sInv[which][i] = 1.f / sqrtf(s + eps);
+    for (int e = 0; e < CH; ++e) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(cw + (int64_t)(hs * DK + c0 + e) * 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tw[e][j] = a[j];
     }
-    __syncthreads();
-    if (key) {
-        for (int i = 0; i < nt; ++i) {
-            const int64_t o = base + (t0 + i) * stride;
-            q[o] = from_f32<In>(sU[0][i][c] * sInv[0][i]);
-            k[o] = from_f32<In>(sU[1][i][c] * sInv[1][i]);
+    float win[3][CH];  // inputs at t - 3, t - 2, t - 1
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int tt = t0 - 3 + j;
+        if (tt >= 0) {
+            const Vec<In, CH> r = load_vec<In, CH>(x + off0 + (int64_t)(j - 3) * st);
+#pragma unroll
+            for (int e = 0; e < CH; ++e) win[j][e] = to_f32(r.v[e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < CH; ++e) win[j][e] = 0.f;
+        }
+    }
+    const int nt = min(NTW, T - t0);
+    // a full run is unrolled in groups of four tokens whose loads are issued together
+    constexpr int G4 = 4;
+    for (int i0 = 0; i0 < nt; i0 += G4) {
+        Vec<In, CH> rs[G4], grs[G4];
+#pragma unroll
+        for (int d = 0; d < G4; ++d) {
+            const int64_t off = off0 + (int64_t)min(i0 + d, nt - 1) * st;
+            rs[d] = load_vec<In, CH>(x + off);
+            grs[d] = load_vec<In, CH>(gx + off);
+        }
+#pragma unroll
+        for (int d = 0; d < G4; ++d) {
+        const int i = i0 + d;
+        if (i >= nt) break;
+        const int64_t off = off0 + (int64_t)i * st;
+        const Vec<In, CH>& r = rs[d];
+        const Vec<In, CH>& gr = grs[d];
+        float u[CH], ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < CH; ++e) {
+            const float cur = to_f32(r.v[e]);
+            u[e] = silu_f(tw[e][0] * win[0][e] + tw[e][1] * win[1][e] + tw[e][2] * win[2][e] + tw[e][3] * cur);
+            win[0][e] = win[1][e];
+            win[1][e] = win[2][e];
+            win[2][e] = cur;
+            ss += u[e] * u[e];
+        }
+        float gv[CH];
+        if (role == 1) {
+#pragma unroll
+            for (int e = 0; e < CH; ++e) gv[e] = log_sigmoid_f(to_f32(gr.v[e]));
+        } else {
+#pragma unroll
+            for (int e = 0; e < CH; ++e) gv[e] = sigmoid_f(to_f32(gr.v[e]));
+        }
+        if (role < 2) {  // q, k: L2 normalisation over the head
+            ss = group_sum<LPH>(ss);
+            const float inv = 1.f / sqrtf(ss + eps);
+#pragma unroll
+            for (int e = 0; e < CH; ++e) u[e] *= inv;
+        }
+        if (live) {
+            store_n<In, CH>(dst + off, u);
+            if (role == 1) store_n<float, CH>(log_alpha + off, gv);
+            else store_n<In, CH>(gdst + off, gv);
+        }
         }
     }
 }
 
+// RPW rows per wave (64 / RPW lanes per row), EL = DV * RPW / 64 elements per lane
 template <typename OT, typename In, int DV>
 __global__ __launch_bounds__(256) void out_kernel(const OT* __restrict__ o, const In* __restrict__ z,
                                                   const float* __restrict__ gamma, In* __restrict__ y,
                                                   int64_t rows, float eps) {
-    constexpr int PER = DV / 64;  // elements per lane
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;
+    constexpr int EL = 4, LPR = DV / EL, RPW = 64 / LPR;
     const int lane = threadIdx.x & 63;
-    const int64_t off = row * DV + lane * PER;
-    const Vec<OT, PER> ov = load_vec<OT, PER>(o + off);
-    const Vec<In, PER> zv = load_vec<In, PER>(z + off);
-    float x[PER], s = 0.f;
+    const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / LPR;
+    const int c0 = (lane % LPR) * EL;
+    const bool live = row < rows;
+    const int64_t off = (live ? row : 0) * DV + c0;
+    const Vec<OT, EL> ov = load_vec<OT, EL>(o + off);
+    const Vec<In, EL> zv = load_vec<In, EL>(z + off);
+    const f32x4 g = *reinterpret_cast<const f32x4*>(gamma + c0);
+    float x[EL], s = 0.f;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
+    for (int e = 0; e < EL; ++e) {
         x[e] = to_f32(ov.v[e]);
         s += x[e] * x[e];
     }
-    s = wave_sum(s);
+    s = group_sum<LPR>(s);
     const float inv = 1.f / sqrtf(s * (1.f / DV) + eps);
-    float r[PER];
+    float r[EL];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) r[e] = x[e] * inv * gamma[lane * PER + e] * silu_f(to_f32(zv.v[e]));
-    if constexpr (PER == 1) {
-        y[off] = from_f32<In>(r[0]);
-    } else {
-        typedef In V __attribute__((ext_vector_type(PER)));
-        V out;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) out[e] = from_f32<In>(r[e]);
-        *reinterpret_cast<V*>(y + off) = out;
-    }
+    for (int e = 0; e < EL; ++e) r[e] = x[e] * inv * g[e] * silu_f(to_f32(zv.v[e]));
+    if (live) store_n<In, EL>(y + off, r);
 }
 
 template <typename In, int D>
 hipError_t launch_prep_t(const MixerPrepArgs& a) {
-    const int nblk = (int)((a.T + TBK - 1) / TBK);
-    hipLaunchKernelGGL((prep_kernel<In, D, D>), dim3((unsigned)(a.B * a.H * nblk)), dim3(2 * D), 0,
+    constexpr int HPW = 64 / (D / 8);  // heads per wave
+    const int nrun = (int)((a.T + NTW - 1) / NTW);  // workgroups along the tokens
+    const int nhg = (int)((a.H + HPW - 1) / HPW);
+    hipLaunchKernelGGL((prep_kernel<In, D, D>), dim3((unsigned)(a.B * nrun * nhg)), dim3(192), 0,
                        (hipStream_t)a.stream, (const In*)a.xq, (const In*)a.xk, (const In*)a.xv, (const In*)a.xb,
                        (const In*)a.xw, (const In*)a.xa, a.conv_q, a.conv_k, a.conv_v, (In*)a.q, (In*)a.k, (In*)a.v,
-                       (In*)a.b, (In*)a.w, a.log_alpha, (int)a.T, (int)a.H, nblk, a.eps);
+                       (In*)a.b, (In*)a.w, a.log_alpha, (int)a.T, (int)a.H, nrun, nhg, a.eps);
     return hipGetLastError();
 }
 
 template <typename OT, typename In, int D>
 hipError_t launch_out_t(const MixerOutArgs& a) {
     const int64_t rows = a.B * a.T * a.H;
-    hipLaunchKernelGGL((out_kernel<OT, In, D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
-                       (hipStream_t)a.stream, (const OT*)a.o, (const In*)a.z, a.gamma, (In*)a.y, rows, a.eps);
+    constexpr int RPW = 64 / (D / 4);  // rows per wave
+    const int64_t rows_per_group = 4 * RPW;
+    hipLaunchKernelGGL((out_kernel<OT, In, D>), dim3((unsigned)((rows + rows_per_group - 1) / rows_per_group)),
+                       dim3(256), 0, (hipStream_t)a.stream, (const OT*)a.o, (const In*)a.z, a.gamma, (In*)a.y,
+                       rows, a.eps);
     return hipGetLastError();
 }
 
