@@ -56,6 +56,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
+// A value the compiler cannot see through: lane indices made opaque at the top of every chunk
+// keep the chunk loop's address arithmetic inside the loop (hoisted out of it, the addresses
+// outnumber the registers and are spilled to scratch).
+__device__ __forceinline__ int opq(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 __device__ __forceinline__ f32x4 mfma4(const f32x4& acc, float a, float b) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
 }
@@ -81,6 +89,82 @@ __device__ __forceinline__ void mm(f32x4& acc, FA A, FB B, int k0, int k1, int l
     for (int k = k0; k < k1; k += 16) {
 #pragma unroll
         for (int s = 0; s < 16; s += 4) acc = mfma4(acc, A(l16, k + s + g4), B(k + s + g4, l16));
+    }
+}
+
+// NTILE independent 16 x 16 products over the same contraction length K (compile time), fully
+// unrolled with the steps of all tiles interleaved, so that the MFMA chains of different tiles
+// hide each other's latency: acc[t] += sum_k A(t, m, k) B(t, k, n).  A B operand that does not
+// depend on t is loaded once per step.
+template <int NTILE, int K, class FA, class FB>
+__device__ __forceinline__ void mm_n(f32x4 (&acc)[NTILE], FA A, FB B, int l16, int g4) {
+    // unrolled 16 deep: deeper unrolling lets the compiler hoist more operand loads than the
+    // register file holds
+#pragma unroll 1
+    for (int k0 = 0; k0 < K; k0 += 16) {
+#pragma unroll
+        for (int k = k0; k < k0 + 16; k += 4) {
+            float a[NTILE], b[NTILE];
+#pragma unroll
+            for (int t = 0; t < NTILE; ++t) {
+                a[t] = A(t, l16, k + g4);
+                b[t] = B(t, k + g4, l16);
+            }
+#pragma unroll
+            for (int t = 0; t < NTILE; ++t) acc[t] = mfma4(acc[t], a[t], b[t]);
+        }
+    }
+}
+
+// acc += the product over [0, K) as NS independent chains over consecutive parts of K, summed
+// at the end (one output tile, its MFMA latency hidden by its own parts)
+template <int NS, int K, class FA, class FB>
+__device__ __forceinline__ void mm_split(f32x4& acc, FA A, FB B, int l16, int g4) {
+    static_assert(K % (4 * NS) == 0, "split");
+    f32x4 part[NS];
+#pragma unroll
+    for (int t = 0; t < NS; ++t) part[t] = zero4();
+    mm_n<NS, K / NS>(part, [&](int t, int m, int kk) { return A(m, t * (K / NS) + kk); },
+                     [&](int t, int kk, int nn) { return B(t * (K / NS) + kk, nn); }, l16, g4);
+#pragma unroll
+    for (int t = 0; t < NS; ++t) acc += part[t];
+}
+
+// acc += the product over the 16-wide blocks kb0 <= kb < 4 of a 64-long contraction (kb0
+// runtime), each block its own chain
+template <class FA, class FB>
+__device__ __forceinline__ void mm_tail64(f32x4& acc, FA A, FB B, int kb0, int l16, int g4) {
+    f32x4 part[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) part[t] = zero4();
+#pragma unroll
+    for (int k = 0; k < 16; k += 4) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            if (t >= kb0) part[t] = mfma4(part[t], A(l16, t * 16 + k + g4), B(t * 16 + k + g4, l16));
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc += part[t];
+}
+
+// This thread's L tokens of key channel c in the element phase, every load issued at once: a
+// token past the end reads the last token, and the caller zeroes it.
+template <typename In, int L>
+struct KeyIn {
+    float g[L];
+    In q[L], k[L], b[L];
+};
+template <typename In, int L>
+__device__ __forceinline__ void load_key(KeyIn<In, L>& in, const In* __restrict__ q, const In* __restrict__ k,
+                                         const In* __restrict__ b, const float* __restrict__ g, int64_t base,
+                                         int64_t rk, int t0, int T) {
+#pragma unroll
+    for (int m = 0; m < L; ++m) {
+        const int64_t o = base + (int64_t)min(t0 + m, T - 1) * rk;
+        in.g[m] = g[o];
+        in.q[m] = q[o];
+        in.k[m] = k[o];
+        in.b[m] = b[o];
     }
 }
 
@@ -147,7 +231,7 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int lane = tid & 63, lane16 = lane & 15, grp4 = lane >> 4;
     const int bh = blockIdx.x / nslices, slice = blockIdx.x % nslices;
     const int bi = bh / H, h = bh % H, col0 = slice * DVS;
     const int nch = (T + C - 1) / C;
@@ -162,7 +246,7 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
         const int u = wave + 8 * s;
         if (initial_state && u < NST) {
             const int st = u % KT, ct = u / KT;
-            const float* src = initial_state + ((int64_t)bh * DK + st * 16 + g4 * 4) * DV + col0 + ct * 16 + l16;
+            const float* src = initial_state + ((int64_t)bh * DK + st * 16 + grp4 * 4) * DV + col0 + ct * 16 + lane16;
 #pragma unroll
             for (int r = 0; r < 4; ++r) S[s][r] = src[(int64_t)r * DV];
         }
@@ -171,8 +255,9 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
     const int LI = wave < 3 ? wave + 1 : (wave < 5 ? wave - 1 : 3);
     const int LJ = wave < 3 ? wave : (wave < 5 ? wave - 3 : 0);
 
-    const int ec = tid % DK, etb = tid / DK;
+    const int ec_ = tid % DK, etb_ = tid / DK;
     for (int n = 0; n < nch; ++n) {
+        const int l16 = opq(lane16), g4 = opq(grp4), ec = opq(ec_), etb = opq(etb_);
         const int t0 = n * C;
         float* tpn = tp + ((int64_t)bh * nch + n) * 2 * C * C;
         // the state entering the chunk: checkpoint and operand copy
@@ -190,14 +275,16 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
             }
         }
         if (tid == 0) *sFLG = 0;
-        // element phase, pass 1: cumulative log-decay within the token block; w.v of the slice
+        // element phase, pass 1: the chunk's inputs; cumulative log-decay within the token block;
+        // w.v of the slice
+        KeyIn<In, L> in;
+        load_key<In, L>(in, q, k, bgate, log_alpha, base_k + ec, rk, t0 + etb * L, T);
         float x[L];
         {
             float run = 0.f;
 #pragma unroll
             for (int m = 0; m < L; ++m) {
-                const int t = t0 + etb * L + m;
-                run += t < T ? log_alpha[base_k + (int64_t)t * rk + ec] : 0.f;
+                run += t0 + etb * L + m < T ? in.g[m] : 0.f;
                 x[m] = run;
             }
             sTOT[etb * DK + ec] = run;
@@ -243,10 +330,9 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
             const int i = etb * L + m, t = t0 + i;
             In qv = from_f32<In>(0.f), kv = qv, bv = qv;
             if (t < T) {
-                const int64_t o = base_k + (int64_t)t * rk + ec;
-                qv = q[o];
-                kv = k[o];
-                bv = bgate[o];
+                qv = in.q[m];
+                kv = in.k[m];
+                bv = in.b[m];
             }
             const float Gi = x[m] + off;
             if (mild) {
@@ -264,28 +350,45 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
         __syncthreads();
         // A (strictly lower, into the A/T tile) and, in slice 0, P (lower, to tp)
         if (mild) {
-            const int nt = slice == 0 ? 10 + 16 : 10;
-            for (int u = wave; u < nt; u += 8) {
+            // lower 16 x 16 blocks (I >= J) in the order (0,0) (1,0) (1,1) (2,0) ...: blocks 0-9 of
+            // A and, in slice 0, blocks 10-19 of P; wave w takes blocks w, w + 8, w + 16
+            const int nt = slice == 0 ? 20 : 10;
+            auto blk = [](int u, int& I, int& J) {
+                const int x = u % 10;
+                I = x < 1 ? 0 : (x < 3 ? 1 : (x < 6 ? 2 : 3));
+                J = x - I * (I + 1) / 2;
+            };
+            f32x4 acc[3];
+#pragma unroll
+            for (int t = 0; t < 3; ++t) acc[t] = zero4();
+            mm_n<3, DK>(acc,
+                [&](int t, int m, int kk) {
+                    int I, J;
+                    blk(wave + 8 * t, I, J);
+                    return (wave + 8 * t >= 10 ? sQG : sKG)[(I * 16 + m) * LDF + kk];
+                },
+                [&](int t, int kk, int nn) {
+                    int I, J;
+                    blk(wave + 8 * t, I, J);
+                    return sKI[(J * 16 + nn) * LDF + kk];
+                }, l16, g4);
+#pragma unroll
+            for (int t = 0; t < 3; ++t) {
+                const int u = wave + 8 * t;
+                if (u >= nt) continue;
                 int I, J;
-                const bool isA = u < 10;
-                if (isA) {  // lower blocks in the order (0,0) (1,0) (1,1) (2,0) ...
-                    I = u < 1 ? 0 : (u < 3 ? 1 : (u < 6 ? 2 : 3));
-                    J = u - I * (I + 1) / 2;
-                } else {
-                    I = (u - 10) / 4;
-                    J = (u - 10) % 4;
-                }
-                f32x4 acc = zero4();
-                if (J <= I) {
-                    const float* X = isA ? sKG : sQG;
-                    mm(acc, [&](int m, int kk) { return X[(I * 16 + m) * LDF + kk]; },
-                       [&](int kk, int nn) { return sKI[(J * 16 + nn) * LDF + kk]; }, 0, DK, l16, g4);
-                }
+                blk(u, I, J);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = I * 16 + g4 * 4 + r, j = J * 16 + l16;
-                    if (isA) sAT[i * LDC + j] = j < i ? acc[r] : 0.f;
-                    else tpn[C * C + i * C + j] = j <= i ? acc[r] : 0.f;
+                    if (u < 10) sAT[i * LDC + j] = j < i ? acc[t][r] : 0.f;
+                    else tpn[C * C + i * C + j] = j <= i ? acc[t][r] : 0.f;
+                }
+            }
+            if (slice == 0) {  // P above the diagonal blocks is zero
+                for (int e = tid; e < C * C; e += NT) {
+                    const int i = e / C, j = e % C;
+                    if (j / 16 > i / 16) tpn[C * C + e] = 0.f;
                 }
             }
         } else {
@@ -317,7 +420,7 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
                 sKI[i * LDF + ec] *= sGC[ec];
             } else {
                 float kv = 0.f, bv = 0.f;
-                if (t < T) {
+                if (t < T) {  // reloaded: keeping the raw inputs live costs registers everywhere
                     const int64_t o = base_k + (int64_t)t * rk + ec;
                     kv = to_f32(k[o]);
                     bv = to_f32(bgate[o]);
@@ -339,6 +442,9 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
                 const float xm = xs[m];
 #pragma unroll
                 for (int i = m + 1; i < 16; ++i) xs[i] -= Ab[i * LDC + m] * xm;
+                // keep each step's loads in their step: hoisted, the 120 loads would need as
+                // many registers
+                __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int i = 0; i < 16; ++i) Ab[i * LDC + lane] = xs[i];
@@ -386,8 +492,8 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
         for (int u = wave; u < 4 * NCT; u += 8) {
             const int it = u % 4, ct = u / 4;
             f32x4 acc = zero4();
-            mm(acc, [&](int m, int kk) { return sKG[(it * 16 + m) * LDF + kk]; },
-               [&](int kk, int nn) { return sSC[kk * LDV + ct * 16 + nn]; }, 0, DK, l16, g4);
+            mm_split<4, DK>(acc, [&](int m, int kk) { return sKG[(it * 16 + m) * LDF + kk]; },
+                            [&](int kk, int nn) { return sSC[kk * LDV + ct * 16 + nn]; }, l16, g4);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float* p = sWV + (it * 16 + g4 * 4 + r) * LDV + ct * 16 + l16;
@@ -399,8 +505,9 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
         for (int u = wave; u < 4 * NCT; u += 8) {
             const int it = u % 4, ct = u / 4;
             f32x4 acc = zero4();
-            mm(acc, [&](int m, int kk) { return sAT[(it * 16 + m) * LDC + kk]; },
-               [&](int kk, int nn) { return sWV[kk * LDV + ct * 16 + nn]; }, 0, it * 16 + 16, l16, g4);
+            // T is lower triangular: blocks 0..it of the contraction, as separate chains
+            mm_tail64(acc, [&](int m, int kk) { return kk < it * 16 + 16 ? sAT[(it * 16 + m) * LDC + kk] : 0.f; },
+                      [&](int kk, int nn) { return sWV[kk * LDV + ct * 16 + nn]; }, 0, l16, g4);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = it * 16 + g4 * 4 + r, t = t0 + i;
@@ -418,8 +525,8 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
                 f32x4 acc;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[r] = S[s][r] * sGC[st * 16 + g4 * 4 + r];
-                mm(acc, [&](int m, int kk) { return sKI[kk * LDF + st * 16 + m]; },
-                   [&](int kk, int nn) { return sUU[kk * LDV + ct * 16 + nn]; }, 0, C, l16, g4);
+                mm_split<4, C>(acc, [&](int m, int kk) { return sKI[kk * LDF + st * 16 + m]; },
+                               [&](int kk, int nn) { return sUU[kk * LDV + ct * 16 + nn]; }, l16, g4);
                 S[s] = acc;
             }
         }
@@ -482,7 +589,7 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int lane = tid & 63, lane16 = lane & 15, grp4 = lane >> 4;
     const int bh = blockIdx.x / nslices, slice = blockIdx.x % nslices;
     const int bi = bh / H, h = bh % H, col0 = slice * DVS;
     const int nch = (T + C - 1) / C;
@@ -499,14 +606,15 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(
         const int u = wave + 8 * s;
         if (d_final && u < NST) {
             const int st = u % KT, ct = u / KT;
-            const float* src = d_final + ((int64_t)bh * DK + st * 16 + g4 * 4) * DV + col0 + ct * 16 + l16;
+            const float* src = d_final + ((int64_t)bh * DK + st * 16 + grp4 * 4) * DV + col0 + ct * 16 + lane16;
 #pragma unroll
             for (int r = 0; r < 4; ++r) dS[s][r] = src[(int64_t)r * DV];
         }
     }
 
-    const int ec = tid % DK, etb = tid / DK;  // element phase: channel, token block
+    const int ec_ = tid % DK, etb_ = tid / DK;  // element phase: channel, token block
     for (int n = nch - 1; n >= 0; --n) {
+        const int l16 = opq(lane16), g4 = opq(grp4), ec = opq(ec_), etb = opq(etb_);
         const int t0 = n * C;
         // dS' of this chunk: checkpoint for kernel 3 and operand copy
 #pragma unroll
@@ -522,14 +630,15 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(
                 }
             }
         }
-        // element phase, pass 1: cumulative log-decay within the token block
+        // element phase, pass 1: the chunk's inputs; cumulative log-decay within the token block
+        KeyIn<In, L> in;
+        load_key<In, L>(in, q, k, bgate, log_alpha, base_k + ec, rk, t0 + etb * L, T);
         float x[L];
         {
             float run = 0.f;
 #pragma unroll
             for (int m = 0; m < L; ++m) {
-                const int t = t0 + etb * L + m;
-                run += t < T ? log_alpha[base_k + (int64_t)t * rk + ec] : 0.f;
+                run += t0 + etb * L + m < T ? in.g[m] : 0.f;
                 x[m] = run;
             }
             sTOT[etb * DK + ec] = run;
@@ -569,10 +678,9 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(
                 const int i = etb * L + m, t = t0 + i;
                 float qv = 0.f, kv = 0.f, bv = 0.f;
                 if (t < T) {
-                    const int64_t o = base_k + (int64_t)t * rk + ec;
-                    qv = to_f32(q[o]);
-                    kv = to_f32(k[o]);
-                    bv = to_f32(bgate[o]);
+                    qv = to_f32(in.q[m]);
+                    kv = to_f32(in.k[m]);
+                    bv = to_f32(in.b[m]);
                 }
                 const float Gi = x[m] + off;
                 const float ga = exp_any(Gi);
@@ -586,10 +694,10 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(
         for (int u = wave; u < 4 * NCT; u += 8) {
             const int jt = u % 4, ct = u / 4;
             f32x4 acc = zero4();
-            mm(acc, [&](int m, int kk) { return sP[kk * LDC + jt * 16 + m]; },
-               [&](int kk, int nn) { return sDO[kk * LDV + ct * 16 + nn]; }, jt * 16, C, l16, g4);
-            mm(acc, [&](int m, int kk) { return sKR[(jt * 16 + m) * LDF + kk]; },
-               [&](int kk, int nn) { return sDS[kk * LDV + ct * 16 + nn]; }, 0, DK, l16, g4);
+            mm_tail64(acc, [&](int m, int kk) { return sP[kk * LDC + jt * 16 + m]; },
+                      [&](int kk, int nn) { return sDO[kk * LDV + ct * 16 + nn]; }, jt, l16, g4);
+            mm_split<4, DK>(acc, [&](int m, int kk) { return sKR[(jt * 16 + m) * LDF + kk]; },
+                            [&](int kk, int nn) { return sDS[kk * LDV + ct * 16 + nn]; }, l16, g4);
 #pragma unroll
             for (int r = 0; r < 4; ++r) sDU[(jt * 16 + g4 * 4 + r) * LDV + ct * 16 + l16] = acc[r];
         }
@@ -598,8 +706,8 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(
         for (int u = wave; u < 4 * NCT; u += 8) {
             const int it = u % 4, ct = u / 4;
             f32x4 acc = zero4();
-            mm(acc, [&](int m, int kk) { return sT[kk * LDC + it * 16 + m]; },
-               [&](int kk, int nn) { return sDU[kk * LDV + ct * 16 + nn]; }, it * 16, C, l16, g4);
+            mm_tail64(acc, [&](int m, int kk) { return sT[kk * LDC + it * 16 + m]; },
+                      [&](int kk, int nn) { return sDU[kk * LDV + ct * 16 + nn]; }, it, l16, g4);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = it * 16 + g4 * 4 + r, t = t0 + i;
@@ -621,14 +729,11 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(
             const int u = wave + 8 * s;
             if (u < NST) {
                 const int st = u % KT, ct = u / KT;
-                f32x4 pos = zero4(), neg = zero4();
+                f32x4 acc2[2] = {zero4(), zero4()};
+                mm_n<2, C>(acc2, [&](int t, int m, int kk) { return (t ? sKG : sQG)[kk * LDF + st * 16 + m]; },
+                           [&](int t, int kk, int nn) { return (t ? sDR : sDO)[kk * LDV + ct * 16 + nn]; }, l16, g4);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) pos[r] = dS[s][r] * sGC[st * 16 + g4 * 4 + r];
-                mm(pos, [&](int m, int kk) { return sQG[kk * LDF + st * 16 + m]; },
-                   [&](int kk, int nn) { return sDO[kk * LDV + ct * 16 + nn]; }, 0, C, l16, g4);
-                mm(neg, [&](int m, int kk) { return sKG[kk * LDF + st * 16 + m]; },
-                   [&](int kk, int nn) { return sDR[kk * LDV + ct * 16 + nn]; }, 0, C, l16, g4);
-                dS[s] = pos - neg;
+                for (int r = 0; r < 4; ++r) dS[s][r] = dS[s][r] * sGC[st * 16 + g4 * 4 + r] + acc2[0][r] - acc2[1][r];
             }
         }
         __syncthreads();
@@ -639,7 +744,7 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(
             const int u = wave + 8 * s;
             if (u < NST) {
                 const int st = u % KT, ct = u / KT;
-                float* dst = d_initial + ((int64_t)bh * DK + st * 16 + g4 * 4) * DV + col0 + ct * 16 + l16;
+                float* dst = d_initial + ((int64_t)bh * DK + st * 16 + grp4 * 4) * DV + col0 + ct * 16 + lane16;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) dst[(int64_t)r * DV] = dS[s][r];
             }
@@ -787,13 +892,24 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
             *reinterpret_cast<f32x4*>(sSH + r * LDH + c4) = *reinterpret_cast<const f32x4*>(Sg + r * DV + hh * HV + c4);
         }
         __syncthreads();
+        {
+            f32x4 acc[2 * TPW];
 #pragma unroll
-        for (int j = 0; j < TPW; ++j) {
-            const int it = it0 + ITS * j;
-            mm(X1[j], [&](int m, int kk) { return sDO[(it * 16 + m) * LDV + hh * HV + kk]; },
-               [&](int kk, int nn) { return sSH[(ct * 16 + nn) * LDH + kk]; }, 0, HV, l16, g4);
-            mm(X2[j], [&](int m, int kk) { return sDR[(it * 16 + m) * LDV + hh * HV + kk]; },
-               [&](int kk, int nn) { return sSH[(ct * 16 + nn) * LDH + kk]; }, 0, HV, l16, g4);
+            for (int j = 0; j < TPW; ++j) {
+                acc[j] = X1[j];
+                acc[TPW + j] = X2[j];
+            }
+            mm_n<2 * TPW, HV>(acc,
+                [&](int t, int m, int kk) {
+                    const float* X = t < TPW ? sDO : sDR;
+                    return X[((it0 + ITS * (t % TPW)) * 16 + m) * LDV + hh * HV + kk];
+                },
+                [&](int, int kk, int nn) { return sSH[(ct * 16 + nn) * LDH + kk]; }, l16, g4);
+#pragma unroll
+            for (int j = 0; j < TPW; ++j) {
+                X1[j] = acc[j];
+                X2[j] = acc[TPW + j];
+            }
         }
         __syncthreads();
         for (int e = tid; e < DK * HV / 4; e += NT) {
@@ -804,32 +920,38 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
             atomicAdd(sXD + r, d4[0] * s4[0] + d4[1] * s4[1] + d4[2] * s4[2] + d4[3] * s4[3]);
         }
         __syncthreads();
-#pragma unroll
-        for (int j = 0; j < TPW; ++j) {
-            const int it = it0 + ITS * j;
-            mm(X3[j], [&](int m, int kk) { return sU[(it * 16 + m) * LDV + hh * HV + kk]; },
-               [&](int kk, int nn) { return sSH[(ct * 16 + nn) * LDH + kk]; }, 0, HV, l16, g4);
-        }
+        mm_n<TPW, HV>(X3, [&](int t, int m, int kk) { return sU[((it0 + ITS * t) * 16 + m) * LDV + hh * HV + kk]; },
+                      [&](int, int kk, int nn) { return sSH[(ct * 16 + nn) * LDH + kk]; }, l16, g4);
     }
 #pragma unroll
     for (int j = 0; j < TPW; ++j) X2[j] = -X2[j];  // -dR S^T
     __syncthreads();
 
     // ---- phase 3: dA = -dR U^T (j < i), dP = dO U^T (j <= i); zero above the diagonal ----
-    for (int u = wave; u < 32; u += 8) {
-        const int mat = u / 16, I = (u % 16) / 4, J = u % 4;
-        f32x4 acc = zero4();
-        if (J <= I) {
-            const float* X = mat ? sDO : sDR;
-            mm(acc, [&](int m, int kk) { return X[(I * 16 + m) * LDV + kk]; },
-               [&](int kk, int nn) { return sU[(J * 16 + nn) * LDV + kk]; }, 0, DV, l16, g4);
-        }
-        float* dst = mat ? sDP : sDA;
+    {
+        // wave w: block pairs p = w and w + 8, (I, J) = (p / 4, p % 4), both dA and dP
+        f32x4 acc[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = I * 16 + g4 * 4 + r, jj = J * 16 + l16;
-            const bool keep = mat ? (jj <= i) : (jj < i);
-            dst[i * LDC + jj] = keep ? (mat ? acc[r] : -acc[r]) : 0.f;
+        for (int t = 0; t < 4; ++t) acc[t] = zero4();
+        mm_n<4, DV>(acc,
+            [&](int t, int m, int kk) {
+                const int p = wave + 8 * (t >> 1);
+                return (t & 1 ? sDO : sDR)[((p >> 2) * 16 + m) * LDV + kk];
+            },
+            [&](int t, int kk, int nn) {
+                const int p = wave + 8 * (t >> 1);
+                return sU[((p & 3) * 16 + nn) * LDV + kk];
+            }, l16, g4);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int p = wave + 8 * (t >> 1), I = p >> 2, J = p & 3, mat = t & 1;
+            float* dst = mat ? sDP : sDA;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = I * 16 + g4 * 4 + r, jj = J * 16 + l16;
+                const bool keep = mat ? (jj <= i) : (jj < i);
+                dst[i * LDC + jj] = keep ? (mat ? acc[t][r] : -acc[t][r]) : 0.f;
+            }
         }
     }
     __syncthreads();  // region 1 (dO, dR, U) is free from here on
@@ -837,12 +959,13 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
     // element phase: G (chunk-local cumulative log alpha) and the raw q, k, b of the chunk
     const int ec = tid % DK, etb = tid / DK;
     {
+        KeyIn<In, L> in;
+        load_key<In, L>(in, q, k, bgate, log_alpha, base_k + ec, rk, t0 + etb * L, T);
         float x[L];
         float run = 0.f;
 #pragma unroll
         for (int m = 0; m < L; ++m) {
-            const int t = t0 + etb * L + m;
-            run += t < T ? log_alpha[base_k + (int64_t)t * rk + ec] : 0.f;
+            run += t0 + etb * L + m < T ? in.g[m] : 0.f;
             x[m] = run;
         }
         sTOT[etb * DK + ec] = run;
@@ -872,10 +995,9 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
             const int i = etb * L + m, t = t0 + i;
             In qv = from_f32<In>(0.f), kv = qv, bv = qv;
             if (t < T) {
-                const int64_t o = base_k + (int64_t)t * rk + ec;
-                qv = q[o];
-                kv = k[o];
-                bv = bgate[o];
+                qv = in.q[m];
+                kv = in.k[m];
+                bv = in.b[m];
             }
             sG[i * LDF + ec] = x[m];  // block-local
             sQ[i * LDT + ec] = qv;
@@ -909,6 +1031,7 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
         const float gc = sGC[c];
 #pragma unroll
         for (int j = 0; j < TPW; ++j) X3[j] *= gc;
+#pragma unroll
         for (int kb = 0; kb < C; kb += 4) {
             const int r = kb + g4;  // contraction token of this lane group
             const float Gr = Gof(r, c);
