@@ -56,6 +56,16 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not for its
+// global loads, so a prefetch stays in flight across it (no thread reads global memory that
+// another thread of the kernel writes).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt not waited for
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // A value the compiler cannot see through: lane indices made opaque at the top of every chunk
 // keep the chunk loop's address arithmetic inside the loop (hoisted out of it, the addresses
 // outnumber the registers and are spilled to scratch).
@@ -256,6 +266,25 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
     const int LJ = wave < 3 ? wave : (wave < 5 ? wave - 3 : 0);
 
     const int ec_ = tid % DK, etb_ = tid / DK;
+    // the next chunk's inputs are loaded one phase ahead (before the state update of the chunk
+    // before it): key-side inputs, w and v of the slice
+    constexpr int NWV = (C * DVS / 4 + NT - 1) / NT;  // groups of 4 value columns per thread
+    KeyIn<In, L> in;
+    Vec<In, 4> wr[NWV], vr[NWV];
+    auto prefetch = [&](int nn) {
+        const int tt0 = nn * C;
+        load_key<In, L>(in, q, k, bgate, log_alpha, base_k + ec_, rk, tt0 + etb_ * L, T);
+#pragma unroll
+        for (int i = 0; i < NWV; ++i) {
+            const int e = tid + i * NT, r = e / (DVS / 4), c4 = (e % (DVS / 4)) * 4;
+            const int64_t o = base_v + (int64_t)min(tt0 + r, T - 1) * rv + col0 + c4;
+            if (e < C * DVS / 4) {
+                wr[i] = load_vec<In, 4>(wgate + o);
+                vr[i] = load_vec<In, 4>(v + o);
+            }
+        }
+    };
+    prefetch(0);
     for (int n = 0; n < nch; ++n) {
         const int l16 = opq(lane16), g4 = opq(grp4), ec = opq(ec_), etb = opq(etb_);
         const int t0 = n * C;
@@ -275,10 +304,8 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
             }
         }
         if (tid == 0) *sFLG = 0;
-        // element phase, pass 1: the chunk's inputs; cumulative log-decay within the token block;
+        // element phase, pass 1 (inputs prefetched): cumulative log-decay within the token block;
         // w.v of the slice
-        KeyIn<In, L> in;
-        load_key<In, L>(in, q, k, bgate, log_alpha, base_k + ec, rk, t0 + etb * L, T);
         float x[L];
         {
             float run = 0.f;
@@ -288,19 +315,20 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
                 x[m] = run;
             }
             sTOT[etb * DK + ec] = run;
-            for (int e = tid; e < C * DVS / 4; e += NT) {
-                const int r = e / (DVS / 4), c4 = (e % (DVS / 4)) * 4, t = t0 + r;
-                f32x4 wv = zero4();
-                if (t < T) {
-                    const int64_t o = base_v + (int64_t)t * rv + col0 + c4;
-                    const Vec<In, 4> w4 = load_vec<In, 4>(wgate + o), v4 = load_vec<In, 4>(v + o);
 #pragma unroll
-                    for (int z = 0; z < 4; ++z) wv[z] = to_f32(w4.v[z]) * to_f32(v4.v[z]);
+            for (int i = 0; i < NWV; ++i) {
+                const int e = tid + i * NT, r = e / (DVS / 4), c4 = (e % (DVS / 4)) * 4;
+                if (e < C * DVS / 4) {
+                    f32x4 wv = zero4();
+                    if (t0 + r < T) {
+#pragma unroll
+                        for (int z = 0; z < 4; ++z) wv[z] = to_f32(wr[i].v[z]) * to_f32(vr[i].v[z]);
+                    }
+                    *reinterpret_cast<f32x4*>(sWV + r * LDV + c4) = wv;
                 }
-                *reinterpret_cast<f32x4*>(sWV + r * LDV + c4) = wv;
             }
         }
-        __syncthreads();
+        lds_barrier();
         float off = 0.f, tot = 0.f, after = 0.f, oh = 0.f, ol = 0.f;
 #pragma unroll
         for (int j = 0; j < TB; ++j) {
@@ -322,7 +350,7 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
             sGC[ec] = exp_any(tot);
             if (!(tot >= kMildLog)) *sFLG = 1;
         }
-        __syncthreads();
+        lds_barrier();
         const bool mild = *sFLG == 0;
         // element phase, pass 2: operand tiles
 #pragma unroll
@@ -347,7 +375,8 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
                 sRQ[i * LDT + ec] = qv;
             }
         }
-        __syncthreads();
+        if (n + 1 < nch) prefetch(n + 1);
+        lds_barrier();
         // A (strictly lower, into the A/T tile) and, in slice 0, P (lower, to tp)
         if (mild) {
             // lower 16 x 16 blocks (I >= J) in the order (0,0) (1,0) (1,1) (2,0) ...: blocks 0-9 of
@@ -411,7 +440,7 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
                 if (slice == 0) tpn[C * C + i * C + j] = p;
             }
         }
-        __syncthreads();
+        lds_barrier();
         // KG and KR = k.Gamma_C / Gamma for the state products
 #pragma unroll
         for (int m = 0; m < L; ++m) {
@@ -449,7 +478,7 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
 #pragma unroll
             for (int i = 0; i < 16; ++i) Ab[i * LDC + lane] = xs[i];
         }
-        __syncthreads();
+        lds_barrier();
         // off-diagonal blocks, T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ, level by level; every
         // wave first takes the blocks of A it needs, before the levels overwrite them
         float ap[3][4];
@@ -460,7 +489,7 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
                 const int K = LJ + kb;
                 ap[kb][s4] = (wave < 6 && K < LI) ? sAT[(LI * 16 + l16) * LDC + K * 16 + g4 + 4 * s4] : 0.f;
             }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int d = 1; d <= 3; ++d) {
             if (wave < 6 && LI - LJ == d) {
@@ -480,7 +509,7 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sAT[(LI * 16 + g4 * 4 + r) * LDC + LJ * 16 + l16] = -tij[r];
             }
-            __syncthreads();
+            lds_barrier();
         }
         if (slice == 0) {
             for (int e = tid; e < C * C; e += NT) {
@@ -500,7 +529,7 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
                 *p -= acc[r];
             }
         }
-        __syncthreads();
+        lds_barrier();
         // U = T (w.v - KG S)
         for (int u = wave; u < 4 * NCT; u += 8) {
             const int it = u % 4, ct = u / 4;
@@ -515,7 +544,7 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
                 if (t < T) u_out[base_v + (int64_t)t * rv + col0 + ct * 16 + l16] = acc[r];
             }
         }
-        __syncthreads();
+        lds_barrier();
         // S <- Gamma_C S + KR^T U
 #pragma unroll
         for (int s = 0; s < SPW; ++s) {
@@ -530,7 +559,7 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
                 S[s] = acc;
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
 }
 
@@ -613,6 +642,30 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(
     }
 
     const int ec_ = tid % DK, etb_ = tid / DK;  // element phase: channel, token block
+    // the next chunk's inputs are loaded one phase ahead (before the dS update of the chunk
+    // before it): key-side inputs, T and P, the dO slice
+    constexpr int NTP = 2 * C * C / 4 / NT;             // float4 of T and P per thread
+    constexpr int NDO = (C * DVS / 4 + NT - 1) / NT;    // float4 of dO per thread
+    KeyIn<In, L> in;
+    f32x4 tpv[NTP], dov[NDO];
+    auto prefetch_key = [&](int nn) {
+        load_key<In, L>(in, q, k, bgate, log_alpha, base_k + ec_, rk, nn * C + etb_ * L, T);
+    };
+    auto prefetch_tp = [&](int nn) {
+        const int tt0 = nn * C;
+        const float* src = tp + ((int64_t)bh * nch + nn) * 2 * C * C;
+#pragma unroll
+        for (int i = 0; i < NTP; ++i) tpv[i] = *reinterpret_cast<const f32x4*>(src + (tid + i * NT) * 4);
+#pragma unroll
+        for (int i = 0; i < NDO; ++i) {
+            const int e = tid + i * NT, r = e / (DVS / 4), c4 = (e % (DVS / 4)) * 4;
+            const int t = min(tt0 + r, T - 1);
+            dov[i] = e < C * DVS / 4 ? *reinterpret_cast<const f32x4*>(d_o + base_v + (int64_t)t * rv + col0 + c4)
+                                     : zero4();
+        }
+    };
+    prefetch_key(nch - 1);
+    prefetch_tp(nch - 1);
     for (int n = nch - 1; n >= 0; --n) {
         const int l16 = opq(lane16), g4 = opq(grp4), ec = opq(ec_), etb = opq(etb_);
         const int t0 = n * C;
@@ -630,9 +683,7 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(
                 }
             }
         }
-        // element phase, pass 1: the chunk's inputs; cumulative log-decay within the token block
-        KeyIn<In, L> in;
-        load_key<In, L>(in, q, k, bgate, log_alpha, base_k + ec, rk, t0 + etb * L, T);
+        // element phase, pass 1: cumulative log-decay within the token block (inputs prefetched)
         float x[L];
         {
             float run = 0.f;
@@ -643,22 +694,22 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(
             }
             sTOT[etb * DK + ec] = run;
         }
-        // T and P of the chunk, and the dO slice
+        // T and P of the chunk, and the dO slice (prefetched)
         {
-            const float* src = tp + ((int64_t)bh * nch + n) * 2 * C * C;
-            for (int e = tid; e < 2 * C * C / 4; e += NT) {
+#pragma unroll
+            for (int i = 0; i < NTP; ++i) {
+                const int e = tid + i * NT;
                 const int mat = e / (C * C / 4), r = (e / (C / 4)) % C, c4 = (e % (C / 4)) * 4;
-                const f32x4 val = *reinterpret_cast<const f32x4*>(src + mat * C * C + r * C + c4);
-                *reinterpret_cast<f32x4*>((mat ? sP : sT) + r * LDC + c4) = val;
+                *reinterpret_cast<f32x4*>((mat ? sP : sT) + r * LDC + c4) = tpv[i];
             }
-            for (int e = tid; e < C * DVS / 4; e += NT) {
-                const int r = e / (DVS / 4), c4 = (e % (DVS / 4)) * 4, t = t0 + r;
-                f32x4 val = zero4();
-                if (t < T) val = *reinterpret_cast<const f32x4*>(d_o + base_v + (int64_t)t * rv + col0 + c4);
-                *reinterpret_cast<f32x4*>(sDO + r * LDV + c4) = val;
+#pragma unroll
+            for (int i = 0; i < NDO; ++i) {
+                const int e = tid + i * NT, r = e / (DVS / 4), c4 = (e % (DVS / 4)) * 4;
+                if (e < C * DVS / 4) *reinterpret_cast<f32x4*>(sDO + r * LDV + c4) = t0 + r < T ? dov[i] : zero4();
             }
         }
-        __syncthreads();
+        if (n > 0) prefetch_tp(n - 1);
+        lds_barrier();
         // element phase, pass 2: decayed operands (q.Gamma and b.k.Gamma stay in registers until
         // their place is free)
         float qg[L], kg[L];
@@ -689,7 +740,7 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(
                 sKR[i * LDF + ec] = kv * exp_any((run - x[m]) + after);
             }
         }
-        __syncthreads();
+        lds_barrier();
         // dU = P^T dO + KR dS'   (tile: token rows jt, value columns ct)
         for (int u = wave; u < 4 * NCT; u += 8) {
             const int jt = u % 4, ct = u / 4;
@@ -701,7 +752,7 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) sDU[(jt * 16 + g4 * 4 + r) * LDV + ct * 16 + l16] = acc[r];
         }
-        __syncthreads();
+        lds_barrier();
         // dR = T^T dU
         for (int u = wave; u < 4 * NCT; u += 8) {
             const int it = u % 4, ct = u / 4;
@@ -715,14 +766,17 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(
                 if (t < T) dr_out[base_v + (int64_t)t * rv + col0 + ct * 16 + l16] = acc[r];
             }
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int m = 0; m < L; ++m) {
             const int i = etb * L + m;
             sQG[i * LDF + ec] = qg[m];
             sKG[i * LDF + ec] = kg[m];
         }
-        __syncthreads();
+        lds_barrier();
+        // the next chunk's key-side inputs: issued here, their registers are live only across
+        // this phase (earlier, they force spills, and a spill reload would wait behind them)
+        if (n > 0) prefetch_key(n - 1);
         // dS = Gamma_C dS' + QG^T dO - KG^T dR
 #pragma unroll
         for (int s = 0; s < SPW; ++s) {
@@ -736,7 +790,7 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(
                 for (int r = 0; r < 4; ++r) dS[s][r] = dS[s][r] * sGC[st * 16 + g4 * 4 + r] + acc2[0][r] - acc2[1][r];
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
     if (d_initial) {
 #pragma unroll
