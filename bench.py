@@ -198,8 +198,8 @@ def run_bwd(args, torch, gdn2, W, dev):
     out = {"workload": wl.name, "us_per_call": ms * 1e3, "tokens_per_s": tokens / (ms * 1e-3), "GBps": gbps,
            "peak": HBM_PEAK_GBPS, "frac": gbps / HBM_PEAK_GBPS, "algorithmic_bytes_per_call": nbytes,
            "workspace_bytes": ws.numel(),
-           "kernels": "bwd_fwd_kernel (forward re-run), bwd_state_kernel (reverse pass), "
-                      "bwd_chunk_kernel (per-chunk gradients)"}
+           "kernels": "bwd_local_kernel (chunk-local quantities), bwd_fwd_kernel (forward re-run), "
+                      "bwd_state_kernel (reverse pass), bwd_chunk_kernel (per-chunk gradients)"}
     del d, d_o, ws, grads
     torch.cuda.empty_cache()
     return out

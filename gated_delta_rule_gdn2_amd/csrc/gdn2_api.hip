@@ -66,26 +66,26 @@ int device_cus() {
 }
 
 // Workspace of the backward pass: byte offsets of its five fp32 parts, each rounded up to 256
-// bytes.  False if the sizes overflow.
+// bytes.  False if the sizes overflow (or a head dimension exceeds 2^20).
 struct BwdLayout {
-    int64_t s_ckpt, ds_ckpt, u, dr, tp, total;
+    int64_t s_ckpt, ds_ckpt, u, dr, loc, total;
 };
 bool bwd_layout(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, BwdLayout* l) {
-    if (B < 0 || T < 0 || H < 0 || dk < 0 || dv < 0) return false;
+    if (B < 0 || T < 0 || H < 0 || dk < 0 || dv < 0 || dk > (1 << 20) || dv > (1 << 20)) return false;
     const int64_t nc = (T + 63) / 64;
     int64_t bh, bhn, st, btv, tpn;
     if (!mul_ok(B, H, &bh) || !mul_ok(bh, nc, &bhn) || !mul_ok(bhn, dk * dv, &st) || !mul_ok(st, 4, &st))
         return false;
     if (!mul_ok(B * H, T, &btv) || !mul_ok(btv, dv * 4, &btv)) return false;
-    if (!mul_ok(bhn, 2 * 64 * 64 * 4, &tpn)) return false;
+    if (!mul_ok(bhn, gdn2::bwd_rec_floats(dk, dv) * 4, &tpn)) return false;
     auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
     if (st > INT64_MAX / 8 || btv > INT64_MAX / 8 || tpn > INT64_MAX / 8) return false;
     l->s_ckpt = 0;
     l->ds_ckpt = up(st);
     l->u = l->ds_ckpt + up(st);
     l->dr = l->u + up(btv);
-    l->tp = l->dr + up(btv);
-    l->total = l->tp + up(tpn);
+    l->loc = l->dr + up(btv);
+    l->total = l->loc + up(tpn);
     return true;
 }
 
@@ -251,7 +251,7 @@ gdn2_status_t gdn2_chunk_bwd(const void* q, const void* k, const void* v, const 
     gdn2::BwdArgs a{q, k, v, log_alpha, b, w, initial_state, d_o, d_final_state, dq, dk, dv, dlog_alpha, db,
                     dw, d_initial_state, reinterpret_cast<float*>(ws + l.s_ckpt),
                     reinterpret_cast<float*>(ws + l.ds_ckpt), reinterpret_cast<float*>(ws + l.u),
-                    reinterpret_cast<float*>(ws + l.dr), reinterpret_cast<float*>(ws + l.tp), B, T, H, dk_dim,
+                    reinterpret_cast<float*>(ws + l.dr), reinterpret_cast<float*>(ws + l.loc), B, T, H, dk_dim,
                     dv_dim, dtype == GDN2_DTYPE_BF16, stream, cus};
     return gdn2::launch_chunk_bwd(a) == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }

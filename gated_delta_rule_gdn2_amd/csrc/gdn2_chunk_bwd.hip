@@ -74,6 +74,12 @@ __device__ __forceinline__ int opq(int x) {
     return x;
 }
 
+// Materialises x here: the compiler may not sink its computation past this point (a value
+// still being computed when a reload of the registers it reads is issued keeps the old and the
+// new value live together, and the loop then copies a register that a load has not filled yet,
+// which waits for every memory operation in flight).
+__device__ __forceinline__ void pin(f32x4& x) { asm volatile("" : "+v"(x)); }
+
 __device__ __forceinline__ f32x4 mfma4(const f32x4& acc, float a, float b) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
 }
@@ -179,48 +185,53 @@ __device__ __forceinline__ void load_key(KeyIn<In, L>& in, const In* __restrict_
 }
 
 // ---------------------------------------------------------------------------------------
-// Kernel 1: forward re-run in fp32 (one value-column slice per workgroup): the state entering
-// every chunk, U = T (w.v - KG S), and (slice 0) T and P of every chunk
+// Kernel 0: the chunk-local quantities, every chunk independently (a workgroup walks a run of
+// consecutive chunks of one sequence and head, loading the next chunk's inputs one chunk
+// ahead).  Each chunk gets one fp32 record (layout in gdn2_launch.h): T = (I + A)^{-1}, P,
+// W = T KG, KR, QG, U0 = T (w.v) and Gamma_C.
 // ---------------------------------------------------------------------------------------
-template <typename In, int DK, int DV, int DVS>
-struct FwdCfg {
+template <int DK, int DV>
+struct Rec {
+    static constexpr int64_t OT = 0, OP = C * C, OW = 2 * C * C, OKR = OW + C * DK, OQG = OKR + C * DK,
+                             OU0 = OQG + C * DK, OGC = OU0 + C * DV;
+    static constexpr int64_t SIZE = bwd_rec_floats(DK, DV);
+    static_assert(OGC + DK <= SIZE && SIZE % 64 == 0, "record layout");
+};
+
+template <typename In, int DK, int DV>
+struct LocCfg {
     static constexpr int TB = NT / DK, L = C / TB;
-    static constexpr int KT = DK / 16, NCT = DVS / 16;
-    static constexpr int NST = KT * NCT, SPW = (NST + 7) / 8;
+    static constexpr int KT = DK / 16, VT = DV / 16;
     static constexpr int ES = (int)sizeof(In);
     static constexpr int LDF = DK + 4;        // fp32 [64][DK]
     static constexpr int LDT = DK + 16 / ES;  // In [64][DK]
-    static constexpr int LDC = C + 4;
-    static constexpr int LDV = DVS + 4;
-    // operand tiles.  Pivoted chunk: KG = b.k.Gamma, KI = k / Gamma (then KR = KI.Gamma_C in
-    // place), QG = q.Gamma.  Other chunk, while A and P are formed: G (fp32) and the raw k, b,
-    // q; then KG and KR.
+    static constexpr int LDC = C + 4;         // fp32 [64][64]
+    static constexpr int LDW = DV + 4;        // fp32 [64][DV]
+    // operand tiles.  Pivoted chunk: KG = b.k.Gamma, KI = k / Gamma, QG = q.Gamma.  Other chunk,
+    // while A and P are formed: G (fp32, block-local) and the raw k, b, q; afterwards KG.
     static constexpr int KG = 0, KI = C * LDF * 4, QG = 2 * C * LDF * 4;
     static constexpr int GG = 0, RK = C * LDF * 4, RB = RK + C * LDT * ES, RQ = RB + C * LDT * ES;
     static constexpr int TILES = cmax(3 * C * LDF * 4, RQ + C * LDT * ES);
-    static constexpr int AT = TILES;              // [64][LDC] A, then T in place
-    static constexpr int WV = AT + C * LDC * 4;   // [64][LDV] w.v, then w.v - KG S
-    static constexpr int UU = WV + C * LDV * 4;   // [64][LDV] U
-    static constexpr int SC = UU + C * LDV * 4;   // [DK][LDV] S (operand copy)
-    static constexpr int GC = SC + DK * LDV * 4;  // [DK] Gamma_C
-    static constexpr int TOT = GC + DK * 4;       // [TB][DK] block sums of log alpha
-    static constexpr int OFH = TOT + TB * DK * 4; // [TB][DK] sums over the earlier blocks, hi
-    static constexpr int OFL = OFH + TB * DK * 4; // and lo
+    static constexpr int AT = TILES;               // [64][LDC] A, then T in place
+    static constexpr int WV = AT + C * LDC * 4;    // [64][LDW] w.v
+    static constexpr int TOT = WV + C * LDW * 4;   // [TB][DK] block sums of log alpha
+    static constexpr int OFH = TOT + TB * DK * 4;  // [TB][DK] sums over the earlier blocks, hi
+    static constexpr int OFL = OFH + TB * DK * 4;  // and lo
     static constexpr int FLG = OFL + TB * DK * 4;
     static constexpr int BYTES = FLG + 16;
     static_assert(BYTES <= 163840, "LDS budget exceeded");
-    static_assert(NT % DK == 0 && DVS % 16 == 0 && DV % DVS == 0, "shape");
+    static_assert(NT % DK == 0 && (KT + VT) % 4 == 0, "shape");
 };
 
-template <typename In, int DK, int DV, int DVS>
-__global__ __launch_bounds__(NT) void bwd_fwd_kernel(
+template <typename In, int DK, int DV>
+__global__ __launch_bounds__(NT) void bwd_local_kernel(
     const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
     const float* __restrict__ log_alpha, const In* __restrict__ bgate, const In* __restrict__ wgate,
-    const float* __restrict__ initial_state, float* __restrict__ s_ckpt, float* __restrict__ u_out,
-    float* __restrict__ tp, int T, int H, int nslices) {
-    using G = FwdCfg<In, DK, DV, DVS>;
-    constexpr int TB = G::TB, L = G::L, KT = G::KT, NCT = G::NCT, NST = G::NST, SPW = G::SPW;
-    constexpr int LDF = G::LDF, LDT = G::LDT, LDC = G::LDC, LDV = G::LDV;
+    float* __restrict__ loc, int T, int H, int nper) {
+    using G = LocCfg<In, DK, DV>;
+    using R = Rec<DK, DV>;
+    constexpr int TB = G::TB, L = G::L, KT = G::KT, VT = G::VT;
+    constexpr int LDF = G::LDF, LDT = G::LDT, LDC = G::LDC, LDW = G::LDW;
     __shared__ __attribute__((aligned(16))) char smem[G::BYTES];
     float* sKG = reinterpret_cast<float*>(smem + G::KG);
     float* sKI = reinterpret_cast<float*>(smem + G::KI);
@@ -229,46 +240,30 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
     In* sRK = reinterpret_cast<In*>(smem + G::RK);
     In* sRB = reinterpret_cast<In*>(smem + G::RB);
     In* sRQ = reinterpret_cast<In*>(smem + G::RQ);
-    float* sAT = reinterpret_cast<float*>(smem + G::AT);
     float* sWV = reinterpret_cast<float*>(smem + G::WV);
-    float* sUU = reinterpret_cast<float*>(smem + G::UU);
-    float* sSC = reinterpret_cast<float*>(smem + G::SC);
-    float* sGC = reinterpret_cast<float*>(smem + G::GC);
+    float* sAT = reinterpret_cast<float*>(smem + G::AT);
     float* sTOT = reinterpret_cast<float*>(smem + G::TOT);
     float* sOFH = reinterpret_cast<float*>(smem + G::OFH);
     float* sOFL = reinterpret_cast<float*>(smem + G::OFL);
     int* sFLG = reinterpret_cast<int*>(smem + G::FLG);
 
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63, lane16 = lane & 15, grp4 = lane >> 4;
-    const int bh = blockIdx.x / nslices, slice = blockIdx.x % nslices;
-    const int bi = bh / H, h = bh % H, col0 = slice * DVS;
+    const int tid_ = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid_ >> 6);
+    const int lane_ = tid_ & 63, lane16 = lane_ & 15, grp4 = lane_ >> 4;
     const int nch = (T + C - 1) / C;
+    const int ngrp = (nch + nper - 1) / nper;
+    const int bh = blockIdx.x / ngrp, n0 = (blockIdx.x % ngrp) * nper, n1 = min(nch, n0 + nper);
+    const int bi = bh / H, h = bh % H;
     const int64_t rk = (int64_t)H * DK, rv = (int64_t)H * DV;
     const int64_t base_k = ((int64_t)bi * T * H + h) * DK;
     const int64_t base_v = ((int64_t)bi * T * H + h) * DV;
-
-    f32x4 S[SPW];
-#pragma unroll
-    for (int s = 0; s < SPW; ++s) {
-        S[s] = zero4();
-        const int u = wave + 8 * s;
-        if (initial_state && u < NST) {
-            const int st = u % KT, ct = u / KT;
-            const float* src = initial_state + ((int64_t)bh * DK + st * 16 + grp4 * 4) * DV + col0 + ct * 16 + lane16;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) S[s][r] = src[(int64_t)r * DV];
-        }
-    }
     // off-diagonal blocks of T: wave w < 6 forms block (LI, LJ) at level LI - LJ
     const int LI = wave < 3 ? wave + 1 : (wave < 5 ? wave - 1 : 3);
     const int LJ = wave < 3 ? wave : (wave < 5 ? wave - 3 : 0);
 
-    const int ec_ = tid % DK, etb_ = tid / DK;
-    // the next chunk's inputs are loaded one phase ahead (before the state update of the chunk
-    // before it): key-side inputs, w and v of the slice
-    constexpr int NWV = (C * DVS / 4 + NT - 1) / NT;  // groups of 4 value columns per thread
+    const int ec_ = tid_ % DK, etb_ = tid_ / DK;
+    constexpr int NWV = C * DV / 4 / NT;  // groups of 4 value columns per thread
+    static_assert(NWV * 4 * NT == C * DV, "w.v split");
     KeyIn<In, L> in;
     Vec<In, 4> wr[NWV], vr[NWV];
     auto prefetch = [&](int nn) {
@@ -276,36 +271,22 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
         load_key<In, L>(in, q, k, bgate, log_alpha, base_k + ec_, rk, tt0 + etb_ * L, T);
 #pragma unroll
         for (int i = 0; i < NWV; ++i) {
-            const int e = tid + i * NT, r = e / (DVS / 4), c4 = (e % (DVS / 4)) * 4;
-            const int64_t o = base_v + (int64_t)min(tt0 + r, T - 1) * rv + col0 + c4;
-            if (e < C * DVS / 4) {
-                wr[i] = load_vec<In, 4>(wgate + o);
-                vr[i] = load_vec<In, 4>(v + o);
-            }
+            const int e = tid_ + i * NT, r = e / (DV / 4), c4 = (e % (DV / 4)) * 4;
+            const int64_t o = base_v + (int64_t)min(tt0 + r, T - 1) * rv + c4;
+            wr[i] = load_vec<In, 4>(wgate + o);
+            vr[i] = load_vec<In, 4>(v + o);
         }
     };
-    prefetch(0);
-    for (int n = 0; n < nch; ++n) {
+    if (n0 < n1) prefetch(n0);
+    for (int n = n0; n < n1; ++n) {
+        // lane indices opaque per chunk: loop-invariant values derived from them (masks, the
+        // identity columns of the substitution) would otherwise stay live across the loop
         const int l16 = opq(lane16), g4 = opq(grp4), ec = opq(ec_), etb = opq(etb_);
+        const int tid = opq(tid_), lane = tid & 63;
         const int t0 = n * C;
-        float* tpn = tp + ((int64_t)bh * nch + n) * 2 * C * C;
-        // the state entering the chunk: checkpoint and operand copy
-#pragma unroll
-        for (int s = 0; s < SPW; ++s) {
-            const int u = wave + 8 * s;
-            if (u < NST) {
-                const int st = u % KT, ct = u / KT;
-                float* dst = s_ckpt + (((int64_t)bh * nch + n) * DK + st * 16 + g4 * 4) * DV + col0 + ct * 16 + l16;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    dst[(int64_t)r * DV] = S[s][r];
-                    sSC[(st * 16 + g4 * 4 + r) * LDV + ct * 16 + l16] = S[s][r];
-                }
-            }
-        }
+        float* rec = loc + ((int64_t)bh * nch + n) * R::SIZE;
         if (tid == 0) *sFLG = 0;
-        // element phase, pass 1 (inputs prefetched): cumulative log-decay within the token block;
-        // w.v of the slice
+        // element phase, pass 1: cumulative log-decay within the token block; w.v (exact in fp32)
         float x[L];
         {
             float run = 0.f;
@@ -317,42 +298,44 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
             sTOT[etb * DK + ec] = run;
 #pragma unroll
             for (int i = 0; i < NWV; ++i) {
-                const int e = tid + i * NT, r = e / (DVS / 4), c4 = (e % (DVS / 4)) * 4;
-                if (e < C * DVS / 4) {
-                    f32x4 wv = zero4();
-                    if (t0 + r < T) {
+                const int e = tid + i * NT, r = e / (DV / 4), c4 = (e % (DV / 4)) * 4;
+                f32x4 wv = zero4();
+                if (t0 + r < T) {
 #pragma unroll
-                        for (int z = 0; z < 4; ++z) wv[z] = to_f32(wr[i].v[z]) * to_f32(vr[i].v[z]);
-                    }
-                    *reinterpret_cast<f32x4*>(sWV + r * LDV + c4) = wv;
+                    for (int z = 0; z < 4; ++z) wv[z] = to_f32(wr[i].v[z]) * to_f32(vr[i].v[z]);
                 }
+                *reinterpret_cast<f32x4*>(sWV + r * LDW + c4) = wv;
             }
         }
         lds_barrier();
-        float off = 0.f, tot = 0.f, after = 0.f, oh = 0.f, ol = 0.f;
+        float off = 0.f, after = 0.f;
+        {
+            float tot = 0.f, oh = 0.f, ol = 0.f;
 #pragma unroll
-        for (int j = 0; j < TB; ++j) {
-            const float vj = sTOT[j * DK + ec];
-            tot += vj;
-            if (j < etb) {
-                off += vj;
-                float sv, ev;
-                two_sum(oh, vj, sv, ev);
-                oh = sv;
-                ol += ev;
+            for (int j = 0; j < TB; ++j) {
+                const float vj = sTOT[j * DK + ec];
+                tot += vj;
+                if (j < etb) {
+                    off += vj;
+                    float sv, ev;
+                    two_sum(oh, vj, sv, ev);
+                    oh = sv;
+                    ol += ev;
+                }
+                if (j > etb) after += vj;
             }
-            if (j > etb) after += vj;
+            sOFH[etb * DK + ec] = oh;
+            sOFL[etb * DK + ec] = ol;
+            if (etb == 0) {
+                rec[R::OGC + ec] = exp_any(tot);
+                if (!(tot >= kMildLog)) *sFLG = 1;
+            }
         }
-        const float run = sTOT[etb * DK + ec];
-        sOFH[etb * DK + ec] = oh;
-        sOFL[etb * DK + ec] = ol;
-        if (etb == 0) {
-            sGC[ec] = exp_any(tot);
-            if (!(tot >= kMildLog)) *sFLG = 1;
-        }
+        const float run = x[L - 1];
         lds_barrier();
         const bool mild = *sFLG == 0;
-        // element phase, pass 2: operand tiles
+        // element phase, pass 2: QG and KR = k.Gamma_C / Gamma (suffix sums) to the record;
+        // operand tiles of A and P
 #pragma unroll
         for (int m = 0; m < L; ++m) {
             const int i = etb * L + m, t = t0 + i;
@@ -363,11 +346,14 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
                 bv = in.b[m];
             }
             const float Gi = x[m] + off;
+            const float ga = exp_any(Gi);
+            const float qg = to_f32(qv) * ga;
+            rec[R::OQG + i * DK + ec] = qg;
+            rec[R::OKR + i * DK + ec] = to_f32(kv) * exp_any((run - x[m]) + after);
             if (mild) {
-                const float ga = exp_any(Gi);
                 sKG[i * LDF + ec] = to_f32(bv) * to_f32(kv) * ga;
                 sKI[i * LDF + ec] = to_f32(kv) * exp_any(-Gi);
-                sQG[i * LDF + ec] = to_f32(qv) * ga;
+                sQG[i * LDF + ec] = qg;
             } else {
                 sG[i * LDF + ec] = x[m];  // block-local
                 sRK[i * LDT + ec] = kv;
@@ -375,13 +361,12 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
                 sRQ[i * LDT + ec] = qv;
             }
         }
-        if (n + 1 < nch) prefetch(n + 1);
+        prefetch(min(n + 1, n1 - 1));  // on every path (see the serial kernels)
         lds_barrier();
-        // A (strictly lower, into the A/T tile) and, in slice 0, P (lower, to tp)
+        // A (strictly lower, into the A/T tile) and P (lower, to the record)
         if (mild) {
             // lower 16 x 16 blocks (I >= J) in the order (0,0) (1,0) (1,1) (2,0) ...: blocks 0-9 of
-            // A and, in slice 0, blocks 10-19 of P; wave w takes blocks w, w + 8, w + 16
-            const int nt = slice == 0 ? 20 : 10;
+            // A, blocks 10-19 of P; wave w takes blocks w, w + 8, w + 16
             auto blk = [](int u, int& I, int& J) {
                 const int x = u % 10;
                 I = x < 1 ? 0 : (x < 3 ? 1 : (x < 6 ? 2 : 3));
@@ -404,21 +389,20 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
 #pragma unroll
             for (int t = 0; t < 3; ++t) {
                 const int u = wave + 8 * t;
-                if (u >= nt) continue;
+                if (u >= 20) continue;
                 int I, J;
                 blk(u, I, J);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = I * 16 + g4 * 4 + r, j = J * 16 + l16;
                     if (u < 10) sAT[i * LDC + j] = j < i ? acc[t][r] : 0.f;
-                    else tpn[C * C + i * C + j] = j <= i ? acc[t][r] : 0.f;
+                    else rec[R::OP + i * C + j] = j <= i ? acc[t][r] : 0.f;
                 }
             }
-            if (slice == 0) {  // P above the diagonal blocks is zero
-                for (int e = tid; e < C * C; e += NT) {
-                    const int i = e / C, j = e % C;
-                    if (j / 16 > i / 16) tpn[C * C + e] = 0.f;
-                }
+            // P above the diagonal blocks is zero
+            for (int e = tid; e < C * C; e += NT) {
+                const int i = e / C, j = e % C;
+                if (j / 16 > i / 16) rec[R::OP + e] = 0.f;
             }
         } else {
             const int i = tid & 63, jg = tid >> 6;
@@ -437,26 +421,23 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
                     }
                 }
                 sAT[i * LDC + j] = j < i ? a : 0.f;
-                if (slice == 0) tpn[C * C + i * C + j] = p;
+                rec[R::OP + i * C + j] = p;
             }
         }
         lds_barrier();
-        // KG and KR = k.Gamma_C / Gamma for the state products
+        // KG of the other kind of chunk (k and b reloaded: keeping the raw inputs live costs
+        // registers everywhere), over the tiles A and P no longer need
+        if (!mild) {
 #pragma unroll
-        for (int m = 0; m < L; ++m) {
-            const int i = etb * L + m, t = t0 + i;
-            if (mild) {
-                sKI[i * LDF + ec] *= sGC[ec];
-            } else {
+            for (int m = 0; m < L; ++m) {
+                const int i = etb * L + m, t = t0 + i;
                 float kv = 0.f, bv = 0.f;
-                if (t < T) {  // reloaded: keeping the raw inputs live costs registers everywhere
+                if (t < T) {
                     const int64_t o = base_k + (int64_t)t * rk + ec;
                     kv = to_f32(k[o]);
                     bv = to_f32(bgate[o]);
                 }
-                const float Gi = x[m] + off;
-                sKG[i * LDF + ec] = bv * kv * exp_any(Gi);
-                sKI[i * LDF + ec] = kv * exp_any((run - x[m]) + after);
+                sKG[i * LDF + ec] = bv * kv * exp_any(x[m] + off);
             }
         }
         // T = (I + A)^{-1}: diagonal blocks by forward substitution (column j on lane j of
@@ -511,298 +492,412 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(
             }
             lds_barrier();
         }
-        if (slice == 0) {
-            for (int e = tid; e < C * C; e += NT) {
-                const int i = e / C, j = e % C;
-                tpn[e] = j <= i ? sAT[i * LDC + j] : 0.f;
+        for (int e = tid; e < C * C; e += NT) {
+            const int i = e / C, j = e % C;
+            rec[R::OT + e] = j <= i ? sAT[i * LDC + j] : 0.f;
+        }
+        // W = T KG and U0 = T (w.v): wave w takes the row tiles p and 3 - p (p = w mod 2) of the
+        // column tiles cg, cg + 4, ... (cg = w / 2) of [W | U0]; T is lower triangular, so row
+        // tile I runs over the contraction blocks 0..I only
+        {
+            constexpr int NCOL = (KT + VT) / 4;
+            const int p = wave & 1, cg = wave >> 1;
+            f32x4 acc0[NCOL], acc1[NCOL];
+#pragma unroll
+            for (int c = 0; c < NCOL; ++c) acc0[c] = acc1[c] = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+                for (int s = 0; s < 16; s += 4) {
+                    const int kk = kb * 16 + s + g4;
+                    const float a0 = sAT[(p * 16 + l16) * LDC + kk];
+                    const float a1 = sAT[((3 - p) * 16 + l16) * LDC + kk];
+                    float bc[NCOL];
+#pragma unroll
+                    for (int c = 0; c < NCOL; ++c) {
+                        const int ct = cg + 4 * c;
+                        bc[c] = ct < KT ? sKG[kk * LDF + ct * 16 + l16] : sWV[kk * LDW + (ct - KT) * 16 + l16];
+                    }
+#pragma unroll
+                    for (int c = 0; c < NCOL; ++c) {
+                        if (kb <= p) acc0[c] = mfma4(acc0[c], a0, bc[c]);
+                        if (kb <= 3 - p) acc1[c] = mfma4(acc1[c], a1, bc[c]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < NCOL; ++c) {
+                const int ct = cg + 4 * c;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i0 = p * 16 + g4 * 4 + r, i1 = (3 - p) * 16 + g4 * 4 + r;
+                    if (ct < KT) {
+                        rec[R::OW + i0 * DK + ct * 16 + l16] = acc0[c][r];
+                        rec[R::OW + i1 * DK + ct * 16 + l16] = acc1[c][r];
+                    } else {
+                        rec[R::OU0 + i0 * DV + (ct - KT) * 16 + l16] = acc0[c][r];
+                        rec[R::OU0 + i1 * DV + (ct - KT) * 16 + l16] = acc1[c][r];
+                    }
+                }
             }
         }
-        // w.v - KG S, in place
-        for (int u = wave; u < 4 * NCT; u += 8) {
-            const int it = u % 4, ct = u / 4;
-            f32x4 acc = zero4();
-            mm_split<4, DK>(acc, [&](int m, int kk) { return sKG[(it * 16 + m) * LDF + kk]; },
-                            [&](int kk, int nn) { return sSC[kk * LDV + ct * 16 + nn]; }, l16, g4);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float* p = sWV + (it * 16 + g4 * 4 + r) * LDV + ct * 16 + l16;
-                *p -= acc[r];
-            }
-        }
-        lds_barrier();
-        // U = T (w.v - KG S)
-        for (int u = wave; u < 4 * NCT; u += 8) {
-            const int it = u % 4, ct = u / 4;
-            f32x4 acc = zero4();
-            // T is lower triangular: blocks 0..it of the contraction, as separate chains
-            mm_tail64(acc, [&](int m, int kk) { return kk < it * 16 + 16 ? sAT[(it * 16 + m) * LDC + kk] : 0.f; },
-                      [&](int kk, int nn) { return sWV[kk * LDV + ct * 16 + nn]; }, 0, l16, g4);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = it * 16 + g4 * 4 + r, t = t0 + i;
-                sUU[i * LDV + ct * 16 + l16] = acc[r];
-                if (t < T) u_out[base_v + (int64_t)t * rv + col0 + ct * 16 + l16] = acc[r];
-            }
-        }
-        lds_barrier();
-        // S <- Gamma_C S + KR^T U
-#pragma unroll
-        for (int s = 0; s < SPW; ++s) {
-            const int u = wave + 8 * s;
-            if (u < NST) {
-                const int st = u % KT, ct = u / KT;
-                f32x4 acc;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] = S[s][r] * sGC[st * 16 + g4 * 4 + r];
-                mm_split<4, C>(acc, [&](int m, int kk) { return sKI[kk * LDF + st * 16 + m]; },
-                               [&](int kk, int nn) { return sUU[kk * LDV + ct * 16 + nn]; }, l16, g4);
-                S[s] = acc;
-            }
-        }
-        lds_barrier();
+        // the next chunk's first LDS writes (block sums, flag) touch nothing read above, and its
+        // operand tiles come after two barriers
     }
 }
 
 // ---------------------------------------------------------------------------------------
-// Kernel 2: reverse pass over the chunks for dS (one value-column slice per workgroup)
+// Kernels 1 and 2 walk the chunks of one (sequence, head, slice of value columns) in order.
+// Every wave owns one 16 x 16 tile of the slice's state (or state gradient) in MFMA
+// accumulators: key rows 16 st .. 16 st + 15 (st = wave mod KT), value columns 16 ct ..
+// (ct = wave / KT); so a slice is 16 * 8 / KT columns wide.  A product over the key axis
+// with the state as right operand runs as eight partial products, one per wave over its own
+// 16 rows (the accumulator layout is the operand layout), summed in LDS.
 // ---------------------------------------------------------------------------------------
-template <typename In, int DK, int DV, int DVS>
-struct StateCfg {
-    static constexpr int TB = NT / DK;       // token blocks of the element phase
-    static constexpr int L = C / TB;         // tokens per block
-    static constexpr int KT = DK / 16, NCT = DVS / 16;
-    static constexpr int NST = KT * NCT;     // 16 x 16 tiles of the dS slice
-    static constexpr int SPW = (NST + 7) / 8;
-    static constexpr int LDF = DK + 4;       // fp32 [64][DK]
-    static constexpr int LDC = C + 4;        // fp32 [64][64]
-    static constexpr int LDV = DVS + 4;      // fp32 [*][DVS]
-    // KR, P and T are dead once dR is formed; q.Gamma and b.k.Gamma take their place
-    static constexpr int KR = 0;                         // [64][LDF] k.Gamma_C / Gamma
-    static constexpr int PP = KR + C * LDF * 4;          // [64][LDC] P
-    static constexpr int TT = PP + C * LDC * 4;          // [64][LDC] T
-    static constexpr int QG = 0;                         // [64][LDF] q.Gamma
-    static constexpr int KG = QG + C * LDF * 4;          // [64][LDF] b.k.Gamma
-    static constexpr int DO = TT + C * LDC * 4;          // [64][LDV] dO slice
-    static constexpr int DU = DO + C * LDV * 4;          // [64][LDV] dU
-    static constexpr int DR = DU + C * LDV * 4;          // [64][LDV] dR
-    static constexpr int DS = DR + C * LDV * 4;          // [DK][LDV] dS' (operand copy)
-    static constexpr int GC = DS + DK * LDV * 4;         // [DK] Gamma_C
-    static constexpr int TOT = GC + DK * 4;              // [TB][DK] block sums of log alpha
-    static constexpr int BYTES = TOT + TB * DK * 4;
-    static_assert(BYTES <= 163840, "LDS budget exceeded");
-    static_assert(KG + C * LDF * 4 <= DO, "q.Gamma and b.k.Gamma do not fit over KR, P, T");
-    static_assert(NT % DK == 0 && C % TB == 0 && DVS % 16 == 0 && DV % DVS == 0, "shape");
+template <int DK, int DV>
+struct SerCfg {
+    static constexpr int KT = DK / 16;
+    static constexpr int NCT = 8 / KT;       // column tiles of a slice
+    static constexpr int DVS = 16 * NCT;     // value columns of a slice
+    static constexpr int NSL = DV / DVS;     // slices
+    static constexpr int OPT = C * DVS / NT; // summed outputs per thread (consecutive columns)
+    static constexpr int TPR = DVS / OPT;    // threads per row of the sums
+    static_assert(KT * NCT == 8 && DV % DVS == 0 && (OPT == 2 || OPT == 4), "shape");
 };
 
-template <typename In, int DK, int DV, int DVS>
-__global__ __launch_bounds__(NT) void bwd_state_kernel(
-    const In* __restrict__ q, const In* __restrict__ k, const float* __restrict__ log_alpha,
-    const In* __restrict__ bgate, const float* __restrict__ d_o, const float* __restrict__ d_final,
-    const float* __restrict__ tp, float* __restrict__ ds_ckpt, float* __restrict__ dr_out,
-    float* __restrict__ d_initial, int T, int H, int nslices) {
-    using G = StateCfg<In, DK, DV, DVS>;
-    constexpr int TB = G::TB, L = G::L, KT = G::KT, NCT = G::NCT, NST = G::NST, SPW = G::SPW;
-    constexpr int LDF = G::LDF, LDC = G::LDC, LDV = G::LDV;
-    __shared__ __attribute__((aligned(16))) char smem[G::BYTES];
-    float* sQG = reinterpret_cast<float*>(smem + G::QG);
-    float* sKG = reinterpret_cast<float*>(smem + G::KG);
-    float* sKR = reinterpret_cast<float*>(smem + G::KR);
-    float* sT = reinterpret_cast<float*>(smem + G::TT);
-    float* sP = reinterpret_cast<float*>(smem + G::PP);
-    float* sDO = reinterpret_cast<float*>(smem + G::DO);
-    float* sDU = reinterpret_cast<float*>(smem + G::DU);
-    float* sDR = reinterpret_cast<float*>(smem + G::DR);
-    float* sDS = reinterpret_cast<float*>(smem + G::DS);
-    float* sGC = reinterpret_cast<float*>(smem + G::GC);
-    float* sTOT = reinterpret_cast<float*>(smem + G::TOT);
+template <int N>
+__device__ __forceinline__ void load_n(float (&d)[N], const float* p) {
+    if constexpr (N == 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d[i] = x[i];
+    } else {
+        static_assert(N == 2, "width");
+        const float2 x = *reinterpret_cast<const float2*>(p);
+        d[0] = x.x;
+        d[1] = x.y;
+    }
+}
+template <int N>
+__device__ __forceinline__ void store_n(float* p, const float (&d)[N]) {
+    if constexpr (N == 4) {
+        *reinterpret_cast<f32x4*>(p) = f32x4{d[0], d[1], d[2], d[3]};
+    } else {
+        static_assert(N == 2, "width");
+        *reinterpret_cast<float2*>(p) = make_float2(d[0], d[1]);
+    }
+}
+
+// Kernel 1: the forward re-run, U = U0 - W S and S <- Gamma_C.S + KR^T U per chunk; stores
+// the state entering every chunk and U
+template <int OPT>
+struct FwdIn {  // one chunk's record entries for this thread
+    f32x4 Wv[4], GCv;
+    float KRv[16], U0v[OPT];
+};
+template <int DK, int DV>
+__global__ __launch_bounds__(NT) void bwd_fwd_kernel(const float* __restrict__ loc,
+                                                     const float* __restrict__ initial_state,
+                                                     float* __restrict__ s_ckpt, float* __restrict__ u_out,
+                                                     int T, int H, int BH) {
+    using SC = SerCfg<DK, DV>;
+    using R = Rec<DK, DV>;
+    constexpr int KT = SC::KT, DVS = SC::DVS, OPT = SC::OPT, TPR = SC::TPR;
+    __shared__ __attribute__((aligned(16))) float sPart[8 * C * 16];
+    __shared__ __attribute__((aligned(16))) float sU[C * DVS];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63, lane16 = lane & 15, grp4 = lane >> 4;
-    const int bh = blockIdx.x / nslices, slice = blockIdx.x % nslices;
+    const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    // the slices of one sequence and head are BH workgroups apart: on the same L2 when BH is a
+    // multiple of the XCD count
+    const int bh = blockIdx.x % BH, slice = blockIdx.x / BH;
     const int bi = bh / H, h = bh % H, col0 = slice * DVS;
     const int nch = (T + C - 1) / C;
-    const int64_t rk = (int64_t)H * DK, rv = (int64_t)H * DV;  // elements between tokens
-    const int64_t base_k = ((int64_t)bi * T * H + h) * DK;
+    const int st = wave % KT, ct = wave / KT;
+    const int64_t rv = (int64_t)H * DV;
     const int64_t base_v = ((int64_t)bi * T * H + h) * DV;
+    const int ri = tid / TPR, rc = (tid % TPR) * OPT;  // summed outputs: row ri, columns rc..
+    const int rct = rc / 16, rcc = rc % 16;
 
-    // dS slice in accumulators: tile u = wave + 8 s has row tile u % KT, column tile u / KT;
-    // lane (n, g) holds dS[16 st + 4 g + r][16 ct + n]
-    f32x4 dS[SPW];
+    f32x4 S = zero4();
+    if (initial_state) {
+        const float* src = initial_state + ((int64_t)bh * DK + st * 16 + g4 * 4) * DV + col0 + ct * 16 + l16;
 #pragma unroll
-    for (int s = 0; s < SPW; ++s) {
-        dS[s] = zero4();
-        const int u = wave + 8 * s;
-        if (d_final && u < NST) {
-            const int st = u % KT, ct = u / KT;
-            const float* src = d_final + ((int64_t)bh * DK + st * 16 + grp4 * 4) * DV + col0 + ct * 16 + lane16;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dS[s][r] = src[(int64_t)r * DV];
-        }
+        for (int r = 0; r < 4; ++r) S[r] = src[(int64_t)r * DV];
     }
-
-    const int ec_ = tid % DK, etb_ = tid / DK;  // element phase: channel, token block
-    // the next chunk's inputs are loaded one phase ahead (before the dS update of the chunk
-    // before it): key-side inputs, T and P, the dO slice
-    constexpr int NTP = 2 * C * C / 4 / NT;             // float4 of T and P per thread
-    constexpr int NDO = (C * DVS / 4 + NT - 1) / NT;    // float4 of dO per thread
-    KeyIn<In, L> in;
-    f32x4 tpv[NTP], dov[NDO];
-    auto prefetch_key = [&](int nn) {
-        load_key<In, L>(in, q, k, bgate, log_alpha, base_k + ec_, rk, nn * C + etb_ * L, T);
-    };
-    auto prefetch_tp = [&](int nn) {
-        const int tt0 = nn * C;
-        const float* src = tp + ((int64_t)bh * nch + nn) * 2 * C * C;
+    // record entries are loaded two chunks ahead, into the set just consumed, each part right
+    // after its last use
+    auto rec_of = [&](int nn) { return loc + ((int64_t)bh * nch + nn) * R::SIZE; };
+    auto pre_w = [&](FwdIn<OPT>& d, int nn) {
+        const float* rec = rec_of(nn);
 #pragma unroll
-        for (int i = 0; i < NTP; ++i) tpv[i] = *reinterpret_cast<const f32x4*>(src + (tid + i * NT) * 4);
-#pragma unroll
-        for (int i = 0; i < NDO; ++i) {
-            const int e = tid + i * NT, r = e / (DVS / 4), c4 = (e % (DVS / 4)) * 4;
-            const int t = min(tt0 + r, T - 1);
-            dov[i] = e < C * DVS / 4 ? *reinterpret_cast<const f32x4*>(d_o + base_v + (int64_t)t * rv + col0 + c4)
-                                     : zero4();
-        }
+        for (int it = 0; it < 4; ++it)
+            d.Wv[it] = *reinterpret_cast<const f32x4*>(rec + R::OW + (it * 16 + l16) * DK + st * 16 + g4 * 4);
     };
-    prefetch_key(nch - 1);
-    prefetch_tp(nch - 1);
-    for (int n = nch - 1; n >= 0; --n) {
-        const int l16 = opq(lane16), g4 = opq(grp4), ec = opq(ec_), etb = opq(etb_);
+    auto pre_u0 = [&](FwdIn<OPT>& d, int nn) { load_n<OPT>(d.U0v, rec_of(nn) + R::OU0 + ri * DV + col0 + rc); };
+    auto pre_kr = [&](FwdIn<OPT>& d, int nn) {
+        const float* rec = rec_of(nn);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) d.KRv[j] = rec[R::OKR + (4 * j + g4) * DK + st * 16 + l16];
+        d.GCv = *reinterpret_cast<const f32x4*>(rec + R::OGC + st * 16 + g4 * 4);
+    };
+    // the prefetches are issued on every path (the last chunks load the final record again): a
+    // load skipped on some path makes the compiler's wait before each use cover every memory
+    // operation still in flight
+    auto step = [&](FwdIn<OPT>& d, int n) {
         const int t0 = n * C;
-        // dS' of this chunk: checkpoint for kernel 3 and operand copy
+        const int nn = min(n + 2, nch - 1);
+        // checkpoint of the state entering the chunk
+        {
+            float* dst = s_ckpt + (((int64_t)bh * nch + n) * DK + st * 16 + g4 * 4) * DV + col0 + ct * 16 + l16;
 #pragma unroll
-        for (int s = 0; s < SPW; ++s) {
-            const int u = wave + 8 * s;
-            if (u < NST) {
-                const int st = u % KT, ct = u / KT;
-                float* dst = ds_ckpt + (((int64_t)bh * nch + n) * DK + st * 16 + g4 * 4) * DV + col0 + ct * 16 + l16;
+            for (int r = 0; r < 4; ++r) dst[(int64_t)r * DV] = S[r];
+        }
+        // this wave's part of W S
+        {
+            f32x4 acc[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    dst[(int64_t)r * DV] = dS[s][r];
-                    sDS[(st * 16 + g4 * 4 + r) * LDV + ct * 16 + l16] = dS[s][r];
+            for (int it = 0; it < 4; ++it) acc[it] = zero4();
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int it = 0; it < 4; ++it) acc[it] = mfma4(acc[it], d.Wv[it][j], S[j]);
+            __builtin_amdgcn_sched_barrier(0);  // the reload after the last use: same registers
+            pre_w(d, nn);
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sPart[(wave * C + it * 16 + g4 * 4 + r) * 16 + l16] = acc[it][r];
+        }
+        lds_barrier();
+        // U = U0 - W S
+        {
+            float u[OPT];
+#pragma unroll
+            for (int o = 0; o < OPT; ++o) u[o] = d.U0v[o];
+#pragma unroll
+            for (int s2 = 0; s2 < KT; ++s2) {
+                float p[OPT];
+                load_n<OPT>(p, sPart + ((rct * KT + s2) * C + ri) * 16 + rcc);
+#pragma unroll
+                for (int o = 0; o < OPT; ++o) u[o] -= p[o];
+            }
+            store_n<OPT>(sU + ri * DVS + rc, u);
+            if (t0 + ri < T) store_n<OPT>(u_out + base_v + (int64_t)(t0 + ri) * rv + col0 + rc, u);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // the reload after the last use: same registers
+        pre_u0(d, nn);
+        lds_barrier();
+        // S <- Gamma_C.S + KR^T U
+        {
+            f32x4 a2[2];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a2[0][r] = S[r] * d.GCv[r];
+            a2[1] = zero4();
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                a2[j & 1] = mfma4(a2[j & 1], d.KRv[j], sU[(4 * j + g4) * DVS + ct * 16 + l16]);
+            S = a2[0] + a2[1];
+            pin(S);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // the reload after the last use: same registers
+        pre_kr(d, nn);
+    };
+    FwdIn<OPT> in0, in1;
+    pre_w(in0, 0);
+    pre_u0(in0, 0);
+    pre_kr(in0, 0);
+    pre_w(in1, min(1, nch - 1));
+    pre_u0(in1, min(1, nch - 1));
+    pre_kr(in1, min(1, nch - 1));
+    // pairs of chunks, every path through the loop body the same (see above)
+    int n = 0;
+    for (; n + 1 < nch; n += 2) {
+        step(in0, n);
+        step(in1, n + 1);
+    }
+    if (n < nch) step(in0, n);
+}
+
+// Kernel 2: the chunks in reverse order, dU = P^T dO + KR dS', dS = Gamma_C.dS' + QG^T dO -
+// W^T dU (W^T = KG^T T^T), dR = T^T dU; stores dS' of every chunk, dR, and the gradient of the
+// initial state
+template <int DK, int DV>
+__global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__ loc, const float* __restrict__ d_o,
+                                                       const float* __restrict__ d_final,
+                                                       float* __restrict__ ds_ckpt, float* __restrict__ dr_out,
+                                                       float* __restrict__ d_initial, int T, int H, int BH) {
+    using SC = SerCfg<DK, DV>;
+    using R = Rec<DK, DV>;
+    constexpr int KT = SC::KT, DVS = SC::DVS, OPT = SC::OPT, TPR = SC::TPR;
+    constexpr int JW = C / KT;  // tokens of P^T dO in this wave's part
+    constexpr int JS = JW / 4;  // their MFMA steps
+    __shared__ __attribute__((aligned(16))) float sPart[8 * C * 16];
+    __shared__ __attribute__((aligned(16))) float sDU[C * DVS];
+    __shared__ __attribute__((aligned(16))) float sDO[2][C * DVS];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int bh = blockIdx.x % BH, slice = blockIdx.x / BH;
+    const int bi = bh / H, h = bh % H, col0 = slice * DVS;
+    const int nch = (T + C - 1) / C;
+    const int st = wave % KT, ct = wave / KT;
+    const int64_t rv = (int64_t)H * DV;
+    const int64_t base_v = ((int64_t)bi * T * H + h) * DV;
+    const int ri = tid / TPR, rc = (tid % TPR) * OPT;
+    const int rct = rc / 16, rcc = rc % 16;
+    // dR tile of this wave: row tile dri (waves with st < 4), column tile ct
+    const bool has_dr = st < 4;
+    const int dri = st & 3;
+
+    f32x4 dS = zero4();
+    if (d_final) {
+        const float* src = d_final + ((int64_t)bh * DK + st * 16 + g4 * 4) * DV + col0 + ct * 16 + l16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dS[r] = src[(int64_t)r * DV];
+    }
+    f32x4 KRv[4], GCv;
+    float Pv[4][JS], dOp[JS], dOs[OPT], QGv[16], Wt[16], Tv[16];
+    auto rec_of = [&](int nn) { return loc + ((int64_t)bh * nch + nn) * R::SIZE; };
+    auto do_row = [&](int t) { return d_o + base_v + (int64_t)min(t, T - 1) * rv + col0; };
+    auto pre_du = [&](int nn) {  // operands of the dU parts
+        const float* rec = rec_of(nn);
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+            KRv[it] = *reinterpret_cast<const f32x4*>(rec + R::OKR + (it * 16 + l16) * DK + st * 16 + g4 * 4);
+#pragma unroll
+        for (int s = 0; s < JS; ++s) {
+            const int j = st * JW + 4 * s + g4;
+#pragma unroll
+            for (int it = 0; it < 4; ++it) Pv[it][s] = rec[R::OP + j * C + it * 16 + l16];
+            dOp[s] = nn * C + j < T ? do_row(nn * C + j)[ct * 16 + l16] : 0.f;
+        }
+    };
+    auto pre_do = [&](int nn) {  // the dO slice for LDS
+        load_n<OPT>(dOs, do_row(nn * C + ri) + rc);
+        if (nn * C + ri >= T) {
+#pragma unroll
+            for (int o = 0; o < OPT; ++o) dOs[o] = 0.f;
+        }
+    };
+    auto pre_ds = [&](int nn) {  // operands of the dS update
+        const float* rec = rec_of(nn);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            QGv[j] = rec[R::OQG + (4 * j + g4) * DK + st * 16 + l16];
+            Wt[j] = rec[R::OW + (4 * j + g4) * DK + st * 16 + l16];
+        }
+        GCv = *reinterpret_cast<const f32x4*>(rec + R::OGC + st * 16 + g4 * 4);
+    };
+    auto pre_t = [&](int nn) {  // T^T operand of the dR tile: T[j][16 dri + m], j >= 16 dri
+        const float* rec = rec_of(nn);
+        if (has_dr) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    Tv[kb * 4 + s] = kb >= dri ? rec[R::OT + (kb * 16 + 4 * s + g4) * C + dri * 16 + l16] : 0.f;
+        }
+    };
+    pre_du(nch - 1);
+    pre_do(nch - 1);
+    pre_ds(nch - 1);
+    pre_t(nch - 1);
+    // the prefetches are issued on every path (chunk 0 loads its own record again): a load
+    // skipped on some path makes the compiler's wait before each use cover every memory
+    // operation still in flight
+    for (int n = nch - 1; n >= 0; --n) {
+        const int t0 = n * C;
+        float* sDOn = sDO[n & 1];
+        // dS' of this chunk, checkpoint for kernel 3
+        {
+            float* dst = ds_ckpt + (((int64_t)bh * nch + n) * DK + st * 16 + g4 * 4) * DV + col0 + ct * 16 + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[(int64_t)r * DV] = dS[r];
+        }
+        store_n<OPT>(sDOn + ri * DVS + rc, dOs);
+        __builtin_amdgcn_sched_barrier(0);  // the reload after the last use: same registers
+        pre_do(max(n - 1, 0));
+        // this wave's parts of KR dS' (its 16 key rows) and of P^T dO (its JW tokens)
+        {
+            f32x4 acc[4];
+#pragma unroll
+            for (int it = 0; it < 4; ++it) acc[it] = zero4();
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int it = 0; it < 4; ++it) acc[it] = mfma4(acc[it], KRv[it][j], dS[j]);
+#pragma unroll
+            for (int s = 0; s < JS; ++s) {
+                const int jb = (st * JW + 4 * s) / 16;  // token block: P[j][i] = 0 for row tiles past it
+#pragma unroll
+                for (int it = 0; it < 4; ++it)
+                    if (it <= jb) acc[it] = mfma4(acc[it], Pv[it][s], dOp[s]);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // the reload after the last use: same registers
+            pre_du(max(n - 1, 0));
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sPart[(wave * C + it * 16 + g4 * 4 + r) * 16 + l16] = acc[it][r];
+        }
+        lds_barrier();
+        // dU = sum of the parts of this column tile
+        {
+            float u[OPT];
+#pragma unroll
+            for (int o = 0; o < OPT; ++o) u[o] = 0.f;
+#pragma unroll
+            for (int s2 = 0; s2 < KT; ++s2) {
+                float p[OPT];
+                load_n<OPT>(p, sPart + ((rct * KT + s2) * C + ri) * 16 + rcc);
+#pragma unroll
+                for (int o = 0; o < OPT; ++o) u[o] += p[o];
+            }
+            store_n<OPT>(sDU + ri * DVS + rc, u);
+        }
+        lds_barrier();
+        // dS <- Gamma_C.dS' + QG^T dO - W^T dU
+        {
+            f32x4 a2[2] = {zero4(), zero4()};
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int o = (4 * j + g4) * DVS + ct * 16 + l16;
+                a2[0] = mfma4(a2[0], QGv[j], sDOn[o]);
+                a2[1] = mfma4(a2[1], Wt[j], sDU[o]);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dS[r] = dS[r] * GCv[r] + a2[0][r] - a2[1][r];
+            pin(dS);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // the reload after the last use: same registers
+        pre_ds(max(n - 1, 0));
+        // dR = T^T dU (row tile dri)
+        if (has_dr) {
+            f32x4 acc[2] = {zero4(), zero4()};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                if (kb >= dri) {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        acc[s & 1] = mfma4(acc[s & 1], Tv[kb * 4 + s], sDU[(kb * 16 + 4 * s + g4) * DVS + ct * 16 + l16]);
                 }
-            }
-        }
-        // element phase, pass 1: cumulative log-decay within the token block (inputs prefetched)
-        float x[L];
-        {
-            float run = 0.f;
-#pragma unroll
-            for (int m = 0; m < L; ++m) {
-                run += t0 + etb * L + m < T ? in.g[m] : 0.f;
-                x[m] = run;
-            }
-            sTOT[etb * DK + ec] = run;
-        }
-        // T and P of the chunk, and the dO slice (prefetched)
-        {
-#pragma unroll
-            for (int i = 0; i < NTP; ++i) {
-                const int e = tid + i * NT;
-                const int mat = e / (C * C / 4), r = (e / (C / 4)) % C, c4 = (e % (C / 4)) * 4;
-                *reinterpret_cast<f32x4*>((mat ? sP : sT) + r * LDC + c4) = tpv[i];
-            }
-#pragma unroll
-            for (int i = 0; i < NDO; ++i) {
-                const int e = tid + i * NT, r = e / (DVS / 4), c4 = (e % (DVS / 4)) * 4;
-                if (e < C * DVS / 4) *reinterpret_cast<f32x4*>(sDO + r * LDV + c4) = t0 + r < T ? dov[i] : zero4();
-            }
-        }
-        if (n > 0) prefetch_tp(n - 1);
-        lds_barrier();
-        // element phase, pass 2: decayed operands (q.Gamma and b.k.Gamma stay in registers until
-        // their place is free)
-        float qg[L], kg[L];
-        {
-            float off = 0.f, tot = 0.f, after = 0.f;
-#pragma unroll
-            for (int j = 0; j < TB; ++j) {
-                const float vj = sTOT[j * DK + ec];
-                tot += vj;
-                if (j < etb) off += vj;
-                if (j > etb) after += vj;
-            }
-            const float run = sTOT[etb * DK + ec];
-            if (etb == 0) sGC[ec] = exp_any(tot);
-#pragma unroll
-            for (int m = 0; m < L; ++m) {
-                const int i = etb * L + m, t = t0 + i;
-                float qv = 0.f, kv = 0.f, bv = 0.f;
-                if (t < T) {
-                    qv = to_f32(in.q[m]);
-                    kv = to_f32(in.k[m]);
-                    bv = to_f32(in.b[m]);
-                }
-                const float Gi = x[m] + off;
-                const float ga = exp_any(Gi);
-                qg[m] = qv * ga;
-                kg[m] = bv * kv * ga;
-                sKR[i * LDF + ec] = kv * exp_any((run - x[m]) + after);
-            }
-        }
-        lds_barrier();
-        // dU = P^T dO + KR dS'   (tile: token rows jt, value columns ct)
-        for (int u = wave; u < 4 * NCT; u += 8) {
-            const int jt = u % 4, ct = u / 4;
-            f32x4 acc = zero4();
-            mm_tail64(acc, [&](int m, int kk) { return sP[kk * LDC + jt * 16 + m]; },
-                      [&](int kk, int nn) { return sDO[kk * LDV + ct * 16 + nn]; }, jt, l16, g4);
-            mm_split<4, DK>(acc, [&](int m, int kk) { return sKR[(jt * 16 + m) * LDF + kk]; },
-                            [&](int kk, int nn) { return sDS[kk * LDV + ct * 16 + nn]; }, l16, g4);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sDU[(jt * 16 + g4 * 4 + r) * LDV + ct * 16 + l16] = acc[r];
-        }
-        lds_barrier();
-        // dR = T^T dU
-        for (int u = wave; u < 4 * NCT; u += 8) {
-            const int it = u % 4, ct = u / 4;
-            f32x4 acc = zero4();
-            mm_tail64(acc, [&](int m, int kk) { return sT[kk * LDC + it * 16 + m]; },
-                      [&](int kk, int nn) { return sDU[kk * LDV + ct * 16 + nn]; }, it, l16, g4);
+            const f32x4 dr = acc[0] + acc[1];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int i = it * 16 + g4 * 4 + r, t = t0 + i;
-                sDR[i * LDV + ct * 16 + l16] = acc[r];
-                if (t < T) dr_out[base_v + (int64_t)t * rv + col0 + ct * 16 + l16] = acc[r];
+                const int i = dri * 16 + g4 * 4 + r, t = t0 + i;
+                if (t < T) dr_out[base_v + (int64_t)t * rv + col0 + ct * 16 + l16] = dr[r];
             }
         }
-        lds_barrier();
-#pragma unroll
-        for (int m = 0; m < L; ++m) {
-            const int i = etb * L + m;
-            sQG[i * LDF + ec] = qg[m];
-            sKG[i * LDF + ec] = kg[m];
-        }
-        lds_barrier();
-        // the next chunk's key-side inputs: issued here, their registers are live only across
-        // this phase (earlier, they force spills, and a spill reload would wait behind them)
-        if (n > 0) prefetch_key(n - 1);
-        // dS = Gamma_C dS' + QG^T dO - KG^T dR
-#pragma unroll
-        for (int s = 0; s < SPW; ++s) {
-            const int u = wave + 8 * s;
-            if (u < NST) {
-                const int st = u % KT, ct = u / KT;
-                f32x4 acc2[2] = {zero4(), zero4()};
-                mm_n<2, C>(acc2, [&](int t, int m, int kk) { return (t ? sKG : sQG)[kk * LDF + st * 16 + m]; },
-                           [&](int t, int kk, int nn) { return (t ? sDR : sDO)[kk * LDV + ct * 16 + nn]; }, l16, g4);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) dS[s][r] = dS[s][r] * sGC[st * 16 + g4 * 4 + r] + acc2[0][r] - acc2[1][r];
-            }
-        }
-        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);  // the reload after the last use: same registers
+        pre_t(max(n - 1, 0));
     }
     if (d_initial) {
+        float* dst = d_initial + ((int64_t)bh * DK + st * 16 + g4 * 4) * DV + col0 + ct * 16 + l16;
 #pragma unroll
-        for (int s = 0; s < SPW; ++s) {
-            const int u = wave + 8 * s;
-            if (u < NST) {
-                const int st = u % KT, ct = u / KT;
-                float* dst = d_initial + ((int64_t)bh * DK + st * 16 + grp4 * 4) * DV + col0 + ct * 16 + lane16;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) dst[(int64_t)r * DV] = dS[s][r];
-            }
-        }
+        for (int r = 0; r < 4; ++r) dst[(int64_t)r * DV] = dS[r];
     }
 }
 
@@ -1186,13 +1281,6 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
     }
 }
 
-template <typename In, int D, int DVS>
-hipError_t launch_state(const BwdArgs& a, int nslices) {
-    hipLaunchKernelGGL((bwd_state_kernel<In, D, D, DVS>), dim3((unsigned)(a.B * a.H * nslices)), dim3(NT), 0,
-                       (hipStream_t)a.stream, (const In*)a.q, (const In*)a.k, a.log_alpha, (const In*)a.b,
-                       a.d_o, a.d_final_state, a.tp, a.ds_ckpt, a.dr, a.g_s0, (int)a.T, (int)a.H, nslices);
-    return hipGetLastError();
-}
 
 template <typename In, int D>
 hipError_t launch_grad(const BwdArgs& a) {
@@ -1204,30 +1292,25 @@ hipError_t launch_grad(const BwdArgs& a) {
     return hipGetLastError();
 }
 
-template <typename In, int D, int DVS>
-hipError_t launch_fwd(const BwdArgs& a, int nslices) {
-    hipLaunchKernelGGL((bwd_fwd_kernel<In, D, D, DVS>), dim3((unsigned)(a.B * a.H * nslices)), dim3(NT), 0,
-                       (hipStream_t)a.stream, (const In*)a.q, (const In*)a.k, (const In*)a.v, a.log_alpha,
-                       (const In*)a.b, (const In*)a.w, a.initial_state, a.s_ckpt, a.u, a.tp, (int)a.T, (int)a.H,
-                       nslices);
-    return hipGetLastError();
-}
-
 template <typename In, int D>
 hipError_t launch_bwd_typed(const BwdArgs& a) {
-    // forward re-run: at most 32 value columns per workgroup at d = 128 (LDS)
-    hipError_t e;
-    const int64_t bh = a.B * a.H;
-    if (D == 64 && bh >= a.cus) e = launch_fwd<In, D, (D == 64 ? 64 : 32)>(a, D / (D == 64 ? 64 : 32));
-    else if (bh * (D / 32) >= a.cus) e = launch_fwd<In, D, 32>(a, D / 32);
-    else e = launch_fwd<In, D, 16>(a, D / 16);
+    const int64_t bh = a.B * a.H, nch = (a.T + C - 1) / C;
+    // kernel 0: runs of consecutive chunks, about one workgroup per compute unit
+    const int64_t cus = a.cus > 0 ? a.cus : 1;
+    const int64_t nper = (bh * nch + cus - 1) / cus;
+    const int64_t ngrp = (nch + nper - 1) / nper;
+    hipLaunchKernelGGL((bwd_local_kernel<In, D, D>), dim3((unsigned)(bh * ngrp)), dim3(NT), 0, (hipStream_t)a.stream,
+                       (const In*)a.q, (const In*)a.k, (const In*)a.v, a.log_alpha, (const In*)a.b, (const In*)a.w,
+                       a.loc, (int)a.T, (int)a.H, (int)nper);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // reverse pass: the widest value slice (at most 64 columns) that still gives at least one
-    // workgroup per compute unit, else 16 columns
-    if (bh * (D / 64) >= a.cus) e = launch_state<In, D, 64>(a, D / 64);
-    else if (bh * (D / 32) >= a.cus) e = launch_state<In, D, 32>(a, D / 32);
-    else e = launch_state<In, D, 16>(a, D / 16);
-    if (e != hipSuccess) return e;
+    const unsigned nser = (unsigned)(bh * SerCfg<D, D>::NSL);
+    hipLaunchKernelGGL((bwd_fwd_kernel<D, D>), dim3(nser), dim3(NT), 0, (hipStream_t)a.stream, a.loc,
+                       a.initial_state, a.s_ckpt, a.u, (int)a.T, (int)a.H, (int)bh);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_state_kernel<D, D>), dim3(nser), dim3(NT), 0, (hipStream_t)a.stream, a.loc, a.d_o,
+                       a.d_final_state, a.ds_ckpt, a.dr, a.g_s0, (int)a.T, (int)a.H, (int)bh);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     return launch_grad<In, D>(a);
 }
 

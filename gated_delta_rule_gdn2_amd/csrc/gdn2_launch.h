@@ -40,6 +40,12 @@ struct DecodeArgs {
     void* stream;
 };
 
+// Floats of the backward's per-chunk record (64-token chunks): T and P [64][64], W, KR and QG
+// [64][dk], U0 [64][dv], Gamma_C [dk], rounded up to 256 bytes.
+constexpr int64_t bwd_rec_floats(int64_t dk, int64_t dv) {
+    return (2 * 64 * 64 + 3 * 64 * dk + 64 * dv + dk + 63) / 64 * 64;
+}
+
 // Backward pass (vector-Jacobian product) of the chunk forward, fixed-length sequences.
 struct BwdArgs {
     const void* q;
@@ -60,12 +66,13 @@ struct BwdArgs {
     float* g_w;
     float* g_s0;
     // workspace (fp32): states entering every chunk and dS' of every chunk [B,H,NC,dk,dv],
-    // U and dR [B,T,H,dv], T and P of every chunk [B,H,NC,2,64,64]
+    // U and dR [B,T,H,dv], one record of chunk-local quantities per chunk [B,H,NC,
+    // bwd_rec_floats(dk, dv)]
     float* s_ckpt;
     float* ds_ckpt;
     float* u;
     float* dr;
-    float* tp;
+    float* loc;
     int64_t B, T, H, dk, dv;
     bool dtype_bf16;
     void* stream;
