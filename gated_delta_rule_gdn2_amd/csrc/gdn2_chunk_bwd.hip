@@ -548,21 +548,23 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
 
 // ---------------------------------------------------------------------------------------
 // Kernels 1 and 2 walk the chunks of one (sequence, head, slice of value columns) in order.
-// Every wave owns one 16 x 16 tile of the slice's state (or state gradient) in MFMA
-// accumulators: key rows 16 st .. 16 st + 15 (st = wave mod KT), value columns 16 ct ..
-// (ct = wave / KT); so a slice is 16 * 8 / KT columns wide.  A product over the key axis
-// with the state as right operand runs as eight partial products, one per wave over its own
-// 16 rows (the accumulator layout is the operand layout), summed in LDS.
+// The slice's state (or state gradient) lives in MFMA accumulators as 16 x 16 tiles: wave w
+// holds key rows 16 st .. 16 st + 15 (st = w mod KT) of SPW consecutive column tiles from
+// cb = SPW (w / KT).  A product over the key axis with the state as right operand runs as
+// eight partial products, one per wave over its own 16 rows (the accumulator layout is the
+// operand layout), summed in LDS.  Two tiles per wave at dk = 128 (32-column slices): each
+// record entry a wave loads serves both, and one workgroup per compute unit suffices.
 // ---------------------------------------------------------------------------------------
 template <int DK, int DV>
 struct SerCfg {
     static constexpr int KT = DK / 16;
-    static constexpr int NCT = 8 / KT;       // column tiles of a slice
-    static constexpr int DVS = 16 * NCT;     // value columns of a slice
-    static constexpr int NSL = DV / DVS;     // slices
-    static constexpr int OPT = C * DVS / NT; // summed outputs per thread (consecutive columns)
-    static constexpr int TPR = DVS / OPT;    // threads per row of the sums
-    static_assert(KT * NCT == 8 && DV % DVS == 0 && (OPT == 2 || OPT == 4), "shape");
+    static constexpr int SPW = KT == 8 ? 2 : 1;  // column tiles per wave
+    static constexpr int NCT = 8 / KT * SPW;     // column tiles of a slice
+    static constexpr int DVS = 16 * NCT;         // value columns of a slice
+    static constexpr int NSL = DV / DVS;         // slices
+    static constexpr int OPT = C * DVS / NT;     // summed outputs per thread (consecutive columns)
+    static constexpr int TPR = DVS / OPT;        // threads per row of the sums
+    static_assert(KT * NCT == 8 * SPW && DV % DVS == 0 && (OPT == 2 || OPT == 4), "shape");
 };
 
 template <int N>
@@ -590,11 +592,6 @@ __device__ __forceinline__ void store_n(float* p, const float (&d)[N]) {
 
 // Kernel 1: the forward re-run, U = U0 - W S and S <- Gamma_C.S + KR^T U per chunk; stores
 // the state entering every chunk and U
-template <int OPT>
-struct FwdIn {  // one chunk's record entries for this thread
-    f32x4 Wv[4], GCv;
-    float KRv[16], U0v[OPT];
-};
 template <int DK, int DV>
 __global__ __launch_bounds__(NT) void bwd_fwd_kernel(const float* __restrict__ loc,
                                                      const float* __restrict__ initial_state,
@@ -602,8 +599,8 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(const float* __restrict__ l
                                                      int T, int H, int BH) {
     using SC = SerCfg<DK, DV>;
     using R = Rec<DK, DV>;
-    constexpr int KT = SC::KT, DVS = SC::DVS, OPT = SC::OPT, TPR = SC::TPR;
-    __shared__ __attribute__((aligned(16))) float sPart[8 * C * 16];
+    constexpr int KT = SC::KT, SPW = SC::SPW, DVS = SC::DVS, OPT = SC::OPT, TPR = SC::TPR;
+    __shared__ __attribute__((aligned(16))) float sPart[8 * SPW * C * 16];
     __shared__ __attribute__((aligned(16))) float sU[C * DVS];
 
     const int tid = threadIdx.x;
@@ -614,110 +611,121 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(const float* __restrict__ l
     const int bh = blockIdx.x % BH, slice = blockIdx.x / BH;
     const int bi = bh / H, h = bh % H, col0 = slice * DVS;
     const int nch = (T + C - 1) / C;
-    const int st = wave % KT, ct = wave / KT;
+    const int st = wave % KT, cb = (wave / KT) * SPW;
     const int64_t rv = (int64_t)H * DV;
     const int64_t base_v = ((int64_t)bi * T * H + h) * DV;
     const int ri = tid / TPR, rc = (tid % TPR) * OPT;  // summed outputs: row ri, columns rc..
     const int rct = rc / 16, rcc = rc % 16;
 
-    f32x4 S = zero4();
-    if (initial_state) {
-        const float* src = initial_state + ((int64_t)bh * DK + st * 16 + g4 * 4) * DV + col0 + ct * 16 + l16;
+    f32x4 S[SPW];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S[r] = src[(int64_t)r * DV];
+    for (int c = 0; c < SPW; ++c) {
+        S[c] = zero4();
+        if (initial_state) {
+            const float* src = initial_state + ((int64_t)bh * DK + st * 16 + g4 * 4) * DV + col0 + (cb + c) * 16 + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) S[c][r] = src[(int64_t)r * DV];
+        }
     }
-    // record entries are loaded two chunks ahead, into the set just consumed, each part right
-    // after its last use
+    // record entries are loaded one chunk ahead, each part right after its last use
+    f32x4 Wv[4], GCv;
+    float KRv[16], U0v[OPT];
     auto rec_of = [&](int nn) { return loc + ((int64_t)bh * nch + nn) * R::SIZE; };
-    auto pre_w = [&](FwdIn<OPT>& d, int nn) {
+    auto pre_w = [&](int nn) {
         const float* rec = rec_of(nn);
 #pragma unroll
         for (int it = 0; it < 4; ++it)
-            d.Wv[it] = *reinterpret_cast<const f32x4*>(rec + R::OW + (it * 16 + l16) * DK + st * 16 + g4 * 4);
+            Wv[it] = *reinterpret_cast<const f32x4*>(rec + R::OW + (it * 16 + l16) * DK + st * 16 + g4 * 4);
     };
-    auto pre_u0 = [&](FwdIn<OPT>& d, int nn) { load_n<OPT>(d.U0v, rec_of(nn) + R::OU0 + ri * DV + col0 + rc); };
-    auto pre_kr = [&](FwdIn<OPT>& d, int nn) {
+    auto pre_u0 = [&](int nn) { load_n<OPT>(U0v, rec_of(nn) + R::OU0 + ri * DV + col0 + rc); };
+    auto pre_kr = [&](int nn) {
         const float* rec = rec_of(nn);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) d.KRv[j] = rec[R::OKR + (4 * j + g4) * DK + st * 16 + l16];
-        d.GCv = *reinterpret_cast<const f32x4*>(rec + R::OGC + st * 16 + g4 * 4);
+        for (int j = 0; j < 16; ++j) KRv[j] = rec[R::OKR + (4 * j + g4) * DK + st * 16 + l16];
+        GCv = *reinterpret_cast<const f32x4*>(rec + R::OGC + st * 16 + g4 * 4);
     };
-    // the prefetches are issued on every path (the last chunks load the final record again): a
+    pre_w(0);
+    pre_u0(0);
+    pre_kr(0);
+    // The prefetches are issued on every path (the last chunk loads its own record again): a
     // load skipped on some path makes the compiler's wait before each use cover every memory
-    // operation still in flight
-    auto step = [&](FwdIn<OPT>& d, int n) {
-        const int t0 = n * C;
-        const int nn = min(n + 2, nch - 1);
+    // operation still in flight.  A scheduling fence before each keeps the reload after the
+    // last use, in the same registers.
+    for (int n = 0; n < nch; ++n) {
+        const int t0 = n * C, nn = min(n + 1, nch - 1);
         // checkpoint of the state entering the chunk
-        {
-            float* dst = s_ckpt + (((int64_t)bh * nch + n) * DK + st * 16 + g4 * 4) * DV + col0 + ct * 16 + l16;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(int64_t)r * DV] = S[r];
+        for (int c = 0; c < SPW; ++c) {
+            float* dst = s_ckpt + (((int64_t)bh * nch + n) * DK + st * 16 + g4 * 4) * DV + col0 + (cb + c) * 16 + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[(int64_t)r * DV] = S[c][r];
         }
         // this wave's part of W S
         {
-            f32x4 acc[4];
+            f32x4 acc[SPW][4];
 #pragma unroll
-            for (int it = 0; it < 4; ++it) acc[it] = zero4();
+            for (int c = 0; c < SPW; ++c)
+#pragma unroll
+                for (int it = 0; it < 4; ++it) acc[c][it] = zero4();
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int it = 0; it < 4; ++it) acc[it] = mfma4(acc[it], d.Wv[it][j], S[j]);
-            __builtin_amdgcn_sched_barrier(0);  // the reload after the last use: same registers
-            pre_w(d, nn);
+                for (int c = 0; c < SPW; ++c)
 #pragma unroll
-            for (int it = 0; it < 4; ++it)
+                    for (int it = 0; it < 4; ++it) acc[c][it] = mfma4(acc[c][it], Wv[it][j], S[c][j]);
+            __builtin_amdgcn_sched_barrier(0);
+            pre_w(nn);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sPart[(wave * C + it * 16 + g4 * 4 + r) * 16 + l16] = acc[it][r];
+            for (int c = 0; c < SPW; ++c)
+#pragma unroll
+                for (int it = 0; it < 4; ++it)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        sPart[((wave * SPW + c) * C + it * 16 + g4 * 4 + r) * 16 + l16] = acc[c][it][r];
         }
         lds_barrier();
-        // U = U0 - W S
+        // U = U0 - W S: the parts of column tile rct sit with the waves st' + KT (rct / SPW)
         {
             float u[OPT];
 #pragma unroll
-            for (int o = 0; o < OPT; ++o) u[o] = d.U0v[o];
+            for (int o = 0; o < OPT; ++o) u[o] = U0v[o];
 #pragma unroll
             for (int s2 = 0; s2 < KT; ++s2) {
+                const int w2 = s2 + KT * (rct / SPW);
                 float p[OPT];
-                load_n<OPT>(p, sPart + ((rct * KT + s2) * C + ri) * 16 + rcc);
+                load_n<OPT>(p, sPart + ((w2 * SPW + rct % SPW) * C + ri) * 16 + rcc);
 #pragma unroll
                 for (int o = 0; o < OPT; ++o) u[o] -= p[o];
             }
             store_n<OPT>(sU + ri * DVS + rc, u);
             if (t0 + ri < T) store_n<OPT>(u_out + base_v + (int64_t)(t0 + ri) * rv + col0 + rc, u);
         }
-        __builtin_amdgcn_sched_barrier(0);  // the reload after the last use: same registers
-        pre_u0(d, nn);
+        __builtin_amdgcn_sched_barrier(0);
+        pre_u0(nn);
         lds_barrier();
         // S <- Gamma_C.S + KR^T U
         {
-            f32x4 a2[2];
+            f32x4 a2[SPW][2];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) a2[0][r] = S[r] * d.GCv[r];
-            a2[1] = zero4();
+            for (int c = 0; c < SPW; ++c) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) a2[c][0][r] = S[c][r] * GCv[r];
+                a2[c][1] = zero4();
+            }
 #pragma unroll
             for (int j = 0; j < 16; ++j)
-                a2[j & 1] = mfma4(a2[j & 1], d.KRv[j], sU[(4 * j + g4) * DVS + ct * 16 + l16]);
-            S = a2[0] + a2[1];
-            pin(S);
+#pragma unroll
+                for (int c = 0; c < SPW; ++c)
+                    a2[c][j & 1] = mfma4(a2[c][j & 1], KRv[j], sU[(4 * j + g4) * DVS + (cb + c) * 16 + l16]);
+#pragma unroll
+            for (int c = 0; c < SPW; ++c) {
+                S[c] = a2[c][0] + a2[c][1];
+                pin(S[c]);
+            }
         }
-        __builtin_amdgcn_sched_barrier(0);  // the reload after the last use: same registers
-        pre_kr(d, nn);
-    };
-    FwdIn<OPT> in0, in1;
-    pre_w(in0, 0);
-    pre_u0(in0, 0);
-    pre_kr(in0, 0);
-    pre_w(in1, min(1, nch - 1));
-    pre_u0(in1, min(1, nch - 1));
-    pre_kr(in1, min(1, nch - 1));
-    // pairs of chunks, every path through the loop body the same (see above)
-    int n = 0;
-    for (; n + 1 < nch; n += 2) {
-        step(in0, n);
-        step(in1, n + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        pre_kr(nn);
     }
-    if (n < nch) step(in0, n);
 }
 
 // Kernel 2: the chunks in reverse order, dU = P^T dO + KR dS', dS = Gamma_C.dS' + QG^T dO -
@@ -730,10 +738,10 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__
                                                        float* __restrict__ d_initial, int T, int H, int BH) {
     using SC = SerCfg<DK, DV>;
     using R = Rec<DK, DV>;
-    constexpr int KT = SC::KT, DVS = SC::DVS, OPT = SC::OPT, TPR = SC::TPR;
+    constexpr int KT = SC::KT, SPW = SC::SPW, DVS = SC::DVS, OPT = SC::OPT, TPR = SC::TPR;
     constexpr int JW = C / KT;  // tokens of P^T dO in this wave's part
     constexpr int JS = JW / 4;  // their MFMA steps
-    __shared__ __attribute__((aligned(16))) float sPart[8 * C * 16];
+    __shared__ __attribute__((aligned(16))) float sPart[8 * SPW * C * 16];
     __shared__ __attribute__((aligned(16))) float sDU[C * DVS];
     __shared__ __attribute__((aligned(16))) float sDO[2][C * DVS];
 
@@ -743,23 +751,27 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__
     const int bh = blockIdx.x % BH, slice = blockIdx.x / BH;
     const int bi = bh / H, h = bh % H, col0 = slice * DVS;
     const int nch = (T + C - 1) / C;
-    const int st = wave % KT, ct = wave / KT;
+    const int st = wave % KT, cb = (wave / KT) * SPW;
     const int64_t rv = (int64_t)H * DV;
     const int64_t base_v = ((int64_t)bi * T * H + h) * DV;
     const int ri = tid / TPR, rc = (tid % TPR) * OPT;
     const int rct = rc / 16, rcc = rc % 16;
-    // dR tile of this wave: row tile dri (waves with st < 4), column tile ct
+    // dR tiles of this wave: row tile dri (waves with st < 4), its column tiles
     const bool has_dr = st < 4;
     const int dri = st & 3;
 
-    f32x4 dS = zero4();
-    if (d_final) {
-        const float* src = d_final + ((int64_t)bh * DK + st * 16 + g4 * 4) * DV + col0 + ct * 16 + l16;
+    f32x4 dS[SPW];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dS[r] = src[(int64_t)r * DV];
+    for (int c = 0; c < SPW; ++c) {
+        dS[c] = zero4();
+        if (d_final) {
+            const float* src = d_final + ((int64_t)bh * DK + st * 16 + g4 * 4) * DV + col0 + (cb + c) * 16 + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dS[c][r] = src[(int64_t)r * DV];
+        }
     }
     f32x4 KRv[4], GCv;
-    float Pv[4][JS], dOp[JS], dOs[OPT], QGv[16], Wt[16], Tv[16];
+    float Pv[4][JS], dOp[SPW][JS], dOs[OPT], QGv[16], Wt[16], Tv[16];
     auto rec_of = [&](int nn) { return loc + ((int64_t)bh * nch + nn) * R::SIZE; };
     auto do_row = [&](int t) { return d_o + base_v + (int64_t)min(t, T - 1) * rv + col0; };
     auto pre_du = [&](int nn) {  // operands of the dU parts
@@ -772,7 +784,9 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__
             const int j = st * JW + 4 * s + g4;
 #pragma unroll
             for (int it = 0; it < 4; ++it) Pv[it][s] = rec[R::OP + j * C + it * 16 + l16];
-            dOp[s] = nn * C + j < T ? do_row(nn * C + j)[ct * 16 + l16] : 0.f;
+#pragma unroll
+            for (int c = 0; c < SPW; ++c)
+                dOp[c][s] = nn * C + j < T ? do_row(nn * C + j)[(cb + c) * 16 + l16] : 0.f;
         }
     };
     auto pre_do = [&](int nn) {  // the dO slice for LDS
@@ -805,54 +819,64 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__
     pre_do(nch - 1);
     pre_ds(nch - 1);
     pre_t(nch - 1);
-    // the prefetches are issued on every path (chunk 0 loads its own record again): a load
-    // skipped on some path makes the compiler's wait before each use cover every memory
-    // operation still in flight
+    // The prefetches are issued on every path (chunk 0 loads its own record again), each after
+    // a scheduling fence that keeps it behind the last use (see kernel 1).
     for (int n = nch - 1; n >= 0; --n) {
-        const int t0 = n * C;
+        const int t0 = n * C, nn = max(n - 1, 0);
         float* sDOn = sDO[n & 1];
         // dS' of this chunk, checkpoint for kernel 3
-        {
-            float* dst = ds_ckpt + (((int64_t)bh * nch + n) * DK + st * 16 + g4 * 4) * DV + col0 + ct * 16 + l16;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(int64_t)r * DV] = dS[r];
+        for (int c = 0; c < SPW; ++c) {
+            float* dst = ds_ckpt + (((int64_t)bh * nch + n) * DK + st * 16 + g4 * 4) * DV + col0 + (cb + c) * 16 + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[(int64_t)r * DV] = dS[c][r];
         }
         store_n<OPT>(sDOn + ri * DVS + rc, dOs);
-        __builtin_amdgcn_sched_barrier(0);  // the reload after the last use: same registers
-        pre_do(max(n - 1, 0));
+        __builtin_amdgcn_sched_barrier(0);
+        pre_do(nn);
         // this wave's parts of KR dS' (its 16 key rows) and of P^T dO (its JW tokens)
         {
-            f32x4 acc[4];
+            f32x4 acc[SPW][4];
 #pragma unroll
-            for (int it = 0; it < 4; ++it) acc[it] = zero4();
+            for (int c = 0; c < SPW; ++c)
+#pragma unroll
+                for (int it = 0; it < 4; ++it) acc[c][it] = zero4();
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int it = 0; it < 4; ++it) acc[it] = mfma4(acc[it], KRv[it][j], dS[j]);
+                for (int c = 0; c < SPW; ++c)
+#pragma unroll
+                    for (int it = 0; it < 4; ++it) acc[c][it] = mfma4(acc[c][it], KRv[it][j], dS[c][j]);
 #pragma unroll
             for (int s = 0; s < JS; ++s) {
                 const int jb = (st * JW + 4 * s) / 16;  // token block: P[j][i] = 0 for row tiles past it
 #pragma unroll
-                for (int it = 0; it < 4; ++it)
-                    if (it <= jb) acc[it] = mfma4(acc[it], Pv[it][s], dOp[s]);
+                for (int c = 0; c < SPW; ++c)
+#pragma unroll
+                    for (int it = 0; it < 4; ++it)
+                        if (it <= jb) acc[c][it] = mfma4(acc[c][it], Pv[it][s], dOp[c][s]);
             }
-            __builtin_amdgcn_sched_barrier(0);  // the reload after the last use: same registers
-            pre_du(max(n - 1, 0));
+            __builtin_amdgcn_sched_barrier(0);
+            pre_du(nn);
 #pragma unroll
-            for (int it = 0; it < 4; ++it)
+            for (int c = 0; c < SPW; ++c)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sPart[(wave * C + it * 16 + g4 * 4 + r) * 16 + l16] = acc[it][r];
+                for (int it = 0; it < 4; ++it)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        sPart[((wave * SPW + c) * C + it * 16 + g4 * 4 + r) * 16 + l16] = acc[c][it][r];
         }
         lds_barrier();
-        // dU = sum of the parts of this column tile
+        // dU = sum of the parts of column tile rct
         {
             float u[OPT];
 #pragma unroll
             for (int o = 0; o < OPT; ++o) u[o] = 0.f;
 #pragma unroll
             for (int s2 = 0; s2 < KT; ++s2) {
+                const int w2 = s2 + KT * (rct / SPW);
                 float p[OPT];
-                load_n<OPT>(p, sPart + ((rct * KT + s2) * C + ri) * 16 + rcc);
+                load_n<OPT>(p, sPart + ((w2 * SPW + rct % SPW) * C + ri) * 16 + rcc);
 #pragma unroll
                 for (int o = 0; o < OPT; ++o) u[o] += p[o];
             }
@@ -861,43 +885,61 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__
         lds_barrier();
         // dS <- Gamma_C.dS' + QG^T dO - W^T dU
         {
-            f32x4 a2[2] = {zero4(), zero4()};
+            f32x4 a2[SPW][2];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int o = (4 * j + g4) * DVS + ct * 16 + l16;
-                a2[0] = mfma4(a2[0], QGv[j], sDOn[o]);
-                a2[1] = mfma4(a2[1], Wt[j], sDU[o]);
+            for (int c = 0; c < SPW; ++c) a2[c][0] = a2[c][1] = zero4();
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+#pragma unroll
+                for (int c = 0; c < SPW; ++c) {
+                    const int o = (4 * j + g4) * DVS + (cb + c) * 16 + l16;
+                    a2[c][0] = mfma4(a2[c][0], QGv[j], sDOn[o]);
+                    a2[c][1] = mfma4(a2[c][1], Wt[j], sDU[o]);
+                }
+#pragma unroll
+            for (int c = 0; c < SPW; ++c) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dS[c][r] = dS[c][r] * GCv[r] + a2[c][0][r] - a2[c][1][r];
+                pin(dS[c]);
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dS[r] = dS[r] * GCv[r] + a2[0][r] - a2[1][r];
-            pin(dS);
         }
-        __builtin_amdgcn_sched_barrier(0);  // the reload after the last use: same registers
-        pre_ds(max(n - 1, 0));
+        __builtin_amdgcn_sched_barrier(0);
+        pre_ds(nn);
         // dR = T^T dU (row tile dri)
         if (has_dr) {
-            f32x4 acc[2] = {zero4(), zero4()};
+            f32x4 acc[SPW][2];
+#pragma unroll
+            for (int c = 0; c < SPW; ++c) acc[c][0] = acc[c][1] = zero4();
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
                 if (kb >= dri) {
 #pragma unroll
                     for (int s = 0; s < 4; ++s)
-                        acc[s & 1] = mfma4(acc[s & 1], Tv[kb * 4 + s], sDU[(kb * 16 + 4 * s + g4) * DVS + ct * 16 + l16]);
-                }
-            const f32x4 dr = acc[0] + acc[1];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = dri * 16 + g4 * 4 + r, t = t0 + i;
-                if (t < T) dr_out[base_v + (int64_t)t * rv + col0 + ct * 16 + l16] = dr[r];
+                        for (int c = 0; c < SPW; ++c)
+                            acc[c][s & 1] = mfma4(acc[c][s & 1], Tv[kb * 4 + s],
+                                                  sDU[(kb * 16 + 4 * s + g4) * DVS + (cb + c) * 16 + l16]);
+                }
+#pragma unroll
+            for (int c = 0; c < SPW; ++c) {
+                const f32x4 dr = acc[c][0] + acc[c][1];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = dri * 16 + g4 * 4 + r, t = t0 + i;
+                    if (t < T) dr_out[base_v + (int64_t)t * rv + col0 + (cb + c) * 16 + l16] = dr[r];
+                }
             }
         }
-        __builtin_amdgcn_sched_barrier(0);  // the reload after the last use: same registers
-        pre_t(max(n - 1, 0));
+        __builtin_amdgcn_sched_barrier(0);
+        pre_t(nn);
     }
     if (d_initial) {
-        float* dst = d_initial + ((int64_t)bh * DK + st * 16 + g4 * 4) * DV + col0 + ct * 16 + l16;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(int64_t)r * DV] = dS[r];
+        for (int c = 0; c < SPW; ++c) {
+            float* dst = d_initial + ((int64_t)bh * DK + st * 16 + g4 * 4) * DV + col0 + (cb + c) * 16 + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[(int64_t)r * DV] = dS[c][r];
+        }
     }
 }
 
