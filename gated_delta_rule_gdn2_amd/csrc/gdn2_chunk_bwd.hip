@@ -1040,11 +1040,23 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
     const int ct = wave % KT, it0 = wave / KT;
     const int c = ct * 16 + l16;  // the channel of this lane's accumulator column
 
-    if (tid < DK) {
-        sXD[tid] = 0.f;
-        sXR[tid] = 0.f;
-    }
+    if (tid < DK) sXR[tid] = 0.f;
     if (tid == 0) *sFLG = 0;
+
+    constexpr int HV = DV / 2;
+    constexpr int NSH = DK * HV / 4 / NT;  // float4 of a half of S (or dS') per thread
+    static_assert(NSH * 4 * NT == DK * HV, "half split");
+    f32x4 sv[NSH], dsv[NSH];
+    float xd[NSH];  // this thread's part of sum_v dS'[r][v] S[r][v] for its rows
+    auto load_half = [&](f32x4 (&d)[NSH], const float* g, int hh) {
+#pragma unroll
+        for (int i = 0; i < NSH; ++i) {
+            const int e = tid + i * NT, r = e / (HV / 4), c4 = (e % (HV / 4)) * 4;
+            d[i] = *reinterpret_cast<const f32x4*>(g + r * DV + hh * HV + c4);
+        }
+    };
+    load_half(sv, Sg, 0);
+    load_half(dsv, dSg, 0);
 
     // ---- phase 1: dO, dR, U of the chunk; dv = dR.w, dw = dR.v ----
     for (int e = tid; e < C * DV / 4; e += NT) {
@@ -1070,19 +1082,20 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
         *reinterpret_cast<f32x4*>(sU + r * LDV + c4) = u4;
     }
 
-    // ---- phase 2: X1 = dO S^T, X2 = dR S^T, X3 = U dS'^T over two halves of the value axis ----
+    // ---- phase 2: X1 = dO S^T, X2 = dR S^T, X3 = U dS'^T over two halves of the value axis;
+    // each half of S and dS' goes through registers, loaded one step ahead ----
     f32x4 X1[TPW], X2[TPW], X3[TPW];
 #pragma unroll
     for (int j = 0; j < TPW; ++j) X1[j] = X2[j] = X3[j] = zero4();
-    constexpr int HV = DV / 2;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-        __syncthreads();
-        for (int e = tid; e < DK * HV / 4; e += NT) {
-            const int r = e / (HV / 4), c4 = (e % (HV / 4)) * 4;
-            *reinterpret_cast<f32x4*>(sSH + r * LDH + c4) = *reinterpret_cast<const f32x4*>(Sg + r * DV + hh * HV + c4);
+        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < NSH; ++i) {
+            const int e = tid + i * NT, r = e / (HV / 4), c4 = (e % (HV / 4)) * 4;
+            *reinterpret_cast<f32x4*>(sSH + r * LDH + c4) = sv[i];
         }
-        __syncthreads();
+        lds_barrier();
         {
             f32x4 acc[2 * TPW];
 #pragma unroll
@@ -1102,21 +1115,39 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
                 X2[j] = acc[TPW + j];
             }
         }
-        __syncthreads();
-        for (int e = tid; e < DK * HV / 4; e += NT) {
-            const int r = e / (HV / 4), c4 = (e % (HV / 4)) * 4;
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(dSg + r * DV + hh * HV + c4);
-            const f32x4 s4 = *reinterpret_cast<const f32x4*>(Sg + r * DV + hh * HV + c4);
+        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < NSH; ++i) {
+            const int e = tid + i * NT, r = e / (HV / 4), c4 = (e % (HV / 4)) * 4;
+            const f32x4 d4 = dsv[i], s4 = sv[i];
             *reinterpret_cast<f32x4*>(sSH + r * LDH + c4) = d4;
-            atomicAdd(sXD + r, d4[0] * s4[0] + d4[1] * s4[1] + d4[2] * s4[2] + d4[3] * s4[3]);
+            const float p = d4[0] * s4[0] + d4[1] * s4[1] + d4[2] * s4[2] + d4[3] * s4[3];
+            xd[i] = hh == 0 ? p : xd[i] + p;
         }
-        __syncthreads();
+        if (hh == 0) {
+            load_half(sv, Sg, 1);
+            load_half(dsv, dSg, 1);
+        }
+        lds_barrier();
         mm_n<TPW, HV>(X3, [&](int t, int m, int kk) { return sU[((it0 + ITS * t) * 16 + m) * LDV + hh * HV + kk]; },
                       [&](int, int kk, int nn) { return sSH[(ct * 16 + nn) * LDH + kk]; }, l16, g4);
     }
+    // the row sums: the HV / 4 threads of a row are consecutive lanes
+#pragma unroll
+    for (int i = 0; i < NSH; ++i) {
+#pragma unroll
+        for (int o = 1; o < HV / 4; o <<= 1) xd[i] += __shfl_xor(xd[i], o);
+        const int e = tid + i * NT;
+        if (e % (HV / 4) == 0) sXD[e / (HV / 4)] = xd[i];
+    }
 #pragma unroll
     for (int j = 0; j < TPW; ++j) X2[j] = -X2[j];  // -dR S^T
-    __syncthreads();
+    lds_barrier();
+
+    // the key-side inputs of the element phase, in flight during phase 3
+    const int ec = tid % DK, etb = tid / DK;
+    KeyIn<In, L> in;
+    load_key<In, L>(in, q, k, bgate, log_alpha, base_k + ec, rk, t0 + etb * L, T);
 
     // ---- phase 3: dA = -dR U^T (j < i), dP = dO U^T (j <= i); zero above the diagonal ----
     {
@@ -1145,13 +1176,10 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
             }
         }
     }
-    __syncthreads();  // region 1 (dO, dR, U) is free from here on
+    lds_barrier();  // region 1 (dO, dR, U) is free from here on
 
     // element phase: G (chunk-local cumulative log alpha) and the raw q, k, b of the chunk
-    const int ec = tid % DK, etb = tid / DK;
     {
-        KeyIn<In, L> in;
-        load_key<In, L>(in, q, k, bgate, log_alpha, base_k + ec, rk, t0 + etb * L, T);
         float x[L];
         float run = 0.f;
 #pragma unroll
@@ -1160,7 +1188,7 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
             x[m] = run;
         }
         sTOT[etb * DK + ec] = run;
-        __syncthreads();
+        lds_barrier();
         float tot = 0.f, after = 0.f, oh = 0.f, ol = 0.f;
 #pragma unroll
         for (int j = 0; j < TB; ++j) {
@@ -1196,7 +1224,7 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
             sB[i * LDT + ec] = bv;
         }
     }
-    __syncthreads();
+    lds_barrier();
     const bool mild = *sFLG == 0;
 
     // the G_C term of U dS'^T: sum_i k_ic e^{G_C - G_ic} X3_ic
@@ -1280,7 +1308,7 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
             }
         }
     }
-    __syncthreads();  // dA, dP are consumed: region 2 takes dG
+    lds_barrier();  // dA, dP are consumed: region 2 takes dG
 
     // ---- phase 5: dq, dk, db; the per-token decay gradient dG ----
 #pragma unroll
@@ -1301,14 +1329,14 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     // reverse cumulative sum over the chunk, plus the G_C terms
     {
         float run = 0.f;
 #pragma unroll
         for (int m = L - 1; m >= 0; --m) run += sDG[(etb * L + m) * LDF + ec];
         sTOT[etb * DK + ec] = run;
-        __syncthreads();
+        lds_barrier();
         float after = sXR[ec] + sGC[ec] * sXD[ec];
 #pragma unroll
         for (int j = 0; j < TB; ++j)
