@@ -221,6 +221,8 @@ struct LocCfg {
     static constexpr int BYTES = FLG + 16;
     static_assert(BYTES <= 163840, "LDS budget exceeded");
     static_assert(NT % DK == 0 && (KT + VT) % 4 == 0, "shape");
+    static_assert(C * LDC * 4 <= QG - KI, "P does not fit over k / Gamma");
+    static_assert(8 * (KT + VT) / 2 * 256 * 4 <= AT, "the W and U0 staging does not fit");
 };
 
 template <typename In, int DK, int DV>
@@ -241,6 +243,8 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
     In* sRB = reinterpret_cast<In*>(smem + G::RB);
     In* sRQ = reinterpret_cast<In*>(smem + G::RQ);
     float* sWV = reinterpret_cast<float*>(smem + G::WV);
+    float* sPS = reinterpret_cast<float*>(smem + G::KI);  // P, after A and P are formed
+    float* sStage = reinterpret_cast<float*>(smem);       // the record's W and U0 tiles, per wave
     float* sAT = reinterpret_cast<float*>(smem + G::AT);
     float* sTOT = reinterpret_cast<float*>(smem + G::TOT);
     float* sOFH = reinterpret_cast<float*>(smem + G::OFH);
@@ -389,25 +393,33 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
 #pragma unroll
             for (int t = 0; t < 3; ++t) {
                 const int u = wave + 8 * t;
-                if (u >= 20) continue;
+                if (u >= 10) continue;
                 int I, J;
                 blk(u, I, J);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = I * 16 + g4 * 4 + r, j = J * 16 + l16;
-                    if (u < 10) sAT[i * LDC + j] = j < i ? acc[t][r] : 0.f;
-                    else rec[R::OP + i * C + j] = j <= i ? acc[t][r] : 0.f;
+                    sAT[i * LDC + j] = j < i ? acc[t][r] : 0.f;
                 }
             }
-            // P above the diagonal blocks is zero
-            for (int e = tid; e < C * C; e += NT) {
-                const int i = e / C, j = e % C;
-                if (j / 16 > i / 16) rec[R::OP + e] = 0.f;
+            lds_barrier();
+            // P's lower blocks to their tile over k / Gamma (read by every wave until here)
+#pragma unroll
+            for (int t = 0; t < 3; ++t) {
+                const int u = wave + 8 * t;
+                if (u < 10 || u >= 20) continue;
+                int I, J;
+                blk(u, I, J);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sPS[(I * 16 + g4 * 4 + r) * LDC + J * 16 + l16] = acc[t][r];
             }
         } else {
             const int i = tid & 63, jg = tid >> 6;
             const int bI = i / L;
-            for (int j = jg; j < C; j += 8) {
+            float pv[C / 8];
+#pragma unroll
+            for (int m = 0; m < C / 8; ++m) {
+                const int j = jg + 8 * m;
                 float a = 0.f, p = 0.f;
                 if (j <= i) {
                     const int bJ = j / L;
@@ -421,10 +433,12 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
                     }
                 }
                 sAT[i * LDC + j] = j < i ? a : 0.f;
-                rec[R::OP + i * C + j] = p;
+                pv[m] = p;
             }
+            lds_barrier();
+#pragma unroll
+            for (int m = 0; m < C / 8; ++m) sPS[i * LDC + jg + 8 * m] = pv[m];
         }
-        lds_barrier();
         // KG of the other kind of chunk (k and b reloaded: keeping the raw inputs live costs
         // registers everywhere), over the tiles A and P no longer need
         if (!mild) {
@@ -492,9 +506,15 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
             }
             lds_barrier();
         }
-        for (int e = tid; e < C * C; e += NT) {
-            const int i = e / C, j = e % C;
-            rec[R::OT + e] = j <= i ? sAT[i * LDC + j] : 0.f;
+        // T and P to the record, 16-byte rows, zero above the diagonal
+#pragma unroll
+        for (int x = 0; x < 2 * C * C / 4 / NT; ++x) {
+            const int e = tid + x * NT, mat = e / (C * C / 4), i = (e / (C / 4)) % C, j0 = (e % (C / 4)) * 4;
+            f32x4 val = *reinterpret_cast<const f32x4*>((mat ? sPS : sAT) + i * LDC + j0);
+#pragma unroll
+            for (int z = 0; z < 4; ++z)
+                if (j0 + z > i) val[z] = 0.f;
+            *reinterpret_cast<f32x4*>(rec + (mat ? R::OP : R::OT) + i * C + j0) = val;
         }
         // W = T KG and U0 = T (w.v): wave w takes the row tiles p and 3 - p (p = w mod 2) of the
         // column tiles cg, cg + 4, ... (cg = w / 2) of [W | U0]; T is lower triangular, so row
@@ -525,19 +545,30 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
                     }
                 }
             }
+            // to the record in 16-byte rows, through a staging area of this wave's own (once
+            // every wave is done with the operand tiles)
+            lds_barrier();
+            float* stg = sStage + wave * (2 * NCOL * 256);
+#pragma unroll
+            for (int c = 0; c < NCOL; ++c)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    stg[(2 * c) * 256 + (g4 * 4 + r) * 16 + l16] = acc0[c][r];
+                    stg[(2 * c + 1) * 256 + (g4 * 4 + r) * 16 + l16] = acc1[c][r];
+                }
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's own staging writes
+            __builtin_amdgcn_wave_barrier();
+            const int row = lane >> 2, q4 = (lane & 3) * 4;
 #pragma unroll
             for (int c = 0; c < NCOL; ++c) {
                 const int ct = cg + 4 * c;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i0 = p * 16 + g4 * 4 + r, i1 = (3 - p) * 16 + g4 * 4 + r;
-                    if (ct < KT) {
-                        rec[R::OW + i0 * DK + ct * 16 + l16] = acc0[c][r];
-                        rec[R::OW + i1 * DK + ct * 16 + l16] = acc1[c][r];
-                    } else {
-                        rec[R::OU0 + i0 * DV + (ct - KT) * 16 + l16] = acc0[c][r];
-                        rec[R::OU0 + i1 * DV + (ct - KT) * 16 + l16] = acc1[c][r];
-                    }
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const int I = h2 ? 3 - p : p;
+                    const f32x4 val = *reinterpret_cast<const f32x4*>(stg + (2 * c + h2) * 256 + row * 16 + q4);
+                    float* dst = ct < KT ? rec + R::OW + (I * 16 + row) * DK + ct * 16 + q4
+                                         : rec + R::OU0 + (I * 16 + row) * DV + (ct - KT) * 16 + q4;
+                    *reinterpret_cast<f32x4*>(dst) = val;
                 }
             }
         }
