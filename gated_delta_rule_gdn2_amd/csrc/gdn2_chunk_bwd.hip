@@ -28,18 +28,22 @@
 // sum_i KR_i.(U dS'^T)_i + Gamma_C.diag(dS' S^T).  The gradient of log alpha is the reverse
 // cumulative sum of these over the chunk.
 //
-// Three launches:
+// Four launches:
+//   0. bwd_local_kernel, every chunk independently: the chunk-local quantities in fp32 (A and
+//      P from the inputs, T = (I + A)^{-1}, W = T KG, U0 = T (w.v), KR, QG, Gamma_C), one record
+//      per chunk;
 //   1. bwd_fwd_kernel, one workgroup per (sequence, head, slice of value columns): the forward
-//      re-run in fp32 from the inputs (A, P, T = (I + A)^{-1} formed again), storing the state
-//      entering every chunk, U, and T and P of every chunk;
-//   2. bwd_state_kernel, one workgroup per (sequence, head, slice of value columns): the
-//      chunks in reverse order with dS in MFMA accumulators; stores dS' of every chunk, dR,
-//      and dS of the first chunk (the gradient of the initial state);
+//      re-run from the records, U = U0 - W S and S' = Gamma_C.S + KR^T U, storing the state
+//      entering every chunk and U;
+//   2. bwd_state_kernel, one workgroup per (sequence, head, slice): the chunks in reverse order
+//      with dS in MFMA accumulators, dS = Gamma_C.dS' + QG^T dO - W^T dU (KG^T T^T = W^T);
+//      stores dS' of every chunk, dR, and dS of the first chunk (the gradient of the initial
+//      state);
 //   3. bwd_chunk_kernel, one workgroup per (sequence, head, chunk): every gradient of the
 //      chunk's inputs, independently of the other chunks.
 // Products run on fp32 MFMA (v_mfma_f32_16x16x4_f32) with fp32 accumulation.
 //
-// Decays in kernels 1 and 3: a chunk whose whole-chunk decay stays >= e^-40 on every channel
+// Decays in kernels 0 and 3: a chunk whose whole-chunk decay stays >= e^-40 on every channel
 // pivots all factors at the chunk start (k / Gamma is then finite, and every masked product is
 // one MFMA pass); any other chunk forms its masked sums element by element from
 // e^{G_i - G_j}, which never exceeds 1.
@@ -184,16 +188,48 @@ __device__ __forceinline__ void load_key(KeyIn<In, L>& in, const In* __restrict_
     }
 }
 
+// N consecutive floats (N = 2 or 4) as one access
+template <int N>
+__device__ __forceinline__ void load_n(float (&d)[N], const float* p) {
+    if constexpr (N == 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d[i] = x[i];
+    } else {
+        static_assert(N == 2, "width");
+        const float2 x = *reinterpret_cast<const float2*>(p);
+        d[0] = x.x;
+        d[1] = x.y;
+    }
+}
+template <int N>
+__device__ __forceinline__ void store_n(float* p, const float (&d)[N]) {
+    if constexpr (N == 4) {
+        *reinterpret_cast<f32x4*>(p) = f32x4{d[0], d[1], d[2], d[3]};
+    } else {
+        static_assert(N == 2, "width");
+        *reinterpret_cast<float2*>(p) = make_float2(d[0], d[1]);
+    }
+}
+
 // ---------------------------------------------------------------------------------------
 // Kernel 0: the chunk-local quantities, every chunk independently (a workgroup walks a run of
 // consecutive chunks of one sequence and head, loading the next chunk's inputs one chunk
 // ahead).  Each chunk gets one fp32 record (layout in gdn2_launch.h): T = (I + A)^{-1}, P,
 // W = T KG, KR, QG, U0 = T (w.v) and Gamma_C.
 // ---------------------------------------------------------------------------------------
+// Record layout.  W, KR and U0 row-major ([token][channel]); T, P, QG and second copies of W
+// and KR swizzled for reads of one channel over 16 tokens per lane: entry (token i, channel c)
+// of a 64 x n matrix sits at sw(i, c) = [c / 16][i / 16][i mod 4][c mod 16][(i / 4) mod 4],
+// so that lane (g, n16) of a wave reads the tokens 16 j4 + 4 x + g (x = 0..3) of channel
+// 16 b + n16 as one 16-byte unit, and the 64 lanes' units for one j4 are contiguous.
+__host__ __device__ constexpr int sw(int i, int c) {
+    return ((((c >> 4) * 4 + (i >> 4)) * 4 + (i & 3)) * 16 + (c & 15)) * 4 + ((i >> 2) & 3);
+}
 template <int DK, int DV>
 struct Rec {
-    static constexpr int64_t OT = 0, OP = C * C, OW = 2 * C * C, OKR = OW + C * DK, OQG = OKR + C * DK,
-                             OU0 = OQG + C * DK, OGC = OU0 + C * DV;
+    static constexpr int64_t OT = 0, OP = C * C, OW = 2 * C * C, OWS = OW + C * DK, OKR = OWS + C * DK,
+                             OKRS = OKR + C * DK, OQG = OKRS + C * DK, OU0 = OQG + C * DK, OGC = OU0 + C * DV;
     static constexpr int64_t SIZE = bwd_rec_floats(DK, DV);
     static_assert(OGC + DK <= SIZE && SIZE % 64 == 0, "record layout");
 };
@@ -340,6 +376,7 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
         const bool mild = *sFLG == 0;
         // element phase, pass 2: QG and KR = k.Gamma_C / Gamma (suffix sums) to the record;
         // operand tiles of A and P
+        float qgv[L], krv[L];
 #pragma unroll
         for (int m = 0; m < L; ++m) {
             const int i = etb * L + m, t = t0 + i;
@@ -352,8 +389,9 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
             const float Gi = x[m] + off;
             const float ga = exp_any(Gi);
             const float qg = to_f32(qv) * ga;
-            rec[R::OQG + i * DK + ec] = qg;
-            rec[R::OKR + i * DK + ec] = to_f32(kv) * exp_any((run - x[m]) + after);
+            qgv[m] = qg;
+            krv[m] = to_f32(kv) * exp_any((run - x[m]) + after);
+            rec[R::OKR + i * DK + ec] = krv[m];
             if (mild) {
                 sKG[i * LDF + ec] = to_f32(bv) * to_f32(kv) * ga;
                 sKI[i * LDF + ec] = to_f32(kv) * exp_any(-Gi);
@@ -364,6 +402,18 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
                 sRB[i * LDT + ec] = bv;
                 sRQ[i * LDT + ec] = qv;
             }
+        }
+        // the swizzled copies: this thread's tokens with one residue mod 4 are consecutive there
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float a[L / 4], b[L / 4];
+#pragma unroll
+            for (int u = 0; u < L / 4; ++u) {
+                a[u] = qgv[g + 4 * u];
+                b[u] = krv[g + 4 * u];
+            }
+            store_n<L / 4>(rec + R::OQG + sw(etb * L + g, ec), a);
+            store_n<L / 4>(rec + R::OKRS + sw(etb * L + g, ec), b);
         }
         prefetch(min(n + 1, n1 - 1));  // on every path (see the serial kernels)
         lds_barrier();
@@ -506,15 +556,21 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
             }
             lds_barrier();
         }
-        // T and P to the record, 16-byte rows, zero above the diagonal
+        // T and P to the record, swizzled, zero above the diagonal: 16-byte unit u holds rows
+        // 16 j4 + 4 x + g (x = 0..3) of column 16 b + n16, u = ((4 b + j4) 4 + g) 16 + n16
 #pragma unroll
-        for (int x = 0; x < 2 * C * C / 4 / NT; ++x) {
-            const int e = tid + x * NT, mat = e / (C * C / 4), i = (e / (C / 4)) % C, j0 = (e % (C / 4)) * 4;
-            f32x4 val = *reinterpret_cast<const f32x4*>((mat ? sPS : sAT) + i * LDC + j0);
+        for (int y = 0; y < 2 * C * C / 4 / NT; ++y) {
+            const int e = tid + y * NT, mat = e / (C * C / 4), u = e % (C * C / 4);
+            const int n16 = u & 15, g = (u >> 4) & 3, j4 = (u >> 6) & 3, b = u >> 8;
+            const int c = 16 * b + n16;
+            const float* src = mat ? sPS : sAT;
+            f32x4 val;
 #pragma unroll
-            for (int z = 0; z < 4; ++z)
-                if (j0 + z > i) val[z] = 0.f;
-            *reinterpret_cast<f32x4*>(rec + (mat ? R::OP : R::OT) + i * C + j0) = val;
+            for (int z = 0; z < 4; ++z) {
+                const int i = 16 * j4 + 4 * z + g;
+                val[z] = c <= i ? src[i * LDC + c] : 0.f;
+            }
+            *reinterpret_cast<f32x4*>(rec + (mat ? R::OP : R::OT) + 4 * u) = val;
         }
         // W = T KG and U0 = T (w.v): wave w takes the row tiles p and 3 - p (p = w mod 2) of the
         // column tiles cg, cg + 4, ... (cg = w / 2) of [W | U0]; T is lower triangular, so row
@@ -565,10 +621,17 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2) {
                     const int I = h2 ? 3 - p : p;
-                    const f32x4 val = *reinterpret_cast<const f32x4*>(stg + (2 * c + h2) * 256 + row * 16 + q4);
+                    const float* tile = stg + (2 * c + h2) * 256;
+                    const f32x4 val = *reinterpret_cast<const f32x4*>(tile + row * 16 + q4);
                     float* dst = ct < KT ? rec + R::OW + (I * 16 + row) * DK + ct * 16 + q4
                                          : rec + R::OU0 + (I * 16 + row) * DV + (ct - KT) * 16 + q4;
                     *reinterpret_cast<f32x4*>(dst) = val;
+                    if (ct < KT) {  // W swizzled: rows 4 x + g of column l16, as one 16-byte unit
+                        f32x4 sv4;
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) sv4[x] = tile[(4 * x + g4) * 16 + l16];
+                        *reinterpret_cast<f32x4*>(rec + R::OWS + sw(I * 16 + g4, ct * 16 + l16)) = sv4;
+                    }
                 }
             }
         }
@@ -597,29 +660,6 @@ struct SerCfg {
     static constexpr int TPR = DVS / OPT;        // threads per row of the sums
     static_assert(KT * NCT == 8 * SPW && DV % DVS == 0 && (OPT == 2 || OPT == 4), "shape");
 };
-
-template <int N>
-__device__ __forceinline__ void load_n(float (&d)[N], const float* p) {
-    if constexpr (N == 4) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(p);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) d[i] = x[i];
-    } else {
-        static_assert(N == 2, "width");
-        const float2 x = *reinterpret_cast<const float2*>(p);
-        d[0] = x.x;
-        d[1] = x.y;
-    }
-}
-template <int N>
-__device__ __forceinline__ void store_n(float* p, const float (&d)[N]) {
-    if constexpr (N == 4) {
-        *reinterpret_cast<f32x4*>(p) = f32x4{d[0], d[1], d[2], d[3]};
-    } else {
-        static_assert(N == 2, "width");
-        *reinterpret_cast<float2*>(p) = make_float2(d[0], d[1]);
-    }
-}
 
 // Kernel 1: the forward re-run, U = U0 - W S and S <- Gamma_C.S + KR^T U per chunk; stores
 // the state entering every chunk and U
@@ -672,7 +712,11 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(const float* __restrict__ l
     auto pre_kr = [&](int nn) {
         const float* rec = rec_of(nn);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) KRv[j] = rec[R::OKR + (4 * j + g4) * DK + st * 16 + l16];
+        for (int j4 = 0; j4 < 4; ++j4) {  // KR[4 j + g4][16 st + l16], j = 0..15 (swizzled copy)
+            const f32x4 x = *reinterpret_cast<const f32x4*>(rec + R::OKRS + sw(16 * j4 + g4, st * 16 + l16));
+#pragma unroll
+            for (int z = 0; z < 4; ++z) KRv[4 * j4 + z] = x[z];
+        }
         GCv = *reinterpret_cast<const f32x4*>(rec + R::OGC + st * 16 + g4 * 4);
     };
     pre_w(0);
@@ -810,11 +854,12 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__
 #pragma unroll
         for (int it = 0; it < 4; ++it)
             KRv[it] = *reinterpret_cast<const f32x4*>(rec + R::OKR + (it * 16 + l16) * DK + st * 16 + g4 * 4);
+        // P[st JW + 4 s + g4][16 it + l16], s = 0..JS-1: consecutive in the swizzled copy
+#pragma unroll
+        for (int it = 0; it < 4; ++it) load_n<JS>(Pv[it], rec + R::OP + sw(st * JW + g4, it * 16 + l16));
 #pragma unroll
         for (int s = 0; s < JS; ++s) {
             const int j = st * JW + 4 * s + g4;
-#pragma unroll
-            for (int it = 0; it < 4; ++it) Pv[it][s] = rec[R::OP + j * C + it * 16 + l16];
 #pragma unroll
             for (int c = 0; c < SPW; ++c)
                 dOp[c][s] = nn * C + j < T ? do_row(nn * C + j)[(cb + c) * 16 + l16] : 0.f;
@@ -830,20 +875,26 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__
     auto pre_ds = [&](int nn) {  // operands of the dS update
         const float* rec = rec_of(nn);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            QGv[j] = rec[R::OQG + (4 * j + g4) * DK + st * 16 + l16];
-            Wt[j] = rec[R::OW + (4 * j + g4) * DK + st * 16 + l16];
+        for (int j4 = 0; j4 < 4; ++j4) {  // QG and W at [4 j + g4][16 st + l16] (swizzled copies)
+            const f32x4 a = *reinterpret_cast<const f32x4*>(rec + R::OQG + sw(16 * j4 + g4, st * 16 + l16));
+            const f32x4 b = *reinterpret_cast<const f32x4*>(rec + R::OWS + sw(16 * j4 + g4, st * 16 + l16));
+#pragma unroll
+            for (int z = 0; z < 4; ++z) {
+                QGv[4 * j4 + z] = a[z];
+                Wt[4 * j4 + z] = b[z];
+            }
         }
         GCv = *reinterpret_cast<const f32x4*>(rec + R::OGC + st * 16 + g4 * 4);
     };
     auto pre_t = [&](int nn) {  // T^T operand of the dR tile: T[j][16 dri + m], j >= 16 dri
         const float* rec = rec_of(nn);
-        if (has_dr) {
+        if (has_dr) {  // T[16 kb + 4 s + g4][16 dri + l16] (zero for kb < dri), swizzled copy
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
+            for (int kb = 0; kb < 4; ++kb) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(rec + R::OT + sw(16 * kb + g4, dri * 16 + l16));
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    Tv[kb * 4 + s] = kb >= dri ? rec[R::OT + (kb * 16 + 4 * s + g4) * C + dri * 16 + l16] : 0.f;
+                for (int z = 0; z < 4; ++z) Tv[kb * 4 + z] = x[z];
+            }
         }
     };
     pre_du(nch - 1);

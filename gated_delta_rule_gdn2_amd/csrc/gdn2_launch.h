@@ -40,10 +40,11 @@ struct DecodeArgs {
     void* stream;
 };
 
-// Floats of the backward's per-chunk record (64-token chunks): T and P [64][64], W, KR and QG
-// [64][dk], U0 [64][dv], Gamma_C [dk], rounded up to 256 bytes.
+// Floats of the backward's per-chunk record (64-token chunks): T and P (64 x 64), W and KR
+// (64 x dk, row-major and swizzled), QG (64 x dk, swizzled), U0 (64 x dv), Gamma_C (dk),
+// rounded up to 256 bytes.
 constexpr int64_t bwd_rec_floats(int64_t dk, int64_t dv) {
-    return (2 * 64 * 64 + 3 * 64 * dk + 64 * dv + dk + 63) / 64 * 64;
+    return (2 * 64 * 64 + 5 * 64 * dk + 64 * dv + dk + 63) / 64 * 64;
 }
 
 // Backward pass (vector-Jacobian product) of the chunk forward, fixed-length sequences.

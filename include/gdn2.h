@@ -151,7 +151,7 @@ gdn2_status_t gdn2_decode_step(const void* q, const void* k, const void* v,
  * gdn2_chunk_bwd_workspace_bytes -- bytes of device workspace gdn2_chunk_bwd
  * needs for these sizes (NC = ceil(T / 64)): 4 * (2 B H NC dk dv +
  * 2 B T H dv + B H NC R), each of the five parts rounded up to 256 bytes, where
- * R = 2*64*64 + 3*64*dk + 64*dv + dk rounded up to a multiple of 64 (one record
+ * R = 2*64*64 + 5*64*dk + 64*dv + dk rounded up to a multiple of 64 (one record
  * of chunk-local quantities per chunk).  Returns 0 if the sizes overflow or dk
  * or dv exceeds 2^20.
  */

@@ -184,10 +184,10 @@ def test_varlen_validation(lib):
 
 def test_bwd_workspace_bytes(lib):
     # 4 bytes x (2 B H NC dk dv + 2 B T H dv + B H NC R), parts rounded to 256 bytes, with R the
-    # floats of a chunk record: 2*64*64 + 3*64*dk + 64*dv + dk rounded up to 64
+    # floats of a chunk record: 2*64*64 + 5*64*dk + 64*dv + dk rounded up to 64
     B, T, H, d = 2, 130, 3, 64
     nc = 3
-    rec = (2 * 64 * 64 + 3 * 64 * d + 64 * d + d + 63) // 64 * 64
+    rec = (2 * 64 * 64 + 5 * 64 * d + 64 * d + d + 63) // 64 * 64
     parts = [B * H * nc * d * d * 4] * 2 + [B * T * H * d * 4] * 2 + [B * H * nc * rec * 4]
     assert lib.gdn2_chunk_bwd_workspace_bytes(B, T, H, d, d) == sum((x + 255) // 256 * 256 for x in parts)
     assert gdn2.chunk_bwd_workspace_bytes(B, T, H, d, d) == lib.gdn2_chunk_bwd_workspace_bytes(B, T, H, d, d)
