@@ -102,69 +102,31 @@ __device__ __forceinline__ void two_sum(float a, float b, float& s, float& e) {
     e = (a - (s - bb)) + (b - bb);
 }
 
-// acc += sum_{k in [k0, k1)} A(m, k) B(k, n) over one 16 x 16 tile, k0 and k1 multiples of 16:
-// lane (n = l16, g4) supplies A(l16, k + g4) and B(k + g4, l16) at each step of 4.
-template <class FA, class FB>
-__device__ __forceinline__ void mm(f32x4& acc, FA A, FB B, int k0, int k1, int l16, int g4) {
-    for (int k = k0; k < k1; k += 16) {
-#pragma unroll
-        for (int s = 0; s < 16; s += 4) acc = mfma4(acc, A(l16, k + s + g4), B(k + s + g4, l16));
-    }
-}
-
-// NTILE independent 16 x 16 products over the same contraction length K (compile time), fully
-// unrolled with the steps of all tiles interleaved, so that the MFMA chains of different tiles
-// hide each other's latency: acc[t] += sum_k A(t, m, k) B(t, k, n).  A B operand that does not
-// depend on t is loaded once per step.
+// NTILE independent 16 x 16 products over the same contraction length K (compile time), with
+// the steps of all tiles interleaved, so that the MFMA chains of different tiles hide each
+// other's latency: acc[t] += sum_k A(t, m, k) B(t, k, n).  Within each block of 16 along k,
+// lane group g4 supplies k = k0 + 4 g4 + s at step s (the sum is the same in any order), so a
+// lane's four steps read four consecutive k: with k the contiguous index of both operands in
+// LDS, that is one 16-byte read per operand and block.
 template <int NTILE, int K, class FA, class FB>
 __device__ __forceinline__ void mm_n(f32x4 (&acc)[NTILE], FA A, FB B, int l16, int g4) {
-    // unrolled 16 deep: deeper unrolling lets the compiler hoist more operand loads than the
-    // register file holds
+    // one block of 16 at a time: deeper unrolling lets the compiler hoist more operand loads
+    // than the register file holds
 #pragma unroll 1
     for (int k0 = 0; k0 < K; k0 += 16) {
+        float a[4][NTILE], b[4][NTILE];
 #pragma unroll
-        for (int k = k0; k < k0 + 16; k += 4) {
-            float a[NTILE], b[NTILE];
+        for (int t = 0; t < NTILE; ++t)
 #pragma unroll
-            for (int t = 0; t < NTILE; ++t) {
-                a[t] = A(t, l16, k + g4);
-                b[t] = B(t, k + g4, l16);
+            for (int s = 0; s < 4; ++s) {
+                a[s][t] = A(t, l16, k0 + 4 * g4 + s);
+                b[s][t] = B(t, k0 + 4 * g4 + s, l16);
             }
 #pragma unroll
-            for (int t = 0; t < NTILE; ++t) acc[t] = mfma4(acc[t], a[t], b[t]);
-        }
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int t = 0; t < NTILE; ++t) acc[t] = mfma4(acc[t], a[s][t], b[s][t]);
     }
-}
-
-// acc += the product over [0, K) as NS independent chains over consecutive parts of K, summed
-// at the end (one output tile, its MFMA latency hidden by its own parts)
-template <int NS, int K, class FA, class FB>
-__device__ __forceinline__ void mm_split(f32x4& acc, FA A, FB B, int l16, int g4) {
-    static_assert(K % (4 * NS) == 0, "split");
-    f32x4 part[NS];
-#pragma unroll
-    for (int t = 0; t < NS; ++t) part[t] = zero4();
-    mm_n<NS, K / NS>(part, [&](int t, int m, int kk) { return A(m, t * (K / NS) + kk); },
-                     [&](int t, int kk, int nn) { return B(t * (K / NS) + kk, nn); }, l16, g4);
-#pragma unroll
-    for (int t = 0; t < NS; ++t) acc += part[t];
-}
-
-// acc += the product over the 16-wide blocks kb0 <= kb < 4 of a 64-long contraction (kb0
-// runtime), each block its own chain
-template <class FA, class FB>
-__device__ __forceinline__ void mm_tail64(f32x4& acc, FA A, FB B, int kb0, int l16, int g4) {
-    f32x4 part[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) part[t] = zero4();
-#pragma unroll
-    for (int k = 0; k < 16; k += 4) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-            if (t >= kb0) part[t] = mfma4(part[t], A(l16, t * 16 + k + g4), B(t * 16 + k + g4, l16));
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) acc += part[t];
 }
 
 // This thread's L tokens of key channel c in the element phase, every load issued at once: a
