@@ -129,6 +129,40 @@ __device__ __forceinline__ void mm_n(f32x4 (&acc)[NTILE], FA A, FB B, int l16, i
     }
 }
 
+// bf16 hi/lo operands: x = hi + lo + r with hi = bf16(x), lo = bf16(x - hi) and |r| <= 2^-17 |x|;
+// a product takes hi.hi + hi.lo + lo.hi (the dropped lo.lo is below 2^-16 relative), three
+// v_mfma_f32_16x16x32_bf16 for what costs eight v_mfma_f32_16x16x4_f32 per 32 k in fp32.
+__device__ __forceinline__ void split_hl(const f32x4& x, bf16x4& hi, bf16x4& lo) {
+#pragma unroll
+    for (int z = 0; z < 4; ++z) {
+        hi[z] = (bf16)x[z];
+        lo[z] = (bf16)(x[z] - (float)hi[z]);
+    }
+}
+// As mm_n over hi/lo operand planes, K a multiple of 32: lane group g4 supplies k0 + 8 g4 + e
+// (e = 0..7) of each block of 32; A(t, m, k, plane) and B(t, k, n, plane) point at the 8
+// contiguous bf16 of k .. k + 7 (plane 0 hi, 1 lo).
+template <int NTILE, int K, class FA, class FB>
+__device__ __forceinline__ void mm_hl(f32x4 (&acc)[NTILE], FA A, FB B, int l16, int g4) {
+#pragma unroll 1
+    for (int k0 = 0; k0 < K; k0 += 32) {
+        bf16x8 ah[NTILE], al[NTILE], bh[NTILE], bl[NTILE];
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) {
+            ah[t] = *reinterpret_cast<const bf16x8*>(A(t, l16, k0 + 8 * g4, 0));
+            al[t] = *reinterpret_cast<const bf16x8*>(A(t, l16, k0 + 8 * g4, 1));
+            bh[t] = *reinterpret_cast<const bf16x8*>(B(t, k0 + 8 * g4, l16, 0));
+            bl[t] = *reinterpret_cast<const bf16x8*>(B(t, k0 + 8 * g4, l16, 1));
+        }
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[t], bh[t], acc[t], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[t], bl[t], acc[t], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[t], bh[t], acc[t], 0, 0, 0);
+    }
+}
+
 // This thread's L tokens of key channel c in the element phase, every load issued at once: a
 // token past the end reads the last token, and the caller zeroes it.
 template <typename In, int L>
@@ -1002,13 +1036,19 @@ struct GradCfg {
     static constexpr int LDC = C + 4;         // fp32 [64][64]
     static constexpr int LDF = DK + 4;        // fp32 [64][DK]
     static constexpr int LDT = DK + 16 / ES;  // In [64][DK]
-    // region 1: dO, dR, U (phases 1-2); then G and the raw q, k, b (phases 3-5)
-    static constexpr int DO = 0, DR = C * LDV * 4, UU = 2 * C * LDV * 4;
+    // bf16 inputs: the phase 2-3 products on bf16 hi/lo operands, each matrix as a hi and a lo
+    // plane of bf16 rows (LDB, LDS2 elements); fp32 inputs: fp32 rows
+    static constexpr bool HL = ES == 2;
+    static constexpr int LDB = DV + 8, LDS2 = DV / 2 + 8;
+    static constexpr int PB = C * LDB * 2, PS = DK * LDS2 * 2;  // plane bytes
+    static constexpr int MAT = HL ? 2 * PB : C * LDV * 4;       // dO, dR or U
+    // region 1: dO, dR, U (phases 1-3); then G and the raw q, k, b (phases 3-5)
+    static constexpr int DO = 0, DR = MAT, UU = 2 * MAT;
     static constexpr int GG = 0, QQ = C * LDF * 4, KK = QQ + C * LDT * ES, BB = KK + C * LDT * ES;
-    static constexpr int R1 = cmax(3 * C * LDV * 4, BB + C * LDT * ES);
+    static constexpr int R1 = cmax(3 * MAT, BB + C * LDT * ES);
     // region 2: a half of S or dS' (phase 2); then dA, dP (phases 3-4); then dG (phase 5)
     static constexpr int SH = R1, DA = R1, DP = R1 + C * LDC * 4, DG = R1;
-    static constexpr int R2 = cmax(DK * LDH * 4, cmax(2 * C * LDC * 4, C * LDF * 4));
+    static constexpr int R2 = cmax(HL ? 2 * PS : DK * LDH * 4, cmax(2 * C * LDC * 4, C * LDF * 4));
     static constexpr int GC = R1 + R2;        // [DK] Gamma_C
     static constexpr int XD = GC + DK * 4;    // [DK] sum_v dS'[c][v] S[c][v]
     static constexpr int XR = XD + DK * 4;    // [DK] sum_i KR_ic (U dS'^T)_ic
@@ -1053,6 +1093,16 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
     float* sOFL = reinterpret_cast<float*>(smem + G::OFL);
     float* sAFT = reinterpret_cast<float*>(smem + G::AFT);
     int* sFLG = reinterpret_cast<int*>(smem + G::FLG);
+    constexpr int LDB = G::LDB, LDS2 = G::LDS2;
+    // bf16 inputs: a matrix in LDS as hi and lo planes (npl elements apart)
+    auto put_hl = [&](int off, int npl, int ld, int r, int c4, const f32x4& x) {
+        bf16* hi = reinterpret_cast<bf16*>(smem + off) + r * ld + c4;
+        bf16x4 h, l;
+        split_hl(x, h, l);
+        *reinterpret_cast<bf16x4*>(hi) = h;
+        *reinterpret_cast<bf16x4*>(hi + npl) = l;
+    };
+    auto pl_of = [&](int off, int npl, int pl) { return reinterpret_cast<const bf16*>(smem + off) + pl * npl; };
     // G_i (chunk-local), G_i - G_j and G_C - G_i from the block-local tile (see two_sum)
     auto Gof = [&](int i, int c) {
         const int b = i / L;
@@ -1121,9 +1171,15 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
             *reinterpret_cast<f32x4*>(dv + off) = a4;
             *reinterpret_cast<f32x4*>(dw + off) = b4;
         }
-        *reinterpret_cast<f32x4*>(sDO + r * LDV + c4) = o4;
-        *reinterpret_cast<f32x4*>(sDR + r * LDV + c4) = r4;
-        *reinterpret_cast<f32x4*>(sU + r * LDV + c4) = u4;
+        if constexpr (G::HL) {
+            put_hl(G::DO, C * LDB, LDB, r, c4, o4);
+            put_hl(G::DR, C * LDB, LDB, r, c4, r4);
+            put_hl(G::UU, C * LDB, LDB, r, c4, u4);
+        } else {
+            *reinterpret_cast<f32x4*>(sDO + r * LDV + c4) = o4;
+            *reinterpret_cast<f32x4*>(sDR + r * LDV + c4) = r4;
+            *reinterpret_cast<f32x4*>(sU + r * LDV + c4) = u4;
+        }
     }
 
     // ---- phase 2: X1 = dO S^T, X2 = dR S^T, X3 = U dS'^T over two halves of the value axis;
@@ -1137,7 +1193,8 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
 #pragma unroll
         for (int i = 0; i < NSH; ++i) {
             const int e = tid + i * NT, r = e / (HV / 4), c4 = (e % (HV / 4)) * 4;
-            *reinterpret_cast<f32x4*>(sSH + r * LDH + c4) = sv[i];
+            if constexpr (G::HL) put_hl(G::SH, DK * LDS2, LDS2, r, c4, sv[i]);
+            else *reinterpret_cast<f32x4*>(sSH + r * LDH + c4) = sv[i];
         }
         lds_barrier();
         {
@@ -1147,12 +1204,21 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
                 acc[j] = X1[j];
                 acc[TPW + j] = X2[j];
             }
-            mm_n<2 * TPW, HV>(acc,
-                [&](int t, int m, int kk) {
-                    const float* X = t < TPW ? sDO : sDR;
-                    return X[((it0 + ITS * (t % TPW)) * 16 + m) * LDV + hh * HV + kk];
-                },
-                [&](int, int kk, int nn) { return sSH[(ct * 16 + nn) * LDH + kk]; }, l16, g4);
+            if constexpr (G::HL)
+                mm_hl<2 * TPW, HV>(acc,
+                    [&](int t, int m, int kk, int pl) {
+                        return pl_of(t < TPW ? G::DO : G::DR, C * LDB, pl) +
+                               ((it0 + ITS * (t % TPW)) * 16 + m) * LDB + hh * HV + kk;
+                    },
+                    [&](int, int kk, int nn, int pl) { return pl_of(G::SH, DK * LDS2, pl) + (ct * 16 + nn) * LDS2 + kk; },
+                    l16, g4);
+            else
+                mm_n<2 * TPW, HV>(acc,
+                    [&](int t, int m, int kk) {
+                        const float* X = t < TPW ? sDO : sDR;
+                        return X[((it0 + ITS * (t % TPW)) * 16 + m) * LDV + hh * HV + kk];
+                    },
+                    [&](int, int kk, int nn) { return sSH[(ct * 16 + nn) * LDH + kk]; }, l16, g4);
 #pragma unroll
             for (int j = 0; j < TPW; ++j) {
                 X1[j] = acc[j];
@@ -1164,7 +1230,8 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
         for (int i = 0; i < NSH; ++i) {
             const int e = tid + i * NT, r = e / (HV / 4), c4 = (e % (HV / 4)) * 4;
             const f32x4 d4 = dsv[i], s4 = sv[i];
-            *reinterpret_cast<f32x4*>(sSH + r * LDH + c4) = d4;
+            if constexpr (G::HL) put_hl(G::SH, DK * LDS2, LDS2, r, c4, d4);
+            else *reinterpret_cast<f32x4*>(sSH + r * LDH + c4) = d4;
             const float p = d4[0] * s4[0] + d4[1] * s4[1] + d4[2] * s4[2] + d4[3] * s4[3];
             xd[i] = hh == 0 ? p : xd[i] + p;
         }
@@ -1173,8 +1240,16 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
             load_half(dsv, dSg, 1);
         }
         lds_barrier();
-        mm_n<TPW, HV>(X3, [&](int t, int m, int kk) { return sU[((it0 + ITS * t) * 16 + m) * LDV + hh * HV + kk]; },
-                      [&](int, int kk, int nn) { return sSH[(ct * 16 + nn) * LDH + kk]; }, l16, g4);
+        if constexpr (G::HL)
+            mm_hl<TPW, HV>(X3,
+                [&](int t, int m, int kk, int pl) {
+                    return pl_of(G::UU, C * LDB, pl) + ((it0 + ITS * t) * 16 + m) * LDB + hh * HV + kk;
+                },
+                [&](int, int kk, int nn, int pl) { return pl_of(G::SH, DK * LDS2, pl) + (ct * 16 + nn) * LDS2 + kk; },
+                l16, g4);
+        else
+            mm_n<TPW, HV>(X3, [&](int t, int m, int kk) { return sU[((it0 + ITS * t) * 16 + m) * LDV + hh * HV + kk]; },
+                          [&](int, int kk, int nn) { return sSH[(ct * 16 + nn) * LDH + kk]; }, l16, g4);
     }
     // the row sums: the HV / 4 threads of a row are consecutive lanes
 #pragma unroll
@@ -1199,15 +1274,26 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
         f32x4 acc[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc[t] = zero4();
-        mm_n<4, DV>(acc,
-            [&](int t, int m, int kk) {
-                const int p = wave + 8 * (t >> 1);
-                return (t & 1 ? sDO : sDR)[((p >> 2) * 16 + m) * LDV + kk];
-            },
-            [&](int t, int kk, int nn) {
-                const int p = wave + 8 * (t >> 1);
-                return sU[((p & 3) * 16 + nn) * LDV + kk];
-            }, l16, g4);
+        if constexpr (G::HL)
+            mm_hl<4, DV>(acc,
+                [&](int t, int m, int kk, int pl) {
+                    const int p = wave + 8 * (t >> 1);
+                    return pl_of(t & 1 ? G::DO : G::DR, C * LDB, pl) + ((p >> 2) * 16 + m) * LDB + kk;
+                },
+                [&](int t, int kk, int nn, int pl) {
+                    const int p = wave + 8 * (t >> 1);
+                    return pl_of(G::UU, C * LDB, pl) + ((p & 3) * 16 + nn) * LDB + kk;
+                }, l16, g4);
+        else
+            mm_n<4, DV>(acc,
+                [&](int t, int m, int kk) {
+                    const int p = wave + 8 * (t >> 1);
+                    return (t & 1 ? sDO : sDR)[((p >> 2) * 16 + m) * LDV + kk];
+                },
+                [&](int t, int kk, int nn) {
+                    const int p = wave + 8 * (t >> 1);
+                    return sU[((p & 3) * 16 + nn) * LDV + kk];
+                }, l16, g4);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int p = wave + 8 * (t >> 1), I = p >> 2, J = p & 3, mat = t & 1;
