@@ -163,6 +163,22 @@ __device__ __forceinline__ void mm_hl(f32x4 (&acc)[NTILE], FA A, FB B, int l16, 
     }
 }
 
+__device__ __forceinline__ f32x4 mf16(const f32x4& acc, const bf16x4& a, const bf16x4& b) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), acc,
+                                                     0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mf32(const f32x4& acc, const bf16x8& a, const bf16x8& b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+// hi/lo of eight values
+__device__ __forceinline__ void split_hl8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+    for (int z = 0; z < 8; ++z) {
+        hi[z] = (bf16)x[z];
+        lo[z] = (bf16)(x[z] - (float)hi[z]);
+    }
+}
+
 // This thread's L tokens of key channel c in the element phase, every load issued at once: a
 // token past the end reads the last token, and the caller zeroes it.
 template <typename In, int L>
@@ -659,7 +675,7 @@ struct SerCfg {
 
 // Kernel 1: the forward re-run, U = U0 - W S and S <- Gamma_C.S + KR^T U per chunk; stores
 // the state entering every chunk and U
-template <int DK, int DV>
+template <int DK, int DV, bool HL>
 __global__ __launch_bounds__(NT) void bwd_fwd_kernel(const float* __restrict__ loc,
                                                      const float* __restrict__ initial_state,
                                                      float* __restrict__ s_ckpt, float* __restrict__ u_out,
@@ -738,12 +754,26 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(const float* __restrict__ l
             for (int c = 0; c < SPW; ++c)
 #pragma unroll
                 for (int it = 0; it < 4; ++it) acc[c][it] = zero4();
+            if constexpr (HL) {  // the accumulator rows 4 g4 + e are the K = 16 slots of the B operand
+                bf16x4 sh[SPW], sl[SPW];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+                for (int c = 0; c < SPW; ++c) split_hl(S[c], sh[c], sl[c]);
 #pragma unroll
-                for (int c = 0; c < SPW; ++c)
+                for (int it = 0; it < 4; ++it) {
+                    bf16x4 wh, wl;
+                    split_hl(Wv[it], wh, wl);
 #pragma unroll
-                    for (int it = 0; it < 4; ++it) acc[c][it] = mfma4(acc[c][it], Wv[it][j], S[c][j]);
+                    for (int c = 0; c < SPW; ++c)
+                        acc[c][it] = mf16(mf16(mf16(acc[c][it], wh, sh[c]), wh, sl[c]), wl, sh[c]);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int c = 0; c < SPW; ++c)
+#pragma unroll
+                        for (int it = 0; it < 4; ++it) acc[c][it] = mfma4(acc[c][it], Wv[it][j], S[c][j]);
+            }
             __builtin_amdgcn_sched_barrier(0);
             pre_w(nn);
 #pragma unroll
@@ -783,11 +813,31 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(const float* __restrict__ l
                 for (int r = 0; r < 4; ++r) a2[c][0][r] = S[c][r] * GCv[r];
                 a2[c][1] = zero4();
             }
+            if constexpr (HL) {  // slot (g4, e) of block b2: token 4 (8 b2 + e) + g4
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
+                for (int b2 = 0; b2 < 2; ++b2) {
+                    float ka[8];
 #pragma unroll
-                for (int c = 0; c < SPW; ++c)
-                    a2[c][j & 1] = mfma4(a2[c][j & 1], KRv[j], sU[(4 * j + g4) * DVS + (cb + c) * 16 + l16]);
+                    for (int e = 0; e < 8; ++e) ka[e] = KRv[8 * b2 + e];
+                    bf16x8 kh, kl;
+                    split_hl8(ka, kh, kl);
+#pragma unroll
+                    for (int c = 0; c < SPW; ++c) {
+                        float ua[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) ua[e] = sU[(4 * (8 * b2 + e) + g4) * DVS + (cb + c) * 16 + l16];
+                        bf16x8 uh, ul;
+                        split_hl8(ua, uh, ul);
+                        a2[c][b2] = mf32(mf32(mf32(a2[c][b2], kh, uh), kh, ul), kl, uh);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+#pragma unroll
+                    for (int c = 0; c < SPW; ++c)
+                        a2[c][j & 1] = mfma4(a2[c][j & 1], KRv[j], sU[(4 * j + g4) * DVS + (cb + c) * 16 + l16]);
+            }
 #pragma unroll
             for (int c = 0; c < SPW; ++c) {
                 S[c] = a2[c][0] + a2[c][1];
@@ -802,7 +852,7 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(const float* __restrict__ l
 // Kernel 2: the chunks in reverse order, dU = P^T dO + KR dS', dS = Gamma_C.dS' + QG^T dO -
 // W^T dU (W^T = KG^T T^T), dR = T^T dU; stores dS' of every chunk, dR, and the gradient of the
 // initial state
-template <int DK, int DV>
+template <int DK, int DV, bool HL>
 __global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__ loc, const float* __restrict__ d_o,
                                                        const float* __restrict__ d_final,
                                                        float* __restrict__ ds_ckpt, float* __restrict__ dr_out,
@@ -919,12 +969,26 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__
             for (int c = 0; c < SPW; ++c)
 #pragma unroll
                 for (int it = 0; it < 4; ++it) acc[c][it] = zero4();
+            if constexpr (HL) {  // the accumulator rows 4 g4 + e are the K = 16 slots of the B operand
+                bf16x4 sh[SPW], sl[SPW];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+                for (int c = 0; c < SPW; ++c) split_hl(dS[c], sh[c], sl[c]);
 #pragma unroll
-                for (int c = 0; c < SPW; ++c)
+                for (int it = 0; it < 4; ++it) {
+                    bf16x4 kh, kl;
+                    split_hl(KRv[it], kh, kl);
 #pragma unroll
-                    for (int it = 0; it < 4; ++it) acc[c][it] = mfma4(acc[c][it], KRv[it][j], dS[c][j]);
+                    for (int c = 0; c < SPW; ++c)
+                        acc[c][it] = mf16(mf16(mf16(acc[c][it], kh, sh[c]), kh, sl[c]), kl, sh[c]);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int c = 0; c < SPW; ++c)
+#pragma unroll
+                        for (int it = 0; it < 4; ++it) acc[c][it] = mfma4(acc[c][it], KRv[it][j], dS[c][j]);
+            }
 #pragma unroll
             for (int s = 0; s < JS; ++s) {
                 const int jb = (st * JW + 4 * s) / 16;  // token block: P[j][i] = 0 for row tiles past it
@@ -966,14 +1030,44 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__
             f32x4 a2[SPW][2];
 #pragma unroll
             for (int c = 0; c < SPW; ++c) a2[c][0] = a2[c][1] = zero4();
+            if constexpr (HL) {  // slot (g4, e) of block b2: token 4 (8 b2 + e) + g4
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
+                for (int b2 = 0; b2 < 2; ++b2) {
+                    float qa[8], wa[8];
 #pragma unroll
-                for (int c = 0; c < SPW; ++c) {
-                    const int o = (4 * j + g4) * DVS + (cb + c) * 16 + l16;
-                    a2[c][0] = mfma4(a2[c][0], QGv[j], sDOn[o]);
-                    a2[c][1] = mfma4(a2[c][1], Wt[j], sDU[o]);
+                    for (int e = 0; e < 8; ++e) {
+                        qa[e] = QGv[8 * b2 + e];
+                        wa[e] = Wt[8 * b2 + e];
+                    }
+                    bf16x8 qh, ql, wh, wl;
+                    split_hl8(qa, qh, ql);
+                    split_hl8(wa, wh, wl);
+#pragma unroll
+                    for (int c = 0; c < SPW; ++c) {
+                        float oa[8], ua[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int o = (4 * (8 * b2 + e) + g4) * DVS + (cb + c) * 16 + l16;
+                            oa[e] = sDOn[o];
+                            ua[e] = sDU[o];
+                        }
+                        bf16x8 oh, ol, uh, ul;
+                        split_hl8(oa, oh, ol);
+                        split_hl8(ua, uh, ul);
+                        a2[c][0] = mf32(mf32(mf32(a2[c][0], qh, oh), qh, ol), ql, oh);
+                        a2[c][1] = mf32(mf32(mf32(a2[c][1], wh, uh), wh, ul), wl, uh);
+                    }
                 }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+#pragma unroll
+                    for (int c = 0; c < SPW; ++c) {
+                        const int o = (4 * j + g4) * DVS + (cb + c) * 16 + l16;
+                        a2[c][0] = mfma4(a2[c][0], QGv[j], sDOn[o]);
+                        a2[c][1] = mfma4(a2[c][1], Wt[j], sDU[o]);
+                    }
+            }
 #pragma unroll
             for (int c = 0; c < SPW; ++c) {
 #pragma unroll
@@ -988,16 +1082,39 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__
             f32x4 acc[SPW][2];
 #pragma unroll
             for (int c = 0; c < SPW; ++c) acc[c][0] = acc[c][1] = zero4();
+            if constexpr (HL) {  // slot (g4, e) of block b2: token 4 (8 b2 + e) + g4; T is zero above
+                                 // the diagonal, so block 0 adds nothing for row tiles 2 and 3
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-                if (kb >= dri) {
+                for (int b2 = 0; b2 < 2; ++b2)
+                    if (b2 == 1 || dri < 2) {
+                        float ta[8];
 #pragma unroll
-                    for (int s = 0; s < 4; ++s)
+                        for (int e = 0; e < 8; ++e) ta[e] = Tv[8 * b2 + e];
+                        bf16x8 th, tl;
+                        split_hl8(ta, th, tl);
 #pragma unroll
-                        for (int c = 0; c < SPW; ++c)
-                            acc[c][s & 1] = mfma4(acc[c][s & 1], Tv[kb * 4 + s],
-                                                  sDU[(kb * 16 + 4 * s + g4) * DVS + (cb + c) * 16 + l16]);
-                }
+                        for (int c = 0; c < SPW; ++c) {
+                            float ua[8];
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                ua[e] = sDU[(4 * (8 * b2 + e) + g4) * DVS + (cb + c) * 16 + l16];
+                            bf16x8 uh, ul;
+                            split_hl8(ua, uh, ul);
+                            acc[c][b2] = mf32(mf32(mf32(acc[c][b2], th, uh), th, ul), tl, uh);
+                        }
+                    }
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+                    if (kb >= dri) {
+#pragma unroll
+                        for (int s = 0; s < 4; ++s)
+#pragma unroll
+                            for (int c = 0; c < SPW; ++c)
+                                acc[c][s & 1] = mfma4(acc[c][s & 1], Tv[kb * 4 + s],
+                                                      sDU[(kb * 16 + 4 * s + g4) * DVS + (cb + c) * 16 + l16]);
+                    }
+            }
 #pragma unroll
             for (int c = 0; c < SPW; ++c) {
                 const f32x4 dr = acc[c][0] + acc[c][1];
@@ -1504,11 +1621,13 @@ hipError_t launch_bwd_typed(const BwdArgs& a) {
                        a.loc, (int)a.T, (int)a.H, (int)nper);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    // bf16 inputs: the serial passes' products on bf16 hi/lo operands; fp32 inputs: fp32
+    constexpr bool HL = sizeof(In) == 2;
     const unsigned nser = (unsigned)(bh * SerCfg<D, D>::NSL);
-    hipLaunchKernelGGL((bwd_fwd_kernel<D, D>), dim3(nser), dim3(NT), 0, (hipStream_t)a.stream, a.loc,
+    hipLaunchKernelGGL((bwd_fwd_kernel<D, D, HL>), dim3(nser), dim3(NT), 0, (hipStream_t)a.stream, a.loc,
                        a.initial_state, a.s_ckpt, a.u, (int)a.T, (int)a.H, (int)bh);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_state_kernel<D, D>), dim3(nser), dim3(NT), 0, (hipStream_t)a.stream, a.loc, a.d_o,
+    hipLaunchKernelGGL((bwd_state_kernel<D, D, HL>), dim3(nser), dim3(NT), 0, (hipStream_t)a.stream, a.loc, a.d_o,
                        a.d_final_state, a.ds_ckpt, a.dr, a.g_s0, (int)a.T, (int)a.H, (int)bh);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return launch_grad<In, D>(a);
