@@ -79,6 +79,7 @@ struct Cfg {
     static constexpr int TTR = FLG + 8 * 4;                   // [64][LC] T^T (blocks of T_A and T_22)
     static constexpr int BYTES = TTR + C * LC * 2;
     static_assert(BYTES <= 163840, "LDS budget exceeded");
+    static_assert(BYTES >= 4 * (kMaxSort + 1), "no room for the sequence order");
     static_assert(SBT + DVS * LDK * 2 <= TR, "state operand does not fit the work area");
     static_assert(TR + C * LC * 2 <= GC, "T does not fit the work area");
     static_assert(DK % 64 == 0 && DVS % 16 == 0 && DVS <= 64 && TPV >= 1, "shape");
@@ -445,7 +446,10 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
             slice = id % nslices;
         }
     }
-    const int bi = bh / H, h = bh % H;
+    const int h = bh % H;
+    // packed sequences: the longest first
+    const int bi = cu_seqlens ? longest_first(cu_seqlens, B, bh / H, Tparam, reinterpret_cast<int*>(smem)) : bh / H;
+    bh = bi * H + h;
     const int col0 = slice * DVS;
     // sequence bi covers tokens [tok0, tok0 + Tlen) of the token axis: fixed length Tparam,
     // or packed sequences delimited by offsets (clamped into [0, Tparam], so any offsets

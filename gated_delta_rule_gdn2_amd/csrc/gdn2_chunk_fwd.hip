@@ -79,6 +79,7 @@ struct ChunkCfg {
     static constexpr int BLK = GC + DK * 4;                         // [4][DK] fp32 block decays
     static constexpr int BYTES = BLK + 4 * DK * 4;
     static_assert(BYTES <= 163840, "LDS budget exceeded");
+    static_assert(BYTES >= 4 * (kMaxSort + 1), "no room for the sequence order");
     static_assert(DK % 64 == 0 && DVS % 16 == 0 && DVS <= 64, "shape");
 };
 
@@ -392,7 +393,10 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(
             slice = id % nslices;
         }
     }
-    const int bi = bh / H, h = bh % H;
+    const int h = bh % H;
+    // packed sequences: the longest first
+    const int bi = cu_seqlens ? longest_first(cu_seqlens, B, bh / H, Tparam, reinterpret_cast<int*>(smem)) : bh / H;
+    bh = bi * H + h;
     const int col0 = slice * DVS;  // first value column of this slice
     // sequence bi covers tokens [tok0, tok0 + Tlen) of the token axis: fixed length Tparam,
     // or packed sequences delimited by offsets (clamped into [0, Tparam], so any offsets

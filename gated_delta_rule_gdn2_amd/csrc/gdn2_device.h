@@ -166,4 +166,36 @@ __device__ __forceinline__ Vec<T, N> load_vec(const T* p) {
 // exp(x) for x <= 0 through the hardware base-2 exponential
 __device__ __forceinline__ float exp_neg(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
+
+// Packed sequences, longest first.  A launch walks its ns sequences in workgroup order, one
+// chain of chunks per (sequence, head, slice); when the lengths differ, a long sequence that
+// starts late sets the launch's length.  So sequence slot r (in dispatch order) takes the
+// r-th longest sequence, ties in index order.  Lengths are the offsets clamped into
+// [0, Tparam] as the kernels clamp them.  Every thread of the workgroup calls this, before
+// anything else uses LDS; scratch holds ns + 1 ints.  For ns > kMaxSort, slot r takes
+// sequence r.
+constexpr int kMaxSort = 512;
+__device__ __forceinline__ int longest_first(const int64_t* __restrict__ cu, int ns, int r, int Tparam, int* scratch) {
+    if (ns > kMaxSort) return r;
+    for (int i = threadIdx.x; i < ns; i += blockDim.x) {
+        const int64_t lo = min(max(cu[i], (int64_t)0), (int64_t)Tparam);
+        const int64_t hi = min(max(cu[i + 1], lo), (int64_t)Tparam);
+        scratch[i] = (int)(hi - lo);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < ns; i += blockDim.x) {
+        const int li = scratch[i];
+        int rank = 0;
+        for (int j = 0; j < ns; ++j) {
+            const int lj = scratch[j];
+            rank += (lj > li) || (lj == li && j < i);
+        }
+        if (rank == r) scratch[kMaxSort] = i;  // ranks are a permutation: one writer
+    }
+    __syncthreads();
+    const int sel = scratch[kMaxSort];
+    __syncthreads();
+    return sel;
+}
+
 }  // namespace gdn2

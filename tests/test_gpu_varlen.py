@@ -210,3 +210,56 @@ def test_multi_token_steps_in_place_continue_the_sequences():
         es = rel_max_err(state[n], s_ref[0])
         say("  sequence %d: o err %.3e   S err %.3e" % (n, eo, es))
         assert eo <= TOL_BF16 and es <= TOL_BF16, (n, eo, es)
+
+
+def test_sequence_order_does_not_change_results():
+    """Workgroups take the packed sequences longest first; every sequence's o and S_T are
+    bit-identical when the same sequences are packed in the reverse order."""
+    say("case: varlen order independence, bf16 d128")
+    lengths, H = [300, 5, 130, 64, 1, 257], 2
+    inp = packed_case(torch.bfloat16, 128, H, lengths, 210)
+    o, s = run_varlen(inp)
+    cu = inp["cu_seqlens"].tolist()
+    N = len(lengths)
+    rev = {}
+    for nm in ("q", "k", "v", "log_alpha", "b", "w"):
+        rev[nm] = torch.cat([inp[nm][cu[n]:cu[n + 1]] for n in reversed(range(N))])
+    rev["s0"] = inp["s0"].flip(0).contiguous()
+    rcu = [0]
+    for n in reversed(range(N)):
+        rcu.append(rcu[-1] + lengths[n])
+    rev["cu_seqlens"] = torch.tensor(rcu, dtype=torch.int64)
+    o2, s2 = run_varlen(rev)
+    for n in range(N):
+        m = N - 1 - n
+        assert torch.equal(o[cu[n]:cu[n + 1]], o2[rcu[m]:rcu[m + 1]]), n
+        assert torch.equal(s[n], s2[m]), n
+
+
+def _split(inp, lo, hi):
+    """Sequences lo..hi-1 of a packed batch as a packed batch of their own."""
+    cu = inp["cu_seqlens"].tolist()
+    out = {nm: inp[nm][cu[lo]:cu[hi]] for nm in ("q", "k", "v", "log_alpha", "b", "w")}
+    out["cu_seqlens"] = torch.tensor([c - cu[lo] for c in cu[lo:hi + 1]], dtype=torch.int64)
+    out["s0"] = None if inp["s0"] is None else inp["s0"][lo:hi].contiguous()
+    return out
+
+
+def test_more_sequences_than_the_sorted_range():
+    """600 packed sequences (past the 512 the longest-first order sorts; they go in index
+    order), lengths 0-70.  bf16: bit-identical to the same sequences in two calls of 300
+    (sorted order).  fp32: against the oracle per sequence."""
+    gen = torch.Generator("cpu").manual_seed(211)
+    lengths = torch.randint(0, 71, (600,), generator=gen).tolist()
+    say("case: varlen 600 sequences bf16 d64, one call vs two")
+    inp = packed_case(torch.bfloat16, 64, 1, lengths, 211)
+    o, s = run_varlen(inp)
+    cu = inp["cu_seqlens"].tolist()
+    for lo, hi in ((0, 300), (300, 600)):
+        o2, s2 = run_varlen(_split(inp, lo, hi))
+        assert torch.equal(o[cu[lo]:cu[hi]], o2), (lo, hi)
+        assert torch.equal(s[lo:hi], s2), (lo, hi)
+    say("case: varlen 600 sequences fp32 d64 vs oracle")
+    inp = packed_case(torch.float32, 64, 1, lengths, 212)
+    o, s = run_varlen(inp)
+    check_all(inp, o, s, TOL_F32, "600 sequences fp32")
