@@ -31,10 +31,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 // reciprocal (about 1 ulp each); these passes are limited by vector ALU issue, not by HBM,
 // once IEEE division and a library log1p are in them.
 __device__ __forceinline__ float sigmoid_f(float x) {
-    // 1 / (1 + e^-x) without overflow: e^-|x| <= 1
-    const float e = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
-    const float r = __builtin_amdgcn_rcpf(1.f + e);
-    return x >= 0.f ? r : e * r;
+    // 1 / (1 + e^-x): for x below about -88, e^-x overflows to infinity and the reciprocal of
+    // infinity is the limit 0
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2e));
 }
 __device__ __forceinline__ float log_sigmoid_f(float x) {
     // min(x, 0) - log(1 + e), e = e^-|x| in (0, 1]; log(1 + e) by its series below 2^-7
@@ -155,7 +154,7 @@ __global__ __launch_bounds__(192) void prep_kernel(
         }
         if (role < 2) {  // q, k: L2 normalisation over the head
             ss = group_sum<LPH>(ss);
-            const float inv = 1.f / sqrtf(ss + eps);
+            const float inv = __builtin_amdgcn_rsqf(ss + eps);  // hardware 1/sqrt (about 1 ulp)
 #pragma unroll
             for (int e = 0; e < CH; ++e) u[e] *= inv;
         }
@@ -189,7 +188,7 @@ __global__ __launch_bounds__(256) void out_kernel(const OT* __restrict__ o, cons
         s += x[e] * x[e];
     }
     s = group_sum<LPR>(s);
-    const float inv = 1.f / sqrtf(s * (1.f / DV) + eps);
+    const float inv = __builtin_amdgcn_rsqf(s * (1.f / DV) + eps);  // hardware 1/sqrt (about 1 ulp)
     float r[EL];
 #pragma unroll
     for (int e = 0; e < EL; ++e) r[e] = x[e] * inv * g[e] * silu_f(to_f32(zv.v[e]));
