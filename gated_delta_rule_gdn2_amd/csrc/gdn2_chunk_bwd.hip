@@ -1269,35 +1269,57 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
     load_half(sv, Sg, 0);
     load_half(dsv, dSg, 0);
 
-    // ---- phase 1: dO, dR, U of the chunk; dv = dR.w, dw = dR.v ----
-    for (int e = tid; e < C * DV / 4; e += NT) {
-        const int r = e / (DV / 4), c4 = (e % (DV / 4)) * 4, t = t0 + r;
-        f32x4 o4 = zero4(), r4 = zero4(), u4 = zero4();
-        if (t < T) {
-            const int64_t off = base_v + (int64_t)t * rv + c4;
-            o4 = *reinterpret_cast<const f32x4*>(d_o + off);
-            r4 = *reinterpret_cast<const f32x4*>(dr_in + off);
-            u4 = *reinterpret_cast<const f32x4*>(u_in + off);
-            const Vec<In, 4> w4 = load_vec<In, 4>(wgate + off), v4 = load_vec<In, 4>(v + off);
-            f32x4 a4, b4;
+    // ---- phase 1, by halves of the value axis: dO, dR, U of the chunk into LDS; dv = dR.w,
+    // dw = dR.v.  The second half's loads are in flight during the first half's products ----
+    constexpr int NP1 = C * HV / 4 / NT;  // float4 of a value half per thread
+    static_assert(NP1 * 4 * NT == C * HV, "phase 1 split");
+    f32x4 p1o[NP1], p1r[NP1], p1u[NP1];
+    Vec<In, 4> p1w[NP1], p1v[NP1];
+    auto p1_load = [&](int hh) {  // rows past the end read the last token, zeroed in p1_use
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                a4[x] = r4[x] * to_f32(w4.v[x]);
-                b4[x] = r4[x] * to_f32(v4.v[x]);
+        for (int x = 0; x < NP1; ++x) {
+            const int e = tid + x * NT, r = e / (HV / 4), c4 = hh * HV + (e % (HV / 4)) * 4;
+            const int64_t off = base_v + (int64_t)min(t0 + r, T - 1) * rv + c4;
+            p1o[x] = *reinterpret_cast<const f32x4*>(d_o + off);
+            p1r[x] = *reinterpret_cast<const f32x4*>(dr_in + off);
+            p1u[x] = *reinterpret_cast<const f32x4*>(u_in + off);
+            p1w[x] = load_vec<In, 4>(wgate + off);
+            p1v[x] = load_vec<In, 4>(v + off);
+        }
+    };
+    auto p1_use = [&](int hh) {
+#pragma unroll
+        for (int x = 0; x < NP1; ++x) {
+            const int e = tid + x * NT, r = e / (HV / 4), c4 = hh * HV + (e % (HV / 4)) * 4, t = t0 + r;
+            f32x4 o4 = zero4(), r4 = zero4(), u4 = zero4();
+            if (t < T) {
+                o4 = p1o[x];
+                r4 = p1r[x];
+                u4 = p1u[x];
+                const int64_t off = base_v + (int64_t)t * rv + c4;
+                f32x4 a4, b4;
+#pragma unroll
+                for (int z = 0; z < 4; ++z) {
+                    a4[z] = r4[z] * to_f32(p1w[x].v[z]);
+                    b4[z] = r4[z] * to_f32(p1v[x].v[z]);
+                }
+                *reinterpret_cast<f32x4*>(dv + off) = a4;
+                *reinterpret_cast<f32x4*>(dw + off) = b4;
             }
-            *reinterpret_cast<f32x4*>(dv + off) = a4;
-            *reinterpret_cast<f32x4*>(dw + off) = b4;
+            if constexpr (G::HL) {
+                put_hl(G::DO, C * LDB, LDB, r, c4, o4);
+                put_hl(G::DR, C * LDB, LDB, r, c4, r4);
+                put_hl(G::UU, C * LDB, LDB, r, c4, u4);
+            } else {
+                *reinterpret_cast<f32x4*>(sDO + r * LDV + c4) = o4;
+                *reinterpret_cast<f32x4*>(sDR + r * LDV + c4) = r4;
+                *reinterpret_cast<f32x4*>(sU + r * LDV + c4) = u4;
+            }
         }
-        if constexpr (G::HL) {
-            put_hl(G::DO, C * LDB, LDB, r, c4, o4);
-            put_hl(G::DR, C * LDB, LDB, r, c4, r4);
-            put_hl(G::UU, C * LDB, LDB, r, c4, u4);
-        } else {
-            *reinterpret_cast<f32x4*>(sDO + r * LDV + c4) = o4;
-            *reinterpret_cast<f32x4*>(sDR + r * LDV + c4) = r4;
-            *reinterpret_cast<f32x4*>(sU + r * LDV + c4) = u4;
-        }
-    }
+    };
+    p1_load(0);
+    p1_use(0);
+    p1_load(1);
 
     // ---- phase 2: X1 = dO S^T, X2 = dR S^T, X3 = U dS'^T over two halves of the value axis;
     // each half of S and dS' goes through registers, loaded one step ahead ----
@@ -1367,6 +1389,7 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
         else
             mm_n<TPW, HV>(X3, [&](int t, int m, int kk) { return sU[((it0 + ITS * t) * 16 + m) * LDV + hh * HV + kk]; },
                           [&](int, int kk, int nn) { return sSH[(ct * 16 + nn) * LDH + kk]; }, l16, g4);
+        if (hh == 0) p1_use(1);  // the second value half of dO, dR, U (columns no product reads yet)
     }
     // the row sums: the HV / 4 threads of a row are consecutive lanes
 #pragma unroll
