@@ -1266,8 +1266,6 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
             d[i] = *reinterpret_cast<const f32x4*>(g + r * DV + hh * HV + c4);
         }
     };
-    load_half(sv, Sg, 0);
-    load_half(dsv, dSg, 0);
 
     // ---- phase 1, by halves of the value axis: dO, dR, U of the chunk into LDS; dv = dR.w,
     // dw = dR.v.  The second half's loads are in flight during the first half's products ----
@@ -1317,7 +1315,10 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
             }
         }
     };
+    // loads in the order of use (a wait covers every load issued before the one it needs)
     p1_load(0);
+    load_half(sv, Sg, 0);
+    load_half(dsv, dSg, 0);
     p1_use(0);
     p1_load(1);
 
