@@ -1521,25 +1521,41 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
         const float gc = sGC[c];
 #pragma unroll
         for (int j = 0; j < TPW; ++j) X3[j] *= gc;
+        // blocks of 16 contraction tokens; lane group g4 takes the tokens 16 b + 4 g4 + s of
+        // block b at the four MFMA steps s (its factors for four tokens at once, and the dP, dA
+        // rows of X1, X2 as 16-byte reads)
 #pragma unroll
-        for (int kb = 0; kb < C; kb += 4) {
-            const int r = kb + g4;  // contraction token of this lane group
-            const float Gr = Gof(r, c);
-            const float kr = to_f32(sK[r * LDT + c]);
-            const float ep = exp_any(Gr), en = exp_any(-Gr);
-            const float ki = kr * en;                        // k / Gamma
-            const float kg = to_f32(sB[r * LDT + c]) * kr * ep;  // kh.Gamma
-            const float qg = to_f32(sQ[r * LDT + c]) * ep;       // q.Gamma
+        for (int b16 = 0; b16 < C / 16; ++b16) {
+            float ki[4], kg[4], qg[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int r = b16 * 16 + 4 * g4 + s;
+                const float Gr = Gof(r, c);
+                const float kr = to_f32(sK[r * LDT + c]);
+                const float ep = exp_any(Gr), en = exp_any(-Gr);
+                ki[s] = kr * en;                                // k / Gamma
+                kg[s] = to_f32(sB[r * LDT + c]) * kr * ep;      // kh.Gamma
+                qg[s] = to_f32(sQ[r * LDT + c]) * ep;           // q.Gamma
+            }
 #pragma unroll
             for (int j = 0; j < TPW; ++j) {
                 const int it = it0 + ITS * j;
-                if (kb < it * 16 + 16) {
-                    X1[j] = mfma4(X1[j], sDP[(it * 16 + l16) * LDC + r], ki);
-                    X2[j] = mfma4(X2[j], sDA[(it * 16 + l16) * LDC + r], ki);
+                if (b16 <= it) {  // X1, X2: tokens up to i (dP, dA are zero above the diagonal)
+                    const f32x4 p4 = *reinterpret_cast<const f32x4*>(sDP + (it * 16 + l16) * LDC + b16 * 16 + 4 * g4);
+                    const f32x4 a4 = *reinterpret_cast<const f32x4*>(sDA + (it * 16 + l16) * LDC + b16 * 16 + 4 * g4);
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        X1[j] = mfma4(X1[j], p4[s], ki[s]);
+                        X2[j] = mfma4(X2[j], a4[s], ki[s]);
+                    }
                 }
-                if (kb + 4 > it * 16) {
-                    X3[j] = mfma4(X3[j], sDA[r * LDC + it * 16 + l16], kg);
-                    X3[j] = mfma4(X3[j], sDP[r * LDC + it * 16 + l16], qg);
+                if (b16 >= it) {  // X3: tokens from i on
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const int r = b16 * 16 + 4 * g4 + s;
+                        X3[j] = mfma4(X3[j], sDA[r * LDC + it * 16 + l16], kg[s]);
+                        X3[j] = mfma4(X3[j], sDP[r * LDC + it * 16 + l16], qg[s]);
+                    }
                 }
             }
         }
