@@ -593,13 +593,14 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
             f32x4 acc0[NCOL], acc1[NCOL];
 #pragma unroll
             for (int c = 0; c < NCOL; ++c) acc0[c] = acc1[c] = zero4();
+            // lane group g4 takes the tokens 16 kb + 4 g4 + s at step s: T's rows as 16-byte reads
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
+                const f32x4 a0 = *reinterpret_cast<const f32x4*>(sAT + (p * 16 + l16) * LDC + kb * 16 + 4 * g4);
+                const f32x4 a1 = *reinterpret_cast<const f32x4*>(sAT + ((3 - p) * 16 + l16) * LDC + kb * 16 + 4 * g4);
 #pragma unroll
-                for (int s = 0; s < 16; s += 4) {
-                    const int kk = kb * 16 + s + g4;
-                    const float a0 = sAT[(p * 16 + l16) * LDC + kk];
-                    const float a1 = sAT[((3 - p) * 16 + l16) * LDC + kk];
+                for (int s = 0; s < 4; ++s) {
+                    const int kk = kb * 16 + 4 * g4 + s;
                     float bc[NCOL];
 #pragma unroll
                     for (int c = 0; c < NCOL; ++c) {
@@ -608,8 +609,8 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
                     }
 #pragma unroll
                     for (int c = 0; c < NCOL; ++c) {
-                        if (kb <= p) acc0[c] = mfma4(acc0[c], a0, bc[c]);
-                        if (kb <= 3 - p) acc1[c] = mfma4(acc1[c], a1, bc[c]);
+                        if (kb <= p) acc0[c] = mfma4(acc0[c], a0[s], bc[c]);
+                        if (kb <= 3 - p) acc1[c] = mfma4(acc1[c], a1[s], bc[c]);
                     }
                 }
             }
