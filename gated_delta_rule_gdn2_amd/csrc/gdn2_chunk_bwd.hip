@@ -270,6 +270,7 @@ struct LocCfg {
     static_assert(BYTES <= 163840, "LDS budget exceeded");
     static_assert(NT % DK == 0 && (KT + VT) % 4 == 0, "shape");
     static_assert(C * LDC * 4 <= QG - KI, "P does not fit over k / Gamma");
+    static_assert(4 * 4 * 256 * 4 <= AT - QG, "the diagonal inverses' scratch does not fit");
     static_assert(8 * (KT + VT) / 2 * 256 * 4 <= AT, "the W and U0 staging does not fit");
 };
 
@@ -516,24 +517,55 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
                 sKG[i * LDF + ec] = bv * kv * exp_any(x[m] + off);
             }
         }
-        // T = (I + A)^{-1}: diagonal blocks by forward substitution (column j on lane j of
-        // wave I), in place
-        if (wave < 4 && lane < 16) {
+        // T = (I + A)^{-1}: diagonal block I on wave I, in place.  N = A_II is strictly lower,
+        // so N^16 = 0 and (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8): six 16 x 16 products
+        // on fp32 MFMA through this wave's scratch over the QG tile (free once A and P exist)
+        if (wave < 4) {
+            float* mN = reinterpret_cast<float*>(smem + G::QG) + wave * 4 * 256;  // [16][16] each
+            float* mN2 = mN + 256;
+            float* mN4 = mN + 512;
+            float* mM = mN + 768;
+            float* mN8 = mN;  // N is last read for N^3
             float* Ab = sAT + wave * 16 * LDC + wave * 16;
-            float xs[16];
+            auto sync = [] {  // the wave's own LDS writes, before other lanes read them
+                __builtin_amdgcn_s_waitcnt(0xc07f);
+                __builtin_amdgcn_wave_barrier();
+                asm volatile("" ::: "memory");
+            };
+            auto put = [&](float* Z, const f32x4& x) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) xs[i] = i == lane ? 1.f : 0.f;
+                for (int r = 0; r < 4; ++r) Z[(4 * g4 + r) * 16 + l16] = x[r];
+            };
+            auto prod = [&](const float* X, const float* Y) {  // X Y; lane holds rows 4 g4 + r of column l16
+                f32x4 acc = zero4();
 #pragma unroll
-            for (int m = 0; m < 15; ++m) {
-                const float xm = xs[m];
+                for (int s4 = 0; s4 < 4; ++s4) acc = mfma4(acc, X[l16 * 16 + 4 * g4 + s4], Y[(4 * g4 + s4) * 16 + l16]);
+                return acc;
+            };
+            f32x4 n;
 #pragma unroll
-                for (int i = m + 1; i < 16; ++i) xs[i] -= Ab[i * LDC + m] * xm;
-                // keep each step's loads in their step: hoisted, the 120 loads would need as
-                // many registers
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            for (int r = 0; r < 4; ++r) n[r] = Ab[(4 * g4 + r) * LDC + l16];
+            put(mN, n);
+            sync();
+            const f32x4 n2 = prod(mN, mN);
+            put(mN2, n2);
+            sync();
+            const f32x4 n4 = prod(mN2, mN2), n3 = prod(mN, mN2);
+            put(mN4, n4);
+            f32x4 m;  // (I - N)(I + N^2) = I - N + N^2 - N^3
 #pragma unroll
-            for (int i = 0; i < 16; ++i) Ab[i * LDC + lane] = xs[i];
+            for (int r = 0; r < 4; ++r) m[r] = (4 * g4 + r == l16 ? 1.f : 0.f) - n[r] + n2[r] - n3[r];
+            put(mM, m);
+            sync();
+            const f32x4 n8 = prod(mN4, mN4);
+            m += prod(mM, mN4);  // times (I + N^4)
+            put(mN8, n8);
+            sync();
+            put(mM, m);  // after every lane's reads of the previous contents (one wave, in order)
+            sync();
+            m += prod(mM, mN8);  // times (I + N^8)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Ab[(4 * g4 + r) * LDC + l16] = m[r];
         }
         lds_barrier();
         // off-diagonal blocks, T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ, level by level; every
