@@ -238,6 +238,22 @@ __device__ __forceinline__ void store_n(float* p, const float (&d)[N]) {
 __host__ __device__ constexpr int sw(int i, int c) {
     return ((((c >> 4) * 4 + (i >> 4)) * 4 + (i & 3)) * 16 + (c & 15)) * 4 + ((i >> 2) & 3);
 }
+// With bf16 inputs the products over tokens in the serial passes take bf16 hi/lo operands, so
+// T, QG and the second copies of W and KR are stored split: a hi and a lo plane of bf16
+// (64 n elements apart, the fp32 matrix's bytes), entry (token i, channel c) at element
+// hl_unit(i, c) * 8 + i mod 8 of each, hl_unit = [c / 16][i / 32][(i / 8) mod 4][c mod 16]:
+// lane (g, n16) reads the tokens 32 b + 8 g .. 32 b + 8 g + 7 of channel 16 cb + n16 as one
+// 16-byte unit per plane.
+__host__ __device__ constexpr int hl_unit(int i, int c) {
+    return (((c >> 4) * 2 + (i >> 5)) * 4 + ((i >> 3) & 3)) * 16 + (c & 15);
+}
+// eight consecutive tokens' values, split, to unit u of the planes at base (npl elements apart)
+__device__ __forceinline__ void put_hl8(bf16* base, int npl, int u, const float (&x)[8]) {
+    bf16x8 h, l;
+    split_hl8(x, h, l);
+    *reinterpret_cast<bf16x8*>(base + u * 8) = h;
+    *reinterpret_cast<bf16x8*>(base + npl + u * 8) = l;
+}
 template <int DK, int DV>
 struct Rec {
     static constexpr int64_t OT = 0, OP = C * C, OW = 2 * C * C, OWS = OW + C * DK, OKR = OWS + C * DK,
@@ -251,6 +267,7 @@ struct LocCfg {
     static constexpr int TB = NT / DK, L = C / TB;
     static constexpr int KT = DK / 16, VT = DV / 16;
     static constexpr int ES = (int)sizeof(In);
+    static constexpr bool HL = ES == 2;       // bf16 inputs: split copies in the record
     static constexpr int LDF = DK + 4;        // fp32 [64][DK]
     static constexpr int LDT = DK + 16 / ES;  // In [64][DK]
     static constexpr int LDC = C + 4;         // fp32 [64][64]
@@ -416,17 +433,31 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
                 sRQ[i * LDT + ec] = qv;
             }
         }
-        // the swizzled copies: this thread's tokens with one residue mod 4 are consecutive there
+        if constexpr (G::HL) {  // split copies: this thread's tokens, eight at a time
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            float a[L / 4], b[L / 4];
+            for (int h8 = 0; h8 < L / 8; ++h8) {
+                float a[8], b[8];
 #pragma unroll
-            for (int u = 0; u < L / 4; ++u) {
-                a[u] = qgv[g + 4 * u];
-                b[u] = krv[g + 4 * u];
+                for (int e = 0; e < 8; ++e) {
+                    a[e] = qgv[8 * h8 + e];
+                    b[e] = krv[8 * h8 + e];
+                }
+                const int u = hl_unit(etb * L + 8 * h8, ec);
+                put_hl8(reinterpret_cast<bf16*>(rec + R::OQG), C * DK, u, a);
+                put_hl8(reinterpret_cast<bf16*>(rec + R::OKRS), C * DK, u, b);
             }
-            store_n<L / 4>(rec + R::OQG + sw(etb * L + g, ec), a);
-            store_n<L / 4>(rec + R::OKRS + sw(etb * L + g, ec), b);
+        } else {  // swizzled copies: this thread's tokens with one residue mod 4 are consecutive
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float a[L / 4], b[L / 4];
+#pragma unroll
+                for (int u = 0; u < L / 4; ++u) {
+                    a[u] = qgv[g + 4 * u];
+                    b[u] = krv[g + 4 * u];
+                }
+                store_n<L / 4>(rec + R::OQG + sw(etb * L + g, ec), a);
+                store_n<L / 4>(rec + R::OKRS + sw(etb * L + g, ec), b);
+            }
         }
         prefetch(min(n + 1, n1 - 1));  // on every path (see the serial kernels)
         lds_barrier();
@@ -605,6 +636,7 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
 #pragma unroll
         for (int y = 0; y < 2 * C * C / 4 / NT; ++y) {
             const int e = tid + y * NT, mat = e / (C * C / 4), u = e % (C * C / 4);
+            if (G::HL && mat == 0) continue;  // T goes split (below)
             const int n16 = u & 15, g = (u >> 4) & 3, j4 = (u >> 6) & 3, b = u >> 8;
             const int c = 16 * b + n16;
             const float* src = mat ? sPS : sAT;
@@ -615,6 +647,18 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
                 val[z] = c <= i ? src[i * LDC + c] : 0.f;
             }
             *reinterpret_cast<f32x4*>(rec + (mat ? R::OP : R::OT) + 4 * u) = val;
+        }
+        if constexpr (G::HL) {  // T split: unit u holds rows 32 b2 + 8 g + e of column 16 cb + n16
+            static_assert(C * C / 8 == NT, "one unit of T per thread");
+            const int u = tid, n16 = u & 15, g = (u >> 4) & 3, b2 = (u >> 6) & 1, cb = u >> 7;
+            const int c = 16 * cb + n16;
+            float x[8];
+#pragma unroll
+            for (int e2 = 0; e2 < 8; ++e2) {
+                const int i = 32 * b2 + 8 * g + e2;
+                x[e2] = c <= i ? sAT[i * LDC + c] : 0.f;
+            }
+            put_hl8(reinterpret_cast<bf16*>(rec + R::OT), C * C, u, x);
         }
         // W = T KG and U0 = T (w.v): wave w takes the row tiles p and 3 - p (p = w mod 2) of the
         // column tiles cg, cg + 4, ... (cg = w / 2) of [W | U0]; T is lower triangular, so row
@@ -671,7 +715,18 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
                     float* dst = ct < KT ? rec + R::OW + (I * 16 + row) * DK + ct * 16 + q4
                                          : rec + R::OU0 + (I * 16 + row) * DV + (ct - KT) * 16 + q4;
                     *reinterpret_cast<f32x4*>(dst) = val;
-                    if (ct < KT) {  // W swizzled: rows 4 x + g of column l16, as one 16-byte unit
+                    if constexpr (G::HL) {
+                        if (ct < KT) {  // W split: lane (plane, half, column) writes rows 8 half + e
+                            const int hf = (lane >> 4) & 1, pl = lane >> 5;
+                            float x[8];
+#pragma unroll
+                            for (int e2 = 0; e2 < 8; ++e2) x[e2] = tile[(8 * hf + e2) * 16 + l16];
+                            bf16x8 hi, lo;
+                            split_hl8(x, hi, lo);
+                            *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(rec + R::OWS) + pl * C * DK +
+                                                       hl_unit(I * 16 + 8 * hf, ct * 16 + l16) * 8) = pl ? lo : hi;
+                        }
+                    } else if (ct < KT) {  // W swizzled: rows 4 x + g of column l16, as one unit
                         f32x4 sv4;
 #pragma unroll
                         for (int x = 0; x < 4; ++x) sv4[x] = tile[(4 * x + g4) * 16 + l16];
@@ -717,7 +772,10 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(const float* __restrict__ l
     using R = Rec<DK, DV>;
     constexpr int KT = SC::KT, SPW = SC::SPW, DVS = SC::DVS, OPT = SC::OPT, TPR = SC::TPR;
     __shared__ __attribute__((aligned(16))) float sPart[8 * SPW * C * 16];
-    __shared__ __attribute__((aligned(16))) float sU[C * DVS];
+    // U: fp32 [64][DVS], or (HL) transposed hi and lo bf16 planes [DVS][LDU]
+    constexpr int LDU = C + 8;
+    __shared__ __attribute__((aligned(16))) float sU[HL ? 4 : C * DVS];
+    __shared__ __attribute__((aligned(16))) bf16 sUt[HL ? 2 * DVS * LDU : 8];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -746,6 +804,7 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(const float* __restrict__ l
     // record entries are loaded one chunk ahead, each part right after its last use
     f32x4 Wv[4], GCv;
     float KRv[16], U0v[OPT];
+    bf16x8 KRh[2], KRl[2];  // (HL) KR[32 b2 + 8 g4 + e][16 st + l16], split
     auto rec_of = [&](int nn) { return loc + ((int64_t)bh * nch + nn) * R::SIZE; };
     auto pre_w = [&](int nn) {
         const float* rec = rec_of(nn);
@@ -756,11 +815,21 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(const float* __restrict__ l
     auto pre_u0 = [&](int nn) { load_n<OPT>(U0v, rec_of(nn) + R::OU0 + ri * DV + col0 + rc); };
     auto pre_kr = [&](int nn) {
         const float* rec = rec_of(nn);
+        if constexpr (HL) {
+            const bf16* kp = reinterpret_cast<const bf16*>(rec + R::OKRS);
 #pragma unroll
-        for (int j4 = 0; j4 < 4; ++j4) {  // KR[4 j + g4][16 st + l16], j = 0..15 (swizzled copy)
-            const f32x4 x = *reinterpret_cast<const f32x4*>(rec + R::OKRS + sw(16 * j4 + g4, st * 16 + l16));
+            for (int b2 = 0; b2 < 2; ++b2) {
+                const int u = hl_unit(32 * b2 + 8 * g4, st * 16 + l16);
+                KRh[b2] = *reinterpret_cast<const bf16x8*>(kp + u * 8);
+                KRl[b2] = *reinterpret_cast<const bf16x8*>(kp + C * DK + u * 8);
+            }
+        } else {
 #pragma unroll
-            for (int z = 0; z < 4; ++z) KRv[4 * j4 + z] = x[z];
+            for (int j4 = 0; j4 < 4; ++j4) {  // KR[4 j + g4][16 st + l16], j = 0..15 (swizzled copy)
+                const f32x4 x = *reinterpret_cast<const f32x4*>(rec + R::OKRS + sw(16 * j4 + g4, st * 16 + l16));
+#pragma unroll
+                for (int z = 0; z < 4; ++z) KRv[4 * j4 + z] = x[z];
+            }
         }
         GCv = *reinterpret_cast<const f32x4*>(rec + R::OGC + st * 16 + g4 * 4);
     };
@@ -831,7 +900,16 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(const float* __restrict__ l
 #pragma unroll
                 for (int o = 0; o < OPT; ++o) u[o] -= p[o];
             }
-            store_n<OPT>(sU + ri * DVS + rc, u);
+            if constexpr (HL) {
+#pragma unroll
+                for (int o = 0; o < OPT; ++o) {
+                    const bf16 h = (bf16)u[o];
+                    sUt[(rc + o) * LDU + ri] = h;
+                    sUt[DVS * LDU + (rc + o) * LDU + ri] = (bf16)(u[o] - (float)h);
+                }
+            } else {
+                store_n<OPT>(sU + ri * DVS + rc, u);
+            }
             if (t0 + ri < T) store_n<OPT>(u_out + base_v + (int64_t)(t0 + ri) * rv + col0 + rc, u);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -846,24 +924,16 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(const float* __restrict__ l
                 for (int r = 0; r < 4; ++r) a2[c][0][r] = S[c][r] * GCv[r];
                 a2[c][1] = zero4();
             }
-            if constexpr (HL) {  // slot (g4, e) of block b2: token 4 (8 b2 + e) + g4
+            if constexpr (HL) {  // slot (g4, e) of block b2: token 32 b2 + 8 g4 + e, split operands
 #pragma unroll
-                for (int b2 = 0; b2 < 2; ++b2) {
-                    float ka[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) ka[e] = KRv[8 * b2 + e];
-                    bf16x8 kh, kl;
-                    split_hl8(ka, kh, kl);
+                for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
                     for (int c = 0; c < SPW; ++c) {
-                        float ua[8];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) ua[e] = sU[(4 * (8 * b2 + e) + g4) * DVS + (cb + c) * 16 + l16];
-                        bf16x8 uh, ul;
-                        split_hl8(ua, uh, ul);
-                        a2[c][b2] = mf32(mf32(mf32(a2[c][b2], kh, uh), kh, ul), kl, uh);
+                        const bf16* up = sUt + ((cb + c) * 16 + l16) * LDU + 32 * b2 + 8 * g4;
+                        const bf16x8 uh = *reinterpret_cast<const bf16x8*>(up);
+                        const bf16x8 ul = *reinterpret_cast<const bf16x8*>(up + DVS * LDU);
+                        a2[c][b2] = mf32(mf32(mf32(a2[c][b2], KRh[b2], uh), KRh[b2], ul), KRl[b2], uh);
                     }
-                }
             } else {
 #pragma unroll
                 for (int j = 0; j < 16; ++j)
@@ -896,8 +966,12 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__
     constexpr int JW = C / KT;  // tokens of P^T dO in this wave's part
     constexpr int JS = JW / 4;  // their MFMA steps
     __shared__ __attribute__((aligned(16))) float sPart[8 * SPW * C * 16];
-    __shared__ __attribute__((aligned(16))) float sDU[C * DVS];
-    __shared__ __attribute__((aligned(16))) float sDO[2][C * DVS];
+    // dU and dO: fp32 [64][DVS], or (HL) transposed hi and lo bf16 planes [DVS][LDU]
+    constexpr int LDU = C + 8;
+    __shared__ __attribute__((aligned(16))) float sDU[HL ? 4 : C * DVS];
+    __shared__ __attribute__((aligned(16))) float sDO[2][HL ? 4 : C * DVS];
+    __shared__ __attribute__((aligned(16))) bf16 sDUt[HL ? 2 * DVS * LDU : 8];
+    __shared__ __attribute__((aligned(16))) bf16 sDOt[2][HL ? 2 * DVS * LDU : 8];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -926,6 +1000,7 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__
     }
     f32x4 KRv[4], GCv;
     float Pv[4][JS], dOp[SPW][JS], dOs[OPT], QGv[16], Wt[16], Tv[16];
+    bf16x8 QGh[2], QGl[2], Wh[2], Wl[2], Th[2], Tl[2];  // (HL) split, tokens 32 b2 + 8 g4 + e
     auto rec_of = [&](int nn) { return loc + ((int64_t)bh * nch + nn) * R::SIZE; };
     auto do_row = [&](int t) { return d_o + base_v + (int64_t)min(t, T - 1) * rv + col0; };
     auto pre_du = [&](int nn) {  // operands of the dU parts
@@ -953,6 +1028,18 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__
     };
     auto pre_ds = [&](int nn) {  // operands of the dS update
         const float* rec = rec_of(nn);
+        if constexpr (HL) {
+            const bf16* qp = reinterpret_cast<const bf16*>(rec + R::OQG);
+            const bf16* wp = reinterpret_cast<const bf16*>(rec + R::OWS);
+#pragma unroll
+            for (int b2 = 0; b2 < 2; ++b2) {
+                const int u = hl_unit(32 * b2 + 8 * g4, st * 16 + l16);
+                QGh[b2] = *reinterpret_cast<const bf16x8*>(qp + u * 8);
+                QGl[b2] = *reinterpret_cast<const bf16x8*>(qp + C * DK + u * 8);
+                Wh[b2] = *reinterpret_cast<const bf16x8*>(wp + u * 8);
+                Wl[b2] = *reinterpret_cast<const bf16x8*>(wp + C * DK + u * 8);
+            }
+        } else
 #pragma unroll
         for (int j4 = 0; j4 < 4; ++j4) {  // QG and W at [4 j + g4][16 st + l16] (swizzled copies)
             const f32x4 a = *reinterpret_cast<const f32x4*>(rec + R::OQG + sw(16 * j4 + g4, st * 16 + l16));
@@ -967,7 +1054,15 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__
     };
     auto pre_t = [&](int nn) {  // T^T operand of the dR tile: T[j][16 dri + m], j >= 16 dri
         const float* rec = rec_of(nn);
-        if (has_dr) {  // T[16 kb + 4 s + g4][16 dri + l16] (zero for kb < dri), swizzled copy
+        if (HL && has_dr) {  // T[32 b2 + 8 g4 + e][16 dri + l16], split
+            const bf16* tp = reinterpret_cast<const bf16*>(rec + R::OT);
+#pragma unroll
+            for (int b2 = 0; b2 < 2; ++b2) {
+                const int u = hl_unit(32 * b2 + 8 * g4, dri * 16 + l16);
+                Th[b2] = *reinterpret_cast<const bf16x8*>(tp + u * 8);
+                Tl[b2] = *reinterpret_cast<const bf16x8*>(tp + C * C + u * 8);
+            }
+        } else if (has_dr) {  // T[16 kb + 4 s + g4][16 dri + l16] (zero for kb < dri), swizzled copy
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
                 const f32x4 x = *reinterpret_cast<const f32x4*>(rec + R::OT + sw(16 * kb + g4, dri * 16 + l16));
@@ -985,6 +1080,7 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__
     for (int n = nch - 1; n >= 0; --n) {
         const int t0 = n * C, nn = max(n - 1, 0);
         float* sDOn = sDO[n & 1];
+        bf16* sDOtn = sDOt[n & 1];
         // dS' of this chunk, checkpoint for kernel 3
 #pragma unroll
         for (int c = 0; c < SPW; ++c) {
@@ -992,7 +1088,16 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__
 #pragma unroll
             for (int r = 0; r < 4; ++r) dst[(int64_t)r * DV] = dS[c][r];
         }
-        store_n<OPT>(sDOn + ri * DVS + rc, dOs);
+        if constexpr (HL) {
+#pragma unroll
+            for (int o = 0; o < OPT; ++o) {
+                const bf16 h = (bf16)dOs[o];
+                sDOtn[(rc + o) * LDU + ri] = h;
+                sDOtn[DVS * LDU + (rc + o) * LDU + ri] = (bf16)(dOs[o] - (float)h);
+            }
+        } else {
+            store_n<OPT>(sDOn + ri * DVS + rc, dOs);
+        }
         __builtin_amdgcn_sched_barrier(0);
         pre_do(nn);
         // this wave's parts of KR dS' (its 16 key rows) and of P^T dO (its JW tokens)
@@ -1055,7 +1160,16 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__
 #pragma unroll
                 for (int o = 0; o < OPT; ++o) u[o] += p[o];
             }
-            store_n<OPT>(sDU + ri * DVS + rc, u);
+            if constexpr (HL) {
+#pragma unroll
+                for (int o = 0; o < OPT; ++o) {
+                    const bf16 h = (bf16)u[o];
+                    sDUt[(rc + o) * LDU + ri] = h;
+                    sDUt[DVS * LDU + (rc + o) * LDU + ri] = (bf16)(u[o] - (float)h);
+                }
+            } else {
+                store_n<OPT>(sDU + ri * DVS + rc, u);
+            }
         }
         lds_barrier();
         // dS <- Gamma_C.dS' + QG^T dO - W^T dU
@@ -1063,34 +1177,19 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__
             f32x4 a2[SPW][2];
 #pragma unroll
             for (int c = 0; c < SPW; ++c) a2[c][0] = a2[c][1] = zero4();
-            if constexpr (HL) {  // slot (g4, e) of block b2: token 4 (8 b2 + e) + g4
+            if constexpr (HL) {  // slot (g4, e) of block b2: token 32 b2 + 8 g4 + e, split operands
 #pragma unroll
-                for (int b2 = 0; b2 < 2; ++b2) {
-                    float qa[8], wa[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        qa[e] = QGv[8 * b2 + e];
-                        wa[e] = Wt[8 * b2 + e];
-                    }
-                    bf16x8 qh, ql, wh, wl;
-                    split_hl8(qa, qh, ql);
-                    split_hl8(wa, wh, wl);
+                for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
                     for (int c = 0; c < SPW; ++c) {
-                        float oa[8], ua[8];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const int o = (4 * (8 * b2 + e) + g4) * DVS + (cb + c) * 16 + l16;
-                            oa[e] = sDOn[o];
-                            ua[e] = sDU[o];
-                        }
-                        bf16x8 oh, ol, uh, ul;
-                        split_hl8(oa, oh, ol);
-                        split_hl8(ua, uh, ul);
-                        a2[c][0] = mf32(mf32(mf32(a2[c][0], qh, oh), qh, ol), ql, oh);
-                        a2[c][1] = mf32(mf32(mf32(a2[c][1], wh, uh), wh, ul), wl, uh);
+                        const int o = ((cb + c) * 16 + l16) * LDU + 32 * b2 + 8 * g4;
+                        const bf16x8 oh = *reinterpret_cast<const bf16x8*>(sDOtn + o);
+                        const bf16x8 ol = *reinterpret_cast<const bf16x8*>(sDOtn + DVS * LDU + o);
+                        const bf16x8 uh = *reinterpret_cast<const bf16x8*>(sDUt + o);
+                        const bf16x8 ul = *reinterpret_cast<const bf16x8*>(sDUt + DVS * LDU + o);
+                        a2[c][0] = mf32(mf32(mf32(a2[c][0], QGh[b2], oh), QGh[b2], ol), QGl[b2], oh);
+                        a2[c][1] = mf32(mf32(mf32(a2[c][1], Wh[b2], uh), Wh[b2], ul), Wl[b2], uh);
                     }
-                }
             } else {
 #pragma unroll
                 for (int j = 0; j < 16; ++j)
@@ -1115,25 +1214,17 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__
             f32x4 acc[SPW][2];
 #pragma unroll
             for (int c = 0; c < SPW; ++c) acc[c][0] = acc[c][1] = zero4();
-            if constexpr (HL) {  // slot (g4, e) of block b2: token 4 (8 b2 + e) + g4; T is zero above
+            if constexpr (HL) {  // slot (g4, e) of block b2: token 32 b2 + 8 g4 + e; T is zero above
                                  // the diagonal, so block 0 adds nothing for row tiles 2 and 3
 #pragma unroll
                 for (int b2 = 0; b2 < 2; ++b2)
                     if (b2 == 1 || dri < 2) {
-                        float ta[8];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) ta[e] = Tv[8 * b2 + e];
-                        bf16x8 th, tl;
-                        split_hl8(ta, th, tl);
 #pragma unroll
                         for (int c = 0; c < SPW; ++c) {
-                            float ua[8];
-#pragma unroll
-                            for (int e = 0; e < 8; ++e)
-                                ua[e] = sDU[(4 * (8 * b2 + e) + g4) * DVS + (cb + c) * 16 + l16];
-                            bf16x8 uh, ul;
-                            split_hl8(ua, uh, ul);
-                            acc[c][b2] = mf32(mf32(mf32(acc[c][b2], th, uh), th, ul), tl, uh);
+                            const int o = ((cb + c) * 16 + l16) * LDU + 32 * b2 + 8 * g4;
+                            const bf16x8 uh = *reinterpret_cast<const bf16x8*>(sDUt + o);
+                            const bf16x8 ul = *reinterpret_cast<const bf16x8*>(sDUt + DVS * LDU + o);
+                            acc[c][b2] = mf32(mf32(mf32(acc[c][b2], Th[b2], uh), Th[b2], ul), Tl[b2], uh);
                         }
                     }
             } else {
