@@ -39,14 +39,17 @@
 //      with dS in MFMA accumulators, dS = Gamma_C.dS' + QG^T dO - W^T dU (KG^T T^T = W^T);
 //      stores dS' of every chunk, dR, and dS of the first chunk (the gradient of the initial
 //      state);
-//   3. bwd_chunk_kernel, one workgroup per (sequence, head, chunk): every gradient of the
-//      chunk's inputs, independently of the other chunks.
+//   3. bwd_chunk_kernel, runs of consecutive chunks of one (sequence, head) per workgroup:
+//      every gradient of each chunk's inputs, independently of the other chunks; the next
+//      chunk's first loads are in flight during the current chunk's last phase.
 // Products run on fp32 MFMA (v_mfma_f32_16x16x4_f32) with fp32 accumulation.
 //
 // Decays in kernels 0 and 3: a chunk whose whole-chunk decay stays >= e^-40 on every channel
 // pivots all factors at the chunk start (k / Gamma is then finite, and every masked product is
 // one MFMA pass); any other chunk forms its masked sums element by element from
 // e^{G_i - G_j}, which never exceeds 1.
+#include <type_traits>
+
 #include "gdn2_device.h"
 #include "gdn2_launch.h"
 
@@ -181,22 +184,35 @@ __device__ __forceinline__ void split_hl8(const float (&x)[8], bf16x8& hi, bf16x
 
 // This thread's L tokens of key channel c in the element phase, every load issued at once: a
 // token past the end reads the last token, and the caller zeroes it.
+// p advanced by a byte offset: with p uniform across the wave and the offset a 32-bit per-lane
+// value, the access takes a scalar base and one vector register for the address
+template <typename T>
+__device__ __forceinline__ T* at_byte(T* p, uint32_t off) {
+    return reinterpret_cast<T*>(reinterpret_cast<char*>(p) + off);
+}
+template <typename T>
+__device__ __forceinline__ const T* at_byte(const T* p, uint32_t off) {
+    return reinterpret_cast<const T*>(reinterpret_cast<const char*>(p) + off);
+}
+
 template <typename In, int L>
 struct KeyIn {
     float g[L];
     In q[L], k[L], b[L];
 };
+// tokens t0 .. t0 + L - 1 (the last token past the end) of channel ch; base and t0 uniform
+// across the wave, so each load takes a scalar row address and the lane's channel offset
 template <typename In, int L>
 __device__ __forceinline__ void load_key(KeyIn<In, L>& in, const In* __restrict__ q, const In* __restrict__ k,
                                          const In* __restrict__ b, const float* __restrict__ g, int64_t base,
-                                         int64_t rk, int t0, int T) {
+                                         int ch, int64_t rk, int t0, int T) {
 #pragma unroll
     for (int m = 0; m < L; ++m) {
         const int64_t o = base + (int64_t)min(t0 + m, T - 1) * rk;
-        in.g[m] = g[o];
-        in.q[m] = q[o];
-        in.k[m] = k[o];
-        in.b[m] = b[o];
+        in.g[m] = *at_byte(g + o, (uint32_t)ch * 4u);
+        in.q[m] = *at_byte(q + o, (uint32_t)ch * (uint32_t)sizeof(In));
+        in.k[m] = *at_byte(k + o, (uint32_t)ch * (uint32_t)sizeof(In));
+        in.b[m] = *at_byte(b + o, (uint32_t)ch * (uint32_t)sizeof(In));
     }
 }
 
@@ -338,7 +354,7 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
     Vec<In, 4> wr[NWV], vr[NWV];
     auto prefetch = [&](int nn) {
         const int tt0 = nn * C;
-        load_key<In, L>(in, q, k, bgate, log_alpha, base_k + ec_, rk, tt0 + etb_ * L, T);
+        load_key<In, L>(in, q, k, bgate, log_alpha, base_k, ec_, rk, tt0 + wave * 64 / DK * L, T);
 #pragma unroll
         for (int i = 0; i < NWV; ++i) {
             const int e = tid_ + i * NT, r = e / (DV / 4), c4 = (e % (DV / 4)) * 4;
@@ -1310,7 +1326,7 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
     const float* __restrict__ d_o, const float* __restrict__ s_ckpt, const float* __restrict__ ds_ckpt,
     const float* __restrict__ u_in, const float* __restrict__ dr_in, float* __restrict__ dq,
     float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dg, float* __restrict__ db,
-    float* __restrict__ dw, int T, int H) {
+    float* __restrict__ dw, int T, int H, int nper) {
     using G = GradCfg<In, DK, DV>;
     constexpr int TB = G::TB, L = G::L, KT = G::KT, TPW = G::TPW, ITS = G::ITS;
     constexpr int LDV = G::LDV, LDH = G::LDH, LDC = G::LDC, LDF = G::LDF, LDT = G::LDT;
@@ -1359,35 +1375,33 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
         return (sTOT[b * DK + c] - sG[i * LDF + c]) + sAFT[b * DK + c];
     };
 
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int tid_ = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid_ >> 6);
+    // a run of nper consecutive chunks of one (sequence, head) per workgroup
     const int nch = (T + C - 1) / C;
-    const int n = blockIdx.x % nch, bh = blockIdx.x / nch;
-    const int bi = bh / H, h = bh % H, t0 = n * C;
+    const int ngrp = (nch + nper - 1) / nper;
+    const int bh = blockIdx.x / ngrp, n0 = (blockIdx.x % ngrp) * nper, n1 = min(nch, n0 + nper);
+    const int bi = bh / H, h = bh % H;
     const int64_t rk = (int64_t)H * DK, rv = (int64_t)H * DV;
     const int64_t base_k = ((int64_t)bi * T * H + h) * DK;
     const int64_t base_v = ((int64_t)bi * T * H + h) * DV;
-    const float* Sg = s_ckpt + ((int64_t)bh * nch + n) * DK * DV;
-    const float* dSg = ds_ckpt + ((int64_t)bh * nch + n) * DK * DV;
+    auto state_of = [&](const float* base, int nn) { return base + ((int64_t)bh * nch + nn) * DK * DV; };
 
     // this wave's output tiles: channel column tile ct, token row tiles it0 + ITS j
     const int ct = wave % KT, it0 = wave / KT;
-    const int c = ct * 16 + l16;  // the channel of this lane's accumulator column
-
-    if (tid < DK) sXR[tid] = 0.f;
-    if (tid == 0) *sFLG = 0;
 
     constexpr int HV = DV / 2;
     constexpr int NSH = DK * HV / 4 / NT;  // float4 of a half of S (or dS') per thread
     static_assert(NSH * 4 * NT == DK * HV, "half split");
     f32x4 sv[NSH], dsv[NSH];
     float xd[NSH];  // this thread's part of sum_v dS'[r][v] S[r][v] for its rows
-    auto load_half = [&](f32x4 (&d)[NSH], const float* g, int hh) {
+    // (a wave-uniform row base plus a 32-bit lane offset for every global access below)
+    auto load_half = [&](int lane, f32x4 (&d)[NSH], const float* g, int hh) {
 #pragma unroll
         for (int i = 0; i < NSH; ++i) {
-            const int e = tid + i * NT, r = e / (HV / 4), c4 = (e % (HV / 4)) * 4;
-            d[i] = *reinterpret_cast<const f32x4*>(g + r * DV + hh * HV + c4);
+            const int rb = (wave * 64 + i * NT) / (HV / 4);
+            const uint32_t lo = ((lane / (HV / 4)) * DV + (lane % (HV / 4)) * 4) * 4;
+            d[i] = *reinterpret_cast<const f32x4*>(at_byte(g + rb * DV + hh * HV, lo));
         }
     };
 
@@ -1397,379 +1411,421 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
     static_assert(NP1 * 4 * NT == C * HV, "phase 1 split");
     f32x4 p1o[NP1], p1r[NP1], p1u[NP1];
     Vec<In, 4> p1w[NP1], p1v[NP1];
-    auto p1_load = [&](int hh) {  // rows past the end read the last token, zeroed in p1_use
+    auto p1_load = [&](int lane, int nn, int hh) {  // rows past the end read the last token, zeroed in p1_use
 #pragma unroll
         for (int x = 0; x < NP1; ++x) {
-            const int e = tid + x * NT, r = e / (HV / 4), c4 = hh * HV + (e % (HV / 4)) * 4;
-            const int64_t off = base_v + (int64_t)min(t0 + r, T - 1) * rv + c4;
-            p1o[x] = *reinterpret_cast<const f32x4*>(d_o + off);
-            p1r[x] = *reinterpret_cast<const f32x4*>(dr_in + off);
-            p1u[x] = *reinterpret_cast<const f32x4*>(u_in + off);
-            p1w[x] = load_vec<In, 4>(wgate + off);
-            p1v[x] = load_vec<In, 4>(v + off);
+            const int r0 = nn * C + (wave * 64 + x * NT) / (HV / 4);  // the wave's first row
+            const int u = min(r0, T - 1);
+            const int dl = min(r0 + lane / (HV / 4), T - 1) - u;      // the lane's row, from u
+            const int c4 = hh * HV + (lane % (HV / 4)) * 4;
+            const int64_t ro = base_v + (int64_t)u * rv;
+            const uint32_t lo = (uint32_t)dl * (uint32_t)rv + (uint32_t)c4;
+            p1o[x] = *reinterpret_cast<const f32x4*>(at_byte(d_o + ro, lo * 4));
+            p1r[x] = *reinterpret_cast<const f32x4*>(at_byte(dr_in + ro, lo * 4));
+            p1u[x] = *reinterpret_cast<const f32x4*>(at_byte(u_in + ro, lo * 4));
+            p1w[x] = load_vec<In, 4>(at_byte(wgate + ro, lo * (uint32_t)sizeof(In)));
+            p1v[x] = load_vec<In, 4>(at_byte(v + ro, lo * (uint32_t)sizeof(In)));
         }
     };
-    auto p1_use = [&](int hh) {
-#pragma unroll
-        for (int x = 0; x < NP1; ++x) {
-            const int e = tid + x * NT, r = e / (HV / 4), c4 = hh * HV + (e % (HV / 4)) * 4, t = t0 + r;
-            f32x4 o4 = zero4(), r4 = zero4(), u4 = zero4();
-            if (t < T) {
-                o4 = p1o[x];
-                r4 = p1r[x];
-                u4 = p1u[x];
-                const int64_t off = base_v + (int64_t)t * rv + c4;
-                f32x4 a4, b4;
-#pragma unroll
-                for (int z = 0; z < 4; ++z) {
-                    a4[z] = r4[z] * to_f32(p1w[x].v[z]);
-                    b4[z] = r4[z] * to_f32(p1v[x].v[z]);
+    // the first chunk's loads, in the order of use (a wait covers every load issued before the
+    // one it needs); every later chunk's come during phase 5 of the chunk before it
+    p1_load(tid_ & 63, n0, 0);
+    load_half(tid_ & 63, sv, state_of(s_ckpt, n0), 0);
+    load_half(tid_ & 63, dsv, state_of(ds_ckpt, n0), 0);
+    // one chunk; FULL: every token of the chunk is in the sequence, so no store is conditional
+    // (a conditional store would make the waits for the next chunk's loads, issued before it,
+    // drain the stores that follow them)
+    auto chunk = [&](const int n, auto full_c) __attribute__((always_inline)) {
+        constexpr bool FULL = decltype(full_c)::value;
+        // lane indices opaque per chunk: values derived from them (LDS addresses of the
+        // products) would otherwise be hoisted out of the loop and stay live across it
+        const int tid = opq(tid_);
+        const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+        const int c = ct * 16 + l16;  // the channel of this lane's accumulator column
+        auto p1_use = [&](int t0, int hh) {
+    #pragma unroll
+            for (int x = 0; x < NP1; ++x) {
+                const int e = tid + x * NT, r = e / (HV / 4), c4 = hh * HV + (e % (HV / 4)) * 4, t = t0 + r;
+                f32x4 o4 = zero4(), r4 = zero4(), u4 = zero4();
+                if (FULL || t < T) {
+                    o4 = p1o[x];
+                    r4 = p1r[x];
+                    u4 = p1u[x];
+                    // a wave-uniform row base plus a 32-bit lane offset
+                    const int64_t ro = base_v + (int64_t)(t0 + (wave * 64 + x * NT) / (HV / 4)) * rv;
+                    const uint32_t lo = ((uint32_t)(lane / (HV / 4)) * (uint32_t)rv + (uint32_t)c4) * 4u;
+                    f32x4 a4, b4;
+    #pragma unroll
+                    for (int z = 0; z < 4; ++z) {
+                        a4[z] = r4[z] * to_f32(p1w[x].v[z]);
+                        b4[z] = r4[z] * to_f32(p1v[x].v[z]);
+                    }
+                    *reinterpret_cast<f32x4*>(at_byte(dv + ro, lo)) = a4;
+                    *reinterpret_cast<f32x4*>(at_byte(dw + ro, lo)) = b4;
                 }
-                *reinterpret_cast<f32x4*>(dv + off) = a4;
-                *reinterpret_cast<f32x4*>(dw + off) = b4;
+                if constexpr (G::HL) {
+                    put_hl(G::DO, C * LDB, LDB, r, c4, o4);
+                    put_hl(G::DR, C * LDB, LDB, r, c4, r4);
+                    put_hl(G::UU, C * LDB, LDB, r, c4, u4);
+                } else {
+                    *reinterpret_cast<f32x4*>(sDO + r * LDV + c4) = o4;
+                    *reinterpret_cast<f32x4*>(sDR + r * LDV + c4) = r4;
+                    *reinterpret_cast<f32x4*>(sU + r * LDV + c4) = u4;
+                }
             }
-            if constexpr (G::HL) {
-                put_hl(G::DO, C * LDB, LDB, r, c4, o4);
-                put_hl(G::DR, C * LDB, LDB, r, c4, r4);
-                put_hl(G::UU, C * LDB, LDB, r, c4, u4);
-            } else {
-                *reinterpret_cast<f32x4*>(sDO + r * LDV + c4) = o4;
-                *reinterpret_cast<f32x4*>(sDR + r * LDV + c4) = r4;
-                *reinterpret_cast<f32x4*>(sU + r * LDV + c4) = u4;
-            }
-        }
-    };
-    // loads in the order of use (a wait covers every load issued before the one it needs)
-    p1_load(0);
-    load_half(sv, Sg, 0);
-    load_half(dsv, dSg, 0);
-    p1_use(0);
-    p1_load(1);
+        };
+        const int t0 = n * C;
+        const float* Sg = state_of(s_ckpt, n);
+        const float* dSg = state_of(ds_ckpt, n);
+        p1_use(t0, 0);
+        p1_load(lane, n, 1);
 
-    // ---- phase 2: X1 = dO S^T, X2 = dR S^T, X3 = U dS'^T over two halves of the value axis;
-    // each half of S and dS' goes through registers, loaded one step ahead ----
-    f32x4 X1[TPW], X2[TPW], X3[TPW];
-#pragma unroll
-    for (int j = 0; j < TPW; ++j) X1[j] = X2[j] = X3[j] = zero4();
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        lds_barrier();
-#pragma unroll
-        for (int i = 0; i < NSH; ++i) {
-            const int e = tid + i * NT, r = e / (HV / 4), c4 = (e % (HV / 4)) * 4;
-            if constexpr (G::HL) put_hl(G::SH, DK * LDS2, LDS2, r, c4, sv[i]);
-            else *reinterpret_cast<f32x4*>(sSH + r * LDH + c4) = sv[i];
-        }
-        lds_barrier();
-        {
-            f32x4 acc[2 * TPW];
-#pragma unroll
-            for (int j = 0; j < TPW; ++j) {
-                acc[j] = X1[j];
-                acc[TPW + j] = X2[j];
+        // ---- phase 2: X1 = dO S^T, X2 = dR S^T, X3 = U dS'^T over two halves of the value axis;
+        // each half of S and dS' goes through registers, loaded one step ahead ----
+        f32x4 X1[TPW], X2[TPW], X3[TPW];
+    #pragma unroll
+        for (int j = 0; j < TPW; ++j) X1[j] = X2[j] = X3[j] = zero4();
+    #pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            lds_barrier();
+            if (hh == 0) {  // every thread is past the previous chunk's reads of these
+                if (tid < DK) sXR[tid] = 0.f;
+                if (tid == 0) *sFLG = 0;
             }
+    #pragma unroll
+            for (int i = 0; i < NSH; ++i) {
+                const int e = tid + i * NT, r = e / (HV / 4), c4 = (e % (HV / 4)) * 4;
+                if constexpr (G::HL) put_hl(G::SH, DK * LDS2, LDS2, r, c4, sv[i]);
+                else *reinterpret_cast<f32x4*>(sSH + r * LDH + c4) = sv[i];
+            }
+            lds_barrier();
+            {
+                f32x4 acc[2 * TPW];
+    #pragma unroll
+                for (int j = 0; j < TPW; ++j) {
+                    acc[j] = X1[j];
+                    acc[TPW + j] = X2[j];
+                }
+                if constexpr (G::HL)
+                    mm_hl<2 * TPW, HV>(acc,
+                        [&](int t, int m, int kk, int pl) {
+                            return pl_of(t < TPW ? G::DO : G::DR, C * LDB, pl) +
+                                   ((it0 + ITS * (t % TPW)) * 16 + m) * LDB + hh * HV + kk;
+                        },
+                        [&](int, int kk, int nn, int pl) { return pl_of(G::SH, DK * LDS2, pl) + (ct * 16 + nn) * LDS2 + kk; },
+                        l16, g4);
+                else
+                    mm_n<2 * TPW, HV>(acc,
+                        [&](int t, int m, int kk) {
+                            const float* X = t < TPW ? sDO : sDR;
+                            return X[((it0 + ITS * (t % TPW)) * 16 + m) * LDV + hh * HV + kk];
+                        },
+                        [&](int, int kk, int nn) { return sSH[(ct * 16 + nn) * LDH + kk]; }, l16, g4);
+    #pragma unroll
+                for (int j = 0; j < TPW; ++j) {
+                    X1[j] = acc[j];
+                    X2[j] = acc[TPW + j];
+                }
+            }
+            lds_barrier();
+    #pragma unroll
+            for (int i = 0; i < NSH; ++i) {
+                const int e = tid + i * NT, r = e / (HV / 4), c4 = (e % (HV / 4)) * 4;
+                const f32x4 d4 = dsv[i], s4 = sv[i];
+                if constexpr (G::HL) put_hl(G::SH, DK * LDS2, LDS2, r, c4, d4);
+                else *reinterpret_cast<f32x4*>(sSH + r * LDH + c4) = d4;
+                const float p = d4[0] * s4[0] + d4[1] * s4[1] + d4[2] * s4[2] + d4[3] * s4[3];
+                xd[i] = hh == 0 ? p : xd[i] + p;
+            }
+            if (hh == 0) {
+                load_half(lane, sv, Sg, 1);
+                load_half(lane, dsv, dSg, 1);
+            }
+            lds_barrier();
             if constexpr (G::HL)
-                mm_hl<2 * TPW, HV>(acc,
+                mm_hl<TPW, HV>(X3,
                     [&](int t, int m, int kk, int pl) {
-                        return pl_of(t < TPW ? G::DO : G::DR, C * LDB, pl) +
-                               ((it0 + ITS * (t % TPW)) * 16 + m) * LDB + hh * HV + kk;
+                        return pl_of(G::UU, C * LDB, pl) + ((it0 + ITS * t) * 16 + m) * LDB + hh * HV + kk;
                     },
                     [&](int, int kk, int nn, int pl) { return pl_of(G::SH, DK * LDS2, pl) + (ct * 16 + nn) * LDS2 + kk; },
                     l16, g4);
             else
-                mm_n<2 * TPW, HV>(acc,
-                    [&](int t, int m, int kk) {
-                        const float* X = t < TPW ? sDO : sDR;
-                        return X[((it0 + ITS * (t % TPW)) * 16 + m) * LDV + hh * HV + kk];
-                    },
-                    [&](int, int kk, int nn) { return sSH[(ct * 16 + nn) * LDH + kk]; }, l16, g4);
-#pragma unroll
-            for (int j = 0; j < TPW; ++j) {
-                X1[j] = acc[j];
-                X2[j] = acc[TPW + j];
-            }
+                mm_n<TPW, HV>(X3, [&](int t, int m, int kk) { return sU[((it0 + ITS * t) * 16 + m) * LDV + hh * HV + kk]; },
+                              [&](int, int kk, int nn) { return sSH[(ct * 16 + nn) * LDH + kk]; }, l16, g4);
+            if (hh == 0) p1_use(t0, 1);  // the second value half of dO, dR, U (columns no product reads yet)
         }
-        lds_barrier();
-#pragma unroll
+        // the row sums: the HV / 4 threads of a row are consecutive lanes
+    #pragma unroll
         for (int i = 0; i < NSH; ++i) {
-            const int e = tid + i * NT, r = e / (HV / 4), c4 = (e % (HV / 4)) * 4;
-            const f32x4 d4 = dsv[i], s4 = sv[i];
-            if constexpr (G::HL) put_hl(G::SH, DK * LDS2, LDS2, r, c4, d4);
-            else *reinterpret_cast<f32x4*>(sSH + r * LDH + c4) = d4;
-            const float p = d4[0] * s4[0] + d4[1] * s4[1] + d4[2] * s4[2] + d4[3] * s4[3];
-            xd[i] = hh == 0 ? p : xd[i] + p;
+    #pragma unroll
+            for (int o = 1; o < HV / 4; o <<= 1) xd[i] += __shfl_xor(xd[i], o);
+            const int e = tid + i * NT;
+            if (e % (HV / 4) == 0) sXD[e / (HV / 4)] = xd[i];
         }
-        if (hh == 0) {
-            load_half(sv, Sg, 1);
-            load_half(dsv, dSg, 1);
+    #pragma unroll
+        for (int j = 0; j < TPW; ++j) X2[j] = -X2[j];  // -dR S^T
+        lds_barrier();
+
+        // the key-side inputs of the element phase, in flight during phase 3
+        const int ec = tid % DK, etb = tid / DK;
+        KeyIn<In, L> in;
+        load_key<In, L>(in, q, k, bgate, log_alpha, base_k, ec, rk, t0 + wave * 64 / DK * L, T);
+
+        // ---- phase 3: dA = -dR U^T (j < i), dP = dO U^T (j <= i); zero above the diagonal ----
+        {
+            // wave w: block pairs p = w and w + 8, (I, J) = (p / 4, p % 4), both dA and dP
+            f32x4 acc[4];
+    #pragma unroll
+            for (int t = 0; t < 4; ++t) acc[t] = zero4();
+            if constexpr (G::HL)
+                mm_hl<4, DV>(acc,
+                    [&](int t, int m, int kk, int pl) {
+                        const int p = wave + 8 * (t >> 1);
+                        return pl_of(t & 1 ? G::DO : G::DR, C * LDB, pl) + ((p >> 2) * 16 + m) * LDB + kk;
+                    },
+                    [&](int t, int kk, int nn, int pl) {
+                        const int p = wave + 8 * (t >> 1);
+                        return pl_of(G::UU, C * LDB, pl) + ((p & 3) * 16 + nn) * LDB + kk;
+                    }, l16, g4);
+            else
+                mm_n<4, DV>(acc,
+                    [&](int t, int m, int kk) {
+                        const int p = wave + 8 * (t >> 1);
+                        return (t & 1 ? sDO : sDR)[((p >> 2) * 16 + m) * LDV + kk];
+                    },
+                    [&](int t, int kk, int nn) {
+                        const int p = wave + 8 * (t >> 1);
+                        return sU[((p & 3) * 16 + nn) * LDV + kk];
+                    }, l16, g4);
+    #pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int p = wave + 8 * (t >> 1), I = p >> 2, J = p & 3, mat = t & 1;
+                float* dst = mat ? sDP : sDA;
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = I * 16 + g4 * 4 + r, jj = J * 16 + l16;
+                    const bool keep = mat ? (jj <= i) : (jj < i);
+                    dst[i * LDC + jj] = keep ? (mat ? acc[t][r] : -acc[t][r]) : 0.f;
+                }
+            }
+        }
+        lds_barrier();  // region 1 (dO, dR, U) is free from here on
+
+        // element phase: G (chunk-local cumulative log alpha) and the raw q, k, b of the chunk
+        {
+            float x[L];
+            float run = 0.f;
+    #pragma unroll
+            for (int m = 0; m < L; ++m) {
+                run += FULL || t0 + etb * L + m < T ? in.g[m] : 0.f;
+                x[m] = run;
+            }
+            sTOT[etb * DK + ec] = run;
+            lds_barrier();
+            float tot = 0.f, after = 0.f, oh = 0.f, ol = 0.f;
+    #pragma unroll
+            for (int j = 0; j < TB; ++j) {
+                const float vj = sTOT[j * DK + ec];
+                tot += vj;
+                if (j < etb) {
+                    float sv, ev;
+                    two_sum(oh, vj, sv, ev);
+                    oh = sv;
+                    ol += ev;
+                }
+                if (j > etb) after += vj;
+            }
+            sOFH[etb * DK + ec] = oh;
+            sOFL[etb * DK + ec] = ol;
+            sAFT[etb * DK + ec] = after;
+            if (etb == 0) {
+                sGC[ec] = exp_any(tot);
+                if (!(tot >= kMildLog)) *sFLG = 1;
+            }
+    #pragma unroll
+            for (int m = 0; m < L; ++m) {
+                const int i = etb * L + m, t = t0 + i;
+                In qv = from_f32<In>(0.f), kv = qv, bv = qv;
+                if (FULL || t < T) {
+                    qv = in.q[m];
+                    kv = in.k[m];
+                    bv = in.b[m];
+                }
+                sG[i * LDF + ec] = x[m];  // block-local
+                sQ[i * LDT + ec] = qv;
+                sK[i * LDT + ec] = kv;
+                sB[i * LDT + ec] = bv;
+            }
         }
         lds_barrier();
-        if constexpr (G::HL)
-            mm_hl<TPW, HV>(X3,
-                [&](int t, int m, int kk, int pl) {
-                    return pl_of(G::UU, C * LDB, pl) + ((it0 + ITS * t) * 16 + m) * LDB + hh * HV + kk;
-                },
-                [&](int, int kk, int nn, int pl) { return pl_of(G::SH, DK * LDS2, pl) + (ct * 16 + nn) * LDS2 + kk; },
-                l16, g4);
-        else
-            mm_n<TPW, HV>(X3, [&](int t, int m, int kk) { return sU[((it0 + ITS * t) * 16 + m) * LDV + hh * HV + kk]; },
-                          [&](int, int kk, int nn) { return sSH[(ct * 16 + nn) * LDH + kk]; }, l16, g4);
-        if (hh == 0) p1_use(1);  // the second value half of dO, dR, U (columns no product reads yet)
-    }
-    // the row sums: the HV / 4 threads of a row are consecutive lanes
-#pragma unroll
-    for (int i = 0; i < NSH; ++i) {
-#pragma unroll
-        for (int o = 1; o < HV / 4; o <<= 1) xd[i] += __shfl_xor(xd[i], o);
-        const int e = tid + i * NT;
-        if (e % (HV / 4) == 0) sXD[e / (HV / 4)] = xd[i];
-    }
-#pragma unroll
-    for (int j = 0; j < TPW; ++j) X2[j] = -X2[j];  // -dR S^T
-    lds_barrier();
+        const bool mild = *sFLG == 0;
 
-    // the key-side inputs of the element phase, in flight during phase 3
-    const int ec = tid % DK, etb = tid / DK;
-    KeyIn<In, L> in;
-    load_key<In, L>(in, q, k, bgate, log_alpha, base_k + ec, rk, t0 + etb * L, T);
-
-    // ---- phase 3: dA = -dR U^T (j < i), dP = dO U^T (j <= i); zero above the diagonal ----
-    {
-        // wave w: block pairs p = w and w + 8, (I, J) = (p / 4, p % 4), both dA and dP
-        f32x4 acc[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[t] = zero4();
-        if constexpr (G::HL)
-            mm_hl<4, DV>(acc,
-                [&](int t, int m, int kk, int pl) {
-                    const int p = wave + 8 * (t >> 1);
-                    return pl_of(t & 1 ? G::DO : G::DR, C * LDB, pl) + ((p >> 2) * 16 + m) * LDB + kk;
-                },
-                [&](int t, int kk, int nn, int pl) {
-                    const int p = wave + 8 * (t >> 1);
-                    return pl_of(G::UU, C * LDB, pl) + ((p & 3) * 16 + nn) * LDB + kk;
-                }, l16, g4);
-        else
-            mm_n<4, DV>(acc,
-                [&](int t, int m, int kk) {
-                    const int p = wave + 8 * (t >> 1);
-                    return (t & 1 ? sDO : sDR)[((p >> 2) * 16 + m) * LDV + kk];
-                },
-                [&](int t, int kk, int nn) {
-                    const int p = wave + 8 * (t >> 1);
-                    return sU[((p & 3) * 16 + nn) * LDV + kk];
-                }, l16, g4);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int p = wave + 8 * (t >> 1), I = p >> 2, J = p & 3, mat = t & 1;
-            float* dst = mat ? sDP : sDA;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = I * 16 + g4 * 4 + r, jj = J * 16 + l16;
-                const bool keep = mat ? (jj <= i) : (jj < i);
-                dst[i * LDC + jj] = keep ? (mat ? acc[t][r] : -acc[t][r]) : 0.f;
-            }
-        }
-    }
-    lds_barrier();  // region 1 (dO, dR, U) is free from here on
-
-    // element phase: G (chunk-local cumulative log alpha) and the raw q, k, b of the chunk
-    {
-        float x[L];
-        float run = 0.f;
-#pragma unroll
-        for (int m = 0; m < L; ++m) {
-            run += t0 + etb * L + m < T ? in.g[m] : 0.f;
-            x[m] = run;
-        }
-        sTOT[etb * DK + ec] = run;
-        lds_barrier();
-        float tot = 0.f, after = 0.f, oh = 0.f, ol = 0.f;
-#pragma unroll
-        for (int j = 0; j < TB; ++j) {
-            const float vj = sTOT[j * DK + ec];
-            tot += vj;
-            if (j < etb) {
-                float sv, ev;
-                two_sum(oh, vj, sv, ev);
-                oh = sv;
-                ol += ev;
-            }
-            if (j > etb) after += vj;
-        }
-        sOFH[etb * DK + ec] = oh;
-        sOFL[etb * DK + ec] = ol;
-        sAFT[etb * DK + ec] = after;
-        if (etb == 0) {
-            sGC[ec] = exp_any(tot);
-            if (!(tot >= kMildLog)) *sFLG = 1;
-        }
-#pragma unroll
-        for (int m = 0; m < L; ++m) {
-            const int i = etb * L + m, t = t0 + i;
-            In qv = from_f32<In>(0.f), kv = qv, bv = qv;
-            if (t < T) {
-                qv = in.q[m];
-                kv = in.k[m];
-                bv = in.b[m];
-            }
-            sG[i * LDF + ec] = x[m];  // block-local
-            sQ[i * LDT + ec] = qv;
-            sK[i * LDT + ec] = kv;
-            sB[i * LDT + ec] = bv;
-        }
-    }
-    lds_barrier();
-    const bool mild = *sFLG == 0;
-
-    // the G_C term of U dS'^T: sum_i k_ic e^{G_C - G_ic} X3_ic
-    {
-        float part = 0.f;
-#pragma unroll
-        for (int j = 0; j < TPW; ++j) {
-            const int it = it0 + ITS * j;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = it * 16 + g4 * 4 + r;
-                part += to_f32(sK[i * LDT + c]) * exp_any(Gsuf(i, c)) * X3[j][r];
-            }
-        }
-        part += __shfl_xor(part, 16);
-        part += __shfl_xor(part, 32);
-        if (g4 == 0) atomicAdd(sXR + c, part);
-    }
-
-    // ---- phase 4: the masked decay products; afterwards X1 = dq, X2 = d(kh), X3 = dk through
-    // the decays (without b.d(kh)) ----
-    if (mild) {
-        const float gc = sGC[c];
-#pragma unroll
-        for (int j = 0; j < TPW; ++j) X3[j] *= gc;
-        // blocks of 16 contraction tokens; lane group g4 takes the tokens 16 b + 4 g4 + s of
-        // block b at the four MFMA steps s (its factors for four tokens at once, and the dP, dA
-        // rows of X1, X2 as 16-byte reads)
-#pragma unroll
-        for (int b16 = 0; b16 < C / 16; ++b16) {
-            float ki[4], kg[4], qg[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int r = b16 * 16 + 4 * g4 + s;
-                const float Gr = Gof(r, c);
-                const float kr = to_f32(sK[r * LDT + c]);
-                const float ep = exp_any(Gr), en = exp_any(-Gr);
-                ki[s] = kr * en;                                // k / Gamma
-                kg[s] = to_f32(sB[r * LDT + c]) * kr * ep;      // kh.Gamma
-                qg[s] = to_f32(sQ[r * LDT + c]) * ep;           // q.Gamma
-            }
-#pragma unroll
+        // the G_C term of U dS'^T: sum_i k_ic e^{G_C - G_ic} X3_ic
+        {
+            float part = 0.f;
+    #pragma unroll
             for (int j = 0; j < TPW; ++j) {
                 const int it = it0 + ITS * j;
-                if (b16 <= it) {  // X1, X2: tokens up to i (dP, dA are zero above the diagonal)
-                    const f32x4 p4 = *reinterpret_cast<const f32x4*>(sDP + (it * 16 + l16) * LDC + b16 * 16 + 4 * g4);
-                    const f32x4 a4 = *reinterpret_cast<const f32x4*>(sDA + (it * 16 + l16) * LDC + b16 * 16 + 4 * g4);
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        X1[j] = mfma4(X1[j], p4[s], ki[s]);
-                        X2[j] = mfma4(X2[j], a4[s], ki[s]);
-                    }
-                }
-                if (b16 >= it) {  // X3: tokens from i on
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        const int r = b16 * 16 + 4 * g4 + s;
-                        X3[j] = mfma4(X3[j], sDA[r * LDC + it * 16 + l16], kg[s]);
-                        X3[j] = mfma4(X3[j], sDP[r * LDC + it * 16 + l16], qg[s]);
-                    }
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = it * 16 + g4 * 4 + r;
+                    part += to_f32(sK[i * LDT + c]) * exp_any(Gsuf(i, c)) * X3[j][r];
                 }
             }
+            part += __shfl_xor(part, 16);
+            part += __shfl_xor(part, 32);
+            if (g4 == 0) atomicAdd(sXR + c, part);
         }
-#pragma unroll
-        for (int j = 0; j < TPW; ++j) {
-            const int it = it0 + ITS * j;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float Gi = Gof(it * 16 + g4 * 4 + r, c);
-                const float ep = exp_any(Gi);
-                X1[j][r] *= ep;
-                X2[j][r] *= ep;
-                X3[j][r] *= exp_any(-Gi);
-            }
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < TPW; ++j) {
-            const int it = it0 + ITS * j;
-            for (int r = 0; r < 4; ++r) {
-                const int i = it * 16 + g4 * 4 + r;
-                float sq = 0.f, sh = 0.f, sk = 0.f;
-                for (int jj = 0; jj <= i; ++jj) {
-                    const float f = exp_any(Gdiff(i, jj, c)) * to_f32(sK[jj * LDT + c]);
-                    sq += sDP[i * LDC + jj] * f;
-                    sh += sDA[i * LDC + jj] * f;
-                }
-                for (int ii = i; ii < C; ++ii) {
-                    const float f = exp_any(Gdiff(ii, i, c));
-                    const float kh = to_f32(sB[ii * LDT + c]) * to_f32(sK[ii * LDT + c]);
-                    sk += (sDA[ii * LDC + i] * kh + sDP[ii * LDC + i] * to_f32(sQ[ii * LDT + c])) * f;
-                }
-                const float ep = exp_any(Gof(i, c));
-                X1[j][r] = ep * X1[j][r] + sq;
-                X2[j][r] = ep * X2[j][r] + sh;
-                X3[j][r] = exp_any(Gsuf(i, c)) * X3[j][r] + sk;
-            }
-        }
-    }
-    lds_barrier();  // dA, dP are consumed: region 2 takes dG
 
-    // ---- phase 5: dq, dk, db; the per-token decay gradient dG ----
-#pragma unroll
-    for (int j = 0; j < TPW; ++j) {
-        const int it = it0 + ITS * j;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = it * 16 + g4 * 4 + r, t = t0 + i;
-            const float qv = to_f32(sQ[i * LDT + c]), kv = to_f32(sK[i * LDT + c]), bv = to_f32(sB[i * LDT + c]);
-            const float dqv = X1[j][r], dkh = X2[j][r];
-            const float dkv = X3[j][r] + bv * dkh;
-            sDG[i * LDF + c] = qv * dqv + 2.f * bv * kv * dkh - kv * dkv;
-            if (t < T) {
-                const int64_t o = base_k + (int64_t)t * rk + c;
-                dq[o] = dqv;
-                dk[o] = dkv;
-                db[o] = kv * dkh;
+        // ---- phase 4: the masked decay products; afterwards X1 = dq, X2 = d(kh), X3 = dk through
+        // the decays (without b.d(kh)) ----
+        if (mild) {
+            const float gc = sGC[c];
+    #pragma unroll
+            for (int j = 0; j < TPW; ++j) X3[j] *= gc;
+            // blocks of 16 contraction tokens; lane group g4 takes the tokens 16 b + 4 g4 + s of
+            // block b at the four MFMA steps s (its factors for four tokens at once, and the dP, dA
+            // rows of X1, X2 as 16-byte reads)
+    #pragma unroll
+            for (int b16 = 0; b16 < C / 16; ++b16) {
+                float ki[4], kg[4], qg[4];
+    #pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int r = b16 * 16 + 4 * g4 + s;
+                    const float Gr = Gof(r, c);
+                    const float kr = to_f32(sK[r * LDT + c]);
+                    const float ep = exp_any(Gr), en = exp_any(-Gr);
+                    ki[s] = kr * en;                                // k / Gamma
+                    kg[s] = to_f32(sB[r * LDT + c]) * kr * ep;      // kh.Gamma
+                    qg[s] = to_f32(sQ[r * LDT + c]) * ep;           // q.Gamma
+                }
+    #pragma unroll
+                for (int j = 0; j < TPW; ++j) {
+                    const int it = it0 + ITS * j;
+                    if (b16 <= it) {  // X1, X2: tokens up to i (dP, dA are zero above the diagonal)
+                        const f32x4 p4 = *reinterpret_cast<const f32x4*>(sDP + (it * 16 + l16) * LDC + b16 * 16 + 4 * g4);
+                        const f32x4 a4 = *reinterpret_cast<const f32x4*>(sDA + (it * 16 + l16) * LDC + b16 * 16 + 4 * g4);
+    #pragma unroll
+                        for (int s = 0; s < 4; ++s) {
+                            X1[j] = mfma4(X1[j], p4[s], ki[s]);
+                            X2[j] = mfma4(X2[j], a4[s], ki[s]);
+                        }
+                    }
+                    if (b16 >= it) {  // X3: tokens from i on
+    #pragma unroll
+                        for (int s = 0; s < 4; ++s) {
+                            const int r = b16 * 16 + 4 * g4 + s;
+                            X3[j] = mfma4(X3[j], sDA[r * LDC + it * 16 + l16], kg[s]);
+                            X3[j] = mfma4(X3[j], sDP[r * LDC + it * 16 + l16], qg[s]);
+                        }
+                    }
+                }
+            }
+    #pragma unroll
+            for (int j = 0; j < TPW; ++j) {
+                const int it = it0 + ITS * j;
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float Gi = Gof(it * 16 + g4 * 4 + r, c);
+                    const float ep = exp_any(Gi);
+                    X1[j][r] *= ep;
+                    X2[j][r] *= ep;
+                    X3[j][r] *= exp_any(-Gi);
+                }
+            }
+        } else {
+    #pragma unroll
+            for (int j = 0; j < TPW; ++j) {
+                const int it = it0 + ITS * j;
+                for (int r = 0; r < 4; ++r) {
+                    const int i = it * 16 + g4 * 4 + r;
+                    float sq = 0.f, sh = 0.f, sk = 0.f;
+                    for (int jj = 0; jj <= i; ++jj) {
+                        const float f = exp_any(Gdiff(i, jj, c)) * to_f32(sK[jj * LDT + c]);
+                        sq += sDP[i * LDC + jj] * f;
+                        sh += sDA[i * LDC + jj] * f;
+                    }
+                    for (int ii = i; ii < C; ++ii) {
+                        const float f = exp_any(Gdiff(ii, i, c));
+                        const float kh = to_f32(sB[ii * LDT + c]) * to_f32(sK[ii * LDT + c]);
+                        sk += (sDA[ii * LDC + i] * kh + sDP[ii * LDC + i] * to_f32(sQ[ii * LDT + c])) * f;
+                    }
+                    const float ep = exp_any(Gof(i, c));
+                    X1[j][r] = ep * X1[j][r] + sq;
+                    X2[j][r] = ep * X2[j][r] + sh;
+                    X3[j][r] = exp_any(Gsuf(i, c)) * X3[j][r] + sk;
+                }
             }
         }
-    }
-    lds_barrier();
-    // reverse cumulative sum over the chunk, plus the G_C terms
-    {
-        float run = 0.f;
-#pragma unroll
-        for (int m = L - 1; m >= 0; --m) run += sDG[(etb * L + m) * LDF + ec];
-        sTOT[etb * DK + ec] = run;
-        lds_barrier();
-        float after = sXR[ec] + sGC[ec] * sXD[ec];
-#pragma unroll
-        for (int j = 0; j < TB; ++j)
-            if (j > etb) after += sTOT[j * DK + ec];
-        run = after;
-#pragma unroll
-        for (int m = L - 1; m >= 0; --m) {
-            const int i = etb * L + m, t = t0 + i;
-            run += sDG[i * LDF + ec];
-            if (t < T) dg[base_k + (int64_t)t * rk + ec] = run;
+        lds_barrier();  // dA, dP are consumed: region 2 takes dG
+        {  // the next chunk's first loads (the last chunk reloads its own: no branch, see the serial
+           // kernels), into registers free since phase 2
+            const int nn = min(n + 1, n1 - 1);
+            p1_load(lane, nn, 0);
+            load_half(lane, sv, state_of(s_ckpt, nn), 0);
+            load_half(lane, dsv, state_of(ds_ckpt, nn), 0);
         }
-    }
+
+        // ---- phase 5: dq, dk, db; the per-token decay gradient dG ----
+        // stores at a wave-uniform row base plus a 32-bit lane offset (row 4 g4 + r of the tile)
+        const uint32_t lo5 = ((uint32_t)(4 * g4) * (uint32_t)rk + (uint32_t)c) * 4u;
+    #pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int it = it0 + ITS * j;
+    #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = it * 16 + g4 * 4 + r, t = t0 + i;
+                const float qv = to_f32(sQ[i * LDT + c]), kv = to_f32(sK[i * LDT + c]), bv = to_f32(sB[i * LDT + c]);
+                const float dqv = X1[j][r], dkh = X2[j][r];
+                const float dkv = X3[j][r] + bv * dkh;
+                sDG[i * LDF + c] = qv * dqv + 2.f * bv * kv * dkh - kv * dkv;
+                if (FULL || t < T) {
+                    const int64_t ro = base_k + (int64_t)(t0 + it * 16 + r) * rk;
+                    *at_byte(dq + ro, lo5) = dqv;
+                    *at_byte(dk + ro, lo5) = dkv;
+                    *at_byte(db + ro, lo5) = kv * dkh;
+                }
+            }
+        }
+        lds_barrier();
+        // reverse cumulative sum over the chunk, plus the G_C terms
+        {
+            float run = 0.f;
+    #pragma unroll
+            for (int m = L - 1; m >= 0; --m) run += sDG[(etb * L + m) * LDF + ec];
+            sTOT[etb * DK + ec] = run;
+            lds_barrier();
+            float after = sXR[ec] + sGC[ec] * sXD[ec];
+    #pragma unroll
+            for (int j = 0; j < TB; ++j)
+                if (j > etb) after += sTOT[j * DK + ec];
+            run = after;
+            const int etbw = wave * 64 / DK;  // = etb: a wave's threads share their token block
+    #pragma unroll
+            for (int m = L - 1; m >= 0; --m) {
+                const int i = etb * L + m, t = t0 + etbw * L + m;
+                run += sDG[i * LDF + ec];
+                if (FULL || t < T) *at_byte(dg + base_k + (int64_t)t * rk, (uint32_t)ec * 4u) = run;
+            }
+        }
+    };
+    const int nfull = min(n1, T / C);  // chunks n0 .. nfull - 1 are full
+    for (int n = n0; n < nfull; ++n) chunk(n, std::true_type{});
+    if (nfull < n1) chunk(n1 - 1, std::false_type{});  // the sequence's last, partial chunk
 }
 
 
 template <typename In, int D>
 hipError_t launch_grad(const BwdArgs& a) {
-    const int64_t nch = (a.T + C - 1) / C;
-    hipLaunchKernelGGL((bwd_chunk_kernel<In, D, D>), dim3((unsigned)(a.B * a.H * nch)), dim3(NT), 0,
+    // runs of consecutive chunks, about one workgroup per compute unit
+    const int64_t bh = a.B * a.H, nch = (a.T + C - 1) / C;
+    const int64_t cus = a.cus > 0 ? a.cus : 1;
+    const int64_t nper = (bh * nch + cus - 1) / cus;
+    const int64_t ngrp = (nch + nper - 1) / nper;
+    hipLaunchKernelGGL((bwd_chunk_kernel<In, D, D>), dim3((unsigned)(bh * ngrp)), dim3(NT), 0,
                        (hipStream_t)a.stream, (const In*)a.q, (const In*)a.k, (const In*)a.v, a.log_alpha,
                        (const In*)a.b, (const In*)a.w, a.d_o, a.s_ckpt, a.ds_ckpt, a.u, a.dr, a.g_q, a.g_k,
-                       a.g_v, a.g_log_alpha, a.g_b, a.g_w, (int)a.T, (int)a.H);
+                       a.g_v, a.g_log_alpha, a.g_b, a.g_w, (int)a.T, (int)a.H, (int)nper);
     return hipGetLastError();
 }
 
