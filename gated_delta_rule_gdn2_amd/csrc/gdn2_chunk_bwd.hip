@@ -42,7 +42,10 @@
 //   3. bwd_chunk_kernel, runs of consecutive chunks of one (sequence, head) per workgroup:
 //      every gradient of each chunk's inputs, independently of the other chunks; the next
 //      chunk's first loads are in flight during the current chunk's last phase.
-// Products run on fp32 MFMA (v_mfma_f32_16x16x4_f32) with fp32 accumulation.
+// Precision: with fp32 inputs every product runs on fp32 MFMA (v_mfma_f32_16x16x4_f32); with
+// bf16 inputs the chunk-local kernel keeps fp32 MFMA, and the products of kernels 1-3 take bf16
+// hi/lo operands (three v_mfma_f32_16x16x32_bf16 per product, about 16 significant bits per
+// operand).  Accumulation is fp32 throughout.
 //
 // Decays in kernels 0 and 3: a chunk whose whole-chunk decay stays >= e^-40 on every channel
 // pivots all factors at the chunk start (k / Gamma is then finite, and every masked product is
@@ -182,8 +185,6 @@ __device__ __forceinline__ void split_hl8(const float (&x)[8], bf16x8& hi, bf16x
     }
 }
 
-// This thread's L tokens of key channel c in the element phase, every load issued at once: a
-// token past the end reads the last token, and the caller zeroes it.
 // p advanced by a byte offset: with p uniform across the wave and the offset a 32-bit per-lane
 // value, the access takes a scalar base and one vector register for the address
 template <typename T>
@@ -195,6 +196,8 @@ __device__ __forceinline__ const T* at_byte(const T* p, uint32_t off) {
     return reinterpret_cast<const T*>(reinterpret_cast<const char*>(p) + off);
 }
 
+// This thread's L tokens of key channel c in the element phase, every load issued at once: a
+// token past the end reads the last token, and the caller zeroes it.
 template <typename In, int L>
 struct KeyIn {
     float g[L];
@@ -1683,40 +1686,112 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
             const float gc = sGC[c];
     #pragma unroll
             for (int j = 0; j < TPW; ++j) X3[j] *= gc;
-            // blocks of 16 contraction tokens; lane group g4 takes the tokens 16 b + 4 g4 + s of
-            // block b at the four MFMA steps s (its factors for four tokens at once, and the dP, dA
-            // rows of X1, X2 as 16-byte reads)
+            if constexpr (G::HL) {
+                // bf16 hi/lo products over blocks of 32 contraction tokens: lane group g4 takes
+                // the tokens 32 b + 8 g4 + e (e = 0..7), its factors for those eight at once and
+                // the dP, dA rows of X1, X2 as two 16-byte reads; a block on the zero side of
+                // the diagonal for a row tile is skipped
     #pragma unroll
-            for (int b16 = 0; b16 < C / 16; ++b16) {
-                float ki[4], kg[4], qg[4];
+                for (int b32 = 0; b32 < C / 32; ++b32) {
+                    float ki[8], kg[8], qg[8];
     #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int r = b16 * 16 + 4 * g4 + s;
-                    const float Gr = Gof(r, c);
-                    const float kr = to_f32(sK[r * LDT + c]);
-                    const float ep = exp_any(Gr), en = exp_any(-Gr);
-                    ki[s] = kr * en;                                // k / Gamma
-                    kg[s] = to_f32(sB[r * LDT + c]) * kr * ep;      // kh.Gamma
-                    qg[s] = to_f32(sQ[r * LDT + c]) * ep;           // q.Gamma
-                }
+                    for (int e = 0; e < 8; ++e) {
+                        const int r = b32 * 32 + 8 * g4 + e;
+                        const float Gr = Gof(r, c);
+                        const float kr = to_f32(sK[r * LDT + c]);
+                        const float ep = exp_any(Gr), en = exp_any(-Gr);
+                        ki[e] = kr * en;                                // k / Gamma
+                        kg[e] = to_f32(sB[r * LDT + c]) * kr * ep;      // kh.Gamma
+                        qg[e] = to_f32(sQ[r * LDT + c]) * ep;           // q.Gamma
+                    }
+                    bf16x8 kih, kil, kgh, kgl, qgh, qgl;
+                    split_hl8(ki, kih, kil);
+                    split_hl8(kg, kgh, kgl);
+                    split_hl8(qg, qgh, qgl);
     #pragma unroll
-                for (int j = 0; j < TPW; ++j) {
-                    const int it = it0 + ITS * j;
-                    if (b16 <= it) {  // X1, X2: tokens up to i (dP, dA are zero above the diagonal)
-                        const f32x4 p4 = *reinterpret_cast<const f32x4*>(sDP + (it * 16 + l16) * LDC + b16 * 16 + 4 * g4);
-                        const f32x4 a4 = *reinterpret_cast<const f32x4*>(sDA + (it * 16 + l16) * LDC + b16 * 16 + 4 * g4);
+                    for (int j = 0; j < TPW; ++j) {
+                        const int it = it0 + ITS * j;
+                        if (2 * b32 <= it) {  // X1, X2: tokens up to the tile's rows
+                            const float* pr = sDP + (it * 16 + l16) * LDC + b32 * 32 + 8 * g4;
+                            const float* ar = sDA + (it * 16 + l16) * LDC + b32 * 32 + 8 * g4;
+                            const f32x4 p0 = *reinterpret_cast<const f32x4*>(pr);
+                            const f32x4 p1 = *reinterpret_cast<const f32x4*>(pr + 4);
+                            const f32x4 a0 = *reinterpret_cast<const f32x4*>(ar);
+                            const f32x4 a1 = *reinterpret_cast<const f32x4*>(ar + 4);
+                            float pv[8], av[8];
     #pragma unroll
-                        for (int s = 0; s < 4; ++s) {
-                            X1[j] = mfma4(X1[j], p4[s], ki[s]);
-                            X2[j] = mfma4(X2[j], a4[s], ki[s]);
+                            for (int e = 0; e < 4; ++e) {
+                                pv[e] = p0[e];
+                                pv[4 + e] = p1[e];
+                                av[e] = a0[e];
+                                av[4 + e] = a1[e];
+                            }
+                            bf16x8 ph, pl, ah, al;
+                            split_hl8(pv, ph, pl);
+                            split_hl8(av, ah, al);
+                            X1[j] = mf32(X1[j], ph, kih);
+                            X2[j] = mf32(X2[j], ah, kih);
+                            X1[j] = mf32(X1[j], ph, kil);
+                            X2[j] = mf32(X2[j], ah, kil);
+                            X1[j] = mf32(X1[j], pl, kih);
+                            X2[j] = mf32(X2[j], al, kih);
+                        }
+                        if (2 * b32 + 1 >= it) {  // X3: tokens from the tile's rows on
+                            float at[8], pt[8];
+    #pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                const int r = b32 * 32 + 8 * g4 + e;
+                                at[e] = sDA[r * LDC + it * 16 + l16];
+                                pt[e] = sDP[r * LDC + it * 16 + l16];
+                            }
+                            bf16x8 ath, atl, pth, ptl;
+                            split_hl8(at, ath, atl);
+                            split_hl8(pt, pth, ptl);
+                            X3[j] = mf32(X3[j], ath, kgh);
+                            X3[j] = mf32(X3[j], ath, kgl);
+                            X3[j] = mf32(X3[j], atl, kgh);
+                            X3[j] = mf32(X3[j], pth, qgh);
+                            X3[j] = mf32(X3[j], pth, qgl);
+                            X3[j] = mf32(X3[j], ptl, qgh);
                         }
                     }
-                    if (b16 >= it) {  // X3: tokens from i on
-    #pragma unroll
-                        for (int s = 0; s < 4; ++s) {
-                            const int r = b16 * 16 + 4 * g4 + s;
-                            X3[j] = mfma4(X3[j], sDA[r * LDC + it * 16 + l16], kg[s]);
-                            X3[j] = mfma4(X3[j], sDP[r * LDC + it * 16 + l16], qg[s]);
+                }
+            } else {
+                // blocks of 16 contraction tokens; lane group g4 takes the tokens 16 b + 4 g4 + s of
+                // block b at the four MFMA steps s (its factors for four tokens at once, and the dP, dA
+                // rows of X1, X2 as 16-byte reads)
+        #pragma unroll
+                for (int b16 = 0; b16 < C / 16; ++b16) {
+                    float ki[4], kg[4], qg[4];
+        #pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const int r = b16 * 16 + 4 * g4 + s;
+                        const float Gr = Gof(r, c);
+                        const float kr = to_f32(sK[r * LDT + c]);
+                        const float ep = exp_any(Gr), en = exp_any(-Gr);
+                        ki[s] = kr * en;                                // k / Gamma
+                        kg[s] = to_f32(sB[r * LDT + c]) * kr * ep;      // kh.Gamma
+                        qg[s] = to_f32(sQ[r * LDT + c]) * ep;           // q.Gamma
+                    }
+        #pragma unroll
+                    for (int j = 0; j < TPW; ++j) {
+                        const int it = it0 + ITS * j;
+                        if (b16 <= it) {  // X1, X2: tokens up to i (dP, dA are zero above the diagonal)
+                            const f32x4 p4 = *reinterpret_cast<const f32x4*>(sDP + (it * 16 + l16) * LDC + b16 * 16 + 4 * g4);
+                            const f32x4 a4 = *reinterpret_cast<const f32x4*>(sDA + (it * 16 + l16) * LDC + b16 * 16 + 4 * g4);
+        #pragma unroll
+                            for (int s = 0; s < 4; ++s) {
+                                X1[j] = mfma4(X1[j], p4[s], ki[s]);
+                                X2[j] = mfma4(X2[j], a4[s], ki[s]);
+                            }
+                        }
+                        if (b16 >= it) {  // X3: tokens from i on
+        #pragma unroll
+                            for (int s = 0; s < 4; ++s) {
+                                const int r = b16 * 16 + 4 * g4 + s;
+                                X3[j] = mfma4(X3[j], sDA[r * LDC + it * 16 + l16], kg[s]);
+                                X3[j] = mfma4(X3[j], sDP[r * LDC + it * 16 + l16], qg[s]);
+                            }
                         }
                     }
                 }
