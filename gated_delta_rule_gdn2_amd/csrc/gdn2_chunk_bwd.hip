@@ -350,7 +350,8 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
     const int LI = wave < 3 ? wave + 1 : (wave < 5 ? wave - 1 : 3);
     const int LJ = wave < 3 ? wave : (wave < 5 ? wave - 3 : 0);
 
-    const int ec_ = tid_ % DK, etb_ = tid_ / DK;
+    const int ec_ = tid_ % DK;
+    static_assert(DK % 64 == 0, "a wave's threads share one token block");
     constexpr int NWV = C * DV / 4 / NT;  // groups of 4 value columns per thread
     static_assert(NWV * 4 * NT == C * DV, "w.v split");
     KeyIn<In, L> in;
@@ -370,7 +371,8 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
     for (int n = n0; n < n1; ++n) {
         // lane indices opaque per chunk: loop-invariant values derived from them (masks, the
         // identity columns of the substitution) would otherwise stay live across the loop
-        const int l16 = opq(lane16), g4 = opq(grp4), ec = opq(ec_), etb = opq(etb_);
+        const int l16 = opq(lane16), g4 = opq(grp4), ec = opq(ec_);
+        const int etb = wave * 64 / DK;  // = thread / DK: the threads of a wave share a token block
         const int tid = opq(tid_), lane = tid & 63;
         const int t0 = n * C;
         float* rec = loc + ((int64_t)bh * nch + n) * R::SIZE;
@@ -425,31 +427,39 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
         const bool mild = *sFLG == 0;
         // element phase, pass 2: QG and KR = k.Gamma_C / Gamma (suffix sums) to the record;
         // operand tiles of A and P
-        float qgv[L], krv[L];
+        float qgv[L], krv[L], gav[L];
+        In qin[L], kin[L], bin[L];
+        float* const krow = rec + R::OKR + etb * L * DK;  // this wave's first token row of KR
 #pragma unroll
         for (int m = 0; m < L; ++m) {
-            const int i = etb * L + m, t = t0 + i;
-            In qv = from_f32<In>(0.f), kv = qv, bv = qv;
+            const int t = t0 + etb * L + m;
+            qin[m] = kin[m] = bin[m] = from_f32<In>(0.f);
             if (t < T) {
-                qv = in.q[m];
-                kv = in.k[m];
-                bv = in.b[m];
+                qin[m] = in.q[m];
+                kin[m] = in.k[m];
+                bin[m] = in.b[m];
             }
-            const float Gi = x[m] + off;
-            const float ga = exp_any(Gi);
-            const float qg = to_f32(qv) * ga;
-            qgv[m] = qg;
-            krv[m] = to_f32(kv) * exp_any((run - x[m]) + after);
-            rec[R::OKR + i * DK + ec] = krv[m];
-            if (mild) {
-                sKG[i * LDF + ec] = to_f32(bv) * to_f32(kv) * ga;
-                sKI[i * LDF + ec] = to_f32(kv) * exp_any(-Gi);
-                sQG[i * LDF + ec] = qg;
-            } else {
+            gav[m] = exp_any(x[m] + off);
+            qgv[m] = to_f32(qin[m]) * gav[m];
+            krv[m] = to_f32(kin[m]) * exp_any((run - x[m]) + after);
+            *at_byte(krow + m * DK, (uint32_t)ec * 4u) = krv[m];
+        }
+        if (mild) {
+#pragma unroll
+            for (int m = 0; m < L; ++m) {
+                const int i = etb * L + m;
+                sKG[i * LDF + ec] = to_f32(bin[m]) * to_f32(kin[m]) * gav[m];
+                sKI[i * LDF + ec] = to_f32(kin[m]) * exp_any(-(x[m] + off));
+                sQG[i * LDF + ec] = qgv[m];
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < L; ++m) {
+                const int i = etb * L + m;
                 sG[i * LDF + ec] = x[m];  // block-local
-                sRK[i * LDT + ec] = kv;
-                sRB[i * LDT + ec] = bv;
-                sRQ[i * LDT + ec] = qv;
+                sRK[i * LDT + ec] = kin[m];
+                sRB[i * LDT + ec] = bin[m];
+                sRQ[i * LDT + ec] = qin[m];
             }
         }
         if constexpr (G::HL) {  // split copies: this thread's tokens, eight at a time
@@ -1570,7 +1580,7 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
         lds_barrier();
 
         // the key-side inputs of the element phase, in flight during phase 3
-        const int ec = tid % DK, etb = tid / DK;
+        const int ec = tid % DK, etb = wave * 64 / DK;  // a wave's threads share a token block
         KeyIn<In, L> in;
         load_key<In, L>(in, q, k, bgate, log_alpha, base_k, ec, rk, t0 + wave * 64 / DK * L, T);
 
@@ -1875,10 +1885,9 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
             for (int j = 0; j < TB; ++j)
                 if (j > etb) after += sTOT[j * DK + ec];
             run = after;
-            const int etbw = wave * 64 / DK;  // = etb: a wave's threads share their token block
     #pragma unroll
             for (int m = L - 1; m >= 0; --m) {
-                const int i = etb * L + m, t = t0 + etbw * L + m;
+                const int i = etb * L + m, t = t0 + i;
                 run += sDG[i * LDF + ec];
                 if (FULL || t < T) *at_byte(dg + base_k + (int64_t)t * rk, (uint32_t)ec * 4u) = run;
             }
