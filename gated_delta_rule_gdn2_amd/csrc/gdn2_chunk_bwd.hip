@@ -196,6 +196,18 @@ __device__ __forceinline__ const T* at_byte(const T* p, uint32_t off) {
     return reinterpret_cast<const T*>(reinterpret_cast<const char*>(p) + off);
 }
 
+// Eight packed bf16 values split at n: the first n (n clamped to 0..8) in `first`, the others
+// in `rest`, zeros elsewhere (bit masks on the two 16-bit halves of each 32-bit word)
+__device__ __forceinline__ void take_first(const bf16x8& x, int n, bf16x8& first, bf16x8& rest) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_bit_cast(u32x4, x);
+    u32x4 m;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) m[q] = (2 * q < n ? 0xffffu : 0u) | (2 * q + 1 < n ? 0xffff0000u : 0u);
+    first = __builtin_bit_cast(bf16x8, v & m);
+    rest = __builtin_bit_cast(bf16x8, v & ~m);
+}
+
 // This thread's L tokens of key channel c in the element phase, every load issued at once: a
 // token past the end reads the last token, and the caller zeroes it.
 template <typename In, int L>
@@ -1318,7 +1330,11 @@ struct GradCfg {
     static constexpr int R1 = cmax(3 * MAT, BB + C * LDT * ES);
     // region 2: a half of S or dS' (phase 2); then dA, dP (phases 3-4); then dG (phase 5)
     static constexpr int SH = R1, DA = R1, DP = R1 + C * LDC * 4, DG = R1;
-    static constexpr int R2 = cmax(HL ? 2 * PS : DK * LDH * 4, cmax(2 * C * LDC * 4, C * LDF * 4));
+    // bf16 inputs, phases 3-4: dA and dP as two packed matrices of hi and lo planes [64][LDM],
+    // M1 = dP on and below the diagonal with dA^T above it, M2 = dA below with dP^T on and above
+    static constexpr int LDM = C + 8, PM = C * LDM * 2;
+    static constexpr int M1H = R1, M1L = R1 + PM, M2H = R1 + 2 * PM, M2L = R1 + 3 * PM;
+    static constexpr int R2 = cmax(HL ? cmax(2 * PS, 4 * PM) : cmax(DK * LDH * 4, 2 * C * LDC * 4), C * LDF * 4);
     static constexpr int GC = R1 + R2;        // [DK] Gamma_C
     static constexpr int XD = GC + DK * 4;    // [DK] sum_v dS'[c][v] S[c][v]
     static constexpr int XR = XD + DK * 4;    // [DK] sum_i KR_ic (U dS'^T)_ic
@@ -1373,6 +1389,11 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
         *reinterpret_cast<bf16x4*>(hi + npl) = l;
     };
     auto pl_of = [&](int off, int npl, int pl) { return reinterpret_cast<const bf16*>(smem + off) + pl * npl; };
+    // entry (a, b) of a packed matrix (bf16 inputs, phases 3-4) as hi + lo
+    auto pk = [&](int off, int a, int b) {
+        const bf16* x = reinterpret_cast<const bf16*>(smem + off) + a * G::LDM + b;
+        return (float)x[0] + (float)x[G::PM / 2];
+    };
     // G_i (chunk-local), G_i - G_j and G_C - G_i from the block-local tile (see two_sum)
     auto Gof = [&](int i, int c) {
         const int b = i / L;
@@ -1584,32 +1605,84 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
         KeyIn<In, L> in;
         load_key<In, L>(in, q, k, bgate, log_alpha, base_k, ec, rk, t0 + wave * 64 / DK * L, T);
 
-        // ---- phase 3: dA = -dR U^T (j < i), dP = dO U^T (j <= i); zero above the diagonal ----
-        {
-            // wave w: block pairs p = w and w + 8, (I, J) = (p / 4, p % 4), both dA and dP
+        // ---- phase 3: dA = -dR U^T (j < i), dP = dO U^T (j <= i) ----
+        if constexpr (G::HL) {
+            // the 20 lower 16 x 16 blocks (I >= J), u < 10 of dA and u >= 10 of dP, block u mod 10
+            // in the order (0,0) (1,0) (1,1) (2,0) ...; wave w takes u = w, w + 8, w + 16.  Each
+            // value is split once and written twice: into its own triangle of one packed matrix
+            // and transposed into the other's
+            auto blk = [](int u, int& I, int& J) {
+                const int x = u % 10;
+                I = x < 1 ? 0 : (x < 3 ? 1 : (x < 6 ? 2 : 3));
+                J = x - I * (I + 1) / 2;
+            };
+            f32x4 acc[3];
+    #pragma unroll
+            for (int t = 0; t < 3; ++t) acc[t] = zero4();
+            mm_hl<3, DV>(acc,
+                [&](int t, int m, int kk, int pl) {
+                    const int u = min(wave + 8 * t, 19);
+                    int I, J;
+                    blk(u, I, J);
+                    return pl_of(u >= 10 ? G::DO : G::DR, C * LDB, pl) + (I * 16 + m) * LDB + kk;
+                },
+                [&](int t, int kk, int nn, int pl) {
+                    const int u = min(wave + 8 * t, 19);
+                    int I, J;
+                    blk(u, I, J);
+                    return pl_of(G::UU, C * LDB, pl) + (J * 16 + nn) * LDB + kk;
+                }, l16, g4);
+            bf16* m1h = reinterpret_cast<bf16*>(smem + G::M1H);
+            bf16* m2h = reinterpret_cast<bf16*>(smem + G::M2H);
+            constexpr int PL = G::PM / 2;  // elements from a hi plane to its lo plane
+    #pragma unroll
+            for (int t = 0; t < 3; ++t) {
+                const int u = wave + 8 * t;
+                if (u >= 20) continue;
+                int I, J;
+                blk(u, I, J);
+                const bool isP = u >= 10;
+                const int jj = J * 16 + l16, i0 = I * 16 + 4 * g4;
+                f32x4 x = isP ? acc[t] : -acc[t];
+                bf16x4 h, l;
+                split_hl(x, h, l);
+                bf16* own = isP ? m1h : m2h;  // dP into M1 (j <= i), dA into M2 (j < i)
+                bf16* oth = isP ? m2h : m1h;  // transposed: dP^T into M2, dA^T into M1
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (isP ? jj <= i0 + r : jj < i0 + r) {
+                        own[(i0 + r) * G::LDM + jj] = h[r];
+                        own[(i0 + r) * G::LDM + jj + PL] = l[r];
+                    }
+                }
+                if (I > J) {  // the transposed block lies wholly in the other triangle
+                    *reinterpret_cast<bf16x4*>(oth + jj * G::LDM + i0) = h;
+                    *reinterpret_cast<bf16x4*>(oth + jj * G::LDM + i0 + PL) = l;
+                } else {
+    #pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if (isP ? jj <= i0 + r : jj < i0 + r) {
+                            oth[jj * G::LDM + i0 + r] = h[r];
+                            oth[jj * G::LDM + i0 + r + PL] = l[r];
+                        }
+                    }
+                }
+            }
+        } else {
+            // wave w: block pairs p = w and w + 8, (I, J) = (p / 4, p % 4), both dA and dP; zero
+            // above the diagonal
             f32x4 acc[4];
     #pragma unroll
             for (int t = 0; t < 4; ++t) acc[t] = zero4();
-            if constexpr (G::HL)
-                mm_hl<4, DV>(acc,
-                    [&](int t, int m, int kk, int pl) {
-                        const int p = wave + 8 * (t >> 1);
-                        return pl_of(t & 1 ? G::DO : G::DR, C * LDB, pl) + ((p >> 2) * 16 + m) * LDB + kk;
-                    },
-                    [&](int t, int kk, int nn, int pl) {
-                        const int p = wave + 8 * (t >> 1);
-                        return pl_of(G::UU, C * LDB, pl) + ((p & 3) * 16 + nn) * LDB + kk;
-                    }, l16, g4);
-            else
-                mm_n<4, DV>(acc,
-                    [&](int t, int m, int kk) {
-                        const int p = wave + 8 * (t >> 1);
-                        return (t & 1 ? sDO : sDR)[((p >> 2) * 16 + m) * LDV + kk];
-                    },
-                    [&](int t, int kk, int nn) {
-                        const int p = wave + 8 * (t >> 1);
-                        return sU[((p & 3) * 16 + nn) * LDV + kk];
-                    }, l16, g4);
+            mm_n<4, DV>(acc,
+                [&](int t, int m, int kk) {
+                    const int p = wave + 8 * (t >> 1);
+                    return (t & 1 ? sDO : sDR)[((p >> 2) * 16 + m) * LDV + kk];
+                },
+                [&](int t, int kk, int nn) {
+                    const int p = wave + 8 * (t >> 1);
+                    return sU[((p & 3) * 16 + nn) * LDV + kk];
+                }, l16, g4);
     #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int p = wave + 8 * (t >> 1), I = p >> 2, J = p & 3, mat = t & 1;
@@ -1721,48 +1794,48 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
     #pragma unroll
                     for (int j = 0; j < TPW; ++j) {
                         const int it = it0 + ITS * j;
-                        if (2 * b32 <= it) {  // X1, X2: tokens up to the tile's rows
-                            const float* pr = sDP + (it * 16 + l16) * LDC + b32 * 32 + 8 * g4;
-                            const float* ar = sDA + (it * 16 + l16) * LDC + b32 * 32 + 8 * g4;
-                            const f32x4 p0 = *reinterpret_cast<const f32x4*>(pr);
-                            const f32x4 p1 = *reinterpret_cast<const f32x4*>(pr + 4);
-                            const f32x4 a0 = *reinterpret_cast<const f32x4*>(ar);
-                            const f32x4 a1 = *reinterpret_cast<const f32x4*>(ar + 4);
-                            float pv[8], av[8];
-    #pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                pv[e] = p0[e];
-                                pv[4 + e] = p1[e];
-                                av[e] = a0[e];
-                                av[4 + e] = a1[e];
-                            }
-                            bf16x8 ph, pl, ah, al;
-                            split_hl8(pv, ph, pl);
-                            split_hl8(av, ah, al);
-                            X1[j] = mf32(X1[j], ph, kih);
-                            X2[j] = mf32(X2[j], ah, kih);
-                            X1[j] = mf32(X1[j], ph, kil);
-                            X2[j] = mf32(X2[j], ah, kil);
-                            X1[j] = mf32(X1[j], pl, kih);
-                            X2[j] = mf32(X2[j], al, kih);
-                        }
-                        if (2 * b32 + 1 >= it) {  // X3: tokens from the tile's rows on
-                            float at[8], pt[8];
-    #pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                const int r = b32 * 32 + 8 * g4 + e;
-                                at[e] = sDA[r * LDC + it * 16 + l16];
-                                pt[e] = sDP[r * LDC + it * 16 + l16];
-                            }
-                            bf16x8 ath, atl, pth, ptl;
-                            split_hl8(at, ath, atl);
-                            split_hl8(pt, pth, ptl);
-                            X3[j] = mf32(X3[j], ath, kgh);
-                            X3[j] = mf32(X3[j], ath, kgl);
-                            X3[j] = mf32(X3[j], atl, kgh);
-                            X3[j] = mf32(X3[j], pth, qgh);
-                            X3[j] = mf32(X3[j], pth, qgl);
-                            X3[j] = mf32(X3[j], ptl, qgh);
+                        // row i of M1 and M2 over this lane's eight tokens: below the diagonal M1 is
+                        // dP and M2 dA (X1, X2), above it M1 is dA^T and M2 dP^T (X3)
+                        const int row = (it * 16 + l16) * G::LDM + b32 * 32 + 8 * g4;
+                        const bf16* pm = reinterpret_cast<const bf16*>(smem + G::M1H) + row;
+                        const bf16x8 m1h = *reinterpret_cast<const bf16x8*>(pm);
+                        const bf16x8 m1l = *reinterpret_cast<const bf16x8*>(pm + G::PM / 2);
+                        const bf16x8 m2h = *reinterpret_cast<const bf16x8*>(pm + G::PM);
+                        const bf16x8 m2l = *reinterpret_cast<const bf16x8*>(pm + 3 * G::PM / 2);
+                        if (2 * b32 == (it & ~1)) {
+                            // the block on the diagonal: tokens r <= i (e <= n) to X1, r < i to X2
+                            const int n = it * 16 + l16 - b32 * 32 - 8 * g4;
+                            bf16x8 p1h, p1l, a1h, a1l, a2h, a2l, p2h, p2l;
+                            take_first(m1h, n + 1, p1h, a1h);
+                            take_first(m1l, n + 1, p1l, a1l);
+                            take_first(m2h, n, a2h, p2h);
+                            take_first(m2l, n, a2l, p2l);
+                            X1[j] = mf32(X1[j], p1h, kih);
+                            X2[j] = mf32(X2[j], a2h, kih);
+                            X1[j] = mf32(X1[j], p1h, kil);
+                            X2[j] = mf32(X2[j], a2h, kil);
+                            X1[j] = mf32(X1[j], p1l, kih);
+                            X2[j] = mf32(X2[j], a2l, kih);
+                            X3[j] = mf32(X3[j], a1h, kgh);
+                            X3[j] = mf32(X3[j], a1h, kgl);
+                            X3[j] = mf32(X3[j], a1l, kgh);
+                            X3[j] = mf32(X3[j], p2h, qgh);
+                            X3[j] = mf32(X3[j], p2h, qgl);
+                            X3[j] = mf32(X3[j], p2l, qgh);
+                        } else if (2 * b32 < it) {  // wholly below: X1, X2
+                            X1[j] = mf32(X1[j], m1h, kih);
+                            X2[j] = mf32(X2[j], m2h, kih);
+                            X1[j] = mf32(X1[j], m1h, kil);
+                            X2[j] = mf32(X2[j], m2h, kil);
+                            X1[j] = mf32(X1[j], m1l, kih);
+                            X2[j] = mf32(X2[j], m2l, kih);
+                        } else {  // wholly above: X3
+                            X3[j] = mf32(X3[j], m1h, kgh);
+                            X3[j] = mf32(X3[j], m1h, kgl);
+                            X3[j] = mf32(X3[j], m1l, kgh);
+                            X3[j] = mf32(X3[j], m2h, qgh);
+                            X3[j] = mf32(X3[j], m2h, qgl);
+                            X3[j] = mf32(X3[j], m2l, qgh);
                         }
                     }
                 }
@@ -1825,15 +1898,32 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
                 for (int r = 0; r < 4; ++r) {
                     const int i = it * 16 + g4 * 4 + r;
                     float sq = 0.f, sh = 0.f, sk = 0.f;
+                    // dP[i][jj], dA[i][jj] (jj <= i) and dA[ii][i], dP[ii][i] (ii >= i)
+                    auto dp_row = [&](int jj) {
+                        if constexpr (G::HL) return pk(G::M1H, i, jj);
+                        else return sDP[i * LDC + jj];
+                    };
+                    auto da_row = [&](int jj) {
+                        if constexpr (G::HL) return jj < i ? pk(G::M2H, i, jj) : 0.f;
+                        else return sDA[i * LDC + jj];
+                    };
+                    auto da_col = [&](int ii) {
+                        if constexpr (G::HL) return ii > i ? pk(G::M1H, i, ii) : 0.f;
+                        else return sDA[ii * LDC + i];
+                    };
+                    auto dp_col = [&](int ii) {
+                        if constexpr (G::HL) return pk(G::M2H, i, ii);
+                        else return sDP[ii * LDC + i];
+                    };
                     for (int jj = 0; jj <= i; ++jj) {
                         const float f = exp_any(Gdiff(i, jj, c)) * to_f32(sK[jj * LDT + c]);
-                        sq += sDP[i * LDC + jj] * f;
-                        sh += sDA[i * LDC + jj] * f;
+                        sq += dp_row(jj) * f;
+                        sh += da_row(jj) * f;
                     }
                     for (int ii = i; ii < C; ++ii) {
                         const float f = exp_any(Gdiff(ii, i, c));
                         const float kh = to_f32(sB[ii * LDT + c]) * to_f32(sK[ii * LDT + c]);
-                        sk += (sDA[ii * LDC + i] * kh + sDP[ii * LDC + i] * to_f32(sQ[ii * LDT + c])) * f;
+                        sk += (da_col(ii) * kh + dp_col(ii) * to_f32(sQ[ii * LDT + c])) * f;
                     }
                     const float ep = exp_any(Gof(i, c));
                     X1[j][r] = ep * X1[j][r] + sq;
