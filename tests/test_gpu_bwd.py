@@ -83,7 +83,7 @@ def test_bwd_single_token():
     check(run_bwd(inp), oracle_vjp(inp), TOL_F32, "T=1")
 
 
-@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64)])
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.bfloat16, 64), (torch.float32, 64)])
 def test_bwd_strong_decay_chunks(dtype, d):
     """log alpha in [-5, -1]: every chunk's decay is far below e^-40, so the per-chunk gradient
     kernel takes its element-by-element path."""
@@ -92,15 +92,16 @@ def test_bwd_strong_decay_chunks(dtype, d):
     check(run_bwd(inp), oracle_vjp(inp), TOL_F32 if dtype == torch.float32 else TOL_BF16, "strong decay")
 
 
-def test_bwd_mixed_chunk_kinds():
+@pytest.mark.parametrize("d", [128, 64])
+def test_bwd_mixed_chunk_kinds(d):
     """Chunks 1, 3 and 5 of each sequence take log alpha in [-3, -1] (whole-chunk decay far below
     e^-40, element-by-element path), the others the default [-0.2, -0.001] (pivoted path)."""
-    say("case: bwd mixed chunk kinds bf16 d128")
-    inp = make_case(torch.bfloat16, 128, 1, 512, 2, 309)
+    say("case: bwd mixed chunk kinds bf16 d%d" % d)
+    inp = make_case(torch.bfloat16, d, 1, 512, 2, 309)
     gen = torch.Generator("cpu").manual_seed(309)
     for n in (1, 3, 5):
-        inp["log_alpha"][:, n * 64:(n + 1) * 64] = -1.0 - 2.0 * torch.rand((1, 64, 2, 128), generator=gen)
-    G = inp["log_alpha"].double().reshape(1, 8, 64, 2, 128).sum(2)  # whole-chunk log decays
+        inp["log_alpha"][:, n * 64:(n + 1) * 64] = -1.0 - 2.0 * torch.rand((1, 64, 2, d), generator=gen)
+    G = inp["log_alpha"].double().reshape(1, 8, 64, 2, d).sum(2)  # whole-chunk log decays
     kinds = (G.min(-1).values >= -40.0)
     assert kinds.any() and (~kinds).any(), "expected both chunk kinds"
     check(run_bwd(inp), oracle_vjp(inp), TOL_BF16, "mixed chunks")
