@@ -857,51 +857,50 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
         // T = [[T_A, 0], [T_C, T_B]] with T_A = [[T_00, 0], [T_10, T_11]], T_B likewise, and
         // T_10 = -T_11 A_10 T_00, T_32 = -T_33 A_32 T_22, T_C = -T_B A_BA T_A.  The local store
         // holds -A, so every product below adds.  B operands that are columns of T come from T^T.
-        if (wave < 2) {
-            const int J = 2 * wave, Ib = J + 1;
-            const int tb = opq((l16 * LC + g4 * 4) * 2);
-            const Frag16<bf16> fa = load16(B16(G::AM + tb + (Ib * 16 * LC + J * 16) * 2));
-            const Frag16<bf16> fj = load16(B16(G::TTR + tb + (J * 16 * LC + J * 16) * 2));
-            const Frag16<bf16> ft = load16(B16(G::TR + tb + (Ib * 16 * LC + Ib * 16) * 2));
-            sched_fence();
-            f32x4 z = zero4();
-            mma16(z, fa, fj);
-            const Frag16<bf16> zf = frag16_from_acc<bf16>(z);
-            if (wave == 0) {
-                // T_10 in the orientation of T^T (lane (n, g): T_10[4 g + r][n]), T_10 rows scattered
-                f32x4 t = zero4();
-                mma16(t, ft, zf);
-                float x[4];
-                acc_to_array(t, x);
-                store_bf16<4>(B16(G::TTR + tb + (0 * LC + 16) * 2), x);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) *B16(G::TR + ((16 + 4 * g4 + r) * LC + l16) * 2) = (bf16)x[r];
-            } else {
-                // T_32 rows (lane (i, g): T_32[i][4 g + r])
-                f32x4 t = zero4();
-                mma16(t, zf, ft);
-                float x[4];
-                acc_to_array(t, x);
-                store_bf16<4>(B16(G::TR + tb + (48 * LC + 32) * 2), x);
-            }
-        }
-        lds_barrier();
         if (wave < 4) {
             // block (R, J) of T_C, one per wave: Z_xJ = (-A_x0) T_0J + (-A_x1) T_1J, then
             // T_2J = T_22 Z_2J and T_3J = T_32 Z_2J + T_33 Z_3J, formed transposed so that
-            // lane (i, g) holds a row: T_RJ[i][4 g + r]
+            // lane (i, g) holds a row: T_RJ[i][4 g + r].  T_10 (needed for J = 0) and T_32 (for
+            // R = 3) come from the diagonal blocks alone; the waves that need them form them here
+            // (waves 0 and 3 also store them for the W and U0 products), so no level of their own
+            // and no barrier sits between the diagonal blocks and T_C.
             const int J = wave & 1, R = 2 + (wave >> 1);
             const int tb = opq((l16 * LC + g4 * 4) * 2);
+            Frag16<bf16> t10, t32;
+            if (J == 0) {  // T_10 = T_11 (-A_10) T_00, lane (n, g): T_10[4 g + r][n] (T^T's orientation)
+                const Frag16<bf16> fa = load16(B16(G::AM + tb + (16 * LC) * 2));
+                const Frag16<bf16> fj = load16(B16(G::TTR + tb));
+                const Frag16<bf16> ft = load16(B16(G::TR + tb + (16 * LC + 16) * 2));
+                sched_fence();
+                f32x4 z = zero4(), t = zero4();
+                mma16(z, fa, fj);
+                mma16(t, ft, frag16_from_acc<bf16>(z));
+                t10 = frag16_from_acc<bf16>(t);
+                if (wave == 0) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) *B16(G::TR + ((16 + 4 * g4 + r) * LC + l16) * 2) = t10.v[r];
+                }
+            }
+            if (R == 3) {  // T_32 = T_33 (-A_32) T_22, lane (i, g): T_32[i][4 g + r]
+                const Frag16<bf16> fa = load16(B16(G::AM + tb + (48 * LC + 32) * 2));
+                const Frag16<bf16> fj = load16(B16(G::TTR + tb + (32 * LC + 32) * 2));
+                const Frag16<bf16> ft = load16(B16(G::TR + tb + (48 * LC + 48) * 2));
+                sched_fence();
+                f32x4 z = zero4(), t = zero4();
+                mma16(z, fa, fj);
+                mma16(t, frag16_from_acc<bf16>(z), ft);
+                t32 = frag16_from_acc<bf16>(t);
+                if (wave == 3) *reinterpret_cast<bf16x4*>(B16(G::TR + tb + (48 * LC + 32) * 2)) = t32.v;
+            }
             Frag16<bf16> tf[2], a2[2], a3[2];
 #pragma unroll
             for (int K = 0; K < 2; ++K) {
                 if (K < J) continue;
-                tf[K] = load16(B16(G::TTR + tb + (J * 16 * LC + K * 16) * 2));
+                tf[K] = (K == 1 && J == 0) ? t10 : load16(B16(G::TTR + tb + (J * 16 * LC + K * 16) * 2));
                 a2[K] = load16(B16(G::AM + tb + (32 * LC + K * 16) * 2));
                 a3[K] = load16(B16(G::AM + tb + (48 * LC + K * 16) * 2));
             }
             const Frag16<bf16> t22 = load16(B16(G::TR + tb + (32 * LC + 32) * 2));
-            const Frag16<bf16> t32 = load16(B16(G::TR + tb + (48 * LC + 32) * 2));
             const Frag16<bf16> t33 = load16(B16(G::TR + tb + (48 * LC + 48) * 2));
             sched_fence();
             f32x4 z2 = zero4(), z3 = zero4();
@@ -1133,7 +1132,9 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                 }
             }
         }
-        lds_barrier();
+        // No barrier here: the next chunk's first pass writes only the votes, the block decays
+        // and (w.v)^T, which nothing above reads, and the barrier after that pass keeps its
+        // operand tiles behind every wave's reads of U, P and KG^T here.
     }
 
     if (state_owner && final_state) {
