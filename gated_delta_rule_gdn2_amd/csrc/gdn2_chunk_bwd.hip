@@ -1511,8 +1511,6 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
         const int t0 = n * C;
         const float* Sg = state_of(s_ckpt, n);
         const float* dSg = state_of(ds_ckpt, n);
-        p1_use(t0, 0);
-        p1_load(lane, n, 1);
 
         // ---- phase 2: X1 = dO S^T, X2 = dR S^T, X3 = U dS'^T over two halves of the value axis;
         // each half of S and dS' goes through registers, loaded one step ahead ----
@@ -1525,6 +1523,8 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
             if (hh == 0) {  // every thread is past the previous chunk's reads of these
                 if (tid < DK) sXR[tid] = 0.f;
                 if (tid == 0) *sFLG = 0;
+                p1_use(t0, 0);  // region 1: the previous chunk's q, k, b are read
+                p1_load(lane, n, 1);
             }
     #pragma unroll
             for (int i = 0; i < NSH; ++i) {
@@ -1944,6 +1944,7 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
         // ---- phase 5: dq, dk, db; the per-token decay gradient dG ----
         // stores at a wave-uniform row base plus a 32-bit lane offset (row 4 g4 + r of the tile)
         const uint32_t lo5 = ((uint32_t)(4 * g4) * (uint32_t)rk + (uint32_t)c) * 4u;
+        float dgv[TPW][4];
     #pragma unroll
         for (int j = 0; j < TPW; ++j) {
             const int it = it0 + ITS * j;
@@ -1953,7 +1954,8 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
                 const float qv = to_f32(sQ[i * LDT + c]), kv = to_f32(sK[i * LDT + c]), bv = to_f32(sB[i * LDT + c]);
                 const float dqv = X1[j][r], dkh = X2[j][r];
                 const float dkv = X3[j][r] + bv * dkh;
-                sDG[i * LDF + c] = qv * dqv + 2.f * bv * kv * dkh - kv * dkv;
+                dgv[j][r] = qv * dqv + 2.f * bv * kv * dkh - kv * dkv;
+                if constexpr (KT != 8) sDG[i * LDF + c] = dgv[j][r];
                 if (FULL || t < T) {
                     const int64_t ro = base_k + (int64_t)(t0 + it * 16 + r) * rk;
                     *at_byte(dq + ro, lo5) = dqv;
@@ -1962,9 +1964,29 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(
                 }
             }
         }
-        lds_barrier();
         // reverse cumulative sum over the chunk, plus the G_C terms
-        {
+        if constexpr (KT == 8) {
+            // a wave holds all 64 tokens of its 16 channels (row tiles j, lane group g4 has tokens
+            // 16 j + 4 g4 + r): the sum runs in registers, over the lane's four tokens of a tile and
+            // across the four lane groups of the channel (lanes 16 apart)
+            float after = sXR[c] + sGC[c] * sXD[c];  // complete since the barrier after phase 4
+    #pragma unroll
+            for (int j = TPW - 1; j >= 0; --j) {
+                const float sj = (dgv[j][0] + dgv[j][1]) + (dgv[j][2] + dgv[j][3]);
+                const float s1 = __shfl_xor(sj, 16), s2 = __shfl_xor(sj, 32), s3 = __shfl_xor(sj, 48);
+                // the lane groups after g4: for g4 = 0 all three, 1: g4 ^ 2 and g4 ^ 3, 2: g4 ^ 1
+                const float later = g4 == 0 ? (s1 + s2) + s3 : (g4 == 1 ? s2 + s3 : (g4 == 2 ? s1 : 0.f));
+                float run = after + later;
+    #pragma unroll
+                for (int r = 3; r >= 0; --r) {
+                    run += dgv[j][r];
+                    if (FULL || t0 + j * 16 + 4 * g4 + r < T)
+                        *at_byte(dg + base_k + (int64_t)(t0 + j * 16 + r) * rk, lo5) = run;
+                }
+                after += (sj + s1) + (s2 + s3);
+            }
+        } else {
+            lds_barrier();
             float run = 0.f;
     #pragma unroll
             for (int m = L - 1; m >= 0; --m) run += sDG[(etb * L + m) * LDF + ec];
