@@ -358,9 +358,6 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
     const int64_t rk = (int64_t)H * DK, rv = (int64_t)H * DV;
     const int64_t base_k = ((int64_t)bi * T * H + h) * DK;
     const int64_t base_v = ((int64_t)bi * T * H + h) * DV;
-    // off-diagonal blocks of T: wave w < 6 forms block (LI, LJ) at level LI - LJ
-    const int LI = wave < 3 ? wave + 1 : (wave < 5 ? wave - 1 : 3);
-    const int LJ = wave < 3 ? wave : (wave < 5 ? wave - 3 : 0);
 
     const int ec_ = tid_ % DK;
     static_assert(DK % 64 == 0, "a wave's threads share one token block");
@@ -640,35 +637,68 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
             for (int r = 0; r < 4; ++r) Ab[(4 * g4 + r) * LDC + l16] = m[r];
         }
         lds_barrier();
-        // off-diagonal blocks, T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ, level by level; every
-        // wave first takes the blocks of A it needs, before the levels overwrite them
-        float ap[3][4];
-#pragma unroll
-        for (int kb = 0; kb < 3; ++kb)
-#pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
-                const int K = LJ + kb;
-                ap[kb][s4] = (wave < 6 && K < LI) ? sAT[(LI * 16 + l16) * LDC + K * 16 + g4 + 4 * s4] : 0.f;
+        // off-diagonal blocks of T through halves of 32 tokens: T = [[T_A, 0], [T_C, T_B]] with
+        // T_10 = -T_11 A_10 T_00, T_32 = -T_33 A_32 T_22 and the blocks of T_C from
+        // Z_xJ = sum_{K=J}^{1} A_xK T_KJ: T_2J = -T_22 Z_2J, T_3J = -T_33 (Z_3J + A_32 T_2J).
+        // Every wave first takes the rows of A it needs (T is formed in place over A); then wave
+        // (R, J) = (2 + w / 2, w % 2), w < 4, forms its block of T_C with T_10 and T_2J in its own
+        // registers, and waves 4 and 5 form and store T_10 and T_32: one step, no levels.
+        // Operands: a row of a 16 x 16 block, lane (m, g4) holding X[m][4 g4 + e], times a block
+        // that is a diagonal block of T in LDS or an accumulator (rows 4 g4 + r of column n).
+        {
+            auto arow = [&](int I, int J) {
+                return *reinterpret_cast<const f32x4*>(sAT + (I * 16 + l16) * LDC + J * 16 + 4 * g4);
+            };
+            auto times_diag = [&](f32x4 acc, const f32x4& x, int D) {  // acc + X T_DD
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) acc = mfma4(acc, x[e], sAT[(D * 16 + 4 * g4 + e) * LDC + D * 16 + l16]);
+                return acc;
+            };
+            auto times_acc = [&](f32x4 acc, const f32x4& x, const f32x4& z) {  // acc + X Z
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) acc = mfma4(acc, x[e], z[e]);
+                return acc;
+            };
+            auto neg_diag_times = [&](int D, const f32x4& z) {  // -T_DD Z
+                return -times_acc(zero4(), arow(D, D), z);
+            };
+            auto put = [&](int I, int J, const f32x4& t) {
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) sAT[(I * 16 + g4 * 4 + r) * LDC + J * 16 + l16] = t[r];
+            };
+            const int J = wave & 1, R = 2 + ((wave >> 1) & 1);
+            const bool tc = wave < 4, need10 = (tc && J == 0) || wave == 4;
+            f32x4 a10 = zero4(), a2J = zero4(), a21 = zero4(), a3J = zero4(), a31 = zero4(), a32 = zero4();
+            if (need10) a10 = arow(1, 0);
+            if (tc) {
+                a2J = arow(2, J);
+                if (J == 0) a21 = arow(2, 1);
+                if (R == 3) {
+                    a3J = arow(3, J);
+                    if (J == 0) a31 = arow(3, 1);
+                }
             }
-        lds_barrier();
-#pragma unroll
-        for (int d = 1; d <= 3; ++d) {
-            if (wave < 6 && LI - LJ == d) {
-                f32x4 z = zero4();
-#pragma unroll
-                for (int kb = 0; kb < 3; ++kb) {
-                    const int K = LJ + kb;
-                    if (K < LI) {
-#pragma unroll
-                        for (int s4 = 0; s4 < 4; ++s4)
-                            z = mfma4(z, ap[kb][s4], sAT[(K * 16 + g4 + 4 * s4) * LDC + LJ * 16 + l16]);
+            if ((tc && R == 3) || wave == 5) a32 = arow(3, 2);
+            lds_barrier();
+            if (need10 || tc) {
+                f32x4 t10 = zero4();
+                if (need10) t10 = neg_diag_times(1, times_diag(zero4(), a10, 0));
+                if (wave == 4) put(1, 0, t10);
+                if (tc) {
+                    f32x4 z2 = times_diag(zero4(), a2J, J);
+                    if (J == 0) z2 = times_acc(z2, a21, t10);
+                    const f32x4 t2 = neg_diag_times(2, z2);
+                    if (R == 2) {
+                        put(2, J, t2);
+                    } else {
+                        f32x4 z3 = times_diag(zero4(), a3J, J);
+                        if (J == 0) z3 = times_acc(z3, a31, t10);
+                        z3 = times_acc(z3, a32, t2);
+                        put(3, J, neg_diag_times(3, z3));
                     }
                 }
-                f32x4 tij = zero4();
-#pragma unroll
-                for (int e = 0; e < 4; ++e) tij = mfma4(tij, sAT[(LI * 16 + l16) * LDC + LI * 16 + 4 * g4 + e], z[e]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sAT[(LI * 16 + g4 * 4 + r) * LDC + LJ * 16 + l16] = -tij[r];
+            } else if (wave == 5) {
+                put(3, 2, neg_diag_times(3, times_diag(zero4(), a32, 2)));
             }
             lds_barrier();
         }
