@@ -636,11 +636,11 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) Ab[(4 * g4 + r) * LDC + l16] = m[r];
         }
-        lds_barrier();
         // off-diagonal blocks of T through halves of 32 tokens: T = [[T_A, 0], [T_C, T_B]] with
         // T_10 = -T_11 A_10 T_00, T_32 = -T_33 A_32 T_22 and the blocks of T_C from
         // Z_xJ = sum_{K=J}^{1} A_xK T_KJ: T_2J = -T_22 Z_2J, T_3J = -T_33 (Z_3J + A_32 T_2J).
-        // Every wave first takes the rows of A it needs (T is formed in place over A); then wave
+        // Every wave first takes the rows of A it needs (T is formed in place over A; the
+        // diagonal blocks above touch no off-diagonal block, so one barrier covers both); then wave
         // (R, J) = (2 + w / 2, w % 2), w < 4, forms its block of T_C with T_10 and T_2J in its own
         // registers, and waves 4 and 5 form and store T_10 and T_32: one step, no levels.
         // Operands: a row of a 16 x 16 block, lane (m, g4) holding X[m][4 g4 + e], times a block
@@ -679,7 +679,7 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
                 }
             }
             if ((tc && R == 3) || wave == 5) a32 = arow(3, 2);
-            lds_barrier();
+            lds_barrier();  // T's diagonal blocks complete, every row of A taken
             if (need10 || tc) {
                 f32x4 t10 = zero4();
                 if (need10) t10 = neg_diag_times(1, times_diag(zero4(), a10, 0));
