@@ -107,22 +107,25 @@ def test_bwd_mixed_chunk_kinds(d):
     check(run_bwd(inp), oracle_vjp(inp), TOL_BF16, "mixed chunks")
 
 
-def test_bwd_chunk_runs_with_partial_tail():
-    """Enough chunks that the per-chunk gradient kernel walks runs of several consecutive chunks
-    per workgroup (8 heads x 72 chunks over the compute units), the last run ending in a partial
-    chunk (T = 71 x 64 + 10), with element-by-element chunks (log alpha in [-3, -1]) inside runs
-    and as the partial chunk; every gradient of every head against the oracle."""
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64)])
+def test_bwd_chunk_runs_with_partial_tail(dtype, d):
+    """Enough chunks that the chunk-local and per-chunk gradient kernels walk runs of several
+    consecutive chunks per workgroup (8 heads x 72 chunks over the compute units), the last run
+    ending in a partial chunk (T = 71 x 64 + 10), with element-by-element chunks (log alpha in
+    [-3, -1]) inside runs and as the partial chunk; every gradient of every head against the
+    oracle."""
     B, T, H = 1, 71 * 64 + 10, 8
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     nch = (T + 63) // 64
     nper = (B * H * nch + cus - 1) // cus
-    say("case: bwd chunk runs bf16 d128 B%d T%d H%d (%d chunks per run on %d CUs)" % (B, T, H, nper, cus))
-    inp = make_case(torch.bfloat16, 128, B, T, H, 313)
+    say("case: bwd chunk runs %s d%d B%d T%d H%d (%d chunks per run on %d CUs)" % (dtype, d, B, T, H, nper, cus))
+    inp = make_case(dtype, d, B, T, H, 313)
     gen = torch.Generator("cpu").manual_seed(313)
     for n in (2, 5, 40, 70, 71):
         t1 = min(T, (n + 1) * 64)
-        inp["log_alpha"][:, n * 64:t1] = -1.0 - 2.0 * torch.rand((B, t1 - n * 64, H, 128), generator=gen)
-    check(run_bwd(inp), oracle_vjp(inp), TOL_BF16, "chunk runs, partial tail")
+        inp["log_alpha"][:, n * 64:t1] = -1.0 - 2.0 * torch.rand((B, t1 - n * 64, H, d), generator=gen)
+    check(run_bwd(inp), oracle_vjp(inp), TOL_F32 if dtype == torch.float32 else TOL_BF16,
+          "chunk runs, partial tail")
 
 
 def test_bwd_without_initial_state_grad():
