@@ -1358,7 +1358,9 @@ struct GradCfg {
     static constexpr int DO = 0, DR = MAT, UU = 2 * MAT;
     static constexpr int GG = 0, QQ = C * LDF * 4, KK = QQ + C * LDT * ES, BB = KK + C * LDT * ES;
     static constexpr int R1 = cmax(3 * MAT, BB + C * LDT * ES);
-    // region 2: a half of S or dS' (phase 2); then dA, dP (phases 3-4); then dG (phase 5)
+    // region 2: a half of S or dS' (phase 2); then dA, dP (phases 3-4: fp32 tiles, or with bf16
+    // inputs the packed planes below); then dG (phase 5, when a wave does not hold every token of
+    // its channels)
     static constexpr int SH = R1, DA = R1, DP = R1 + C * LDC * 4, DG = R1;
     // bf16 inputs, phases 3-4: dA and dP as two packed matrices of hi and lo planes [64][LDM],
     // M1 = dP on and below the diagonal with dA^T above it, M2 = dA below with dP^T on and above
