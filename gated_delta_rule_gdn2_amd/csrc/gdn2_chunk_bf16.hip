@@ -787,15 +787,14 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
             // single pivot at the chunk start: A = BG KI^T, P = QG KI^T on the lower blocks
             if (wave < 4) {
                 // diagonal block I = wave: A_II in both orientations, then its inverse
-                f32x4 nt = zero4(), nn = zero4(), pd = zero4();
+                f32x4 nt = zero4(), nn = zero4();
                 const int rk = opq(((wave * 16 + l16) * LDK + g4 * 8) * 2);
                 const int rkx = opq(rk + G::RX);
-                Frag<bf16> fk[DK / 32], fa[DK / 32], fq[DK / 32];
+                Frag<bf16> fk[DK / 32], fa[DK / 32];
 #pragma unroll
                 for (int kk = 0; kk < DK / 32; ++kk) {
                     fk[kk] = load_contig(B16(rkx + C * LDK * 2 + kk * 64));
                     fa[kk] = load_contig(B16(rkx + kk * 64));
-                    fq[kk] = load_contig(B16(rk + kk * 64));
                 }
                 sched_fence();
 #pragma unroll
@@ -804,19 +803,34 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                     mma(nn, fa[kk], fk[kk]);  // lane holds A[4 g4 + r][l16]
                 }
 #pragma unroll
-                for (int kk = 0; kk < DK / 32; ++kk) mma(pd, fk[kk], fq[kk]);  // P[l16][4 g4 + r]
-                float pp[4];
-#pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int j = 4 * g4 + r;
                     nt[r] = j < l16 ? nt[r] : 0.f;
                     nn[r] = j > l16 ? nn[r] : 0.f;
-                    pp[r] = j <= l16 ? pd[r] : 0.f;
                 }
-                const int idx = (wave * 16 + l16) * LC + wave * 16 + g4 * 4;
-                store_bf16_split<4>(sPh + idx, sPl + idx, pp);
                 store_tdiag<G>(smem, wave, l16, g4, unit_lower_inverse(nt, nn, l16, g4));
-            } else if (wave < 7) {
+            } else if (wave == 7) {
+                // the diagonal blocks of P, so that waves 0-3 go straight to their inverses
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    const int rk = opq(((I * 16 + l16) * LDK + g4 * 8) * 2);
+                    Frag<bf16> fk[DK / 32], fq[DK / 32];
+#pragma unroll
+                    for (int kk = 0; kk < DK / 32; ++kk) {
+                        fk[kk] = load_contig(B16(rk + G::RX + C * LDK * 2 + kk * 64));
+                        fq[kk] = load_contig(B16(rk + kk * 64));
+                    }
+                    sched_fence();
+                    f32x4 pd = zero4();
+#pragma unroll
+                    for (int kk = 0; kk < DK / 32; ++kk) mma(pd, fk[kk], fq[kk]);  // P[l16][4 g4 + r]
+                    float pp[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) pp[r] = 4 * g4 + r <= l16 ? pd[r] : 0.f;
+                    const int idx = (I * 16 + l16) * LC + I * 16 + g4 * 4;
+                    store_bf16_split<4>(sPh + idx, sPl + idx, pp);
+                }
+            } else {
                 // off-diagonal pairs, two per wave sharing a block row or column:
                 // wave 4: (1,0) (2,0); wave 5: (2,1) (3,1); wave 6: (3,0) (3,2)
                 const int rl = opq((l16 * LDK + g4 * 8) * 2);
