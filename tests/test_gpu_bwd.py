@@ -107,7 +107,7 @@ def test_bwd_mixed_chunk_kinds(d):
     check(run_bwd(inp), oracle_vjp(inp), TOL_BF16, "mixed chunks")
 
 
-@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64)])
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.bfloat16, 64), (torch.float32, 64)])
 def test_bwd_chunk_runs_with_partial_tail(dtype, d):
     """Enough chunks that the chunk-local and per-chunk gradient kernels walk runs of several
     consecutive chunks per workgroup (8 heads x 72 chunks over the compute units), the last run
