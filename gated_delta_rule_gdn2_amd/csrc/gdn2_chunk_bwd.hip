@@ -451,7 +451,7 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
             gav[m] = exp_any(x[m] + off);
             qgv[m] = to_f32(qin[m]) * gav[m];
             krv[m] = to_f32(kin[m]) * exp_any((run - x[m]) + after);
-            *at_byte(krow + m * DK, (uint32_t)ec * 4u) = krv[m];
+            if constexpr (!G::HL) *at_byte(krow + m * DK, (uint32_t)ec * 4u) = krv[m];  // (bf16: split copy only)
         }
         if (mild) {
 #pragma unroll
@@ -785,7 +785,7 @@ __global__ __launch_bounds__(NT) void bwd_local_kernel(
                     const f32x4 val = *reinterpret_cast<const f32x4*>(tile + row * 16 + q4);
                     float* dst = ct < KT ? rec + R::OW + (I * 16 + row) * DK + ct * 16 + q4
                                          : rec + R::OU0 + (I * 16 + row) * DV + (ct - KT) * 16 + q4;
-                    *reinterpret_cast<f32x4*>(dst) = val;
+                    if (!G::HL || ct >= KT) *reinterpret_cast<f32x4*>(dst) = val;  // (bf16: W split only)
                     if constexpr (G::HL) {
                         if (ct < KT) {  // W split: lane (plane, half, column) writes rows 8 half + e
                             const int hf = (lane >> 4) & 1, pl = lane >> 5;
@@ -847,6 +847,11 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(const float* __restrict__ l
     constexpr int LDU = C + 8;
     __shared__ __attribute__((aligned(16))) float sU[HL ? 4 : C * DVS];
     __shared__ __attribute__((aligned(16))) bf16 sUt[HL ? 2 * DVS * LDU : 8];
+    // (HL) this wave's 16 columns of W (its key rows of the state) for all 64 tokens, hi and lo
+    // planes [64][LWT], staged from the record's split copy (tokens contiguous) so that a lane
+    // reads four consecutive keys of a token
+    constexpr int LWT = 20;
+    __shared__ __attribute__((aligned(16))) bf16 sWt[HL ? 8 * 2 * C * LWT : 8];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -874,14 +879,37 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(const float* __restrict__ l
     }
     // record entries are loaded one chunk ahead, each part right after its last use
     f32x4 Wv[4], GCv;
+    bf16x8 Wu[2][2];  // (HL) split units of W: tokens 8 (g4 + 4 u) .. + 7 of key 16 st + l16
     float KRv[16], U0v[OPT];
     bf16x8 KRh[2], KRl[2];  // (HL) KR[32 b2 + 8 g4 + e][16 st + l16], split
     auto rec_of = [&](int nn) { return loc + ((int64_t)bh * nch + nn) * R::SIZE; };
     auto pre_w = [&](int nn) {
         const float* rec = rec_of(nn);
+        if constexpr (HL) {  // the wave's units are contiguous: hl_unit(8 (g4 + 4 u), 16 st + l16)
+            const bf16* wp = reinterpret_cast<const bf16*>(rec + R::OWS) + (st * 128 + lane) * 8;
 #pragma unroll
-        for (int it = 0; it < 4; ++it)
-            Wv[it] = *reinterpret_cast<const f32x4*>(rec + R::OW + (it * 16 + l16) * DK + st * 16 + g4 * 4);
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int pl = 0; pl < 2; ++pl) Wu[u][pl] = *reinterpret_cast<const bf16x8*>(wp + u * 512 + pl * C * DK);
+        } else {
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                Wv[it] = *reinterpret_cast<const f32x4*>(rec + R::OW + (it * 16 + l16) * DK + st * 16 + g4 * 4);
+        }
+    };
+    bf16* const wt = sWt + wave * 2 * C * LWT;
+    auto stage_w = [&]() {  // (HL) the units to the wave's tile: token rows, key columns
+        if constexpr (HL) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) wt[pl * C * LWT + (8 * (g4 + 4 * u) + e) * LWT + l16] = Wu[u][pl][e];
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's writes before its reads
+            __builtin_amdgcn_wave_barrier();
+            asm volatile("" ::: "memory");
+        }
     };
     auto pre_u0 = [&](int nn) { load_n<OPT>(U0v, rec_of(nn) + R::OU0 + ri * DV + col0 + rc); };
     auto pre_kr = [&](int nn) {
@@ -905,6 +933,7 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(const float* __restrict__ l
         GCv = *reinterpret_cast<const f32x4*>(rec + R::OGC + st * 16 + g4 * 4);
     };
     pre_w(0);
+    stage_w();
     pre_u0(0);
     pre_kr(0);
     // The prefetches are issued on every path (the last chunk loads its own record again): a
@@ -933,8 +962,9 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(const float* __restrict__ l
                 for (int c = 0; c < SPW; ++c) split_hl(S[c], sh[c], sl[c]);
 #pragma unroll
                 for (int it = 0; it < 4; ++it) {
-                    bf16x4 wh, wl;
-                    split_hl(Wv[it], wh, wl);
+                    const bf16* wr = wt + (it * 16 + l16) * LWT + 4 * g4;
+                    const bf16x4 wh = *reinterpret_cast<const bf16x4*>(wr);
+                    const bf16x4 wl = *reinterpret_cast<const bf16x4*>(wr + C * LWT);
 #pragma unroll
                     for (int c = 0; c < SPW; ++c)
                         acc[c][it] = mf16(mf16(mf16(acc[c][it], wh, sh[c]), wh, sl[c]), wl, sh[c]);
@@ -1020,6 +1050,7 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(const float* __restrict__ l
         }
         __builtin_amdgcn_sched_barrier(0);
         pre_kr(nn);
+        stage_w();  // the next chunk's W, loaded after this chunk's W S
     }
 }
 
@@ -1043,6 +1074,11 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__
     __shared__ __attribute__((aligned(16))) float sDO[2][HL ? 4 : C * DVS];
     __shared__ __attribute__((aligned(16))) bf16 sDUt[HL ? 2 * DVS * LDU : 8];
     __shared__ __attribute__((aligned(16))) bf16 sDOt[2][HL ? 2 * DVS * LDU : 8];
+    // (HL) this wave's 16 columns of KR (its key rows of dS') for all 64 tokens, hi and lo planes
+    // [64][LKT], staged from the record's split copy (tokens contiguous) so that a lane reads four
+    // consecutive keys of a token
+    constexpr int LKT = 20;
+    __shared__ __attribute__((aligned(16))) bf16 sKt[HL ? 8 * 2 * C * LKT : 8];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1070,15 +1106,24 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__
         }
     }
     f32x4 KRv[4], GCv;
+    bf16x8 Ku[2][2];  // (HL) split units of KR: tokens 8 (g4 + 4 u) .. + 7 of key 16 st + l16
     float Pv[4][JS], dOp[SPW][JS], dOs[OPT], QGv[16], Wt[16], Tv[16];
     bf16x8 QGh[2], QGl[2], Wh[2], Wl[2], Th[2], Tl[2];  // (HL) split, tokens 32 b2 + 8 g4 + e
     auto rec_of = [&](int nn) { return loc + ((int64_t)bh * nch + nn) * R::SIZE; };
     auto do_row = [&](int t) { return d_o + base_v + (int64_t)min(t, T - 1) * rv + col0; };
     auto pre_du = [&](int nn) {  // operands of the dU parts
         const float* rec = rec_of(nn);
+        if constexpr (HL) {  // the wave's units are contiguous: hl_unit(8 (g4 + 4 u), 16 st + l16)
+            const bf16* kp = reinterpret_cast<const bf16*>(rec + R::OKRS) + (st * 128 + lane) * 8;
 #pragma unroll
-        for (int it = 0; it < 4; ++it)
-            KRv[it] = *reinterpret_cast<const f32x4*>(rec + R::OKR + (it * 16 + l16) * DK + st * 16 + g4 * 4);
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int pl = 0; pl < 2; ++pl) Ku[u][pl] = *reinterpret_cast<const bf16x8*>(kp + u * 512 + pl * C * DK);
+        } else {
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                KRv[it] = *reinterpret_cast<const f32x4*>(rec + R::OKR + (it * 16 + l16) * DK + st * 16 + g4 * 4);
+        }
         // P[st JW + 4 s + g4][16 it + l16], s = 0..JS-1: consecutive in the swizzled copy
 #pragma unroll
         for (int it = 0; it < 4; ++it) load_n<JS>(Pv[it], rec + R::OP + sw(st * JW + g4, it * 16 + l16));
@@ -1142,7 +1187,22 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__
             }
         }
     };
+    bf16* const kt = sKt + wave * 2 * C * LKT;
+    auto stage_kr = [&]() {  // (HL) the units to the wave's tile: token rows, key columns
+        if constexpr (HL) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) kt[pl * C * LKT + (8 * (g4 + 4 * u) + e) * LKT + l16] = Ku[u][pl][e];
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's writes before its reads
+            __builtin_amdgcn_wave_barrier();
+            asm volatile("" ::: "memory");
+        }
+    };
     pre_du(nch - 1);
+    stage_kr();
     pre_do(nch - 1);
     pre_ds(nch - 1);
     pre_t(nch - 1);
@@ -1184,8 +1244,9 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__
                 for (int c = 0; c < SPW; ++c) split_hl(dS[c], sh[c], sl[c]);
 #pragma unroll
                 for (int it = 0; it < 4; ++it) {
-                    bf16x4 kh, kl;
-                    split_hl(KRv[it], kh, kl);
+                    const bf16* kr = kt + (it * 16 + l16) * LKT + 4 * g4;
+                    const bf16x4 kh = *reinterpret_cast<const bf16x4*>(kr);
+                    const bf16x4 kl = *reinterpret_cast<const bf16x4*>(kr + C * LKT);
 #pragma unroll
                     for (int c = 0; c < SPW; ++c)
                         acc[c][it] = mf16(mf16(mf16(acc[c][it], kh, sh[c]), kh, sl[c]), kl, sh[c]);
@@ -1322,6 +1383,7 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__
         }
         __builtin_amdgcn_sched_barrier(0);
         pre_t(nn);
+        stage_kr();  // the next chunk's KR, loaded after this chunk's partial products
     }
     if (d_initial) {
 #pragma unroll
