@@ -196,6 +196,35 @@ __device__ __forceinline__ const T* at_byte(const T* p, uint32_t off) {
     return reinterpret_cast<const T*>(reinterpret_cast<const char*>(p) + off);
 }
 
+// Writes a wave's split units of one 16-key column block into its LDS tile of token rows,
+// [2][C][LD] bf16 (hi plane, then lo): U[u][pl] holds tokens 8 (g4 + 4 u) .. + 7 of key l16.
+// The lanes of each even/odd pair (keys 2m and 2m + 1) swap half of their tokens through a
+// DPP quad permutation, so that a lane writes four-byte key pairs (tokens 0..3 of its unit from
+// the even lane, 4..7 from the odd one) instead of two-byte elements.  Every lane of the wave
+// must be active.
+template <int LD>
+__device__ __forceinline__ void stage_key_pairs(bf16* tile, const bf16x8 (&U)[2][2], int l16, int g4) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const bool odd = l16 & 1;
+    const int m = l16 >> 1;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl) {
+            const u32x4 w = __builtin_bit_cast(u32x4, U[u][pl]);  // word k: tokens 2k (low), 2k + 1
+            unsigned* dst = reinterpret_cast<unsigned*>(tile + pl * C * LD + (8 * (g4 + 4 * u) + 4 * odd) * LD) + m;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const unsigned mine = odd ? w[2 + q] : w[q];
+                const unsigned give = odd ? w[q] : w[2 + q];
+                const unsigned got = (unsigned)__builtin_amdgcn_update_dpp(0, (int)give, 0xB1, 0xF, 0xF, false);
+                const unsigned lo = odd ? got : mine, hi = odd ? mine : got;  // keys 2m, 2m + 1
+                dst[(2 * q) * (LD / 2)] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+                dst[(2 * q + 1) * (LD / 2)] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+            }
+        }
+}
+
 // Eight packed bf16 values split at n: the first n (n clamped to 0..8) in `first`, the others
 // in `rest`, zeros elsewhere (bit masks on the two 16-bit halves of each 32-bit word)
 __device__ __forceinline__ void take_first(const bf16x8& x, int n, bf16x8& first, bf16x8& rest) {
@@ -900,12 +929,7 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(const float* __restrict__ l
     bf16* const wt = sWt + wave * 2 * C * LWT;
     auto stage_w = [&]() {  // (HL) the units to the wave's tile: token rows, key columns
         if constexpr (HL) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int pl = 0; pl < 2; ++pl)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) wt[pl * C * LWT + (8 * (g4 + 4 * u) + e) * LWT + l16] = Wu[u][pl][e];
+            stage_key_pairs<LWT>(wt, Wu, l16, g4);
             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's writes before its reads
             __builtin_amdgcn_wave_barrier();
             asm volatile("" ::: "memory");
@@ -1190,12 +1214,7 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const float* __restrict__
     bf16* const kt = sKt + wave * 2 * C * LKT;
     auto stage_kr = [&]() {  // (HL) the units to the wave's tile: token rows, key columns
         if constexpr (HL) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int pl = 0; pl < 2; ++pl)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) kt[pl * C * LKT + (8 * (g4 + 4 * u) + e) * LKT + l16] = Ku[u][pl][e];
+            stage_key_pairs<LKT>(kt, Ku, l16, g4);
             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's writes before its reads
             __builtin_amdgcn_wave_barrier();
             asm volatile("" ::: "memory");
