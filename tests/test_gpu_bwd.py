@@ -174,3 +174,25 @@ def test_fwdbwd_workload_sampled():
     got = {n: torch.stack([g[n][b, :, h] for b, h in pairs])[:, :, None] for n in GRADS}
     got["d_initial_state"] = torch.stack([g["d_initial_state"][b, h] for b, h in pairs])[:, None]
     check(got, ref, TOL_BF16, "fwdbwd sampled")
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64)])
+def test_bwd_caller_workspace_and_outputs(dtype, d):
+    """A caller's workspace and gradient buffers, filled with NaN bytes first and reused by a
+    smaller second call, give bit for bit the gradients of calls that allocate their own:
+    nothing reads a workspace slot it has not written, and every output element is written."""
+    cases = [make_case(dtype, d, 2, 300, 2, 314), make_case(dtype, d, 1, 70, 3, 315)]
+    need = max(gdn2.chunk_bwd_workspace_bytes(*c["q"].shape[:3], d, d) for c in cases)
+    say("case: bwd caller workspace %s d%d (%d bytes, NaN-filled)" % (dtype, d, need))
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    names = GRADS + ("d_initial_state",)
+    for inp in cases:
+        ref = run_bwd(inp)
+        x = to_dev(inp)
+        grads = {n: torch.full_like(ref[n], float("nan")) for n in names}
+        g = gdn2.chunk_bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], x["do"], x["s0"], x["dsT"],
+                           workspace=ws, grads=grads)
+        torch.cuda.synchronize()
+        for n in names:
+            assert g[n] is grads[n], n
+            assert torch.equal(g[n], ref[n]), n

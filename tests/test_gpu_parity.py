@@ -300,3 +300,18 @@ def test_decode_bf16_output_is_fp32_output_rounded_once():
                            out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert torch.equal(o16, o32.to(torch.bfloat16)) and torch.equal(st1, st2)
+
+
+@pytest.mark.parametrize("dtype,dk", [(torch.bfloat16, 128), (torch.float32, 64)])
+def test_caller_outputs_are_fully_written(dtype, dk):
+    """Output buffers passed in, filled with NaN first, come back bit for bit equal to the
+    outputs of a call that allocates its own: every element of o and S_T is written, with a
+    ragged last chunk."""
+    wl = dataclasses.replace(W.TRAIN_4K, name="outs", dtype=dtype, dk=dk, dv=dk, H=3, s0_std=0.05)
+    say("case: caller outputs %s dk=%d B=2 T=300 H=3" % (dtype, dk))
+    inp = W.make_inputs(wl, seed=17, B=2, T=300)
+    o_ref, s_ref = run_gpu(inp)
+    o_buf, s_buf = torch.full_like(o_ref, float("nan")), torch.full_like(s_ref, float("nan"))
+    o, s = run_gpu(inp, o=o_buf, final_state=s_buf)
+    assert o is o_buf and s is s_buf
+    assert torch.equal(o, o_ref) and torch.equal(s, s_ref)
