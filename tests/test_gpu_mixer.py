@@ -149,3 +149,24 @@ def test_prep_training_shape_sampled():
         ref = oracle_prep(sub)
         for n in PREP_OUT:
             assert check_close(got[n][bi:bi + 1, :, h:h + 1], ref[n], wl.dtype, "%s (%d,%d)" % (n, bi, h))
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64)])
+def test_caller_outputs_are_fully_written(dtype, d):
+    """Output buffers of both passes, filled with NaN first, come back bit for bit equal to the
+    outputs of calls that allocate their own."""
+    x = mixer_case(dtype, d, 2, 150, 3, 415)
+    ref = run_prep(x)
+    dx = {n: x[n].cuda() for n in X_IN}
+    bufs = {n: torch.full_like(t, float("nan")) for n, t in ref.items()}
+    got = gdn2.mixer_prep(*[dx[n] for n in X_IN], out=bufs)
+    gen = torch.Generator("cpu").manual_seed(415)
+    o = (3.0 * torch.randn((2, 150, 3, d), generator=gen)).cuda()
+    z, gamma = x["z"].cuda(), x["gamma"].cuda()
+    y_ref = gdn2.mixer_out(o, z, gamma)
+    y_buf = torch.full_like(y_ref, float("nan"))
+    y = gdn2.mixer_out(o, z, gamma, y=y_buf)
+    torch.cuda.synchronize()
+    for n in ref:
+        assert got[n] is bufs[n] and torch.equal(got[n], ref[n]), n
+    assert y is y_buf and torch.equal(y, y_ref)

@@ -263,3 +263,15 @@ def test_more_sequences_than_the_sorted_range():
     inp = packed_case(torch.float32, 64, 1, lengths, 212)
     o, s = run_varlen(inp)
     check_all(inp, o, s, TOL_F32, "600 sequences fp32")
+
+
+def test_caller_outputs_are_fully_written():
+    """o and S_T buffers passed in, filled with NaN first, come back bit for bit equal to those
+    of a call that allocates its own, for packed lengths with an empty sequence, a one-token
+    sequence and ragged last chunks."""
+    inp = packed_case(torch.bfloat16, 128, 2, [70, 0, 150, 1, 64], 216)
+    o_ref, s_ref = run_varlen(inp)
+    o_buf, s_buf = torch.full_like(o_ref, float("nan")), torch.full_like(s_ref, float("nan"))
+    o, s = run_varlen(inp, o=o_buf, final_state=s_buf)
+    assert o is o_buf and s is s_buf
+    assert torch.equal(o, o_ref) and torch.equal(s, s_ref)
