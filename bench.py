@@ -4,15 +4,19 @@
 
 A step is one chunk-parallel forward (gdn2_chunk_fwd) over the training-shape
 workload B=8, T=4096, H=16, dk=dv=128 (bf16 q,k,v,b,w, fp32 log alpha, zero
-initial state, fp32 o and final state), inputs resident in HBM before timing.
-The decode workload (N=256 sequences x H=16, 128x128 fp32 state, one token per
-step) is timed in the same run and reported under "decode".
+initial state, fp32 final state; o in fp32 unless --out-bf16), inputs resident
+in HBM before timing.  The decode workload (N=256 sequences x H=16, 128x128 fp32
+state, one token per step, 1024 steps) is timed in the same run and reported
+under "decode"; the long-context workload (B=1, T=32768) under "long_context";
+a sweep of T at B*T = 32768 under "t_sweep".
 
-Prints one JSON line.  `value` is tokens/s (B*T tokens per step); `roofline`
-gives the chunk kernel's algorithmic HBM bytes per launch over its average
-launch time, measured with HIP events on the stream the kernel runs on;
-`cpu_baseline` is the fp64 oracle timed on a bounded sample of the same
-workload on this host's cores.
+Prints one JSON line.  `value` is tokens/s (B*T tokens per step).  `roofline`
+gives the chunk kernel's algorithmic HBM bytes per launch (2,048 B per
+head-token: q, k, b, v, w in bf16, log alpha fp32, o counted as bf16, plus the
+fp32 final state) over its average launch time, measured with HIP events on the
+stream the kernel runs on; the extra bytes of an fp32 o are listed beside it.
+`cpu_baseline` is the fp64 oracle timed on the same workload on this host's
+cores.
 """
 from __future__ import annotations
 
@@ -31,21 +35,43 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 
-def chunk_bytes(B, T, H, dk, dv, in_bytes=2, out_bytes=4, with_s0=False):
-    """Algorithmic HBM bytes of one forward: every input read once, o and S_T written once."""
-    per_head_token = 3 * dk * in_bytes + 2 * dv * in_bytes + dk * 4 + dv * out_bytes
+def chunk_bytes(B, T, H, dk, dv, in_bytes=2, with_s0=False):
+    """Algorithmic HBM bytes of one forward: q, k, b, v, w read once in the input dtype, log
+    alpha fp32, o written once in the input dtype (2,048 B per head-token at d = 128 in bf16),
+    plus the fp32 final state (and the initial state when one is given)."""
+    per_head_token = 3 * dk * in_bytes + 2 * dv * in_bytes + dk * 4 + dv * in_bytes
     state = B * H * dk * dv * 4 * (2 if with_s0 else 1)
     return B * T * H * per_head_token + state
 
 
+def fp32_o_extra_bytes(B, T, H, dv, in_bytes=2):
+    """Bytes an fp32 o writes beyond the input-dtype o that chunk_bytes counts."""
+    return B * T * H * dv * (4 - in_bytes)
+
+
 def chunk_flops(B, T, H, dk, dv, C=64):
-    """Algorithmic matrix flops of the chunk form per launch (2 per multiply-add): per chunk the
-    C x C products A and P (2 x C*C*dk), W = T(b.k.Gamma) and U = T(w.v) (C*C*(dk+dv)), the
-    triangular inverse (C^3/3), and the state products W S, (q.Gamma) S, k'^T U (3 x C*dk*dv) and
-    P U (C*C*dv)."""
+    """Algorithmic matrix flops of the chunk form per launch (2 per multiply-add), counting the
+    causal (triangular) parts only: per chunk A (C(C-1)/2 dk), P (C(C+1)/2 dk), W = T(b.k.Gamma)
+    (C(C+1)/2 dk), U0 = T(w.v) and P U (C(C+1)/2 dv each), the triangular inverse (C^3/6) and the
+    state products W S, (q.Gamma) S, (k.Gamma')^T U (3 C dk dv)."""
     nchunks = B * H * ((T + C - 1) // C)
-    per_chunk = 2 * (2 * C * C * dk + C * C * (dk + dv) + C ** 3 // 3 + 3 * C * dk * dv + C * C * dv)
-    return nchunks * per_chunk
+    tri_lo, tri = C * (C - 1) // 2, C * (C + 1) // 2
+    mac = tri_lo * dk + tri * dk + tri * dk + 2 * tri * dv + C ** 3 / 6 + 3 * C * dk * dv
+    return int(nchunks * 2 * mac)
+
+
+def host_info():
+    """CPU model and logical CPU count of this host."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "cpu_count": os.cpu_count()}
 
 
 def decode_bytes(N, H, dk, dv, in_bytes=2, out_bytes=4):
@@ -103,20 +129,44 @@ def cpu_baseline(wl, torch):
 
     Bs, Ts = wl.B, wl.T
     inp = W.make_inputs(wl, B=Bs, T=Ts)
-    threads = oracle.default_threads()
+    threads = min(oracle.default_threads(), Bs * wl.H)
     t0 = time.perf_counter()
     oracle.fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["b"], inp["w"], inp["s0"],
                nthreads=threads)
     dt = time.perf_counter() - t0
-    return {"value": Bs * Ts / dt, "unit": "tokens/s", "cores": min(threads, Bs * wl.H),
-            "kind": "oracle",
-            "sample": "fp64 oracle on the whole workload: B=%d T=%d H=%d d=%d (%d of %d sequences, "
-                      "%d tokens each), %.2f s wall" % (Bs, Ts, wl.H, wl.dk, Bs * wl.H, wl.B * wl.H,
-                                                        Ts, dt)}
+    out = {"value": Bs * Ts / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": "fp64 oracle on the whole workload: B=%d T=%d H=%d d=%d (%d of %d sequences, "
+                     "%d tokens each), %.2f s wall on %d threads" % (Bs, Ts, wl.H, wl.dk, Bs * wl.H,
+                                                                    wl.B * wl.H, Ts, dt, threads)}
+    out.update(host_info())
+    return out
 
 
-def run_chunk(args, torch, gdn2, W, dev, out_dtype):
-    """Chunk forward on the training-shape workload; returns (ms per launch, workload, bytes)."""
+def cpu_baseline_decode(steps=8):
+    """The oracle's decode step on the decode workload (all 256 sequences x 16 heads), a bounded
+    number of steps: steps/s and the fp64 state bytes it streams (read + written) per second."""
+    import oracle
+    import workloads as W
+
+    wl = W.DECODE
+    pool = W.make_decode_pool(wl)
+    state = pool["state"].double().numpy()
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        p = s % wl.pool
+        _, state = oracle.decode(pool["q"][p], pool["k"][p], pool["v"][p], pool["log_alpha"][p],
+                                 pool["b"][p], pool["w"][p], state, nthreads=threads)
+    dt = (time.perf_counter() - t0) / steps
+    state_bytes = 2 * wl.B * wl.H * wl.dk * wl.dv * 8
+    return {"us_per_step": dt * 1e6, "state_GBps_fp64": state_bytes / dt / 1e9, "cores": threads,
+            "kind": "oracle", "sample": "%d steps of N=%d x H=%d, d=%d (fp64 state %d MB)" % (
+                steps, wl.B, wl.H, wl.dk, state_bytes // 2 // 1000000)}
+
+
+def run_chunk(args, torch, gdn2, W, dev, out_dtype, keep=False):
+    """Chunk forward on the training-shape workload; returns (ms per launch, workload, bytes,
+    device inputs if keep)."""
     wl = W.TRAIN_4K
     inp = W.make_inputs(wl)
     d = {n: (None if x is None else x.to(dev)) for n, x in inp.items()}
@@ -129,10 +179,62 @@ def run_chunk(args, torch, gdn2, W, dev, out_dtype):
                        final_state=sT, out_dtype=out_dtype)
 
     ms = time_launches(step, args.steps, args.warmup, torch)
-    nbytes = chunk_bytes(wl.B, wl.T, wl.H, wl.dk, wl.dv, out_bytes=out_dtype.itemsize)
+    nbytes = chunk_bytes(wl.B, wl.T, wl.H, wl.dk, wl.dv)
+    del o, sT
+    if not keep:
+        del d
+        d = None
+    torch.cuda.empty_cache()
+    return ms, wl, nbytes, d
+
+
+def run_long(args, torch, gdn2, W, dev, out_dtype):
+    """The long-context workload: one sequence of 32,768 tokens, 16 heads (half with strong
+    decay), the same kernel and byte count per head-token as the training shape."""
+    wl = W.LONG_32K
+    inp = W.make_inputs(wl)
+    d = {n: (None if x is None else x.to(dev)) for n, x in inp.items()}
+    del inp
+    o = torch.empty((wl.B, wl.T, wl.H, wl.dv), dtype=out_dtype, device=dev)
+    sT = torch.empty((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=dev)
+
+    def step():
+        gdn2.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["s0"], o=o,
+                       final_state=sT, out_dtype=out_dtype)
+
+    ms = time_launches(step, max(3, args.steps // 4), 2, torch)
+    nbytes = chunk_bytes(wl.B, wl.T, wl.H, wl.dk, wl.dv)
+    gbps = nbytes / (ms * 1e-3) / 1e9
     del d, o, sT
     torch.cuda.empty_cache()
-    return ms, wl, nbytes
+    return {"workload": wl.name, "us_per_launch": ms * 1e3, "tokens_per_s": wl.B * wl.T / (ms * 1e-3),
+            "GBps": gbps, "peak": HBM_PEAK_GBPS, "frac": gbps / HBM_PEAK_GBPS,
+            "algorithmic_bytes_per_launch": nbytes,
+            "note": "B*H = 16 (sequence, head) chains of 512 chunks each"}
+
+
+def run_sweep(args, torch, gdn2, d, dev, out_dtype, H=16, dk=128, dv=128, total=32768):
+    """Tokens/s against sequence length at a fixed B*T = 32,768 tokens: the training-shape inputs
+    (already on the device) viewed as B = 32768 / T sequences of T tokens each."""
+    out = []
+    for T in (512, 1024, 2048, 4096, 8192, 16384, 32768):
+        B = total // T
+        v = {n: x.view(B, T, *x.shape[2:]) for n, x in d.items() if x is not None}
+        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
+        sT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+
+        def step():
+            gdn2.chunk_fwd(v["q"], v["k"], v["v"], v["log_alpha"], v["b"], v["w"], None, o=o, final_state=sT,
+                           out_dtype=out_dtype)
+
+        ms = time_launches(step, max(3, args.steps // 4), 2, torch)
+        nbytes = chunk_bytes(B, T, H, dk, dv)
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out.append({"T": T, "B": B, "us_per_launch": ms * 1e3, "tokens_per_s": total / (ms * 1e-3),
+                    "frac": gbps / HBM_PEAK_GBPS})
+        del o, sT
+    torch.cuda.empty_cache()
+    return out
 
 
 def run_prefill(args, torch, gdn2, W, dev, out_dtype):
@@ -152,8 +254,9 @@ def run_prefill(args, torch, gdn2, W, dev, out_dtype):
                               d["s0"], o=o, final_state=sT, out_dtype=out_dtype)
 
     ms = time_launches(step, args.steps, args.warmup, torch)
-    per_tok = 3 * wl.dk * 2 + 2 * wl.dv * 2 + wl.dk * 4 + wl.dv * out_dtype.itemsize
+    per_tok = 3 * wl.dk * 2 + 2 * wl.dv * 2 + wl.dk * 4 + wl.dv * 2  # o counted in the input dtype
     nbytes = total * wl.H * per_tok + 2 * wl.B * wl.H * wl.dk * wl.dv * 4 + (wl.B + 1) * 8
+    extra = fp32_o_extra_bytes(1, total, wl.H, wl.dv) if out_dtype == torch.float32 else 0
     gbps = nbytes / (ms * 1e-3) / 1e9
     del d, o, sT
     torch.cuda.empty_cache()
@@ -162,7 +265,7 @@ def run_prefill(args, torch, gdn2, W, dev, out_dtype):
             "us_per_launch": ms * 1e3, "tokens_per_s": total / (ms * 1e-3), "GBps": gbps,
             "peak": HBM_PEAK_GBPS, "frac": gbps / HBM_PEAK_GBPS,
             "traffic": recorded_traffic(*PREFILL_PROFILE) if out_dtype == torch.float32 else None,
-            "algorithmic_bytes_per_launch": nbytes}
+            "algorithmic_bytes_per_launch": nbytes, "fp32_o_extra_bytes_per_launch": extra}
 
 
 def bwd_bytes(B, T, H, dk, dv, in_bytes=2, s0=True):
@@ -238,30 +341,53 @@ def run_mixer(args, torch, gdn2, W, dev):
 
 
 def run_decode(args, torch, gdn2, W, dev, out_dtype):
-    """Decode workload: N=256 sequences x H=16, one token per step, state updated in place."""
+    """Decode workload: N=256 sequences x H=16, one token per step, state updated in place.  The
+    whole loop of --decode-steps steps (1024, the workload's length) is timed as one event pair
+    (per-step time includes the host launch gaps), then the same loop captured once in a HIP
+    graph (kernel nodes only) and replayed, timed the same way."""
     dwl = W.DECODE
     pool = W.make_decode_pool(dwl)
     state = pool["state"].to(dev)
     dp = {n: pool[n].to(dev) for n in ("q", "k", "v", "log_alpha", "b", "w")}
     del pool
     o_dec = torch.empty((dwl.B, dwl.H, dwl.dv), dtype=out_dtype, device=dev)
-    it = [0]
+    nsteps = args.decode_steps
+    toks = [{n: dp[n][s % dwl.pool] for n in dp} for s in range(dwl.pool)]
 
-    def dstep():
-        p = it[0] % dwl.pool
-        it[0] += 1
-        gdn2.decode_step(dp["q"][p], dp["k"][p], dp["v"][p], dp["log_alpha"][p], dp["b"][p],
-                         dp["w"][p], state, o=o_dec, out_dtype=out_dtype)
+    def loop():
+        for s in range(nsteps):
+            t = toks[s % dwl.pool]
+            gdn2.decode_step(t["q"], t["k"], t["v"], t["log_alpha"], t["b"], t["w"], state, o=o_dec,
+                             out_dtype=out_dtype)
 
-    dms = time_launches(dstep, args.decode_steps, 5, torch)
+    loop()  # warm-up pass over the whole loop
+    dms = time_launches(loop, 1, 0, torch) / nsteps
     dbytes = decode_bytes(dwl.B, dwl.H, dwl.dk, dwl.dv, out_bytes=out_dtype.itemsize)
     dgbps = dbytes / (dms * 1e-3) / 1e9
-    del state, dp, o_dec
+    graph = None
+    try:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                loop()
+        torch.cuda.current_stream().wait_stream(side)
+        g.replay()  # first replay uploads the graph
+        gms = time_launches(g.replay, 1, 0, torch) / nsteps
+        ggbps = dbytes / (gms * 1e-3) / 1e9
+        graph = {"us_per_step": gms * 1e3, "state_GBps": ggbps, "frac": ggbps / HBM_PEAK_GBPS,
+                 "steps": nsteps}
+        del g
+    except RuntimeError as e:  # report, do not hide, a capture failure
+        graph = {"error": str(e)[:200]}
+    del state, dp, o_dec, toks
     torch.cuda.empty_cache()
     return {"workload": dwl.name, "us_per_step": dms * 1e3, "state_GBps": dgbps,
             "peak": HBM_PEAK_GBPS, "frac": dgbps / HBM_PEAK_GBPS,
             "traffic": recorded_traffic(*DECODE_PROFILE) if out_dtype == torch.float32 else None,
-            "algorithmic_bytes_per_step": dbytes, "steps": args.decode_steps}
+            "algorithmic_bytes_per_step": dbytes, "steps": nsteps,
+            "timing": "the whole loop as one event pair, launch gaps included", "graph": graph}
 
 
 def main():
@@ -269,11 +395,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--decode-steps", type=int, default=64)
+    ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out-bf16", action="store_true", help="write o in bf16 instead of fp32")
-    ap.add_argument("--only", choices=("chunk", "decode", "prefill", "bwd", "mixer"), default=None,
-                    help="time one workload only (profiler runs); prints its figures")
+    ap.add_argument("--only", choices=("chunk", "decode", "prefill", "bwd", "mixer", "long", "sweep"),
+                    default=None, help="time one workload only (profiler runs); prints its figures")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run only a plain device-to-device copy of MIB MiB (--steps times): "
                          "the reference point that scales the FETCH_SIZE / WRITE_SIZE counters")
@@ -301,30 +427,37 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "avg_launch_us": ms * 1e3,
                           "GBps": 2 * n / (ms * 1e-3) / 1e9}))
         return
-    if args.only == "decode":
-        print(json.dumps({"decode": run_decode(args, torch, gdn2, W, dev, out_dtype)}))
+    only = {"decode": lambda: {"decode": run_decode(args, torch, gdn2, W, dev, out_dtype)},
+            "prefill": lambda: {"prefill_varlen": run_prefill(args, torch, gdn2, W, dev, out_dtype)},
+            "bwd": lambda: {"backward": run_bwd(args, torch, gdn2, W, dev)},
+            "mixer": lambda: {"mixer": run_mixer(args, torch, gdn2, W, dev)},
+            "long": lambda: {"long_context": run_long(args, torch, gdn2, W, dev, out_dtype)}}
+    if args.only in only:
+        print(json.dumps(only[args.only]()), flush=True)
         return
-    if args.only == "prefill":
-        print(json.dumps({"prefill_varlen": run_prefill(args, torch, gdn2, W, dev, out_dtype)}))
-        return
-    if args.only == "bwd":
-        print(json.dumps({"backward": run_bwd(args, torch, gdn2, W, dev)}))
-        return
-    if args.only == "mixer":
-        print(json.dumps({"mixer": run_mixer(args, torch, gdn2, W, dev)}))
-        return
-    ms, wl, nbytes = run_chunk(args, torch, gdn2, W, dev, out_dtype)
+    ms, wl, nbytes, d = run_chunk(args, torch, gdn2, W, dev, out_dtype, keep=True)
     tokens = wl.B * wl.T
     achieved = nbytes / (ms * 1e-3) / 1e9
     if args.only == "chunk":
         print(json.dumps({"workload": wl.name, "avg_launch_us": ms * 1e3,
-                          "tokens_per_s": tokens / (ms * 1e-3), "achieved_GBps": achieved}))
+                          "tokens_per_s": tokens / (ms * 1e-3), "achieved_GBps": achieved}), flush=True)
         return
+    sweep = run_sweep(args, torch, gdn2, d, dev, out_dtype)
+    del d
+    torch.cuda.empty_cache()
+    if args.only == "sweep":
+        print(json.dumps({"t_sweep": sweep}), flush=True)
+        return
+    print("chunk forward %.1f us; sweep done" % (ms * 1e3), file=sys.stderr, flush=True)
+    long_ctx = run_long(args, torch, gdn2, W, dev, out_dtype)
     dec = run_decode(args, torch, gdn2, W, dev, out_dtype)
+    print("decode done", file=sys.stderr, flush=True)
     pre = run_prefill(args, torch, gdn2, W, dev, out_dtype)
     bwd = run_bwd(args, torch, gdn2, W, dev)
     mixer = run_mixer(args, torch, gdn2, W, dev)
+    print("prefill, backward, mixer done", file=sys.stderr, flush=True)
     flops = chunk_flops(wl.B, wl.T, wl.H, wl.dk, wl.dv)
+    extra = fp32_o_extra_bytes(wl.B, wl.T, wl.H, wl.dv) if out_dtype == torch.float32 else 0
 
     result = {
         "metric": METRIC,
@@ -346,10 +479,16 @@ def main():
                      "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": recorded_traffic(*CHUNK_PROFILE) if not args.out_bf16 else None,
                      "kernel": "chunk_bf16_kernel", "algorithmic_bytes_per_launch": nbytes,
+                     "bytes_per_head_token": 3 * wl.dk * 2 + 2 * wl.dv * 2 + wl.dk * 4 + wl.dv * 2,
+                     "fp32_o_extra_bytes_per_launch": extra,
+                     "frac_with_fp32_o_bytes": (nbytes + extra) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                      "avg_launch_us": ms * 1e3,
                      "mfma_context": {"algorithmic_flops_per_launch": flops,
+                                      "count": "causal (triangular) multiply-adds x 2",
                                       "TFLOPs": flops / (ms * 1e-3) / 1e12,
                                       "frac_of_bf16_peak": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}},
+        "long_context": long_ctx,
+        "t_sweep": sweep,
         "decode": dec,
         "prefill_varlen": pre,
         "backward": bwd,
@@ -357,7 +496,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, torch)
-    print(json.dumps(result))
+        result["decode"]["cpu_baseline"] = cpu_baseline_decode()
+    print(json.dumps(result), flush=True)
 
 
 if __name__ == "__main__":

@@ -27,7 +27,7 @@ import threading
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_bwd", "chunk_bwd_workspace_bytes", "decode_step", "mixer_prep",
+__all__ = ["chunk_fwd", "chunk_fwd_workspace_bytes", "chunk_fwd_varlen", "chunk_bwd", "chunk_bwd_workspace_bytes", "decode_step", "mixer_prep",
            "mixer_out", "supported", "version", "library_path", "Gdn2Error", "CHUNK"]
 
 CHUNK = 64
@@ -38,7 +38,7 @@ _lib = None
 
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 _STATUS = {0: "GDN2_OK", 1: "GDN2_ERR_NULL", 2: "GDN2_ERR_SHAPE", 3: "GDN2_ERR_UNSUPPORTED",
-           4: "GDN2_ERR_MISALIGNED", 5: "GDN2_ERR_ALIAS", 6: "GDN2_ERR_HIP", 7: "GDN2_ERR_WORKSPACE"}
+           4: "GDN2_ERR_MISALIGNED", 5: "GDN2_ERR_ALIAS", 6: "GDN2_ERR_WORKSPACE", 7: "GDN2_ERR_HIP"}
 
 
 class Gdn2Error(RuntimeError):
@@ -62,8 +62,10 @@ def _load():
                 "`python -m gated_delta_rule_gdn2_amd.build`" % _LIB_PATH)
         lib = ctypes.CDLL(_LIB_PATH)
         P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-        lib.gdn2_chunk_fwd.argtypes = [P] * 9 + [I64] * 5 + [I32, I32, P]
+        lib.gdn2_chunk_fwd.argtypes = [P] * 9 + [I64] * 5 + [I32, I32, P, ctypes.c_size_t, P]
         lib.gdn2_chunk_fwd.restype = I32
+        lib.gdn2_chunk_fwd_workspace_bytes.argtypes = [I64] * 5 + [I32]
+        lib.gdn2_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
         lib.gdn2_chunk_fwd_varlen.argtypes = [P] * 10 + [I64] * 5 + [I32, I32, P]
         lib.gdn2_chunk_fwd_varlen.restype = I32
         lib.gdn2_decode_step.argtypes = [P] * 8 + [I64] * 4 + [I32, I32, P]
@@ -147,9 +149,11 @@ def chunk_fwd(q, k, v, log_alpha, b, w, initial_state=None, *, o=None, final_sta
         final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     elif final_state is not None:
         _check("final_state", final_state, (B, H, dk, dv), torch.float32, dev)
+    ws_bytes = _load().gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, _DTYPES[dt])
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     st = _load().gdn2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
                                 _ptr(initial_state), _ptr(o), _ptr(final_state), B, T, H, dk, dv,
-                                _DTYPES[dt], _DTYPES[out_dtype], _stream_handle(dev))
+                                _DTYPES[dt], _DTYPES[out_dtype], _ptr(ws), ws_bytes, _stream_handle(dev))
     if st != 0:
         raise Gdn2Error("gdn2_chunk_fwd", st, _load().gdn2_status_string(st).decode())
     return o, final_state
@@ -231,6 +235,11 @@ def decode_step(q, k, v, log_alpha, b, w, state, *, o=None, out_dtype=torch.floa
     if st != 0:
         raise Gdn2Error("gdn2_decode_step", st, _load().gdn2_status_string(st).decode())
     return o
+
+
+def chunk_fwd_workspace_bytes(B, T, H, dk, dv, dtype=torch.bfloat16) -> int:
+    """Device workspace (bytes) that chunk_fwd needs for these sizes (0: the forward is fused)."""
+    return int(_load().gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, _DTYPES[dtype]))
 
 
 def chunk_bwd_workspace_bytes(B, T, H, dk, dv) -> int:

@@ -146,13 +146,22 @@ gdn2_status_t chunk_fwd_common(const void* q, const void* k, const void* v, cons
 
 extern "C" {
 
+size_t gdn2_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                      gdn2_dtype_t dtype) {
+    (void)B; (void)T; (void)H; (void)dk; (void)dv; (void)dtype;
+    return 0;  // one fused kernel: every intermediate lives in registers and LDS
+}
+
 gdn2_status_t gdn2_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
                              const void* b, const void* w, const float* initial_state, void* o,
                              float* final_state, int64_t B, int64_t T, int64_t H, int64_t dk,
-                             int64_t dv, gdn2_dtype_t dtype, gdn2_dtype_t o_dtype, void* stream) {
+                             int64_t dv, gdn2_dtype_t dtype, gdn2_dtype_t o_dtype, void* workspace,
+                             size_t workspace_bytes, void* stream) {
     if (B < 1 || T < 1) return GDN2_ERR_SHAPE;
     int64_t BT;
     if (!mul_ok(B, T, &BT)) return GDN2_ERR_SHAPE;
+    const size_t need = gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, dtype);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return GDN2_ERR_WORKSPACE;
     return chunk_fwd_common(q, k, v, log_alpha, b, w, initial_state, o, final_state, nullptr, B, T, BT, H,
                             dk, dv, dtype, o_dtype, stream);
 }
@@ -330,8 +339,8 @@ const char* gdn2_status_string(gdn2_status_t s) {
         case GDN2_ERR_UNSUPPORTED: return "(dk, dv, dtype) is not supported";
         case GDN2_ERR_MISALIGNED: return "a tensor pointer is not 16-byte aligned";
         case GDN2_ERR_ALIAS: return "an output overlaps an input";
-        case GDN2_ERR_HIP: return "the HIP runtime rejected the call";
         case GDN2_ERR_WORKSPACE: return "the workspace is missing or too small";
+        case GDN2_ERR_HIP: return "the HIP runtime rejected the call";
     }
     return "unknown status";
 }

@@ -172,8 +172,9 @@ __device__ __forceinline__ float exp_neg(float x) { return __builtin_amdgcn_exp2
 // starts late sets the launch's length.  So sequence slot r (in dispatch order) takes the
 // r-th longest sequence, ties in index order.  Lengths are the offsets clamped into
 // [0, Tparam] as the kernels clamp them.  Every thread of the workgroup calls this, before
-// anything else uses LDS; scratch holds ns + 1 ints.  For ns > kMaxSort, slot r takes
-// sequence r.
+// anything else uses LDS; scratch must hold kMaxSort + 1 ints: the lengths in [0, ns) and the
+// selected sequence at index kMaxSort (every caller's LDS block asserts that size).  For
+// ns > kMaxSort, slot r takes sequence r and scratch is not touched.
 constexpr int kMaxSort = 512;
 __device__ __forceinline__ int longest_first(const int64_t* __restrict__ cu, int ns, int r, int Tparam, int* scratch) {
     if (ns > kMaxSort) return r;

@@ -65,8 +65,8 @@ typedef enum gdn2_status {
     GDN2_ERR_UNSUPPORTED = 3, /* (dk, dv, dtype) is not built into this library */
     GDN2_ERR_MISALIGNED = 4,  /* a tensor pointer is not 16-byte aligned */
     GDN2_ERR_ALIAS = 5,       /* an output overlaps an input it must not overlap */
-    GDN2_ERR_HIP = 6,         /* the HIP runtime rejected a query or a launch */
-    GDN2_ERR_WORKSPACE = 7    /* the workspace is NULL or smaller than required */
+    GDN2_ERR_WORKSPACE = 6,   /* the workspace is NULL or smaller than required */
+    GDN2_ERR_HIP = 7          /* the HIP runtime rejected a query or a launch */
 } gdn2_status_t;
 
 /*
@@ -89,12 +89,26 @@ typedef enum gdn2_status {
  * o must not overlap any input; final_state must not overlap any input other
  * than an identical initial_state.  H * dk and H * dv (the elements between
  * consecutive tokens of one tensor) must be below 2^24, else GDN2_ERR_SHAPE.
+ * workspace / workspace_bytes: caller-owned device memory of at least
+ * gdn2_chunk_fwd_workspace_bytes(...) bytes (currently 0: NULL and 0 are
+ * accepted); a shorter one returns GDN2_ERR_WORKSPACE.
  */
 gdn2_status_t gdn2_chunk_fwd(const void* q, const void* k, const void* v,
                              const float* log_alpha, const void* b, const void* w,
                              const float* initial_state, void* o, float* final_state,
                              int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
-                             gdn2_dtype_t dtype, gdn2_dtype_t o_dtype, void* stream);
+                             gdn2_dtype_t dtype, gdn2_dtype_t o_dtype, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
+ * gdn2_chunk_fwd_workspace_bytes -- bytes of device workspace gdn2_chunk_fwd
+ * needs for these sizes.  The forward is one fused kernel whose intermediates
+ * stay in registers and LDS, so this is 0 for every supported combination
+ * (and gdn2_chunk_fwd accepts workspace = NULL, workspace_bytes = 0).
+ * Returns 0 for unsupported combinations too; gdn2_chunk_fwd reports those.
+ */
+size_t gdn2_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                      gdn2_dtype_t dtype);
 
 /*
  * gdn2_chunk_fwd_varlen -- the same forward over N sequences of different

@@ -45,3 +45,33 @@ def take_sequences(inp, pairs):
 
 def to_dev(inp, dev="cuda"):
     return {n: (None if x is None else x.to(dev).contiguous()) for n, x in inp.items()}
+
+
+class ErrAccum:
+    """The whole-tensor parity metric built up over pieces of a tensor: max |x - x_ref| over
+    every piece, divided by the RMS of x_ref over every piece (fp64); inf once any piece holds
+    a non-finite value."""
+
+    def __init__(self):
+        self.maxabs = 0.0
+        self.sumsq = 0.0
+        self.n = 0
+        self.finite = True
+
+    def add(self, x, ref):
+        x = np.asarray(x.detach().cpu().to(torch.float64) if isinstance(x, torch.Tensor) else x,
+                       dtype=np.float64)
+        ref = np.asarray(ref, dtype=np.float64)
+        assert x.shape == ref.shape, (x.shape, ref.shape)
+        if not np.isfinite(x).all():
+            self.finite = False
+            return
+        self.maxabs = max(self.maxabs, float(np.abs(x - ref).max()) if x.size else 0.0)
+        self.sumsq += float(np.sum(ref * ref))
+        self.n += ref.size
+
+    def value(self):
+        if not self.finite:
+            return float("inf")
+        rms = np.sqrt(self.sumsq / max(self.n, 1))
+        return self.maxabs / rms if rms > 0 else self.maxabs

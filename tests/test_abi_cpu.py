@@ -14,7 +14,7 @@ import gated_delta_rule_gdn2_amd as gdn2
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdn2.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_ALIAS, ERR_HIP, ERR_WORKSPACE = range(8)
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_ALIAS, ERR_WORKSPACE, ERR_HIP = range(8)
 BF16, F32 = 1, 0
 
 
@@ -33,8 +33,9 @@ def declared_functions():
 
 def test_header_declares_the_calls():
     names = declared_functions()
-    for name in ("gdn2_chunk_fwd", "gdn2_chunk_fwd_varlen", "gdn2_chunk_bwd", "gdn2_chunk_bwd_workspace_bytes",
-                 "gdn2_decode_step", "gdn2_mixer_prep", "gdn2_mixer_out"):
+    for name in ("gdn2_chunk_fwd", "gdn2_chunk_fwd_workspace_bytes", "gdn2_chunk_fwd_varlen", "gdn2_chunk_bwd",
+                 "gdn2_chunk_bwd_workspace_bytes", "gdn2_decode_step", "gdn2_mixer_prep", "gdn2_mixer_out",
+                 "gdn2_status_string", "gdn2_version"):
         assert name in names, name
 
 
@@ -87,7 +88,8 @@ def chunk(lib, f, B=1, T=64, H=1, dk=64, dv=64, dtype=BF16, odt=F32, **over):
                 sT=None)
     args.update(over)
     return lib.gdn2_chunk_fwd(args["q"], args["k"], args["v"], args["g"], args["b"], args["w"],
-                              args["s0"], args["o"], args["sT"], B, T, H, dk, dv, dtype, odt, None)
+                              args["s0"], args["o"], args["sT"], B, T, H, dk, dv, dtype, odt,
+                              args.get("ws"), args.get("ws_bytes", 0), None)
 
 
 def decode(lib, f, N=1, H=1, dk=64, dv=64, dtype=BF16, odt=F32, **over):
@@ -180,6 +182,24 @@ def test_varlen_validation(lib):
     # offsets inside o, final state overlapping the offsets
     assert varlen(lib, f, cu=f.p(7, 8)) == ERR_ALIAS
     assert varlen(lib, f, sT=f.p(9)) == ERR_ALIAS
+
+
+def test_status_values_follow_the_boundary_table(lib):
+    """GDN2_ERR_WORKSPACE is 6 and GDN2_ERR_HIP is 7; the strings name them."""
+    assert b"workspace" in lib.gdn2_status_string(ERR_WORKSPACE)
+    assert b"HIP" in lib.gdn2_status_string(ERR_HIP)
+    assert (ERR_WORKSPACE, ERR_HIP) == (6, 7)
+
+
+def test_fwd_workspace_bytes(lib):
+    """The forward keeps every intermediate on chip: no workspace for any size or dtype, and
+    a NULL workspace of 0 bytes passes validation (the call below fails later, on alignment)."""
+    for dt in (BF16, F32):
+        for (B, T, H, d) in ((1, 1, 1, 64), (8, 4096, 16, 128), (1, 32768, 16, 128)):
+            assert lib.gdn2_chunk_fwd_workspace_bytes(B, T, H, d, d, dt) == 0
+    assert gdn2.chunk_fwd_workspace_bytes(8, 4096, 16, 128, 128) == 0
+    f = Fake()
+    assert chunk(lib, f, q=f.p(0, 2), ws=None, ws_bytes=0) == ERR_MISALIGNED
 
 
 def test_bwd_workspace_bytes(lib):

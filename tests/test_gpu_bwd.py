@@ -5,7 +5,7 @@ VJP on the same inputs, upstream gradients d_o and d_final_state included, with 
 forward's bars: max |x - x_ref| / RMS(x_ref) <= 1e-4 for fp32 inputs, 3e-2 for bf16 inputs.
 The cases span several chunks with a ragged tail, a single token, chunks whose decay takes
 the element-by-element path (whole-chunk decay below e^-40), a mix of both kinds, and the
-full fwd+bwd workload on sampled sequences."""
+full fwd+bwd workload compared as whole tensors."""
 import dataclasses
 
 import pytest
@@ -14,7 +14,7 @@ import torch
 import gated_delta_rule_gdn2_amd as gdn2
 import oracle
 import workloads as W
-from tests.parity_util import TOL_BF16, TOL_F32, rel_max_err, say, take_sequences, to_dev
+from tests.parity_util import TOL_BF16, TOL_F32, rel_max_err, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -154,26 +154,24 @@ def test_bwd_deterministic():
         assert torch.equal(a[n], b[n]), n
 
 
-def test_fwdbwd_workload_sampled():
+def test_fwdbwd_workload_whole_tensor():
     """The fwd+bwd workload at full size (B=4, T=4096, H=16, d=128, bf16, S_0 ~ N(0, 0.02^2),
-    d_o ~ N(0,1)) in the launch the benchmark times; two (b, h) sequences against the oracle,
-    every gradient finite."""
+    d_o ~ N(0,1)) in the launch the benchmark times; the oracle's reverse sweep over every
+    (sequence, head), every gradient compared as a whole tensor and per head."""
     wl = W.FWD_BWD_4K
-    say("case: %s sampled" % wl.name)
+    say("case: %s (full size, whole tensors)" % wl.name)
     inp = W.make_inputs(wl)
     inp["do"] = W.make_upstream_grad(wl)
     inp["dsT"] = None
     g = run_bwd(inp)
-    for n in GRADS + ("d_initial_state",):
-        assert torch.isfinite(g[n]).all(), n
-    pairs = [(0, 0), (3, 15)]
-    sub = take_sequences(inp, pairs)
-    sub["do"] = torch.stack([inp["do"][b, :, h] for b, h in pairs])[:, :, None].contiguous()
-    sub["dsT"] = None
-    ref = oracle_vjp(sub)
-    got = {n: torch.stack([g[n][b, :, h] for b, h in pairs])[:, :, None] for n in GRADS}
-    got["d_initial_state"] = torch.stack([g["d_initial_state"][b, h] for b, h in pairs])[:, None]
-    check(got, ref, TOL_BF16, "fwdbwd sampled")
+    ref = oracle_vjp(inp)
+    check(g, ref, TOL_BF16, "fwdbwd whole tensors")
+    worst = {}
+    for n in GRADS:
+        worst[n] = max(rel_max_err(g[n][:, :, h], ref[n][:, :, h]) for h in range(wl.H))
+    worst["d_initial_state"] = max(rel_max_err(g["d_initial_state"][:, h], ref["ds0"][:, h]) for h in range(wl.H))
+    say("  worst head: %s" % "  ".join("%s %.2e" % (n, e) for n, e in worst.items()))
+    assert all(e <= TOL_BF16 for e in worst.values()), worst
 
 
 @pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64)])

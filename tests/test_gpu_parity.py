@@ -4,10 +4,9 @@ Bars (max |x - x_ref| / RMS(x_ref) per output tensor, no non-finite value):
 1e-4 for fp32 inputs, 3e-2 for bf16 inputs with fp32 accumulation.  The oracle
 sees exactly the values the GPU sees (bf16 inputs upcast exactly).
 
-Small cases span several chunks and a ragged last chunk and run the oracle on
-everything; the full-size workloads run exactly the launch the benchmark times
-and check sampled (sequence, head) pairs one by one, plus properties on all
-outputs (finiteness)."""
+Small cases span several chunks and a ragged last chunk; the full-size workloads
+run exactly the launch the benchmark times.  Every case runs the oracle on every
+(sequence, head) and takes the metric over the whole output tensors."""
 import dataclasses
 
 import numpy as np
@@ -17,7 +16,7 @@ import torch
 import gated_delta_rule_gdn2_amd as gdn2
 import oracle
 import workloads as W
-from tests.parity_util import TOL_BF16, TOL_F32, rel_max_err, say, take_sequences, to_dev, tol_for
+from tests.parity_util import TOL_BF16, TOL_F32, ErrAccum, rel_max_err, say, to_dev, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -113,66 +112,81 @@ def test_mixed_decay_heads_small():
 
 
 # ----------------------------------------------------------- full sizes ----
+# Every (sequence, head) of each full-size workload, in the launch the benchmark times, against
+# the oracle run on the whole workload: the metric is taken over the whole o and S_T tensors,
+# and per head so that the weak heads' RMS cannot hide a strong head's error.
 
-def _sampled(wl, pairs):
-    say("case: %s (full size), sampled (b,h) = %s" % (wl.name, pairs))
+def _whole(wl, report_bf16_o=False):
+    say("case: %s (full size, whole tensors)" % wl.name)
     inp = W.make_inputs(wl)
     o, s = run_gpu(inp)
-    assert torch.isfinite(o.float()).all() and torch.isfinite(s).all()
-    sub = take_sequences(inp, pairs)
-    o_ref, s_ref = run_oracle(sub)
+    o_ref, s_ref = run_oracle(inp)
     tol = tol_for(wl.dtype)
-    for n, (b, h) in enumerate(pairs):
-        eo = rel_max_err(o[b, :, h], o_ref[n, :, 0])
-        es = rel_max_err(s[b, h], s_ref[n, 0])
-        say("  (b=%d,h=%2d)  o %.3e  S %.3e" % (b, h, eo, es))
-        assert eo <= tol and es <= tol, (b, h, eo, es)
+    eo, es = rel_max_err(o, o_ref), rel_max_err(s, s_ref)
+    say("  whole tensors: o err %.3e   S_T err %.3e   (bar %.0e)" % (eo, es, tol))
+    worst = (0.0, 0.0)
+    for h in range(wl.H):
+        eoh, esh = rel_max_err(o[:, :, h], o_ref[:, :, h]), rel_max_err(s[:, h], s_ref[:, h])
+        worst = (max(worst[0], eoh), max(worst[1], esh))
+        if wl.H <= 16:
+            say("  head %2d  o %.3e  S %.3e" % (h, eoh, esh))
+    say("  worst head: o %.3e  S %.3e" % worst)
+    if report_bf16_o:
+        o16, _ = run_gpu(inp, out_dtype=torch.bfloat16, output_final_state=False)
+        say("  bf16 o (rounded once on the store): o err %.3e (informational)" % rel_max_err(o16, o_ref))
+        del o16
+    assert eo <= tol and es <= tol, (wl.name, eo, es)
+    assert worst[0] <= tol and worst[1] <= tol, (wl.name, worst)
 
 
-def test_train_4k_full_size_sampled():
-    _sampled(W.TRAIN_4K, [(0, 0), (3, 7), (5, 12), (7, 15)])
+def test_train_4k_full_size_whole_tensor():
+    _whole(W.TRAIN_4K, report_bf16_o=True)
 
 
-def test_long_32k_full_size_sampled():
-    _sampled(W.LONG_32K, [(0, 0), (0, 7), (0, 8), (0, 15)])
+def test_long_32k_full_size_whole_tensor():
+    _whole(W.LONG_32K, report_bf16_o=True)
 
 
-def test_fwdbwd_4k_forward_full_size_sampled():
-    _sampled(W.FWD_BWD_4K, [(0, 0), (1, 5), (3, 15)])
+def test_fwdbwd_4k_forward_full_size_whole_tensor():
+    _whole(W.FWD_BWD_4K)
 
 
 # --------------------------------------------------------------- decode ----
 
-def test_decode_workload_sampled():
-    """1024 steps over N=256 sequences; every step's o and the final state of
-    two sequences (all heads) are checked against the oracle's replay."""
+def test_decode_workload_whole():
+    """All 1024 steps over all N=256 sequences: o of every step and the final state against
+    the oracle.  The oracle runs the 1024 tokens of each (sequence, head) as one sequence
+    (decode steps equal the forward over the same tokens: a pinned property of the oracle),
+    in batches of sequences."""
     wl = W.DECODE
-    say("case: %s" % wl.name)
+    say("case: %s (all sequences, all steps)" % wl.name)
     pool = W.make_decode_pool(wl)
     dpool = to_dev({k: v for k, v in pool.items() if k != "state"})
     state = pool["state"].cuda().contiguous()
-    seqs = [0, 201]
-    o_hist = []
+    o_all = torch.empty((wl.steps, wl.B, wl.H, wl.dv), dtype=torch.float32)
     for s in range(wl.steps):
         p = s % wl.pool
         o = gdn2.decode_step(dpool["q"][p], dpool["k"][p], dpool["v"][p], dpool["log_alpha"][p],
                              dpool["b"][p], dpool["w"][p], state)
-        o_hist.append(o[seqs].float().cpu())
+        o_all[s].copy_(o, non_blocking=False)
     torch.cuda.synchronize()
-    ref_state = pool["state"][seqs].double().numpy()
-    worst_o = 0.0
-    for s in range(wl.steps):
-        p = s % wl.pool
-        tok = {n: pool[n][p][seqs] for n in ("q", "k", "v", "log_alpha", "b", "w")}
-        o_ref, ref_state = oracle.decode(tok["q"], tok["k"], tok["v"], tok["log_alpha"], tok["b"],
-                                         tok["w"], ref_state)
-        e = rel_max_err(o_hist[s], o_ref)
-        worst_o = max(worst_o, e)
-        assert e <= TOL_BF16, (s, e)
-    es = rel_max_err(state[seqs], ref_state)
-    say("  worst o err over %d steps %.3e   final state err %.3e" % (wl.steps, worst_o, es))
-    assert es <= TOL_BF16
-    assert torch.isfinite(state).all()
+    state_gpu = state.cpu()
+    del dpool, state
+    idx = torch.arange(wl.steps) % wl.pool
+    acc_o, acc_s = ErrAccum(), ErrAccum()
+    nb = 32
+    for n0 in range(0, wl.B, nb):
+        seq = {n: pool[n][idx, n0:n0 + nb].transpose(0, 1).contiguous()
+               for n in ("q", "k", "v", "log_alpha", "b", "w")}
+        o_ref, s_ref = oracle.fwd(seq["q"], seq["k"], seq["v"], seq["log_alpha"], seq["b"], seq["w"],
+                                  pool["state"][n0:n0 + nb])
+        acc_o.add(o_all[:, n0:n0 + nb].transpose(0, 1), o_ref)
+        acc_s.add(state_gpu[n0:n0 + nb], s_ref)
+        say("  sequences %3d-%3d checked" % (n0, n0 + nb - 1))
+    eo, es = acc_o.value(), acc_s.value()
+    say("  o over all %d steps and %d sequences: err %.3e   final state err %.3e   (bar %.0e)"
+        % (wl.steps, wl.B, eo, es, TOL_BF16))
+    assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
 
 
 @pytest.mark.parametrize("dtype,d", [(torch.float32, 64), (torch.float32, 128), (torch.bfloat16, 64),

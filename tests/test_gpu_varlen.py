@@ -160,23 +160,16 @@ def test_prefill_then_decode_continues_the_sequences():
     say("  prefill -> decode, worst err %.3e (bar %.0e)" % (worst, TOL_BF16))
 
 
-def test_serving_prefill_workload_sampled():
+def test_serving_prefill_workload_whole():
     """The serving prefill workload at full size (64 prompts, seeded length mix, H=16,
-    d=128, continuation states), in the launch the benchmark times; sampled sequences
-    against the oracle, every output finite."""
+    d=128, continuation states), in the launch the benchmark times; every sequence against
+    the oracle run on it alone, the metric over the whole o and S_T tensors."""
     wl = W.SERVE_PREFILL
     lengths = W.make_lengths(wl.B, wl.seed)
     say("case: %s total %d tokens" % (wl.name, sum(lengths)))
     inp = W.make_packed_inputs(wl, lengths)
     o, s = run_varlen(inp)
-    assert torch.isfinite(o).all() and torch.isfinite(s).all()
-    cu = inp["cu_seqlens"].tolist()
-    for n in (0, 17, 63):
-        o_ref, s_ref = oracle_sequence({**inp, "q": inp["q"], "s0": inp["s0"]}, n)
-        eo = rel_max_err(o[cu[n]:cu[n + 1]], o_ref)
-        es = rel_max_err(s[n], s_ref)
-        say("  sequence %d (length %d): o err %.3e   S_T err %.3e" % (n, lengths[n], eo, es))
-        assert eo <= TOL_BF16 and es <= TOL_BF16
+    check_all(inp, o, s, TOL_BF16, "serving prefill, all 64 sequences")
 
 
 def test_multi_token_steps_in_place_continue_the_sequences():
