@@ -27,7 +27,8 @@ import threading
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_workspace_bytes", "chunk_fwd_varlen", "chunk_bwd", "chunk_bwd_workspace_bytes", "decode_step", "mixer_prep",
+__all__ = ["chunk_fwd", "chunk_fwd_workspace_bytes", "chunk_fwd_varlen", "chunk_bwd", "chunk_bwd_workspace_bytes",
+           "chunk_bwd_noalloc", "SCRATCH_BYTES", "decode_step", "mixer_prep",
            "mixer_out", "supported", "version", "library_path", "Gdn2Error", "CHUNK"]
 
 CHUNK = 64
@@ -74,6 +75,8 @@ def _load():
         lib.gdn2_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.gdn2_chunk_bwd.argtypes = [P] * 17 + [ctypes.c_size_t] + [I64] * 5 + [I32, P]
         lib.gdn2_chunk_bwd.restype = I32
+        lib.gdn2_chunk_bwd_noalloc.argtypes = [P] * 16 + [I64] * 5 + [I32, P]
+        lib.gdn2_chunk_bwd_noalloc.restype = I32
         lib.gdn2_mixer_prep.argtypes = [P] * 15 + [I64] * 5 + [ctypes.c_float, I32, P]
         lib.gdn2_mixer_prep.restype = I32
         lib.gdn2_mixer_out.argtypes = [P] * 4 + [I64] * 4 + [ctypes.c_float, I32, I32, P]
@@ -247,6 +250,46 @@ def chunk_bwd_workspace_bytes(B, T, H, dk, dv) -> int:
     return int(_load().gdn2_chunk_bwd_workspace_bytes(B, T, H, dk, dv))
 
 
+def _bwd_outputs(q, k, v, log_alpha, b, w, d_o, initial_state, d_final_state, grads,
+                 want_initial_state_grad, name):
+    if q.dim() != 4:
+        raise ValueError("q must be [B,T,H,dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("%s runs on the GPU; got tensors on %s" % (name, dev))
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise TypeError("q dtype must be float32 or bfloat16")
+    for nm, t, shp, tdt in (("k", k, (B, T, H, dk), dt), ("v", v, (B, T, H, dv), dt),
+                            ("log_alpha", log_alpha, (B, T, H, dk), torch.float32),
+                            ("b", b, (B, T, H, dk), dt), ("w", w, (B, T, H, dv), dt),
+                            ("q", q, (B, T, H, dk), dt), ("d_o", d_o, (B, T, H, dv), torch.float32)):
+        _check(nm, t, shp, tdt, dev)
+    for nm, t in (("initial_state", initial_state), ("d_final_state", d_final_state)):
+        if t is not None:
+            _check(nm, t, (B, H, dk, dv), torch.float32, dev)
+    shapes = {"dq": (B, T, H, dk), "dk": (B, T, H, dk), "dv": (B, T, H, dv), "dlog_alpha": (B, T, H, dk),
+              "db": (B, T, H, dk), "dw": (B, T, H, dv), "d_initial_state": (B, H, dk, dv)}
+    out = dict(grads) if grads is not None else {}
+    for nm, shp in shapes.items():
+        if nm == "d_initial_state" and not want_initial_state_grad:
+            out[nm] = None
+            continue
+        if out.get(nm) is None:
+            out[nm] = torch.empty(shp, dtype=torch.float32, device=dev)
+        else:
+            _check(nm, out[nm], shp, torch.float32, dev)
+    return (B, T, H, dk, dv, dev, dt), out
+
+
+def _bwd_ptrs(q, k, v, log_alpha, b, w, initial_state, d_o, d_final_state, out):
+    return [_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(initial_state), _ptr(d_o),
+            _ptr(d_final_state), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlog_alpha"]),
+            _ptr(out["db"]), _ptr(out["dw"]), _ptr(out["d_initial_state"])]
+
+
 def chunk_bwd(q, k, v, log_alpha, b, w, d_o, initial_state=None, d_final_state=None, *, workspace=None,
               grads=None, want_initial_state_grad=True):
     """Gradients of sum(d_o * o) + sum(d_final_state * S_T) for the forward chunk_fwd(q, k, v,
@@ -254,47 +297,36 @@ def chunk_bwd(q, k, v, log_alpha, b, w, d_o, initial_state=None, d_final_state=N
     Returns a dict of fp32 tensors dq, dk, dv, dlog_alpha, db, dw and d_initial_state (None
     when not requested).  ``workspace`` (uint8, at least chunk_bwd_workspace_bytes) and
     ``grads`` (a dict of preallocated outputs) may be passed to avoid allocations."""
-    if q.dim() != 4:
-        raise ValueError("q must be [B,T,H,dk]")
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
-    dev = q.device
-    if dev.type != "cuda":
-        raise ValueError("chunk_bwd runs on the GPU; got tensors on %s" % dev)
-    dt = q.dtype
-    if dt not in _DTYPES:
-        raise TypeError("q dtype must be float32 or bfloat16")
-    for name, t, shp, tdt in (("k", k, (B, T, H, dk), dt), ("v", v, (B, T, H, dv), dt),
-                              ("log_alpha", log_alpha, (B, T, H, dk), torch.float32),
-                              ("b", b, (B, T, H, dk), dt), ("w", w, (B, T, H, dv), dt),
-                              ("q", q, (B, T, H, dk), dt), ("d_o", d_o, (B, T, H, dv), torch.float32)):
-        _check(name, t, shp, tdt, dev)
-    for name, t in (("initial_state", initial_state), ("d_final_state", d_final_state)):
-        if t is not None:
-            _check(name, t, (B, H, dk, dv), torch.float32, dev)
-    shapes = {"dq": (B, T, H, dk), "dk": (B, T, H, dk), "dv": (B, T, H, dv), "dlog_alpha": (B, T, H, dk),
-              "db": (B, T, H, dk), "dw": (B, T, H, dv), "d_initial_state": (B, H, dk, dv)}
-    out = dict(grads) if grads is not None else {}
-    for name, shp in shapes.items():
-        if name == "d_initial_state" and not want_initial_state_grad:
-            out[name] = None
-            continue
-        if out.get(name) is None:
-            out[name] = torch.empty(shp, dtype=torch.float32, device=dev)
-        else:
-            _check(name, out[name], shp, torch.float32, dev)
+    (B, T, H, dk, dv, dev, dt), out = _bwd_outputs(q, k, v, log_alpha, b, w, d_o, initial_state, d_final_state,
+                                                   grads, want_initial_state_grad, "chunk_bwd")
     need = chunk_bwd_workspace_bytes(B, T, H, dk, dv)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     elif workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on %s" % dev)
-    st = _load().gdn2_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
-                                _ptr(initial_state), _ptr(d_o), _ptr(d_final_state), _ptr(out["dq"]),
-                                _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlog_alpha"]), _ptr(out["db"]),
-                                _ptr(out["dw"]), _ptr(out["d_initial_state"]), _ptr(workspace),
-                                workspace.numel(), B, T, H, dk, dv, _DTYPES[dt], _stream_handle(dev))
+    st = _load().gdn2_chunk_bwd(*_bwd_ptrs(q, k, v, log_alpha, b, w, initial_state, d_o, d_final_state, out),
+                                _ptr(workspace), workspace.numel(), B, T, H, dk, dv, _DTYPES[dt],
+                                _stream_handle(dev))
     if st != 0:
         raise Gdn2Error("gdn2_chunk_bwd", st, _load().gdn2_status_string(st).decode())
+    return out
+
+
+SCRATCH_BYTES = 64 << 20  # GDN2_SCRATCH_BYTES of include/gdn2.h
+
+
+def chunk_bwd_noalloc(q, k, v, log_alpha, b, w, d_o, initial_state=None, d_final_state=None, *, grads,
+                      want_initial_state_grad=True):
+    """chunk_bwd through gdn2_chunk_bwd_noalloc: the library's fixed device array serves as the
+    workspace, so with ``grads`` preallocated nothing is allocated (for capture into a HIP
+    graph, say).  Sizes whose workspace exceeds SCRATCH_BYTES raise Gdn2Error
+    (GDN2_ERR_WORKSPACE).  Calls that may overlap on one GPU race on the array."""
+    (B, T, H, dk, dv, dev, dt), out = _bwd_outputs(q, k, v, log_alpha, b, w, d_o, initial_state, d_final_state,
+                                                   grads, want_initial_state_grad, "chunk_bwd_noalloc")
+    st = _load().gdn2_chunk_bwd_noalloc(*_bwd_ptrs(q, k, v, log_alpha, b, w, initial_state, d_o, d_final_state,
+                                                   out), B, T, H, dk, dv, _DTYPES[dt], _stream_handle(dev))
+    if st != 0:
+        raise Gdn2Error("gdn2_chunk_bwd_noalloc", st, _load().gdn2_status_string(st).decode())
     return out
 
 

@@ -5,8 +5,10 @@
 // call, so an invalid call enqueues nothing and writes nothing.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/gdn2.h"
 #include "gdn2_launch.h"
@@ -142,6 +144,91 @@ gdn2_status_t chunk_fwd_common(const void* q, const void* k, const void* v, cons
     return gdn2::launch_chunk_fwd(a, dvs) == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
+// The allocation-free backward: its workspace is this file-scope device array, one per GPU the
+// library runs on (held until the process ends).  Host code never uses the array's name as an
+// address: each device's address is looked up once, with that device current, and kept.
+constexpr size_t kScratchBytes = GDN2_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// This device's address of the scratch array (looked up on the first call on the device).
+gdn2_status_t scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GDN2_ERR_HIP;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GDN2_ERR_HIP;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return GDN2_OK;
+}
+
+gdn2_status_t chunk_bwd_common(const void* q, const void* k, const void* v, const float* log_alpha,
+                             const void* b, const void* w, const float* initial_state, const float* d_o,
+                             const float* d_final_state, float* dq, float* dk, float* dv, float* dlog_alpha,
+                             float* db, float* dw, float* d_initial_state, void* workspace,
+                             size_t workspace_bytes, int64_t B, int64_t T, int64_t H, int64_t dk_dim,
+                             int64_t dv_dim, gdn2_dtype_t dtype, void* stream, bool use_scratch) {
+    if (!q || !k || !v || !log_alpha || !b || !w || !d_o) return GDN2_ERR_NULL;
+    if (!dq || !dk || !dv || !dlog_alpha || !db || !dw) return GDN2_ERR_NULL;
+    if (dtype != GDN2_DTYPE_F32 && dtype != GDN2_DTYPE_BF16) return GDN2_ERR_UNSUPPORTED;
+    if (B < 1 || T < 1 || H < 1 || dk_dim < 1 || dv_dim < 1) return GDN2_ERR_SHAPE;
+    if (!chunk_supported(dk_dim, dv_dim, dtype)) return GDN2_ERR_UNSUPPORTED;
+    int64_t BT, NTH, nk, nv, ns;
+    if (B > INT_MAX || T > INT_MAX || H > INT_MAX) return GDN2_ERR_SHAPE;
+    if (!mul_ok(B, T, &BT) || !mul_ok(BT, H, &NTH) || !mul_ok(NTH, dk_dim, &nk) || !mul_ok(NTH, dv_dim, &nv))
+        return GDN2_ERR_SHAPE;
+    if (!mul_ok(B * H, dk_dim * dv_dim, &ns)) return GDN2_ERR_SHAPE;
+    if (H * dk_dim >= (int64_t(1) << 24) || H * dv_dim >= (int64_t(1) << 24)) return GDN2_ERR_SHAPE;
+    BwdLayout l;
+    if (!bwd_layout(B, T, H, dk_dim, dv_dim, &l)) return GDN2_ERR_SHAPE;
+    if (B * H * ((T + 63) / 64) > UINT_MAX / 2 || B * H * (dv_dim / 16) > UINT_MAX / 2) return GDN2_ERR_SHAPE;
+    const void* ptrs[] = {q, k, v, log_alpha, b, w, initial_state, d_o, d_final_state, dq, dk, dv,
+                          dlog_alpha, db, dw, d_initial_state};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDN2_ERR_MISALIGNED;
+    if (use_scratch) {
+        // the scratch array is a separate allocation, so it overlaps no argument
+        if ((size_t)l.total > kScratchBytes) return GDN2_ERR_WORKSPACE;
+        const gdn2_status_t st = scratch_address(&workspace);
+        if (st != GDN2_OK) return st;
+        workspace_bytes = kScratchBytes;
+    }
+    if (!workspace || workspace_bytes < (size_t)l.total) return GDN2_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return GDN2_ERR_MISALIGNED;
+    const int64_t es = dtype == GDN2_DTYPE_BF16 ? 2 : 4;
+    const Range ins[] = {range_of(q, nk * es), range_of(k, nk * es), range_of(v, nv * es),
+                         range_of(log_alpha, nk * 4), range_of(b, nk * es), range_of(w, nv * es),
+                         range_of(initial_state, initial_state ? ns * 4 : 0), range_of(d_o, nv * 4),
+                         range_of(d_final_state, d_final_state ? ns * 4 : 0)};
+    const Range outs[] = {range_of(dq, nk * 4), range_of(dk, nk * 4), range_of(dv, nv * 4),
+                          range_of(dlog_alpha, nk * 4), range_of(db, nk * 4), range_of(dw, nv * 4),
+                          range_of(d_initial_state, d_initial_state ? ns * 4 : 0), range_of(workspace, l.total)};
+    constexpr int NO = sizeof(outs) / sizeof(outs[0]);
+    for (int i = 0; i < NO; ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r)) return GDN2_ERR_ALIAS;
+        for (int j = i + 1; j < NO; ++j)
+            if (overlap(outs[i], outs[j])) return GDN2_ERR_ALIAS;
+    }
+    const int cus = device_cus();
+    if (cus <= 0) return GDN2_ERR_HIP;
+    char* ws = static_cast<char*>(workspace);
+    gdn2::BwdArgs a{q, k, v, log_alpha, b, w, initial_state, d_o, d_final_state, dq, dk, dv, dlog_alpha, db,
+                    dw, d_initial_state, reinterpret_cast<float*>(ws + l.s_ckpt),
+                    reinterpret_cast<float*>(ws + l.ds_ckpt), reinterpret_cast<float*>(ws + l.u),
+                    reinterpret_cast<float*>(ws + l.dr), reinterpret_cast<float*>(ws + l.loc), B, T, H, dk_dim,
+                    dv_dim, dtype == GDN2_DTYPE_BF16, stream, cus};
+    return gdn2::launch_chunk_bwd(a) == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -219,50 +306,19 @@ gdn2_status_t gdn2_chunk_bwd(const void* q, const void* k, const void* v, const 
                              float* db, float* dw, float* d_initial_state, void* workspace,
                              size_t workspace_bytes, int64_t B, int64_t T, int64_t H, int64_t dk_dim,
                              int64_t dv_dim, gdn2_dtype_t dtype, void* stream) {
-    if (!q || !k || !v || !log_alpha || !b || !w || !d_o) return GDN2_ERR_NULL;
-    if (!dq || !dk || !dv || !dlog_alpha || !db || !dw) return GDN2_ERR_NULL;
-    if (dtype != GDN2_DTYPE_F32 && dtype != GDN2_DTYPE_BF16) return GDN2_ERR_UNSUPPORTED;
-    if (B < 1 || T < 1 || H < 1 || dk_dim < 1 || dv_dim < 1) return GDN2_ERR_SHAPE;
-    if (!chunk_supported(dk_dim, dv_dim, dtype)) return GDN2_ERR_UNSUPPORTED;
-    int64_t BT, NTH, nk, nv, ns;
-    if (B > INT_MAX || T > INT_MAX || H > INT_MAX) return GDN2_ERR_SHAPE;
-    if (!mul_ok(B, T, &BT) || !mul_ok(BT, H, &NTH) || !mul_ok(NTH, dk_dim, &nk) || !mul_ok(NTH, dv_dim, &nv))
-        return GDN2_ERR_SHAPE;
-    if (!mul_ok(B * H, dk_dim * dv_dim, &ns)) return GDN2_ERR_SHAPE;
-    if (H * dk_dim >= (int64_t(1) << 24) || H * dv_dim >= (int64_t(1) << 24)) return GDN2_ERR_SHAPE;
-    BwdLayout l;
-    if (!bwd_layout(B, T, H, dk_dim, dv_dim, &l)) return GDN2_ERR_SHAPE;
-    if (B * H * ((T + 63) / 64) > UINT_MAX / 2 || B * H * (dv_dim / 16) > UINT_MAX / 2) return GDN2_ERR_SHAPE;
-    const void* ptrs[] = {q, k, v, log_alpha, b, w, initial_state, d_o, d_final_state, dq, dk, dv,
-                          dlog_alpha, db, dw, d_initial_state};
-    for (const void* p : ptrs)
-        if (p && !aligned16(p)) return GDN2_ERR_MISALIGNED;
-    if (!workspace || workspace_bytes < (size_t)l.total) return GDN2_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return GDN2_ERR_MISALIGNED;
-    const int64_t es = dtype == GDN2_DTYPE_BF16 ? 2 : 4;
-    const Range ins[] = {range_of(q, nk * es), range_of(k, nk * es), range_of(v, nv * es),
-                         range_of(log_alpha, nk * 4), range_of(b, nk * es), range_of(w, nv * es),
-                         range_of(initial_state, initial_state ? ns * 4 : 0), range_of(d_o, nv * 4),
-                         range_of(d_final_state, d_final_state ? ns * 4 : 0)};
-    const Range outs[] = {range_of(dq, nk * 4), range_of(dk, nk * 4), range_of(dv, nv * 4),
-                          range_of(dlog_alpha, nk * 4), range_of(db, nk * 4), range_of(dw, nv * 4),
-                          range_of(d_initial_state, d_initial_state ? ns * 4 : 0), range_of(workspace, l.total)};
-    constexpr int NO = sizeof(outs) / sizeof(outs[0]);
-    for (int i = 0; i < NO; ++i) {
-        for (const Range& r : ins)
-            if (overlap(outs[i], r)) return GDN2_ERR_ALIAS;
-        for (int j = i + 1; j < NO; ++j)
-            if (overlap(outs[i], outs[j])) return GDN2_ERR_ALIAS;
-    }
-    const int cus = device_cus();
-    if (cus <= 0) return GDN2_ERR_HIP;
-    char* ws = static_cast<char*>(workspace);
-    gdn2::BwdArgs a{q, k, v, log_alpha, b, w, initial_state, d_o, d_final_state, dq, dk, dv, dlog_alpha, db,
-                    dw, d_initial_state, reinterpret_cast<float*>(ws + l.s_ckpt),
-                    reinterpret_cast<float*>(ws + l.ds_ckpt), reinterpret_cast<float*>(ws + l.u),
-                    reinterpret_cast<float*>(ws + l.dr), reinterpret_cast<float*>(ws + l.loc), B, T, H, dk_dim,
-                    dv_dim, dtype == GDN2_DTYPE_BF16, stream, cus};
-    return gdn2::launch_chunk_bwd(a) == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+    return chunk_bwd_common(q, k, v, log_alpha, b, w, initial_state, d_o, d_final_state, dq, dk, dv, dlog_alpha,
+                            db, dw, d_initial_state, workspace, workspace_bytes, B, T, H, dk_dim, dv_dim, dtype,
+                            stream, false);
+}
+
+gdn2_status_t gdn2_chunk_bwd_noalloc(const void* q, const void* k, const void* v, const float* log_alpha,
+                                     const void* b, const void* w, const float* initial_state,
+                                     const float* d_o, const float* d_final_state, float* dq, float* dk,
+                                     float* dv, float* dlog_alpha, float* db, float* dw,
+                                     float* d_initial_state, int64_t B, int64_t T, int64_t H,
+                                     int64_t dk_dim, int64_t dv_dim, gdn2_dtype_t dtype, void* stream) {
+    return chunk_bwd_common(q, k, v, log_alpha, b, w, initial_state, d_o, d_final_state, dq, dk, dv, dlog_alpha,
+                            db, dw, d_initial_state, nullptr, 0, B, T, H, dk_dim, dv_dim, dtype, stream, true);
 }
 
 gdn2_status_t gdn2_mixer_prep(const void* xq, const void* xk, const void* xv, const void* xb, const void* xw,

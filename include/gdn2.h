@@ -29,8 +29,10 @@
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
  *     enqueued asynchronously; the caller keeps every buffer alive until the
  *     stream has passed the call.
- *   - The library never allocates, frees or synchronises, keeps no reference
- *     after returning, and has no global mutable state: calls are reentrant.
+ *   - The library never allocates, frees or synchronises and keeps no reference
+ *     after returning.  Its only global state is the per-device address of the
+ *     fixed array gdn2_chunk_bwd_noalloc works in, looked up once under a lock;
+ *     every other call is reentrant.
  *   - All validation happens before anything is enqueued.  On any error the
  *     call returns a non-zero status and writes nothing.  A launch rejected by
  *     the HIP runtime returns GDN2_ERR_HIP.  Faults inside a kernel surface at
@@ -205,6 +207,37 @@ gdn2_status_t gdn2_chunk_bwd(const void* q, const void* k, const void* v,
                              void* workspace, size_t workspace_bytes, int64_t B, int64_t T,
                              int64_t H, int64_t dk_dim, int64_t dv_dim, gdn2_dtype_t dtype,
                              void* stream);
+
+/* Bytes of the device array that gdn2_chunk_bwd_noalloc uses as its workspace (64 MiB). */
+#define GDN2_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * gdn2_chunk_bwd_noalloc -- gdn2_chunk_bwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving or training loops,
+ * harnesses that forbid hipMalloc): the same gradients, computed by the same
+ * kernels, with the workspace taken from a fixed array of GDN2_SCRATCH_BYTES
+ * inside the library instead of from the caller.  Nothing is allocated or freed.
+ *
+ *   arguments       as for gdn2_chunk_bwd, without workspace / workspace_bytes
+ *
+ * Calls whose gdn2_chunk_bwd_workspace_bytes(B, T, H, dk, dv) exceeds
+ * GDN2_SCRATCH_BYTES return GDN2_ERR_WORKSPACE (for example B = 1, H = 16,
+ * dk = dv = 128 fits up to T = 576).  Each GPU the library runs on holds its own
+ * array from the first call on that device until the process ends; the first
+ * call on a device looks up the array's address (GDN2_ERR_HIP if that fails).
+ * Every call on one GPU uses that GPU's one array, which keeps the last call's
+ * contents: calls that may run at the same time on one GPU (different streams,
+ * different host threads without ordering) race and must not overlap.  No part
+ * of the array needs clearing: every call writes each slot before reading it.
+ */
+gdn2_status_t gdn2_chunk_bwd_noalloc(const void* q, const void* k, const void* v,
+                                     const float* log_alpha, const void* b, const void* w,
+                                     const float* initial_state, const float* d_o,
+                                     const float* d_final_state, float* dq, float* dk, float* dv,
+                                     float* dlog_alpha, float* db, float* dw,
+                                     float* d_initial_state, int64_t B, int64_t T, int64_t H,
+                                     int64_t dk_dim, int64_t dv_dim, gdn2_dtype_t dtype,
+                                     void* stream);
 
 /*
  * gdn2_mixer_prep -- the elementwise steps between the layer's projections and

@@ -284,3 +284,25 @@ def test_mixer_validation(lib):
     assert mout(lib, f, y=f.p(3, 4)) == ERR_MISALIGNED
     assert mout(lib, f, y=f.p(0, 64)) == ERR_ALIAS
     assert mout(lib, f, y=f.p(2)) == ERR_ALIAS
+
+
+def bwd_noalloc(lib, f, B=1, T=64, H=1, dk=64, dv=64, dtype=BF16, **over):
+    names = ("q k v g b w s0 do dsT gq gk gv gg gb gw gs0").split()
+    args = {n: f.p(i) for i, n in enumerate(names)}
+    args["s0"] = args["dsT"] = args["gs0"] = None
+    args.update(over)
+    return lib.gdn2_chunk_bwd_noalloc(*[args[n] for n in names], B, T, H, dk, dv, dtype, None)
+
+
+def test_bwd_noalloc_validation(lib):
+    """The allocation-free backward validates like gdn2_chunk_bwd, and a size whose workspace
+    exceeds the library's array (64 MiB) is GDN2_ERR_WORKSPACE, all before any HIP call."""
+    f = Fake(slots=18)
+    assert bwd_noalloc(lib, f, q=None) == ERR_NULL
+    assert bwd_noalloc(lib, f, B=0) == ERR_SHAPE
+    assert bwd_noalloc(lib, f, dk=96, dv=96) == ERR_UNSUPPORTED
+    assert bwd_noalloc(lib, f, gq=f.p(9, 4)) == ERR_MISALIGNED
+    assert gdn2.SCRATCH_BYTES == 64 << 20
+    assert lib.gdn2_chunk_bwd_workspace_bytes(1, 640, 16, 128, 128) > gdn2.SCRATCH_BYTES
+    assert lib.gdn2_chunk_bwd_workspace_bytes(1, 576, 16, 128, 128) <= gdn2.SCRATCH_BYTES
+    assert bwd_noalloc(lib, f, T=640, H=16, dk=128, dv=128) == ERR_WORKSPACE
