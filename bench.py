@@ -106,7 +106,23 @@ DECODE_PROFILE = ("decode_step_N256_H16_d128.md", ("gdn2_decode.hip", "gdn2_devi
 PREFILL_PROFILE = ("prefill_varlen_N64_H16_d128.md", ("gdn2_chunk_bf16.hip", "gdn2_device.h"))
 
 
-def time_launches(fn, steps, warmup, torch):
+def spin_up(fn, torch, seconds=0.3):
+    """Run fn untimed for about `seconds` of GPU time: the GPU's clocks ramp up over the first
+    tenths of a second of work, and a short warm-up alone times a cold GPU."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds or n < 2:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
+def time_launches(fn, steps, warmup, torch, spin=True):
+    if spin:
+        spin_up(fn, torch)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -173,19 +189,23 @@ def run_chunk(args, torch, gdn2, W, dev, out_dtype, keep=False):
     del inp
     o = torch.empty((wl.B, wl.T, wl.H, wl.dv), dtype=out_dtype, device=dev)
     sT = torch.empty((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdn2.chunk_fwd_workspace_bytes(wl.B, wl.T, wl.H, wl.dk, wl.dv, split=True) + 256,
+                     dtype=torch.uint8, device=dev)
 
-    def step():
+    def step(fused=None):
         gdn2.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["s0"], o=o,
-                       final_state=sT, out_dtype=out_dtype)
+                       final_state=sT, out_dtype=out_dtype, workspace=ws, fused=fused)
 
     ms = time_launches(step, args.steps, args.warmup, torch)
+    forms = {"fused": time_launches(lambda: step(True), args.steps, args.warmup, torch),
+             "split": time_launches(lambda: step(False), args.steps, args.warmup, torch)}
     nbytes = chunk_bytes(wl.B, wl.T, wl.H, wl.dk, wl.dv)
-    del o, sT
+    del o, sT, ws
     if not keep:
         del d
         d = None
     torch.cuda.empty_cache()
-    return ms, wl, nbytes, d
+    return ms, wl, nbytes, d, forms
 
 
 def run_long(args, torch, gdn2, W, dev, out_dtype):
@@ -197,19 +217,24 @@ def run_long(args, torch, gdn2, W, dev, out_dtype):
     del inp
     o = torch.empty((wl.B, wl.T, wl.H, wl.dv), dtype=out_dtype, device=dev)
     sT = torch.empty((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdn2.chunk_fwd_workspace_bytes(wl.B, wl.T, wl.H, wl.dk, wl.dv, split=True) + 256,
+                     dtype=torch.uint8, device=dev)
 
-    def step():
+    def step(fused=None):
         gdn2.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["s0"], o=o,
-                       final_state=sT, out_dtype=out_dtype)
+                       final_state=sT, out_dtype=out_dtype, workspace=ws, fused=fused)
 
     ms = time_launches(step, max(3, args.steps // 4), 2, torch)
+    ms_fused = time_launches(lambda: step(True), 3, 1, torch)
+    ms_split = time_launches(lambda: step(False), 3, 1, torch, spin=False)
     nbytes = chunk_bytes(wl.B, wl.T, wl.H, wl.dk, wl.dv)
     gbps = nbytes / (ms * 1e-3) / 1e9
-    del d, o, sT
+    del d, o, sT, ws
     torch.cuda.empty_cache()
     return {"workload": wl.name, "us_per_launch": ms * 1e3, "tokens_per_s": wl.B * wl.T / (ms * 1e-3),
             "GBps": gbps, "peak": HBM_PEAK_GBPS, "frac": gbps / HBM_PEAK_GBPS,
-            "algorithmic_bytes_per_launch": nbytes,
+            "algorithmic_bytes_per_launch": nbytes, "fused_us": ms_fused * 1e3, "split_us": ms_split * 1e3,
+            "form": "split" if gdn2.chunk_fwd_workspace_bytes(wl.B, wl.T, wl.H, wl.dk, wl.dv) else "fused",
             "note": "B*H = 16 (sequence, head) chains of 512 chunks each"}
 
 
@@ -222,17 +247,22 @@ def run_sweep(args, torch, gdn2, d, dev, out_dtype, H=16, dk=128, dv=128, total=
         v = {n: x.view(B, T, *x.shape[2:]) for n, x in d.items() if x is not None}
         o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
         sT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        ws = torch.empty(gdn2.chunk_fwd_workspace_bytes(B, T, H, dk, dv, split=True) + 256, dtype=torch.uint8,
+                         device=dev)
 
-        def step():
+        def step(fused=None):
             gdn2.chunk_fwd(v["q"], v["k"], v["v"], v["log_alpha"], v["b"], v["w"], None, o=o, final_state=sT,
-                           out_dtype=out_dtype)
+                           out_dtype=out_dtype, workspace=ws, fused=fused)
 
         ms = time_launches(step, max(3, args.steps // 4), 2, torch)
+        ms_fused = time_launches(lambda: step(True), 3, 1, torch, spin=False)
+        ms_split = time_launches(lambda: step(False), 3, 1, torch, spin=False)
         nbytes = chunk_bytes(B, T, H, dk, dv)
         gbps = nbytes / (ms * 1e-3) / 1e9
         out.append({"T": T, "B": B, "us_per_launch": ms * 1e3, "tokens_per_s": total / (ms * 1e-3),
-                    "frac": gbps / HBM_PEAK_GBPS})
-        del o, sT
+                    "frac": gbps / HBM_PEAK_GBPS, "fused_us": ms_fused * 1e3, "split_us": ms_split * 1e3,
+                    "form": "split" if gdn2.chunk_fwd_workspace_bytes(B, T, H, dk, dv) else "fused"})
+        del o, sT, ws
     torch.cuda.empty_cache()
     return out
 
@@ -361,7 +391,7 @@ def run_decode(args, torch, gdn2, W, dev, out_dtype):
                              out_dtype=out_dtype)
 
     loop()  # warm-up pass over the whole loop
-    dms = time_launches(loop, 1, 0, torch) / nsteps
+    dms = time_launches(loop, 1, 0, torch, spin=False) / nsteps
     dbytes = decode_bytes(dwl.B, dwl.H, dwl.dk, dwl.dv, out_bytes=out_dtype.itemsize)
     dgbps = dbytes / (dms * 1e-3) / 1e9
     graph = None
@@ -374,7 +404,7 @@ def run_decode(args, torch, gdn2, W, dev, out_dtype):
                 loop()
         torch.cuda.current_stream().wait_stream(side)
         g.replay()  # first replay uploads the graph
-        gms = time_launches(g.replay, 1, 0, torch) / nsteps
+        gms = time_launches(g.replay, 1, 0, torch, spin=False) / nsteps
         ggbps = dbytes / (gms * 1e-3) / 1e9
         graph = {"us_per_step": gms * 1e3, "state_GBps": ggbps, "frac": ggbps / HBM_PEAK_GBPS,
                  "steps": nsteps}
@@ -435,11 +465,12 @@ def main():
     if args.only in only:
         print(json.dumps(only[args.only]()), flush=True)
         return
-    ms, wl, nbytes, d = run_chunk(args, torch, gdn2, W, dev, out_dtype, keep=True)
+    ms, wl, nbytes, d, forms = run_chunk(args, torch, gdn2, W, dev, out_dtype, keep=True)
     tokens = wl.B * wl.T
     achieved = nbytes / (ms * 1e-3) / 1e9
     if args.only == "chunk":
         print(json.dumps({"workload": wl.name, "avg_launch_us": ms * 1e3,
+                          "forms_us": {f: t * 1e3 for f, t in forms.items()},
                           "tokens_per_s": tokens / (ms * 1e-3), "achieved_GBps": achieved}), flush=True)
         return
     sweep = run_sweep(args, torch, gdn2, d, dev, out_dtype)
@@ -478,7 +509,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": recorded_traffic(*CHUNK_PROFILE) if not args.out_bf16 else None,
-                     "kernel": "chunk_bf16_kernel", "algorithmic_bytes_per_launch": nbytes,
+                     "kernel": "chunk_bf16_kernel" if not gdn2.chunk_fwd_workspace_bytes(
+                         wl.B, wl.T, wl.H, wl.dk, wl.dv) else "local_kernel + state_kernel",
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "forms_us": {f: t * 1e3 for f, t in forms.items()},
                      "bytes_per_head_token": 3 * wl.dk * 2 + 2 * wl.dv * 2 + wl.dk * 4 + wl.dv * 2,
                      "fp32_o_extra_bytes_per_launch": extra,
                      "frac_with_fp32_o_bytes": (nbytes + extra) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,

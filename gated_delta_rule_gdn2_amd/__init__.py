@@ -67,6 +67,8 @@ def _load():
         lib.gdn2_chunk_fwd.restype = I32
         lib.gdn2_chunk_fwd_workspace_bytes.argtypes = [I64] * 5 + [I32]
         lib.gdn2_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.gdn2_chunk_fwd_split_workspace_bytes.argtypes = [I64] * 5 + [I32]
+        lib.gdn2_chunk_fwd_split_workspace_bytes.restype = ctypes.c_size_t
         lib.gdn2_chunk_fwd_varlen.argtypes = [P] * 10 + [I64] * 5 + [I32, I32, P]
         lib.gdn2_chunk_fwd_varlen.restype = I32
         lib.gdn2_decode_step.argtypes = [P] * 8 + [I64] * 4 + [I32, I32, P]
@@ -121,10 +123,14 @@ def _stream_handle(device):
 
 
 def chunk_fwd(q, k, v, log_alpha, b, w, initial_state=None, *, o=None, final_state=None,
-              output_final_state=True, out_dtype=torch.float32):
+              output_final_state=True, out_dtype=torch.float32, workspace=None, fused=None):
     """Chunk-parallel forward.  Returns (o, S_T); S_T is None when
     ``output_final_state`` is False.  ``final_state`` may be passed (and may be
-    ``initial_state`` itself, for an in-place update)."""
+    ``initial_state`` itself, for an in-place update).  ``fused=None`` runs the
+    form the library reports faster for the shape (chunk_fwd_workspace_bytes);
+    ``fused=True`` the single fused kernel; ``fused=False`` the two-kernel form
+    where it exists (bf16, d = 64 or 128).  The two-kernel form's workspace is
+    allocated here unless ``workspace`` (uint8) is passed."""
     if q.dim() != 4:
         raise ValueError("q must be [B,T,H,dk]")
     B, T, H, dk = q.shape
@@ -152,11 +158,24 @@ def chunk_fwd(q, k, v, log_alpha, b, w, initial_state=None, *, o=None, final_sta
         final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     elif final_state is not None:
         _check("final_state", final_state, (B, H, dk, dv), torch.float32, dev)
-    ws_bytes = _load().gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, _DTYPES[dt])
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    if fused is None:
+        ws_bytes = _load().gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, _DTYPES[dt])
+    else:
+        ws_bytes = 0 if fused else _load().gdn2_chunk_fwd_split_workspace_bytes(B, T, H, dk, dv, _DTYPES[dt])
+    ws = None
+    if ws_bytes:
+        if workspace is None:
+            workspace = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
+        elif workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 tensor on %s" % dev)
+        off = (-workspace.data_ptr()) % 256  # 256-byte alignment
+        ws = workspace[off:]
+        if ws.numel() < ws_bytes:
+            raise ValueError("workspace holds %d bytes, %d needed" % (ws.numel(), ws_bytes))
     st = _load().gdn2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
                                 _ptr(initial_state), _ptr(o), _ptr(final_state), B, T, H, dk, dv,
-                                _DTYPES[dt], _DTYPES[out_dtype], _ptr(ws), ws_bytes, _stream_handle(dev))
+                                _DTYPES[dt], _DTYPES[out_dtype], _ptr(ws), ws.numel() if ws is not None else 0,
+                                _stream_handle(dev))
     if st != 0:
         raise Gdn2Error("gdn2_chunk_fwd", st, _load().gdn2_status_string(st).decode())
     return o, final_state
@@ -240,9 +259,11 @@ def decode_step(q, k, v, log_alpha, b, w, state, *, o=None, out_dtype=torch.floa
     return o
 
 
-def chunk_fwd_workspace_bytes(B, T, H, dk, dv, dtype=torch.bfloat16) -> int:
-    """Device workspace (bytes) that chunk_fwd needs for these sizes (0: the forward is fused)."""
-    return int(_load().gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, _DTYPES[dtype]))
+def chunk_fwd_workspace_bytes(B, T, H, dk, dv, dtype=torch.bfloat16, split=False) -> int:
+    """Device workspace (bytes) of chunk_fwd's faster form for these sizes (0: the fused kernel);
+    with ``split=True``, that of the two-kernel form whichever is faster (0 where it does not exist)."""
+    f = _load().gdn2_chunk_fwd_split_workspace_bytes if split else _load().gdn2_chunk_fwd_workspace_bytes
+    return int(f(B, T, H, dk, dv, _DTYPES[dtype]))
 
 
 def chunk_bwd_workspace_bytes(B, T, H, dk, dv) -> int:

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libgdn2.so")
 OBJDIR = os.path.join(HERE, "_build")
 
-SOURCES = ["gdn2_api.hip", "gdn2_chunk_fwd.hip", "gdn2_chunk_bf16.hip", "gdn2_chunk_bwd.hip", "gdn2_decode.hip", "gdn2_mixer.hip"]
+SOURCES = ["gdn2_api.hip", "gdn2_chunk_fwd.hip", "gdn2_chunk_bf16.hip", "gdn2_chunk_split.hip", "gdn2_chunk_bwd.hip", "gdn2_decode.hip", "gdn2_mixer.hip"]
 ARCH = "gfx950"
 
 COMMON = [

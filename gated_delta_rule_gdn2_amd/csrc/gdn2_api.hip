@@ -38,6 +38,10 @@ bool chunk_supported(int64_t dk, int64_t dv, gdn2_dtype_t dt) {
     if (dt == GDN2_DTYPE_F32) return dk == 64 && dv == 64;
     return false;
 }
+// the two-kernel forward: bf16 inputs, dk = dv = 64 or 128, sequences of one length
+bool split_supported(bool packed, int64_t dk, int64_t dv, gdn2_dtype_t dt) {
+    return !packed && dt == GDN2_DTYPE_BF16 && dk == dv && (dk == 64 || dk == 128);
+}
 bool mixer_supported(int64_t dk, int64_t dv, gdn2_dtype_t dt) {
     if (dt != GDN2_DTYPE_BF16 && dt != GDN2_DTYPE_F32) return false;
     return (dk == 128 && dv == 128) || (dk == 64 && dv == 64);
@@ -98,7 +102,8 @@ gdn2_status_t chunk_fwd_common(const void* q, const void* k, const void* v, cons
                                const void* b, const void* w, const float* initial_state, void* o,
                                float* final_state, const int64_t* cu_seqlens, int64_t NS,
                                int64_t T_or_total, int64_t NT, int64_t H, int64_t dk, int64_t dv,
-                               gdn2_dtype_t dtype, gdn2_dtype_t o_dtype, void* stream) {
+                               gdn2_dtype_t dtype, gdn2_dtype_t o_dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
     if (!q || !k || !v || !log_alpha || !b || !w || !o) return GDN2_ERR_NULL;
     if (dtype != GDN2_DTYPE_F32 && dtype != GDN2_DTYPE_BF16) return GDN2_ERR_UNSUPPORTED;
     if (o_dtype != GDN2_DTYPE_F32 && o_dtype != dtype) return GDN2_ERR_UNSUPPORTED;
@@ -135,11 +140,27 @@ gdn2_status_t chunk_fwd_common(const void* q, const void* k, const void* v, cons
         if (initial_state && initial_state != final_state && overlap(rf, range_of(initial_state, ns * 4)))
             return GDN2_ERR_ALIAS;
     }
+    // the two-kernel path when the caller passes its workspace, else the single fused kernel
+    const bool split = workspace != nullptr || workspace_bytes != 0;
+    if (split) {
+        const size_t need = split_supported(cu_seqlens != nullptr, dk, dv, dtype)
+                                ? gdn2_chunk_fwd_split_workspace_bytes(NS, T_or_total, H, dk, dv, dtype) : 0;
+        if (need == 0) return GDN2_ERR_WORKSPACE;  // this call takes no workspace
+        if (!workspace || workspace_bytes < need) return GDN2_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(workspace) & 255u) return GDN2_ERR_MISALIGNED;
+        const Range rw = range_of(workspace, (int64_t)need);
+        for (const Range& r : in_ranges)
+            if (overlap(rw, r)) return GDN2_ERR_ALIAS;
+        if (overlap(rw, ro) || (initial_state && overlap(rw, range_of(initial_state, ns * 4))) ||
+            (final_state && overlap(rw, range_of(final_state, ns * 4))))
+            return GDN2_ERR_ALIAS;
+    }
     if (NT == 0 && !final_state) return GDN2_OK;  // nothing to compute or write
     const int cus = device_cus();
     if (cus <= 0) return GDN2_ERR_HIP;
     gdn2::ChunkArgs a{q, k, v, log_alpha, b, w, initial_state, o, final_state, NS, T_or_total, H, dk, dv,
-                      dtype == GDN2_DTYPE_BF16, o_dtype == GDN2_DTYPE_F32, stream, cu_seqlens};
+                      dtype == GDN2_DTYPE_BF16, o_dtype == GDN2_DTYPE_F32, stream, cu_seqlens, cus};
+    if (split) return gdn2::launch_chunk_split(a, workspace) == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
     const int dvs = choose_dvs(NS * H, dv, cus);
     return gdn2::launch_chunk_fwd(a, dvs) == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
@@ -233,10 +254,22 @@ gdn2_status_t chunk_bwd_common(const void* q, const void* k, const void* v, cons
 
 extern "C" {
 
+size_t gdn2_chunk_fwd_split_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                            gdn2_dtype_t dtype) {
+    if (!split_supported(false, dk, dv, dtype) || B < 1 || T < 1 || H < 1 || B > INT_MAX || T > INT_MAX ||
+        H > INT_MAX || B * H > INT_MAX / 64)
+        return 0;
+    return gdn2::split_workspace_bytes(B, T, H, dk);
+}
+
 size_t gdn2_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                                       gdn2_dtype_t dtype) {
-    (void)B; (void)T; (void)H; (void)dk; (void)dv; (void)dtype;
-    return 0;  // one fused kernel: every intermediate lives in registers and LDS
+    // The fused kernel walks each (sequence, head, 64-column slice) on one compute unit; when
+    // those chains cannot fill the GPU, the two-kernel form is faster (its chunk-local work is
+    // spread over every chunk).  Below that point the fused kernel needs no workspace.
+    const int64_t cus = device_cus() > 0 ? device_cus() : 256;
+    if (B < 1 || H < 1 || B > INT_MAX || H > INT_MAX || B * H * ((dv + 63) / 64) >= cus) return 0;
+    return gdn2_chunk_fwd_split_workspace_bytes(B, T, H, dk, dv, dtype);
 }
 
 gdn2_status_t gdn2_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -247,10 +280,8 @@ gdn2_status_t gdn2_chunk_fwd(const void* q, const void* k, const void* v, const 
     if (B < 1 || T < 1) return GDN2_ERR_SHAPE;
     int64_t BT;
     if (!mul_ok(B, T, &BT)) return GDN2_ERR_SHAPE;
-    const size_t need = gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, dtype);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return GDN2_ERR_WORKSPACE;
     return chunk_fwd_common(q, k, v, log_alpha, b, w, initial_state, o, final_state, nullptr, B, T, BT, H,
-                            dk, dv, dtype, o_dtype, stream);
+                            dk, dv, dtype, o_dtype, workspace, workspace_bytes, stream);
 }
 
 gdn2_status_t gdn2_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -262,7 +293,7 @@ gdn2_status_t gdn2_chunk_fwd_varlen(const void* q, const void* k, const void* v,
     if (N < 1 || total_T < 0) return GDN2_ERR_SHAPE;
     if (reinterpret_cast<uintptr_t>(cu_seqlens) & 7u) return GDN2_ERR_MISALIGNED;
     return chunk_fwd_common(q, k, v, log_alpha, b, w, initial_state, o, final_state, cu_seqlens, N, total_T,
-                            total_T, H, dk, dv, dtype, o_dtype, stream);
+                            total_T, H, dk, dv, dtype, o_dtype, nullptr, 0, stream);
 }
 
 gdn2_status_t gdn2_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,

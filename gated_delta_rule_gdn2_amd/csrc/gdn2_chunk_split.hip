@@ -1,0 +1,883 @@
+// gdn2_chunk_split.hip -- the chunk forward in two kernels, bf16 inputs, gfx950.
+//
+// The recurrence (page "Why NVIDIA Gated DeltaNet-2 separates erase and write gates",
+// axbrief.com, section "Gated Delta Rule-2"; chunk size 64 from the same section) in chunk
+// form (the WY form of a block of rank-1 updates, page "Why Qwen3.5 chose Gated DeltaNet",
+// laonpeople.com, section on the WY representation):
+//
+//   A[i,j] = sum_c (b.k)_ic Gamma_{i<-j,c} k_jc  (j < i),     P[i,j] = the same with q_i (j <= i)
+//   T = (I + A)^{-1},   U = T (w.v - BG S),   O = QG S + P U,   S_next = Diag(Gamma_C) S + KG^T U
+//
+// with QG = q.Gamma, BG = (b.k).Gamma (Gamma: decay from the chunk start through the token) and
+// KG = k.Gamma' (Gamma': decay after the token to the chunk end).  Everything but the last line's
+// S-products depends on the chunk's own tokens only, so it is formed for every chunk at once:
+//
+//   * local_kernel: one workgroup per run of consecutive chunks of a (sequence, head), the next
+//     chunk's inputs loaded one chunk ahead.  Per chunk it forms QG, BG, KG^T, Gamma_C, P and T -- the decay pivoting,
+//     the A / P products and the triangular inverse of the fused forward (gdn2_bf16_ops.h) --
+//     and writes them as one record.
+//   * state_kernel: one workgroup of four waves per (sequence, head, 64 value columns); wave w
+//     owns 16 columns of the state for all dk rows, in MFMA accumulators, for the whole
+//     sequence.  Per chunk: R = w.v - BG S and Y = QG S (S as a hi / lo bf16 pair), U = T R,
+//     O = Y + P U, S <- Gamma_C S + KG^T U, all in that wave's registers; the record is staged
+//     into LDS one chunk ahead, the only data the waves share.
+//
+// The host walks the chunks in batches of about a thousand chunk-heads: the local kernel for a
+// batch, then the state kernel for it, so a batch's records (about 74 KB per chunk-head) are
+// read back while the GPU's last-level cache still holds them.
+//
+// Record of one chunk-head (D = dk = dv), each part row-major:
+//   QG [64][D] bf16 | BG [64][D] bf16 | KG^T [D][64] bf16 |
+//   T hi, T lo: rows 0-31 x cols 0-31, then rows 32-63 x cols 0-63 (bf16; blocks above the
+//   diagonal blocks are zero) | P hi, P lo: the same | Gamma_C [D] fp32.
+
+#include "gdn2_bf16_ops.h"
+#include "gdn2_launch.h"
+
+namespace gdn2 {
+namespace sp {
+
+using cb::C;
+
+// ------------------------------------------------------------------ record layout ----
+template <int D>
+struct Rec {
+    static constexpr int QG = 0;
+    static constexpr int BG = QG + C * D * 2;
+    static constexpr int KGT = BG + C * D * 2;
+    static constexpr int TRI = 32 * 32 + 32 * 64;  // elements of one plane of T or P
+    static constexpr int T = KGT + D * C * 2;      // hi plane, then lo plane
+    static constexpr int P = T + 2 * TRI * 2;
+    static constexpr int GC = P + 2 * TRI * 2;
+    // padded to whole rounds of the state kernel's staging (256 threads x 16 bytes)
+    static constexpr int BYTES = (GC + D * 4 + 4095) / 4096 * 4096;
+    static constexpr int UNITS = BYTES / 16;
+};
+
+// element (row, col) of a triangle plane: rows 0-31 hold cols 0-31, rows 32-63 cols 0-63
+__device__ __forceinline__ int tri_index(int row, int col) {
+    return row < 32 ? row * 32 + col : 1024 + (row - 32) * 64 + col;
+}
+
+// ------------------------------------------------------------------ local kernel ----
+constexpr int NT_LOCAL = 512;
+
+// LDS layout of the local kernel (bytes), at most 80 KiB.
+// RX: 192 rows of LDK bf16 -- mild chunk: BG rows 0-63, k / Gamma rows 64-127, QG rows 128-191;
+// strong chunk: the pivoted group and level tiles.  AM: -A below the diagonal blocks; TR, TTR:
+// the diagonal blocks of T and their transposes (the block inverses' inputs to T_C).  The block
+// decays and strong-decay votes of the element phase share AM's bytes (a barrier separates the
+// uses).
+template <int DK>
+struct LocalCfg {
+    static constexpr int CPL = DK / 32;
+    static constexpr int LDK = DK + 8;
+    static constexpr int LC = C + 8;
+    static constexpr int RX = 0;
+    static constexpr int QGR = RX + 2 * C * LDK * 2;  // mild: QG rows inside RX
+    static constexpr int AM = RX + 192 * LDK * 2;
+    static constexpr int BLK = AM;                    // [4][DK] fp32 block decays (element phase)
+    static constexpr int FLG = BLK + 4 * DK * 4;      // [8] int votes (element phase)
+    static constexpr int TR = AM + C * LC * 2;
+    static constexpr int TTR = TR + C * LC * 2;
+    static constexpr int BYTES = TTR + C * LC * 2;
+    static_assert(BYTES <= 81920, "LDS budget");
+    static_assert(FLG + 32 <= TR, "votes inside AM");
+};
+
+template <int CPL>
+struct InK {
+    Vec<float, CPL> g[4];
+    Vec<bf16, CPL> q[4], k[4], b[4];
+};
+
+// 4 consecutive values of a row as hi and lo bf16 planes of a record
+__device__ __forceinline__ void put_split4(char* rec_plane_hi, char* rec_plane_lo, int idx, const float (&x)[4]) {
+    bf16x4 h, l;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        bf16 a, b;
+        cb::split_bf16(x[r], a, b);
+        h[r] = a;
+        l[r] = b;
+    }
+    *reinterpret_cast<bf16x4*>(rec_plane_hi + idx * 2) = h;
+    *reinterpret_cast<bf16x4*>(rec_plane_lo + idx * 2) = l;
+}
+
+template <int DK>
+__global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ log_alpha,
+    const bf16* __restrict__ bgate, char* __restrict__ recs, int Tparam, int H, int c_begin, int c_end,
+    int run) {
+    using G = LocalCfg<DK>;
+    using R = Rec<DK>;
+    constexpr int CPL = G::CPL, LDK = G::LDK, LC = G::LC;
+    __shared__ __attribute__((aligned(16))) char smem[G::BYTES];
+    bf16* sA = reinterpret_cast<bf16*>(smem + G::AM);
+    float* sBLK = reinterpret_cast<float*>(smem + G::BLK);
+    auto B16 = [&](int byte_off) { return reinterpret_cast<bf16*>(smem + byte_off); };
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nb = c_end - c_begin;                 // chunks per head in this batch
+    const int runs = (nb + run - 1) / run;
+    const int bh = blockIdx.x / runs;
+    const int rr = blockIdx.x % runs;
+    const int cr0 = rr * run;                       // first chunk of the run, batch-relative
+    const int cr1 = min(cr0 + run, nb);
+    const int h = bh % H;
+    const int Tlen = Tparam;
+    const int64_t tok0 = (int64_t)(bh / H) * Tparam;
+
+    const int I = wave & 3, hf = wave >> 2;         // element phase: token block, channel half
+    const int64_t tok_stride_k = (int64_t)H * DK;
+    const int64_t seq_base_k = (tok0 * H + h) * DK;
+    const int rsk = H * DK;
+
+    auto load_first = [&](int n, InK<CPL>& in) {
+        const int lane = tid & 63, ts = lane >> 4;
+        const int c0 = hf * (DK / 2) + (lane & 15) * CPL;
+        const int t0 = n * C, last = Tlen - 1 - t0;
+        const int64_t cbase = seq_base_k + (int64_t)t0 * tok_stride_k;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint32_t e = __umul24(min(I * 16 + ts * 4 + m, last), rsk) + c0;
+            in.g[m] = cb::gload<float, CPL>(log_alpha + cbase, e * 4);
+            in.q[m] = cb::gload<bf16, CPL>(q + cbase, e * 2);
+        }
+    };
+    auto load_second = [&](int n, InK<CPL>& in) {
+        const int lane = tid & 63, ts = lane >> 4;
+        const int c0 = hf * (DK / 2) + (lane & 15) * CPL;
+        const int t0 = n * C, last = Tlen - 1 - t0;
+        const int64_t cbase = seq_base_k + (int64_t)t0 * tok_stride_k;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint32_t e = __umul24(min(I * 16 + ts * 4 + m, last), rsk) + c0;
+            in.k[m] = cb::gload<bf16, CPL>(k + cbase, e * 2);
+            in.b[m] = cb::gload<bf16, CPL>(bgate + cbase, e * 2);
+        }
+    };
+
+    InK<CPL> in;
+    if (cr0 < cr1) {
+        load_first(c_begin + cr0, in);
+        load_second(c_begin + cr0, in);
+    }
+
+    for (int cr = cr0; cr < cr1; ++cr) {
+        const int n = c_begin + cr;                 // chunk index in the sequence
+        const int t0 = n * C;
+        const int nnext = cr + 1 < cr1 ? n + 1 : n;
+        char* rec = recs + ((int64_t)bh * nb + cr) * R::BYTES;
+        const int tidv = cb::opq(tid);
+        const int lane = tidv & 63;
+        const int l16 = lane & 15, g4 = lane >> 4, ts = lane >> 4;
+        const int c0 = hf * (DK / 2) + (lane & 15) * CPL;
+        // =============== element phase, pass 1: decays within the block ===============
+        if (t0 + C > Tlen) {
+            // tokens past the end of the sequence act as the identity: no decay, no read, no write
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                if (t0 + I * 16 + ts * 4 + m >= Tlen) {
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) {
+                        in.g[m].v[c] = 0.f;
+                        in.q[m].v[c] = (bf16)0.f;
+                        in.k[m].v[c] = (bf16)0.f;
+                        in.b[m].v[c] = (bf16)0.f;
+                    }
+                }
+            }
+        }
+        float lp[CPL][4], ls[CPL][4], ex[CPL], es[CPL];
+        {
+            float blkv[CPL];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                float al[4];
+                float p = 1.f;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    al[m] = exp_neg(in.g[m].v[c]);
+                    p *= al[m];
+                    lp[c][m] = p;
+                }
+                float sfx = 1.f;
+#pragma unroll
+                for (int m = 3; m >= 0; --m) { ls[c][m] = sfx; sfx *= al[m]; }
+                const float x16 = __shfl_xor(p, 16), x32 = __shfl_xor(p, 32), x48 = __shfl_xor(p, 48);
+                const float x3248 = x32 * x48;
+                ex[c] = ((ts & 1) ? x16 : 1.f) * ((ts & 2) ? x3248 : 1.f);
+                es[c] = ((ts & 1) ? 1.f : x16) * ((ts & 2) ? 1.f : x3248);
+                blkv[c] = ex[c] * p * es[c];
+            }
+            bool low = false;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) low |= !(blkv[c] >= 0x1p-16f);
+            const int vote = __any(low);
+            if (lane == 0) *reinterpret_cast<int*>(smem + G::FLG + wave * 4) = vote;
+            if (ts == 0) {
+                typedef float V __attribute__((ext_vector_type(CPL)));
+                V x;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) x[c] = blkv[c];
+                *reinterpret_cast<V*>(sBLK + I * DK + c0) = x;
+            }
+        }
+        cb::lds_barrier();
+
+        // =============== element phase, pass 2: scaled operands ===============
+        float blk[CPL][4], invgc[CPL];
+        int strong;
+        {
+            const int4 f0 = *reinterpret_cast<const int4*>(smem + G::FLG);
+            const int4 f1 = *reinterpret_cast<const int4*>(smem + G::FLG + 16);
+            strong = (f0.x | f0.y | f0.z | f0.w | f1.x | f1.y | f1.z | f1.w) != 0;
+            Vec<float, CPL> bl[4];
+#pragma unroll
+            for (int K = 0; K < 4; ++K) bl[K] = load_vec<float, CPL>(sBLK + K * DK + c0);
+            float gcv[CPL];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+#pragma unroll
+                for (int K = 0; K < 4; ++K) blk[c][K] = bl[K].v[c];
+                gcv[c] = blk[c][0] * blk[c][1] * blk[c][2] * blk[c][3];
+                invgc[c] = __builtin_amdgcn_rcpf(gcv[c]);
+            }
+            if (I == 0 && ts == 0) {
+                typedef float V __attribute__((ext_vector_type(CPL)));
+                V x;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) x[c] = gcv[c];
+                *reinterpret_cast<V*>(rec + R::GC + c0 * 4) = x;
+            }
+        }
+        strong = __builtin_amdgcn_readfirstlane(strong);
+        {
+            float before[CPL], after[CPL];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                before[c] = 1.f;
+                after[c] = 1.f;
+#pragma unroll
+                for (int K = 0; K < 4; ++K) {
+                    if (K < I) before[c] *= blk[c][K];
+                    if (K > I) after[c] *= blk[c][K];
+                }
+            }
+            float kgt[CPL][4];
+            // record rows of this lane's tokens: QG and BG [token][DK]
+            char* rq = rec + R::QG + ((I * 16 + ts * 4) * DK + c0) * 2;
+            char* rb = rec + R::BG + ((I * 16 + ts * 4) * DK + c0) * 2;
+            if (!strong) {
+                const int eb = cb::opq(((I * 16 + ts * 4) * LDK + c0) * 2);
+                float bex[CPL], esa[CPL];
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    bex[c] = before[c] * ex[c];
+                    esa[c] = es[c] * after[c];
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    float xq[CPL], xb[CPL], xki[CPL];
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) {
+                        const float kv = (float)in.k[m].v[c];
+                        const float gam = bex[c] * lp[c][m];
+                        xq[c] = (float)in.q[m].v[c] * gam;
+                        xb[c] = (float)in.b[m].v[c] * kv * gam;
+                        kgt[c][m] = kv * (ls[c][m] * esa[c]);
+                        xki[c] = kgt[c][m] * invgc[c];
+                    }
+                    cb::store_bf16<CPL>(B16(G::QGR + eb + m * LDK * 2), xq);
+                    cb::store_bf16<CPL>(B16(G::RX + eb + m * LDK * 2), xb);
+                    cb::store_bf16<CPL>(B16(G::RX + eb + (C + m) * LDK * 2), xki);
+                    cb::store_bf16<CPL>(reinterpret_cast<bf16*>(rq + m * DK * 2), xq);
+                    cb::store_bf16<CPL>(reinterpret_cast<bf16*>(rb + m * DK * 2), xb);
+                }
+            } else {
+                const int wkb = cb::opq(G::RX + (ts * 4 * LDK + c0) * 2);
+                float pre[CPL][4], suf[CPL][4];
+#pragma unroll
+                for (int c = 0; c < CPL; ++c)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        pre[c][m] = ex[c] * lp[c][m];
+                        suf[c][m] = ls[c][m] * es[c];
+                    }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    // y: level-64 rows/columns (pivot token 31), z: level-32 ones (pivots 15, 47)
+                    float xq[CPL], xb[CPL], ya[CPL], yp[CPL], za[CPL], zp[CPL];
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) {
+                        const float qv = (float)in.q[m].v[c];
+                        const float kv = (float)in.k[m].v[c];
+                        const float bk = (float)in.b[m].v[c] * kv;
+                        const float gam = before[c] * pre[c][m];
+                        xq[c] = qv * gam;
+                        xb[c] = bk * gam;
+                        kgt[c][m] = kv * suf[c][m] * after[c];
+                        if (I >= 2) {
+                            const float f = I == 3 ? blk[c][2] * pre[c][m] : pre[c][m];
+                            ya[c] = bk * f;
+                            yp[c] = qv * f;
+                        } else {
+                            ya[c] = kv * suf[c][m] * (I == 0 ? blk[c][1] : 1.f);
+                            yp[c] = 0.f;
+                        }
+                        if (I & 1) {
+                            za[c] = bk * pre[c][m];
+                            zp[c] = qv * pre[c][m];
+                        } else {
+                            za[c] = kv * suf[c][m];
+                            zp[c] = 0.f;
+                        }
+                    }
+                    cb::store_bf16<CPL>(reinterpret_cast<bf16*>(rq + m * DK * 2), xq);
+                    cb::store_bf16<CPL>(reinterpret_cast<bf16*>(rb + m * DK * 2), xb);
+                    bf16* wk = B16(wkb + m * LDK * 2);
+                    if (I >= 2) {
+                        cb::store_bf16<CPL>(wk + (I - 2) * 16 * LDK, ya);
+                        cb::store_bf16<CPL>(wk + I * 16 * LDK, yp);
+                    } else {
+                        cb::store_bf16<CPL>(wk + (4 + I) * 16 * LDK, ya);
+                    }
+                    if (I & 1) {
+                        cb::store_bf16<CPL>(wk + (6 + I / 2) * 16 * LDK, za);
+                        cb::store_bf16<CPL>(wk + (8 + I / 2) * 16 * LDK, zp);
+                    } else {
+                        cb::store_bf16<CPL>(wk + (10 + I / 2) * 16 * LDK, za);
+                    }
+                }
+            }
+            // KG^T [DK][64]: this lane's 4 tokens of each of its channels
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+                cb::store_bf16<4>(reinterpret_cast<bf16*>(rec + R::KGT + ((c0 + c) * C + I * 16 + ts * 4) * 2), kgt[c]);
+        }
+        cb::lds_barrier();
+
+        // =============== A, P and the diagonal blocks of T = (I + A)^{-1} ===============
+        char* th = rec + R::T;
+        char* tl = rec + R::T + R::TRI * 2;
+        char* ph = rec + R::P;
+        char* pl = rec + R::P + R::TRI * 2;
+        auto put_p = [=](int row, int col, const float (&p)[4]) { put_split4(ph, pl, tri_index(row, col), p); };
+        if (!strong) {
+            load_first(nnext, in);
+            if (wave < 4) {
+                // diagonal block I = wave: A_II in both orientations, then its inverse
+                f32x4 nt = zero4(), nn = zero4();
+                const int rk = cb::opq(((wave * 16 + l16) * LDK + g4 * 8) * 2);
+                const int rkx = cb::opq(rk + G::RX);
+                Frag<bf16> fk[DK / 32], fa[DK / 32];
+#pragma unroll
+                for (int kk = 0; kk < DK / 32; ++kk) {
+                    fk[kk] = load_contig(B16(rkx + C * LDK * 2 + kk * 64));
+                    fa[kk] = load_contig(B16(rkx + kk * 64));
+                }
+                cb::sched_fence();
+#pragma unroll
+                for (int kk = 0; kk < DK / 32; ++kk) {
+                    mma(nt, fk[kk], fa[kk]);
+                    mma(nn, fa[kk], fk[kk]);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = 4 * g4 + r;
+                    nt[r] = j < l16 ? nt[r] : 0.f;
+                    nn[r] = j > l16 ? nn[r] : 0.f;
+                }
+                const f32x4 t = cb::unit_lower_inverse(nt, nn, l16, g4);
+                cb::store_tdiag<G>(smem, wave, l16, g4, t);
+                float x[4];
+                cb::acc_to_array(t, x);
+                put_split4(th, tl, tri_index(wave * 16 + l16, wave * 16 + g4 * 4), x);
+            } else if (wave == 7) {
+#pragma unroll
+                for (int Ib = 0; Ib < 4; ++Ib) {
+                    const int rk = cb::opq(((Ib * 16 + l16) * LDK + g4 * 8) * 2);
+                    Frag<bf16> fk[DK / 32], fq[DK / 32];
+#pragma unroll
+                    for (int kk = 0; kk < DK / 32; ++kk) {
+                        fk[kk] = load_contig(B16(rk + G::RX + C * LDK * 2 + kk * 64));
+                        fq[kk] = load_contig(B16(rk + G::QGR + kk * 64));
+                    }
+                    cb::sched_fence();
+                    f32x4 pd = zero4();
+#pragma unroll
+                    for (int kk = 0; kk < DK / 32; ++kk) mma(pd, fk[kk], fq[kk]);
+                    float pp[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) pp[r] = 4 * g4 + r <= l16 ? pd[r] : 0.f;
+                    put_p(Ib * 16 + l16, Ib * 16 + g4 * 4, pp);
+                }
+            } else {
+                // off-diagonal pairs: wave 4: (1,0) (2,0); wave 5: (2,1) (3,1); wave 6: (3,0) (3,2)
+                const int rl = cb::opq((l16 * LDK + g4 * 8) * 2);
+#pragma unroll
+                for (int pi = 0; pi < 2; ++pi) {
+                    const int Ib = wave == 4 ? 1 + pi : wave == 5 ? 2 + pi : 3;
+                    const int Jb = wave == 4 ? 0 : wave == 5 ? 1 : 2 * pi;
+                    f32x4 accA = zero4(), accP = zero4();
+                    Frag<bf16> fk[DK / 32], fa[DK / 32], fq[DK / 32];
+#pragma unroll
+                    for (int kk = 0; kk < DK / 32; ++kk) {
+                        fk[kk] = load_contig(B16(rl + G::RX + (C + Jb * 16) * LDK * 2 + kk * 64));
+                        fa[kk] = load_contig(B16(rl + G::RX + Ib * 16 * LDK * 2 + kk * 64));
+                        fq[kk] = load_contig(B16(rl + G::QGR + Ib * 16 * LDK * 2 + kk * 64));
+                    }
+                    cb::sched_fence();
+#pragma unroll
+                    for (int kk = 0; kk < DK / 32; ++kk) {
+                        mma(accA, fk[kk], fa[kk]);
+                        mma(accP, fk[kk], fq[kk]);
+                    }
+                    float a[4], pp[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) { a[r] = -accA[r]; pp[r] = accP[r]; }
+                    cb::store_bf16<4>(sA + (Ib * 16 + l16) * LC + Jb * 16 + g4 * 4, a);
+                    put_p(Ib * 16 + l16, Jb * 16 + g4 * 4, pp);
+                }
+            }
+        } else {
+            cb::strong_ap_body<G, DK>(smem, q, k, bgate, log_alpha, seq_base_k + (int64_t)t0 * tok_stride_k, tok_stride_k,
+                                 Tlen - t0, put_p, [=](int Ib, const f32x4& t) {
+                                     float x[4];
+                                     cb::acc_to_array(t, x);
+                                     put_split4(th, tl, tri_index(Ib * 16 + l16, Ib * 16 + g4 * 4), x);
+                                 });
+            load_first(nnext, in);
+        }
+        cb::lds_barrier();
+
+        // =============== off-diagonal blocks of T, through halves of 32 tokens ===============
+        if (wave < 4) {
+            const int J = wave & 1, Rb = 2 + (wave >> 1);
+            const int tb = cb::opq((l16 * LC + g4 * 4) * 2);
+            Frag16<bf16> t10, t32;
+            if (J == 0) {  // T_10 = T_11 (-A_10) T_00, lane (n, g): T_10[4 g + r][n]
+                const Frag16<bf16> fa = load16(B16(G::AM + tb + (16 * LC) * 2));
+                const Frag16<bf16> fj = load16(B16(G::TTR + tb));
+                const Frag16<bf16> ft = load16(B16(G::TR + tb + (16 * LC + 16) * 2));
+                cb::sched_fence();
+                f32x4 z = zero4(), t = zero4();
+                mma16(z, fa, fj);
+                mma16(t, ft, frag16_from_acc<bf16>(z));
+                t10 = frag16_from_acc<bf16>(t);
+                if (wave == 0) {
+                    // record: T[16 + 4 g + r][n]
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        bf16 a, b;
+                        cb::split_bf16(t[r], a, b);
+                        const int idx = tri_index(16 + 4 * g4 + r, l16);
+                        *reinterpret_cast<bf16*>(th + idx * 2) = a;
+                        *reinterpret_cast<bf16*>(tl + idx * 2) = b;
+                    }
+                }
+            }
+            if (Rb == 3) {  // T_32 = T_33 (-A_32) T_22, lane (i, g): T_32[i][4 g + r]
+                const Frag16<bf16> fa = load16(B16(G::AM + tb + (48 * LC + 32) * 2));
+                const Frag16<bf16> fj = load16(B16(G::TTR + tb + (32 * LC + 32) * 2));
+                const Frag16<bf16> ft = load16(B16(G::TR + tb + (48 * LC + 48) * 2));
+                cb::sched_fence();
+                f32x4 z = zero4(), t = zero4();
+                mma16(z, fa, fj);
+                mma16(t, frag16_from_acc<bf16>(z), ft);
+                t32 = frag16_from_acc<bf16>(t);
+                if (wave == 3) {
+                    float x[4];
+                    cb::acc_to_array(t, x);
+                    put_split4(th, tl, tri_index(48 + l16, 32 + g4 * 4), x);
+                }
+            }
+            Frag16<bf16> tf[2], a2[2], a3[2];
+#pragma unroll
+            for (int K = 0; K < 2; ++K) {
+                if (K < J) continue;
+                tf[K] = (K == 1 && J == 0) ? t10 : load16(B16(G::TTR + tb + (J * 16 * LC + K * 16) * 2));
+                a2[K] = load16(B16(G::AM + tb + (32 * LC + K * 16) * 2));
+                a3[K] = load16(B16(G::AM + tb + (48 * LC + K * 16) * 2));
+            }
+            const Frag16<bf16> t22 = load16(B16(G::TR + tb + (32 * LC + 32) * 2));
+            const Frag16<bf16> t33 = load16(B16(G::TR + tb + (48 * LC + 48) * 2));
+            cb::sched_fence();
+            f32x4 z2 = zero4(), z3 = zero4();
+#pragma unroll
+            for (int K = 0; K < 2; ++K) {
+                if (K < J) continue;
+                mma16(z2, a2[K], tf[K]);
+                if (Rb == 3) mma16(z3, a3[K], tf[K]);
+            }
+            const Frag16<bf16> z2f = frag16_from_acc<bf16>(z2);
+            f32x4 t = zero4();
+            if (Rb == 2) {
+                mma16(t, z2f, t22);
+            } else {
+                mma16(t, z2f, t32);
+                mma16(t, frag16_from_acc<bf16>(z3), t33);
+            }
+            float x[4];
+            cb::acc_to_array(t, x);
+            put_split4(th, tl, tri_index(Rb * 16 + l16, J * 16 + g4 * 4), x);
+        } else {
+            // waves 4-7: the zero blocks (0,1) and (2,3) of T and P
+            const int w4 = wave - 4;                   // 0..3
+            const int blkrow = w4 < 2 ? 0 : 2;         // zero blocks start at rows 0 and 32
+            const float z[4] = {0.f, 0.f, 0.f, 0.f};
+            const int row = blkrow * 16 + l16, col = (blkrow + 1) * 16 + g4 * 4;
+            if (w4 & 1) put_split4(ph, pl, tri_index(row, col), z);
+            else put_split4(th, tl, tri_index(row, col), z);
+        }
+        // the next chunk's keys and gates
+        load_second(nnext, in);
+        cb::lds_barrier();
+    }
+}
+
+// ------------------------------------------------------------------ state kernel ----
+constexpr int NT_STATE = 256;
+
+// XOR swizzle of 16-byte units inside a row of rb bytes (rb a power of two, 64..256), so that
+// the 16 rows a fragment load touches fall on distinct LDS banks.
+__device__ __forceinline__ int swz_unit(int row, int unit, int rb) {
+    return unit ^ ((row * rb / 256) % (rb / 16));
+}
+
+template <int D>
+struct StateCfg {
+    using R = Rec<D>;
+    static constexpr int BUF = R::BYTES;             // one staged record
+    static constexpr int BYTES = 2 * BUF;
+    static_assert(BYTES <= 163840, "LDS budget exceeded");
+    static constexpr int UPT = (R::UNITS + NT_STATE - 1) / NT_STATE;  // 16-byte units per thread
+};
+
+// LDS byte offset of 16-byte unit ub + t of a record (same parts and order as the record, each
+// part swizzled by rows); ub is a multiple of 256, so the part is known from ub alone.
+template <int D>
+__device__ __forceinline__ int stage_offset(int ub, int t) {
+    using R = Rec<D>;
+    constexpr int UQ = C * D * 2 / 16;  // units of QG (= of BG, of KG^T); a multiple of 256
+    constexpr int RBQ = D * 2;          // row bytes of QG, BG
+    const int u = ub + t;
+    if (ub < 2 * UQ) {
+        const int part = u / UQ, v = u % UQ;
+        const int row = v / (RBQ / 16), un = v % (RBQ / 16);
+        return part * UQ * 16 + row * RBQ + swz_unit(row, un, RBQ) * 16;
+    }
+    if (ub < 3 * UQ) {
+        const int v = u - 2 * UQ;       // KG^T rows of 64 tokens = 128 bytes
+        const int row = v / 8, un = v % 8;
+        return R::KGT + row * 128 + swz_unit(row, un, 128) * 16;
+    }
+    if (ub < R::GC / 16) {
+        const int v = u - R::T / 16;    // T and P planes: 4 planes of TRI elements
+        const int plane = v / (R::TRI * 2 / 16), w = v % (R::TRI * 2 / 16);
+        // rows 0-31: 64-byte rows (units 0-127); rows 32-63: 128-byte rows
+        const bool top = w < 128;
+        const int row = top ? w / 4 : (w - 128) / 8, un = top ? w % 4 : (w - 128) % 8;
+        const int off = top ? row * 64 + swz_unit(row, un, 64) * 16 : 2048 + row * 128 + swz_unit(row, un, 128) * 16;
+        return R::T + plane * R::TRI * 2 + off;
+    }
+    return u * 16;                      // Gamma_C and the padding
+}
+
+// A-operand fragment (permuted slot map) of rows 16 rt + m, columns 32 kk .. 32 kk + 31 of a
+// staged row-major part with rb-byte rows: lane (m, g) takes columns 32 kk + 4 g + e and
+// 32 kk + 16 + 4 g + e (e = 0..3), the slots where a pair of accumulator tiles keeps its rows.
+__device__ __forceinline__ Frag<bf16> frag_perm(const char* part, int row, int kk, int g, int rb) {
+    const int c0 = 32 * kk + 4 * g, c1 = c0 + 16;  // first column of each 8-byte half
+    const int u0 = c0 / 8, u1 = c1 / 8;
+    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(part + row * rb + swz_unit(row, u0, rb) * 16 + (c0 % 8) * 2);
+    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(part + row * rb + swz_unit(row, u1, rb) * 16 + (c1 % 8) * 2);
+    Frag<bf16> f;
+    f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return f;
+}
+
+// the same from a staged triangle plane (rows 0-31: 64-byte rows; rows 32-63: 128-byte rows)
+__device__ __forceinline__ Frag<bf16> frag_tri(const char* plane, int row, int kk, int g) {
+    return row < 32 ? frag_perm(plane, row, kk, g, 64) : frag_perm(plane + 2048, row - 32, kk, g, 128);
+}
+
+// hi / lo K = 32 operands of an accumulator pair (permuted slot map)
+__device__ __forceinline__ cb::Split32 split_pair(const f32x4& a, const f32x4& b) { return cb::split32(a, b); }
+
+template <typename OutT, int D>
+__global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
+    const char* __restrict__ recs, const bf16* __restrict__ v, const bf16* __restrict__ wgate,
+    const float* state_in, float* state_out, OutT* __restrict__ o, int Tparam, int H, int nslices,
+    int xcd_map, int c_begin, int c_end) {
+    using Cf = StateCfg<D>;
+    using R = Rec<D>;
+    constexpr int KT = D / 16;           // 16-row key tiles of the state
+    constexpr int KK = KT / 2;           // 32-row steps over the keys
+    __shared__ __attribute__((aligned(16))) char smem[Cf::BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int bh, slice;
+    {
+        const int id = blockIdx.x;
+        if (xcd_map) {
+            const int kk = id >> 3;
+            bh = 8 * (kk / nslices) + (id & 7);
+            slice = kk % nslices;
+        } else {
+            bh = id / nslices;
+            slice = id % nslices;
+        }
+    }
+    const int h = bh % H;
+    const int nb = c_end - c_begin;
+    const int Tlen = Tparam;
+    const int64_t tok0 = (int64_t)(bh / H) * Tparam;
+    const int col = slice * 64 + wave * 16 + l16;   // this lane's state / value column
+    const int64_t tok_stride_v = (int64_t)H * D;
+    const char* rec0 = recs + (int64_t)bh * nb * R::BYTES;
+
+    // the state's 16 columns of this wave, all D rows: tile st, lane (n, g) holds S[16 st + 4 g + r][col]
+    f32x4 S[KT];
+#pragma unroll
+    for (int st = 0; st < KT; ++st) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            S[st][r] = state_in ? state_in[((int64_t)bh * D + st * 16 + g4 * 4 + r) * D + col] : 0.f;
+    }
+
+    // w.v of one chunk in accumulator layout: tile rt, lane (n, g) holds token 16 rt + 4 g + r.  Tokens
+    // past the end read the last token and are zeroed when used.
+    auto load_wv = [&](int n, bf16 (&wv)[2][4][4]) {
+        const int t0 = n * C;
+        const int64_t base = (tok0 + t0) * tok_stride_v + (int64_t)h * D + col;
+        const int last = Tlen - 1 - t0;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t e = base + (int64_t)min(rt * 16 + g4 * 4 + r, last) * tok_stride_v;
+                wv[0][rt][r] = wgate[e];
+                wv[1][rt][r] = v[e];
+            }
+    };
+    // record staging: this thread's 16-byte units of record i (batch-relative) into registers
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    auto load_rec = [&](int i, i32x4 (&st)[Cf::UPT]) {
+        const i32x4* src = reinterpret_cast<const i32x4*>(rec0 + (int64_t)i * R::BYTES);
+#pragma unroll
+        for (int j = 0; j < Cf::UPT; ++j) st[j] = src[j * NT_STATE + tid];
+    };
+    auto put_rec = [&](int buf, const i32x4 (&st)[Cf::UPT]) {
+#pragma unroll
+        for (int j = 0; j < Cf::UPT; ++j)
+            *reinterpret_cast<i32x4*>(smem + buf * Cf::BUF + stage_offset<D>(j * NT_STATE, tid)) = st[j];
+    };
+
+    i32x4 stg[Cf::UPT];
+    bf16 wv[2][4][4];
+    if (nb > 0) {
+        load_rec(0, stg);
+        load_wv(c_begin, wv);
+        put_rec(0, stg);
+        if (nb > 1) load_rec(1, stg);
+    }
+    __syncthreads();
+
+    for (int i = 0; i < nb; ++i) {
+        const int n = c_begin + i;
+        const int t0 = n * C;
+        const char* rb = smem + (i & 1) * Cf::BUF;
+        const char* th = rb + R::T;
+        const char* tl = rb + R::T + R::TRI * 2;
+        const char* ph = rb + R::P;
+        const char* pl = rb + R::P + R::TRI * 2;
+        // ---- X = BG S and Y = QG S, S as hi / lo bf16 pairs over 32 key rows; the fragments of
+        // each step are loaded one step ahead ----
+        f32x4 X[4], Y[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) { X[rt] = zero4(); Y[rt] = zero4(); }
+        Frag<bf16> fb[2][4], fq[2][4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            fb[0][rt] = frag_perm(rb + R::BG, rt * 16 + l16, 0, g4, D * 2);
+            fq[0][rt] = frag_perm(rb + R::QG, rt * 16 + l16, 0, g4, D * 2);
+        }
+        // the triangle fragments of U = T R and O = Y + P U: (rt, kk) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+        Frag<bf16> fth[6], ftl[6], fph[6], fpl[6];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            if (kk + 1 < KK) {
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    fb[(kk + 1) & 1][rt] = frag_perm(rb + R::BG, rt * 16 + l16, kk + 1, g4, D * 2);
+                    fq[(kk + 1) & 1][rt] = frag_perm(rb + R::QG, rt * 16 + l16, kk + 1, g4, D * 2);
+                }
+            } else {
+#pragma unroll
+                for (int p = 0; p < 6; ++p) {
+                    const int rt = p < 2 ? p : 2 + (p - 2) / 2, k2 = p < 2 ? 0 : (p - 2) % 2;
+                    fth[p] = frag_tri(th, rt * 16 + l16, k2, g4);
+                    ftl[p] = frag_tri(tl, rt * 16 + l16, k2, g4);
+                    fph[p] = frag_tri(ph, rt * 16 + l16, k2, g4);
+                    fpl[p] = frag_tri(pl, rt * 16 + l16, k2, g4);
+                }
+            }
+            const cb::Split32 sp = split_pair(S[2 * kk], S[2 * kk + 1]);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                mma(X[rt], fb[kk & 1][rt], sp.hi);
+                mma(Y[rt], fq[kk & 1][rt], sp.hi);
+                mma(X[rt], fb[kk & 1][rt], sp.lo);
+                mma(Y[rt], fq[kk & 1][rt], sp.lo);
+            }
+        }
+        // ---- R = w.v - X; U = T R through 32-token halves (T is lower triangular) ----
+        f32x4 Rr[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool in = t0 + rt * 16 + g4 * 4 + r < Tlen;
+                Rr[rt][r] = (in ? (float)wv[0][rt][r] * (float)wv[1][rt][r] : 0.f) - X[rt][r];
+            }
+        if (i + 1 < nb) load_wv(n + 1, wv);
+        // the key-row fragments of the state update
+        Frag<bf16> fk[KT][2];
+#pragma unroll
+        for (int st = 0; st < KT; ++st)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) fk[st][kk] = frag_perm(rb + R::KGT, st * 16 + l16, kk, g4, 128);
+        const cb::Split32 r0 = split_pair(Rr[0], Rr[1]), r1 = split_pair(Rr[2], Rr[3]);
+        f32x4 U[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) U[rt] = zero4();
+#pragma unroll
+        for (int p = 0; p < 6; ++p) {
+            const int rt = p < 2 ? p : 2 + (p - 2) / 2, k2 = p < 2 ? 0 : (p - 2) % 2;
+            const cb::Split32& rs = k2 == 0 ? r0 : r1;
+            mma(U[rt], fth[p], rs.hi);
+            mma(U[rt], fth[p], rs.lo);
+            mma(U[rt], ftl[p], rs.hi);
+        }
+        const cb::Split32 u0 = split_pair(U[0], U[1]), u1 = split_pair(U[2], U[3]);
+        // ---- S <- Gamma_C S + KG^T U ----
+        const float* gc = reinterpret_cast<const float*>(rb + R::GC);
+#pragma unroll
+        for (int st = 0; st < KT; ++st) {
+            const f32x4 g = *reinterpret_cast<const f32x4*>(gc + st * 16 + g4 * 4);
+            S[st] *= g;
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const cb::Split32& us = kk == 0 ? u0 : u1;
+#pragma unroll
+            for (int st = 0; st < KT; ++st) {
+                mma(S[st], fk[st][kk], us.hi);
+                mma(S[st], fk[st][kk], us.lo);
+            }
+        }
+        // ---- O = Y + P U ----
+#pragma unroll
+        for (int p = 0; p < 6; ++p) {
+            const int rt = p < 2 ? p : 2 + (p - 2) / 2, k2 = p < 2 ? 0 : (p - 2) % 2;
+            const cb::Split32& us = k2 == 0 ? u0 : u1;
+            mma(Y[rt], fph[p], us.hi);
+            mma(Y[rt], fph[p], us.lo);
+            mma(Y[rt], fpl[p], us.hi);
+        }
+        OutT* ob = o + (tok0 + t0) * tok_stride_v + (int64_t)h * D + col;
+        if (t0 + C <= Tlen) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ob[(int64_t)(rt * 16 + g4 * 4 + r) * tok_stride_v] = from_f32<OutT>(Y[rt][r]);
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (t0 + rt * 16 + g4 * 4 + r < Tlen)
+                        ob[(int64_t)(rt * 16 + g4 * 4 + r) * tok_stride_v] = from_f32<OutT>(Y[rt][r]);
+        }
+        // ---- stage record i + 1 (loaded during this chunk), start loading record i + 2 ----
+        if (i + 1 < nb) {
+            put_rec((i + 1) & 1, stg);
+            if (i + 2 < nb) load_rec(i + 2, stg);
+        }
+        // LDS-only barrier: the loads of record i + 2 and of the next w and v stay in flight
+        cb::lds_barrier();
+    }
+
+    if (state_out) {
+#pragma unroll
+        for (int st = 0; st < KT; ++st)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) state_out[((int64_t)bh * D + st * 16 + g4 * 4 + r) * D + col] = S[st][r];
+    }
+}
+
+}  // namespace sp
+
+// ------------------------------------------------------------------ host side ----
+// Chunk-heads per batch: the records of one batch stay within the last-level cache.
+constexpr int64_t kSplitBatchChunkHeads = 1024;
+
+int64_t split_record_bytes(int64_t d) { return d == 128 ? sp::Rec<128>::BYTES : d == 64 ? sp::Rec<64>::BYTES : 0; }
+
+int64_t split_batch_chunks(int64_t BH, int64_t nchunks) {
+    int64_t c = kSplitBatchChunkHeads / (BH > 0 ? BH : 1);
+    if (c < 1) c = 1;
+    return c < nchunks ? c : nchunks;
+}
+
+size_t split_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d) {
+    const int64_t rb = split_record_bytes(d);
+    if (rb == 0 || B < 1 || T < 1 || H < 1) return 0;
+    const int64_t nc = (T + 63) / 64;
+    const int64_t bc = split_batch_chunks(B * H, nc);
+    // records of one batch, then the state carried between batches
+    return (size_t)(B * H * bc * rb + B * H * d * d * 4);
+}
+
+template <typename OutT, int D>
+hipError_t launch_split_d(const ChunkArgs& a, char* ws) {
+    const int64_t BH = a.B * a.H;
+    const int nc = (int)((a.T + 63) / 64);
+    const int bc = (int)split_batch_chunks(BH, nc);
+    const int nslices = D / 64;
+    const int xcd_map = BH % 8 == 0 ? 1 : 0;
+    float* carry = a.final_state ? a.final_state : reinterpret_cast<float*>(ws + BH * bc * sp::Rec<D>::BYTES);
+    hipStream_t st = (hipStream_t)a.stream;
+    for (int c0 = 0; c0 < nc; c0 += bc) {
+        const int c1 = c0 + bc < nc ? c0 + bc : nc;
+        // runs of consecutive chunks per local workgroup: one round of workgroups over the CUs
+        const int64_t per = (BH * (c1 - c0) + a.cus - 1) / a.cus;
+        const int run = (int)(per < 1 ? 1 : per > c1 - c0 ? c1 - c0 : per);
+        const int runs = (c1 - c0 + run - 1) / run;
+        hipLaunchKernelGGL((sp::local_kernel<D>), dim3((unsigned)(BH * runs)), dim3(sp::NT_LOCAL), 0, st,
+                           (const bf16*)a.q, (const bf16*)a.k, a.log_alpha, (const bf16*)a.b, ws, (int)a.T,
+                           (int)a.H, c0, c1, run);
+        const float* sin = c0 == 0 ? a.initial_state : carry;
+        float* sout = c1 == nc ? a.final_state : carry;
+        hipLaunchKernelGGL((sp::state_kernel<OutT, D>), dim3((unsigned)(BH * nslices)), dim3(sp::NT_STATE), 0, st,
+                           (const char*)ws, (const bf16*)a.v, (const bf16*)a.w, sin, sout, (OutT*)a.o, (int)a.T,
+                           (int)a.H, nslices, xcd_map, c0, c1);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_split(const ChunkArgs& a, void* workspace) {
+    char* ws = static_cast<char*>(workspace);
+    if (!a.dtype_bf16 || a.dk != a.dv || a.cu_seqlens) return hipErrorInvalidValue;
+    if (a.dk == 128) return a.out_f32 ? launch_split_d<float, 128>(a, ws) : launch_split_d<bf16, 128>(a, ws);
+    if (a.dk == 64) return a.out_f32 ? launch_split_d<float, 64>(a, ws) : launch_split_d<bf16, 64>(a, ws);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdn2

@@ -23,6 +23,7 @@ struct ChunkArgs {
     // packed sequences: B + 1 offsets into the token axis of length T (device memory), or
     // nullptr for B sequences of T tokens each
     const int64_t* cu_seqlens = nullptr;
+    int cus = 256;  // compute units of the device
 };
 
 struct DecodeArgs {
@@ -117,6 +118,10 @@ struct MixerOutArgs {
 
 // dvs: value columns per workgroup slice (16, 32 or 64)
 hipError_t launch_chunk_fwd(const ChunkArgs& a, int dvs);
+// The forward in two kernels (chunk-local records, then the state pass), bf16 inputs with
+// dk = dv = 64 or 128, fixed-length sequences; workspace of split_workspace_bytes bytes.
+size_t split_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d);
+hipError_t launch_chunk_split(const ChunkArgs& a, void* workspace);
 // bf16 inputs (dk = dv = 64 or 128)
 hipError_t launch_chunk_bf16(const ChunkArgs& a, int dvs);
 hipError_t launch_decode_step(const DecodeArgs& a);

@@ -91,9 +91,16 @@ typedef enum gdn2_status {
  * o must not overlap any input; final_state must not overlap any input other
  * than an identical initial_state.  H * dk and H * dv (the elements between
  * consecutive tokens of one tensor) must be below 2^24, else GDN2_ERR_SHAPE.
- * workspace / workspace_bytes: caller-owned device memory of at least
- * gdn2_chunk_fwd_workspace_bytes(...) bytes (currently 0: NULL and 0 are
- * accepted); a shorter one returns GDN2_ERR_WORKSPACE.
+ * workspace / workspace_bytes select the implementation.  With a workspace of
+ * at least gdn2_chunk_fwd_split_workspace_bytes(...) bytes (device memory owned by
+ * the caller, 256-byte aligned, overlapping no argument; its contents on entry
+ * do not matter and on return are unspecified) the forward runs as two kernels
+ * per batch of chunks: one forms every chunk's state-independent quantities in
+ * parallel, the other carries the state through the chunks.  With
+ * workspace = NULL and workspace_bytes = 0 it runs as one fused kernel (same
+ * results within the parity bar, no workspace).  A workspace passed where the
+ * two-kernel form does not exist, or a shorter one, returns GDN2_ERR_WORKSPACE.
+ * gdn2_chunk_fwd_workspace_bytes says which form is faster for a shape.
  */
 gdn2_status_t gdn2_chunk_fwd(const void* q, const void* k, const void* v,
                              const float* log_alpha, const void* b, const void* w,
@@ -103,11 +110,22 @@ gdn2_status_t gdn2_chunk_fwd(const void* q, const void* k, const void* v,
                              size_t workspace_bytes, void* stream);
 
 /*
- * gdn2_chunk_fwd_workspace_bytes -- bytes of device workspace gdn2_chunk_fwd
- * needs for these sizes.  The forward is one fused kernel whose intermediates
- * stay in registers and LDS, so this is 0 for every supported combination
- * (and gdn2_chunk_fwd accepts workspace = NULL, workspace_bytes = 0).
- * Returns 0 for unsupported combinations too; gdn2_chunk_fwd reports those.
+ * gdn2_chunk_fwd_split_workspace_bytes -- bytes of device workspace that the
+ * two-kernel form of gdn2_chunk_fwd needs for these sizes: the chunk records of
+ * one batch of about a thousand (sequence, head, chunk) triples, 77,824 bytes
+ * each at dk = dv = 128 (53,248 at 64), plus one fp32 state [B, H, dk, dv].
+ * The two-kernel form exists for BF16 inputs with dk = dv = 64 or 128; for
+ * every other combination (and for sizes out of range) this returns 0.
+ */
+size_t gdn2_chunk_fwd_split_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                            gdn2_dtype_t dtype);
+
+/*
+ * gdn2_chunk_fwd_workspace_bytes -- the workspace to pass to gdn2_chunk_fwd for
+ * its faster form on the current device: the two-kernel form's size (as above)
+ * when the fused kernel's chains, one per (sequence, head, 64 value columns),
+ * are fewer than the device's compute units, else 0 (run with workspace = NULL,
+ * workspace_bytes = 0: the fused kernel).
  */
 size_t gdn2_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                                       gdn2_dtype_t dtype);

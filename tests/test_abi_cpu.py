@@ -191,15 +191,45 @@ def test_status_values_follow_the_boundary_table(lib):
     assert (ERR_WORKSPACE, ERR_HIP) == (6, 7)
 
 
+def split_ws_bytes(B, T, H, d):
+    """Records of one batch (about 1024 chunk-heads) plus one fp32 state."""
+    rec = (3 * 64 * d * 2 + 2 * 2 * (32 * 32 + 32 * 64) * 2 + d * 4 + 4095) // 4096 * 4096
+    nc = (T + 63) // 64
+    bc = min(max(1024 // (B * H), 1), nc)
+    return B * H * bc * rec + B * H * d * d * 4
+
+
 def test_fwd_workspace_bytes(lib):
-    """The forward keeps every intermediate on chip: no workspace for any size or dtype, and
-    a NULL workspace of 0 bytes passes validation (the call below fails later, on alignment)."""
-    for dt in (BF16, F32):
-        for (B, T, H, d) in ((1, 1, 1, 64), (8, 4096, 16, 128), (1, 32768, 16, 128)):
-            assert lib.gdn2_chunk_fwd_workspace_bytes(B, T, H, d, d, dt) == 0
-    assert gdn2.chunk_fwd_workspace_bytes(8, 4096, 16, 128, 128) == 0
-    f = Fake()
-    assert chunk(lib, f, q=f.p(0, 2), ws=None, ws_bytes=0) == ERR_MISALIGNED
+    """bf16 with d = 64 or 128 has the two-kernel form: its workspace is the records of one
+    batch of chunks plus a state; fp32 and other sizes take none."""
+    assert split_ws_bytes(1, 64, 1, 128) - 128 * 128 * 4 == 77824
+    assert split_ws_bytes(1, 64, 1, 64) - 64 * 64 * 4 == 53248
+    for (B, T, H, d) in ((1, 1, 1, 64), (8, 4096, 16, 128), (1, 32768, 16, 128), (3, 1000, 5, 64)):
+        assert lib.gdn2_chunk_fwd_split_workspace_bytes(B, T, H, d, d, BF16) == split_ws_bytes(B, T, H, d)
+        assert lib.gdn2_chunk_fwd_split_workspace_bytes(B, T, H, d, d, F32) == 0
+    assert lib.gdn2_chunk_fwd_split_workspace_bytes(1, 64, 1, 96, 96, BF16) == 0
+    assert lib.gdn2_chunk_fwd_split_workspace_bytes(0, 64, 1, 128, 128, BF16) == 0
+    assert gdn2.chunk_fwd_workspace_bytes(8, 4096, 16, 128, 128, split=True) == split_ws_bytes(8, 4096, 16, 128)
+    # the faster form: the two-kernel form only when the fused kernel's chains, one per
+    # (sequence, head, 64 columns), are fewer than the compute units (256 here: no GPU)
+    assert lib.gdn2_chunk_fwd_workspace_bytes(1, 32768, 16, 128, 128, BF16) == split_ws_bytes(1, 32768, 16, 128)
+    assert lib.gdn2_chunk_fwd_workspace_bytes(8, 4096, 16, 128, 128, BF16) == 0
+    assert lib.gdn2_chunk_fwd_workspace_bytes(1, 32768, 16, 128, 128, F32) == 0
+
+
+def test_fwd_workspace_validation(lib):
+    """No workspace selects the fused kernel; a workspace must be large enough, 256-byte aligned,
+    overlap nothing, and only where the two-kernel form exists (all before any HIP call)."""
+    f = Fake(nbytes=1 << 22, slots=12)
+    need = lib.gdn2_chunk_fwd_split_workspace_bytes(1, 64, 1, 64, 64, BF16)
+    a256 = lambda slot: f.p(slot, (-f.p(slot).value) % 256)
+    ws = a256(10)
+    assert chunk(lib, f, q=f.p(0, 2), ws=None, ws_bytes=0) == ERR_MISALIGNED  # fused path, fails later
+    assert chunk(lib, f, ws=ws, ws_bytes=need - 1) == ERR_WORKSPACE
+    assert chunk(lib, f, ws=None, ws_bytes=need) == ERR_WORKSPACE
+    assert chunk(lib, f, ws=ctypes.c_void_p(ws.value + 16), ws_bytes=need) == ERR_MISALIGNED
+    assert chunk(lib, f, ws=a256(2), ws_bytes=need) == ERR_ALIAS              # overlaps v
+    assert chunk(lib, f, dtype=F32, odt=F32, ws=ws, ws_bytes=need) == ERR_WORKSPACE
 
 
 def test_bwd_workspace_bytes(lib):

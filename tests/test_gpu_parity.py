@@ -73,36 +73,89 @@ SMALL = [
 ]
 
 
+# fused: the single-kernel forward (no workspace); otherwise bf16 runs the two-kernel form
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("dtype,dk,B,T,H,with_s0,seed", SMALL)
-def test_small_cases(dtype, dk, B, T, H, with_s0, seed):
+def test_small_cases(dtype, dk, B, T, H, with_s0, seed, fused):
+    if fused and dtype == torch.float32:
+        pytest.skip("fp32 inputs always run the fused kernel")
     wl = dataclasses.replace(W.TRAIN_4K, name="small", dtype=dtype, dk=dk, dv=dk, H=H,
                              s0_std=0.05 if with_s0 else None)
-    say("case: %s dk=%d B=%d T=%d H=%d s0=%s seed=%d" % (dtype, dk, B, T, H, with_s0, seed))
+    say("case: %s dk=%d B=%d T=%d H=%d s0=%s seed=%d fused=%s" % (dtype, dk, B, T, H, with_s0, seed, fused))
     inp = W.make_inputs(wl, seed=seed, B=B, T=T)
-    o, s = run_gpu(inp)
+    o, s = run_gpu(inp, fused=fused)
     o_ref, s_ref = run_oracle(inp)
     check(o, s, o_ref, s_ref, tol_for(dtype), "small")
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("dtype,dk", [(torch.float32, 64), (torch.bfloat16, 128), (torch.bfloat16, 64)])
 @pytest.mark.parametrize("g_lo,g_hi", [(-5.0, -1.0), (-60.0, -20.0), (-3.0, 0.0)])
-def test_strong_and_extreme_decay(dtype, dk, g_lo, g_hi):
+def test_strong_and_extreme_decay(dtype, dk, g_lo, g_hi, fused):
     """Chunk decays far below fp32 range take the boundary-pivoted path; must stay exact."""
+    if fused and dtype == torch.float32:
+        pytest.skip("fp32 inputs always run the fused kernel")
     wl = dataclasses.replace(W.TRAIN_4K, name="decay", dtype=dtype, dk=dk, dv=dk, H=4,
                              g_lo=g_lo, g_hi=g_hi, s0_std=0.05)
-    say("case: decay U[%g,%g] %s dk=%d" % (g_lo, g_hi, dtype, dk))
+    say("case: decay U[%g,%g] %s dk=%d fused=%s" % (g_lo, g_hi, dtype, dk, fused))
     inp = W.make_inputs(wl, seed=7, B=2, T=300)
-    o, s = run_gpu(inp)
+    o, s = run_gpu(inp, fused=fused)
     o_ref, s_ref = run_oracle(inp)
     check(o, s, o_ref, s_ref, tol_for(dtype), "decay U[%g,%g]" % (g_lo, g_hi))
 
 
-def test_mixed_decay_heads_small():
+# Sizes whose chunk-heads exceed one batch of the two-kernel form (about 1024), with ragged
+# tails: the state is carried between batches, through final_state or the workspace.
+@pytest.mark.parametrize("B,T,H,d,with_s0,final", [
+    (2, 2100, 16, 128, True, "new"),      # 34 chunks x 32 heads: batches of 32 chunks + 2
+    (1, 5000, 20, 64, False, "none"),     # no final state: carried in the workspace
+    (3, 1500, 16, 128, True, "inplace"),  # final state written over the initial state
+])
+def test_split_across_batches(B, T, H, d, with_s0, final):
+    wl = dataclasses.replace(W.TRAIN_4K, name="batches", dk=d, dv=d, H=H, s0_std=0.05 if with_s0 else None)
+    say("case: across batches B=%d T=%d H=%d d=%d s0=%s final=%s (workspace %d bytes)"
+        % (B, T, H, d, with_s0, final, gdn2.chunk_fwd_workspace_bytes(B, T, H, d, d, split=True)))
+    inp = W.make_inputs(wl, seed=61, B=B, T=T)
+    x = to_dev(inp)
+    if final == "inplace":
+        st = x["s0"].clone()
+        o, s = gdn2.chunk_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], st, final_state=st,
+                              fused=False)
+        assert s.data_ptr() == st.data_ptr()
+    else:
+        o, s = gdn2.chunk_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], x["s0"],
+                              output_final_state=final == "new", fused=False)
+    torch.cuda.synchronize()
+    o_ref, s_ref = run_oracle(inp)
+    if final == "none":
+        assert s is None
+        eo = rel_max_err(o, o_ref)
+        say("  o err %.3e" % eo)
+        assert eo <= TOL_BF16
+    else:
+        check(o, s, o_ref, s_ref, TOL_BF16, "across batches")
+
+
+def test_split_and_fused_agree():
+    """The two forms compute the same function: on the same inputs their outputs differ by no
+    more than the bar allows each of them against the oracle."""
+    inp = W.make_inputs(W.TRAIN_4K, seed=62, B=2, T=700)
+    o1, s1 = run_gpu(inp, fused=False)
+    o2, s2 = run_gpu(inp, fused=True)
+    o_ref, s_ref = run_oracle(inp)
+    say("  split vs fused: o %.3e  S %.3e" % (rel_max_err(o1, o2.double().cpu().numpy()),
+                                             rel_max_err(s1, s2.double().cpu().numpy())))
+    check(o1, s1, o_ref, s_ref, TOL_BF16, "split")
+    check(o2, s2, o_ref, s_ref, TOL_BF16, "fused")
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_mixed_decay_heads_small(fused):
     """The long-context recipe (strong heads 0-7, weak 8-15) at T = 1024: per-head bar."""
     wl = W.LONG_32K
-    say("case: %s at T=1024" % wl.name)
+    say("case: %s at T=1024 fused=%s" % (wl.name, fused))
     inp = W.make_inputs(wl, T=1024)
-    o, s = run_gpu(inp)
+    o, s = run_gpu(inp, fused=fused)
     o_ref, s_ref = run_oracle(inp)
     for h in range(wl.H):
         eo = rel_max_err(o[:, :, h], o_ref[:, :, h])
@@ -116,10 +169,10 @@ def test_mixed_decay_heads_small():
 # the oracle run on the whole workload: the metric is taken over the whole o and S_T tensors,
 # and per head so that the weak heads' RMS cannot hide a strong head's error.
 
-def _whole(wl, report_bf16_o=False):
-    say("case: %s (full size, whole tensors)" % wl.name)
+def _whole(wl, report_bf16_o=False, fused=False):
+    say("case: %s (full size, whole tensors) fused=%s" % (wl.name, fused))
     inp = W.make_inputs(wl)
-    o, s = run_gpu(inp)
+    o, s = run_gpu(inp, fused=fused)
     o_ref, s_ref = run_oracle(inp)
     tol = tol_for(wl.dtype)
     eo, es = rel_max_err(o, o_ref), rel_max_err(s, s_ref)
@@ -132,19 +185,21 @@ def _whole(wl, report_bf16_o=False):
             say("  head %2d  o %.3e  S %.3e" % (h, eoh, esh))
     say("  worst head: o %.3e  S %.3e" % worst)
     if report_bf16_o:
-        o16, _ = run_gpu(inp, out_dtype=torch.bfloat16, output_final_state=False)
+        o16, _ = run_gpu(inp, out_dtype=torch.bfloat16, output_final_state=False, fused=fused)
         say("  bf16 o (rounded once on the store): o err %.3e (informational)" % rel_max_err(o16, o_ref))
         del o16
     assert eo <= tol and es <= tol, (wl.name, eo, es)
     assert worst[0] <= tol and worst[1] <= tol, (wl.name, worst)
 
 
-def test_train_4k_full_size_whole_tensor():
-    _whole(W.TRAIN_4K, report_bf16_o=True)
+@pytest.mark.parametrize("fused", [False, True])
+def test_train_4k_full_size_whole_tensor(fused):
+    _whole(W.TRAIN_4K, report_bf16_o=True, fused=fused)
 
 
-def test_long_32k_full_size_whole_tensor():
-    _whole(W.LONG_32K, report_bf16_o=True)
+@pytest.mark.parametrize("fused", [False, True])
+def test_long_32k_full_size_whole_tensor(fused):
+    _whole(W.LONG_32K, report_bf16_o=True, fused=fused)
 
 
 def test_fwdbwd_4k_forward_full_size_whole_tensor():
@@ -250,11 +305,12 @@ def test_no_final_state_requested():
     assert rel_max_err(o, o_ref) <= TOL_BF16
 
 
-def test_run_twice_bitwise_identical():
+@pytest.mark.parametrize("fused", [False, True])
+def test_run_twice_bitwise_identical(fused):
     inp = W.make_inputs(W.TRAIN_4K, seed=44, B=4, T=512)
-    say("case: determinism")
-    o1, s1 = run_gpu(inp)
-    o2, s2 = run_gpu(inp)
+    say("case: determinism fused=%s" % fused)
+    o1, s1 = run_gpu(inp, fused=fused)
+    o2, s2 = run_gpu(inp, fused=fused)
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
 
 

@@ -91,6 +91,8 @@ def test_packed_strong_decay():
 
 
 def test_equal_lengths_match_fixed_length_call_exactly():
+    """Packed sequences run the fused kernel: with equal lengths they are bit-identical to the
+    fixed-length call in its fused form."""
     say("case: varlen == fixed length, bf16 d128, 4 x 130 tokens")
     L, N, H = 130, 4, 3
     inp = packed_case(torch.bfloat16, 128, H, [L] * N, 205)
@@ -98,7 +100,7 @@ def test_equal_lengths_match_fixed_length_call_exactly():
     d = to_dev(inp)
     shp = lambda x: x.reshape(N, L, H, x.shape[-1])
     o2, s2 = gdn2.chunk_fwd(shp(d["q"]), shp(d["k"]), shp(d["v"]), shp(d["log_alpha"]), shp(d["b"]),
-                            shp(d["w"]), d["s0"])
+                            shp(d["w"]), d["s0"], fused=True)
     torch.cuda.synchronize()
     assert torch.equal(o.reshape(N, L, H, -1), o2)
     assert torch.equal(s, s2)
