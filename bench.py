@@ -44,6 +44,13 @@ def chunk_bytes(B, T, H, dk, dv, in_bytes=2, with_s0=False):
     return B * T * H * per_head_token + state
 
 
+def logits_chunk_bytes(B, T, H, dk, dv, in_bytes=2):
+    """The same for the forward from gate logits: the decay logits are read in the input dtype
+    instead of an fp32 log alpha (1,792 B per head-token at d = 128 in bf16)."""
+    per_head_token = 4 * dk * in_bytes + 2 * dv * in_bytes + dv * in_bytes
+    return B * T * H * per_head_token + B * H * dk * dv * 4
+
+
 def fp32_o_extra_bytes(B, T, H, dv, in_bytes=2):
     """Bytes an fp32 o writes beyond the input-dtype o that chunk_bytes counts."""
     return B * T * H * dv * (4 - in_bytes)
@@ -370,6 +377,48 @@ def run_mixer(args, torch, gdn2, W, dev):
                     "frac": go / HBM_PEAK_GBPS, "algorithmic_bytes_per_launch": bo}}
 
 
+def run_logits(args, torch, gdn2, W, dev, out_dtype):
+    """Gate activations inside the recurrence kernels, on the training shape: the forward from
+    gate logits alone, and the layer's two passes both ways -- prep forming every input
+    (q, k, v, b, w, log alpha) then the forward, against prep forming q, k, v only then the
+    forward from logits.  Inputs are the mixer workload's projection outputs."""
+    wl = W.TRAIN_4K
+    x = {n: t.to(dev) for n, t in W.make_mixer_inputs(wl).items()}
+    names = ("xq", "xk", "xv", "xb", "xw", "xa", "conv_q", "conv_k", "conv_v")
+    full = gdn2.mixer_prep(*[x[n] for n in names])
+    part = gdn2.mixer_prep(*[x[n] for n in names], gates=False)
+    o = torch.empty((wl.B, wl.T, wl.H, wl.dv), dtype=out_dtype, device=dev)
+    sT = torch.empty((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=dev)
+
+    def fwd_logits():
+        gdn2.chunk_fwd_logits(part["q"], part["k"], part["v"], x["xa"], x["xb"], x["xw"], None, o=o,
+                              final_state=sT, out_dtype=out_dtype)
+
+    def layer_activated():
+        gdn2.mixer_prep(*[x[n] for n in names], out=full)
+        gdn2.chunk_fwd(full["q"], full["k"], full["v"], full["log_alpha"], full["b"], full["w"], None, o=o,
+                       final_state=sT, out_dtype=out_dtype)
+
+    def layer_logits():
+        gdn2.mixer_prep(*[x[n] for n in names], out=part, gates=False)
+        fwd_logits()
+
+    ms = time_launches(fwd_logits, args.steps, args.warmup, torch)
+    ms_la = time_launches(layer_activated, args.steps, args.warmup, torch)
+    ms_ll = time_launches(layer_logits, args.steps, args.warmup, torch)
+    nbytes = logits_chunk_bytes(wl.B, wl.T, wl.H, wl.dk, wl.dv)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    del x, full, part, o, sT
+    torch.cuda.empty_cache()
+    return {"workload": wl.name + " (gate logits)", "us_per_launch": ms * 1e3,
+            "tokens_per_s": wl.B * wl.T / (ms * 1e-3), "GBps": gbps, "peak": HBM_PEAK_GBPS,
+            "frac": gbps / HBM_PEAK_GBPS, "algorithmic_bytes_per_launch": nbytes,
+            "bytes_per_head_token": 4 * wl.dk * 2 + 3 * wl.dv * 2,
+            "prep_then_forward_us": {"activated_gates": ms_la * 1e3, "gates_in_kernel": ms_ll * 1e3},
+            "activations_not_stored_bytes": wl.B * wl.T * wl.H * (wl.dk * 4 + wl.dk * 2 + wl.dv * 2),
+            "note": "alpha, b, w = sigmoid of bf16 logits, formed on load; no activated copy is written"}
+
+
 def run_decode(args, torch, gdn2, W, dev, out_dtype):
     """Decode workload: N=256 sequences x H=16, one token per step, state updated in place.  The
     whole loop of --decode-steps steps (1024, the workload's length) is timed as one event pair
@@ -428,7 +477,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out-bf16", action="store_true", help="write o in bf16 instead of fp32")
-    ap.add_argument("--only", choices=("chunk", "decode", "prefill", "bwd", "mixer", "long", "sweep"),
+    ap.add_argument("--only", choices=("chunk", "decode", "prefill", "bwd", "mixer", "long", "sweep", "logits"),
                     default=None, help="time one workload only (profiler runs); prints its figures")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run only a plain device-to-device copy of MIB MiB (--steps times): "
@@ -461,7 +510,8 @@ def main():
             "prefill": lambda: {"prefill_varlen": run_prefill(args, torch, gdn2, W, dev, out_dtype)},
             "bwd": lambda: {"backward": run_bwd(args, torch, gdn2, W, dev)},
             "mixer": lambda: {"mixer": run_mixer(args, torch, gdn2, W, dev)},
-            "long": lambda: {"long_context": run_long(args, torch, gdn2, W, dev, out_dtype)}}
+            "long": lambda: {"long_context": run_long(args, torch, gdn2, W, dev, out_dtype)},
+            "logits": lambda: {"gates_in_kernel": run_logits(args, torch, gdn2, W, dev, out_dtype)}}
     if args.only in only:
         print(json.dumps(only[args.only]()), flush=True)
         return
@@ -486,6 +536,7 @@ def main():
     pre = run_prefill(args, torch, gdn2, W, dev, out_dtype)
     bwd = run_bwd(args, torch, gdn2, W, dev)
     mixer = run_mixer(args, torch, gdn2, W, dev)
+    mixer["gates_in_kernel"] = run_logits(args, torch, gdn2, W, dev, out_dtype)
     print("prefill, backward, mixer done", file=sys.stderr, flush=True)
     flops = chunk_flops(wl.B, wl.T, wl.H, wl.dk, wl.dv)
     extra = fp32_o_extra_bytes(wl.B, wl.T, wl.H, wl.dv) if out_dtype == torch.float32 else 0

@@ -27,7 +27,7 @@ import threading
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_workspace_bytes", "chunk_fwd_varlen", "chunk_bwd", "chunk_bwd_workspace_bytes",
+__all__ = ["chunk_fwd", "chunk_fwd_logits", "chunk_fwd_workspace_bytes", "chunk_fwd_varlen", "chunk_bwd", "chunk_bwd_workspace_bytes",
            "chunk_bwd_noalloc", "SCRATCH_BYTES", "decode_step", "mixer_prep",
            "mixer_out", "supported", "version", "library_path", "Gdn2Error", "CHUNK"]
 
@@ -65,6 +65,8 @@ def _load():
         P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         lib.gdn2_chunk_fwd.argtypes = [P] * 9 + [I64] * 5 + [I32, I32, P, ctypes.c_size_t, P]
         lib.gdn2_chunk_fwd.restype = I32
+        lib.gdn2_chunk_fwd_logits.argtypes = [P] * 9 + [I64] * 5 + [I32, I32, P, ctypes.c_size_t, P]
+        lib.gdn2_chunk_fwd_logits.restype = I32
         lib.gdn2_chunk_fwd_workspace_bytes.argtypes = [I64] * 5 + [I32]
         lib.gdn2_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
         lib.gdn2_chunk_fwd_split_workspace_bytes.argtypes = [I64] * 5 + [I32]
@@ -131,18 +133,34 @@ def chunk_fwd(q, k, v, log_alpha, b, w, initial_state=None, *, o=None, final_sta
     ``fused=True`` the single fused kernel; ``fused=False`` the two-kernel form
     where it exists (bf16, d = 64 or 128).  The two-kernel form's workspace is
     allocated here unless ``workspace`` (uint8) is passed."""
+    return _chunk_fwd_call("gdn2_chunk_fwd", q, k, v, log_alpha, torch.float32, b, w, initial_state, o,
+                           final_state, output_final_state, out_dtype, workspace, fused)
+
+
+def chunk_fwd_logits(q, k, v, a_logit, b_logit, w_logit, initial_state=None, *, o=None, final_state=None,
+                     output_final_state=True, out_dtype=torch.float32, workspace=None, fused=None):
+    """chunk_fwd from the projections' outputs: the kernels form alpha = sigmoid(a_logit),
+    b = sigmoid(b_logit) and w = sigmoid(w_logit) on load.  a_logit, b_logit [B,T,H,dk] and
+    w_logit [B,T,H,dv] in the inputs' dtype (bf16 only).  Everything else as chunk_fwd."""
+    return _chunk_fwd_call("gdn2_chunk_fwd_logits", q, k, v, a_logit, q.dtype, b_logit, w_logit, initial_state,
+                           o, final_state, output_final_state, out_dtype, workspace, fused)
+
+
+def _chunk_fwd_call(fn, q, k, v, decay, decay_dtype, b, w, initial_state, o, final_state,
+                    output_final_state, out_dtype, workspace, fused):
     if q.dim() != 4:
         raise ValueError("q must be [B,T,H,dk]")
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev = q.device
     if dev.type != "cuda":
-        raise ValueError("chunk_fwd runs on the GPU; got tensors on %s" % dev)
+        raise ValueError("%s runs on the GPU; got tensors on %s" % (fn, dev))
     dt = q.dtype
     if dt not in _DTYPES:
         raise TypeError("q dtype must be float32 or bfloat16")
+    decay_name = "log_alpha" if fn == "gdn2_chunk_fwd" else "a_logit"
     for name, t, shp, tdt in (("k", k, (B, T, H, dk), dt), ("v", v, (B, T, H, dv), dt),
-                              ("log_alpha", log_alpha, (B, T, H, dk), torch.float32),
+                              (decay_name, decay, (B, T, H, dk), decay_dtype),
                               ("b", b, (B, T, H, dk), dt), ("w", w, (B, T, H, dv), dt),
                               ("q", q, (B, T, H, dk), dt)):
         _check(name, t, shp, tdt, dev)
@@ -172,12 +190,12 @@ def chunk_fwd(q, k, v, log_alpha, b, w, initial_state=None, *, o=None, final_sta
         ws = workspace[off:]
         if ws.numel() < ws_bytes:
             raise ValueError("workspace holds %d bytes, %d needed" % (ws.numel(), ws_bytes))
-    st = _load().gdn2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
-                                _ptr(initial_state), _ptr(o), _ptr(final_state), B, T, H, dk, dv,
-                                _DTYPES[dt], _DTYPES[out_dtype], _ptr(ws), ws.numel() if ws is not None else 0,
-                                _stream_handle(dev))
+    st = getattr(_load(), fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(b), _ptr(w),
+                              _ptr(initial_state), _ptr(o), _ptr(final_state), B, T, H, dk, dv,
+                              _DTYPES[dt], _DTYPES[out_dtype], _ptr(ws), ws.numel() if ws is not None else 0,
+                              _stream_handle(dev))
     if st != 0:
-        raise Gdn2Error("gdn2_chunk_fwd", st, _load().gdn2_status_string(st).decode())
+        raise Gdn2Error(fn, st, _load().gdn2_status_string(st).decode())
     return o, final_state
 
 
@@ -351,12 +369,13 @@ def chunk_bwd_noalloc(q, k, v, log_alpha, b, w, d_o, initial_state=None, d_final
     return out
 
 
-def mixer_prep(xq, xk, xv, xb, xw, xa, conv_q, conv_k, conv_v, eps=1e-6, *, out=None):
+def mixer_prep(xq, xk, xv, xb, xw, xa, conv_q, conv_k, conv_v, eps=1e-6, *, out=None, gates=True):
     """The recurrence's inputs from the layer's projection outputs, in one pass:
     q, k = L2(SiLU(conv(xq, xk))), v = SiLU(conv(xv)), b, w = sigmoid(xb, xw),
     log_alpha = log sigmoid(xa).  x* [B,T,H,d] in one dtype (bf16 or fp32); conv_* [H*d, 4]
     fp32 causal depthwise taps.  Returns a dict q, k, v, b, w (input dtype) and log_alpha
-    (fp32); ``out`` may hold preallocated outputs."""
+    (fp32); ``out`` may hold preallocated outputs.  ``gates=False`` forms q, k and v only
+    (xb, xw, xa may be None): for chunk_fwd_logits, which activates the gates itself."""
     if xq.dim() != 4:
         raise ValueError("xq must be [B,T,H,dk]")
     B, T, H, dk = xq.shape
@@ -367,16 +386,20 @@ def mixer_prep(xq, xk, xv, xb, xw, xa, conv_q, conv_k, conv_v, eps=1e-6, *, out=
     dt = xq.dtype
     if dt not in _DTYPES:
         raise TypeError("xq dtype must be float32 or bfloat16")
-    for name, t, shp, tdt in (("xk", xk, (B, T, H, dk), dt), ("xv", xv, (B, T, H, dv), dt),
-                              ("xb", xb, (B, T, H, dk), dt), ("xw", xw, (B, T, H, dv), dt),
-                              ("xa", xa, (B, T, H, dk), dt), ("xq", xq, (B, T, H, dk), dt),
-                              ("conv_q", conv_q, (H * dk, 4), torch.float32),
-                              ("conv_k", conv_k, (H * dk, 4), torch.float32),
-                              ("conv_v", conv_v, (H * dv, 4), torch.float32)):
+    checks = [("xk", xk, (B, T, H, dk), dt), ("xv", xv, (B, T, H, dv), dt), ("xq", xq, (B, T, H, dk), dt),
+              ("conv_q", conv_q, (H * dk, 4), torch.float32), ("conv_k", conv_k, (H * dk, 4), torch.float32),
+              ("conv_v", conv_v, (H * dv, 4), torch.float32)]
+    if gates:
+        checks += [("xb", xb, (B, T, H, dk), dt), ("xw", xw, (B, T, H, dv), dt), ("xa", xa, (B, T, H, dk), dt)]
+    else:
+        xb = xw = xa = None
+    for name, t, shp, tdt in checks:
         _check(name, t, shp, tdt, dev)
-    shapes = {"q": ((B, T, H, dk), dt), "k": ((B, T, H, dk), dt), "v": ((B, T, H, dv), dt),
-              "b": ((B, T, H, dk), dt), "w": ((B, T, H, dv), dt), "log_alpha": ((B, T, H, dk), torch.float32)}
-    res = dict(out) if out is not None else {}
+    shapes = {"q": ((B, T, H, dk), dt), "k": ((B, T, H, dk), dt), "v": ((B, T, H, dv), dt)}
+    if gates:
+        shapes.update({"b": ((B, T, H, dk), dt), "w": ((B, T, H, dv), dt),
+                       "log_alpha": ((B, T, H, dk), torch.float32)})
+    res = {n: t for n, t in (dict(out) if out is not None else {}).items() if n in shapes}
     for name, (shp, tdt) in shapes.items():
         if res.get(name) is None:
             res[name] = torch.empty(shp, dtype=tdt, device=dev)
@@ -384,8 +407,8 @@ def mixer_prep(xq, xk, xv, xb, xw, xa, conv_q, conv_k, conv_v, eps=1e-6, *, out=
             _check(name, res[name], shp, tdt, dev)
     st = _load().gdn2_mixer_prep(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(xb), _ptr(xw), _ptr(xa), _ptr(conv_q),
                                  _ptr(conv_k), _ptr(conv_v), _ptr(res["q"]), _ptr(res["k"]), _ptr(res["v"]),
-                                 _ptr(res["b"]), _ptr(res["w"]), _ptr(res["log_alpha"]), B, T, H, dk, dv,
-                                 float(eps), _DTYPES[dt], _stream_handle(dev))
+                                 _ptr(res.get("b")), _ptr(res.get("w")), _ptr(res.get("log_alpha")), B, T, H,
+                                 dk, dv, float(eps), _DTYPES[dt], _stream_handle(dev))
     if st != 0:
         raise Gdn2Error("gdn2_mixer_prep", st, _load().gdn2_status_string(st).decode())
     return res

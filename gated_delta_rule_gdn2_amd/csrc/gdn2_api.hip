@@ -97,15 +97,17 @@ bool bwd_layout(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, BwdLayo
 
 // Validation and launch shared by the fixed-length and the packed-sequence forward.  NS
 // sequences (states [NS, H, dk, dv]); the token tensors hold NT tokens in all; T_or_total is
-// the kernels' token parameter (T per sequence, or the packed total).
-gdn2_status_t chunk_fwd_common(const void* q, const void* k, const void* v, const float* log_alpha,
+// the kernels' token parameter (T per sequence, or the packed total).  decay is log alpha
+// (fp32), or with logits the decay logits in the input dtype, and b, w are then gate logits.
+gdn2_status_t chunk_fwd_common(const void* q, const void* k, const void* v, const void* decay,
                                const void* b, const void* w, const float* initial_state, void* o,
                                float* final_state, const int64_t* cu_seqlens, int64_t NS,
                                int64_t T_or_total, int64_t NT, int64_t H, int64_t dk, int64_t dv,
                                gdn2_dtype_t dtype, gdn2_dtype_t o_dtype, void* workspace,
-                               size_t workspace_bytes, void* stream) {
-    if (!q || !k || !v || !log_alpha || !b || !w || !o) return GDN2_ERR_NULL;
+                               size_t workspace_bytes, void* stream, bool logits = false) {
+    if (!q || !k || !v || !decay || !b || !w || !o) return GDN2_ERR_NULL;
     if (dtype != GDN2_DTYPE_F32 && dtype != GDN2_DTYPE_BF16) return GDN2_ERR_UNSUPPORTED;
+    if (logits && dtype != GDN2_DTYPE_BF16) return GDN2_ERR_UNSUPPORTED;
     if (o_dtype != GDN2_DTYPE_F32 && o_dtype != dtype) return GDN2_ERR_UNSUPPORTED;
     if (H < 1 || dk < 1 || dv < 1) return GDN2_ERR_SHAPE;
     if (!chunk_supported(dk, dv, dtype)) return GDN2_ERR_UNSUPPORTED;
@@ -118,13 +120,13 @@ gdn2_status_t chunk_fwd_common(const void* q, const void* k, const void* v, cons
     if (NS * H * (dv / 16) > UINT_MAX / 2) return GDN2_ERR_SHAPE;
     // per-lane offsets inside one chunk are formed with 24-bit multiplies of the token stride
     if (H * dk >= (int64_t(1) << 24) || H * dv >= (int64_t(1) << 24)) return GDN2_ERR_SHAPE;
-    const void* ptrs[] = {q, k, v, log_alpha, b, w, initial_state, o, final_state};
+    const void* ptrs[] = {q, k, v, decay, b, w, initial_state, o, final_state};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return GDN2_ERR_MISALIGNED;
     const int64_t es = dtype == GDN2_DTYPE_BF16 ? 2 : 4;
     const int64_t eo = o_dtype == GDN2_DTYPE_BF16 ? 2 : 4;
     const Range in_ranges[] = {range_of(q, nk * es), range_of(k, nk * es), range_of(v, nv * es),
-                               range_of(log_alpha, nk * 4), range_of(b, nk * es),
+                               range_of(decay, nk * (logits ? es : 4)), range_of(b, nk * es),
                                range_of(w, nv * es)};
     const Range ro = range_of(o, nv * eo);
     for (const Range& r : in_ranges)
@@ -158,8 +160,11 @@ gdn2_status_t chunk_fwd_common(const void* q, const void* k, const void* v, cons
     if (NT == 0 && !final_state) return GDN2_OK;  // nothing to compute or write
     const int cus = device_cus();
     if (cus <= 0) return GDN2_ERR_HIP;
-    gdn2::ChunkArgs a{q, k, v, log_alpha, b, w, initial_state, o, final_state, NS, T_or_total, H, dk, dv,
-                      dtype == GDN2_DTYPE_BF16, o_dtype == GDN2_DTYPE_F32, stream, cu_seqlens, cus};
+    gdn2::ChunkArgs a{q, k, v, logits ? nullptr : static_cast<const float*>(decay), b, w, initial_state, o,
+                      final_state, NS, T_or_total, H, dk, dv, dtype == GDN2_DTYPE_BF16,
+                      o_dtype == GDN2_DTYPE_F32, stream, cu_seqlens, cus};
+    a.gate_logits = logits;
+    a.decay_logits = logits ? decay : nullptr;
     if (split) return gdn2::launch_chunk_split(a, workspace) == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
     const int dvs = choose_dvs(NS * H, dv, cus);
     return gdn2::launch_chunk_fwd(a, dvs) == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
@@ -284,6 +289,18 @@ gdn2_status_t gdn2_chunk_fwd(const void* q, const void* k, const void* v, const 
                             dk, dv, dtype, o_dtype, workspace, workspace_bytes, stream);
 }
 
+gdn2_status_t gdn2_chunk_fwd_logits(const void* q, const void* k, const void* v, const void* a_logit,
+                                    const void* b_logit, const void* w_logit, const float* initial_state,
+                                    void* o, float* final_state, int64_t B, int64_t T, int64_t H, int64_t dk,
+                                    int64_t dv, gdn2_dtype_t dtype, gdn2_dtype_t o_dtype, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    if (B < 1 || T < 1) return GDN2_ERR_SHAPE;
+    int64_t BT;
+    if (!mul_ok(B, T, &BT)) return GDN2_ERR_SHAPE;
+    return chunk_fwd_common(q, k, v, a_logit, b_logit, w_logit, initial_state, o, final_state, nullptr, B, T,
+                            BT, H, dk, dv, dtype, o_dtype, workspace, workspace_bytes, stream, true);
+}
+
 gdn2_status_t gdn2_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha,
                                     const void* b, const void* w, const float* initial_state, void* o,
                                     float* final_state, const int64_t* cu_seqlens, int64_t N,
@@ -357,8 +374,11 @@ gdn2_status_t gdn2_mixer_prep(const void* xq, const void* xk, const void* xv, co
                               void* q, void* k, void* v, void* b, void* w, float* log_alpha, int64_t B,
                               int64_t T, int64_t H, int64_t dk, int64_t dv, float eps, gdn2_dtype_t dtype,
                               void* stream) {
-    if (!xq || !xk || !xv || !xb || !xw || !xa || !conv_q || !conv_k || !conv_v) return GDN2_ERR_NULL;
-    if (!q || !k || !v || !b || !w || !log_alpha) return GDN2_ERR_NULL;
+    // b, w and log_alpha all NULL: the gates are left to gdn2_chunk_fwd_logits (xb, xw, xa unused)
+    const bool gates = b || w || log_alpha;
+    if (!gates) xb = xw = xa = nullptr;
+    if (!xq || !xk || !xv || !conv_q || !conv_k || !conv_v || !q || !k || !v) return GDN2_ERR_NULL;
+    if (gates && (!xb || !xw || !xa || !b || !w || !log_alpha)) return GDN2_ERR_NULL;
     if (dtype != GDN2_DTYPE_F32 && dtype != GDN2_DTYPE_BF16) return GDN2_ERR_UNSUPPORTED;
     if (B < 1 || T < 1 || H < 1 || dk < 1 || dv < 1 || !(eps >= 0.f) || eps > 1e30f) return GDN2_ERR_SHAPE;
     if (!mixer_supported(dk, dv, dtype)) return GDN2_ERR_UNSUPPORTED;
@@ -371,11 +391,12 @@ gdn2_status_t gdn2_mixer_prep(const void* xq, const void* xk, const void* xv, co
     for (const void* p : ptrs)
         if (!aligned16(p)) return GDN2_ERR_MISALIGNED;
     const int64_t es = dtype == GDN2_DTYPE_BF16 ? 2 : 4;
-    const Range ins[] = {range_of(xq, nk * es), range_of(xk, nk * es), range_of(xv, nv * es), range_of(xb, nk * es),
-                         range_of(xw, nv * es), range_of(xa, nk * es), range_of(conv_q, H * dk * 16),
+    const int64_t gk = gates ? nk : 0, gv = gates ? nv : 0;  // gate tensors: empty ranges when absent
+    const Range ins[] = {range_of(xq, nk * es), range_of(xk, nk * es), range_of(xv, nv * es), range_of(xb, gk * es),
+                         range_of(xw, gv * es), range_of(xa, gk * es), range_of(conv_q, H * dk * 16),
                          range_of(conv_k, H * dk * 16), range_of(conv_v, H * dv * 16)};
-    const Range outs[] = {range_of(q, nk * es), range_of(k, nk * es), range_of(v, nv * es), range_of(b, nk * es),
-                          range_of(w, nv * es), range_of(log_alpha, nk * 4)};
+    const Range outs[] = {range_of(q, nk * es), range_of(k, nk * es), range_of(v, nv * es), range_of(b, gk * es),
+                          range_of(w, gv * es), range_of(log_alpha, gk * 4)};
     constexpr int NO = sizeof(outs) / sizeof(outs[0]);
     for (int i = 0; i < NO; ++i) {
         for (const Range& r : ins)

@@ -176,9 +176,10 @@ __device__ __forceinline__ void store_tdiag(char* smem, int I, int l16, int g4, 
 // G: the LDS layout (RX work rows of G::LDK bf16, AM, TR, TTR of G::LC); PutP: stores a row
 // segment of P, put_p(row, col, p[4]) for P[row][col .. col + 3]; PutT: receives each diagonal
 // block of T in fp32 as well, put_t(I, t) with lane (i, g) of t holding T_II[i][4 g + r].
-template <typename G, int DK, typename PutP, typename PutT>
+template <typename G, int DK, typename Gt, typename PutP, typename PutT>
 __device__ __forceinline__ void strong_ap_body(char* smem, const bf16* __restrict__ q, const bf16* __restrict__ k,
-                                               const bf16* __restrict__ bgate, const float* __restrict__ log_alpha,
+                                               const bf16* __restrict__ bgate,
+                                               const typename Gt::Decay* __restrict__ decay,
                                                int64_t chunk_base, int64_t tok_stride_k, int ntok, PutP put_p,
                                                PutT put_t) {
     constexpr int CPL = DK / 32, LDK = G::LDK, LC = G::LC;
@@ -224,10 +225,10 @@ __device__ __forceinline__ void strong_ap_body(char* smem, const bf16* __restric
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         const int i = I * 16 + ts * 4 + m;
-        const Vec<float, CPL> g =
-            load_vec<float, CPL>(log_alpha + chunk_base + (int64_t)min(i, ntok - 1) * tok_stride_k + c0);
+        const Vec<typename Gt::Decay, CPL> g = load_vec<typename Gt::Decay, CPL>(
+            decay + chunk_base + (int64_t)min(i, ntok - 1) * tok_stride_k + c0);
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) al[c][m] = i < ntok ? exp_neg(g.v[c]) : 1.f;
+        for (int c = 0; c < CPL; ++c) al[c][m] = i < ntok ? Gt::alpha((float)g.v[c]) : 1.f;
     }
 #pragma unroll
     for (int c = 0; c < CPL; ++c) x16[c] = __shfl_xor(al[c][0] * al[c][1] * al[c][2] * al[c][3], 16);
@@ -278,7 +279,7 @@ __device__ __forceinline__ void strong_ap_body(char* smem, const bf16* __restric
             for (int c = 0; c < CPL; ++c) {
                 const float qv = valid ? (float)xq.v[c] : 0.f;
                 const float kv = valid ? (float)xk.v[c] : 0.f;
-                const float bk = valid ? (float)xb.v[c] * kv : 0.f;
+                const float bk = valid ? Gt::gate((float)xb.v[c]) * kv : 0.f;
                 if (L == 4) {
                     ra[c] = 0.f; rp[c] = qv; cl[c] = kv;
                 } else {
@@ -328,12 +329,12 @@ __device__ __forceinline__ void strong_ap_body(char* smem, const bf16* __restric
 
 // The same out of line, for a loop whose register allocation the strong path must not raise.
 // (Its LDS and global accesses then go through flat addresses; strong chunks are rare there.)
-template <typename G, int DK, typename PutP, typename PutT>
+template <typename G, int DK, typename Gt, typename PutP, typename PutT>
 __device__ __noinline__ void strong_ap(char* smem, const bf16* __restrict__ q, const bf16* __restrict__ k,
-                                       const bf16* __restrict__ bgate, const float* __restrict__ log_alpha,
+                                       const bf16* __restrict__ bgate, const typename Gt::Decay* __restrict__ decay,
                                        int64_t chunk_base, int64_t tok_stride_k, int ntok, PutP put_p,
                                        PutT put_t) {
-    strong_ap_body<G, DK>(smem, q, k, bgate, log_alpha, chunk_base, tok_stride_k, ntok, put_p, put_t);
+    strong_ap_body<G, DK, Gt>(smem, q, k, bgate, decay, chunk_base, tok_stride_k, ntok, put_p, put_t);
 }
 
 }  // namespace cb

@@ -86,17 +86,17 @@ struct Cfg {
 
 // Inputs of one chunk as one thread loads them: CPL key channels of 4 tokens, and VC value
 // columns of TPV tokens.
-template <int CPL, int TPV, int VC>
+template <int CPL, int TPV, int VC, typename Decay>
 struct In {
-    Vec<float, CPL> g[4];
+    Vec<Decay, CPL> g[4];
     Vec<bf16, CPL> q[4], k[4], b[4];
     Vec<bf16, VC> w[TPV], v[TPV];
 };
 
-template <typename OutT, int DK, int DV, int DVS>
+template <typename OutT, int DK, int DV, int DVS, typename Gt>
 __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const float* __restrict__ log_alpha, const bf16* __restrict__ bgate, const bf16* __restrict__ wgate,
+    const typename Gt::Decay* __restrict__ decay, const bf16* __restrict__ bgate, const bf16* __restrict__ wgate,
     const float* initial_state, OutT* __restrict__ o, float* final_state, int B, int Tparam, int H,
     int nslices, int xcd_map, const int64_t* __restrict__ cu_seqlens) {
     using G = Cfg<DK, DVS>;
@@ -193,19 +193,21 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
     const int rsk = H * DK, rsv = H * DV;  // elements between consecutive tokens
     // The next chunk's inputs are loaded in two batches (decays and queries; keys, gates and
     // values), issued well before they are needed.
-    auto load_first = [&](int n, In<CPL, TPV, VC>& in) {
+    using Decay = typename Gt::Decay;
+    using InC = In<CPL, TPV, VC, Decay>;
+    auto load_first = [&](int n, InC& in) {
         const int t0 = n * C, last = Tlen - 1 - t0;
         const int64_t cb = seq_base_k + (int64_t)t0 * tok_stride_k;
-        const float* gb = log_alpha + cb;
+        const Decay* gb = decay + cb;
         const bf16* qb = q + cb;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const uint32_t e = __umul24(min(I * 16 + ts * 4 + m, last), rsk) + c0;
-            in.g[m] = gload<float, CPL>(gb, e * 4);
+            in.g[m] = gload<Decay, CPL>(gb, e * (uint32_t)sizeof(Decay));
             in.q[m] = gload<bf16, CPL>(qb, e * 2);
         }
     };
-    auto load_second = [&](int n, In<CPL, TPV, VC>& in) {
+    auto load_second = [&](int n, InC& in) {
         const int t0 = n * C, last = Tlen - 1 - t0;
         const int64_t cb = seq_base_k + (int64_t)t0 * tok_stride_k;
         const bf16* kb = k + cb;
@@ -227,7 +229,7 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
         }
     };
 
-    In<CPL, TPV, VC> in;
+    InC in;
     if (Tlen > 0) {
         load_first(0, in);
         load_second(0, in);
@@ -252,7 +254,7 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                 if (t0 + I * 16 + ts * 4 + m >= Tlen) {
 #pragma unroll
                     for (int c = 0; c < CPL; ++c) {
-                        in.g[m].v[c] = 0.f;
+                        in.g[m].v[c] = Gt::no_decay();
                         in.q[m].v[c] = (bf16)0.f;
                         in.k[m].v[c] = (bf16)0.f;
                         in.b[m].v[c] = (bf16)0.f;
@@ -281,7 +283,7 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                 float p = 1.f;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    al[m] = exp_neg(in.g[m].v[c]);
+                    al[m] = Gt::alpha((float)in.g[m].v[c]);
                     p *= al[m];
                     lp[c][m] = p;
                 }
@@ -310,14 +312,14 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                 *reinterpret_cast<V*>(sBLK + I * DK + c0) = x;
             }
         }
-        // write gate times value, transposed ([column][token]) in fp32 (exact: a product of
-        // two bf16 numbers)
+        // write gate times value, transposed ([column][token]) in fp32 (exact for given gates: a
+        // product of two bf16 numbers)
         const int wvb = opq(G::WVT + (vcol * LCF + vtok) * 4);
 #pragma unroll
         for (int j = 0; j < VC; ++j) {
             float x[TPV];
 #pragma unroll
-            for (int i = 0; i < TPV; ++i) x[i] = (float)in.w[i].v[j] * (float)in.v[i].v[j];
+            for (int i = 0; i < TPV; ++i) x[i] = Gt::gate((float)in.w[i].v[j]) * (float)in.v[i].v[j];
             if constexpr (TPV == 1) {
                 *F32(wvb + j * LCF * 4) = x[0];
             } else {
@@ -389,7 +391,7 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                         const float kv = (float)in.k[m].v[c];
                         const float gam = bex[c] * lp[c][m];
                         xq[c] = (float)in.q[m].v[c] * gam;
-                        xb[c] = (float)in.b[m].v[c] * kv * gam;
+                        xb[c] = Gt::gate((float)in.b[m].v[c]) * kv * gam;
                         kgt[c][m] = kv * (ls[c][m] * esa[c]);
                         xki[c] = kgt[c][m] * invgc[c];
                         bgt[c][m] = xb[c];
@@ -417,7 +419,7 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                     for (int c = 0; c < CPL; ++c) {
                         const float qv = (float)in.q[m].v[c];
                         const float kv = (float)in.k[m].v[c];
-                        const float bk = (float)in.b[m].v[c] * kv;
+                        const float bk = Gt::gate((float)in.b[m].v[c]) * kv;
                         const float gam = before[c] * pre[c][m];
                         xq[c] = qv * gam;
                         bgt[c][m] = bk * gam;
@@ -547,7 +549,7 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                 }
             }
         } else {
-            strong_ap<G, DK>(smem, q, k, bgate, log_alpha, seq_base_k + (int64_t)t0 * tok_stride_k, tok_stride_k,
+            strong_ap<G, DK, Gt>(smem, q, k, bgate, decay, seq_base_k + (int64_t)t0 * tok_stride_k, tok_stride_k,
                              Tlen - t0, [&](int row, int col, const float (&p)[4]) {
                                  const int idx = row * LC + col;
                                  store_bf16_split<4>(sPh + idx, sPl + idx, p);
@@ -851,34 +853,40 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
     }
 }
 
-template <typename OutT, int D, int DVS>
+template <typename OutT, int D, int DVS, typename Gt>
 hipError_t launch(const ChunkArgs& a) {
     const int nslices = D / DVS;
     const int64_t groups = (int64_t)a.B * a.H * nslices;
     const int xcd_map = ((int64_t)a.B * a.H) % 8 == 0 ? 1 : 0;
-    hipLaunchKernelGGL((chunk_bf16_kernel<OutT, D, D, DVS>), dim3((unsigned)groups), dim3(NT), 0,
+    hipLaunchKernelGGL((chunk_bf16_kernel<OutT, D, D, DVS, Gt>), dim3((unsigned)groups), dim3(NT), 0,
                        (hipStream_t)a.stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
-                       a.log_alpha, (const bf16*)a.b, (const bf16*)a.w, a.initial_state, (OutT*)a.o,
-                       a.final_state, (int)a.B, (int)a.T, (int)a.H, nslices, xcd_map, a.cu_seqlens);
+                       (const typename Gt::Decay*)a.decay(), (const bf16*)a.b, (const bf16*)a.w,
+                       a.initial_state, (OutT*)a.o, a.final_state, (int)a.B, (int)a.T, (int)a.H, nslices,
+                       xcd_map, a.cu_seqlens);
     return hipGetLastError();
 }
 
-template <typename OutT, int D>
+template <typename OutT, int D, typename Gt>
 hipError_t launch_dvs(const ChunkArgs& a, int dvs) {
     switch (dvs) {
-        case 16: return launch<OutT, D, 16>(a);
-        case 32: return launch<OutT, D, 32>(a);
-        case 64: return launch<OutT, D, 64>(a);
+        case 16: return launch<OutT, D, 16, Gt>(a);
+        case 32: return launch<OutT, D, 32, Gt>(a);
+        case 64: return launch<OutT, D, 64, Gt>(a);
     }
     return hipErrorInvalidValue;
+}
+
+template <typename OutT, int D>
+hipError_t launch_gates(const ChunkArgs& a, int dvs) {
+    return a.gate_logits ? launch_dvs<OutT, D, GatesLogits>(a, dvs) : launch_dvs<OutT, D, GatesActivated>(a, dvs);
 }
 
 }  // namespace cb
 
 hipError_t launch_chunk_bf16(const ChunkArgs& a, int dvs) {
     if (a.dk != a.dv || !a.dtype_bf16) return hipErrorInvalidValue;
-    if (a.dk == 128) return a.out_f32 ? cb::launch_dvs<float, 128>(a, dvs) : cb::launch_dvs<bf16, 128>(a, dvs);
-    if (a.dk == 64) return a.out_f32 ? cb::launch_dvs<float, 64>(a, dvs) : cb::launch_dvs<bf16, 64>(a, dvs);
+    if (a.dk == 128) return a.out_f32 ? cb::launch_gates<float, 128>(a, dvs) : cb::launch_gates<bf16, 128>(a, dvs);
+    if (a.dk == 64) return a.out_f32 ? cb::launch_gates<float, 64>(a, dvs) : cb::launch_gates<bf16, 64>(a, dvs);
     return hipErrorInvalidValue;
 }
 

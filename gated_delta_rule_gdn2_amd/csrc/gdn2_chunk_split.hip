@@ -85,9 +85,9 @@ struct LocalCfg {
     static_assert(FLG + 32 <= TR, "votes inside AM");
 };
 
-template <int CPL>
+template <int CPL, typename Decay>
 struct InK {
-    Vec<float, CPL> g[4];
+    Vec<Decay, CPL> g[4];
     Vec<bf16, CPL> q[4], k[4], b[4];
 };
 
@@ -105,9 +105,9 @@ __device__ __forceinline__ void put_split4(char* rec_plane_hi, char* rec_plane_l
     *reinterpret_cast<bf16x4*>(rec_plane_lo + idx * 2) = l;
 }
 
-template <int DK>
+template <int DK, typename Gt>
 __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ log_alpha,
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const typename Gt::Decay* __restrict__ decay,
     const bf16* __restrict__ bgate, char* __restrict__ recs, int Tparam, int H, int c_begin, int c_end,
     int run) {
     using G = LocalCfg<DK>;
@@ -135,7 +135,8 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
     const int64_t seq_base_k = (tok0 * H + h) * DK;
     const int rsk = H * DK;
 
-    auto load_first = [&](int n, InK<CPL>& in) {
+    using Decay = typename Gt::Decay;
+    auto load_first = [&](int n, InK<CPL, Decay>& in) {
         const int lane = tid & 63, ts = lane >> 4;
         const int c0 = hf * (DK / 2) + (lane & 15) * CPL;
         const int t0 = n * C, last = Tlen - 1 - t0;
@@ -143,11 +144,11 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const uint32_t e = __umul24(min(I * 16 + ts * 4 + m, last), rsk) + c0;
-            in.g[m] = cb::gload<float, CPL>(log_alpha + cbase, e * 4);
+            in.g[m] = cb::gload<Decay, CPL>(decay + cbase, e * (uint32_t)sizeof(Decay));
             in.q[m] = cb::gload<bf16, CPL>(q + cbase, e * 2);
         }
     };
-    auto load_second = [&](int n, InK<CPL>& in) {
+    auto load_second = [&](int n, InK<CPL, Decay>& in) {
         const int lane = tid & 63, ts = lane >> 4;
         const int c0 = hf * (DK / 2) + (lane & 15) * CPL;
         const int t0 = n * C, last = Tlen - 1 - t0;
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
         }
     };
 
-    InK<CPL> in;
+    InK<CPL, Decay> in;
     if (cr0 < cr1) {
         load_first(c_begin + cr0, in);
         load_second(c_begin + cr0, in);
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
                 if (t0 + I * 16 + ts * 4 + m >= Tlen) {
 #pragma unroll
                     for (int c = 0; c < CPL; ++c) {
-                        in.g[m].v[c] = 0.f;
+                        in.g[m].v[c] = Gt::no_decay();
                         in.q[m].v[c] = (bf16)0.f;
                         in.k[m].v[c] = (bf16)0.f;
                         in.b[m].v[c] = (bf16)0.f;
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
                 float p = 1.f;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    al[m] = exp_neg(in.g[m].v[c]);
+                    al[m] = Gt::alpha((float)in.g[m].v[c]);
                     p *= al[m];
                     lp[c][m] = p;
                 }
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
                         const float kv = (float)in.k[m].v[c];
                         const float gam = bex[c] * lp[c][m];
                         xq[c] = (float)in.q[m].v[c] * gam;
-                        xb[c] = (float)in.b[m].v[c] * kv * gam;
+                        xb[c] = Gt::gate((float)in.b[m].v[c]) * kv * gam;
                         kgt[c][m] = kv * (ls[c][m] * esa[c]);
                         xki[c] = kgt[c][m] * invgc[c];
                     }
@@ -315,7 +316,7 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
                     for (int c = 0; c < CPL; ++c) {
                         const float qv = (float)in.q[m].v[c];
                         const float kv = (float)in.k[m].v[c];
-                        const float bk = (float)in.b[m].v[c] * kv;
+                        const float bk = Gt::gate((float)in.b[m].v[c]) * kv;
                         const float gam = before[c] * pre[c][m];
                         xq[c] = qv * gam;
                         xb[c] = bk * gam;
@@ -444,7 +445,7 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
                 }
             }
         } else {
-            cb::strong_ap_body<G, DK>(smem, q, k, bgate, log_alpha, seq_base_k + (int64_t)t0 * tok_stride_k, tok_stride_k,
+            cb::strong_ap_body<G, DK, Gt>(smem, q, k, bgate, decay, seq_base_k + (int64_t)t0 * tok_stride_k, tok_stride_k,
                                  Tlen - t0, put_p, [=](int Ib, const f32x4& t) {
                                      float x[4];
                                      cb::acc_to_array(t, x);
@@ -608,7 +609,7 @@ __device__ __forceinline__ Frag<bf16> frag_tri(const char* plane, int row, int k
 // hi / lo K = 32 operands of an accumulator pair (permuted slot map)
 __device__ __forceinline__ cb::Split32 split_pair(const f32x4& a, const f32x4& b) { return cb::split32(a, b); }
 
-template <typename OutT, int D>
+template <typename OutT, int D, typename Gt>
 __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
     const char* __restrict__ recs, const bf16* __restrict__ v, const bf16* __restrict__ wgate,
     const float* state_in, float* state_out, OutT* __restrict__ o, int Tparam, int H, int nslices,
@@ -744,7 +745,7 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const bool in = t0 + rt * 16 + g4 * 4 + r < Tlen;
-                Rr[rt][r] = (in ? (float)wv[0][rt][r] * (float)wv[1][rt][r] : 0.f) - X[rt][r];
+                Rr[rt][r] = (in ? Gt::gate((float)wv[0][rt][r]) * (float)wv[1][rt][r] : 0.f) - X[rt][r];
             }
         if (i + 1 < nb) load_wv(n + 1, wv);
         // the key-row fragments of the state update
@@ -845,7 +846,7 @@ size_t split_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d) {
     return (size_t)(B * H * bc * rb + B * H * d * d * 4);
 }
 
-template <typename OutT, int D>
+template <typename OutT, int D, typename Gt>
 hipError_t launch_split_d(const ChunkArgs& a, char* ws) {
     const int64_t BH = a.B * a.H;
     const int nc = (int)((a.T + 63) / 64);
@@ -860,23 +861,28 @@ hipError_t launch_split_d(const ChunkArgs& a, char* ws) {
         const int64_t per = (BH * (c1 - c0) + a.cus - 1) / a.cus;
         const int run = (int)(per < 1 ? 1 : per > c1 - c0 ? c1 - c0 : per);
         const int runs = (c1 - c0 + run - 1) / run;
-        hipLaunchKernelGGL((sp::local_kernel<D>), dim3((unsigned)(BH * runs)), dim3(sp::NT_LOCAL), 0, st,
-                           (const bf16*)a.q, (const bf16*)a.k, a.log_alpha, (const bf16*)a.b, ws, (int)a.T,
-                           (int)a.H, c0, c1, run);
+        hipLaunchKernelGGL((sp::local_kernel<D, Gt>), dim3((unsigned)(BH * runs)), dim3(sp::NT_LOCAL), 0, st,
+                           (const bf16*)a.q, (const bf16*)a.k, (const typename Gt::Decay*)a.decay(),
+                           (const bf16*)a.b, ws, (int)a.T, (int)a.H, c0, c1, run);
         const float* sin = c0 == 0 ? a.initial_state : carry;
         float* sout = c1 == nc ? a.final_state : carry;
-        hipLaunchKernelGGL((sp::state_kernel<OutT, D>), dim3((unsigned)(BH * nslices)), dim3(sp::NT_STATE), 0, st,
+        hipLaunchKernelGGL((sp::state_kernel<OutT, D, Gt>), dim3((unsigned)(BH * nslices)), dim3(sp::NT_STATE), 0, st,
                            (const char*)ws, (const bf16*)a.v, (const bf16*)a.w, sin, sout, (OutT*)a.o, (int)a.T,
                            (int)a.H, nslices, xcd_map, c0, c1);
     }
     return hipGetLastError();
 }
 
+template <typename OutT, int D>
+hipError_t launch_split_g(const ChunkArgs& a, char* ws) {
+    return a.gate_logits ? launch_split_d<OutT, D, GatesLogits>(a, ws) : launch_split_d<OutT, D, GatesActivated>(a, ws);
+}
+
 hipError_t launch_chunk_split(const ChunkArgs& a, void* workspace) {
     char* ws = static_cast<char*>(workspace);
     if (!a.dtype_bf16 || a.dk != a.dv || a.cu_seqlens) return hipErrorInvalidValue;
-    if (a.dk == 128) return a.out_f32 ? launch_split_d<float, 128>(a, ws) : launch_split_d<bf16, 128>(a, ws);
-    if (a.dk == 64) return a.out_f32 ? launch_split_d<float, 64>(a, ws) : launch_split_d<bf16, 64>(a, ws);
+    if (a.dk == 128) return a.out_f32 ? launch_split_g<float, 128>(a, ws) : launch_split_g<bf16, 128>(a, ws);
+    if (a.dk == 64) return a.out_f32 ? launch_split_g<float, 64>(a, ws) : launch_split_g<bf16, 64>(a, ws);
     return hipErrorInvalidValue;
 }
 

@@ -166,6 +166,33 @@ __device__ __forceinline__ Vec<T, N> load_vec(const T* p) {
 // exp(x) for x <= 0 through the hardware base-2 exponential
 __device__ __forceinline__ float exp_neg(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
+// 1 / (1 + e^-x) through the hardware base-2 exponential and reciprocal (about 1 ulp each); for
+// x below about -88, e^-x overflows to infinity and the reciprocal of infinity is the limit 0
+__device__ __forceinline__ float sigmoid_f(float x) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+}
+
+// How a forward kernel takes the per-token decay and the two gates (page "Why NVIDIA Gated
+// DeltaNet-2 separates erase and write gates", axbrief.com, section "Gated Delta Rule-2": b and
+// w are sigmoids of projections of the token; the decay takes the same form, alpha = sigmoid(a)).
+//   GatesActivated: log alpha in fp32, b and w as given;
+//   GatesLogits:    the projections' outputs a, xb, xw in the input dtype, activated on load
+//                   (alpha = sigmoid(a), b = sigmoid(xb), w = sigmoid(xw)), so no activated copy
+//                   of them is ever stored.
+struct GatesActivated {
+    using Decay = float;
+    // the decay input of a token that decays nothing (alpha = 1)
+    __device__ static __forceinline__ Decay no_decay() { return 0.f; }
+    __device__ static __forceinline__ float alpha(float log_alpha) { return exp_neg(log_alpha); }
+    __device__ static __forceinline__ float gate(float g) { return g; }
+};
+struct GatesLogits {
+    using Decay = bf16;
+    __device__ static __forceinline__ Decay no_decay() { return (bf16)__builtin_inff(); }
+    __device__ static __forceinline__ float alpha(float a) { return sigmoid_f(a); }
+    __device__ static __forceinline__ float gate(float x) { return sigmoid_f(x); }
+};
+
 
 // Packed sequences, longest first.  A launch walks its ns sequences in workgroup order, one
 // chain of chunks per (sequence, head, slice); when the lengths differ, a long sequence that

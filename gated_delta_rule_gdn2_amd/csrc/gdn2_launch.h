@@ -24,6 +24,12 @@ struct ChunkArgs {
     // nullptr for B sequences of T tokens each
     const int64_t* cu_seqlens = nullptr;
     int cus = 256;  // compute units of the device
+    // gate logits instead of activated gates (bf16 inputs only): decay_logits [.., dk] holds a
+    // with alpha = sigmoid(a), and b, w hold logits xb, xw with b = sigmoid(xb), w = sigmoid(xw);
+    // log_alpha is then unused
+    bool gate_logits = false;
+    const void* decay_logits = nullptr;
+    const void* decay() const { return gate_logits ? decay_logits : (const void*)log_alpha; }
 };
 
 struct DecodeArgs {

@@ -28,13 +28,8 @@ constexpr int NTW = 16;  // consecutive tokens per prep workgroup
 constexpr float kLn2 = 0.6931471805599453f;
 
 // The activations use the hardware base-2 exponential and logarithm and the hardware
-// reciprocal (about 1 ulp each); these passes are limited by vector ALU issue, not by HBM,
-// once IEEE division and a library log1p are in them.
-__device__ __forceinline__ float sigmoid_f(float x) {
-    // 1 / (1 + e^-x): for x below about -88, e^-x overflows to infinity and the reciprocal of
-    // infinity is the limit 0
-    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2e));
-}
+// reciprocal (about 1 ulp each; the sigmoid is gdn2_device.h's); these passes are limited by
+// vector ALU issue, not by HBM, once IEEE division and a library log1p are in them.
 __device__ __forceinline__ float log_sigmoid_f(float x) {
     // min(x, 0) - log(1 + e), e = e^-|x| in (0, 1]; log(1 + e) by its series below 2^-7
     // (three terms, error < e^4 / 4), else through the hardware logarithm
@@ -72,7 +67,8 @@ __device__ __forceinline__ void store_n(In* p, const float (&x)[N]) {
 // (and w).  Each walks the run with its four taps per channel and the last three convolution
 // inputs in registers, so every input row is read once, plus three rows before the run; the
 // L2 norms are reductions over a head's lanes (no LDS, no barrier).
-template <typename In, int DK, int DV>
+// GATES false: q, k and v only (the gates are activated inside the recurrence kernel).
+template <typename In, int DK, int DV, bool GATES>
 __global__ __launch_bounds__(192) void prep_kernel(
     const In* __restrict__ xq, const In* __restrict__ xk, const In* __restrict__ xv,
     const In* __restrict__ xb, const In* __restrict__ xw, const In* __restrict__ xa,
@@ -125,7 +121,7 @@ __global__ __launch_bounds__(192) void prep_kernel(
         for (int d = 0; d < G4; ++d) {
             const int64_t off = off0 + (int64_t)min(i0 + d, nt - 1) * st;
             rs[d] = load_vec<In, CH>(x + off);
-            grs[d] = load_vec<In, CH>(gx + off);
+            if constexpr (GATES) grs[d] = load_vec<In, CH>(gx + off);
         }
 #pragma unroll
         for (int d = 0; d < G4; ++d) {
@@ -145,12 +141,14 @@ __global__ __launch_bounds__(192) void prep_kernel(
             ss += u[e] * u[e];
         }
         float gv[CH];
-        if (role == 1) {
+        if constexpr (GATES) {
+            if (role == 1) {
 #pragma unroll
-            for (int e = 0; e < CH; ++e) gv[e] = log_sigmoid_f(to_f32(gr.v[e]));
-        } else {
+                for (int e = 0; e < CH; ++e) gv[e] = log_sigmoid_f(to_f32(gr.v[e]));
+            } else {
 #pragma unroll
-            for (int e = 0; e < CH; ++e) gv[e] = sigmoid_f(to_f32(gr.v[e]));
+                for (int e = 0; e < CH; ++e) gv[e] = sigmoid_f(to_f32(gr.v[e]));
+            }
         }
         if (role < 2) {  // q, k: L2 normalisation over the head
             ss = group_sum<LPH>(ss);
@@ -160,8 +158,10 @@ __global__ __launch_bounds__(192) void prep_kernel(
         }
         if (live) {
             store_n<In, CH>(dst + off, u);
-            if (role == 1) store_n<float, CH>(log_alpha + off, gv);
-            else store_n<In, CH>(gdst + off, gv);
+            if constexpr (GATES) {
+                if (role == 1) store_n<float, CH>(log_alpha + off, gv);
+                else store_n<In, CH>(gdst + off, gv);
+            }
         }
         }
     }
@@ -200,8 +200,8 @@ hipError_t launch_prep_t(const MixerPrepArgs& a) {
     constexpr int HPW = 64 / (D / 8);  // heads per wave
     const int nrun = (int)((a.T + NTW - 1) / NTW);  // workgroups along the tokens
     const int nhg = (int)((a.H + HPW - 1) / HPW);
-    hipLaunchKernelGGL((prep_kernel<In, D, D>), dim3((unsigned)(a.B * nrun * nhg)), dim3(192), 0,
-                       (hipStream_t)a.stream, (const In*)a.xq, (const In*)a.xk, (const In*)a.xv, (const In*)a.xb,
+    auto kern = a.b ? prep_kernel<In, D, D, true> : prep_kernel<In, D, D, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a.B * nrun * nhg)), dim3(192), 0, (hipStream_t)a.stream, (const In*)a.xq, (const In*)a.xk, (const In*)a.xv, (const In*)a.xb,
                        (const In*)a.xw, (const In*)a.xa, a.conv_q, a.conv_k, a.conv_v, (In*)a.q, (In*)a.k, (In*)a.v,
                        (In*)a.b, (In*)a.w, a.log_alpha, (int)a.T, (int)a.H, nrun, nhg, a.eps);
     return hipGetLastError();

@@ -15,7 +15,8 @@
  *
  * The calls: a chunk-parallel forward over whole sequences (the same page,
  * section "Gated Delta Rule-2", gives the chunk size of 64 used by the fused
- * training kernels), the same forward over packed sequences of different
+ * training kernels), the same forward from gate logits (activations formed in
+ * the kernels), the same forward over packed sequences of different
  * lengths, its backward pass (vector-Jacobian product; the same section: the
  * gates enter the gradient inner products, so the backward is derived with
  * them), a single-token recurrent decode step (the page's opening section:
@@ -108,6 +109,35 @@ gdn2_status_t gdn2_chunk_fwd(const void* q, const void* k, const void* v,
                              int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                              gdn2_dtype_t dtype, gdn2_dtype_t o_dtype, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/*
+ * gdn2_chunk_fwd_logits -- gdn2_chunk_fwd with the gate activations done in
+ * the kernels: it takes the projections' outputs instead of the activated
+ * decay and gates.  The erase and write gates are sigmoids of projections of
+ * the token (page "Why NVIDIA Gated DeltaNet-2 separates erase and write
+ * gates", axbrief.com, section "Gated Delta Rule-2"); the decay takes the
+ * same form (alpha = sigmoid(a), so log alpha = log sigmoid(a)).  Forming the
+ * activation inside the recurrence kernel so that no full-sequence activation
+ * tensor is stored is the "gate-in-kernel" fusion of page "CARVE:
+ * Content-Aware Recurrent with Value Efficiency for Chunk-Parallel Linear
+ * Attention" (gist.science), section 2.3 "Key-Axis Decay and Fusion".
+ *
+ *   a_logit       [B, T, H, dk]  dtype        decay logits: alpha = sigmoid(a)
+ *   b_logit       [B, T, H, dk]  dtype        erase-gate logits: b = sigmoid(.)
+ *   w_logit       [B, T, H, dv]  dtype        write-gate logits: w = sigmoid(.)
+ *
+ * Every other argument, the workspace rule (gdn2_chunk_fwd_workspace_bytes
+ * applies unchanged) and every error are as for gdn2_chunk_fwd.  dtype must be
+ * BF16 (dk = dv = 64 or 128), else GDN2_ERR_UNSUPPORTED.  The activations are
+ * formed in fp32 from the bf16 logits; a logit below about -88 gives a decay
+ * or gate of exactly 0.
+ */
+gdn2_status_t gdn2_chunk_fwd_logits(const void* q, const void* k, const void* v,
+                                    const void* a_logit, const void* b_logit, const void* w_logit,
+                                    const float* initial_state, void* o, float* final_state,
+                                    int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                    gdn2_dtype_t dtype, gdn2_dtype_t o_dtype, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 /*
  * gdn2_chunk_fwd_split_workspace_bytes -- bytes of device workspace that the
@@ -281,6 +311,10 @@ gdn2_status_t gdn2_chunk_bwd_noalloc(const void* q, const void* k, const void* v
  * The sigmoid form of the decay is this library's reading: the pages give the
  * decay no activation.  Built: dtype BF16 or F32 with dk = dv = 64 or 128.  No
  * output may overlap an input or another output.  eps >= 0.
+ * With b, w and log_alpha all NULL only q, k and v are formed (xb, xw and xa
+ * are then not read and may be NULL): the gates are left to
+ * gdn2_chunk_fwd_logits, which activates them inside the recurrence kernels.
+ * Some but not all of b, w, log_alpha NULL returns GDN2_ERR_NULL.
  */
 gdn2_status_t gdn2_mixer_prep(const void* xq, const void* xk, const void* xv, const void* xb,
                               const void* xw, const void* xa, const float* conv_q,

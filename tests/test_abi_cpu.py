@@ -33,7 +33,8 @@ def declared_functions():
 
 def test_header_declares_the_calls():
     names = declared_functions()
-    for name in ("gdn2_chunk_fwd", "gdn2_chunk_fwd_workspace_bytes", "gdn2_chunk_fwd_varlen", "gdn2_chunk_bwd",
+    for name in ("gdn2_chunk_fwd", "gdn2_chunk_fwd_logits", "gdn2_chunk_fwd_workspace_bytes", "gdn2_chunk_fwd_varlen",
+                 "gdn2_chunk_bwd",
                  "gdn2_chunk_bwd_workspace_bytes", "gdn2_decode_step", "gdn2_mixer_prep", "gdn2_mixer_out",
                  "gdn2_status_string", "gdn2_version"):
         assert name in names, name
@@ -90,6 +91,15 @@ def chunk(lib, f, B=1, T=64, H=1, dk=64, dv=64, dtype=BF16, odt=F32, **over):
     return lib.gdn2_chunk_fwd(args["q"], args["k"], args["v"], args["g"], args["b"], args["w"],
                               args["s0"], args["o"], args["sT"], B, T, H, dk, dv, dtype, odt,
                               args.get("ws"), args.get("ws_bytes", 0), None)
+
+
+def chunk_logits(lib, f, B=1, T=64, H=1, dk=64, dv=64, dtype=BF16, odt=F32, **over):
+    args = dict(q=f.p(0), k=f.p(1), v=f.p(2), a=f.p(3), b=f.p(4), w=f.p(5), s0=None, o=f.p(7),
+                sT=None)
+    args.update(over)
+    return lib.gdn2_chunk_fwd_logits(args["q"], args["k"], args["v"], args["a"], args["b"], args["w"],
+                                     args["s0"], args["o"], args["sT"], B, T, H, dk, dv, dtype, odt,
+                                     args.get("ws"), args.get("ws_bytes", 0), None)
 
 
 def decode(lib, f, N=1, H=1, dk=64, dv=64, dtype=BF16, odt=F32, **over):
@@ -336,3 +346,41 @@ def test_bwd_noalloc_validation(lib):
     assert lib.gdn2_chunk_bwd_workspace_bytes(1, 640, 16, 128, 128) > gdn2.SCRATCH_BYTES
     assert lib.gdn2_chunk_bwd_workspace_bytes(1, 576, 16, 128, 128) <= gdn2.SCRATCH_BYTES
     assert bwd_noalloc(lib, f, T=640, H=16, dk=128, dv=128) == ERR_WORKSPACE
+
+
+def test_chunk_logits_validation(lib):
+    """The logits forward validates like gdn2_chunk_fwd, with bf16 inputs only and its decay
+    logits counted in the input dtype (2 bytes an element) for the overlap checks."""
+    f = Fake()
+    for name in ("q", "k", "v", "a", "b", "w", "o"):
+        assert chunk_logits(lib, f, **{name: None}) == ERR_NULL, name
+    assert chunk_logits(lib, f, B=0) == ERR_SHAPE
+    assert chunk_logits(lib, f, T=0) == ERR_SHAPE
+    assert chunk_logits(lib, f, dtype=F32) == ERR_UNSUPPORTED
+    assert chunk_logits(lib, f, dk=128, dv=128, dtype=F32) == ERR_UNSUPPORTED
+    assert chunk_logits(lib, f, dk=96, dv=96) == ERR_UNSUPPORTED
+    assert chunk_logits(lib, f, a=f.p(3, 2)) == ERR_MISALIGNED
+    # decay logits [1,64,1,64] bf16 span 8,192 bytes: o at +4,096 overlaps them; o at +8,192
+    # passes the overlap checks and then fails the workspace check (a short workspace), which
+    # comes after them -- so no call here reaches the HIP runtime
+    assert chunk_logits(lib, f, a=f.p(3), o=f.p(3, 4096)) == ERR_ALIAS
+    assert chunk_logits(lib, f, a=f.p(3), o=f.p(3, 8192), ws=f.p(9), ws_bytes=16) == ERR_WORKSPACE
+
+
+def test_mixer_prep_gate_pointers(lib):
+    """Gates all absent (b, w, log_alpha NULL) is a valid request; some but not all absent is
+    GDN2_ERR_NULL.  Checked on calls that fail validation (a misaligned q, or a NULL), so none
+    reaches the HIP runtime."""
+    f = Fake()
+    P = f.p
+
+    def prep(b, w, g, xb=P(3), xw=P(4), xa=P(5), q=P(9)):
+        return lib.gdn2_mixer_prep(P(0), P(1), P(2), xb, xw, xa, P(6), P(7), P(8), q, P(10), P(11), b, w, g,
+                                   1, 64, 1, 64, 64, ctypes.c_float(1e-6), BF16, None)
+
+    assert prep(P(12), None, P(14)) == ERR_NULL
+    assert prep(None, P(13), None) == ERR_NULL
+    assert prep(P(12), P(13), P(14), xb=None) == ERR_NULL
+    # all gates absent: xb, xw, xa are not needed; a misaligned q is still caught
+    assert prep(None, None, None, xb=None, xw=None, xa=None, q=P(9, 2)) == ERR_MISALIGNED
+    assert prep(None, None, None, q=P(9, 2)) == ERR_MISALIGNED

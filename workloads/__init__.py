@@ -166,6 +166,24 @@ def make_mixer_inputs(wl: Workload, seed: Optional[int] = None, B=None, T=None):
     return out
 
 
+def make_logit_inputs(wl: Workload, seed: Optional[int] = None, B: Optional[int] = None,
+                      T: Optional[int] = None, a_lo: float = 2.0, a_hi: float = 7.0):
+    """Inputs of the forward that activates its gates in the kernel: q, k, v and s0 as
+    make_inputs draws them for the same seed, then from their own stream the decay logits
+    xa ~ U[a_lo, a_hi] per key channel per token (the default puts log sigmoid(xa) in
+    [-0.13, -0.001], the range of the workloads' log alpha; U[-6, -1] gives strong decay) and
+    the gate logits xb [.., dk], xw [.., dv] ~ N(0, 2^2), all three in the workload's dtype."""
+    base = make_inputs(wl, seed=seed, B=B, T=T)
+    seed = (wl.seed if seed is None else seed) + 4_000_037
+    B, T, H = base["q"].shape[0], base["q"].shape[1], wl.H
+    gen = torch.Generator("cpu").manual_seed(seed)
+    dt = wl.dtype
+    xa = _uniform(gen, (B, T, H, wl.dk), a_lo, a_hi).to(dt)
+    xb = (2.0 * torch.randn((B, T, H, wl.dk), generator=gen, dtype=torch.float32)).to(dt)
+    xw = (2.0 * torch.randn((B, T, H, wl.dv), generator=gen, dtype=torch.float32)).to(dt)
+    return dict(q=base["q"], k=base["k"], v=base["v"], xa=xa, xb=xb, xw=xw, s0=base["s0"])
+
+
 def make_decode_pool(wl: Workload, seed: Optional[int] = None, N: Optional[int] = None):
     """Decode workload: initial state [N,H,dk,dv] fp32 ~ N(0, s0_std^2) and a pool
     of ``wl.pool`` token sets (q,k,v,log_alpha,b,w each [P,N,H,d]); step s uses
