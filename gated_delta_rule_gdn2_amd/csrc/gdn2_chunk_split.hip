@@ -19,17 +19,18 @@
 //   * state_kernel: one workgroup of four waves per (sequence, head, 64 value columns); wave w
 //     owns 16 columns of the state for all dk rows, in MFMA accumulators, for the whole
 //     sequence.  Per chunk: R = w.v - BG S and Y = QG S (S as a hi / lo bf16 pair), U = T R,
-//     O = Y + P U, S <- Gamma_C S + KG^T U, all in that wave's registers; the record is staged
-//     into LDS one chunk ahead, the only data the waves share.
+//     O = Y + P U, S <- Gamma_C S + KG^T U (KG^T as a hi / lo pair), all in that wave's
+//     registers; the record goes from global memory straight into LDS (no register staging),
+//     the next chunk's parts loading while this one is computed.
 //
 // The host walks the chunks in batches of about a thousand chunk-heads: the local kernel for a
-// batch, then the state kernel for it, so a batch's records (about 74 KB per chunk-head) are
-// read back while the GPU's last-level cache still holds them.
+// batch, then the state kernel for it, so a batch's records (89 KiB per chunk-head at d = 128)
+// are read back while the GPU's last-level cache still holds them.
 //
 // Record of one chunk-head (D = dk = dv), each part row-major:
-//   QG [64][D] bf16 | BG [64][D] bf16 | KG^T [D][64] bf16 |
+//   QG [64][D] bf16 | BG [64][D] bf16 | KG^T hi, KG^T lo [D][64] bf16 |
 //   T hi, T lo: rows 0-31 x cols 0-31, then rows 32-63 x cols 0-63 (bf16; blocks above the
-//   diagonal blocks are zero) | P hi, P lo: the same | Gamma_C [D] fp32.
+//   diagonal blocks are zero) | P hi, P lo: the same | Gamma_C [D] fp32 | padding to a KiB.
 
 #include "gdn2_bf16_ops.h"
 #include "gdn2_launch.h"
@@ -40,18 +41,22 @@ namespace sp {
 using cb::C;
 
 // ------------------------------------------------------------------ record layout ----
+// Two parts, each a whole number of KiB (one 16-byte load per lane of a wave): part A, the
+// operands of X = BG S and Y = QG S; part B, everything after them.
 template <int D>
 struct Rec {
     static constexpr int QG = 0;
     static constexpr int BG = QG + C * D * 2;
-    static constexpr int KGT = BG + C * D * 2;
+    static constexpr int A_BYTES = BG + C * D * 2;
+    static constexpr int KGT = A_BYTES;            // KG^T hi plane
+    static constexpr int KGL = KGT + D * C * 2;    // KG^T lo plane
     static constexpr int TRI = 32 * 32 + 32 * 64;  // elements of one plane of T or P
-    static constexpr int T = KGT + D * C * 2;      // hi plane, then lo plane
+    static constexpr int T = KGL + D * C * 2;      // hi plane, then lo plane
     static constexpr int P = T + 2 * TRI * 2;
     static constexpr int GC = P + 2 * TRI * 2;
-    // padded to whole rounds of the state kernel's staging (256 threads x 16 bytes)
-    static constexpr int BYTES = (GC + D * 4 + 4095) / 4096 * 4096;
-    static constexpr int UNITS = BYTES / 16;
+    static constexpr int B_BYTES = (GC + D * 4 - A_BYTES + 1023) / 1024 * 1024;
+    static constexpr int BYTES = A_BYTES + B_BYTES;
+    static_assert(A_BYTES % 1024 == 0, "part A in whole KiB");
 };
 
 // element (row, col) of a triangle plane: rows 0-31 hold cols 0-31, rows 32-63 cols 0-63
@@ -354,10 +359,13 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
                     }
                 }
             }
-            // KG^T [DK][64]: this lane's 4 tokens of each of its channels
+            // KG^T [DK][64] as hi and lo planes: this lane's 4 tokens of each of its channels
 #pragma unroll
-            for (int c = 0; c < CPL; ++c)
-                cb::store_bf16<4>(reinterpret_cast<bf16*>(rec + R::KGT + ((c0 + c) * C + I * 16 + ts * 4) * 2), kgt[c]);
+            for (int c = 0; c < CPL; ++c) {
+                const int e = ((c0 + c) * C + I * 16 + ts * 4) * 2;
+                cb::store_bf16_split<4>(reinterpret_cast<bf16*>(rec + R::KGT + e),
+                                        reinterpret_cast<bf16*>(rec + R::KGL + e), kgt[c]);
+            }
         }
         cb::lds_barrier();
 
@@ -544,49 +552,78 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
 constexpr int NT_STATE = 256;
 
 // XOR swizzle of 16-byte units inside a row of rb bytes (rb a power of two, 64..256), so that
-// the 16 rows a fragment load touches fall on distinct LDS banks.
+// the 16 rows a fragment load touches fall on distinct LDS banks.  An involution: the same call
+// maps a staged unit back to its record unit.
 __device__ __forceinline__ int swz_unit(int row, int unit, int rb) {
     return unit ^ ((row * rb / 256) % (rb / 16));
 }
 
+// LDS of the state kernel: part A of one record (single: its next copy is loaded once every wave
+// is past X and Y), then two buffers for part B (the next chunk's copy loads during this chunk).
 template <int D>
 struct StateCfg {
     using R = Rec<D>;
-    static constexpr int BUF = R::BYTES;             // one staged record
-    static constexpr int BYTES = 2 * BUF;
+    static constexpr int A = 0;
+    static constexpr int B0 = R::A_BYTES;
+    static constexpr int BYTES = R::A_BYTES + 2 * R::B_BYTES;
     static_assert(BYTES <= 163840, "LDS budget exceeded");
-    static constexpr int UPT = (R::UNITS + NT_STATE - 1) / NT_STATE;  // 16-byte units per thread
 };
 
-// LDS byte offset of 16-byte unit ub + t of a record (same parts and order as the record, each
-// part swizzled by rows); ub is a multiple of 256, so the part is known from ub alone.
+// Record unit staged at LDS unit u of part A (QG then BG, rows of 2 D bytes, each swizzled).
 template <int D>
-__device__ __forceinline__ int stage_offset(int ub, int t) {
+__device__ __forceinline__ int src_unit_a(int u) {
+    constexpr int UPR = D * 2 / 16;  // units per row
+    const int row = u / UPR, un = u % UPR;
+    return row * UPR + swz_unit(row, un, D * 2);
+}
+// The same for part B: KG^T hi and lo (rows of 64 tokens, 128 bytes), the four triangle planes
+// (rows 0-31 of 64 bytes, rows 32-63 of 128 bytes), then Gamma_C and padding as they are.
+template <int D>
+__device__ __forceinline__ int src_unit_b(int u) {
     using R = Rec<D>;
-    constexpr int UQ = C * D * 2 / 16;  // units of QG (= of BG, of KG^T); a multiple of 256
-    constexpr int RBQ = D * 2;          // row bytes of QG, BG
-    const int u = ub + t;
-    if (ub < 2 * UQ) {
-        const int part = u / UQ, v = u % UQ;
-        const int row = v / (RBQ / 16), un = v % (RBQ / 16);
-        return part * UQ * 16 + row * RBQ + swz_unit(row, un, RBQ) * 16;
+    constexpr int UK = 2 * D * C * 2 / 16;      // units of the two KG^T planes
+    constexpr int UT = 4 * R::TRI * 2 / 16;     // units of the four triangle planes
+    if (u < UK) {
+        const int row = u / 8, un = u % 8;
+        return row * 8 + swz_unit(row, un, 128);
     }
-    if (ub < 3 * UQ) {
-        const int v = u - 2 * UQ;       // KG^T rows of 64 tokens = 128 bytes
-        const int row = v / 8, un = v % 8;
-        return R::KGT + row * 128 + swz_unit(row, un, 128) * 16;
-    }
-    if (ub < R::GC / 16) {
-        const int v = u - R::T / 16;    // T and P planes: 4 planes of TRI elements
-        const int plane = v / (R::TRI * 2 / 16), w = v % (R::TRI * 2 / 16);
-        // rows 0-31: 64-byte rows (units 0-127); rows 32-63: 128-byte rows
+    if (u < UK + UT) {
+        const int v = u - UK;
+        constexpr int UP = R::TRI * 2 / 16;     // units of one plane: 128 (rows 0-31) + 256
+        const int plane = v / UP, w = v % UP;
         const bool top = w < 128;
         const int row = top ? w / 4 : (w - 128) / 8, un = top ? w % 4 : (w - 128) % 8;
-        const int off = top ? row * 64 + swz_unit(row, un, 64) * 16 : 2048 + row * 128 + swz_unit(row, un, 128) * 16;
-        return R::T + plane * R::TRI * 2 + off;
+        const int sw = top ? row * 4 + swz_unit(row, un, 64) : 128 + row * 8 + swz_unit(row, un, 128);
+        return UK + plane * UP + sw;
     }
-    return u * 16;                      // Gamma_C and the padding
+    return u;
 }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One part of a record straight from global memory into LDS: load jj of the part (1 KiB) goes
+// to LDS bytes [1024 jj, 1024 jj + 1024) of the part, lane l writing 16 bytes at 16 l; wave w
+// takes loads jj = w, w + 4, ...  The lane's source byte offsets (the same for every record)
+// come precomputed in off[].  Complete once the issuing wave's vmcnt has drained.
+template <int NLOADS>
+struct StageOffsets {
+    static constexpr int PER_WAVE = (NLOADS + 3) / 4;
+    int off[PER_WAVE];
+    template <typename Src>
+    __device__ __forceinline__ void init(int wave, int lane, Src src) {
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; ++j) off[j] = src(min(j * 4 + wave, NLOADS - 1) * 64 + lane) * 16;
+    }
+    __device__ __forceinline__ void issue(const char* rec_part, char* lds_part, int wave) const {
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; ++j) {
+            const int jj = j * 4 + wave;
+            if (jj < NLOADS)
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(rec_part + off[j]),
+                                                 (lds_void*)(lds_part + jj * 1024), 16, 0, 0);
+        }
+    }
+};
 
 // A-operand fragment (permuted slot map) of rows 16 rt + m, columns 32 kk .. 32 kk + 31 of a
 // staged row-major part with rb-byte rows: lane (m, g) takes columns 32 kk + 4 g + e and
@@ -609,6 +646,12 @@ __device__ __forceinline__ Frag<bf16> frag_tri(const char* plane, int row, int k
 // hi / lo K = 32 operands of an accumulator pair (permuted slot map)
 __device__ __forceinline__ cb::Split32 split_pair(const f32x4& a, const f32x4& b) { return cb::split32(a, b); }
 
+// Four waves per (sequence, head, 64 value columns); wave w owns 16 columns of the state for all
+// D rows, in MFMA accumulators, for the whole run of chunks.  Per chunk, two LDS-only barriers:
+//   start: part B of the next record starts loading into the other B buffer;
+//   X = BG S, Y = QG S (S as hi / lo), then barrier M: part A is free, the next one starts loading;
+//   R = w.v - X, U = T R, S <- Gamma_C S + KG^T U (KG^T as hi / lo), O = Y + P U;
+//   the wave's own loads drain, barrier F publishes both parts; O is stored after F.
 template <typename OutT, int D, typename Gt>
 __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
     const char* __restrict__ recs, const bf16* __restrict__ v, const bf16* __restrict__ wgate,
@@ -618,7 +661,8 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
     using R = Rec<D>;
     constexpr int KT = D / 16;           // 16-row key tiles of the state
     constexpr int KK = KT / 2;           // 32-row steps over the keys
-    __shared__ __attribute__((aligned(16))) char smem[Cf::BYTES];
+    constexpr int NLA = R::A_BYTES / 1024, NLB = R::B_BYTES / 1024;
+    __shared__ __attribute__((aligned(1024))) char smem[Cf::BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
@@ -642,6 +686,14 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
     const int col = slice * 64 + wave * 16 + l16;   // this lane's state / value column
     const int64_t tok_stride_v = (int64_t)H * D;
     const char* rec0 = recs + (int64_t)bh * nb * R::BYTES;
+    StageOffsets<NLA> soa;
+    StageOffsets<NLB> sob;
+    soa.init(wave, lane, [](int u) { return src_unit_a<D>(u); });
+    sob.init(wave, lane, [](int u) { return src_unit_b<D>(u); });
+    auto stage_a = [&](int i) { soa.issue(rec0 + (int64_t)i * R::BYTES, smem + Cf::A, wave); };
+    auto stage_b = [&](int i) {
+        sob.issue(rec0 + (int64_t)i * R::BYTES + R::A_BYTES, smem + Cf::B0 + (i & 1) * R::B_BYTES, wave);
+    };
 
     // the state's 16 columns of this wave, all D rows: tile st, lane (n, g) holds S[16 st + 4 g + r][col]
     f32x4 S[KT];
@@ -667,131 +719,9 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
                 wv[1][rt][r] = v[e];
             }
     };
-    // record staging: this thread's 16-byte units of record i (batch-relative) into registers
-    typedef int i32x4 __attribute__((ext_vector_type(4)));
-    auto load_rec = [&](int i, i32x4 (&st)[Cf::UPT]) {
-        const i32x4* src = reinterpret_cast<const i32x4*>(rec0 + (int64_t)i * R::BYTES);
-#pragma unroll
-        for (int j = 0; j < Cf::UPT; ++j) st[j] = src[j * NT_STATE + tid];
-    };
-    auto put_rec = [&](int buf, const i32x4 (&st)[Cf::UPT]) {
-#pragma unroll
-        for (int j = 0; j < Cf::UPT; ++j)
-            *reinterpret_cast<i32x4*>(smem + buf * Cf::BUF + stage_offset<D>(j * NT_STATE, tid)) = st[j];
-    };
-
-    i32x4 stg[Cf::UPT];
-    bf16 wv[2][4][4];
-    if (nb > 0) {
-        load_rec(0, stg);
-        load_wv(c_begin, wv);
-        put_rec(0, stg);
-        if (nb > 1) load_rec(1, stg);
-    }
-    __syncthreads();
-
-    for (int i = 0; i < nb; ++i) {
-        const int n = c_begin + i;
+    // O of a chunk, this lane's 16 values, to global memory
+    auto store_o = [&](int n, const f32x4 (&Y)[4]) {
         const int t0 = n * C;
-        const char* rb = smem + (i & 1) * Cf::BUF;
-        const char* th = rb + R::T;
-        const char* tl = rb + R::T + R::TRI * 2;
-        const char* ph = rb + R::P;
-        const char* pl = rb + R::P + R::TRI * 2;
-        // ---- X = BG S and Y = QG S, S as hi / lo bf16 pairs over 32 key rows; the fragments of
-        // each step are loaded one step ahead ----
-        f32x4 X[4], Y[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) { X[rt] = zero4(); Y[rt] = zero4(); }
-        Frag<bf16> fb[2][4], fq[2][4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            fb[0][rt] = frag_perm(rb + R::BG, rt * 16 + l16, 0, g4, D * 2);
-            fq[0][rt] = frag_perm(rb + R::QG, rt * 16 + l16, 0, g4, D * 2);
-        }
-        // the triangle fragments of U = T R and O = Y + P U: (rt, kk) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
-        Frag<bf16> fth[6], ftl[6], fph[6], fpl[6];
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            if (kk + 1 < KK) {
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    fb[(kk + 1) & 1][rt] = frag_perm(rb + R::BG, rt * 16 + l16, kk + 1, g4, D * 2);
-                    fq[(kk + 1) & 1][rt] = frag_perm(rb + R::QG, rt * 16 + l16, kk + 1, g4, D * 2);
-                }
-            } else {
-#pragma unroll
-                for (int p = 0; p < 6; ++p) {
-                    const int rt = p < 2 ? p : 2 + (p - 2) / 2, k2 = p < 2 ? 0 : (p - 2) % 2;
-                    fth[p] = frag_tri(th, rt * 16 + l16, k2, g4);
-                    ftl[p] = frag_tri(tl, rt * 16 + l16, k2, g4);
-                    fph[p] = frag_tri(ph, rt * 16 + l16, k2, g4);
-                    fpl[p] = frag_tri(pl, rt * 16 + l16, k2, g4);
-                }
-            }
-            const cb::Split32 sp = split_pair(S[2 * kk], S[2 * kk + 1]);
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                mma(X[rt], fb[kk & 1][rt], sp.hi);
-                mma(Y[rt], fq[kk & 1][rt], sp.hi);
-                mma(X[rt], fb[kk & 1][rt], sp.lo);
-                mma(Y[rt], fq[kk & 1][rt], sp.lo);
-            }
-        }
-        // ---- R = w.v - X; U = T R through 32-token halves (T is lower triangular) ----
-        f32x4 Rr[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const bool in = t0 + rt * 16 + g4 * 4 + r < Tlen;
-                Rr[rt][r] = (in ? Gt::gate((float)wv[0][rt][r]) * (float)wv[1][rt][r] : 0.f) - X[rt][r];
-            }
-        if (i + 1 < nb) load_wv(n + 1, wv);
-        // the key-row fragments of the state update
-        Frag<bf16> fk[KT][2];
-#pragma unroll
-        for (int st = 0; st < KT; ++st)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) fk[st][kk] = frag_perm(rb + R::KGT, st * 16 + l16, kk, g4, 128);
-        const cb::Split32 r0 = split_pair(Rr[0], Rr[1]), r1 = split_pair(Rr[2], Rr[3]);
-        f32x4 U[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) U[rt] = zero4();
-#pragma unroll
-        for (int p = 0; p < 6; ++p) {
-            const int rt = p < 2 ? p : 2 + (p - 2) / 2, k2 = p < 2 ? 0 : (p - 2) % 2;
-            const cb::Split32& rs = k2 == 0 ? r0 : r1;
-            mma(U[rt], fth[p], rs.hi);
-            mma(U[rt], fth[p], rs.lo);
-            mma(U[rt], ftl[p], rs.hi);
-        }
-        const cb::Split32 u0 = split_pair(U[0], U[1]), u1 = split_pair(U[2], U[3]);
-        // ---- S <- Gamma_C S + KG^T U ----
-        const float* gc = reinterpret_cast<const float*>(rb + R::GC);
-#pragma unroll
-        for (int st = 0; st < KT; ++st) {
-            const f32x4 g = *reinterpret_cast<const f32x4*>(gc + st * 16 + g4 * 4);
-            S[st] *= g;
-        }
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const cb::Split32& us = kk == 0 ? u0 : u1;
-#pragma unroll
-            for (int st = 0; st < KT; ++st) {
-                mma(S[st], fk[st][kk], us.hi);
-                mma(S[st], fk[st][kk], us.lo);
-            }
-        }
-        // ---- O = Y + P U ----
-#pragma unroll
-        for (int p = 0; p < 6; ++p) {
-            const int rt = p < 2 ? p : 2 + (p - 2) / 2, k2 = p < 2 ? 0 : (p - 2) % 2;
-            const cb::Split32& us = k2 == 0 ? u0 : u1;
-            mma(Y[rt], fph[p], us.hi);
-            mma(Y[rt], fph[p], us.lo);
-            mma(Y[rt], fpl[p], us.hi);
-        }
         OutT* ob = o + (tok0 + t0) * tok_stride_v + (int64_t)h * D + col;
         if (t0 + C <= Tlen) {
 #pragma unroll
@@ -806,13 +736,150 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
                     if (t0 + rt * 16 + g4 * 4 + r < Tlen)
                         ob[(int64_t)(rt * 16 + g4 * 4 + r) * tok_stride_v] = from_f32<OutT>(Y[rt][r]);
         }
-        // ---- stage record i + 1 (loaded during this chunk), start loading record i + 2 ----
-        if (i + 1 < nb) {
-            put_rec((i + 1) & 1, stg);
-            if (i + 2 < nb) load_rec(i + 2, stg);
+    };
+
+    bf16 wv[2][4][4];
+    if (nb > 0) {
+        stage_a(0);
+        stage_b(0);
+        load_wv(c_begin, wv);
+    }
+    __syncthreads();  // vmcnt(0): this wave's loads have landed; the barrier publishes every wave's
+
+    const char* ra = smem + Cf::A;
+    f32x4 Y[4];
+    for (int i = 0; i < nb; ++i) {
+        const int n = c_begin + i;
+        const int t0 = n * C;
+        const char* rb = smem + Cf::B0 + (i & 1) * R::B_BYTES;
+        const char* th = rb + (R::T - R::A_BYTES);
+        const char* tl = th + R::TRI * 2;
+        const char* ph = rb + (R::P - R::A_BYTES);
+        const char* pl = ph + R::TRI * 2;
+        // part B of the next record into the other buffer (last read in the previous chunk)
+        if (i + 1 < nb) stage_b(i + 1);
+        // ---- X = BG S and Y = QG S, S as hi / lo bf16 pairs over 32 key rows; the fragments of
+        // each step are loaded one step ahead ----
+        f32x4 X[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) { X[rt] = zero4(); Y[rt] = zero4(); }
+        Frag<bf16> fb[2][4], fq[2][4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            fb[0][rt] = frag_perm(ra + R::BG, rt * 16 + l16, 0, g4, D * 2);
+            fq[0][rt] = frag_perm(ra + R::QG, rt * 16 + l16, 0, g4, D * 2);
         }
-        // LDS-only barrier: the loads of record i + 2 and of the next w and v stay in flight
+        // the triangle fragments of U = T R: (rt, kk) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+        Frag<bf16> fth[6], ftl[6];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            if (kk + 1 < KK) {
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    fb[(kk + 1) & 1][rt] = frag_perm(ra + R::BG, rt * 16 + l16, kk + 1, g4, D * 2);
+                    fq[(kk + 1) & 1][rt] = frag_perm(ra + R::QG, rt * 16 + l16, kk + 1, g4, D * 2);
+                }
+            } else {
+#pragma unroll
+                for (int p = 0; p < 6; ++p) {
+                    const int rt = p < 2 ? p : 2 + (p - 2) / 2, k2 = p < 2 ? 0 : (p - 2) % 2;
+                    fth[p] = frag_tri(th, rt * 16 + l16, k2, g4);
+                    ftl[p] = frag_tri(tl, rt * 16 + l16, k2, g4);
+                }
+            }
+            // the hi products of the step for every tile, then the lo ones: an accumulator's next
+            // product issues eight MFMAs after its last, past the dependent-issue latency
+            const cb::Split32 sp = split_pair(S[2 * kk], S[2 * kk + 1]);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                mma(X[rt], fb[kk & 1][rt], sp.hi);
+                mma(Y[rt], fq[kk & 1][rt], sp.hi);
+            }
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                mma(X[rt], fb[kk & 1][rt], sp.lo);
+                mma(Y[rt], fq[kk & 1][rt], sp.lo);
+            }
+        }
+        // barrier M: every wave is past part A; the next part A loads during the rest of the chunk
         cb::lds_barrier();
+        if (i + 1 < nb) stage_a(i + 1);
+        // ---- R = w.v - X; U = T R through 32-token halves (T is lower triangular) ----
+        f32x4 Rr[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool in = t0 + rt * 16 + g4 * 4 + r < Tlen;
+                Rr[rt][r] = (in ? Gt::gate((float)wv[0][rt][r]) * (float)wv[1][rt][r] : 0.f) - X[rt][r];
+            }
+        if (i + 1 < nb) load_wv(n + 1, wv);
+        const cb::Split32 r0 = split_pair(Rr[0], Rr[1]), r1 = split_pair(Rr[2], Rr[3]);
+        f32x4 U[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) U[rt] = zero4();
+        // the three hi / lo terms of each block, term by term over the blocks in the order
+        // (0,0) (1,0) (2,0) (3,0) (2,1) (3,1), so that consecutive MFMAs update different tiles
+        constexpr int kOrd[6] = {0, 1, 2, 4, 3, 5};  // block index p in that order
+#pragma unroll
+        for (int term = 0; term < 3; ++term)
+#pragma unroll
+            for (int q6 = 0; q6 < 6; ++q6) {
+                const int p = kOrd[q6];
+                const int rt = p < 2 ? p : 2 + (p - 2) / 2, k2 = p < 2 ? 0 : (p - 2) % 2;
+                const cb::Split32& rs = k2 == 0 ? r0 : r1;
+                if (term == 0) mma(U[rt], fth[p], rs.hi);
+                else if (term == 1) mma(U[rt], fth[p], rs.lo);
+                else mma(U[rt], ftl[p], rs.hi);
+            }
+        const cb::Split32 u0 = split_pair(U[0], U[1]), u1 = split_pair(U[2], U[3]);
+        // ---- S <- Gamma_C S + KG^T U, KG^T as hi / lo: per 32-token half, the key-row fragments
+        // of every tile, then each hi / lo term over all tiles (independent accumulators) ----
+        const float* gc = reinterpret_cast<const float*>(rb + (R::GC - R::A_BYTES));
+        const char* kh = rb + (R::KGT - R::A_BYTES);
+        const char* kl = rb + (R::KGL - R::A_BYTES);
+#pragma unroll
+        for (int st = 0; st < KT; ++st) S[st] *= *reinterpret_cast<const f32x4*>(gc + st * 16 + g4 * 4);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const cb::Split32& us = kk == 0 ? u0 : u1;
+            Frag<bf16> fkh[KT], fkl[KT];
+#pragma unroll
+            for (int st = 0; st < KT; ++st) {
+                fkh[st] = frag_perm(kh, st * 16 + l16, kk, g4, 128);
+                fkl[st] = frag_perm(kl, st * 16 + l16, kk, g4, 128);
+            }
+#pragma unroll
+            for (int st = 0; st < KT; ++st) mma(S[st], fkh[st], us.hi);
+#pragma unroll
+            for (int st = 0; st < KT; ++st) mma(S[st], fkh[st], us.lo);
+#pragma unroll
+            for (int st = 0; st < KT; ++st) mma(S[st], fkl[st], us.hi);
+        }
+        // ---- O = Y + P U, term by term over the blocks as for U ----
+        Frag<bf16> fph[6], fpl[6];
+#pragma unroll
+        for (int p = 0; p < 6; ++p) {
+            const int rt = p < 2 ? p : 2 + (p - 2) / 2, k2 = p < 2 ? 0 : (p - 2) % 2;
+            fph[p] = frag_tri(ph, rt * 16 + l16, k2, g4);
+            fpl[p] = frag_tri(pl, rt * 16 + l16, k2, g4);
+        }
+#pragma unroll
+        for (int term = 0; term < 3; ++term)
+#pragma unroll
+            for (int q6 = 0; q6 < 6; ++q6) {
+                const int p = kOrd[q6];
+                const int rt = p < 2 ? p : 2 + (p - 2) / 2, k2 = p < 2 ? 0 : (p - 2) % 2;
+                const cb::Split32& us = k2 == 0 ? u0 : u1;
+                if (term == 0) mma(Y[rt], fph[p], us.hi);
+                else if (term == 1) mma(Y[rt], fph[p], us.lo);
+                else mma(Y[rt], fpl[p], us.hi);
+            }
+        // barrier F: this wave's loads (the next parts A and B, the next w and v, the previous
+        // chunk's O stores) have drained; the barrier publishes every wave's parts and frees part
+        // B of this chunk.  Then O, whose stores overlap the next chunk.
+        __syncthreads();
+        store_o(n, Y);
     }
 
     if (state_out) {

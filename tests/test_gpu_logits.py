@@ -97,15 +97,11 @@ def test_logits_training_shape_whole(fused):
     assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
 
 
-# The two-kernel form carries KG = k.Gamma' into the state update as a single bf16 operand; on
-# this distribution (SiLU values with a non-zero mean under weak decay, so the state grows) its
-# rounding alone puts S_T at the bar: an fp64 emulation of the kernel's roundings gives S_T
-# 2.96e-2, and 8.9e-3 with KG exact.  Expected to fail until KG enters as a hi / lo pair.
-SPLIT_KG_LIMIT = pytest.mark.xfail(reason="S_T at the bar: KG^T single bf16 in the two-kernel state update",
-                                   strict=False)
-
-
-@pytest.mark.parametrize("fused", [pytest.param(False, marks=SPLIT_KG_LIMIT), True])
+# SiLU values with a non-zero mean under weak decay make the state grow; with KG^T a single bf16
+# operand in the state update (as the fused kernel still has it) an fp64 emulation of the
+# kernel's roundings puts S_T at 2.96e-2 here, 8.9e-3 with KG^T as a hi / lo pair (the
+# two-kernel form).
+@pytest.mark.parametrize("fused", [False, True])
 def test_layer_from_logits_matches_oracle(fused):
     """The layer's recurrence half with the gates left to the kernels: mixer_prep forming q, k, v
     only, then the forward from logits, against the oracle mixer and forward; the gate-less prep
