@@ -127,8 +127,11 @@ def spin_up(fn, torch, seconds=0.3):
     torch.cuda.synchronize()
 
 
+SPIN_UP = True  # --no-spin-up clears it (counter runs, where every dispatch is collected)
+
+
 def time_launches(fn, steps, warmup, torch, spin=True):
-    if spin:
+    if spin and SPIN_UP:
         spin_up(fn, torch)
     for _ in range(warmup):
         fn()
@@ -476,6 +479,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-spin-up", action="store_true",
+                    help="skip the untimed clock spin-up before each timing (counter runs: fewer dispatches)")
     ap.add_argument("--out-bf16", action="store_true", help="write o in bf16 instead of fp32")
     ap.add_argument("--only", choices=("chunk", "decode", "prefill", "bwd", "mixer", "long", "sweep", "logits"),
                     default=None, help="time one workload only (profiler runs); prints its figures")
@@ -483,6 +488,8 @@ def main():
                     help="run only a plain device-to-device copy of MIB MiB (--steps times): "
                          "the reference point that scales the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
+    global SPIN_UP
+    SPIN_UP = not args.no_spin_up
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the GDN-2 recurrence shards over independent "
               "(sequence, head) pairs with no exchange, so more GPUs only replicate this "

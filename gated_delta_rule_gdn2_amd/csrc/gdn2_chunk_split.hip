@@ -20,17 +20,18 @@
 //     owns 16 columns of the state for all dk rows, in MFMA accumulators, for the whole
 //     sequence.  Per chunk: R = w.v - BG S and Y = QG S (S as a hi / lo bf16 pair), U = T R,
 //     O = Y + P U, S <- Gamma_C S + KG^T U (KG^T as a hi / lo pair), all in that wave's
-//     registers; the record goes from global memory straight into LDS (no register staging),
-//     the next chunk's parts loading while this one is computed.
+//     registers; the record, w and v go from global memory straight into LDS (no register
+//     staging), the next chunk's parts loading while this one is computed.
 //
 // The host walks the chunks in batches of about a thousand chunk-heads: the local kernel for a
-// batch, then the state kernel for it, so a batch's records (89 KiB per chunk-head at d = 128)
+// batch, then the state kernel for it, so a batch's records (83 KiB per chunk-head at d = 128)
 // are read back while the GPU's last-level cache still holds them.
 //
-// Record of one chunk-head (D = dk = dv), each part row-major:
+// Record of one chunk-head (D = dk = dv), each part row-major, the columns of every row in the
+// order rec_col gives (groups of four interleaved within blocks of 32):
 //   QG [64][D] bf16 | BG [64][D] bf16 | KG^T hi, KG^T lo [D][64] bf16 |
-//   T hi, T lo: rows 0-31 x cols 0-31, then rows 32-63 x cols 0-63 (bf16; blocks above the
-//   diagonal blocks are zero) | P hi, P lo: the same | Gamma_C [D] fp32 | padding to a KiB.
+//   T: rows 0-31 x cols 0-31, then rows 32-63 x cols 0-63 (bf16; blocks above the diagonal
+//   blocks are zero) | P hi, P lo: the same | Gamma_C [D] fp32 | padding to a KiB.
 
 #include "gdn2_bf16_ops.h"
 #include "gdn2_launch.h"
@@ -51,17 +52,26 @@ struct Rec {
     static constexpr int KGT = A_BYTES;            // KG^T hi plane
     static constexpr int KGL = KGT + D * C * 2;    // KG^T lo plane
     static constexpr int TRI = 32 * 32 + 32 * 64;  // elements of one plane of T or P
-    static constexpr int T = KGL + D * C * 2;      // hi plane, then lo plane
-    static constexpr int P = T + 2 * TRI * 2;
+    static constexpr int T = KGL + D * C * 2;      // one bf16 plane
+    static constexpr int P = T + TRI * 2;          // hi plane, then lo plane
     static constexpr int GC = P + 2 * TRI * 2;
     static constexpr int B_BYTES = (GC + D * 4 - A_BYTES + 1023) / 1024 * 1024;
     static constexpr int BYTES = A_BYTES + B_BYTES;
     static_assert(A_BYTES % 1024 == 0, "part A in whole KiB");
 };
 
+// Position of column c in a record row: inside each block of 32 columns the groups of four are
+// stored in the order 0, 4, 1, 5, 2, 6, 3, 7, so that columns 4 g .. 4 g + 3 and 16 + 4 g ..
+// 16 + 4 g + 3 -- the eight contraction slots one lane of an MFMA operand takes in the permuted
+// slot map -- are 16 contiguous bytes.  A group of four columns (4-aligned) stays contiguous.
+__device__ __forceinline__ int rec_col(int c) {
+    const int g = (c >> 2) & 7;
+    return (c & ~31) | ((g & 3) << 3) | ((g >> 2) << 2) | (c & 3);
+}
+
 // element (row, col) of a triangle plane: rows 0-31 hold cols 0-31, rows 32-63 cols 0-63
 __device__ __forceinline__ int tri_index(int row, int col) {
-    return row < 32 ? row * 32 + col : 1024 + (row - 32) * 64 + col;
+    return row < 32 ? row * 32 + rec_col(col) : 1024 + (row - 32) * 64 + rec_col(col);
 }
 
 // ------------------------------------------------------------------ local kernel ----
@@ -95,6 +105,14 @@ struct InK {
     Vec<Decay, CPL> g[4];
     Vec<bf16, CPL> q[4], k[4], b[4];
 };
+
+// 4 consecutive values of a row into one bf16 plane of a record (rounded once)
+__device__ __forceinline__ void put4(char* rec_plane, int idx, const float (&x)[4]) {
+    bf16x4 h;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) h[r] = (bf16)x[r];
+    *reinterpret_cast<bf16x4*>(rec_plane + idx * 2) = h;
+}
 
 // 4 consecutive values of a row as hi and lo bf16 planes of a record
 __device__ __forceinline__ void put_split4(char* rec_plane_hi, char* rec_plane_lo, int idx, const float (&x)[4]) {
@@ -275,8 +293,8 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
             }
             float kgt[CPL][4];
             // record rows of this lane's tokens: QG and BG [token][DK]
-            char* rq = rec + R::QG + ((I * 16 + ts * 4) * DK + c0) * 2;
-            char* rb = rec + R::BG + ((I * 16 + ts * 4) * DK + c0) * 2;
+            char* rq = rec + R::QG + ((I * 16 + ts * 4) * DK + rec_col(c0)) * 2;
+            char* rb = rec + R::BG + ((I * 16 + ts * 4) * DK + rec_col(c0)) * 2;
             if (!strong) {
                 const int eb = cb::opq(((I * 16 + ts * 4) * LDK + c0) * 2);
                 float bex[CPL], esa[CPL];
@@ -362,7 +380,7 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
             // KG^T [DK][64] as hi and lo planes: this lane's 4 tokens of each of its channels
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
-                const int e = ((c0 + c) * C + I * 16 + ts * 4) * 2;
+                const int e = ((c0 + c) * C + rec_col(I * 16 + ts * 4)) * 2;
                 cb::store_bf16_split<4>(reinterpret_cast<bf16*>(rec + R::KGT + e),
                                         reinterpret_cast<bf16*>(rec + R::KGL + e), kgt[c]);
             }
@@ -371,7 +389,6 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
 
         // =============== A, P and the diagonal blocks of T = (I + A)^{-1} ===============
         char* th = rec + R::T;
-        char* tl = rec + R::T + R::TRI * 2;
         char* ph = rec + R::P;
         char* pl = rec + R::P + R::TRI * 2;
         auto put_p = [=](int row, int col, const float (&p)[4]) { put_split4(ph, pl, tri_index(row, col), p); };
@@ -404,7 +421,7 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
                 cb::store_tdiag<G>(smem, wave, l16, g4, t);
                 float x[4];
                 cb::acc_to_array(t, x);
-                put_split4(th, tl, tri_index(wave * 16 + l16, wave * 16 + g4 * 4), x);
+                put4(th, tri_index(wave * 16 + l16, wave * 16 + g4 * 4), x);
             } else if (wave == 7) {
 #pragma unroll
                 for (int Ib = 0; Ib < 4; ++Ib) {
@@ -457,7 +474,7 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
                                  Tlen - t0, put_p, [=](int Ib, const f32x4& t) {
                                      float x[4];
                                      cb::acc_to_array(t, x);
-                                     put_split4(th, tl, tri_index(Ib * 16 + l16, Ib * 16 + g4 * 4), x);
+                                     put4(th, tri_index(Ib * 16 + l16, Ib * 16 + g4 * 4), x);
                                  });
             load_first(nnext, in);
         }
@@ -480,13 +497,8 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
                 if (wave == 0) {
                     // record: T[16 + 4 g + r][n]
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        bf16 a, b;
-                        cb::split_bf16(t[r], a, b);
-                        const int idx = tri_index(16 + 4 * g4 + r, l16);
-                        *reinterpret_cast<bf16*>(th + idx * 2) = a;
-                        *reinterpret_cast<bf16*>(tl + idx * 2) = b;
-                    }
+                    for (int r = 0; r < 4; ++r)
+                        *reinterpret_cast<bf16*>(th + tri_index(16 + 4 * g4 + r, l16) * 2) = (bf16)t[r];
                 }
             }
             if (Rb == 3) {  // T_32 = T_33 (-A_32) T_22, lane (i, g): T_32[i][4 g + r]
@@ -501,7 +513,7 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
                 if (wave == 3) {
                     float x[4];
                     cb::acc_to_array(t, x);
-                    put_split4(th, tl, tri_index(48 + l16, 32 + g4 * 4), x);
+                    put4(th, tri_index(48 + l16, 32 + g4 * 4), x);
                 }
             }
             Frag16<bf16> tf[2], a2[2], a3[2];
@@ -532,7 +544,7 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
             }
             float x[4];
             cb::acc_to_array(t, x);
-            put_split4(th, tl, tri_index(Rb * 16 + l16, J * 16 + g4 * 4), x);
+            put4(th, tri_index(Rb * 16 + l16, J * 16 + g4 * 4), x);
         } else {
             // waves 4-7: the zero blocks (0,1) and (2,3) of T and P
             const int w4 = wave - 4;                   // 0..3
@@ -540,7 +552,7 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
             const float z[4] = {0.f, 0.f, 0.f, 0.f};
             const int row = blkrow * 16 + l16, col = (blkrow + 1) * 16 + g4 * 4;
             if (w4 & 1) put_split4(ph, pl, tri_index(row, col), z);
-            else put_split4(th, tl, tri_index(row, col), z);
+            else put4(th, tri_index(row, col), z);
         }
         // the next chunk's keys and gates
         load_second(nnext, in);
@@ -558,14 +570,18 @@ __device__ __forceinline__ int swz_unit(int row, int unit, int rb) {
     return unit ^ ((row * rb / 256) % (rb / 16));
 }
 
-// LDS of the state kernel: part A of one record (single: its next copy is loaded once every wave
-// is past X and Y), then two buffers for part B (the next chunk's copy loads during this chunk).
+// LDS of the state kernel.  Region A (single: its next contents load once every wave is past X,
+// Y and R): part A of the record (QG, BG), then w and v of the workgroup's 64 value columns
+// ([64 tokens][64 columns] bf16 each).  Then two buffers for part B of the record (the next
+// chunk's copy loads during this chunk).
 template <int D>
 struct StateCfg {
     using R = Rec<D>;
     static constexpr int A = 0;
-    static constexpr int B0 = R::A_BYTES;
-    static constexpr int BYTES = R::A_BYTES + 2 * R::B_BYTES;
+    static constexpr int WV = R::A_BYTES;              // w, then v: 8 KiB each
+    static constexpr int A_BYTES = R::A_BYTES + 2 * C * 64 * 2;
+    static constexpr int B0 = A_BYTES;
+    static constexpr int BYTES = A_BYTES + 2 * R::B_BYTES;
     static_assert(BYTES <= 163840, "LDS budget exceeded");
 };
 
@@ -576,13 +592,14 @@ __device__ __forceinline__ int src_unit_a(int u) {
     const int row = u / UPR, un = u % UPR;
     return row * UPR + swz_unit(row, un, D * 2);
 }
-// The same for part B: KG^T hi and lo (rows of 64 tokens, 128 bytes), the four triangle planes
-// (rows 0-31 of 64 bytes, rows 32-63 of 128 bytes), then Gamma_C and padding as they are.
+// The same for part B: KG^T hi and lo (rows of 64 tokens, 128 bytes), the three triangle planes
+// T, P hi, P lo (rows 0-31 of 64 bytes, rows 32-63 of 128 bytes), then Gamma_C and padding as
+// they are.
 template <int D>
 __device__ __forceinline__ int src_unit_b(int u) {
     using R = Rec<D>;
     constexpr int UK = 2 * D * C * 2 / 16;      // units of the two KG^T planes
-    constexpr int UT = 4 * R::TRI * 2 / 16;     // units of the four triangle planes
+    constexpr int UT = 3 * R::TRI * 2 / 16;     // units of the three triangle planes
     if (u < UK) {
         const int row = u / 8, un = u % 8;
         return row * 8 + swz_unit(row, un, 128);
@@ -598,6 +615,10 @@ __device__ __forceinline__ int src_unit_b(int u) {
     }
     return u;
 }
+// w and v tiles: token t's 64 columns are a 128-byte row; its eight 16-byte units are permuted
+// by XOR with 2 ((t / 4) % 4), so that the four token rows one read of the accumulator layout
+// touches (4 apart, each 32 bytes of one wave's columns) fall on distinct banks.
+__device__ __forceinline__ int wv_unit(int t, int u) { return u ^ (((t >> 2) & 3) << 1); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -625,16 +646,13 @@ struct StageOffsets {
     }
 };
 
-// A-operand fragment (permuted slot map) of rows 16 rt + m, columns 32 kk .. 32 kk + 31 of a
-// staged row-major part with rb-byte rows: lane (m, g) takes columns 32 kk + 4 g + e and
-// 32 kk + 16 + 4 g + e (e = 0..3), the slots where a pair of accumulator tiles keeps its rows.
+// A-operand fragment (permuted slot map) of row `row`, columns 32 kk .. 32 kk + 31 of a staged
+// row-major part with rb-byte rows: lane (m, g) takes columns 32 kk + 4 g + e and 32 kk + 16 +
+// 4 g + e (e = 0..3), the slots where a pair of accumulator tiles keeps its rows -- in the
+// record's column order the 16 bytes of unit 4 kk + g, one LDS read.
 __device__ __forceinline__ Frag<bf16> frag_perm(const char* part, int row, int kk, int g, int rb) {
-    const int c0 = 32 * kk + 4 * g, c1 = c0 + 16;  // first column of each 8-byte half
-    const int u0 = c0 / 8, u1 = c1 / 8;
-    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(part + row * rb + swz_unit(row, u0, rb) * 16 + (c0 % 8) * 2);
-    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(part + row * rb + swz_unit(row, u1, rb) * 16 + (c1 % 8) * 2);
     Frag<bf16> f;
-    f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    f.v = *reinterpret_cast<const bf16x8*>(part + row * rb + swz_unit(row, 4 * kk + g, rb) * 16);
     return f;
 }
 
@@ -649,9 +667,12 @@ __device__ __forceinline__ cb::Split32 split_pair(const f32x4& a, const f32x4& b
 // Four waves per (sequence, head, 64 value columns); wave w owns 16 columns of the state for all
 // D rows, in MFMA accumulators, for the whole run of chunks.  Per chunk, two LDS-only barriers:
 //   start: part B of the next record starts loading into the other B buffer;
-//   X = BG S, Y = QG S (S as hi / lo), then barrier M: part A is free, the next one starts loading;
-//   R = w.v - X, U = T R, S <- Gamma_C S + KG^T U (KG^T as hi / lo), O = Y + P U;
-//   the wave's own loads drain, barrier F publishes both parts; O is stored after F.
+//   X = BG S, Y = QG S (S as hi / lo), R = w.v - X, then barrier M: region A is free and the next
+//   chunk's part A, w and v start loading;
+//   U = T R (R as hi / lo), S <- Gamma_C S + KG^T U (KG^T as hi / lo), O = Y + P U (P as hi / lo);
+//   the wave's own loads drain, barrier F publishes the next chunk's data; O is stored after F.
+// Every global access but the O stores goes straight to LDS, so a wave keeps few vector-memory
+// instructions in flight.
 template <typename OutT, int D, typename Gt>
 __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
     const char* __restrict__ recs, const bf16* __restrict__ v, const bf16* __restrict__ wgate,
@@ -690,7 +711,28 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
     StageOffsets<NLB> sob;
     soa.init(wave, lane, [](int u) { return src_unit_a<D>(u); });
     sob.init(wave, lane, [](int u) { return src_unit_b<D>(u); });
-    auto stage_a = [&](int i) { soa.issue(rec0 + (int64_t)i * R::BYTES, smem + Cf::A, wave); };
+    // w and v of chunk n into region A: 16 loads of 1 KiB (8 tokens x 64 columns of one tensor),
+    // wave w taking loads w, w + 4, w + 8, w + 12; lane l takes token 8 j + l / 8, LDS unit l % 8
+    // of its row (swizzled: the source unit is wv_unit of it).  Tokens past the end of the
+    // sequence read its last token (zeroed in R).
+    const int wv_t = lane >> 3, wv_u = lane & 7;
+    auto stage_wv = [&](int n) {
+        const int t0 = n * C;
+        const int last = min(C, Tlen - t0) - 1;
+        const int64_t chunk = (tok0 + t0) * tok_stride_v + (int64_t)h * D + slice * 64;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int jj = j * 4 + wave, tensor = jj >> 3, part = jj & 7;
+            const int t = part * 8 + wv_t;
+            const bf16* src = (tensor ? v : wgate) + chunk + (int64_t)min(t, last) * tok_stride_v + wv_unit(t, wv_u) * 8;
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                             (lds_void*)(smem + Cf::WV + jj * 1024), 16, 0, 0);
+        }
+    };
+    auto stage_a = [&](int i) {
+        soa.issue(rec0 + (int64_t)i * R::BYTES, smem + Cf::A, wave);
+        stage_wv(c_begin + i);
+    };
     auto stage_b = [&](int i) {
         sob.issue(rec0 + (int64_t)i * R::BYTES + R::A_BYTES, smem + Cf::B0 + (i & 1) * R::B_BYTES, wave);
     };
@@ -704,56 +746,46 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
             S[st][r] = state_in ? state_in[((int64_t)bh * D + st * 16 + g4 * 4 + r) * D + col] : 0.f;
     }
 
-    // w.v of one chunk in accumulator layout: tile rt, lane (n, g) holds token 16 rt + 4 g + r.  Tokens
-    // past the end read the last token and are zeroed when used.
-    auto load_wv = [&](int n, bf16 (&wv)[2][4][4]) {
+    // O of a chunk through a buffer resource: the chunk's first element of this head as a uniform
+    // base, the rows of its tokens as the range (a last partial chunk drops its stores past the
+    // end of the sequence), this lane's column and token group as a 32-bit offset and each (tile,
+    // row) step as a scalar offset -- no per-store vector address arithmetic.  Lane (n, g) of
+    // tile rt holds token 16 rt + 4 g + r.
+    const uint32_t lane_tok = (uint32_t)(g4 * 4 * tok_stride_v + col);  // elements
+    auto store_o = [&](int n, const f32x4 (&Y)[4]) {
         const int t0 = n * C;
-        const int64_t base = (tok0 + t0) * tok_stride_v + (int64_t)h * D + col;
-        const int last = Tlen - 1 - t0;
+        const int ntok = min(C, Tlen - t0);
+        const auto ro = __builtin_amdgcn_make_buffer_rsrc(o + (tok0 + t0) * tok_stride_v + (int64_t)h * D, 0,
+                                                          ntok * (int)tok_stride_v * (int)sizeof(OutT), 0x00020000);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t e = base + (int64_t)min(rt * 16 + g4 * 4 + r, last) * tok_stride_v;
-                wv[0][rt][r] = wgate[e];
-                wv[1][rt][r] = v[e];
+                const int so = (rt * 16 + r) * (int)tok_stride_v * (int)sizeof(OutT);
+                if constexpr (sizeof(OutT) == 4)
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, (float)Y[rt][r]), ro,
+                                                          lane_tok * 4, so, 0);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, from_f32<bf16>(Y[rt][r])), ro,
+                                                          lane_tok * 2, so, 0);
             }
     };
-    // O of a chunk, this lane's 16 values, to global memory
-    auto store_o = [&](int n, const f32x4 (&Y)[4]) {
-        const int t0 = n * C;
-        OutT* ob = o + (tok0 + t0) * tok_stride_v + (int64_t)h * D + col;
-        if (t0 + C <= Tlen) {
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) ob[(int64_t)(rt * 16 + g4 * 4 + r) * tok_stride_v] = from_f32<OutT>(Y[rt][r]);
-        } else {
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (t0 + rt * 16 + g4 * 4 + r < Tlen)
-                        ob[(int64_t)(rt * 16 + g4 * 4 + r) * tok_stride_v] = from_f32<OutT>(Y[rt][r]);
-        }
-    };
 
-    bf16 wv[2][4][4];
     if (nb > 0) {
         stage_a(0);
         stage_b(0);
-        load_wv(c_begin, wv);
     }
     __syncthreads();  // vmcnt(0): this wave's loads have landed; the barrier publishes every wave's
 
     const char* ra = smem + Cf::A;
+    // this lane's column within the w / v rows: unit and byte offset
+    const int wcol = wave * 16 + l16, wu = wcol >> 3, wb = (wcol & 7) * 2;
     f32x4 Y[4];
     for (int i = 0; i < nb; ++i) {
         const int n = c_begin + i;
         const int t0 = n * C;
         const char* rb = smem + Cf::B0 + (i & 1) * R::B_BYTES;
         const char* th = rb + (R::T - R::A_BYTES);
-        const char* tl = th + R::TRI * 2;
         const char* ph = rb + (R::P - R::A_BYTES);
         const char* pl = ph + R::TRI * 2;
         // part B of the next record into the other buffer (last read in the previous chunk)
@@ -770,7 +802,7 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
             fq[0][rt] = frag_perm(ra + R::QG, rt * 16 + l16, 0, g4, D * 2);
         }
         // the triangle fragments of U = T R: (rt, kk) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
-        Frag<bf16> fth[6], ftl[6];
+        Frag<bf16> ft[6];
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             if (kk + 1 < KK) {
@@ -783,12 +815,10 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
 #pragma unroll
                 for (int p = 0; p < 6; ++p) {
                     const int rt = p < 2 ? p : 2 + (p - 2) / 2, k2 = p < 2 ? 0 : (p - 2) % 2;
-                    fth[p] = frag_tri(th, rt * 16 + l16, k2, g4);
-                    ftl[p] = frag_tri(tl, rt * 16 + l16, k2, g4);
+                    ft[p] = frag_tri(th, rt * 16 + l16, k2, g4);
                 }
             }
-            // the hi products of the step for every tile, then the lo ones: an accumulator's next
-            // product issues eight MFMAs after its last, past the dependent-issue latency
+            // the hi products of the step for every tile, then the lo ones
             const cb::Split32 sp = split_pair(S[2 * kk], S[2 * kk + 1]);
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
@@ -801,36 +831,45 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
                 mma(Y[rt], fq[kk & 1][rt], sp.lo);
             }
         }
-        // barrier M: every wave is past part A; the next part A loads during the rest of the chunk
-        cb::lds_barrier();
-        if (i + 1 < nb) stage_a(i + 1);
-        // ---- R = w.v - X; U = T R through 32-token halves (T is lower triangular) ----
+        // ---- R = w.v - X from the staged w and v (tokens past the end of the sequence: zero) ----
         f32x4 Rr[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const bool in = t0 + rt * 16 + g4 * 4 + r < Tlen;
-                Rr[rt][r] = (in ? Gt::gate((float)wv[0][rt][r]) * (float)wv[1][rt][r] : 0.f) - X[rt][r];
+                const int t = rt * 16 + g4 * 4 + r;
+                const int off = t * 128 + wv_unit(t, wu) * 16 + wb;
+                const float wt = (float)*reinterpret_cast<const bf16*>(smem + Cf::WV + off);
+                const float vt = (float)*reinterpret_cast<const bf16*>(smem + Cf::WV + 8192 + off);
+                Rr[rt][r] = Gt::gate(wt) * vt - X[rt][r];
             }
-        if (i + 1 < nb) load_wv(n + 1, wv);
+        if (t0 + C > Tlen) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (t0 + rt * 16 + g4 * 4 + r >= Tlen) Rr[rt][r] = 0.f;
+        }
+        // barrier M: every wave is past region A; the next chunk's part A, w and v load during the
+        // rest of the chunk
+        cb::lds_barrier();
+        if (i + 1 < nb) stage_a(i + 1);
+        // ---- U = T R through 32-token halves (T is lower triangular), R as hi / lo ----
         const cb::Split32 r0 = split_pair(Rr[0], Rr[1]), r1 = split_pair(Rr[2], Rr[3]);
         f32x4 U[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) U[rt] = zero4();
-        // the three hi / lo terms of each block, term by term over the blocks in the order
-        // (0,0) (1,0) (2,0) (3,0) (2,1) (3,1), so that consecutive MFMAs update different tiles
+        // term by term over the blocks in the order (0,0) (1,0) (2,0) (3,0) (2,1) (3,1), so that
+        // consecutive MFMAs update different tiles
         constexpr int kOrd[6] = {0, 1, 2, 4, 3, 5};  // block index p in that order
 #pragma unroll
-        for (int term = 0; term < 3; ++term)
+        for (int term = 0; term < 2; ++term)
 #pragma unroll
             for (int q6 = 0; q6 < 6; ++q6) {
                 const int p = kOrd[q6];
                 const int rt = p < 2 ? p : 2 + (p - 2) / 2, k2 = p < 2 ? 0 : (p - 2) % 2;
                 const cb::Split32& rs = k2 == 0 ? r0 : r1;
-                if (term == 0) mma(U[rt], fth[p], rs.hi);
-                else if (term == 1) mma(U[rt], fth[p], rs.lo);
-                else mma(U[rt], ftl[p], rs.hi);
+                mma(U[rt], ft[p], term == 0 ? rs.hi : rs.lo);
             }
         const cb::Split32 u0 = split_pair(U[0], U[1]), u1 = split_pair(U[2], U[3]);
         // ---- S <- Gamma_C S + KG^T U, KG^T as hi / lo: per 32-token half, the key-row fragments
@@ -875,9 +914,9 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
                 else if (term == 1) mma(Y[rt], fph[p], us.lo);
                 else mma(Y[rt], fpl[p], us.hi);
             }
-        // barrier F: this wave's loads (the next parts A and B, the next w and v, the previous
-        // chunk's O stores) have drained; the barrier publishes every wave's parts and frees part
-        // B of this chunk.  Then O, whose stores overlap the next chunk.
+        // barrier F: this wave's loads (the next chunk's parts A and B, w and v, the previous
+        // chunk's O stores) have drained; the barrier publishes every wave's and frees part B of
+        // this chunk.  Then O, whose stores overlap the next chunk.
         __syncthreads();
         store_o(n, Y);
     }

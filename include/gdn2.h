@@ -142,8 +142,8 @@ gdn2_status_t gdn2_chunk_fwd_logits(const void* q, const void* k, const void* v,
 /*
  * gdn2_chunk_fwd_split_workspace_bytes -- bytes of device workspace that the
  * two-kernel form of gdn2_chunk_fwd needs for these sizes: the chunk records of
- * one batch of about a thousand (sequence, head, chunk) triples, 91,136 bytes
- * each at dk = dv = 128 (58,368 at 64), plus one fp32 state [B, H, dk, dv].
+ * one batch of about a thousand (sequence, head, chunk) triples, 84,992 bytes
+ * each at dk = dv = 128 (52,224 at 64), plus one fp32 state [B, H, dk, dv].
  * The two-kernel form exists for BF16 inputs with dk = dv = 64 or 128; for
  * every other combination (and for sizes out of range) this returns 0.
  */

@@ -204,7 +204,7 @@ def test_status_values_follow_the_boundary_table(lib):
 def split_ws_bytes(B, T, H, d):
     """Records of one batch (about 1024 chunk-heads) plus one fp32 state."""
     part_a = 2 * 64 * d * 2                                   # QG, BG
-    part_b = 2 * d * 64 * 2 + 4 * (32 * 32 + 32 * 64) * 2 + d * 4  # KG^T hi, lo; T, P hi, lo; Gamma_C
+    part_b = 2 * d * 64 * 2 + 3 * (32 * 32 + 32 * 64) * 2 + d * 4  # KG^T hi, lo; T; P hi, lo; Gamma_C
     rec = part_a + (part_b + 1023) // 1024 * 1024
     nc = (T + 63) // 64
     bc = min(max(1024 // (B * H), 1), nc)
@@ -214,8 +214,8 @@ def split_ws_bytes(B, T, H, d):
 def test_fwd_workspace_bytes(lib):
     """bf16 with d = 64 or 128 has the two-kernel form: its workspace is the records of one
     batch of chunks plus a state; fp32 and other sizes take none."""
-    assert split_ws_bytes(1, 64, 1, 128) - 128 * 128 * 4 == 91136
-    assert split_ws_bytes(1, 64, 1, 64) - 64 * 64 * 4 == 58368
+    assert split_ws_bytes(1, 64, 1, 128) - 128 * 128 * 4 == 84992
+    assert split_ws_bytes(1, 64, 1, 64) - 64 * 64 * 4 == 52224
     for (B, T, H, d) in ((1, 1, 1, 64), (8, 4096, 16, 128), (1, 32768, 16, 128), (3, 1000, 5, 64)):
         assert lib.gdn2_chunk_fwd_split_workspace_bytes(B, T, H, d, d, BF16) == split_ws_bytes(B, T, H, d)
         assert lib.gdn2_chunk_fwd_split_workspace_bytes(B, T, H, d, d, F32) == 0
