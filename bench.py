@@ -108,9 +108,9 @@ def recorded_traffic(profile, sources):
     return int(m.group(2))
 
 
-CHUNK_PROFILE = ("chunk_fwd_train_B8_T4096_H16_d128.md", ("gdn2_chunk_bf16.hip", "gdn2_device.h"))
+CHUNK_PROFILE = ("chunk_fwd_train_B8_T4096_H16_d128.md", ("gdn2_chunk_bf16.hip", "gdn2_bf16_ops.h", "gdn2_device.h"))
 DECODE_PROFILE = ("decode_step_N256_H16_d128.md", ("gdn2_decode.hip", "gdn2_device.h"))
-PREFILL_PROFILE = ("prefill_varlen_N64_H16_d128.md", ("gdn2_chunk_bf16.hip", "gdn2_device.h"))
+PREFILL_PROFILE = ("prefill_varlen_N64_H16_d128.md", ("gdn2_chunk_bf16.hip", "gdn2_bf16_ops.h", "gdn2_device.h"))
 
 
 def spin_up(fn, torch, seconds=0.3):
