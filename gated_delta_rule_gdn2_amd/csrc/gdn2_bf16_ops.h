@@ -91,6 +91,41 @@ __device__ __forceinline__ Vec<T, N> gload(const void* base, uint32_t byte_off) 
     return load_vec<T, N>(reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off));
 }
 
+// N elements of T (bf16 or float) as loaded: raw 32-bit words, each element widened to fp32 where
+// it is used.  Inputs loaded for the next chunk are carried across the chunk loop in this form: a
+// bf16 vector carried element by element is unpacked, one register per element, at the bottom of
+// the loop, which makes every wave wait there for all of its loads and stores.
+template <typename T, int N>
+struct Raw {
+    static_assert((N * sizeof(T)) % 4 == 0, "whole 32-bit words");
+    static constexpr int W = N * (int)sizeof(T) / 4;
+    uint32_t u[W];
+    __device__ __forceinline__ float f(int i) const {
+        if constexpr (sizeof(T) == 4) {
+            return __uint_as_float(u[i]);
+        } else {
+            // bf16 -> fp32: the 16 bits become the high half of the fp32 pattern
+            return __uint_as_float((i & 1) ? (u[i >> 1] & 0xffff0000u) : (u[i >> 1] << 16));
+        }
+    }
+};
+
+template <typename T, int N>
+__device__ __forceinline__ Raw<T, N> gload_raw(const void* base, uint32_t byte_off) {
+    constexpr int W = Raw<T, N>::W;
+    const char* p = reinterpret_cast<const char*>(base) + byte_off;
+    Raw<T, N> r;
+    if constexpr (W == 1) {
+        r.u[0] = *reinterpret_cast<const uint32_t*>(__builtin_assume_aligned(p, 4));
+    } else {
+        typedef uint32_t V __attribute__((ext_vector_type(W)));
+        const V x = *reinterpret_cast<const V*>(__builtin_assume_aligned(p, W * 4));
+#pragma unroll
+        for (int i = 0; i < W; ++i) r.u[i] = x[i];
+    }
+    return r;
+}
+
 // Workgroup barrier for data exchanged through LDS only: waits for this wave's LDS accesses,
 // not for its global loads, so the next chunk's loads stay in flight across it (a full
 // __syncthreads() would drain them).  Waves never exchange data through global memory.
@@ -165,23 +200,25 @@ __device__ __forceinline__ void store_tdiag(char* smem, int I, int l16, int g4, 
     bf16* row = reinterpret_cast<bf16*>(smem + G::TR + ((I * 16 + l16) * LC + I * 16 + g4 * 4) * 2);
     store_bf16<4>(row, x);
     if ((I & 1) == 0) {
-        const float z[4] = {0.f, 0.f, 0.f, 0.f};
-        store_bf16<4>(row + 16, z);
+        // zeros made here: a zero pair kept in registers from the top of the kernel is what the
+        // register allocator spills first, and its reload would wait for every load in flight
+        uint32_t z0, z1;
+        asm volatile("v_mov_b32 %0, 0\n\tv_mov_b32 %1, 0" : "=v"(z0), "=v"(z1));
+        *reinterpret_cast<uint2*>(row + 16) = make_uint2(z0, z1);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r)
         *reinterpret_cast<bf16*>(smem + G::TTR + ((I * 16 + g4 * 4 + r) * LC + I * 16 + l16) * 2) = (bf16)x[r];
 }
 
-// G: the LDS layout (RX work rows of G::LDK bf16, AM, TR, TTR of G::LC); PutP: stores a row
-// segment of P, put_p(row, col, p[4]) for P[row][col .. col + 3]; PutT: receives each diagonal
-// block of T in fp32 as well, put_t(I, t) with lane (i, g) of t holding T_II[i][4 g + r].
-template <typename G, int DK, typename Gt, typename PutP, typename PutT>
-__device__ __forceinline__ void strong_ap_body(char* smem, const bf16* __restrict__ q, const bf16* __restrict__ k,
-                                               const bf16* __restrict__ bgate,
-                                               const typename Gt::Decay* __restrict__ decay,
-                                               int64_t chunk_base, int64_t tok_stride_k, int ntok, PutP put_p,
-                                               PutT put_t) {
+// G: the LDS layout (RX work rows of G::LDK bf16, AM, TR, TTR of G::LC); Src: the inputs of
+// this lane's token slot m (token 16 I + 4 ts + m, channels c0 .. c0 + CPL - 1),
+// src(m, decay, q, k, b) fills four float[CPL] arrays -- read from global memory, or handed over
+// from the registers the element phase loaded them into; PutP: stores a row segment of P, put_p(row, col, p[4]) for
+// P[row][col .. col + 3]; PutT: receives each diagonal block of T in fp32 as well, put_t(I, t)
+// with lane (i, g) of t holding T_II[i][4 g + r].
+template <typename G, int DK, typename Gt, typename Src, typename PutP, typename PutT>
+__device__ __forceinline__ void strong_ap_body(char* smem, Src src, int ntok, PutP put_p, PutT put_t) {
     constexpr int CPL = DK / 32, LDK = G::LDK, LC = G::LC;
     bf16* sX = reinterpret_cast<bf16*>(smem + G::RX);
     bf16* sA = reinterpret_cast<bf16*>(smem + G::AM);
@@ -225,10 +262,10 @@ __device__ __forceinline__ void strong_ap_body(char* smem, const bf16* __restric
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         const int i = I * 16 + ts * 4 + m;
-        const Vec<typename Gt::Decay, CPL> g = load_vec<typename Gt::Decay, CPL>(
-            decay + chunk_base + (int64_t)min(i, ntok - 1) * tok_stride_k + c0);
+        float g[CPL], xq[CPL], xk[CPL], xb[CPL];
+        src(m, g, xq, xk, xb);
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) al[c][m] = i < ntok ? Gt::alpha((float)g.v[c]) : 1.f;
+        for (int c = 0; c < CPL; ++c) al[c][m] = i < ntok ? Gt::alpha(g[c]) : 1.f;
     }
 #pragma unroll
     for (int c = 0; c < CPL; ++c) x16[c] = __shfl_xor(al[c][0] * al[c][1] * al[c][2] * al[c][3], 16);
@@ -242,10 +279,8 @@ __device__ __forceinline__ void strong_ap_body(char* smem, const bf16* __restric
         for (int m = 0; m < 4; ++m) {
             const int i = ts * 4 + m;  // token within the block
             const bool valid = I * 16 + i < ntok;
-            const int64_t off = chunk_base + (int64_t)min(I * 16 + i, ntok - 1) * tok_stride_k + c0;
-            const Vec<bf16, CPL> xq = load_vec<bf16, CPL>(q + off);
-            const Vec<bf16, CPL> xk = load_vec<bf16, CPL>(k + off);
-            const Vec<bf16, CPL> xb = load_vec<bf16, CPL>(bgate + off);
+            float xg[CPL], xq[CPL], xk[CPL], xb[CPL];
+            src(m, xg, xq, xk, xb);
             // split point p of the segment of i (last token of its lower half); a token in the
             // upper half is a row with factor Gamma_{i<-p}, one in the lower half a column with
             // factor Gamma_{p<-i}; both are products of at most one lane's decays and x16
@@ -277,9 +312,9 @@ __device__ __forceinline__ void strong_ap_body(char* smem, const bf16* __restric
             float ra[CPL], rp[CPL], cl[CPL];
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
-                const float qv = valid ? (float)xq.v[c] : 0.f;
-                const float kv = valid ? (float)xk.v[c] : 0.f;
-                const float bk = valid ? Gt::gate((float)xb.v[c]) * kv : 0.f;
+                const float qv = valid ? xq[c] : 0.f;
+                const float kv = valid ? xk[c] : 0.f;
+                const float bk = valid ? Gt::gate(xb[c]) * kv : 0.f;
                 if (L == 4) {
                     ra[c] = 0.f; rp[c] = qv; cl[c] = kv;
                 } else {
@@ -329,12 +364,32 @@ __device__ __forceinline__ void strong_ap_body(char* smem, const bf16* __restric
 
 // The same out of line, for a loop whose register allocation the strong path must not raise.
 // (Its LDS and global accesses then go through flat addresses; strong chunks are rare there.)
+// (Its inputs come from global memory, where the element phase's copies are in L2.)
 template <typename G, int DK, typename Gt, typename PutP, typename PutT>
 __device__ __noinline__ void strong_ap(char* smem, const bf16* __restrict__ q, const bf16* __restrict__ k,
                                        const bf16* __restrict__ bgate, const typename Gt::Decay* __restrict__ decay,
                                        int64_t chunk_base, int64_t tok_stride_k, int ntok, PutP put_p,
                                        PutT put_t) {
-    strong_ap_body<G, DK, Gt>(smem, q, k, bgate, decay, chunk_base, tok_stride_k, ntok, put_p, put_t);
+    constexpr int CPL = DK / 32;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, I = wave & 3, hf = wave >> 2, ts = lane >> 4;
+    const int c0 = hf * (DK / 2) + (lane & 15) * CPL;
+    auto src = [=](int m, float (&g)[CPL], float (&xq)[CPL], float (&xk)[CPL], float (&xb)[CPL]) {
+        const int64_t off = chunk_base + (int64_t)min(I * 16 + ts * 4 + m, ntok - 1) * tok_stride_k + c0;
+        const auto vg = load_vec<typename Gt::Decay, CPL>(decay + off);
+        const auto vq = load_vec<bf16, CPL>(q + off);
+        const auto vk = load_vec<bf16, CPL>(k + off);
+        const auto vb = load_vec<bf16, CPL>(bgate + off);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            g[c] = (float)vg.v[c];
+            xq[c] = (float)vq.v[c];
+            xk[c] = (float)vk.v[c];
+            xb[c] = (float)vb.v[c];
+        }
+    };
+    strong_ap_body<G, DK, Gt>(smem, src, ntok, put_p, put_t);
 }
 
 }  // namespace cb

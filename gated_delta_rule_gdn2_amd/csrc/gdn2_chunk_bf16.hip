@@ -88,9 +88,9 @@ struct Cfg {
 // columns of TPV tokens.
 template <int CPL, int TPV, int VC, typename Decay>
 struct In {
-    Vec<Decay, CPL> g[4];
-    Vec<bf16, CPL> q[4], k[4], b[4];
-    Vec<bf16, VC> w[TPV], v[TPV];
+    Raw<Decay, CPL> g[4];
+    Raw<bf16, CPL> q[4], k[4], b[4];
+    Raw<bf16, VC> w[TPV], v[TPV];
 };
 
 template <typename OutT, int DK, int DV, int DVS, typename Gt>
@@ -176,8 +176,10 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
             for (int r = 0; r < 4; ++r) S[i][r] = src[(int64_t)r * DV];
         }
     }
-    const bool state_owner = wave + 8 * (SPW - 1) < KT * NCT;
-    const bool uo_owner = wave + 8 * (UPW - 1) < 4 * NCT;
+    // (true for every wave where the tiles divide evenly; said so at compile time, so that no branch
+    // surrounds the output stores and the compiler can count them as in flight afterwards)
+    const bool state_owner = 8 * SPW == KT * NCT || wave + 8 * (SPW - 1) < KT * NCT;
+    const bool uo_owner = 8 * UPW == 4 * NCT || wave + 8 * (UPW - 1) < 4 * NCT;
 
     const int nchunks = (Tlen + C - 1) / C;
     const int64_t tok_stride_k = (int64_t)H * DK;
@@ -203,8 +205,8 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const uint32_t e = __umul24(min(I * 16 + ts * 4 + m, last), rsk) + c0;
-            in.g[m] = gload<Decay, CPL>(gb, e * (uint32_t)sizeof(Decay));
-            in.q[m] = gload<bf16, CPL>(qb, e * 2);
+            in.g[m] = gload_raw<Decay, CPL>(gb, e * (uint32_t)sizeof(Decay));
+            in.q[m] = gload_raw<bf16, CPL>(qb, e * 2);
         }
     };
     auto load_second = [&](int n, InC& in) {
@@ -215,8 +217,8 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const uint32_t e = __umul24(min(I * 16 + ts * 4 + m, last), rsk) + c0;
-            in.k[m] = gload<bf16, CPL>(kb, e * 2);
-            in.b[m] = gload<bf16, CPL>(bb, e * 2);
+            in.k[m] = gload_raw<bf16, CPL>(kb, e * 2);
+            in.b[m] = gload_raw<bf16, CPL>(bb, e * 2);
         }
         const int64_t cv = seq_base_v + (int64_t)t0 * tok_stride_v + col0;
         const bf16* wb = wgate + cv;
@@ -224,8 +226,8 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < TPV; ++i) {
             const uint32_t e = __umul24(min(vtok + i, last), rsv) + vcol;
-            in.w[i] = gload<bf16, VC>(wb, e * 2);
-            in.v[i] = gload<bf16, VC>(vb, e * 2);
+            in.w[i] = gload_raw<bf16, VC>(wb, e * 2);
+            in.v[i] = gload_raw<bf16, VC>(vb, e * 2);
         }
     };
 
@@ -247,31 +249,13 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
         const int c0 = hf * (DK / 2) + (lane & 15) * CPL;
         const int vcol = (tidv % (DVS / VC)) * VC, vtok = (tidv / (DVS / VC)) * TPV;
         // =============== element phase, pass 1: decays within the block ===============
-        if (t0 + C > Tlen) {
-            // tokens past the end of the sequence act as the identity: no decay, no read, no write
+        // Tokens past the end of the sequence (their loads read the last token) act as the identity:
+        // no decay and k = 0 (which zeroes their A, P-column, BG and KG entries; q, b, w, v may stay:
+        // what they feed reaches only the rows of those tokens, which are never stored).  Applied
+        // where alpha and k are used, so that no register of a load still in flight is written here.
+        bool tok_ok[4];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                if (t0 + I * 16 + ts * 4 + m >= Tlen) {
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c) {
-                        in.g[m].v[c] = Gt::no_decay();
-                        in.q[m].v[c] = (bf16)0.f;
-                        in.k[m].v[c] = (bf16)0.f;
-                        in.b[m].v[c] = (bf16)0.f;
-                    }
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < TPV; ++i) {
-                if (t0 + vtok + i >= Tlen) {
-#pragma unroll
-                    for (int j = 0; j < VC; ++j) {
-                        in.w[i].v[j] = (bf16)0.f;
-                        in.v[i].v[j] = (bf16)0.f;
-                    }
-                }
-            }
-        }
+        for (int m = 0; m < 4; ++m) tok_ok[m] = t0 + I * 16 + ts * 4 + m < Tlen;
         // decay from the block start through token m = ex * lp[m]; after token m to the block
         // end = ls[m] * es (lp, ls: this lane's 4 tokens; ex, es: the block's other token slots)
         float lp[CPL][4], ls[CPL][4], ex[CPL], es[CPL];
@@ -283,7 +267,7 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                 float p = 1.f;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    al[m] = Gt::alpha((float)in.g[m].v[c]);
+                    al[m] = tok_ok[m] ? Gt::alpha(in.g[m].f(c)) : 1.f;
                     p *= al[m];
                     lp[c][m] = p;
                 }
@@ -312,14 +296,24 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                 *reinterpret_cast<V*>(sBLK + I * DK + c0) = x;
             }
         }
+        lds_barrier();
+
+        // =============== element phase, pass 2: scaled operands ===============
+        // the gate and value registers are first read here (kept from being read earlier: the
+        // wait for their loads then falls after the first pass)
+#pragma unroll
+        for (int i = 0; i < TPV; ++i)
+#pragma unroll
+            for (int j = 0; j < Raw<bf16, VC>::W; ++j) asm volatile("" : "+v"(in.w[i].u[j]), "+v"(in.v[i].u[j]));
         // write gate times value, transposed ([column][token]) in fp32 (exact for given gates: a
-        // product of two bf16 numbers)
+        // product of two bf16 numbers).  Here rather than in pass 1: w and v are the later of the
+        // two batches of loads, and pass 1 then waits for the first batch only.
         const int wvb = opq(G::WVT + (vcol * LCF + vtok) * 4);
 #pragma unroll
         for (int j = 0; j < VC; ++j) {
             float x[TPV];
 #pragma unroll
-            for (int i = 0; i < TPV; ++i) x[i] = Gt::gate((float)in.w[i].v[j]) * (float)in.v[i].v[j];
+            for (int i = 0; i < TPV; ++i) x[i] = Gt::gate(in.w[i].f(j)) * in.v[i].f(j);
             if constexpr (TPV == 1) {
                 *F32(wvb + j * LCF * 4) = x[0];
             } else {
@@ -330,9 +324,6 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                 *reinterpret_cast<V*>(F32(wvb + j * LCF * 4)) = y;
             }
         }
-        lds_barrier();
-
-        // =============== element phase, pass 2: scaled operands ===============
         float blk[CPL][4], invgc[CPL];
         int strong;
         {
@@ -388,10 +379,10 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                     float xq[CPL], xb[CPL], xki[CPL];
 #pragma unroll
                     for (int c = 0; c < CPL; ++c) {
-                        const float kv = (float)in.k[m].v[c];
+                        const float kv = tok_ok[m] ? in.k[m].f(c) : 0.f;
                         const float gam = bex[c] * lp[c][m];
-                        xq[c] = (float)in.q[m].v[c] * gam;
-                        xb[c] = Gt::gate((float)in.b[m].v[c]) * kv * gam;
+                        xq[c] = in.q[m].f(c) * gam;
+                        xb[c] = Gt::gate(in.b[m].f(c)) * kv * gam;
                         kgt[c][m] = kv * (ls[c][m] * esa[c]);
                         xki[c] = kgt[c][m] * invgc[c];
                         bgt[c][m] = xb[c];
@@ -417,9 +408,9 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                     float xq[CPL], ya[CPL], yp[CPL], za[CPL], zp[CPL];
 #pragma unroll
                     for (int c = 0; c < CPL; ++c) {
-                        const float qv = (float)in.q[m].v[c];
-                        const float kv = (float)in.k[m].v[c];
-                        const float bk = Gt::gate((float)in.b[m].v[c]) * kv;
+                        const float qv = in.q[m].f(c);
+                        const float kv = tok_ok[m] ? in.k[m].f(c) : 0.f;
+                        const float bk = Gt::gate(in.b[m].f(c)) * kv;
                         const float gam = before[c] * pre[c][m];
                         xq[c] = qv * gam;
                         bgt[c][m] = bk * gam;
@@ -549,12 +540,15 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                 }
             }
         } else {
+            // the next chunk's first loads go out before the call (the strong path reads its
+            // inputs from global memory): issued after it, they would leave the compiler unable to
+            // count the loads in flight at the top of the loop, and it would wait for all of them
+            load_first(nnext, in);
             strong_ap<G, DK, Gt>(smem, q, k, bgate, decay, seq_base_k + (int64_t)t0 * tok_stride_k, tok_stride_k,
                              Tlen - t0, [&](int row, int col, const float (&p)[4]) {
                                  const int idx = row * LC + col;
                                  store_bf16_split<4>(sPh + idx, sPl + idx, p);
                              }, [](int, const f32x4&) {});
-            load_first(nnext, in);
         }
         lds_barrier();
 
@@ -782,7 +776,13 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                 }
             }
             sched_fence();
-            const OutT* ob = o + seq_base_v + (int64_t)t0 * tok_stride_v + col0;
+            // O through a buffer resource over this chunk's tokens of the head: a last partial
+            // chunk's rows past the end of the sequence fall outside its range and are dropped,
+            // so the stores need no branch (a branch around them would make the compiler assume
+            // they may not be in flight, and wait for every load at the top of the next chunk)
+            const int ntok = min(C, Tlen - t0);
+            const auto ro = __builtin_amdgcn_make_buffer_rsrc(
+                o + seq_base_v + (int64_t)t0 * tok_stride_v, 0, ntok * rsv * (int)sizeof(OutT), 0x00020000);
 #pragma unroll
             for (int i = 0; i < UPW; ++i) {
                 const int u = wave + 8 * i, ct = u % NCT, rt = u / NCT;
@@ -793,16 +793,16 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                     mma(Y[i], ul[kk], ph[i][kk]);
                     mma(Y[i], uh[kk], pl[i][kk]);
                 }
-                if (t0 + rt * 16 + l16 < Tlen) {
-                    const uint32_t e = __umul24(rt * 16 + l16, rsv) + ct * 16 + g4 * 4;
-                    OutT* dst = const_cast<OutT*>(ob) + e;
-                    if constexpr (sizeof(OutT) == 4) {
-                        *reinterpret_cast<f32x4*>(dst) = Y[i];
-                    } else {
-                        float x[4];
-                        acc_to_array(Y[i], x);
-                        store_bf16<4>(reinterpret_cast<bf16*>(dst), x);
-                    }
+                const uint32_t e = (__umul24(rt * 16 + l16, rsv) + col0 + ct * 16 + g4 * 4) * sizeof(OutT);
+                if constexpr (sizeof(OutT) == 4) {
+                    typedef uint32_t U4 __attribute__((ext_vector_type(4)));
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(U4, Y[i]), ro, (int)e, 0, 0);
+                } else {
+                    typedef uint32_t U2 __attribute__((ext_vector_type(2)));
+                    bf16x4 y;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) y[r] = (bf16)Y[i][r];
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(U2, y), ro, (int)e, 0, 0);
                 }
             }
         }
@@ -837,9 +837,9 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                 }
             }
         }
-        // No barrier here: the next chunk's first pass writes only the votes, the block decays
-        // and (w.v)^T, which nothing above reads, and the barrier after that pass keeps its
-        // operand tiles behind every wave's reads of U, P and KG^T here.
+        // No barrier here: the next chunk's first pass writes only the votes and the block
+        // decays, which nothing above reads, and the barrier after that pass keeps its operand
+        // tiles behind every wave's reads of U, P and KG^T here.
     }
 
     if (state_owner && final_state) {

@@ -102,8 +102,8 @@ struct LocalCfg {
 
 template <int CPL, typename Decay>
 struct InK {
-    Vec<Decay, CPL> g[4];
-    Vec<bf16, CPL> q[4], k[4], b[4];
+    cb::Raw<Decay, CPL> g[4];
+    cb::Raw<bf16, CPL> q[4], k[4], b[4];
 };
 
 // 4 consecutive values of a row into one bf16 plane of a record (rounded once)
@@ -167,8 +167,8 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const uint32_t e = __umul24(min(I * 16 + ts * 4 + m, last), rsk) + c0;
-            in.g[m] = cb::gload<Decay, CPL>(decay + cbase, e * (uint32_t)sizeof(Decay));
-            in.q[m] = cb::gload<bf16, CPL>(q + cbase, e * 2);
+            in.g[m] = cb::gload_raw<Decay, CPL>(decay + cbase, e * (uint32_t)sizeof(Decay));
+            in.q[m] = cb::gload_raw<bf16, CPL>(q + cbase, e * 2);
         }
     };
     auto load_second = [&](int n, InK<CPL, Decay>& in) {
@@ -179,8 +179,8 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const uint32_t e = __umul24(min(I * 16 + ts * 4 + m, last), rsk) + c0;
-            in.k[m] = cb::gload<bf16, CPL>(k + cbase, e * 2);
-            in.b[m] = cb::gload<bf16, CPL>(bgate + cbase, e * 2);
+            in.k[m] = cb::gload_raw<bf16, CPL>(k + cbase, e * 2);
+            in.b[m] = cb::gload_raw<bf16, CPL>(bgate + cbase, e * 2);
         }
     };
 
@@ -200,21 +200,13 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
         const int l16 = lane & 15, g4 = lane >> 4, ts = lane >> 4;
         const int c0 = hf * (DK / 2) + (lane & 15) * CPL;
         // =============== element phase, pass 1: decays within the block ===============
-        if (t0 + C > Tlen) {
-            // tokens past the end of the sequence act as the identity: no decay, no read, no write
+        // Tokens past the end of the sequence (their loads read the last token) act as the identity:
+        // no decay and k = 0 (which zeroes their A, P-column, BG and KG entries; q, b, w, v may stay:
+        // what they feed reaches only the rows of those tokens, which are never stored).  Applied
+        // where alpha and k are used, so that no register of a load still in flight is written here.
+        bool tok_ok[4];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                if (t0 + I * 16 + ts * 4 + m >= Tlen) {
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c) {
-                        in.g[m].v[c] = Gt::no_decay();
-                        in.q[m].v[c] = (bf16)0.f;
-                        in.k[m].v[c] = (bf16)0.f;
-                        in.b[m].v[c] = (bf16)0.f;
-                    }
-                }
-            }
-        }
+        for (int m = 0; m < 4; ++m) tok_ok[m] = t0 + I * 16 + ts * 4 + m < Tlen;
         float lp[CPL][4], ls[CPL][4], ex[CPL], es[CPL];
         {
             float blkv[CPL];
@@ -224,7 +216,7 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
                 float p = 1.f;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    al[m] = Gt::alpha((float)in.g[m].v[c]);
+                    al[m] = tok_ok[m] ? Gt::alpha(in.g[m].f(c)) : 1.f;
                     p *= al[m];
                     lp[c][m] = p;
                 }
@@ -308,10 +300,10 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
                     float xq[CPL], xb[CPL], xki[CPL];
 #pragma unroll
                     for (int c = 0; c < CPL; ++c) {
-                        const float kv = (float)in.k[m].v[c];
+                        const float kv = tok_ok[m] ? in.k[m].f(c) : 0.f;
                         const float gam = bex[c] * lp[c][m];
-                        xq[c] = (float)in.q[m].v[c] * gam;
-                        xb[c] = Gt::gate((float)in.b[m].v[c]) * kv * gam;
+                        xq[c] = in.q[m].f(c) * gam;
+                        xb[c] = Gt::gate(in.b[m].f(c)) * kv * gam;
                         kgt[c][m] = kv * (ls[c][m] * esa[c]);
                         xki[c] = kgt[c][m] * invgc[c];
                     }
@@ -337,9 +329,9 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
                     float xq[CPL], xb[CPL], ya[CPL], yp[CPL], za[CPL], zp[CPL];
 #pragma unroll
                     for (int c = 0; c < CPL; ++c) {
-                        const float qv = (float)in.q[m].v[c];
-                        const float kv = (float)in.k[m].v[c];
-                        const float bk = Gt::gate((float)in.b[m].v[c]) * kv;
+                        const float qv = in.q[m].f(c);
+                        const float kv = tok_ok[m] ? in.k[m].f(c) : 0.f;
+                        const float bk = Gt::gate(in.b[m].f(c)) * kv;
                         const float gam = before[c] * pre[c][m];
                         xq[c] = qv * gam;
                         xb[c] = bk * gam;
@@ -470,8 +462,18 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
                 }
             }
         } else {
-            cb::strong_ap_body<G, DK, Gt>(smem, q, k, bgate, decay, seq_base_k + (int64_t)t0 * tok_stride_k, tok_stride_k,
-                                 Tlen - t0, put_p, [=](int Ib, const f32x4& t) {
+            // the chunk's inputs, still in the registers the element phase loaded them into (zero,
+            // and no decay, past the end of the sequence)
+            auto src = [&](int m, float (&g)[CPL], float (&xq)[CPL], float (&xk)[CPL], float (&xb)[CPL]) {
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    g[c] = in.g[m].f(c);
+                    xq[c] = in.q[m].f(c);
+                    xk[c] = in.k[m].f(c);
+                    xb[c] = in.b[m].f(c);
+                }
+            };
+            cb::strong_ap_body<G, DK, Gt>(smem, src, Tlen - t0, put_p, [=](int Ib, const f32x4& t) {
                                      float x[4];
                                      cb::acc_to_array(t, x);
                                      put4(th, tri_index(Ib * 16 + l16, Ib * 16 + g4 * 4), x);
