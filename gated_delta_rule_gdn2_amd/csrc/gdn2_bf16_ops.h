@@ -126,6 +126,32 @@ __device__ __forceinline__ Raw<T, N> gload_raw(const void* base, uint32_t byte_o
     return r;
 }
 
+// A buffer resource over `bytes` bytes from `base`: loads past the end read zeros and stores
+// past the end are dropped
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// N elements of T at a byte offset into a buffer resource (zeros past its end)
+template <typename T, int N>
+__device__ __forceinline__ Raw<T, N> bload_raw(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    constexpr int W = Raw<T, N>::W;
+    Raw<T, N> x;
+    if constexpr (W == 1) {
+        x.u[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, 0);
+    } else if constexpr (W == 2) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)byte_off, 0, 0);
+        x.u[0] = v[0];
+        x.u[1] = v[1];
+    } else {
+        static_assert(W == 4, "1, 2 or 4 words");
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x.u[i] = v[i];
+    }
+    return x;
+}
+
 // Workgroup barrier for data exchanged through LDS only: waits for this wave's LDS accesses,
 // not for its global loads, so the next chunk's loads stay in flight across it (a full
 // __syncthreads() would drain them).  Waves never exchange data through global memory.

@@ -53,7 +53,6 @@ struct Cfg {
     static constexpr int SPW = KT * NCT >= 8 ? KT * NCT / 8 : 1;  // 16 x 16 state tiles per wave
     static constexpr int LDK = DK + 8;    // bf16 row stride of [token][channel] tiles
     static constexpr int LC = C + 8;      // bf16 row stride of [*][token] tiles
-    static constexpr int LCF = C + 4;     // fp32 row stride of [column][token] tiles
     static constexpr int VC = C * DVS / NT >= 4 ? 4 : C * DVS / NT;  // value columns per lane
     static constexpr int TPV = C * DVS / (NT * VC);                  // value tokens per lane
     // LDS regions (byte offsets); lifetimes within a chunk in the comments
@@ -62,8 +61,9 @@ struct Cfg {
     static constexpr int BGT_BYTES = (DK > 2 * DVS ? DK : 2 * DVS) * LC * 2;
     static constexpr int BGT = KGT + DK * LC * 2;             // [DK][LC] (b.k.Gamma)^T: element -> W;
                                                               // then 2 x [DVS][LC] U^T hi, lo
-    static constexpr int WVT = BGT + BGT_BYTES;               // [DVS][LCF] fp32 (w.v)^T: element -> U0
-    static constexpr int PM = WVT + DVS * LCF * 4;            // 2 x [64][LC] P hi, lo: A,P -> state
+    static constexpr int WVT = BGT + BGT_BYTES;               // 2 x [DVS][64] (w.v)^T hi, lo (16-byte units
+                                                              // swizzled by wv_swz): element -> U0
+    static constexpr int PM = WVT + 2 * DVS * C * 2;          // 2 x [64][LC] P hi, lo: A,P -> state
     static constexpr int AM = PM + 2 * C * LC * 2;            // [64][LC] -A_IJ (J < I), (I + A_II)^{-1}
     static constexpr int RX = AM + C * LC * 2;                // work area, 192 rows of [LDK]:
                                                               //   mild: BG rows 0-63, K/Gamma rows 64-127
@@ -84,6 +84,11 @@ struct Cfg {
     static_assert(DK % 64 == 0 && DVS % 16 == 0 && DVS <= 64 && TPV >= 1, "shape");
 };
 
+// Unpadded [column][token] bf16 rows of 64 tokens (128 bytes): the 16-byte unit u of row r sits
+// at unit u ^ wv_swz(r).  The element phase stores rows 4 apart from neighbouring lanes, the
+// U0 product reads 8 consecutive rows per unit: both spread over distinct units.
+__device__ __forceinline__ int wv_swz(int r) { return (r ^ (r >> 2)) & 7; }
+
 // Inputs of one chunk as one thread loads them: CPL key channels of 4 tokens, and VC value
 // columns of TPV tokens.
 template <int CPL, int TPV, int VC, typename Decay>
@@ -101,7 +106,7 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
     int nslices, int xcd_map, const int64_t* __restrict__ cu_seqlens) {
     using G = Cfg<DK, DVS>;
     constexpr int CPL = G::CPL, KT = G::KT, NCT = G::NCT, SPW = G::SPW, UPW = G::UPW;
-    constexpr int LDK = G::LDK, LC = G::LC, LCF = G::LCF, VC = G::VC, TPV = G::TPV;
+    constexpr int LDK = G::LDK, LC = G::LC, VC = G::VC, TPV = G::TPV;
     __shared__ __attribute__((aligned(16))) char smem[G::BYTES];
     // regions the strong path and a few single accesses address directly; the rest goes
     // through byte offsets (see opq)
@@ -187,47 +192,46 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
     const int64_t seq_base_k = (tok0 * H + h) * DK;
     const int64_t seq_base_v = (tok0 * H + h) * DV;
 
-    // Every global load of a chunk, issued without a branch: a token past the end of the
-    // sequence reads the last token and is zeroed before use.  Two batches (decays and
-    // queries; keys, gates and values), each issued well before it is needed.
-    // addresses: a per-chunk base pointer (uniform) plus a per-lane offset within the chunk,
-    // (token * H * D + channel) * element size, which the host keeps below 2^24 * 4 bytes
-    const int rsk = H * DK, rsv = H * DV;  // elements between consecutive tokens
     // The next chunk's inputs are loaded in two batches (decays and queries; keys, gates and
-    // values), issued well before they are needed.
+    // values), each issued well before it is needed and without a branch.  Each array is read
+    // through a buffer resource over the chunk's tokens of this head: a token past the end of
+    // the sequence reads zeros (k = 0, and for activated gates log alpha = 0, no decay).
+    // Offsets: (token * H * D + channel) * element size from the chunk's first token, which the
+    // host keeps below 2^24 * 4 bytes.
+    const int rsk = H * DK, rsv = H * DV;  // elements between consecutive tokens
     using Decay = typename Gt::Decay;
     using InC = In<CPL, TPV, VC, Decay>;
     auto load_first = [&](int n, InC& in) {
-        const int t0 = n * C, last = Tlen - 1 - t0;
+        const int t0 = n * C, ntok = min(C, Tlen - t0);
         const int64_t cb = seq_base_k + (int64_t)t0 * tok_stride_k;
-        const Decay* gb = decay + cb;
-        const bf16* qb = q + cb;
+        const auto rg = buffer_over(decay + cb, ntok * rsk * (int)sizeof(Decay));
+        const auto rq = buffer_over(q + cb, ntok * rsk * 2);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const uint32_t e = __umul24(min(I * 16 + ts * 4 + m, last), rsk) + c0;
-            in.g[m] = gload_raw<Decay, CPL>(gb, e * (uint32_t)sizeof(Decay));
-            in.q[m] = gload_raw<bf16, CPL>(qb, e * 2);
+            const uint32_t e = __umul24(I * 16 + ts * 4 + m, rsk) + c0;
+            in.g[m] = bload_raw<Decay, CPL>(rg, e * (uint32_t)sizeof(Decay));
+            in.q[m] = bload_raw<bf16, CPL>(rq, e * 2);
         }
     };
     auto load_second = [&](int n, InC& in) {
-        const int t0 = n * C, last = Tlen - 1 - t0;
+        const int t0 = n * C, ntok = min(C, Tlen - t0);
         const int64_t cb = seq_base_k + (int64_t)t0 * tok_stride_k;
-        const bf16* kb = k + cb;
-        const bf16* bb = bgate + cb;
+        const auto rk = buffer_over(k + cb, ntok * rsk * 2);
+        const auto rb = buffer_over(bgate + cb, ntok * rsk * 2);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const uint32_t e = __umul24(min(I * 16 + ts * 4 + m, last), rsk) + c0;
-            in.k[m] = gload_raw<bf16, CPL>(kb, e * 2);
-            in.b[m] = gload_raw<bf16, CPL>(bb, e * 2);
+            const uint32_t e = __umul24(I * 16 + ts * 4 + m, rsk) + c0;
+            in.k[m] = bload_raw<bf16, CPL>(rk, e * 2);
+            in.b[m] = bload_raw<bf16, CPL>(rb, e * 2);
         }
         const int64_t cv = seq_base_v + (int64_t)t0 * tok_stride_v + col0;
-        const bf16* wb = wgate + cv;
-        const bf16* vb = v + cv;
+        const auto rw = buffer_over(wgate + cv, ntok * rsv * 2);
+        const auto rv = buffer_over(v + cv, ntok * rsv * 2);
 #pragma unroll
         for (int i = 0; i < TPV; ++i) {
-            const uint32_t e = __umul24(min(vtok + i, last), rsv) + vcol;
-            in.w[i] = gload_raw<bf16, VC>(wb, e * 2);
-            in.v[i] = gload_raw<bf16, VC>(vb, e * 2);
+            const uint32_t e = __umul24(vtok + i, rsv) + vcol;
+            in.w[i] = bload_raw<bf16, VC>(rw, e * 2);
+            in.v[i] = bload_raw<bf16, VC>(rv, e * 2);
         }
     };
 
@@ -249,13 +253,12 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
         const int c0 = hf * (DK / 2) + (lane & 15) * CPL;
         const int vcol = (tidv % (DVS / VC)) * VC, vtok = (tidv / (DVS / VC)) * TPV;
         // =============== element phase, pass 1: decays within the block ===============
-        // Tokens past the end of the sequence (their loads read the last token) act as the identity:
-        // no decay and k = 0 (which zeroes their A, P-column, BG and KG entries; q, b, w, v may stay:
-        // what they feed reaches only the rows of those tokens, which are never stored).  Applied
-        // where alpha and k are used, so that no register of a load still in flight is written here.
+        // Tokens past the end of the sequence (read as zeros) act as the identity: k = 0 zeroes
+        // their A, P-column, BG and KG entries, and their decay is 1 (a zero log alpha is;
+        // a zero logit is not, and is replaced).
         bool tok_ok[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) tok_ok[m] = t0 + I * 16 + ts * 4 + m < Tlen;
+        for (int m = 0; m < 4; ++m) tok_ok[m] = Gt::zero_is_identity || t0 + I * 16 + ts * 4 + m < Tlen;
         // decay from the block start through token m = ex * lp[m]; after token m to the block
         // end = ls[m] * es (lp, ls: this lane's 4 tokens; ex, es: the block's other token slots)
         float lp[CPL][4], ls[CPL][4], ex[CPL], es[CPL];
@@ -305,23 +308,24 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
         for (int i = 0; i < TPV; ++i)
 #pragma unroll
             for (int j = 0; j < Raw<bf16, VC>::W; ++j) asm volatile("" : "+v"(in.w[i].u[j]), "+v"(in.v[i].u[j]));
-        // write gate times value, transposed ([column][token]) in fp32 (exact for given gates: a
-        // product of two bf16 numbers).  Here rather than in pass 1: w and v are the later of the
-        // two batches of loads, and pass 1 then waits for the first batch only.
-        const int wvb = opq(G::WVT + (vcol * LCF + vtok) * 4);
+        // gate times value, transposed ([column][token]), as a hi + lo bf16 pair: the product of
+        // two bf16 numbers has at most 16 significant bits, so the pair holds it exactly.  Here
+        // rather than in pass 1: w and v are the later of the two batches of loads, and pass 1
+        // then waits for the first batch only.
 #pragma unroll
         for (int j = 0; j < VC; ++j) {
+            const int row = vcol + j;
+            const int wvb = opq(G::WVT + row * C * 2 + ((((vtok >> 3) ^ wv_swz(row)) << 3) | (vtok & 7)) * 2);
             float x[TPV];
 #pragma unroll
             for (int i = 0; i < TPV; ++i) x[i] = Gt::gate(in.w[i].f(j)) * in.v[i].f(j);
             if constexpr (TPV == 1) {
-                *F32(wvb + j * LCF * 4) = x[0];
+                bf16 h, l;
+                split_bf16(x[0], h, l);
+                *B16(wvb) = h;
+                *B16(wvb + DVS * C * 2) = l;
             } else {
-                typedef float V __attribute__((ext_vector_type(TPV)));
-                V y;
-#pragma unroll
-                for (int i = 0; i < TPV; ++i) y[i] = x[i];
-                *reinterpret_cast<V*>(F32(wvb + j * LCF * 4)) = y;
+                store_bf16_split<TPV>(B16(wvb), B16(wvb + DVS * C * 2), x);
             }
         }
         float blk[CPL][4], invgc[CPL];
@@ -379,7 +383,7 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                     float xq[CPL], xb[CPL], xki[CPL];
 #pragma unroll
                     for (int c = 0; c < CPL; ++c) {
-                        const float kv = tok_ok[m] ? in.k[m].f(c) : 0.f;
+                        const float kv = in.k[m].f(c);
                         const float gam = bex[c] * lp[c][m];
                         xq[c] = in.q[m].f(c) * gam;
                         xb[c] = Gt::gate(in.b[m].f(c)) * kv * gam;
@@ -409,7 +413,7 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
 #pragma unroll
                     for (int c = 0; c < CPL; ++c) {
                         const float qv = in.q[m].f(c);
-                        const float kv = tok_ok[m] ? in.k[m].f(c) : 0.f;
+                        const float kv = in.k[m].f(c);
                         const float bk = Gt::gate(in.b[m].f(c)) * kv;
                         const float gam = before[c] * pre[c][m];
                         xq[c] = qv * gam;
@@ -665,17 +669,17 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
         if (uo_owner) {
             // U0 tiles (rt, ct): lane (n, g) holds U0[16 rt + 4 g + r][16 ct + n]
             const int tb = opq((l16 * LC + g4 * 8) * 2);
-            f32x4 wa[UPW][2], wb[UPW][2];
-            Frag<bf16> ft[UPW][2];
+            Frag<bf16> fh[UPW][2], fl[UPW][2], ft[UPW][2];
 #pragma unroll
             for (int i = 0; i < UPW; ++i) {
                 const int u = wave + 8 * i, ct = u % NCT, rt = u / NCT;
-                const int wv = opq(G::WVT + ((ct * 16 + l16) * LCF + g4 * 8) * 4);
+                const int row = ct * 16 + l16;
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
                     if (kk > rt / 2) continue;
-                    wa[i][kk] = *reinterpret_cast<const f32x4*>(F32(wv + kk * 128));
-                    wb[i][kk] = *reinterpret_cast<const f32x4*>(F32(wv + kk * 128 + 16));
+                    const int wv = opq(G::WVT + row * C * 2 + (((kk * 4 + g4) ^ wv_swz(row)) << 4));
+                    fh[i][kk] = load_contig(B16(wv));
+                    fl[i][kk] = load_contig(B16(wv + DVS * C * 2));
                     ft[i][kk] = load_contig(B16(G::TR + tb + (rt * 16 * LC + kk * 32) * 2));
                 }
             }
@@ -687,15 +691,8 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
                     if (kk > rt / 2) continue;
-                    Frag<bf16> fh, fl;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        bf16 h, l;
-                        split_bf16(wa[i][kk][e], h, l); fh.v[e] = h; fl.v[e] = l;
-                        split_bf16(wb[i][kk][e], h, l); fh.v[e + 4] = h; fl.v[e + 4] = l;
-                    }
-                    mma(U[i], ft[i][kk], fh);
-                    mma(U[i], ft[i][kk], fl);
+                    mma(U[i], ft[i][kk], fh[i][kk]);
+                    mma(U[i], ft[i][kk], fl[i][kk]);
                 }
             }
         }

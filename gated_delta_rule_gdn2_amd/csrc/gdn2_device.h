@@ -183,12 +183,15 @@ struct GatesActivated {
     using Decay = float;
     // the decay input of a token that decays nothing (alpha = 1)
     __device__ static __forceinline__ Decay no_decay() { return 0.f; }
+    // a decay input of zero decays nothing: a token read as zeros is the identity
+    static constexpr bool zero_is_identity = true;
     __device__ static __forceinline__ float alpha(float log_alpha) { return exp_neg(log_alpha); }
     __device__ static __forceinline__ float gate(float g) { return g; }
 };
 struct GatesLogits {
     using Decay = bf16;
     __device__ static __forceinline__ Decay no_decay() { return (bf16)__builtin_inff(); }
+    static constexpr bool zero_is_identity = false;  // sigmoid(0) = 1/2
     __device__ static __forceinline__ float alpha(float a) { return sigmoid_f(a); }
     __device__ static __forceinline__ float gate(float x) { return sigmoid_f(x); }
 };
