@@ -264,7 +264,8 @@ size_t gdn2_chunk_fwd_split_workspace_bytes(int64_t B, int64_t T, int64_t H, int
     if (!split_supported(false, dk, dv, dtype) || B < 1 || T < 1 || H < 1 || B > INT_MAX || T > INT_MAX ||
         H > INT_MAX || B * H > INT_MAX / 64)
         return 0;
-    return gdn2::split_workspace_bytes(B, T, H, dk);
+    const int cus = device_cus();
+    return gdn2::split_workspace_bytes(B, T, H, dk, cus > 0 ? cus : 256);
 }
 
 size_t gdn2_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,

@@ -27,6 +27,13 @@
 // batch, then the state kernel for it, so a batch's records (83 KiB per chunk-head at d = 128)
 // are read back while the GPU's last-level cache still holds them.
 //
+// With few chains (long sequences of few heads) the state kernel's workgroups would leave most
+// compute units idle.  The state update is affine in the state, S_end = A S_start + B over any
+// run of chunks, so each sequence is cut into segments: one pass finds every segment's (A, B)
+// by carrying the identity (no write term) and zero (with it) through the segment, a small
+// kernel chains the segments' start states, and the forward proper then walks all segments
+// in parallel from those starts.  Every chunk's record is kept for the two passes.
+//
 // Record of one chunk-head (D = dk = dv), each part row-major, the columns of every row in the
 // order rec_col gives (groups of four interleaved within blocks of 32):
 //   QG [64][D] bf16 | BG [64][D] bf16 | KG^T hi, KG^T lo [D][64] bf16 |
@@ -675,11 +682,22 @@ __device__ __forceinline__ cb::Split32 split_pair(const f32x4& a, const f32x4& b
 //   the wave's own loads drain, barrier F publishes the next chunk's data; O is stored after F.
 // Every global access but the O stores goes straight to LDS, so a wave keeps few vector-memory
 // instructions in flight.
-template <typename OutT, int D, typename Gt>
+//
+// Segments (few chains: the sequence is cut into nseg runs of seg_len chunks, walked in
+// parallel).  Workgroup id -> (chain, slice) with chain = segment * BH + bh.  MODE kOut: the
+// forward proper; segment 0 starts from state_in, segment g > 0 from starts[g - 1]; the last
+// segment writes state_out.  MODE kTrans: a segment's transition S_end = A S_start + B_seg,
+// found by carrying 2 D columns through the same chunks: slices 0 .. nslices - 1 start from the
+// identity and take no write term (their end state is A), slices nslices .. 2 nslices - 1 start
+// from zero with the write term (B_seg); no output; the end state goes to trans[segment][bh] as
+// [D][2 D] fp32.
+constexpr int kOut = 0, kTrans = 1;
+template <typename OutT, int D, typename Gt, int MODE>
 __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
     const char* __restrict__ recs, const bf16* __restrict__ v, const bf16* __restrict__ wgate,
     const float* state_in, float* state_out, OutT* __restrict__ o, int Tparam, int H, int nslices,
-    int xcd_map, int c_begin, int c_end) {
+    int xcd_map, int c_begin, int c_end, int BH, int seg_len, const float* __restrict__ starts,
+    float* __restrict__ trans) {
     using Cf = StateCfg<D>;
     using R = Rec<D>;
     constexpr int KT = D / 16;           // 16-row key tiles of the state
@@ -690,25 +708,32 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    int bh, slice;
+    const int ns = MODE == kTrans ? 2 * nslices : nslices;  // workgroups per chain
+    int chain, slice;
     {
         const int id = blockIdx.x;
         if (xcd_map) {
             const int kk = id >> 3;
-            bh = 8 * (kk / nslices) + (id & 7);
-            slice = kk % nslices;
+            chain = 8 * (kk / ns) + (id & 7);
+            slice = kk % ns;
         } else {
-            bh = id / nslices;
-            slice = id % nslices;
+            chain = id / ns;
+            slice = id % ns;
         }
     }
+    const int seg = chain / BH, bh = chain % BH;
     const int h = bh % H;
-    const int nb = c_end - c_begin;
+    const int nb_all = c_end - c_begin;             // records per head
+    const int s0 = seg * seg_len, nb = min(seg_len, nb_all - s0);  // this workgroup's chunks
     const int Tlen = Tparam;
     const int64_t tok0 = (int64_t)(bh / H) * Tparam;
-    const int col = slice * 64 + wave * 16 + l16;   // this lane's state / value column
+    // the identity-start columns of a transition take no write term (w, v are staged for the
+    // value slice of the same index all the same, and unused)
+    const bool homog = MODE == kTrans && slice < nslices;
+    const int vslice = slice < nslices ? slice : slice - nslices;
+    const int col = vslice * 64 + wave * 16 + l16;  // this lane's state / value column
     const int64_t tok_stride_v = (int64_t)H * D;
-    const char* rec0 = recs + (int64_t)bh * nb * R::BYTES;
+    const char* rec0 = recs + ((int64_t)bh * nb_all + s0) * R::BYTES;
     StageOffsets<NLA> soa;
     StageOffsets<NLB> sob;
     soa.init(wave, lane, [](int u) { return src_unit_a<D>(u); });
@@ -721,7 +746,7 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
     auto stage_wv = [&](int n) {
         const int t0 = n * C;
         const int last = min(C, Tlen - t0) - 1;
-        const int64_t chunk = (tok0 + t0) * tok_stride_v + (int64_t)h * D + slice * 64;
+        const int64_t chunk = (tok0 + t0) * tok_stride_v + (int64_t)h * D + vslice * 64;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int jj = j * 4 + wave, tensor = jj >> 3, part = jj & 7;
@@ -733,7 +758,7 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
     };
     auto stage_a = [&](int i) {
         soa.issue(rec0 + (int64_t)i * R::BYTES, smem + Cf::A, wave);
-        stage_wv(c_begin + i);
+        stage_wv(c_begin + s0 + i);
     };
     auto stage_b = [&](int i) {
         sob.issue(rec0 + (int64_t)i * R::BYTES + R::A_BYTES, smem + Cf::B0 + (i & 1) * R::B_BYTES, wave);
@@ -741,11 +766,19 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
 
     // the state's 16 columns of this wave, all D rows: tile st, lane (n, g) holds S[16 st + 4 g + r][col]
     f32x4 S[KT];
+    {
+        const float* sin = seg == 0 ? state_in : starts + (int64_t)(seg - 1) * BH * D * D;
 #pragma unroll
-    for (int st = 0; st < KT; ++st) {
+        for (int st = 0; st < KT; ++st) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            S[st][r] = state_in ? state_in[((int64_t)bh * D + st * 16 + g4 * 4 + r) * D + col] : 0.f;
+            for (int r = 0; r < 4; ++r) {
+                const int row = st * 16 + g4 * 4 + r;
+                if constexpr (MODE == kTrans)
+                    S[st][r] = homog && row == col ? 1.f : 0.f;
+                else
+                    S[st][r] = sin ? sin[((int64_t)bh * D + row) * D + col] : 0.f;
+            }
+        }
     }
 
     // O of a chunk through a buffer resource: the chunk's first element of this head as a uniform
@@ -784,7 +817,7 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
     const int wcol = wave * 16 + l16, wu = wcol >> 3, wb = (wcol & 7) * 2;
     f32x4 Y[4];
     for (int i = 0; i < nb; ++i) {
-        const int n = c_begin + i;
+        const int n = c_begin + s0 + i;
         const int t0 = n * C;
         const char* rb = smem + Cf::B0 + (i & 1) * R::B_BYTES;
         const char* th = rb + (R::T - R::A_BYTES);
@@ -801,7 +834,7 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             fb[0][rt] = frag_perm(ra + R::BG, rt * 16 + l16, 0, g4, D * 2);
-            fq[0][rt] = frag_perm(ra + R::QG, rt * 16 + l16, 0, g4, D * 2);
+            if constexpr (MODE == kOut) fq[0][rt] = frag_perm(ra + R::QG, rt * 16 + l16, 0, g4, D * 2);
         }
         // the triangle fragments of U = T R: (rt, kk) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
         Frag<bf16> ft[6];
@@ -811,7 +844,8 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
                     fb[(kk + 1) & 1][rt] = frag_perm(ra + R::BG, rt * 16 + l16, kk + 1, g4, D * 2);
-                    fq[(kk + 1) & 1][rt] = frag_perm(ra + R::QG, rt * 16 + l16, kk + 1, g4, D * 2);
+                    if constexpr (MODE == kOut)
+                        fq[(kk + 1) & 1][rt] = frag_perm(ra + R::QG, rt * 16 + l16, kk + 1, g4, D * 2);
                 }
             } else {
 #pragma unroll
@@ -825,12 +859,12 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 mma(X[rt], fb[kk & 1][rt], sp.hi);
-                mma(Y[rt], fq[kk & 1][rt], sp.hi);
+                if constexpr (MODE == kOut) mma(Y[rt], fq[kk & 1][rt], sp.hi);
             }
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 mma(X[rt], fb[kk & 1][rt], sp.lo);
-                mma(Y[rt], fq[kk & 1][rt], sp.lo);
+                if constexpr (MODE == kOut) mma(Y[rt], fq[kk & 1][rt], sp.lo);
             }
         }
         // ---- R = w.v - X from the staged w and v (tokens past the end of the sequence: zero) ----
@@ -843,7 +877,7 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
                 const int off = t * 128 + wv_unit(t, wu) * 16 + wb;
                 const float wt = (float)*reinterpret_cast<const bf16*>(smem + Cf::WV + off);
                 const float vt = (float)*reinterpret_cast<const bf16*>(smem + Cf::WV + 8192 + off);
-                Rr[rt][r] = Gt::gate(wt) * vt - X[rt][r];
+                Rr[rt][r] = (homog ? 0.f : Gt::gate(wt) * vt) - X[rt][r];
             }
         if (t0 + C > Tlen) {
 #pragma unroll
@@ -898,6 +932,7 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
             for (int st = 0; st < KT; ++st) mma(S[st], fkl[st], us.hi);
         }
         // ---- O = Y + P U, term by term over the blocks as for U ----
+        if constexpr (MODE == kOut) {
         Frag<bf16> fph[6], fpl[6];
 #pragma unroll
         for (int p = 0; p < 6; ++p) {
@@ -916,18 +951,69 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
                 else if (term == 1) mma(Y[rt], fph[p], us.lo);
                 else mma(Y[rt], fpl[p], us.hi);
             }
+        }
         // barrier F: this wave's loads (the next chunk's parts A and B, w and v, the previous
         // chunk's O stores) have drained; the barrier publishes every wave's and frees part B of
         // this chunk.  Then O, whose stores overlap the next chunk.
         __syncthreads();
-        store_o(n, Y);
+        if constexpr (MODE == kOut) store_o(n, Y);
     }
 
-    if (state_out) {
+    if constexpr (MODE == kTrans) {
+        float* dst = trans + ((int64_t)chain * D) * (2 * D) + slice * 64 + wave * 16 + l16;
 #pragma unroll
         for (int st = 0; st < KT; ++st)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) state_out[((int64_t)bh * D + st * 16 + g4 * 4 + r) * D + col] = S[st][r];
+            for (int r = 0; r < 4; ++r) dst[(int64_t)(st * 16 + g4 * 4 + r) * (2 * D)] = S[st][r];
+    } else {
+        if (state_out && s0 + nb == nb_all) {
+#pragma unroll
+            for (int st = 0; st < KT; ++st)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    state_out[((int64_t)bh * D + st * 16 + g4 * 4 + r) * D + col] = S[st][r];
+        }
+    }
+}
+
+// Start states of the segments after the first: S_g = A_{g-1} S_{g-1} + B_{g-1} (the
+// transitions of the state kernel's kTrans mode, [D][2 D] per segment and head), S_0 the
+// initial state (zero if none).  One workgroup per (head, 16 state columns); the columns of a
+// state are independent, so each workgroup walks the segments on its own, in fp32.
+template <int D>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ trans, const float* s_init,
+                                                      float* __restrict__ starts, int BH, int nseg) {
+    constexpr int TPR = 256 / D;   // threads per state row
+    constexpr int CPT = 16 / TPR;  // columns per thread
+    __shared__ float sS[D][16];
+    const int bh = blockIdx.x / (D / 16), ct = blockIdx.x % (D / 16);
+    const int tid = threadIdx.x, r = tid / TPR, c0 = (tid % TPR) * CPT;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+        sS[r][c0 + c] = s_init ? s_init[((int64_t)bh * D + r) * D + ct * 16 + c0 + c] : 0.f;
+    for (int g = 1; g < nseg; ++g) {
+        __syncthreads();
+        const float* tr = trans + ((int64_t)(g - 1) * BH + bh) * D * (2 * D) + (int64_t)r * (2 * D);
+        float acc[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) acc[c] = tr[D + ct * 16 + c0 + c];
+        for (int k = 0; k < D; k += 4) {
+            const float4 a = *reinterpret_cast<const float4*>(tr + k);
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                acc[c] = fmaf(a.x, sS[k][c0 + c], acc[c]);
+                acc[c] = fmaf(a.y, sS[k + 1][c0 + c], acc[c]);
+                acc[c] = fmaf(a.z, sS[k + 2][c0 + c], acc[c]);
+                acc[c] = fmaf(a.w, sS[k + 3][c0 + c], acc[c]);
+            }
+        }
+        __syncthreads();
+        float* dst = starts + ((int64_t)(g - 1) * BH + bh) * D * D + (int64_t)r * D + ct * 16 + c0;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            sS[r][c0 + c] = acc[c];
+            dst[c] = acc[c];
+        }
     }
 }
 
@@ -945,24 +1031,69 @@ int64_t split_batch_chunks(int64_t BH, int64_t nchunks) {
     return c < nchunks ? c : nchunks;
 }
 
-size_t split_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d) {
+// Segments of the few-chains form: when the (sequence, head, 64-column) chains fill at most
+// half of the compute units, each sequence is cut into segments walked in parallel (enough of
+// them that the segments' chains fill the compute units, each at least 16 chunks long), joined
+// by their transitions.  1: the batched form.
+int64_t split_segments(int64_t BH, int64_t nchunks, int64_t d, int64_t cus) {
+    const int64_t chains = BH * (d / 64);
+    if (chains < 1 || 2 * chains > cus) return 1;
+    int64_t g = cus / chains;
+    if (g > nchunks / 16) g = nchunks / 16;
+    if (g < 2) return 1;
+    const int64_t len = (nchunks + g - 1) / g;  // chunks per segment; no segment left empty
+    return (nchunks + len - 1) / len;
+}
+
+size_t split_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d, int64_t cus) {
     const int64_t rb = split_record_bytes(d);
     if (rb == 0 || B < 1 || T < 1 || H < 1) return 0;
-    const int64_t nc = (T + 63) / 64;
-    const int64_t bc = split_batch_chunks(B * H, nc);
+    const int64_t nc = (T + 63) / 64, BH = B * H;
+    const int64_t g = split_segments(BH, nc, d, cus);
+    if (g > 1)  // every chunk's record, the transitions and the start states of segments 1 ..
+        return (size_t)(BH * nc * rb + (g - 1) * BH * d * (3 * d) * 4);
+    const int64_t bc = split_batch_chunks(BH, nc);
     // records of one batch, then the state carried between batches
-    return (size_t)(B * H * bc * rb + B * H * d * d * 4);
+    return (size_t)(BH * bc * rb + BH * d * d * 4);
 }
 
 template <typename OutT, int D, typename Gt>
 hipError_t launch_split_d(const ChunkArgs& a, char* ws) {
     const int64_t BH = a.B * a.H;
     const int nc = (int)((a.T + 63) / 64);
-    const int bc = (int)split_batch_chunks(BH, nc);
     const int nslices = D / 64;
+    hipStream_t st = (hipStream_t)a.stream;
+    const int g = (int)split_segments(BH, nc, D, a.cus);
+    if (g > 1) {
+        const int len = (nc + g - 1) / g;
+        char* trans = ws + BH * nc * sp::Rec<D>::BYTES;
+        float* tr = reinterpret_cast<float*>(trans);
+        float* starts = tr + (int64_t)(g - 1) * BH * D * 2 * D;
+        // every chunk's record, in one launch
+        const int64_t per = (BH * nc + a.cus - 1) / a.cus;
+        const int run = (int)(per < 1 ? 1 : per > nc ? nc : per);
+        const int runs = (nc + run - 1) / run;
+        hipLaunchKernelGGL((sp::local_kernel<D, Gt>), dim3((unsigned)(BH * runs)), dim3(sp::NT_LOCAL), 0, st,
+                           (const bf16*)a.q, (const bf16*)a.k, (const typename Gt::Decay*)a.decay(),
+                           (const bf16*)a.b, ws, (int)a.T, (int)a.H, 0, nc, run);
+        // the transitions of segments 0 .. g - 2
+        const int64_t tchains = (int64_t)(g - 1) * BH;
+        hipLaunchKernelGGL((sp::state_kernel<OutT, D, Gt, sp::kTrans>), dim3((unsigned)(tchains * 2 * nslices)),
+                           dim3(sp::NT_STATE), 0, st, (const char*)ws, (const bf16*)a.v, (const bf16*)a.w,
+                           (const float*)nullptr, (float*)nullptr, (OutT*)nullptr, (int)a.T, (int)a.H, nslices,
+                           tchains % 8 == 0 ? 1 : 0, 0, nc, (int)BH, len, (const float*)nullptr, tr);
+        hipLaunchKernelGGL((sp::combine_kernel<D>), dim3((unsigned)(BH * (D / 16))), dim3(256), 0, st,
+                           (const float*)tr, a.initial_state, starts, (int)BH, g);
+        const int64_t chains = (int64_t)g * BH;
+        hipLaunchKernelGGL((sp::state_kernel<OutT, D, Gt, sp::kOut>), dim3((unsigned)(chains * nslices)),
+                           dim3(sp::NT_STATE), 0, st, (const char*)ws, (const bf16*)a.v, (const bf16*)a.w,
+                           a.initial_state, a.final_state, (OutT*)a.o, (int)a.T, (int)a.H, nslices,
+                           chains % 8 == 0 ? 1 : 0, 0, nc, (int)BH, len, (const float*)starts, (float*)nullptr);
+        return hipGetLastError();
+    }
+    const int bc = (int)split_batch_chunks(BH, nc);
     const int xcd_map = BH % 8 == 0 ? 1 : 0;
     float* carry = a.final_state ? a.final_state : reinterpret_cast<float*>(ws + BH * bc * sp::Rec<D>::BYTES);
-    hipStream_t st = (hipStream_t)a.stream;
     for (int c0 = 0; c0 < nc; c0 += bc) {
         const int c1 = c0 + bc < nc ? c0 + bc : nc;
         // runs of consecutive chunks per local workgroup: one round of workgroups over the CUs
@@ -974,9 +1105,10 @@ hipError_t launch_split_d(const ChunkArgs& a, char* ws) {
                            (const bf16*)a.b, ws, (int)a.T, (int)a.H, c0, c1, run);
         const float* sin = c0 == 0 ? a.initial_state : carry;
         float* sout = c1 == nc ? a.final_state : carry;
-        hipLaunchKernelGGL((sp::state_kernel<OutT, D, Gt>), dim3((unsigned)(BH * nslices)), dim3(sp::NT_STATE), 0, st,
-                           (const char*)ws, (const bf16*)a.v, (const bf16*)a.w, sin, sout, (OutT*)a.o, (int)a.T,
-                           (int)a.H, nslices, xcd_map, c0, c1);
+        hipLaunchKernelGGL((sp::state_kernel<OutT, D, Gt, sp::kOut>), dim3((unsigned)(BH * nslices)),
+                           dim3(sp::NT_STATE), 0, st, (const char*)ws, (const bf16*)a.v, (const bf16*)a.w, sin,
+                           sout, (OutT*)a.o, (int)a.T, (int)a.H, nslices, xcd_map, c0, c1, (int)BH, c1 - c0,
+                           (const float*)nullptr, (float*)nullptr);
     }
     return hipGetLastError();
 }

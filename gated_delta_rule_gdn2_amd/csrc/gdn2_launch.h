@@ -125,8 +125,9 @@ struct MixerOutArgs {
 // dvs: value columns per workgroup slice (16, 32 or 64)
 hipError_t launch_chunk_fwd(const ChunkArgs& a, int dvs);
 // The forward in two kernels (chunk-local records, then the state pass), bf16 inputs with
-// dk = dv = 64 or 128, fixed-length sequences; workspace of split_workspace_bytes bytes.
-size_t split_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d);
+// dk = dv = 64 or 128, fixed-length sequences; workspace of split_workspace_bytes bytes (which
+// depends on the compute units: with few chains the form cuts sequences into segments).
+size_t split_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d, int64_t cus);
 hipError_t launch_chunk_split(const ChunkArgs& a, void* workspace);
 // bf16 inputs (dk = dv = 64 or 128)
 hipError_t launch_chunk_bf16(const ChunkArgs& a, int dvs);

@@ -141,11 +141,17 @@ gdn2_status_t gdn2_chunk_fwd_logits(const void* q, const void* k, const void* v,
 
 /*
  * gdn2_chunk_fwd_split_workspace_bytes -- bytes of device workspace that the
- * two-kernel form of gdn2_chunk_fwd needs for these sizes: the chunk records of
- * one batch of about a thousand (sequence, head, chunk) triples, 84,992 bytes
- * each at dk = dv = 128 (52,224 at 64), plus one fp32 state [B, H, dk, dv].
- * The two-kernel form exists for BF16 inputs with dk = dv = 64 or 128; for
- * every other combination (and for sizes out of range) this returns 0.
+ * two-kernel form of gdn2_chunk_fwd needs for these sizes on the current device:
+ * the chunk records of one batch of about a thousand (sequence, head, chunk)
+ * triples, 84,992 bytes each at dk = dv = 128 (52,224 at 64), plus one fp32
+ * state [B, H, dk, dv].  When the (sequence, head, 64 value columns) chains
+ * fill at most half of the device's compute units and the sequences hold at
+ * least 32 chunks, the form instead cuts every sequence into segments walked in
+ * parallel and joined through their state transitions: it then needs every
+ * chunk's record plus, per segment after the first, a [dk][2 dv] fp32
+ * transition and a [dk][dv] fp32 start state per (sequence, head).  The
+ * two-kernel form exists for BF16 inputs with dk = dv = 64 or 128; for every
+ * other combination (and for sizes out of range) this returns 0.
  */
 size_t gdn2_chunk_fwd_split_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                                             gdn2_dtype_t dtype);

@@ -201,12 +201,29 @@ def test_status_values_follow_the_boundary_table(lib):
     assert (ERR_WORKSPACE, ERR_HIP) == (6, 7)
 
 
+def split_segments(B, T, H, d, cus=256):
+    """Segments of the few-chains form: with (sequence, head, 64-column) chains filling at most
+    half of the compute units, enough segments of at least 16 chunks to fill them; else 1."""
+    nc, chains = (T + 63) // 64, B * H * (d // 64)
+    if 2 * chains > cus:
+        return 1
+    g = min(cus // chains, nc // 16)
+    if g < 2:
+        return 1
+    ln = -(-nc // g)
+    return -(-nc // ln)
+
+
 def split_ws_bytes(B, T, H, d):
-    """Records of one batch (about 1024 chunk-heads) plus one fp32 state."""
+    """Records of one batch (about 1024 chunk-heads) plus one fp32 state; with segments, every
+    chunk's record, the transitions ([d][2 d]) and start states of segments 1 .. g - 1."""
     part_a = 2 * 64 * d * 2                                   # QG, BG
     part_b = 2 * d * 64 * 2 + 3 * (32 * 32 + 32 * 64) * 2 + d * 4  # KG^T hi, lo; T; P hi, lo; Gamma_C
     rec = part_a + (part_b + 1023) // 1024 * 1024
     nc = (T + 63) // 64
+    g = split_segments(B, T, H, d)
+    if g > 1:
+        return B * H * nc * rec + (g - 1) * B * H * d * 3 * d * 4
     bc = min(max(1024 // (B * H), 1), nc)
     return B * H * bc * rec + B * H * d * d * 4
 
@@ -216,7 +233,10 @@ def test_fwd_workspace_bytes(lib):
     batch of chunks plus a state; fp32 and other sizes take none."""
     assert split_ws_bytes(1, 64, 1, 128) - 128 * 128 * 4 == 84992
     assert split_ws_bytes(1, 64, 1, 64) - 64 * 64 * 4 == 52224
-    for (B, T, H, d) in ((1, 1, 1, 64), (8, 4096, 16, 128), (1, 32768, 16, 128), (3, 1000, 5, 64)):
+    assert [split_segments(*x) for x in ((1, 32768, 16, 128), (8, 4096, 16, 128), (1, 5000, 3, 64),
+                                         (2, 2100, 16, 128), (1, 1000, 1, 64))] == [8, 1, 4, 2, 1]
+    for (B, T, H, d) in ((1, 1, 1, 64), (8, 4096, 16, 128), (1, 32768, 16, 128), (3, 1000, 5, 64),
+                         (1, 5000, 3, 64), (2, 2100, 16, 128)):
         assert lib.gdn2_chunk_fwd_split_workspace_bytes(B, T, H, d, d, BF16) == split_ws_bytes(B, T, H, d)
         assert lib.gdn2_chunk_fwd_split_workspace_bytes(B, T, H, d, d, F32) == 0
     assert lib.gdn2_chunk_fwd_split_workspace_bytes(1, 64, 1, 96, 96, BF16) == 0

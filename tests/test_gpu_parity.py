@@ -104,17 +104,12 @@ def test_strong_and_extreme_decay(dtype, dk, g_lo, g_hi, fused):
     check(o, s, o_ref, s_ref, tol_for(dtype), "decay U[%g,%g]" % (g_lo, g_hi))
 
 
-# Sizes whose chunk-heads exceed one batch of the two-kernel form (about 1024), with ragged
-# tails: the state is carried between batches, through final_state or the workspace.
-@pytest.mark.parametrize("B,T,H,d,with_s0,final", [
-    (2, 2100, 16, 128, True, "new"),      # 34 chunks x 32 heads: batches of 32 chunks + 2
-    (1, 5000, 20, 64, False, "none"),     # no final state: carried in the workspace
-    (3, 1500, 16, 128, True, "inplace"),  # final state written over the initial state
-])
-def test_split_across_batches(B, T, H, d, with_s0, final):
-    wl = dataclasses.replace(W.TRAIN_4K, name="batches", dk=d, dv=d, H=H, s0_std=0.05 if with_s0 else None)
-    say("case: across batches B=%d T=%d H=%d d=%d s0=%s final=%s (workspace %d bytes)"
-        % (B, T, H, d, with_s0, final, gdn2.chunk_fwd_workspace_bytes(B, T, H, d, d, split=True)))
+def _split_final_state_case(B, T, H, d, with_s0, final, label, g_lo=None, g_hi=None):
+    wl = dataclasses.replace(W.TRAIN_4K, name=label, dk=d, dv=d, H=H, s0_std=0.05 if with_s0 else None)
+    if g_lo is not None:
+        wl = dataclasses.replace(wl, g_lo=g_lo, g_hi=g_hi)
+    say("case: %s B=%d T=%d H=%d d=%d s0=%s final=%s decay=%s (workspace %d bytes)"
+        % (label, B, T, H, d, with_s0, final, (g_lo, g_hi), gdn2.chunk_fwd_workspace_bytes(B, T, H, d, d, split=True)))
     inp = W.make_inputs(wl, seed=61, B=B, T=T)
     x = to_dev(inp)
     if final == "inplace":
@@ -133,7 +128,32 @@ def test_split_across_batches(B, T, H, d, with_s0, final):
         say("  o err %.3e" % eo)
         assert eo <= TOL_BF16
     else:
-        check(o, s, o_ref, s_ref, TOL_BF16, "across batches")
+        check(o, s, o_ref, s_ref, TOL_BF16, label)
+
+
+# Sizes whose chunk-heads exceed one batch of the two-kernel form (about 1024), with chains
+# enough (more than half the compute units) that it runs in batches, ragged tails: the state is
+# carried between batches, through final_state or the workspace.
+@pytest.mark.parametrize("B,T,H,d,with_s0,final", [
+    (2, 2100, 48, 128, True, "new"),      # 34 chunks x 96 heads: batches of 10 chunks
+    (9, 1500, 16, 128, False, "none"),    # no final state: carried in the workspace
+    (3, 1500, 16, 128, True, "inplace"),  # final state written over the initial state
+])
+def test_split_across_batches(B, T, H, d, with_s0, final):
+    _split_final_state_case(B, T, H, d, with_s0, final, "across batches")
+
+
+# Few chains: each sequence is cut into segments walked in parallel, joined by their transitions
+# (2 to 4 segments here, ragged or whole last chunks, strong decay in one case).
+@pytest.mark.parametrize("B,T,H,d,with_s0,final,g_lo,g_hi", [
+    (1, 5000, 3, 64, True, "new", None, None),        # 4 segments of 20 chunks, the last partial
+    (2, 2100, 16, 128, True, "inplace", None, None),  # 2 segments of 17 chunks
+    (1, 4196, 4, 128, False, "none", None, None),     # 4 segments, no final state
+    (1, 2560, 2, 128, True, "new", None, None),       # 2 segments of 20 whole chunks
+    (1, 2100, 2, 128, True, "new", -60.0, -20.0),     # strong decay: every chunk pivots
+])
+def test_split_segments(B, T, H, d, with_s0, final, g_lo, g_hi):
+    _split_final_state_case(B, T, H, d, with_s0, final, "segments", g_lo, g_hi)
 
 
 def test_split_and_fused_agree():
