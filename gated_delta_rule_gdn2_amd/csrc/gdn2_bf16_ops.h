@@ -284,14 +284,22 @@ __device__ __forceinline__ void strong_ap_body(char* smem, Src src, int ntok, Pu
     }
     // ---- levels 16, 8, 4, 2 inside block I, then P's diagonal ----
     // decays of this lane's tokens, and the 4-token product of the token slot ts ^ 1
+    // and this lane's q, k and b.k (zero past the end of the sequence), read once for all levels
     float al[CPL][4], x16[CPL];
+    float tq[4][CPL], tk[4][CPL], tb[4][CPL];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         const int i = I * 16 + ts * 4 + m;
+        const bool valid = i < ntok;
         float g[CPL], xq[CPL], xk[CPL], xb[CPL];
         src(m, g, xq, xk, xb);
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) al[c][m] = i < ntok ? Gt::alpha(g[c]) : 1.f;
+        for (int c = 0; c < CPL; ++c) {
+            al[c][m] = valid ? Gt::alpha(g[c]) : 1.f;
+            tq[m][c] = valid ? xq[c] : 0.f;
+            tk[m][c] = valid ? xk[c] : 0.f;
+            tb[m][c] = valid ? Gt::gate(xb[c]) * xk[c] : 0.f;
+        }
     }
 #pragma unroll
     for (int c = 0; c < CPL; ++c) x16[c] = __shfl_xor(al[c][0] * al[c][1] * al[c][2] * al[c][3], 16);
@@ -304,9 +312,6 @@ __device__ __forceinline__ void strong_ap_body(char* smem, Src src, int ntok, Pu
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int i = ts * 4 + m;  // token within the block
-            const bool valid = I * 16 + i < ntok;
-            float xg[CPL], xq[CPL], xk[CPL], xb[CPL];
-            src(m, xg, xq, xk, xb);
             // split point p of the segment of i (last token of its lower half); a token in the
             // upper half is a row with factor Gamma_{i<-p}, one in the lower half a column with
             // factor Gamma_{p<-i}; both are products of at most one lane's decays and x16
@@ -338,9 +343,7 @@ __device__ __forceinline__ void strong_ap_body(char* smem, Src src, int ntok, Pu
             float ra[CPL], rp[CPL], cl[CPL];
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
-                const float qv = valid ? xq[c] : 0.f;
-                const float kv = valid ? xk[c] : 0.f;
-                const float bk = valid ? Gt::gate(xb[c]) * kv : 0.f;
+                const float qv = tq[m][c], kv = tk[m][c], bk = tb[m][c];
                 if (L == 4) {
                     ra[c] = 0.f; rp[c] = qv; cl[c] = kv;
                 } else {
