@@ -644,11 +644,13 @@ struct StageOffsets {
 #pragma unroll
         for (int j = 0; j < PER_WAVE; ++j) off[j] = src(min(j * 4 + wave, NLOADS - 1) * 64 + lane) * 16;
     }
+    // loads [SKIP_LO, SKIP_HI) are left out (parts a pass does not read)
+    template <int SKIP_LO = 0, int SKIP_HI = 0>
     __device__ __forceinline__ void issue(const char* rec_part, char* lds_part, int wave) const {
 #pragma unroll
         for (int j = 0; j < PER_WAVE; ++j) {
             const int jj = j * 4 + wave;
-            if (jj < NLOADS)
+            if (jj < NLOADS && !(jj >= SKIP_LO && jj < SKIP_HI))
                 __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(rec_part + off[j]),
                                                  (lds_void*)(lds_part + jj * 1024), 16, 0, 0);
         }
@@ -756,12 +758,23 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
                                              (lds_void*)(smem + Cf::WV + jj * 1024), 16, 0, 0);
         }
     };
+    // A transition reads neither QG nor P (no output), and its identity-start columns no w, v
+    constexpr int P_LO = (R::P - R::A_BYTES) / 1024, P_HI = (R::GC - R::A_BYTES) / 1024;
+    static_assert((R::P - R::A_BYTES) % 1024 == 0 && (R::GC - R::A_BYTES) % 1024 == 0 && R::BG % 1024 == 0,
+                  "parts skipped by a transition lie in whole KiB");
     auto stage_a = [&](int i) {
-        soa.issue(rec0 + (int64_t)i * R::BYTES, smem + Cf::A, wave);
-        stage_wv(c_begin + s0 + i);
+        if constexpr (MODE == kTrans)
+            soa.template issue<0, R::BG / 1024>(rec0 + (int64_t)i * R::BYTES, smem + Cf::A, wave);
+        else
+            soa.issue(rec0 + (int64_t)i * R::BYTES, smem + Cf::A, wave);
+        if (!homog) stage_wv(c_begin + s0 + i);
     };
     auto stage_b = [&](int i) {
-        sob.issue(rec0 + (int64_t)i * R::BYTES + R::A_BYTES, smem + Cf::B0 + (i & 1) * R::B_BYTES, wave);
+        char* dst = smem + Cf::B0 + (i & 1) * R::B_BYTES;
+        if constexpr (MODE == kTrans)
+            sob.template issue<P_LO, P_HI>(rec0 + (int64_t)i * R::BYTES + R::A_BYTES, dst, wave);
+        else
+            sob.issue(rec0 + (int64_t)i * R::BYTES + R::A_BYTES, dst, wave);
     };
 
     // the state's 16 columns of this wave, all D rows: tile st, lane (n, g) holds S[16 st + 4 g + r][col]
