@@ -365,14 +365,15 @@ def test_exact_retrieval_property_full_shape():
     assert e <= TOL_BF16
 
 
-@pytest.mark.parametrize("d", [64, 128])
-def test_bf16_output_is_fp32_output_rounded_once(d):
+@pytest.mark.parametrize("d,T,fused", [(64, 190, True), (128, 190, True), (128, 190, False),
+                                        (128, 2100, False)])  # the last in 2 segments
+def test_bf16_output_is_fp32_output_rounded_once(d, T, fused):
     """The bf16-output build differs from the fp32-output one only in the store."""
     wl = dataclasses.replace(W.TRAIN_4K, name="outdt", dk=d, dv=d, H=3, s0_std=0.05)
-    inp = W.make_inputs(wl, seed=47, B=2, T=190)
-    say("case: bf16 output vs fp32 output, d=%d" % d)
-    o32, s32 = run_gpu(inp)
-    o16, s16 = run_gpu(inp, out_dtype=torch.bfloat16)
+    inp = W.make_inputs(wl, seed=47, B=1 if T > 1000 else 2, T=T)
+    say("case: bf16 output vs fp32 output, d=%d T=%d fused=%s" % (d, T, fused))
+    o32, s32 = run_gpu(inp, fused=fused)
+    o16, s16 = run_gpu(inp, out_dtype=torch.bfloat16, fused=fused)
     assert o16.dtype == torch.bfloat16
     assert torch.equal(o16, o32.to(torch.bfloat16))
     assert torch.equal(s16, s32)
