@@ -687,7 +687,9 @@ __device__ __forceinline__ cb::Split32 split_pair(const f32x4& a, const f32x4& b
 //
 // Segments (few chains: the sequence is cut into nseg runs of seg_len chunks, walked in
 // parallel).  Workgroup id -> (chain, slice) with chain = segment * BH + bh.  MODE kOut: the
-// forward proper; segment 0 starts from state_in, segment g > 0 from starts[g - 1]; the last
+// forward proper; segment 0 starts from state_in, or with segments from starts[0] (a copy of it,
+// so that a final state written over the initial one cannot race its read), segment g > 0 from
+// starts[g]; the last
 // segment writes state_out.  MODE kTrans: a segment's transition S_end = A S_start + B_seg,
 // found by carrying 2 D columns through the same chunks: slices 0 .. nslices - 1 start from the
 // identity and take no write term (their end state is A), slices nslices .. 2 nslices - 1 start
@@ -780,7 +782,7 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
     // the state's 16 columns of this wave, all D rows: tile st, lane (n, g) holds S[16 st + 4 g + r][col]
     f32x4 S[KT];
     {
-        const float* sin = seg == 0 ? state_in : starts + (int64_t)(seg - 1) * BH * D * D;
+        const float* sin = starts ? starts + (int64_t)seg * BH * D * D : state_in;
 #pragma unroll
         for (int st = 0; st < KT; ++st) {
 #pragma unroll
@@ -989,10 +991,11 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
     }
 }
 
-// Start states of the segments after the first: S_g = A_{g-1} S_{g-1} + B_{g-1} (the
-// transitions of the state kernel's kTrans mode, [D][2 D] per segment and head), S_0 the
-// initial state (zero if none).  One workgroup per (head, 16 state columns); the columns of a
-// state are independent, so each workgroup walks the segments on its own, in fp32.
+// Start states of the segments: S_0 the initial state (zero if none), copied, and
+// S_g = A_{g-1} S_{g-1} + B_{g-1} (the transitions of the state kernel's kTrans mode, [D][2 D]
+// per segment and head), written to starts[g] as [D][D].  One workgroup per (head, 16 state
+// columns); the columns of a state are independent, so each workgroup walks the segments on
+// its own, in fp32.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ trans, const float* s_init,
                                                       float* __restrict__ starts, int BH, int nseg) {
@@ -1002,8 +1005,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int bh = blockIdx.x / (D / 16), ct = blockIdx.x % (D / 16);
     const int tid = threadIdx.x, r = tid / TPR, c0 = (tid % TPR) * CPT;
 #pragma unroll
-    for (int c = 0; c < CPT; ++c)
-        sS[r][c0 + c] = s_init ? s_init[((int64_t)bh * D + r) * D + ct * 16 + c0 + c] : 0.f;
+    for (int c = 0; c < CPT; ++c) {
+        const float x = s_init ? s_init[((int64_t)bh * D + r) * D + ct * 16 + c0 + c] : 0.f;
+        sS[r][c0 + c] = x;
+        starts[((int64_t)bh * D + r) * D + ct * 16 + c0 + c] = x;
+    }
     for (int g = 1; g < nseg; ++g) {
         __syncthreads();
         const float* tr = trans + ((int64_t)(g - 1) * BH + bh) * D * (2 * D) + (int64_t)r * (2 * D);
@@ -1021,7 +1027,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
             }
         }
         __syncthreads();
-        float* dst = starts + ((int64_t)(g - 1) * BH + bh) * D * D + (int64_t)r * D + ct * 16 + c0;
+        float* dst = starts + ((int64_t)g * BH + bh) * D * D + (int64_t)r * D + ct * 16 + c0;
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
             sS[r][c0 + c] = acc[c];
@@ -1063,8 +1069,8 @@ size_t split_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d, int64_t
     if (rb == 0 || B < 1 || T < 1 || H < 1) return 0;
     const int64_t nc = (T + 63) / 64, BH = B * H;
     const int64_t g = split_segments(BH, nc, d, cus);
-    if (g > 1)  // every chunk's record, the transitions and the start states of segments 1 ..
-        return (size_t)(BH * nc * rb + (g - 1) * BH * d * (3 * d) * 4);
+    if (g > 1)  // every chunk's record, the transitions of segments 0 .. g - 2, every start state
+        return (size_t)(BH * nc * rb + (g - 1) * BH * d * (2 * d) * 4 + g * BH * d * d * 4);
     const int64_t bc = split_batch_chunks(BH, nc);
     // records of one batch, then the state carried between batches
     return (size_t)(BH * bc * rb + BH * d * d * 4);

@@ -148,8 +148,9 @@ gdn2_status_t gdn2_chunk_fwd_logits(const void* q, const void* k, const void* v,
  * fill at most half of the device's compute units and the sequences hold at
  * least 32 chunks, the form instead cuts every sequence into segments walked in
  * parallel and joined through their state transitions: it then needs every
- * chunk's record plus, per segment after the first, a [dk][2 dv] fp32
- * transition and a [dk][dv] fp32 start state per (sequence, head).  The
+ * chunk's record plus, per (sequence, head), a [dk][2 dv] fp32 transition for
+ * every segment but the last and a [dk][dv] fp32 start state for every
+ * segment.  The
  * two-kernel form exists for BF16 inputs with dk = dv = 64 or 128; for every
  * other combination (and for sizes out of range) this returns 0.
  */

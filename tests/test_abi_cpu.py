@@ -216,14 +216,15 @@ def split_segments(B, T, H, d, cus=256):
 
 def split_ws_bytes(B, T, H, d):
     """Records of one batch (about 1024 chunk-heads) plus one fp32 state; with segments, every
-    chunk's record, the transitions ([d][2 d]) and start states of segments 1 .. g - 1."""
+    chunk's record, the transitions ([d][2 d]) of segments 0 .. g - 2 and every segment's start
+    state."""
     part_a = 2 * 64 * d * 2                                   # QG, BG
     part_b = 2 * d * 64 * 2 + 3 * (32 * 32 + 32 * 64) * 2 + d * 4  # KG^T hi, lo; T; P hi, lo; Gamma_C
     rec = part_a + (part_b + 1023) // 1024 * 1024
     nc = (T + 63) // 64
     g = split_segments(B, T, H, d)
     if g > 1:
-        return B * H * nc * rec + (g - 1) * B * H * d * 3 * d * 4
+        return B * H * nc * rec + (g - 1) * B * H * d * 2 * d * 4 + g * B * H * d * d * 4
     bc = min(max(1024 // (B * H), 1), nc)
     return B * H * bc * rec + B * H * d * d * 4
 
