@@ -119,7 +119,9 @@ gdn2_status_t chunk_fwd_common(const void* q, const void* k, const void* v, cons
     if (!mul_ok(NS * H, dk * dv, &ns)) return GDN2_ERR_SHAPE;
     if (NS * H * (dv / 16) > UINT_MAX / 2) return GDN2_ERR_SHAPE;
     // per-lane offsets inside one chunk are formed with 24-bit multiplies of the token stride
-    if (H * dk >= (int64_t(1) << 24) || H * dv >= (int64_t(1) << 24)) return GDN2_ERR_SHAPE;
+    // per-lane 32-bit byte offsets within a chunk (64 tokens of up to 4-byte elements) and the
+    // chunk's buffer range stay below 2^30
+    if (H * dk >= (int64_t(1) << 22) || H * dv >= (int64_t(1) << 22)) return GDN2_ERR_SHAPE;
     const void* ptrs[] = {q, k, v, decay, b, w, initial_state, o, final_state};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return GDN2_ERR_MISALIGNED;

@@ -196,8 +196,8 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
     // values), each issued well before it is needed and without a branch.  Each array is read
     // through a buffer resource over the chunk's tokens of this head: a token past the end of
     // the sequence reads zeros (k = 0, and for activated gates log alpha = 0, no decay).
-    // Offsets: (token * H * D + channel) * element size from the chunk's first token, which the
-    // host keeps below 2^24 * 4 bytes.
+    // Offsets: (token * H * D + channel) * element size from the chunk's first token; the host
+    // keeps H * D below 2^22, so offsets and the buffer range stay below 2^30 bytes.
     const int rsk = H * DK, rsv = H * DV;  // elements between consecutive tokens
     using Decay = typename Gt::Decay;
     using InC = In<CPL, TPV, VC, Decay>;

@@ -91,7 +91,7 @@ typedef enum gdn2_status {
  * output rounds it once on the store.  Others return GDN2_ERR_UNSUPPORTED.
  * o must not overlap any input; final_state must not overlap any input other
  * than an identical initial_state.  H * dk and H * dv (the elements between
- * consecutive tokens of one tensor) must be below 2^24, else GDN2_ERR_SHAPE.
+ * consecutive tokens of one tensor) must be below 2^22, else GDN2_ERR_SHAPE.
  * workspace / workspace_bytes select the implementation.  With a workspace of
  * at least gdn2_chunk_fwd_split_workspace_bytes(...) bytes (device memory owned by
  * the caller, 256-byte aligned, overlapping no argument; its contents on entry
