@@ -151,6 +151,8 @@ def test_split_across_batches(B, T, H, d, with_s0, final):
     (1, 4196, 4, 128, False, "none", None, None),     # 4 segments, no final state
     (1, 2560, 2, 128, True, "new", None, None),       # 2 segments of 20 whole chunks
     (1, 2100, 2, 128, True, "new", -60.0, -20.0),     # strong decay: every chunk pivots
+    (1, 2048, 2, 128, True, "new", None, None),       # the fewest chunks cut: 2 segments of 16
+    (1, 2049, 2, 128, True, "new", None, None),       # the same plus a one-token last chunk
 ])
 def test_split_segments(B, T, H, d, with_s0, final, g_lo, g_hi):
     _split_final_state_case(B, T, H, d, with_s0, final, "segments", g_lo, g_hi)
