@@ -30,11 +30,13 @@
 //     with hi + lo bf16 MFMA products; waves 4-6 form the off-diagonal blocks.
 //   * the off-diagonal blocks of T = (I + A)^{-1} through halves of 32 tokens:
 //     T = [[T_A, 0], [T_C, T_B]], T_10 = -T_11 A_10 T_00, T_32 likewise, T_C = -T_B A_BA T_A.
-//   * W = T (b.k.Gamma) and U0 = T (w.v), then the state pass, as independent 16 x 16 tiles
-//     spread over all eight waves; the fp32 state slice lives in MFMA accumulators (four
-//     tiles per wave), and S (bf16) and U (hi / lo bf16) reach the other waves through LDS.
-// Operands that are not bf16 numbers themselves (w.v through U0, U, P) enter the MFMAs as
-// hi + lo bf16 pairs; every product accumulates in fp32.
+//   * the state: wave 4 + j holds the 16 value columns j of the slice, all key rows, in fp32
+//     MFMA accumulators for the whole sequence.  While waves 0-3 form T_C, it forms
+//     Z = ((b.k).Gamma) S and Y = (q.Gamma) S, which need no T; then, in its own registers,
+//     U = T (w.v - Z) (= U0 - W S of the formulas above, with the product regrouped),
+//     O = Y + P U and S_next.  Waves 0-3 meanwhile start the next chunk.
+// Operands that are not bf16 numbers themselves (w.v - Z, U, P) enter the MFMAs as hi + lo
+// bf16 pairs; every product accumulates in fp32.
 
 #include "gdn2_bf16_ops.h"
 #include "gdn2_launch.h"
@@ -48,30 +50,24 @@ template <int DK, int DVS>
 struct Cfg {
     static constexpr int CPL = DK / 32;   // key channels per lane in the element phase
     static constexpr int KT = DK / 16;    // 16-channel tiles
-    static constexpr int NCT = DVS / 16;  // 16-column value tiles of the slice
-    static constexpr int UPW = 4 * NCT >= 8 ? 4 * NCT / 8 : 1;  // (row, column) tiles of U, O per wave
-    static constexpr int SPW = KT * NCT >= 8 ? KT * NCT / 8 : 1;  // 16 x 16 state tiles per wave
+    static constexpr int NCT = DVS / 16;  // 16-column value tiles of the slice: one state wave each
     static constexpr int LDK = DK + 8;    // bf16 row stride of [token][channel] tiles
     static constexpr int LC = C + 8;      // bf16 row stride of [*][token] tiles
     static constexpr int VC = C * DVS / NT >= 4 ? 4 : C * DVS / NT;  // value columns per lane
     static constexpr int TPV = C * DVS / (NT * VC);                  // value tokens per lane
     // LDS regions (byte offsets); lifetimes within a chunk in the comments
-    static constexpr int QG = 0;                              // [64][LDK] q.Gamma: element -> state
-    static constexpr int KGT = QG + C * LDK * 2;              // [DK][LC] (k.Gamma')^T: element -> state
-    static constexpr int BGT_BYTES = (DK > 2 * DVS ? DK : 2 * DVS) * LC * 2;
-    static constexpr int BGT = KGT + DK * LC * 2;             // [DK][LC] (b.k.Gamma)^T: element -> W;
-                                                              // then 2 x [DVS][LC] U^T hi, lo
-    static constexpr int WVT = BGT + BGT_BYTES;               // 2 x [DVS][64] (w.v)^T hi, lo (16-byte units
-                                                              // swizzled by wv_swz): element -> U0
-    static constexpr int PM = WVT + 2 * DVS * C * 2;          // 2 x [64][LC] P hi, lo: A,P -> state
+    static constexpr int QG = 0;                              // [64][LDK] q.Gamma: element -> Y
+    static constexpr int KGT = QG + C * LDK * 2;              // [DK][LC] (k.Gamma')^T: element -> state update
+    static constexpr int BG = KGT + DK * LC * 2;              // [64][LDK] (b.k).Gamma: element -> A (mild), Z
+    static constexpr int WVT = BG + C * LDK * 2;              // [DVS][64] fp32 (w.v)^T (16-byte units
+                                                              // swizzled by wv_swz): element -> state pass
+    static constexpr int PM = WVT + DVS * C * 4;              // 2 x [64][LC] P hi, lo: A,P -> O
     static constexpr int AM = PM + 2 * C * LC * 2;            // [64][LC] -A_IJ (J < I), (I + A_II)^{-1}
     static constexpr int RX = AM + C * LC * 2;                // work area, 192 rows of [LDK]:
-                                                              //   mild: BG rows 0-63, K/Gamma rows 64-127
+                                                              //   mild: K/Gamma rows 64-127
                                                               //   strong: group and level tiles
-                                                              //   then W rows 0-63, S^T (bf16) rows
-                                                              //   64-127, T = (I + A)^{-1} rows 128-
-    static constexpr int SBT = RX + C * LDK * 2;
-    static constexpr int TR = RX + 2 * C * LDK * 2;           // [64][LC] T, row-major
+                                                              //   T = (I + A)^{-1} rows 128-
+    static constexpr int TR = RX + 2 * C * LDK * 2;           // [64][LC] T, row-major: -> state pass
     static constexpr int GC = RX + 192 * LDK * 2;             // [DK] fp32 whole-chunk decays
     static constexpr int BLK = GC + DK * 4;                   // [4][DK] fp32 16-token block decays
     static constexpr int FLG = BLK + 4 * DK * 4;              // [8] int: per-wave strong-decay votes
@@ -79,15 +75,31 @@ struct Cfg {
     static constexpr int BYTES = TTR + C * LC * 2;
     static_assert(BYTES <= 163840, "LDS budget exceeded");
     static_assert(BYTES >= 4 * (kMaxSort + 1), "no room for the sequence order");
-    static_assert(SBT + DVS * LDK * 2 <= TR, "state operand does not fit the work area");
     static_assert(TR + C * LC * 2 <= GC, "T does not fit the work area");
     static_assert(DK % 64 == 0 && DVS % 16 == 0 && DVS <= 64 && TPV >= 1, "shape");
 };
 
-// Unpadded [column][token] bf16 rows of 64 tokens (128 bytes): the 16-byte unit u of row r sits
-// at unit u ^ wv_swz(r).  The element phase stores rows 4 apart from neighbouring lanes, the
-// U0 product reads 8 consecutive rows per unit: both spread over distinct units.
-__device__ __forceinline__ int wv_swz(int r) { return (r ^ (r >> 2)) & 7; }
+// An operand fragment in the permuted slot map of a pair of accumulator tiles: slot (g, e) of
+// the 32-wide contraction block holds element 4 g + e for e < 4 and 16 + 4 g + e - 4 above, so
+// that a pair of 16 x 16 accumulators (lane holds rows 4 g .. 4 g + 3 of each) is directly an
+// operand.  p points at element 4 g of the block's row; two 8-byte halves.
+__device__ __forceinline__ Frag<bf16> load_halves(const bf16* p) {
+    const bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
+    const bf16x4 b = *reinterpret_cast<const bf16x4*>(p + 16);
+    Frag<bf16> f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f.v[e] = a[e];
+        f.v[e + 4] = b[e];
+    }
+    return f;
+}
+
+// Unpadded [column][token] fp32 rows of 64 tokens (256 bytes): the 16-byte unit u (4 tokens) of
+// row r sits at unit u ^ wv_swz(r).  The swizzle is one-to-one on 16 consecutive rows (the state
+// pass's reads) and on 16 rows 4 apart (the element phase's stores), so both fall on distinct
+// banks.
+__device__ __forceinline__ int wv_swz(int r) { return (r ^ (r >> 2)) & 15; }
 
 // Inputs of one chunk as one thread loads them: CPL key channels of 4 tokens, and VC value
 // columns of TPV tokens.
@@ -105,7 +117,7 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
     const float* initial_state, OutT* __restrict__ o, float* final_state, int B, int Tparam, int H,
     int nslices, int xcd_map, const int64_t* __restrict__ cu_seqlens) {
     using G = Cfg<DK, DVS>;
-    constexpr int CPL = G::CPL, KT = G::KT, NCT = G::NCT, SPW = G::SPW, UPW = G::UPW;
+    constexpr int CPL = G::CPL, KT = G::KT, NCT = G::NCT;
     constexpr int LDK = G::LDK, LC = G::LC, VC = G::VC, TPV = G::TPV;
     __shared__ __attribute__((aligned(16))) char smem[G::BYTES];
     // regions the strong path and a few single accesses address directly; the rest goes
@@ -167,24 +179,23 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
     // P above the diagonal blocks is never written: clear once
     for (int x = tid; x < 2 * C * LC; x += NT) sPh[x] = (bf16)0.f;
 
-    // ---- state slice in accumulators: wave w holds the 16 x 16 tiles w + 8 i (row tile st =
-    // index % KT, column tile index / KT); lane (n, g) holds S[16 st + 4 g + r][16 ct + n] ----
-    f32x4 S[SPW];
+    // ---- the state slice in accumulators: wave 4 + j (j < NCT) holds value columns 16 j ..
+    // 16 j + 15 of the slice for every key row, as KT tiles; lane (n, g) of tile st holds
+    // S[16 st + 4 g + r][16 j + n] ----
+    const int sct = wave - 4;
+    const bool owner = sct >= 0 && sct < NCT;  // uniform across the wave
+    const int sc = owner ? sct : 0;
+    f32x4 S[KT];
 #pragma unroll
-    for (int i = 0; i < SPW; ++i) S[i] = zero4();
-    if (initial_state && wave + 8 * (SPW - 1) < KT * NCT) {
+    for (int i = 0; i < KT; ++i) S[i] = zero4();
+    if (initial_state && owner) {
 #pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int st = (wave + 8 * i) % KT, ct = (wave + 8 * i) / KT;
-            const float* src = initial_state + ((int64_t)bh * DK + st * 16 + g4 * 4) * DV + col0 + ct * 16 + l16;
+        for (int st = 0; st < KT; ++st) {
+            const float* src = initial_state + ((int64_t)bh * DK + st * 16 + g4 * 4) * DV + col0 + sc * 16 + l16;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) S[i][r] = src[(int64_t)r * DV];
+            for (int r = 0; r < 4; ++r) S[st][r] = src[(int64_t)r * DV];
         }
     }
-    // (true for every wave where the tiles divide evenly; said so at compile time, so that no branch
-    // surrounds the output stores and the compiler can count them as in flight afterwards)
-    const bool state_owner = 8 * SPW == KT * NCT || wave + 8 * (SPW - 1) < KT * NCT;
-    const bool uo_owner = 8 * UPW == 4 * NCT || wave + 8 * (UPW - 1) < 4 * NCT;
 
     const int nchunks = (Tlen + C - 1) / C;
     const int64_t tok_stride_k = (int64_t)H * DK;
@@ -192,10 +203,11 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
     const int64_t seq_base_k = (tok0 * H + h) * DK;
     const int64_t seq_base_v = (tok0 * H + h) * DV;
 
-    // The next chunk's inputs are loaded in two batches (decays and queries; keys, gates and
-    // values), each issued well before it is needed and without a branch.  Each array is read
-    // through a buffer resource over the chunk's tokens of this head: a token past the end of
-    // the sequence reads zeros (k = 0, and for activated gates log alpha = 0, no decay).
+    // The next chunk's inputs are loaded in two batches (decays; queries, keys, gates and values:
+    // fewer registers held through the T_C step), each issued well before it is needed and
+    // without a branch.  Each array is read through a buffer resource over the chunk's tokens of
+    // this head: a token past the end of the sequence reads zeros (k = 0, and for activated gates
+    // log alpha = 0, no decay).
     // Offsets: (token * H * D + channel) * element size from the chunk's first token; the host
     // keeps H * D below 2^22, so offsets and the buffer range stay below 2^30 bytes.
     const int rsk = H * DK, rsv = H * DV;  // elements between consecutive tokens
@@ -205,22 +217,22 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
         const int t0 = n * C, ntok = min(C, Tlen - t0);
         const int64_t cb = seq_base_k + (int64_t)t0 * tok_stride_k;
         const auto rg = buffer_over(decay + cb, ntok * rsk * (int)sizeof(Decay));
-        const auto rq = buffer_over(q + cb, ntok * rsk * 2);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const uint32_t e = __umul24(I * 16 + ts * 4 + m, rsk) + c0;
             in.g[m] = bload_raw<Decay, CPL>(rg, e * (uint32_t)sizeof(Decay));
-            in.q[m] = bload_raw<bf16, CPL>(rq, e * 2);
         }
     };
     auto load_second = [&](int n, InC& in) {
         const int t0 = n * C, ntok = min(C, Tlen - t0);
         const int64_t cb = seq_base_k + (int64_t)t0 * tok_stride_k;
+        const auto rq = buffer_over(q + cb, ntok * rsk * 2);
         const auto rk = buffer_over(k + cb, ntok * rsk * 2);
         const auto rb = buffer_over(bgate + cb, ntok * rsk * 2);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const uint32_t e = __umul24(I * 16 + ts * 4 + m, rsk) + c0;
+            in.q[m] = bload_raw<bf16, CPL>(rq, e * 2);
             in.k[m] = bload_raw<bf16, CPL>(rk, e * 2);
             in.b[m] = bload_raw<bf16, CPL>(rb, e * 2);
         }
@@ -308,25 +320,18 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
         for (int i = 0; i < TPV; ++i)
 #pragma unroll
             for (int j = 0; j < Raw<bf16, VC>::W; ++j) asm volatile("" : "+v"(in.w[i].u[j]), "+v"(in.v[i].u[j]));
-        // gate times value, transposed ([column][token]), as a hi + lo bf16 pair: the product of
-        // two bf16 numbers has at most 16 significant bits, so the pair holds it exactly.  Here
-        // rather than in pass 1: w and v are the later of the two batches of loads, and pass 1
-        // then waits for the first batch only.
+        // gate times value, transposed ([column][token]), in fp32 (exact: the product of two bf16
+        // numbers has at most 16 significant bits).  Here rather than in pass 1: w and v are the
+        // later of the two batches of loads, and pass 1 then waits for the first batch only.
 #pragma unroll
         for (int j = 0; j < VC; ++j) {
             const int row = vcol + j;
-            const int wvb = opq(G::WVT + row * C * 2 + ((((vtok >> 3) ^ wv_swz(row)) << 3) | (vtok & 7)) * 2);
-            float x[TPV];
+            const int wvb = opq(G::WVT + row * C * 4 + ((((vtok >> 2) ^ wv_swz(row)) << 2) | (vtok & 3)) * 4);
+            typedef float V __attribute__((ext_vector_type(TPV)));
+            V x;
 #pragma unroll
             for (int i = 0; i < TPV; ++i) x[i] = Gt::gate(in.w[i].f(j)) * in.v[i].f(j);
-            if constexpr (TPV == 1) {
-                bf16 h, l;
-                split_bf16(x[0], h, l);
-                *B16(wvb) = h;
-                *B16(wvb + DVS * C * 2) = l;
-            } else {
-                store_bf16_split<TPV>(B16(wvb), B16(wvb + DVS * C * 2), x);
-            }
+            *reinterpret_cast<V*>(__builtin_assume_aligned(smem + wvb, 4 * TPV)) = x;
         }
         float blk[CPL][4], invgc[CPL];
         int strong;
@@ -367,7 +372,7 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                     if (K > I) after[c] *= blk[c][K];
                 }
             }
-            float bgt[CPL][4], kgt[CPL][4];
+            float kgt[CPL][4];
             if (!strong) {
                 // QG = q.Gamma, BG = (b.k).Gamma, KG = k.Gamma' and KI = k / Gamma = KG / Gamma_C
                 const int eb = opq(((I * 16 + ts * 4) * LDK + c0) * 2);
@@ -389,10 +394,9 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                         xb[c] = Gt::gate(in.b[m].f(c)) * kv * gam;
                         kgt[c][m] = kv * (ls[c][m] * esa[c]);
                         xki[c] = kgt[c][m] * invgc[c];
-                        bgt[c][m] = xb[c];
                     }
                     store_bf16<CPL>(B16(eb + m * LDK * 2), xq);
-                    store_bf16<CPL>(B16(ebx + m * LDK * 2), xb);
+                    store_bf16<CPL>(B16(eb + G::BG + m * LDK * 2), xb);
                     store_bf16<CPL>(B16(ebx + (C + m) * LDK * 2), xki);
                 }
             } else {
@@ -409,7 +413,7 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     // y: level-64 rows/columns (pivot token 31), z: level-32 ones (pivots 15, 47)
-                    float xq[CPL], ya[CPL], yp[CPL], za[CPL], zp[CPL];
+                    float xq[CPL], xb[CPL], ya[CPL], yp[CPL], za[CPL], zp[CPL];
 #pragma unroll
                     for (int c = 0; c < CPL; ++c) {
                         const float qv = in.q[m].f(c);
@@ -417,7 +421,7 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                         const float bk = Gt::gate(in.b[m].f(c)) * kv;
                         const float gam = before[c] * pre[c][m];
                         xq[c] = qv * gam;
-                        bgt[c][m] = bk * gam;
+                        xb[c] = bk * gam;
                         kgt[c][m] = kv * suf[c][m] * after[c];
                         if (I >= 2) {
                             const float f = I == 3 ? blk[c][2] * pre[c][m] : pre[c][m];
@@ -436,6 +440,7 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                         }
                     }
                     store_bf16<CPL>(B16(eb + m * LDK * 2), xq);
+                    store_bf16<CPL>(B16(eb + G::BG + m * LDK * 2), xb);
                     // 16-row groups: g0,g1 A rows (blocks 2,3), g2,g3 P rows, g4,g5 columns (blocks 0,1);
                     // g6,g7 A rows (blocks 1,3), g8,g9 P rows, g10,g11 columns (blocks 0,2)
                     bf16* wk = B16(wkb + m * LDK * 2);
@@ -456,10 +461,7 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
             // rows c0 .. c0 + CPL - 1 lie in one 16-row group: one swizzled offset serves them all
             const int tb = opq(G::KGT + (c0 * LC + swz(c0, I * 16 + ts * 4)) * 2);
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                store_bf16<4>(B16(tb + (G::BGT - G::KGT) + c * LC * 2), bgt[c]);
-                store_bf16<4>(B16(tb + c * LC * 2), kgt[c]);
-            }
+            for (int c = 0; c < CPL; ++c) store_bf16<4>(B16(tb + c * LC * 2), kgt[c]);
         }
         lds_barrier();
 
@@ -472,12 +474,11 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                 // diagonal block I = wave: A_II in both orientations, then its inverse
                 f32x4 nt = zero4(), nn = zero4();
                 const int rk = opq(((wave * 16 + l16) * LDK + g4 * 8) * 2);
-                const int rkx = opq(rk + G::RX);
                 Frag<bf16> fk[DK / 32], fa[DK / 32];
 #pragma unroll
                 for (int kk = 0; kk < DK / 32; ++kk) {
-                    fk[kk] = load_contig(B16(rkx + C * LDK * 2 + kk * 64));
-                    fa[kk] = load_contig(B16(rkx + kk * 64));
+                    fk[kk] = load_contig(B16(rk + G::RX + C * LDK * 2 + kk * 64));
+                    fa[kk] = load_contig(B16(rk + G::BG + kk * 64));
                 }
                 sched_fence();
 #pragma unroll
@@ -526,7 +527,7 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
 #pragma unroll
                     for (int kk = 0; kk < DK / 32; ++kk) {
                         fk[kk] = load_contig(B16(rl + G::RX + (C + Jb * 16) * LDK * 2 + kk * 64));
-                        fa[kk] = load_contig(B16(rl + G::RX + Ib * 16 * LDK * 2 + kk * 64));
+                        fa[kk] = load_contig(B16(rl + G::BG + Ib * 16 * LDK * 2 + kk * 64));
                         fq[kk] = load_contig(B16(rl + Ib * 16 * LDK * 2 + kk * 64));
                     }
                     sched_fence();
@@ -557,6 +558,8 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
         lds_barrier();
 
         // =============== off-diagonal blocks of T, through halves of 32 tokens ===============
+        // (waves 0-3; the state waves meanwhile form Z and Y)
+        f32x4 Z[4], Y[4];
         // T = [[T_A, 0], [T_C, T_B]] with T_A = [[T_00, 0], [T_10, T_11]], T_B likewise, and
         // T_10 = -T_11 A_10 T_00, T_32 = -T_33 A_32 T_22, T_C = -T_B A_BA T_A.  The local store
         // holds -A, so every product below adds.  B operands that are columns of T come from T^T.
@@ -565,7 +568,7 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
             // T_2J = T_22 Z_2J and T_3J = T_32 Z_2J + T_33 Z_3J, formed transposed so that
             // lane (i, g) holds a row: T_RJ[i][4 g + r].  T_10 (needed for J = 0) and T_32 (for
             // R = 3) come from the diagonal blocks alone; the waves that need them form them here
-            // (waves 0 and 3 also store them for the W and U0 products), so no level of their own
+            // (waves 0 and 3 also store them for the state pass), so no level of their own
             // and no barrier sits between the diagonal blocks and T_C.
             const int J = wave & 1, R = 2 + (wave >> 1);
             const int tb = opq((l16 * LC + g4 * 4) * 2);
@@ -624,228 +627,168 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
             float x[4];
             acc_to_array(t, x);
             store_bf16<4>(B16(G::TR + tb + (R * 16 * LC + J * 16) * 2), x);
+        } else if (owner) {
+            // Z = BG S and Y = QG S for this wave's 16 value columns, which need no T.  Pairs of
+            // state tiles are the B operands as they stand (slot map of load_halves); the rows of
+            // BG and QG are read in the same map.  Z: lane (n, g) holds Z[16 rt + 4 g + r][n];
+            // Y: lane (i, g) holds Y[16 rt + i][4 g + r], the orientation of the o stores.
+            Frag<bf16> sf[KT / 2];
+#pragma unroll
+            for (int m = 0; m < KT / 2; ++m) sf[m] = frag_from_acc<bf16>(S[2 * m], S[2 * m + 1]);
+            const int rb = opq((l16 * LDK + g4 * 4) * 2);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                Frag<bf16> fb[KT / 2], fq[KT / 2];
+#pragma unroll
+                for (int m = 0; m < KT / 2; ++m) {
+                    fb[m] = load_halves(B16(G::BG + rb + (rt * 16 * LDK + m * 32) * 2));
+                    fq[m] = load_halves(B16(G::QG + rb + (rt * 16 * LDK + m * 32) * 2));
+                }
+                sched_fence();
+                Z[rt] = zero4();
+                Y[rt] = zero4();
+#pragma unroll
+                for (int m = 0; m < KT / 2; ++m) {
+                    mma(Z[rt], fb[m], sf[m]);
+                    mma(Y[rt], sf[m], fq[m]);
+                }
+            }
         }
         // the next chunk's keys, gates and values
         load_second(nnext, in);
 
         lds_barrier();
 
-        // =============== W = T (b.k.Gamma), U0 = T (w.v); bf16 copy of the state ===============
+        // =============== state pass: this wave's 16 value columns ===============
+        // R = w.v - Z, U = T R, O = Y + P U, S <- Diag(Gamma_C) S + KG^T U, all in this wave's
+        // registers: an accumulator pair (16 tokens apart) is the next product's B operand in the
+        // slot map of load_halves, so R and U never go through LDS.  No barrier follows: waves 0-3
+        // go on to the next chunk's first element pass, which writes only the votes and the block
+        // decays; the barrier after it keeps the next operand tiles behind these reads.
+        if (owner) {
+            const int row = sc * 16 + l16;  // this lane's value column: a row of (w.v)^T
+            const int wb = opq(G::WVT + row * C * 4);
+            const int ws = wv_swz(row);
+            const int rl = opq((l16 * LC + g4 * 4) * 2);
+            f32x4 wv[4];
+            Frag<bf16> tf[4][2];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                // tokens 16 rt + 4 g .. + 3: 16-byte unit 4 rt + g
+                wv[rt] = *reinterpret_cast<const f32x4*>(smem + wb + (((4 * rt + g4) ^ ws) << 4));
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    if (m > rt / 2) continue;
+                    tf[rt][m] = load_halves(B16(G::TR + rl + (rt * 16 * LC + m * 32) * 2));
+                }
+            }
+            sched_fence();
+            f32x4 R[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) R[rt][r] = wv[rt][r] - Z[rt][r];
+            const Split32 rs[2] = {split32(R[0], R[1]), split32(R[2], R[3])};
+            // U = T R: lane (n, g) holds U[16 rt + 4 g + r][n]
+            f32x4 U[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                U[rt] = zero4();
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    if (m > rt / 2) continue;
+                    mma(U[rt], tf[rt][m], rs[m].hi);
+                    mma(U[rt], tf[rt][m], rs[m].lo);
+                }
+            }
+            const Split32 us[2] = {split32(U[0], U[1]), split32(U[2], U[3])};
+            // O = Y + P U, in Y's orientation (lane (i, g): O[16 rt + i][4 g + r])
+            Frag<bf16> ph[4][2], pl[4][2];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    if (m > rt / 2) continue;
+                    ph[rt][m] = load_halves(B16(G::PM + rl + (rt * 16 * LC + m * 32) * 2));
+                    pl[rt][m] = load_halves(B16(G::PM + rl + (C * LC + rt * 16 * LC + m * 32) * 2));
+                }
+            sched_fence();
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    if (m > rt / 2) continue;
+                    mma(Y[rt], us[m].hi, ph[rt][m]);
+                    mma(Y[rt], us[m].lo, ph[rt][m]);
+                    mma(Y[rt], us[m].hi, pl[rt][m]);
+                }
+            // S <- Diag(Gamma_C) S + KG^T U, in two halves of the row tiles; KG^T's rows are
+            // swizzled by 16-byte units: unit u of row 16 st + i sits at u ^ st
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                Frag<bf16> kf[KT / 2][2];
+#pragma unroll
+                for (int j = 0; j < KT / 2; ++j) {
+                    const int st = h2 * (KT / 2) + j;
+                    const int kb = opq(G::KGT + (st * 16 + l16) * LC * 2 + ((g4 & 1) << 3));
+#pragma unroll
+                    for (int m = 0; m < 2; ++m) {
+                        const bf16x4 a = *reinterpret_cast<const bf16x4*>(
+                            smem + kb + ((((4 * m + (g4 >> 1)) ^ st) & 7) << 4));
+                        const bf16x4 b = *reinterpret_cast<const bf16x4*>(
+                            smem + kb + ((((4 * m + 2 + (g4 >> 1)) ^ st) & 7) << 4));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            kf[j][m].v[e] = a[e];
+                            kf[j][m].v[e + 4] = b[e];
+                        }
+                    }
+                }
+                sched_fence();
+#pragma unroll
+                for (int j = 0; j < KT / 2; ++j) {
+                    const int st = h2 * (KT / 2) + j;
+                    S[st] *= *reinterpret_cast<const f32x4*>(sGC + st * 16 + g4 * 4);
+#pragma unroll
+                    for (int m = 0; m < 2; ++m) {
+                        mma(S[st], kf[j][m], us[m].hi);
+                        mma(S[st], kf[j][m], us[m].lo);
+                    }
+                }
+            }
+        }
+        // o through a buffer resource over this chunk's tokens of the head: a last partial chunk's
+        // rows past the end of the sequence fall outside its range and are dropped, and so is
+        // everything a wave without state columns issues (range 0).  The stores therefore sit on
+        // no branch (behind one, the compiler would assume a path where they are not in flight
+        // and wait for every load at the top of the next chunk).
         {
-            // W^T tiles (column tile cw of W, row tile rt): lane (i, g) holds W[16 rt + i][16 cw + 4 g + r]
-            constexpr int IPW = KT * 4 / 8;
-            const int tb = opq((l16 * LC + g4 * 8) * 2);
-            Frag<bf16> fb[IPW][2], ft[IPW][2];
-#pragma unroll
-            for (int i = 0; i < IPW; ++i) {
-                const int it = wave * IPW + i;
-                const int cw = it / 4, rt = it % 4;
-                const int y = (g4 ^ cw) & 7;  // swizzle of row 16 cw + l16: unit (4 kk + g4) ^ cw
-                const int bb = opq(G::BGT + (cw * 16 + l16) * LC * 2);
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    if (kk > rt / 2) continue;
-                    fb[i][kk] = load_contig(B16(bb + (((4 * kk) ^ y) << 4)));
-                    ft[i][kk] = load_contig(B16(G::TR + tb + (rt * 16 * LC + kk * 32) * 2));
-                }
-            }
-            sched_fence();
-#pragma unroll
-            for (int i = 0; i < IPW; ++i) {
-                const int it = wave * IPW + i;
-                const int cw = it / 4, rt = it % 4;
-                f32x4 acc = zero4();
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    if (kk > rt / 2) continue;
-                    mma(acc, fb[i][kk], ft[i][kk]);
-                }
-                float x[4];
-                acc_to_array(acc, x);
-                store_bf16<4>(B16(G::RX + ((rt * 16 + l16) * LDK + cw * 16 + g4 * 4) * 2), x);
-            }
-        }
-        f32x4 U[UPW];
-        if (uo_owner) {
-            // U0 tiles (rt, ct): lane (n, g) holds U0[16 rt + 4 g + r][16 ct + n]
-            const int tb = opq((l16 * LC + g4 * 8) * 2);
-            Frag<bf16> fh[UPW][2], fl[UPW][2], ft[UPW][2];
-#pragma unroll
-            for (int i = 0; i < UPW; ++i) {
-                const int u = wave + 8 * i, ct = u % NCT, rt = u / NCT;
-                const int row = ct * 16 + l16;
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    if (kk > rt / 2) continue;
-                    const int wv = opq(G::WVT + row * C * 2 + (((kk * 4 + g4) ^ wv_swz(row)) << 4));
-                    fh[i][kk] = load_contig(B16(wv));
-                    fl[i][kk] = load_contig(B16(wv + DVS * C * 2));
-                    ft[i][kk] = load_contig(B16(G::TR + tb + (rt * 16 * LC + kk * 32) * 2));
-                }
-            }
-            sched_fence();
-#pragma unroll
-            for (int i = 0; i < UPW; ++i) {
-                const int u = wave + 8 * i, rt = u / NCT;
-                U[i] = zero4();
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    if (kk > rt / 2) continue;
-                    mma(U[i], ft[i][kk], fh[i][kk]);
-                    mma(U[i], ft[i][kk], fl[i][kk]);
-                }
-            }
-        }
-        if (state_owner) {
-            // the state as a bf16 operand, transposed: S^T[n][c]
-#pragma unroll
-            for (int i = 0; i < SPW; ++i) {
-                const int st = (wave + 8 * i) % KT, ct = (wave + 8 * i) / KT;
-                float x[4];
-                acc_to_array(S[i], x);
-                store_bf16<4>(B16(G::SBT + ((ct * 16 + l16) * LDK + st * 16 + g4 * 4) * 2), x);
-            }
-        }
-        lds_barrier();
-
-        // =============== state pass ===============
-        // (rt, ct) tiles: X = W S, Y^T = (q.Gamma S)^T, U = U0 - X; then O^T = Y^T + (P U)^T
-        // (lane (i, g) holds O[16 rt + i][16 ct + 4 g + r]); state tiles: S <- Gamma_C S + KG^T U
-        f32x4 Y[UPW];
-        if (uo_owner) {
-            const int rw = opq((l16 * LDK + g4 * 8) * 2);
-            // every tile of this wave has column tile wave % NCT
-            const int ctw = wave % NCT;
-            Frag<bf16> sf[DK / 32], fw[UPW][DK / 32], fq[UPW][DK / 32];
-#pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) sf[kk] = load_contig(B16(G::SBT + rw + (ctw * 16 * LDK + kk * 32) * 2));
-#pragma unroll
-            for (int i = 0; i < UPW; ++i) {
-                const int rt = (wave + 8 * i) / NCT;
-#pragma unroll
-                for (int kk = 0; kk < DK / 32; ++kk) {
-                    fw[i][kk] = load_contig(B16(G::RX + rw + (rt * 16 * LDK + kk * 32) * 2));
-                    fq[i][kk] = load_contig(B16(rw + (rt * 16 * LDK + kk * 32) * 2));
-                }
-            }
-            sched_fence();
-#pragma unroll
-            for (int i = 0; i < UPW; ++i) {
-                const int u = wave + 8 * i, ct = u % NCT, rt = u / NCT;
-                f32x4 X = zero4();
-                Y[i] = zero4();
-#pragma unroll
-                for (int kk = 0; kk < DK / 32; ++kk) {
-                    mma(X, fw[i][kk], sf[kk]);
-                    mma(Y[i], sf[kk], fq[i][kk]);
-                }
-                U[i] -= X;
-                float x[4];
-                acc_to_array(U[i], x);
-                const int idx = ((ct * 16 + l16) * LC + rt * 16 + g4 * 4) * 2;
-                store_bf16_split<4>(B16(G::BGT + idx), B16(G::BGT + DVS * LC * 2 + idx), x);
-            }
-        }
-        lds_barrier();
-        if (uo_owner) {
-            const int rl = opq((l16 * LC + g4 * 8) * 2);
-            // every tile of this wave has column tile wave % NCT; the last tile has the most rows
-            const int ctw = wave % NCT;
-            constexpr int KKU = 2;
-            const int kku = ((wave + 8 * (UPW - 1)) / NCT) / 2 + 1;  // U fragments the tiles use
-            Frag<bf16> uh[KKU], ul[KKU], ph[UPW][2], pl[UPW][2];
-#pragma unroll
-            for (int kk = 0; kk < KKU; ++kk) {
-                if (kk >= kku) continue;
-                const int uo = G::BGT + rl + (ctw * 16 * LC + kk * 32) * 2;
-                uh[kk] = load_contig(B16(uo));
-                ul[kk] = load_contig(B16(uo + DVS * LC * 2));
-            }
-#pragma unroll
-            for (int i = 0; i < UPW; ++i) {
-                const int rt = (wave + 8 * i) / NCT;
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    if (kk > rt / 2) continue;
-                    const int po = G::PM + rl + (rt * 16 * LC + kk * 32) * 2;
-                    ph[i][kk] = load_contig(B16(po));
-                    pl[i][kk] = load_contig(B16(po + C * LC * 2));
-                }
-            }
-            sched_fence();
-            // O through a buffer resource over this chunk's tokens of the head: a last partial
-            // chunk's rows past the end of the sequence fall outside its range and are dropped,
-            // so the stores need no branch (a branch around them would make the compiler assume
-            // they may not be in flight, and wait for every load at the top of the next chunk)
             const int ntok = min(C, Tlen - t0);
-            const auto ro = __builtin_amdgcn_make_buffer_rsrc(
-                o + seq_base_v + (int64_t)t0 * tok_stride_v, 0, ntok * rsv * (int)sizeof(OutT), 0x00020000);
+            const auto ro = __builtin_amdgcn_make_buffer_rsrc(o + seq_base_v + (int64_t)t0 * tok_stride_v, 0,
+                                                              owner ? ntok * rsv * (int)sizeof(OutT) : 0, 0x00020000);
 #pragma unroll
-            for (int i = 0; i < UPW; ++i) {
-                const int u = wave + 8 * i, ct = u % NCT, rt = u / NCT;
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    if (kk > rt / 2) continue;
-                    mma(Y[i], uh[kk], ph[i][kk]);
-                    mma(Y[i], ul[kk], ph[i][kk]);
-                    mma(Y[i], uh[kk], pl[i][kk]);
-                }
-                const uint32_t e = (__umul24(rt * 16 + l16, rsv) + col0 + ct * 16 + g4 * 4) * sizeof(OutT);
+            for (int rt = 0; rt < 4; ++rt) {
+                const uint32_t e = (__umul24(rt * 16 + l16, rsv) + col0 + sc * 16 + g4 * 4) * sizeof(OutT);
                 if constexpr (sizeof(OutT) == 4) {
                     typedef uint32_t U4 __attribute__((ext_vector_type(4)));
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(U4, Y[i]), ro, (int)e, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(U4, Y[rt]), ro, (int)e, 0, 0);
                 } else {
                     typedef uint32_t U2 __attribute__((ext_vector_type(2)));
                     bf16x4 y;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) y[r] = (bf16)Y[i][r];
+                    for (int r = 0; r < 4; ++r) y[r] = (bf16)Y[rt][r];
                     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(U2, y), ro, (int)e, 0, 0);
                 }
             }
         }
-        if (state_owner) {
-            const int rl = opq((l16 * LC + g4 * 8) * 2);
-            // every state tile of this wave has row tile wave % KT
-            const int stw = wave % KT;
-            const int y = (g4 ^ stw) & 7;  // swizzle of row 16 st + l16: unit (4 kk + g4) ^ st
-            const int kb = opq(G::KGT + (stw * 16 + l16) * LC * 2);
-            Frag<bf16> fk[2], fh[SPW][2], fl[SPW][2];
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) fk[kk] = load_contig(B16(kb + (((4 * kk) ^ y) << 4)));
-#pragma unroll
-            for (int i = 0; i < SPW; ++i) {
-                const int ct = (wave + 8 * i) / KT;
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const int uo = G::BGT + rl + (ct * 16 * LC + kk * 32) * 2;
-                    fh[i][kk] = load_contig(B16(uo));
-                    fl[i][kk] = load_contig(B16(uo + DVS * LC * 2));
-                }
-            }
-            sched_fence();
-#pragma unroll
-            for (int i = 0; i < SPW; ++i) {
-                const int st = (wave + 8 * i) % KT;
-                S[i] *= *reinterpret_cast<const f32x4*>(sGC + st * 16 + g4 * 4);
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    mma(S[i], fk[kk], fh[i][kk]);
-                    mma(S[i], fk[kk], fl[i][kk]);
-                }
-            }
-        }
-        // No barrier here: the next chunk's first pass writes only the votes and the block
-        // decays, which nothing above reads, and the barrier after that pass keeps its operand
-        // tiles behind every wave's reads of U, P and KG^T here.
     }
 
-    if (state_owner && final_state) {
+    if (owner && final_state) {
 #pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int st = (wave + 8 * i) % KT, ct = (wave + 8 * i) / KT;
-            float* dst = final_state + ((int64_t)bh * DK + st * 16 + g4 * 4) * DV + col0 + ct * 16 + l16;
+        for (int st = 0; st < KT; ++st) {
+            float* dst = final_state + ((int64_t)bh * DK + st * 16 + g4 * 4) * DV + col0 + sc * 16 + l16;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(int64_t)r * DV] = S[i][r];
+            for (int r = 0; r < 4; ++r) dst[(int64_t)r * DV] = S[st][r];
         }
     }
 }
