@@ -564,6 +564,9 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
         // T_10 = -T_11 A_10 T_00, T_32 = -T_33 A_32 T_22, T_C = -T_B A_BA T_A.  The local store
         // holds -A, so every product below adds.  B operands that are columns of T come from T^T.
         if (wave < 4) {
+            // the next chunk's keys, gates and values, issued ahead of the state waves' share: the
+            // CU's load issue is a queue, and these waves have time to spare in this step
+            load_second(nnext, in);
             // block (R, J) of T_C, one per wave: Z_xJ = (-A_x0) T_0J + (-A_x1) T_1J, then
             // T_2J = T_22 Z_2J and T_3J = T_32 Z_2J + T_33 Z_3J, formed transposed so that
             // lane (i, g) holds a row: T_RJ[i][4 g + r].  T_10 (needed for J = 0) and T_32 (for
@@ -627,35 +630,36 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
             float x[4];
             acc_to_array(t, x);
             store_bf16<4>(B16(G::TR + tb + (R * 16 * LC + J * 16) * 2), x);
-        } else if (owner) {
-            // Z = BG S and Y = QG S for this wave's 16 value columns, which need no T.  Pairs of
-            // state tiles are the B operands as they stand (slot map of load_halves); the rows of
-            // BG and QG are read in the same map.  Z: lane (n, g) holds Z[16 rt + 4 g + r][n];
-            // Y: lane (i, g) holds Y[16 rt + i][4 g + r], the orientation of the o stores.
-            Frag<bf16> sf[KT / 2];
+        } else {
+            if (owner) {
+                // Z = BG S and Y = QG S for this wave's 16 value columns, which need no T.  Pairs of
+                // state tiles are the B operands as they stand (slot map of load_halves); the rows of
+                // BG and QG are read in the same map.  Z: lane (n, g) holds Z[16 rt + 4 g + r][n];
+                // Y: lane (i, g) holds Y[16 rt + i][4 g + r], the orientation of the o stores.
+                Frag<bf16> sf[KT / 2];
 #pragma unroll
-            for (int m = 0; m < KT / 2; ++m) sf[m] = frag_from_acc<bf16>(S[2 * m], S[2 * m + 1]);
-            const int rb = opq((l16 * LDK + g4 * 4) * 2);
+                for (int m = 0; m < KT / 2; ++m) sf[m] = frag_from_acc<bf16>(S[2 * m], S[2 * m + 1]);
+                const int rb = opq((l16 * LDK + g4 * 4) * 2);
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                Frag<bf16> fb[KT / 2], fq[KT / 2];
+                for (int rt = 0; rt < 4; ++rt) {
+                    Frag<bf16> fb[KT / 2], fq[KT / 2];
 #pragma unroll
-                for (int m = 0; m < KT / 2; ++m) {
-                    fb[m] = load_halves(B16(G::BG + rb + (rt * 16 * LDK + m * 32) * 2));
-                    fq[m] = load_halves(B16(G::QG + rb + (rt * 16 * LDK + m * 32) * 2));
-                }
-                sched_fence();
-                Z[rt] = zero4();
-                Y[rt] = zero4();
+                    for (int m = 0; m < KT / 2; ++m) {
+                        fb[m] = load_halves(B16(G::BG + rb + (rt * 16 * LDK + m * 32) * 2));
+                        fq[m] = load_halves(B16(G::QG + rb + (rt * 16 * LDK + m * 32) * 2));
+                    }
+                    sched_fence();
+                    Z[rt] = zero4();
+                    Y[rt] = zero4();
 #pragma unroll
-                for (int m = 0; m < KT / 2; ++m) {
-                    mma(Z[rt], fb[m], sf[m]);
-                    mma(Y[rt], sf[m], fq[m]);
+                    for (int m = 0; m < KT / 2; ++m) {
+                        mma(Z[rt], fb[m], sf[m]);
+                        mma(Y[rt], sf[m], fq[m]);
+                    }
                 }
             }
+            load_second(nnext, in);
         }
-        // the next chunk's keys, gates and values
-        load_second(nnext, in);
 
         lds_barrier();
 
