@@ -19,12 +19,12 @@
 //   * state_kernel: one workgroup of four waves per (sequence, head, 64 value columns); wave w
 //     owns 16 columns of the state for all dk rows, in MFMA accumulators, for the whole
 //     sequence.  Per chunk: R = w.v - BG S and Y = QG S (S as a hi / lo bf16 pair), U = T R,
-//     O = Y + P U, S <- Gamma_C S + KG^T U (KG^T as a hi / lo pair), all in that wave's
+//     O = Y + P U, S <- Gamma_C S + KG^T U (U as a hi / lo pair), all in that wave's
 //     registers; the record, w and v go from global memory straight into LDS (no register
 //     staging), the next chunk's parts loading while this one is computed.
 //
 // The host walks the chunks in batches of about a thousand chunk-heads: the local kernel for a
-// batch, then the state kernel for it, so a batch's records (83 KiB per chunk-head at d = 128)
+// batch, then the state kernel for it, so a batch's records (67 KiB per chunk-head at d = 128)
 // are read back while the GPU's last-level cache still holds them.
 //
 // With few chains (long sequences of few heads) the state kernel's workgroups would leave most
@@ -36,7 +36,7 @@
 //
 // Record of one chunk-head (D = dk = dv), each part row-major, the columns of every row in the
 // order rec_col gives (groups of four interleaved within blocks of 32):
-//   QG [64][D] bf16 | BG [64][D] bf16 | KG^T hi, KG^T lo [D][64] bf16 |
+//   QG [64][D] bf16 | BG [64][D] bf16 | KG^T [D][64] bf16 |
 //   T: rows 0-31 x cols 0-31, then rows 32-63 x cols 0-63 (bf16; blocks above the diagonal
 //   blocks are zero) | P hi, P lo: the same | Gamma_C [D] fp32 | padding to a KiB.
 
@@ -56,10 +56,9 @@ struct Rec {
     static constexpr int QG = 0;
     static constexpr int BG = QG + C * D * 2;
     static constexpr int A_BYTES = BG + C * D * 2;
-    static constexpr int KGT = A_BYTES;            // KG^T hi plane
-    static constexpr int KGL = KGT + D * C * 2;    // KG^T lo plane
+    static constexpr int KGT = A_BYTES;            // KG^T, one bf16 plane
     static constexpr int TRI = 32 * 32 + 32 * 64;  // elements of one plane of T or P
-    static constexpr int T = KGL + D * C * 2;      // one bf16 plane
+    static constexpr int T = KGT + D * C * 2;      // one bf16 plane
     static constexpr int P = T + TRI * 2;          // hi plane, then lo plane
     static constexpr int GC = P + 2 * TRI * 2;
     static constexpr int B_BYTES = (GC + D * 4 - A_BYTES + 1023) / 1024 * 1024;
@@ -376,12 +375,11 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
                     }
                 }
             }
-            // KG^T [DK][64] as hi and lo planes: this lane's 4 tokens of each of its channels
+            // KG^T [DK][64], rounded once: this lane's 4 tokens of each of its channels
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 const int e = ((c0 + c) * C + rec_col(I * 16 + ts * 4)) * 2;
-                cb::store_bf16_split<4>(reinterpret_cast<bf16*>(rec + R::KGT + e),
-                                        reinterpret_cast<bf16*>(rec + R::KGL + e), kgt[c]);
+                cb::store_bf16<4>(reinterpret_cast<bf16*>(rec + R::KGT + e), kgt[c]);
             }
         }
         cb::lds_barrier();
@@ -601,13 +599,13 @@ __device__ __forceinline__ int src_unit_a(int u) {
     const int row = u / UPR, un = u % UPR;
     return row * UPR + swz_unit(row, un, D * 2);
 }
-// The same for part B: KG^T hi and lo (rows of 64 tokens, 128 bytes), the three triangle planes
+// The same for part B: KG^T (rows of 64 tokens, 128 bytes), the three triangle planes
 // T, P hi, P lo (rows 0-31 of 64 bytes, rows 32-63 of 128 bytes), then Gamma_C and padding as
 // they are.
 template <int D>
 __device__ __forceinline__ int src_unit_b(int u) {
     using R = Rec<D>;
-    constexpr int UK = 2 * D * C * 2 / 16;      // units of the two KG^T planes
+    constexpr int UK = D * C * 2 / 16;          // units of the KG^T plane
     constexpr int UT = 3 * R::TRI * 2 / 16;     // units of the three triangle planes
     if (u < UK) {
         const int row = u / 8, un = u % 8;
@@ -680,7 +678,7 @@ __device__ __forceinline__ cb::Split32 split_pair(const f32x4& a, const f32x4& b
 //   start: part B of the next record starts loading into the other B buffer;
 //   X = BG S, Y = QG S (S as hi / lo), R = w.v - X, then barrier M: region A is free and the next
 //   chunk's part A, w and v start loading;
-//   U = T R (R as hi / lo), S <- Gamma_C S + KG^T U (KG^T as hi / lo), O = Y + P U (P as hi / lo);
+//   U = T R (R as hi / lo), S <- Gamma_C S + KG^T U (U as hi / lo), O = Y + P U (P as hi / lo);
 //   the wave's own loads drain, barrier F publishes the next chunk's data; O is stored after F.
 // Every global access but the O stores goes straight to LDS, so a wave keeps few vector-memory
 // instructions in flight.
@@ -923,28 +921,22 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
                 mma(U[rt], ft[p], term == 0 ? rs.hi : rs.lo);
             }
         const cb::Split32 u0 = split_pair(U[0], U[1]), u1 = split_pair(U[2], U[3]);
-        // ---- S <- Gamma_C S + KG^T U, KG^T as hi / lo: per 32-token half, the key-row fragments
-        // of every tile, then each hi / lo term over all tiles (independent accumulators) ----
+        // ---- S <- Gamma_C S + KG^T U, U as hi / lo: per 32-token half, the key-row fragments of
+        // every tile, then each hi / lo term over all tiles (independent accumulators) ----
         const float* gc = reinterpret_cast<const float*>(rb + (R::GC - R::A_BYTES));
         const char* kh = rb + (R::KGT - R::A_BYTES);
-        const char* kl = rb + (R::KGL - R::A_BYTES);
 #pragma unroll
         for (int st = 0; st < KT; ++st) S[st] *= *reinterpret_cast<const f32x4*>(gc + st * 16 + g4 * 4);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const cb::Split32& us = kk == 0 ? u0 : u1;
-            Frag<bf16> fkh[KT], fkl[KT];
+            Frag<bf16> fkh[KT];
 #pragma unroll
-            for (int st = 0; st < KT; ++st) {
-                fkh[st] = frag_perm(kh, st * 16 + l16, kk, g4, 128);
-                fkl[st] = frag_perm(kl, st * 16 + l16, kk, g4, 128);
-            }
+            for (int st = 0; st < KT; ++st) fkh[st] = frag_perm(kh, st * 16 + l16, kk, g4, 128);
 #pragma unroll
             for (int st = 0; st < KT; ++st) mma(S[st], fkh[st], us.hi);
 #pragma unroll
             for (int st = 0; st < KT; ++st) mma(S[st], fkh[st], us.lo);
-#pragma unroll
-            for (int st = 0; st < KT; ++st) mma(S[st], fkl[st], us.hi);
         }
         // ---- O = Y + P U, term by term over the blocks as for U ----
         if constexpr (MODE == kOut) {

@@ -143,7 +143,7 @@ gdn2_status_t gdn2_chunk_fwd_logits(const void* q, const void* k, const void* v,
  * gdn2_chunk_fwd_split_workspace_bytes -- bytes of device workspace that the
  * two-kernel form of gdn2_chunk_fwd needs for these sizes on the current device:
  * the chunk records of one batch of about a thousand (sequence, head, chunk)
- * triples, 84,992 bytes each at dk = dv = 128 (52,224 at 64), plus one fp32
+ * triples, 68,608 bytes each at dk = dv = 128 (44,032 at 64), plus one fp32
  * state [B, H, dk, dv].  When the (sequence, head, 64 value columns) chains
  * fill at most half of the device's compute units and the sequences hold at
  * least 32 chunks, the form instead cuts every sequence into segments walked in
