@@ -13,15 +13,16 @@
 // S-products depends on the chunk's own tokens only, so it is formed for every chunk at once:
 //
 //   * local_kernel: one workgroup per run of consecutive chunks of a (sequence, head), the next
-//     chunk's inputs loaded one chunk ahead.  Per chunk it forms QG, BG, KG^T, Gamma_C, P and T -- the decay pivoting,
-//     the A / P products and the triangular inverse of the fused forward (gdn2_bf16_ops.h) --
-//     and writes them as one record.
-//   * state_kernel: one workgroup of four waves per (sequence, head, 64 value columns); wave w
-//     owns 16 columns of the state for all dk rows, in MFMA accumulators, for the whole
-//     sequence.  Per chunk: R = w.v - BG S and Y = QG S (S as a hi / lo bf16 pair), U = T R,
-//     O = Y + P U, S <- Gamma_C S + KG^T U (U as a hi / lo pair), all in that wave's
-//     registers; the record, w and v go from global memory straight into LDS (no register
-//     staging), the next chunk's parts loading while this one is computed.
+//     chunk's inputs loaded one chunk ahead.  Per chunk it forms QG, BG, KG^T, Gamma_C, P and T
+//     -- the decay pivoting, the A / P products and the triangular inverse of the fused forward
+//     (gdn2_bf16_ops.h) -- and writes them as one record.
+//   * state_kernel: one workgroup of four waves per (sequence, head); wave w owns dv / 4 columns
+//     of the state (two 16-column tiles at d = 128) for all dk rows, in MFMA accumulators, for
+//     the whole sequence, so that each operand fragment it reads from LDS serves both tiles.
+//     Per chunk: R = w.v - BG S and Y = QG S (S as a hi / lo bf16 pair), U = T R, O = Y + P U,
+//     S <- Gamma_C S + KG^T U (U as a hi / lo pair), all in that wave's registers; the record,
+//     w and v go from global memory straight into LDS (no register staging), the next chunk's
+//     parts loading while this one is computed.
 //
 // The host walks the chunks in batches of about a thousand chunk-heads: the local kernel for a
 // batch, then the state kernel for it, so a batch's records (67 KiB per chunk-head at d = 128)
@@ -578,18 +579,24 @@ __device__ __forceinline__ int swz_unit(int row, int unit, int rb) {
 }
 
 // LDS of the state kernel.  Region A (single: its next contents load once every wave is past X,
-// Y and R): part A of the record (QG, BG), then w and v of the workgroup's 64 value columns
-// ([64 tokens][64 columns] bf16 each).  Then two buffers for part B of the record (the next
-// chunk's copy loads during this chunk).
+// Y and R): part A of the record (QG, BG), then w and v of the workgroup's WGC value columns
+// ([64 tokens][WGC columns] bf16 each).  Then two buffers for part B of the record (the next
+// chunk's copy loads during this chunk).  A workgroup covers all D value columns: each of its
+// four waves owns CT = D / 64 tiles of 16 columns, so that every operand fragment read from LDS
+// feeds CT products.
 template <int D>
 struct StateCfg {
     using R = Rec<D>;
+    static constexpr int CT = D / 64;                 // 16-column tiles per wave
+    static constexpr int WGC = 64 * CT;               // value columns per workgroup
+    static constexpr int WRB = WGC * 2;               // bytes of one token's w (or v) row
     static constexpr int A = 0;
-    static constexpr int WV = R::A_BYTES;              // w, then v: 8 KiB each
-    static constexpr int A_BYTES = R::A_BYTES + 2 * C * 64 * 2;
+    static constexpr int WV = R::A_BYTES;             // w, then v: C * WRB bytes each
+    static constexpr int A_BYTES = R::A_BYTES + 2 * C * WRB;
     static constexpr int B0 = A_BYTES;
     static constexpr int BYTES = A_BYTES + 2 * R::B_BYTES;
     static_assert(BYTES <= 163840, "LDS budget exceeded");
+    static_assert(WGC == D, "a workgroup covers every value column");
 };
 
 // Record unit staged at LDS unit u of part A (QG then BG, rows of 2 D bytes, each swizzled).
@@ -622,9 +629,9 @@ __device__ __forceinline__ int src_unit_b(int u) {
     }
     return u;
 }
-// w and v tiles: token t's 64 columns are a 128-byte row; its eight 16-byte units are permuted
-// by XOR with 2 ((t / 4) % 4), so that the four token rows one read of the accumulator layout
-// touches (4 apart, each 32 bytes of one wave's columns) fall on distinct banks.
+// w and v tiles: token t's WGC columns are a row of WRB bytes; its 16-byte units are permuted by
+// XOR with 2 ((t / 4) % 4), so that the four token rows one read of the accumulator layout
+// touches (4 apart, each 32 bytes of one column tile) fall on distinct banks.
 __device__ __forceinline__ int wv_unit(int t, int u) { return u ^ (((t >> 2) & 3) << 1); }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -673,8 +680,9 @@ __device__ __forceinline__ Frag<bf16> frag_tri(const char* plane, int row, int k
 // hi / lo K = 32 operands of an accumulator pair (permuted slot map)
 __device__ __forceinline__ cb::Split32 split_pair(const f32x4& a, const f32x4& b) { return cb::split32(a, b); }
 
-// Four waves per (sequence, head, 64 value columns); wave w owns 16 columns of the state for all
-// D rows, in MFMA accumulators, for the whole run of chunks.  Per chunk, two LDS-only barriers:
+// Four waves per (sequence, head); wave w owns the 16-column tiles CT w .. CT w + CT - 1 of the
+// state for all D rows, in MFMA accumulators, for the whole run of chunks; every fragment a wave
+// reads serves its CT tiles.  Per chunk, two LDS-only barriers:
 //   start: part B of the next record starts loading into the other B buffer;
 //   X = BG S, Y = QG S (S as hi / lo), R = w.v - X, then barrier M: region A is free and the next
 //   chunk's part A, w and v start loading;
@@ -704,6 +712,7 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
     using R = Rec<D>;
     constexpr int KT = D / 16;           // 16-row key tiles of the state
     constexpr int KK = KT / 2;           // 32-row steps over the keys
+    constexpr int CT = Cf::CT, WGC = Cf::WGC, WRB = Cf::WRB;
     constexpr int NLA = R::A_BYTES / 1024, NLB = R::B_BYTES / 1024;
     __shared__ __attribute__((aligned(1024))) char smem[Cf::BYTES];
 
@@ -733,26 +742,28 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
     // value slice of the same index all the same, and unused)
     const bool homog = MODE == kTrans && slice < nslices;
     const int vslice = slice < nslices ? slice : slice - nslices;
-    const int col = vslice * 64 + wave * 16 + l16;  // this lane's state / value column
+    // this lane's state / value column in tile c of the wave
+    auto colc = [&](int c) { return vslice * WGC + (wave * CT + c) * 16 + l16; };
     const int64_t tok_stride_v = (int64_t)H * D;
     const char* rec0 = recs + ((int64_t)bh * nb_all + s0) * R::BYTES;
     StageOffsets<NLA> soa;
     StageOffsets<NLB> sob;
     soa.init(wave, lane, [](int u) { return src_unit_a<D>(u); });
     sob.init(wave, lane, [](int u) { return src_unit_b<D>(u); });
-    // w and v of chunk n into region A: 16 loads of 1 KiB (8 tokens x 64 columns of one tensor),
-    // wave w taking loads w, w + 4, w + 8, w + 12; lane l takes token 8 j + l / 8, LDS unit l % 8
-    // of its row (swizzled: the source unit is wv_unit of it).  Tokens past the end of the
+    // w and v of chunk n into region A: 16 CT loads of 1 KiB (TPL tokens x WGC columns of one
+    // tensor), wave w taking loads w, w + 4, ...; lane l takes token TPL part + l / UPR, LDS unit
+    // l % UPR of its row (swizzled: the source unit is wv_unit of it).  Tokens past the end of the
     // sequence read its last token (zeroed in R).
-    const int wv_t = lane >> 3, wv_u = lane & 7;
+    constexpr int UPR = WRB / 16, TPL = 1024 / WRB, LPT = C / TPL;  // units per row, tokens and loads per tensor
+    const int wv_t = lane / UPR, wv_u = lane % UPR;
     auto stage_wv = [&](int n) {
         const int t0 = n * C;
         const int last = min(C, Tlen - t0) - 1;
-        const int64_t chunk = (tok0 + t0) * tok_stride_v + (int64_t)h * D + vslice * 64;
+        const int64_t chunk = (tok0 + t0) * tok_stride_v + (int64_t)h * D + vslice * WGC;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int jj = j * 4 + wave, tensor = jj >> 3, part = jj & 7;
-            const int t = part * 8 + wv_t;
+        for (int j = 0; j < 2 * LPT / 4; ++j) {
+            const int jj = j * 4 + wave, tensor = jj / LPT, part = jj % LPT;
+            const int t = part * TPL + wv_t;
             const bf16* src = (tensor ? v : wgate) + chunk + (int64_t)min(t, last) * tok_stride_v + wv_unit(t, wv_u) * 8;
             __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
                                              (lds_void*)(smem + Cf::WV + jj * 1024), 16, 0, 0);
@@ -777,21 +788,24 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
             sob.issue(rec0 + (int64_t)i * R::BYTES + R::A_BYTES, dst, wave);
     };
 
-    // the state's 16 columns of this wave, all D rows: tile st, lane (n, g) holds S[16 st + 4 g + r][col]
-    f32x4 S[KT];
+    // the state's CT x 16 columns of this wave, all D rows: tile (c, st), lane (n, g) holds
+    // S[16 st + 4 g + r][colc(c)]
+    f32x4 S[CT][KT];
     {
         const float* sin = starts ? starts + (int64_t)seg * BH * D * D : state_in;
 #pragma unroll
-        for (int st = 0; st < KT; ++st) {
+        for (int c = 0; c < CT; ++c)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = st * 16 + g4 * 4 + r;
-                if constexpr (MODE == kTrans)
-                    S[st][r] = homog && row == col ? 1.f : 0.f;
-                else
-                    S[st][r] = sin ? sin[((int64_t)bh * D + row) * D + col] : 0.f;
+            for (int st = 0; st < KT; ++st) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = st * 16 + g4 * 4 + r;
+                    if constexpr (MODE == kTrans)
+                        S[c][st][r] = homog && row == colc(c) ? 1.f : 0.f;
+                    else
+                        S[c][st][r] = sin ? sin[((int64_t)bh * D + row) * D + colc(c)] : 0.f;
+                }
             }
-        }
     }
 
     // O of a chunk through a buffer resource: the chunk's first element of this head as a uniform
@@ -799,24 +813,27 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
     // end of the sequence), this lane's column and token group as a 32-bit offset and each (tile,
     // row) step as a scalar offset -- no per-store vector address arithmetic.  Lane (n, g) of
     // tile rt holds token 16 rt + 4 g + r.
-    const uint32_t lane_tok = (uint32_t)(g4 * 4 * tok_stride_v + col);  // elements
-    auto store_o = [&](int n, const f32x4 (&Y)[4]) {
+    auto store_o = [&](int n, const f32x4 (&Y)[CT][4]) {
         const int t0 = n * C;
         const int ntok = min(C, Tlen - t0);
         const auto ro = __builtin_amdgcn_make_buffer_rsrc(o + (tok0 + t0) * tok_stride_v + (int64_t)h * D, 0,
                                                           ntok * (int)tok_stride_v * (int)sizeof(OutT), 0x00020000);
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
+        for (int c = 0; c < CT; ++c) {
+            const uint32_t lane_tok = (uint32_t)(g4 * 4 * tok_stride_v + colc(c));  // elements
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int so = (rt * 16 + r) * (int)tok_stride_v * (int)sizeof(OutT);
-                if constexpr (sizeof(OutT) == 4)
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, (float)Y[rt][r]), ro,
-                                                          lane_tok * 4, so, 0);
-                else
-                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, from_f32<bf16>(Y[rt][r])), ro,
-                                                          lane_tok * 2, so, 0);
-            }
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int so = (rt * 16 + r) * (int)tok_stride_v * (int)sizeof(OutT);
+                    if constexpr (sizeof(OutT) == 4)
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, (float)Y[c][rt][r]), ro,
+                                                              lane_tok * 4, so, 0);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, from_f32<bf16>(Y[c][rt][r])),
+                                                              ro, lane_tok * 2, so, 0);
+                }
+        }
     };
 
     if (nb > 0) {
@@ -826,9 +843,7 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
     __syncthreads();  // vmcnt(0): this wave's loads have landed; the barrier publishes every wave's
 
     const char* ra = smem + Cf::A;
-    // this lane's column within the w / v rows: unit and byte offset
-    const int wcol = wave * 16 + l16, wu = wcol >> 3, wb = (wcol & 7) * 2;
-    f32x4 Y[4];
+    f32x4 Y[CT][4];
     for (int i = 0; i < nb; ++i) {
         const int n = c_begin + s0 + i;
         const int t0 = n * C;
@@ -839,10 +854,12 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
         // part B of the next record into the other buffer (last read in the previous chunk)
         if (i + 1 < nb) stage_b(i + 1);
         // ---- X = BG S and Y = QG S, S as hi / lo bf16 pairs over 32 key rows; the fragments of
-        // each step are loaded one step ahead ----
-        f32x4 X[4];
+        // each step are loaded one step ahead and serve every tile of the wave ----
+        f32x4 X[CT][4];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) { X[rt] = zero4(); Y[rt] = zero4(); }
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) { X[c][rt] = zero4(); Y[c][rt] = zero4(); }
         Frag<bf16> fb[2][4], fq[2][4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
@@ -868,96 +885,120 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
                 }
             }
             // the hi products of the step for every tile, then the lo ones
-            const cb::Split32 sp = split_pair(S[2 * kk], S[2 * kk + 1]);
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                mma(X[rt], fb[kk & 1][rt], sp.hi);
-                if constexpr (MODE == kOut) mma(Y[rt], fq[kk & 1][rt], sp.hi);
-            }
+            for (int c = 0; c < CT; ++c) {
+                const cb::Split32 sp = split_pair(S[c][2 * kk], S[c][2 * kk + 1]);
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                mma(X[rt], fb[kk & 1][rt], sp.lo);
-                if constexpr (MODE == kOut) mma(Y[rt], fq[kk & 1][rt], sp.lo);
+                for (int rt = 0; rt < 4; ++rt) {
+                    mma(X[c][rt], fb[kk & 1][rt], sp.hi);
+                    if constexpr (MODE == kOut) mma(Y[c][rt], fq[kk & 1][rt], sp.hi);
+                }
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    mma(X[c][rt], fb[kk & 1][rt], sp.lo);
+                    if constexpr (MODE == kOut) mma(Y[c][rt], fq[kk & 1][rt], sp.lo);
+                }
             }
         }
         // ---- R = w.v - X from the staged w and v (tokens past the end of the sequence: zero) ----
-        f32x4 Rr[4];
+        f32x4 Rr[CT][4];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = rt * 16 + g4 * 4 + r;
-                const int off = t * 128 + wv_unit(t, wu) * 16 + wb;
-                const float wt = (float)*reinterpret_cast<const bf16*>(smem + Cf::WV + off);
-                const float vt = (float)*reinterpret_cast<const bf16*>(smem + Cf::WV + 8192 + off);
-                Rr[rt][r] = (homog ? 0.f : Gt::gate(wt) * vt) - X[rt][r];
-            }
-        if (t0 + C > Tlen) {
+        for (int c = 0; c < CT; ++c) {
+            // this lane's column within the w / v rows: unit and byte offset
+            const int wcol = (wave * CT + c) * 16 + l16, wu = wcol >> 3, wb = (wcol & 7) * 2;
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (t0 + rt * 16 + g4 * 4 + r >= Tlen) Rr[rt][r] = 0.f;
+                for (int r = 0; r < 4; ++r) {
+                    const int t = rt * 16 + g4 * 4 + r;
+                    const int off = t * WRB + wv_unit(t, wu) * 16 + wb;
+                    const float wt = (float)*reinterpret_cast<const bf16*>(smem + Cf::WV + off);
+                    const float vt = (float)*reinterpret_cast<const bf16*>(smem + Cf::WV + C * WRB + off);
+                    Rr[c][rt][r] = (homog ? 0.f : Gt::gate(wt) * vt) - X[c][rt][r];
+                }
+        }
+        if (t0 + C > Tlen) {
+#pragma unroll
+            for (int c = 0; c < CT; ++c)
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (t0 + rt * 16 + g4 * 4 + r >= Tlen) Rr[c][rt][r] = 0.f;
         }
         // barrier M: every wave is past region A; the next chunk's part A, w and v load during the
         // rest of the chunk
         cb::lds_barrier();
         if (i + 1 < nb) stage_a(i + 1);
         // ---- U = T R through 32-token halves (T is lower triangular), R as hi / lo ----
-        const cb::Split32 r0 = split_pair(Rr[0], Rr[1]), r1 = split_pair(Rr[2], Rr[3]);
-        f32x4 U[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) U[rt] = zero4();
         // term by term over the blocks in the order (0,0) (1,0) (2,0) (3,0) (2,1) (3,1), so that
         // consecutive MFMAs update different tiles
         constexpr int kOrd[6] = {0, 1, 2, 4, 3, 5};  // block index p in that order
+        cb::Split32 u0[CT], u1[CT];
 #pragma unroll
-        for (int term = 0; term < 2; ++term)
+        for (int c = 0; c < CT; ++c) {
+            const cb::Split32 r0 = split_pair(Rr[c][0], Rr[c][1]), r1 = split_pair(Rr[c][2], Rr[c][3]);
+            f32x4 U[4];
 #pragma unroll
-            for (int q6 = 0; q6 < 6; ++q6) {
-                const int p = kOrd[q6];
-                const int rt = p < 2 ? p : 2 + (p - 2) / 2, k2 = p < 2 ? 0 : (p - 2) % 2;
-                const cb::Split32& rs = k2 == 0 ? r0 : r1;
-                mma(U[rt], ft[p], term == 0 ? rs.hi : rs.lo);
-            }
-        const cb::Split32 u0 = split_pair(U[0], U[1]), u1 = split_pair(U[2], U[3]);
+            for (int rt = 0; rt < 4; ++rt) U[rt] = zero4();
+#pragma unroll
+            for (int term = 0; term < 2; ++term)
+#pragma unroll
+                for (int q6 = 0; q6 < 6; ++q6) {
+                    const int p = kOrd[q6];
+                    const int rt = p < 2 ? p : 2 + (p - 2) / 2, k2 = p < 2 ? 0 : (p - 2) % 2;
+                    const cb::Split32& rs = k2 == 0 ? r0 : r1;
+                    mma(U[rt], ft[p], term == 0 ? rs.hi : rs.lo);
+                }
+            u0[c] = split_pair(U[0], U[1]);
+            u1[c] = split_pair(U[2], U[3]);
+        }
         // ---- S <- Gamma_C S + KG^T U, U as hi / lo: per 32-token half, the key-row fragments of
         // every tile, then each hi / lo term over all tiles (independent accumulators) ----
         const float* gc = reinterpret_cast<const float*>(rb + (R::GC - R::A_BYTES));
         const char* kh = rb + (R::KGT - R::A_BYTES);
 #pragma unroll
-        for (int st = 0; st < KT; ++st) S[st] *= *reinterpret_cast<const f32x4*>(gc + st * 16 + g4 * 4);
+        for (int st = 0; st < KT; ++st) {
+            const f32x4 gv = *reinterpret_cast<const f32x4*>(gc + st * 16 + g4 * 4);
+#pragma unroll
+            for (int c = 0; c < CT; ++c) S[c][st] *= gv;
+        }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            const cb::Split32& us = kk == 0 ? u0 : u1;
             Frag<bf16> fkh[KT];
 #pragma unroll
             for (int st = 0; st < KT; ++st) fkh[st] = frag_perm(kh, st * 16 + l16, kk, g4, 128);
 #pragma unroll
-            for (int st = 0; st < KT; ++st) mma(S[st], fkh[st], us.hi);
+            for (int c = 0; c < CT; ++c) {
+                const cb::Split32& us = kk == 0 ? u0[c] : u1[c];
 #pragma unroll
-            for (int st = 0; st < KT; ++st) mma(S[st], fkh[st], us.lo);
+                for (int st = 0; st < KT; ++st) mma(S[c][st], fkh[st], us.hi);
+#pragma unroll
+                for (int st = 0; st < KT; ++st) mma(S[c][st], fkh[st], us.lo);
+            }
         }
         // ---- O = Y + P U, term by term over the blocks as for U ----
         if constexpr (MODE == kOut) {
-        Frag<bf16> fph[6], fpl[6];
+            Frag<bf16> fph[6], fpl[6];
 #pragma unroll
-        for (int p = 0; p < 6; ++p) {
-            const int rt = p < 2 ? p : 2 + (p - 2) / 2, k2 = p < 2 ? 0 : (p - 2) % 2;
-            fph[p] = frag_tri(ph, rt * 16 + l16, k2, g4);
-            fpl[p] = frag_tri(pl, rt * 16 + l16, k2, g4);
-        }
-#pragma unroll
-        for (int term = 0; term < 3; ++term)
-#pragma unroll
-            for (int q6 = 0; q6 < 6; ++q6) {
-                const int p = kOrd[q6];
+            for (int p = 0; p < 6; ++p) {
                 const int rt = p < 2 ? p : 2 + (p - 2) / 2, k2 = p < 2 ? 0 : (p - 2) % 2;
-                const cb::Split32& us = k2 == 0 ? u0 : u1;
-                if (term == 0) mma(Y[rt], fph[p], us.hi);
-                else if (term == 1) mma(Y[rt], fph[p], us.lo);
-                else mma(Y[rt], fpl[p], us.hi);
+                fph[p] = frag_tri(ph, rt * 16 + l16, k2, g4);
+                fpl[p] = frag_tri(pl, rt * 16 + l16, k2, g4);
             }
+#pragma unroll
+            for (int c = 0; c < CT; ++c)
+#pragma unroll
+                for (int term = 0; term < 3; ++term)
+#pragma unroll
+                    for (int q6 = 0; q6 < 6; ++q6) {
+                        const int p = kOrd[q6];
+                        const int rt = p < 2 ? p : 2 + (p - 2) / 2, k2 = p < 2 ? 0 : (p - 2) % 2;
+                        const cb::Split32& us = k2 == 0 ? u0[c] : u1[c];
+                        if (term == 0) mma(Y[c][rt], fph[p], us.hi);
+                        else if (term == 1) mma(Y[c][rt], fph[p], us.lo);
+                        else mma(Y[c][rt], fpl[p], us.hi);
+                    }
         }
         // barrier F: this wave's loads (the next chunk's parts A and B, w and v, the previous
         // chunk's O stores) have drained; the barrier publishes every wave's and frees part B of
@@ -967,18 +1008,23 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
     }
 
     if constexpr (MODE == kTrans) {
-        float* dst = trans + ((int64_t)chain * D) * (2 * D) + slice * 64 + wave * 16 + l16;
 #pragma unroll
-        for (int st = 0; st < KT; ++st)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(int64_t)(st * 16 + g4 * 4 + r) * (2 * D)] = S[st][r];
-    } else {
-        if (state_out && s0 + nb == nb_all) {
+        for (int c = 0; c < CT; ++c) {
+            float* dst = trans + ((int64_t)chain * D) * (2 * D) + slice * WGC + (wave * CT + c) * 16 + l16;
 #pragma unroll
             for (int st = 0; st < KT; ++st)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    state_out[((int64_t)bh * D + st * 16 + g4 * 4 + r) * D + col] = S[st][r];
+                for (int r = 0; r < 4; ++r) dst[(int64_t)(st * 16 + g4 * 4 + r) * (2 * D)] = S[c][st][r];
+        }
+    } else {
+        if (state_out && s0 + nb == nb_all) {
+#pragma unroll
+            for (int c = 0; c < CT; ++c)
+#pragma unroll
+                for (int st = 0; st < KT; ++st)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        state_out[((int64_t)bh * D + st * 16 + g4 * 4 + r) * D + colc(c)] = S[c][st][r];
         }
     }
 }
@@ -987,44 +1033,80 @@ __global__ __launch_bounds__(NT_STATE, 1) void state_kernel(
 // S_g = A_{g-1} S_{g-1} + B_{g-1} (the transitions of the state kernel's kTrans mode, [D][2 D]
 // per segment and head), written to starts[g] as [D][D].  One workgroup per (head, 16 state
 // columns); the columns of a state are independent, so each workgroup walks the segments on
-// its own, in fp32.
+// its own, in fp32: wave w forms the 16-row tiles w, w + 4, .. of A_{g-1} S_{g-1} with fp32 MFMA
+// (16 x 16 x 4), the rows of A_{g-1} as its A operands (four contraction steps per 16-byte load)
+// and S_{g-1} transposed in LDS as the B operands; the next transition's rows load during the
+// current step.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ trans, const float* s_init,
                                                       float* __restrict__ starts, int BH, int nseg) {
-    constexpr int TPR = 256 / D;   // threads per state row
-    constexpr int CPT = 16 / TPR;  // columns per thread
-    __shared__ float sS[D][16];
+    constexpr int RT = D / 16;            // 16-row tiles of the state
+    constexpr int TPW = (RT + 3) / 4;     // tiles per wave
+    constexpr int KQ = D / 16;            // 16-wide contraction groups: k = 16 q + 4 g + e
+    constexpr int SR = D + 4;             // floats per row of S^T in LDS (padded: distinct banks)
+    __shared__ __attribute__((aligned(16))) float sT[2][16][SR];
     const int bh = blockIdx.x / (D / 16), ct = blockIdx.x % (D / 16);
-    const int tid = threadIdx.x, r = tid / TPR, c0 = (tid % TPR) * CPT;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-        const float x = s_init ? s_init[((int64_t)bh * D + r) * D + ct * 16 + c0 + c] : 0.f;
-        sS[r][c0 + c] = x;
-        starts[((int64_t)bh * D + r) * D + ct * 16 + c0 + c] = x;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    for (int x = tid; x < D * 16; x += 256) {
+        const int r = x / 16, c = x % 16;
+        const float v = s_init ? s_init[((int64_t)bh * D + r) * D + ct * 16 + c] : 0.f;
+        starts[((int64_t)bh * D + r) * D + ct * 16 + c] = v;
+        sT[0][c][r] = v;
     }
+    // rows of A_{g-1} for this wave's tiles: lane (i, g) holds A[16 rt + i][16 q + 4 g .. + 3]
+    auto load_a = [&](int g, f32x4 (&a)[TPW][KQ]) {
+        const float* tr = trans + ((int64_t)(g - 1) * BH + bh) * D * (2 * D);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int rt = wave + 4 * t;
+#pragma unroll
+            for (int q = 0; q < KQ; ++q)
+                a[t][q] = rt < RT ? *reinterpret_cast<const f32x4*>(tr + (int64_t)(16 * rt + l16) * (2 * D) + 16 * q + 4 * g4)
+                                  : zero4();
+        }
+    };
+    f32x4 a[TPW][KQ];
+    if (nseg > 1) load_a(1, a);
+    __syncthreads();
     for (int g = 1; g < nseg; ++g) {
-        __syncthreads();
-        const float* tr = trans + ((int64_t)(g - 1) * BH + bh) * D * (2 * D) + (int64_t)r * (2 * D);
-        float acc[CPT];
+        const int cur = (g - 1) & 1;
+        f32x4 an[TPW][KQ];
+        if (g + 1 < nseg) load_a(g + 1, an);
+        const float* tr = trans + ((int64_t)(g - 1) * BH + bh) * D * (2 * D);
+        f32x4 acc[TPW];
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) acc[c] = tr[D + ct * 16 + c0 + c];
-        for (int k = 0; k < D; k += 4) {
-            const float4 a = *reinterpret_cast<const float4*>(tr + k);
+        for (int t = 0; t < TPW; ++t) {
+            const int rt = wave + 4 * t;
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) {
-                acc[c] = fmaf(a.x, sS[k][c0 + c], acc[c]);
-                acc[c] = fmaf(a.y, sS[k + 1][c0 + c], acc[c]);
-                acc[c] = fmaf(a.z, sS[k + 2][c0 + c], acc[c]);
-                acc[c] = fmaf(a.w, sS[k + 3][c0 + c], acc[c]);
+            for (int r = 0; r < 4; ++r)
+                acc[t][r] = rt < RT ? tr[(int64_t)(16 * rt + 4 * g4 + r) * (2 * D) + D + ct * 16 + l16] : 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < KQ; ++q) {
+            const f32x4 b = *reinterpret_cast<const f32x4*>(&sT[cur][l16][16 * q + 4 * g4]);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mma_f32x4(acc[t], a[t][q][e], b[e]);
+        }
+        // S_g: lane (n, g) holds rows 16 rt + 4 g + r of column n
+        float* dst = starts + ((int64_t)g * BH + bh) * D * D + ct * 16 + l16;
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int rt = wave + 4 * t;
+            if (rt < RT) {
+                *reinterpret_cast<f32x4*>(&sT[cur ^ 1][l16][16 * rt + 4 * g4]) = acc[t];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dst[(int64_t)(16 * rt + 4 * g4 + r) * D] = acc[t][r];
             }
         }
-        __syncthreads();
-        float* dst = starts + ((int64_t)g * BH + bh) * D * D + (int64_t)r * D + ct * 16 + c0;
+        if (g + 1 < nseg) {
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            sS[r][c0 + c] = acc[c];
-            dst[c] = acc[c];
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int q = 0; q < KQ; ++q) a[t][q] = an[t][q];
         }
+        __syncthreads();
     }
 }
 
@@ -1042,18 +1124,30 @@ int64_t split_batch_chunks(int64_t BH, int64_t nchunks) {
     return c < nchunks ? c : nchunks;
 }
 
-// Segments of the few-chains form: when the (sequence, head, 64-column) chains fill at most
-// half of the compute units, each sequence is cut into segments walked in parallel (enough of
-// them that the segments' chains fill the compute units, each at least 16 chunks long), joined
-// by their transitions.  1: the batched form.
+// Segments of the few-chains form.  Each (sequence, head) is one chain of the state pass (one
+// workgroup).  Cut into g segments of L chunks (at least 16), the form runs a transition pass
+// (2 workgroups per chain and segment but the last) and then the forward pass (one per chain
+// and segment), each L chunk steps long per round of workgroups over the compute units, plus a
+// serial combine of g - 1 steps; in batches, each chain walks all its chunks.  Cost in chunk
+// steps: batches ceil(chains / cus) nchunks; segments (transition rounds + forward rounds) L +
+// 2 (g - 1).  The cheapest wins (two segments never do: they walk as many chunk steps as one).
+// 1: the batched form.
 int64_t split_segments(int64_t BH, int64_t nchunks, int64_t d, int64_t cus) {
-    const int64_t chains = BH * (d / 64);
-    if (chains < 1 || 2 * chains > cus) return 1;
-    int64_t g = cus / chains;
-    if (g > nchunks / 16) g = nchunks / 16;
-    if (g < 2) return 1;
-    const int64_t len = (nchunks + g - 1) / g;  // chunks per segment; no segment left empty
-    return (nchunks + len - 1) / len;
+    (void)d;  // a workgroup covers all dv columns at either head size
+    const int64_t chains = BH;
+    if (chains < 1 || cus < 1 || nchunks < 1) return 1;
+    auto rounds = [&](int64_t wg) { return (wg + cus - 1) / cus; };
+    int64_t best_g = 1, best = rounds(chains) * nchunks;
+    for (int64_t g = 2; g <= nchunks / 16 && g <= 64; ++g) {
+        const int64_t len = (nchunks + g - 1) / g;   // chunks per segment
+        const int64_t gg = (nchunks + len - 1) / len;  // segments, none left empty
+        const int64_t cost = (rounds(2 * (gg - 1) * chains) + rounds(gg * chains)) * len + 2 * (gg - 1);
+        if (cost < best) {
+            best = cost;
+            best_g = gg;
+        }
+    }
+    return best_g;
 }
 
 size_t split_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d, int64_t cus) {
@@ -1072,7 +1166,7 @@ template <typename OutT, int D, typename Gt>
 hipError_t launch_split_d(const ChunkArgs& a, char* ws) {
     const int64_t BH = a.B * a.H;
     const int nc = (int)((a.T + 63) / 64);
-    const int nslices = D / 64;
+    const int nslices = D / sp::StateCfg<D>::WGC;  // 1: a workgroup covers all value columns
     hipStream_t st = (hipStream_t)a.stream;
     const int g = (int)split_segments(BH, nc, D, a.cus);
     if (g > 1) {

@@ -144,9 +144,10 @@ gdn2_status_t gdn2_chunk_fwd_logits(const void* q, const void* k, const void* v,
  * two-kernel form of gdn2_chunk_fwd needs for these sizes on the current device:
  * the chunk records of one batch of about a thousand (sequence, head, chunk)
  * triples, 68,608 bytes each at dk = dv = 128 (44,032 at 64), plus one fp32
- * state [B, H, dk, dv].  When the (sequence, head, 64 value columns) chains
- * fill at most half of the device's compute units and the sequences hold at
- * least 32 chunks, the form instead cuts every sequence into segments walked in
+ * state [B, H, dk, dv].  When the (sequence, head) chains (one workgroup of
+ * the state pass each) fill at most half of the device's compute units and the
+ * sequences hold at least 32 chunks, the form instead cuts every sequence into
+ * segments walked in
  * parallel and joined through their state transitions: it then needs every
  * chunk's record plus, per (sequence, head), a [dk][2 dv] fp32 transition for
  * every segment but the last and a [dk][dv] fp32 start state for every

@@ -203,16 +203,20 @@ def test_status_values_follow_the_boundary_table(lib):
 
 
 def split_segments(B, T, H, d, cus=256):
-    """Segments of the few-chains form: with (sequence, head, 64-column) chains filling at most
-    half of the compute units, enough segments of at least 16 chunks to fill them; else 1."""
-    nc, chains = (T + 63) // 64, B * H * (d // 64)
-    if 2 * chains > cus:
-        return 1
-    g = min(cus // chains, nc // 16)
-    if g < 2:
-        return 1
-    ln = -(-nc // g)
-    return -(-nc // ln)
+    """Segments of the few-chains form, by the library's cost model: each (sequence, head) is a
+    chain; g segments of L chunks cost (transition rounds + forward rounds) * L + 2 (g - 1) chunk
+    steps (two workgroups per chain for the transitions of all segments but the last), batches
+    ceil(chains / cus) * nchunks; the cheapest wins (1: batches)."""
+    nc, chains = (T + 63) // 64, B * H
+    rounds = lambda wg: -(-wg // cus)
+    best_g, best = 1, rounds(chains) * nc
+    for g in range(2, min(nc // 16, 64) + 1):
+        ln = -(-nc // g)
+        gg = -(-nc // ln)
+        cost = (rounds(2 * (gg - 1) * chains) + rounds(gg * chains)) * ln + 2 * (gg - 1)
+        if cost < best:
+            best, best_g = cost, gg
+    return best_g
 
 
 def split_ws_bytes(B, T, H, d):
@@ -236,7 +240,8 @@ def test_fwd_workspace_bytes(lib):
     assert split_ws_bytes(1, 64, 1, 128) - 128 * 128 * 4 == 68608
     assert split_ws_bytes(1, 64, 1, 64) - 64 * 64 * 4 == 44032
     assert [split_segments(*x) for x in ((1, 32768, 16, 128), (8, 4096, 16, 128), (1, 5000, 3, 64),
-                                         (2, 2100, 16, 128), (1, 1000, 1, 64))] == [8, 1, 4, 2, 1]
+                                         (2, 2100, 16, 128), (1, 1000, 1, 64), (4, 8192, 16, 128),
+                                         (2, 16384, 16, 128))] == [16, 1, 4, 1, 1, 3, 8]
     for (B, T, H, d) in ((1, 1, 1, 64), (8, 4096, 16, 128), (1, 32768, 16, 128), (3, 1000, 5, 64),
                          (1, 5000, 3, 64), (2, 2100, 16, 128)):
         assert lib.gdn2_chunk_fwd_split_workspace_bytes(B, T, H, d, d, BF16) == split_ws_bytes(B, T, H, d)

@@ -44,8 +44,8 @@ CASES = [
     (128, 2, 300, 3, True, 506, (-6.0, -1.0)),   # strong decay: every chunk takes the split path
     (64, 1, 190, 2, False, 507, (-6.0, -1.0)),
     (128, 1, 256, 2, False, 508, (-120.0, -90.0)),  # logits below -88: alpha is exactly 0
-    (128, 1, 2600, 2, True, 509, (2.0, 7.0)),    # two-kernel form in 2 segments
-    (64, 1, 2100, 3, False, 510, (-6.0, -1.0)),  # the same, strong decay
+    (128, 1, 3600, 2, True, 509, (2.0, 7.0)),    # two-kernel form in 3 segments
+    (64, 1, 3100, 3, False, 510, (-6.0, -1.0)),  # the same, strong decay
 ]
 
 

@@ -132,10 +132,10 @@ def _split_final_state_case(B, T, H, d, with_s0, final, label, g_lo=None, g_hi=N
 
 
 # Sizes whose chunk-heads exceed one batch of the two-kernel form (about 1024), with chains
-# enough (more than half the compute units) that it runs in batches, ragged tails: the state is
-# carried between batches, through final_state or the workspace.
+# enough (more than half the compute units) or too few chunks to cut, so that it runs in batches,
+# ragged tails: the state is carried between batches, through final_state or the workspace.
 @pytest.mark.parametrize("B,T,H,d,with_s0,final", [
-    (2, 2100, 48, 128, True, "new"),      # 34 chunks x 96 heads: batches of 10 chunks
+    (3, 2100, 48, 128, True, "new"),      # 33 chunks x 144 heads: batches of 7 chunks
     (9, 1500, 16, 128, False, "none"),    # no final state: carried in the workspace
     (3, 1500, 16, 128, True, "inplace"),  # final state written over the initial state
 ])
@@ -144,15 +144,15 @@ def test_split_across_batches(B, T, H, d, with_s0, final):
 
 
 # Few chains: each sequence is cut into segments walked in parallel, joined by their transitions
-# (2 to 4 segments here, ragged or whole last chunks, strong decay in one case).
+# (3 or 4 segments here, ragged or whole last chunks, strong decay in one case).
 @pytest.mark.parametrize("B,T,H,d,with_s0,final,g_lo,g_hi", [
     (1, 5000, 3, 64, True, "new", None, None),        # 4 segments of 20 chunks, the last partial
-    (2, 2100, 16, 128, True, "inplace", None, None),  # 2 segments of 17 chunks
+    (2, 3200, 16, 128, True, "inplace", None, None),  # 3 segments of 17, 17 and 16 chunks
     (1, 4196, 4, 128, False, "none", None, None),     # 4 segments, no final state
-    (1, 2560, 2, 128, True, "new", None, None),       # 2 segments of 20 whole chunks
-    (1, 2100, 2, 128, True, "new", -60.0, -20.0),     # strong decay: every chunk pivots
-    (1, 2048, 2, 128, True, "new", None, None),       # the fewest chunks cut: 2 segments of 16
-    (1, 2049, 2, 128, True, "new", None, None),       # the same plus a one-token last chunk
+    (1, 3840, 2, 128, True, "new", None, None),       # 3 segments of 20 whole chunks
+    (1, 3100, 2, 128, True, "new", -60.0, -20.0),     # strong decay: every chunk pivots
+    (1, 3072, 2, 128, True, "new", None, None),       # the fewest chunks cut: 3 segments of 16
+    (1, 3073, 2, 128, True, "new", None, None),       # 49 chunks, the last of one token
 ])
 def test_split_segments(B, T, H, d, with_s0, final, g_lo, g_hi):
     _split_final_state_case(B, T, H, d, with_s0, final, "segments", g_lo, g_hi)
