@@ -158,6 +158,24 @@ def test_split_segments(B, T, H, d, with_s0, final, g_lo, g_hi):
     _split_final_state_case(B, T, H, d, with_s0, final, "segments", g_lo, g_hi)
 
 
+# The fused kernel's value-column slice follows B * H (16, 32 or 64 columns, so that the
+# workgroups fill the compute units), and with it the number of waves that hold state columns
+# (one per 16 columns).  One case per width and head size, ragged last chunk, initial state.
+@pytest.mark.parametrize("d,B,H,dvs", [
+    (128, 4, 16, 32),   # B H = 64: two state waves of four
+    (128, 1, 5, 16),    # B H = 5: one state wave
+    (64, 8, 16, 32),    # B H = 128 at d = 64
+    (64, 16, 16, 64),   # B H = 256 at d = 64: every state wave
+])
+def test_fused_slice_widths(d, B, H, dvs):
+    wl = dataclasses.replace(W.TRAIN_4K, name="slices", dk=d, dv=d, H=H, s0_std=0.05)
+    say("case: fused d=%d B=%d H=%d (slices of %d columns)" % (d, B, H, dvs))
+    inp = W.make_inputs(wl, seed=71, B=B, T=200)
+    o, s = run_gpu(inp, fused=True, output_final_state=True)
+    o_ref, s_ref = run_oracle(inp)
+    check(o, s, o_ref, s_ref, TOL_BF16, "fused, %d-column slices" % dvs)
+
+
 def test_split_and_fused_agree():
     """The two forms compute the same function: on the same inputs their outputs differ by no
     more than the bar allows each of them against the oracle."""
