@@ -304,6 +304,10 @@ __device__ __forceinline__ void strong_ap_body(char* smem, Src src, int ntok, Pu
 #pragma unroll
     for (int c = 0; c < CPL; ++c) x16[c] = __shfl_xor(al[c][0] * al[c][1] * al[c][2] * al[c][3], 16);
     lds_barrier();  // the level tiles below reuse the group-tile rows
+    // Each wave forms the products of its own channel half (the contraction splits over channels,
+    // and every level's masked sum is linear), so a level needs no barrier: the wave writes its
+    // half of the block's level tiles and reads back only that half.  Waves I and I + 4 then sum
+    // their partial products once.
     bf16* lv = sX + (I * 48) * LDK;  // rows: [0,16) A rows, [16,32) P rows, [32,48) columns
     f32x4 dA = zero4(), dAn = zero4(), dP = zero4();
 #pragma unroll
@@ -356,28 +360,53 @@ __device__ __forceinline__ void strong_ap_body(char* smem, Src src, int ntok, Pu
             store_bf16<CPL>(lv + (16 + i) * LDK + c0, rp);
             store_bf16<CPL>(lv + (32 + i) * LDK + c0, cl);
         }
+        // the wave's own writes before its reads (LDS keeps one wave's accesses in order)
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+        // tA: lane holds A[l16][4 g4 + r] of the block over this channel half; tAn: A[4 g4 + r][l16];
+        // tP like tA
+        f32x4 tA = zero4(), tAn = zero4(), tP = zero4();
+#pragma unroll
+        for (int k2 = 0; k2 < DK / 64; ++k2) {
+            const int kc = (hf * (DK / 64) + k2) * 32 + g4 * 8;
+            const Frag<bf16> fk = load_contig(lv + (32 + l16) * LDK + kc);
+            const Frag<bf16> fq = load_contig(lv + (16 + l16) * LDK + kc);
+            mma(tP, fk, fq);
+            if (L < 4) {
+                const Frag<bf16> fa = load_contig(lv + l16 * LDK + kc);
+                mma(tA, fk, fa);
+                mma(tAn, fa, fk);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = l16, j = g4 * 4 + r;
+            const bool keep = L < 4 ? (i / size == j / size) : (i == j);
+            if (keep) { dA[r] += tA[r]; dAn[r] += tAn[r]; dP[r] += tP[r]; }
+        }
+        // the next level overwrites the tiles this wave has just read
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+    }
+    // waves 4-7 hand their partial sums to waves 0-3 through the upper channel half of their own
+    // block's level rows (DK bytes a row, 16 bytes per lane and sum: DK / 16 lanes a row); the
+    // second barrier keeps these reads ahead of T's diagonal blocks, whose rows overlap
+    {
+        constexpr int LPR = DK / 16, RPS = 64 / LPR;  // lanes per row, rows per sum
+        static_assert(3 * RPS <= 48, "the partial sums fit the block's level rows");
+        char* hand = reinterpret_cast<char*>(lv + DK / 2) + (lane / LPR) * LDK * 2 + (lane % LPR) * 16;
+        if (wave >= 4) {
+            *reinterpret_cast<f32x4*>(hand) = dA;
+            *reinterpret_cast<f32x4*>(hand + RPS * LDK * 2) = dAn;
+            *reinterpret_cast<f32x4*>(hand + 2 * RPS * LDK * 2) = dP;
+        }
         lds_barrier();
         if (wave < 4) {
-            // tA: lane holds A[l16][4 g4 + r] of the block; tAn: A[4 g4 + r][l16]; tP like tA
-            f32x4 tA = zero4(), tAn = zero4(), tP = zero4();
-#pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) {
-                const int kc = kk * 32 + g4 * 8;
-                const Frag<bf16> fk = load_contig(lv + (32 + l16) * LDK + kc);
-                const Frag<bf16> fq = load_contig(lv + (16 + l16) * LDK + kc);
-                mma(tP, fk, fq);
-                if (L < 4) {
-                    const Frag<bf16> fa = load_contig(lv + l16 * LDK + kc);
-                    mma(tA, fk, fa);
-                    mma(tAn, fa, fk);
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = l16, j = g4 * 4 + r;
-                const bool keep = L < 4 ? (i / size == j / size) : (i == j);
-                if (keep) { dA[r] += tA[r]; dAn[r] += tAn[r]; dP[r] += tP[r]; }
-            }
+            dA += *reinterpret_cast<const f32x4*>(hand);
+            dAn += *reinterpret_cast<const f32x4*>(hand + RPS * LDK * 2);
+            dP += *reinterpret_cast<const f32x4*>(hand + 2 * RPS * LDK * 2);
         }
         lds_barrier();
     }

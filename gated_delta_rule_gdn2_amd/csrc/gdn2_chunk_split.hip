@@ -1174,9 +1174,12 @@ hipError_t launch_split_d(const ChunkArgs& a, char* ws) {
         char* trans = ws + BH * nc * sp::Rec<D>::BYTES;
         float* tr = reinterpret_cast<float*>(trans);
         float* starts = tr + (int64_t)(g - 1) * BH * D * 2 * D;
-        // every chunk's record, in one launch
-        const int64_t per = (BH * nc + a.cus - 1) / a.cus;
-        const int run = (int)(per < 1 ? 1 : per > nc ? nc : per);
+        // every chunk's record, in one launch: runs of at least 8 chunks in about four rounds of
+        // workgroups, so that the hardware's dispatch evens out chunks of unequal cost (a
+        // strong-decay chunk takes about twice a mild one, and whole heads can be strong)
+        const int64_t per0 = (BH * nc + 4 * (int64_t)a.cus - 1) / (4 * (int64_t)a.cus);
+        const int64_t per = per0 < 8 ? 8 : per0;
+        const int run = (int)(per > nc ? nc : per);
         const int runs = (nc + run - 1) / run;
         hipLaunchKernelGGL((sp::local_kernel<D, Gt>), dim3((unsigned)(BH * runs)), dim3(sp::NT_LOCAL), 0, st,
                            (const bf16*)a.q, (const bf16*)a.k, (const typename Gt::Decay*)a.decay(),
