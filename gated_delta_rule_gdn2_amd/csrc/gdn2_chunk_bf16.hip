@@ -36,7 +36,8 @@
 //     U = T (w.v - Z) (= U0 - W S of the formulas above, with the product regrouped),
 //     O = Y + P U and S_next.  Waves 0-3 meanwhile start the next chunk.
 // Operands that are not bf16 numbers themselves (w.v - Z, U, P) enter the MFMAs as hi + lo
-// bf16 pairs; every product accumulates in fp32.
+// bf16 pairs, and so does k / Gamma in P on the single-pivot path (its rounding is the
+// largest single source of the output's error there); every product accumulates in fp32.
 
 #include "gdn2_bf16_ops.h"
 #include "gdn2_launch.h"
@@ -64,7 +65,7 @@ struct Cfg {
     static constexpr int PM = WVT + DVS * C * 4;              // 2 x [64][LC] P hi, lo: A,P -> O
     static constexpr int AM = PM + 2 * C * LC * 2;            // [64][LC] -A_IJ (J < I), (I + A_II)^{-1}
     static constexpr int RX = AM + C * LC * 2;                // work area, 192 rows of [LDK]:
-                                                              //   mild: K/Gamma rows 64-127
+                                                              //   mild: K/Gamma hi rows 64-127, lo 0-63
                                                               //   strong: group and level tiles
                                                               //   T = (I + A)^{-1} rows 128-
     static constexpr int TR = RX + 2 * C * LDK * 2;           // [64][LC] T, row-major: -> state pass
@@ -397,7 +398,8 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                     }
                     store_bf16<CPL>(B16(eb + m * LDK * 2), xq);
                     store_bf16<CPL>(B16(eb + G::BG + m * LDK * 2), xb);
-                    store_bf16<CPL>(B16(ebx + (C + m) * LDK * 2), xki);
+                    // KI as a hi/lo pair: hi in work rows 64-127, lo in rows 0-63 (free on this path)
+                    store_bf16_split<CPL>(B16(ebx + (C + m) * LDK * 2), B16(ebx + m * LDK * 2), xki);
                 }
             } else {
                 const int eb = opq(((I * 16 + ts * 4) * LDK + c0) * 2);
@@ -498,16 +500,20 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
 #pragma unroll
                 for (int I = 0; I < 4; ++I) {
                     const int rk = opq(((I * 16 + l16) * LDK + g4 * 8) * 2);
-                    Frag<bf16> fk[DK / 32], fq[DK / 32];
+                    Frag<bf16> fk[DK / 32], fl[DK / 32], fq[DK / 32];
 #pragma unroll
                     for (int kk = 0; kk < DK / 32; ++kk) {
                         fk[kk] = load_contig(B16(rk + G::RX + C * LDK * 2 + kk * 64));
                         fq[kk] = load_contig(B16(rk + kk * 64));
+                        fl[kk] = load_contig(B16(rk + G::RX + kk * 64));  // KI lo
                     }
                     sched_fence();
                     f32x4 pd = zero4();
 #pragma unroll
-                    for (int kk = 0; kk < DK / 32; ++kk) mma(pd, fk[kk], fq[kk]);  // P[l16][4 g4 + r]
+                    for (int kk = 0; kk < DK / 32; ++kk) {
+                        mma(pd, fk[kk], fq[kk]);  // P[l16][4 g4 + r]
+                        mma(pd, fl[kk], fq[kk]);
+                    }
                     float pp[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) pp[r] = 4 * g4 + r <= l16 ? pd[r] : 0.f;
@@ -523,18 +529,20 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                     const int Ib = wave == 4 ? 1 + pi : wave == 5 ? 2 + pi : 3;
                     const int Jb = wave == 4 ? 0 : wave == 5 ? 1 : 2 * pi;
                     f32x4 accA = zero4(), accP = zero4();
-                    Frag<bf16> fk[DK / 32], fa[DK / 32], fq[DK / 32];
+                    Frag<bf16> fk[DK / 32], fl[DK / 32], fa[DK / 32], fq[DK / 32];
 #pragma unroll
                     for (int kk = 0; kk < DK / 32; ++kk) {
                         fk[kk] = load_contig(B16(rl + G::RX + (C + Jb * 16) * LDK * 2 + kk * 64));
                         fa[kk] = load_contig(B16(rl + G::BG + Ib * 16 * LDK * 2 + kk * 64));
                         fq[kk] = load_contig(B16(rl + Ib * 16 * LDK * 2 + kk * 64));
+                        fl[kk] = load_contig(B16(rl + G::RX + Jb * 16 * LDK * 2 + kk * 64));  // KI lo
                     }
                     sched_fence();
 #pragma unroll
                     for (int kk = 0; kk < DK / 32; ++kk) {
                         mma(accA, fk[kk], fa[kk]);
                         mma(accP, fk[kk], fq[kk]);
+                        mma(accP, fl[kk], fq[kk]);
                     }
                     float a[4], pp[4];
 #pragma unroll
