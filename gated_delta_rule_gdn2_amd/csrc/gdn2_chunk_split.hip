@@ -87,9 +87,10 @@ constexpr int NT_LOCAL = 512;
 // LDS layout of the local kernel (bytes), at most 80 KiB.
 // RX: 192 rows of LDK bf16 -- mild chunk: BG rows 0-63, k / Gamma rows 64-127, QG rows 128-191;
 // strong chunk: the pivoted group and level tiles.  AM: -A below the diagonal blocks; TR, TTR:
-// the diagonal blocks of T and their transposes (the block inverses' inputs to T_C).  The block
-// decays and strong-decay votes of the element phase share AM's bytes (a barrier separates the
-// uses).
+// the diagonal blocks of T and their transposes (the block inverses' inputs to T_C); on a mild
+// chunk they first hold the lo plane of k / Gamma for P, and the block inverses are stored after
+// P.  The block decays and strong-decay votes of the element phase share AM's bytes (a barrier
+// separates the uses).
 template <int DK>
 struct LocalCfg {
     static constexpr int CPL = DK / 32;
@@ -103,7 +104,10 @@ struct LocalCfg {
     static constexpr int TR = AM + C * LC * 2;
     static constexpr int TTR = TR + C * LC * 2;
     static constexpr int BYTES = TTR + C * LC * 2;
+    static constexpr int KIL = TR;                    // mild: k / Gamma lo rows, element -> P (T's
+                                                      // diagonal blocks land there after P)
     static_assert(BYTES <= 81920, "LDS budget");
+    static_assert(KIL + C * LDK * 2 <= BYTES, "k / Gamma lo plane");
     static_assert(FLG + 32 <= TR, "votes inside AM");
 };
 
@@ -316,7 +320,8 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
                     }
                     cb::store_bf16<CPL>(B16(G::QGR + eb + m * LDK * 2), xq);
                     cb::store_bf16<CPL>(B16(G::RX + eb + m * LDK * 2), xb);
-                    cb::store_bf16<CPL>(B16(G::RX + eb + (C + m) * LDK * 2), xki);
+                    cb::store_bf16_split<CPL>(B16(G::RX + eb + (C + m) * LDK * 2), B16(G::KIL + eb + m * LDK * 2),
+                                              xki);
                     cb::store_bf16<CPL>(reinterpret_cast<bf16*>(rq + m * DK * 2), xq);
                     cb::store_bf16<CPL>(reinterpret_cast<bf16*>(rb + m * DK * 2), xb);
                 }
@@ -390,6 +395,7 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
         char* ph = rec + R::P;
         char* pl = rec + R::P + R::TRI * 2;
         auto put_p = [=](int row, int col, const float (&p)[4]) { put_split4(ph, pl, tri_index(row, col), p); };
+        f32x4 tdiag = zero4();  // mild: waves 0-3's block inverse, stored once P is formed
         if (!strong) {
             load_first(nnext, in);
             if (wave < 4) {
@@ -415,25 +421,28 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
                     nt[r] = j < l16 ? nt[r] : 0.f;
                     nn[r] = j > l16 ? nn[r] : 0.f;
                 }
-                const f32x4 t = cb::unit_lower_inverse(nt, nn, l16, g4);
-                cb::store_tdiag<G>(smem, wave, l16, g4, t);
+                tdiag = cb::unit_lower_inverse(nt, nn, l16, g4);
                 float x[4];
-                cb::acc_to_array(t, x);
+                cb::acc_to_array(tdiag, x);
                 put4(th, tri_index(wave * 16 + l16, wave * 16 + g4 * 4), x);
             } else if (wave == 7) {
 #pragma unroll
                 for (int Ib = 0; Ib < 4; ++Ib) {
                     const int rk = cb::opq(((Ib * 16 + l16) * LDK + g4 * 8) * 2);
-                    Frag<bf16> fk[DK / 32], fq[DK / 32];
+                    Frag<bf16> fk[DK / 32], fl[DK / 32], fq[DK / 32];
 #pragma unroll
                     for (int kk = 0; kk < DK / 32; ++kk) {
                         fk[kk] = load_contig(B16(rk + G::RX + C * LDK * 2 + kk * 64));
                         fq[kk] = load_contig(B16(rk + G::QGR + kk * 64));
+                        fl[kk] = load_contig(B16(rk + G::KIL + kk * 64));  // k / Gamma lo
                     }
                     cb::sched_fence();
                     f32x4 pd = zero4();
 #pragma unroll
-                    for (int kk = 0; kk < DK / 32; ++kk) mma(pd, fk[kk], fq[kk]);
+                    for (int kk = 0; kk < DK / 32; ++kk) {
+                        mma(pd, fk[kk], fq[kk]);
+                        mma(pd, fl[kk], fq[kk]);
+                    }
                     float pp[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) pp[r] = 4 * g4 + r <= l16 ? pd[r] : 0.f;
@@ -447,18 +456,20 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
                     const int Ib = wave == 4 ? 1 + pi : wave == 5 ? 2 + pi : 3;
                     const int Jb = wave == 4 ? 0 : wave == 5 ? 1 : 2 * pi;
                     f32x4 accA = zero4(), accP = zero4();
-                    Frag<bf16> fk[DK / 32], fa[DK / 32], fq[DK / 32];
+                    Frag<bf16> fk[DK / 32], fl[DK / 32], fa[DK / 32], fq[DK / 32];
 #pragma unroll
                     for (int kk = 0; kk < DK / 32; ++kk) {
                         fk[kk] = load_contig(B16(rl + G::RX + (C + Jb * 16) * LDK * 2 + kk * 64));
                         fa[kk] = load_contig(B16(rl + G::RX + Ib * 16 * LDK * 2 + kk * 64));
                         fq[kk] = load_contig(B16(rl + G::QGR + Ib * 16 * LDK * 2 + kk * 64));
+                        fl[kk] = load_contig(B16(rl + G::KIL + Jb * 16 * LDK * 2 + kk * 64));  // k / Gamma lo
                     }
                     cb::sched_fence();
 #pragma unroll
                     for (int kk = 0; kk < DK / 32; ++kk) {
                         mma(accA, fk[kk], fa[kk]);
                         mma(accP, fk[kk], fq[kk]);
+                        mma(accP, fl[kk], fq[kk]);
                     }
                     float a[4], pp[4];
 #pragma unroll
@@ -487,6 +498,11 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
             load_first(nnext, in);
         }
         cb::lds_barrier();
+        if (!strong) {
+            // the k / Gamma lo rows are read: the block inverses take their place
+            if (wave < 4) cb::store_tdiag<G>(smem, wave, l16, g4, tdiag);
+            cb::lds_barrier();
+        }
 
         // =============== off-diagonal blocks of T, through halves of 32 tokens ===============
         if (wave < 4) {
