@@ -84,13 +84,15 @@ __device__ __forceinline__ int tri_index(int row, int col) {
 // ------------------------------------------------------------------ local kernel ----
 constexpr int NT_LOCAL = 512;
 
-// LDS layout of the local kernel (bytes), at most 80 KiB.
+// LDS layout of the local kernel (bytes), about 95 KiB at DK = 128 (one workgroup per CU either way:
+// its registers allow two waves per SIMD).
 // RX: 192 rows of LDK bf16 -- mild chunk: BG rows 0-63, k / Gamma rows 64-127, QG rows 128-191;
 // strong chunk: the pivoted group and level tiles.  AM: -A below the diagonal blocks; TR, TTR:
 // the diagonal blocks of T and their transposes (the block inverses' inputs to T_C); on a mild
 // chunk they first hold the lo plane of k / Gamma for P, and the block inverses are stored after
-// P.  The block decays and strong-decay votes of the element phase share AM's bytes (a barrier
-// separates the uses).
+// P.  QGL: QG's lo plane on a mild chunk (P takes both k / Gamma and QG as hi + lo pairs).  The
+// block decays and strong-decay votes of the element phase share AM's bytes (a barrier separates
+// the uses).
 template <int DK>
 struct LocalCfg {
     static constexpr int CPL = DK / 32;
@@ -103,11 +105,12 @@ struct LocalCfg {
     static constexpr int FLG = BLK + 4 * DK * 4;      // [8] int votes (element phase)
     static constexpr int TR = AM + C * LC * 2;
     static constexpr int TTR = TR + C * LC * 2;
-    static constexpr int BYTES = TTR + C * LC * 2;
+    static constexpr int QGL = TTR + C * LC * 2;      // mild: QG lo rows, element -> P
+    static constexpr int BYTES = QGL + C * LDK * 2;
     static constexpr int KIL = TR;                    // mild: k / Gamma lo rows, element -> P (T's
                                                       // diagonal blocks land there after P)
-    static_assert(BYTES <= 81920, "LDS budget");
-    static_assert(KIL + C * LDK * 2 <= BYTES, "k / Gamma lo plane");
+    static_assert(BYTES <= 163840, "LDS budget");
+    static_assert(KIL + C * LDK * 2 <= QGL, "k / Gamma lo plane");
     static_assert(FLG + 32 <= TR, "votes inside AM");
 };
 
@@ -318,7 +321,7 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
                         kgt[c][m] = kv * (ls[c][m] * esa[c]);
                         xki[c] = kgt[c][m] * invgc[c];
                     }
-                    cb::store_bf16<CPL>(B16(G::QGR + eb + m * LDK * 2), xq);
+                    cb::store_bf16_split<CPL>(B16(G::QGR + eb + m * LDK * 2), B16(G::QGL + eb + m * LDK * 2), xq);
                     cb::store_bf16<CPL>(B16(G::RX + eb + m * LDK * 2), xb);
                     cb::store_bf16_split<CPL>(B16(G::RX + eb + (C + m) * LDK * 2), B16(G::KIL + eb + m * LDK * 2),
                                               xki);
@@ -429,12 +432,13 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
 #pragma unroll
                 for (int Ib = 0; Ib < 4; ++Ib) {
                     const int rk = cb::opq(((Ib * 16 + l16) * LDK + g4 * 8) * 2);
-                    Frag<bf16> fk[DK / 32], fl[DK / 32], fq[DK / 32];
+                    Frag<bf16> fk[DK / 32], fl[DK / 32], fq[DK / 32], fm[DK / 32];
 #pragma unroll
                     for (int kk = 0; kk < DK / 32; ++kk) {
                         fk[kk] = load_contig(B16(rk + G::RX + C * LDK * 2 + kk * 64));
                         fq[kk] = load_contig(B16(rk + G::QGR + kk * 64));
                         fl[kk] = load_contig(B16(rk + G::KIL + kk * 64));  // k / Gamma lo
+                        fm[kk] = load_contig(B16(rk + G::QGL + kk * 64));  // QG lo
                     }
                     cb::sched_fence();
                     f32x4 pd = zero4();
@@ -442,6 +446,7 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
                     for (int kk = 0; kk < DK / 32; ++kk) {
                         mma(pd, fk[kk], fq[kk]);
                         mma(pd, fl[kk], fq[kk]);
+                        mma(pd, fk[kk], fm[kk]);
                     }
                     float pp[4];
 #pragma unroll
@@ -471,6 +476,12 @@ __global__ __launch_bounds__(NT_LOCAL, 2) void local_kernel(
                         mma(accP, fk[kk], fq[kk]);
                         mma(accP, fl[kk], fq[kk]);
                     }
+#pragma unroll
+                    for (int kk = 0; kk < DK / 32; ++kk)
+                        fq[kk] = load_contig(B16(rl + G::QGL + Ib * 16 * LDK * 2 + kk * 64));  // QG lo
+                    cb::sched_fence();
+#pragma unroll
+                    for (int kk = 0; kk < DK / 32; ++kk) mma(accP, fk[kk], fq[kk]);
                     float a[4], pp[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) { a[r] = -accA[r]; pp[r] = accP[r]; }
