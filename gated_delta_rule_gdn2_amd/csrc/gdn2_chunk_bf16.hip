@@ -27,7 +27,8 @@
 //   * A, P: waves 0-3 form the diagonal block of A in both orientations in fp32
 //     accumulators and invert I + A_II at once by doubling,
 //         (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8),   N strictly lower 16 x 16,
-//     with hi + lo bf16 MFMA products; waves 4-6 form the off-diagonal blocks.
+//     with hi + lo bf16 MFMA products, and the diagonal block of P beside it; waves 4-6 form
+//     the off-diagonal blocks.
 //   * the off-diagonal blocks of T = (I + A)^{-1} through halves of 32 tokens:
 //     T = [[T_A, 0], [T_C, T_B]], T_10 = -T_11 A_10 T_00, T_32 likewise, T_C = -T_B A_BA T_A.
 //   * the state: wave 4 + j holds the 16 value columns j of the slice, all key rows, in fp32
@@ -472,21 +473,31 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
         if (!strong) {
             load_first(nnext, in);
             // single pivot at the chunk start: A = BG KI^T, P = QG KI^T on the lower blocks
+            // (wave 7 has no part here)
             if (wave < 4) {
-                // diagonal block I = wave: A_II in both orientations, then its inverse
+                // diagonal block I = wave: A_II in both orientations, then its inverse, and P_II
                 f32x4 nt = zero4(), nn = zero4();
                 const int rk = opq(((wave * 16 + l16) * LDK + g4 * 8) * 2);
-                Frag<bf16> fk[DK / 32], fa[DK / 32];
+                Frag<bf16> fk[DK / 32], fa[DK / 32], fq[DK / 32], fl[DK / 32];
 #pragma unroll
                 for (int kk = 0; kk < DK / 32; ++kk) {
                     fk[kk] = load_contig(B16(rk + G::RX + C * LDK * 2 + kk * 64));
                     fa[kk] = load_contig(B16(rk + G::BG + kk * 64));
+                    fq[kk] = load_contig(B16(rk + kk * 64));
+                    fl[kk] = load_contig(B16(rk + G::RX + kk * 64));  // KI lo
                 }
                 sched_fence();
+                f32x4 pd = zero4();
 #pragma unroll
                 for (int kk = 0; kk < DK / 32; ++kk) {
                     mma(nt, fk[kk], fa[kk]);  // lane holds A[l16][4 g4 + r]
                     mma(nn, fa[kk], fk[kk]);  // lane holds A[4 g4 + r][l16]
+                }
+                // the diagonal block of P beside it (independent of the inverse's chain)
+#pragma unroll
+                for (int kk = 0; kk < DK / 32; ++kk) {
+                    mma(pd, fk[kk], fq[kk]);  // P[l16][4 g4 + r]
+                    mma(pd, fl[kk], fq[kk]);
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -495,32 +506,12 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(
                     nn[r] = j > l16 ? nn[r] : 0.f;
                 }
                 store_tdiag<G>(smem, wave, l16, g4, unit_lower_inverse(nt, nn, l16, g4));
-            } else if (wave == 7) {
-                // the diagonal blocks of P, so that waves 0-3 go straight to their inverses
+                float pp[4];
 #pragma unroll
-                for (int I = 0; I < 4; ++I) {
-                    const int rk = opq(((I * 16 + l16) * LDK + g4 * 8) * 2);
-                    Frag<bf16> fk[DK / 32], fl[DK / 32], fq[DK / 32];
-#pragma unroll
-                    for (int kk = 0; kk < DK / 32; ++kk) {
-                        fk[kk] = load_contig(B16(rk + G::RX + C * LDK * 2 + kk * 64));
-                        fq[kk] = load_contig(B16(rk + kk * 64));
-                        fl[kk] = load_contig(B16(rk + G::RX + kk * 64));  // KI lo
-                    }
-                    sched_fence();
-                    f32x4 pd = zero4();
-#pragma unroll
-                    for (int kk = 0; kk < DK / 32; ++kk) {
-                        mma(pd, fk[kk], fq[kk]);  // P[l16][4 g4 + r]
-                        mma(pd, fl[kk], fq[kk]);
-                    }
-                    float pp[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) pp[r] = 4 * g4 + r <= l16 ? pd[r] : 0.f;
-                    const int idx = (I * 16 + l16) * LC + I * 16 + g4 * 4;
-                    store_bf16_split<4>(sPh + idx, sPl + idx, pp);
-                }
-            } else {
+                for (int r = 0; r < 4; ++r) pp[r] = 4 * g4 + r <= l16 ? pd[r] : 0.f;
+                const int idx = (wave * 16 + l16) * LC + wave * 16 + g4 * 4;
+                store_bf16_split<4>(sPh + idx, sPl + idx, pp);
+            } else if (wave < 7) {
                 // off-diagonal pairs, two per wave sharing a block row or column:
                 // wave 4: (1,0) (2,0); wave 5: (2,1) (3,1); wave 6: (3,0) (3,2)
                 const int rl = opq((l16 * LDK + g4 * 8) * 2);
